@@ -1,0 +1,255 @@
+"""ctypes marshalling for ``include/harts.h`` (same names, same arguments).
+
+Host arrays are numpy; device buffers are torch tensors passed by data
+pointer, with the current torch stream as the HIP stream.  Every entry point
+checks the shapes it can see and raises :class:`HartsError` with the
+library's message on a negative return code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "_harts.so")
+
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+
+if not os.path.exists(_SO):
+    raise ImportError("HIP library %s is missing: build it with chunkwise_linear_attention_gated_amd.build.build()"
+                      % _SO)
+_L = ctypes.CDLL(_SO)
+library = _SO
+
+P = ctypes.c_void_p
+I32, I64 = ctypes.c_int32, ctypes.c_int64
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("S", I64), ("C", I64), ("chunk_B", I32), ("n_rounds", I32), ("min_calls", I32),
+                ("n_sequences", I32), ("n_slots", I32), ("n_boundaries", I32), ("replay_total", I64),
+                ("n_chunks", I64), ("n_vrows", I64)]
+
+
+class SeqView(ctypes.Structure):
+    _fields_ = [("round", I32), ("init_slot", I32), ("start", I64), ("row_begin", I64), ("row_end", I64),
+                ("replay_off", I64), ("n_replay", I32), ("n_emits", I32), ("emit_off", I64)]
+
+
+class KdaIO(ctypes.Structure):
+    _fields_ = [("q", P), ("k", P), ("v", P), ("g", P), ("beta", P), ("o", P), ("states", P),
+                ("init_states", P), ("final_states", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class KdaGrad(ctypes.Structure):
+    _fields_ = [("dO", P), ("dq", P), ("dk", P), ("dv", P), ("dg", P), ("dbeta", P), ("dstates", P), ("dinit", P)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_L, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_tree_build = _sig("harts_tree_build", I32, P, P, I64, ctypes.POINTER(P))
+_tree_stats = _sig("harts_tree_stats", I32, P, P, P, P, P)
+_tree_free = _sig("harts_tree_free", None, P)
+_plan_create = _sig("harts_plan_create", I32, P, I32, ctypes.POINTER(P))
+_plan_create_varlen = _sig("harts_plan_create_varlen", I32, P, I64, I32, P, I32, ctypes.POINTER(P))
+_plan_info = _sig("harts_plan_info", I32, P, ctypes.POINTER(PlanInfo))
+_plan_maps = _sig("harts_plan_maps", I32, P, P, P, P)
+_plan_sequences = _sig("harts_plan_sequences", I32, P, P)
+_plan_replay_rows = _sig("harts_plan_replay_rows", I32, P, P)
+_plan_emits = _sig("harts_plan_emits", I32, P, P, P)
+_plan_boundary_offsets = _sig("harts_plan_boundary_offsets", I32, P, P)
+_plan_free = _sig("harts_plan_free", None, P)
+_plan_upload = _sig("harts_plan_upload", I32, P, I32, I32, I32, I32, P, ctypes.POINTER(P))
+_ws_size = _sig("harts_kda_workspace_size", I32, P, I32, ctypes.POINTER(ctypes.c_size_t))
+_dev_free = _sig("harts_dev_plan_free", None, P)
+_kda_fwd = _sig("harts_kda_fwd", I32, P, ctypes.POINTER(KdaIO), P)
+_kda_bwd = _sig("harts_kda_bwd", I32, P, ctypes.POINTER(KdaIO), ctypes.POINTER(KdaGrad), P)
+_lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
+_lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
+_last_error = _sig("harts_last_error", ctypes.c_char_p)
+_version = _sig("harts_version", ctypes.c_char_p)
+
+
+class HartsError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("harts error %d: %s" % (code, msg))
+        self.code = code
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise HartsError(rc, _last_error().decode())
+
+
+def version() -> str:
+    return _version().decode()
+
+
+def _np(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return ctypes.c_void_p(stream)
+    import torch
+    if torch.cuda.is_available():
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return ctypes.c_void_p(0)
+
+
+class _PlanBase:
+    _h = None
+
+    @property
+    def info(self) -> PlanInfo:
+        inf = PlanInfo()
+        _check(_plan_info(self._h, ctypes.byref(inf)))
+        return inf
+
+    def maps(self):
+        inf = self.info
+        m = np.empty(inf.S, np.int64)
+        q = np.empty(inf.C, np.int32)
+        n2r = np.empty(inf.C, np.int64)
+        _check(_plan_maps(self._h, m.ctypes.data, q.ctypes.data, n2r.ctypes.data))
+        return m, q, n2r
+
+    def sequences(self):
+        inf = self.info
+        arr = (SeqView * inf.n_sequences)()
+        _check(_plan_sequences(self._h, arr))
+        return [dict((f, getattr(s, f)) for f, _ in SeqView._fields_) for s in arr]
+
+    def replay_rows(self) -> np.ndarray:
+        inf = self.info
+        out = np.empty(inf.replay_total, np.int64)
+        _check(_plan_replay_rows(self._h, out.ctypes.data if inf.replay_total else None))
+        return out
+
+    def emits(self):
+        seqs = self.sequences()
+        n = sum(s["n_emits"] for s in seqs)
+        b = np.empty(n, np.int32)
+        t = np.empty(n, np.int32)
+        _check(_plan_emits(self._h, b.ctypes.data, t.ctypes.data))
+        return b, t
+
+    def __del__(self):
+        if self._h:
+            _plan_free(self._h)
+            self._h = None
+
+
+class TreePlan(_PlanBase):
+    """harts_tree_build + harts_plan_create: trajectories -> compact tokens ->
+    minimum-call packed rounds."""
+
+    def __init__(self, tokens, offsets, chunk_B: int):
+        tokens = _np(tokens, np.int32)
+        offsets = _np(offsets, np.int64)
+        self._tree = P()
+        _check(_tree_build(tokens.ctypes.data, offsets.ctypes.data, len(offsets) - 1, ctypes.byref(self._tree)))
+        h = P()
+        _check(_plan_create(self._tree, chunk_B, ctypes.byref(h)))
+        self._h = h
+
+    def tree_stats(self):
+        v = [I64() for _ in range(4)]
+        _check(_tree_stats(self._tree, *[ctypes.byref(x) for x in v]))
+        return dict(S=v[0].value, C=v[1].value, n_segments=v[2].value, n_forks=v[3].value)
+
+    def __del__(self):
+        super().__del__()
+        if getattr(self, "_tree", None):
+            _tree_free(self._tree)
+            self._tree = None
+
+
+class VarlenPlan(_PlanBase):
+    """harts_plan_create_varlen: independent packed sequences in one call."""
+
+    def __init__(self, cu_seqlens, chunk_B: int, has_init=None, emit_boundaries: bool = False):
+        cu = _np(cu_seqlens, np.int64)
+        hi = None if has_init is None else _np(has_init, np.uint8)
+        h = P()
+        _check(_plan_create_varlen(cu.ctypes.data, len(cu) - 1, chunk_B, None if hi is None else hi.ctypes.data,
+                                   int(bool(emit_boundaries)), ctypes.byref(h)))
+        self._h = h
+        self._n = len(cu) - 1
+
+    def boundary_offsets(self) -> np.ndarray:
+        out = np.empty(self._n + 1, np.int64)
+        _check(_plan_boundary_offsets(self._h, out.ctypes.data))
+        return out
+
+
+class DevicePlan:
+    """harts_plan_upload: descriptors on the device for (H, dk, dv, dtype)."""
+
+    def __init__(self, plan: _PlanBase, H: int, dk: int, dv: int, dtype: int, stream=None):
+        self.plan = plan
+        self.H, self.dk, self.dv, self.dtype = H, dk, dv, dtype
+        h = P()
+        _check(_plan_upload(plan._h, H, dk, dv, dtype, _stream(stream), ctypes.byref(h)))
+        self._h = h
+
+    def workspace_size(self, backward: bool) -> int:
+        n = ctypes.c_size_t()
+        _check(_ws_size(self._h, int(bool(backward)), ctypes.byref(n)))
+        return n.value
+
+    def __del__(self):
+        if getattr(self, "_h", None):
+            _dev_free(self._h)
+            self._h = None
+
+
+def _io(q, k, v, g, beta, o, states, init_states, final_states, workspace):
+    return KdaIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(states), _ptr(init_states),
+                 _ptr(final_states), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
+
+
+def kda_fwd(dplan: DevicePlan, q, k, v, g, beta, o, states=None, init_states=None, final_states=None,
+            workspace=None, stream=None):
+    """harts_kda_fwd over every round of the plan."""
+    io = _io(q, k, v, g, beta, o, states, init_states, final_states, workspace)
+    _check(_kda_fwd(dplan._h, ctypes.byref(io), _stream(stream)))
+
+
+def kda_bwd(dplan: DevicePlan, q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta, states=None, init_states=None,
+            dstates=None, dinit=None, workspace=None, stream=None):
+    """harts_kda_bwd over every round of the plan, in reverse."""
+    io = _io(q, k, v, g, beta, None, states, init_states, None, workspace)
+    gr = KdaGrad(_ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dstates), _ptr(dinit))
+    _check(_kda_bwd(dplan._h, ctypes.byref(io), ctypes.byref(gr), _stream(stream)))
+
+
+def logprob_workspace_size(C: int) -> int:
+    return int(_lp_ws(C))
+
+
+def logprob_gather(logits, m, labels, logp, q=None, lse=None, workspace=None, stream=None):
+    """harts_logprob_gather: logp[s] = logits[m[s], labels[s]] - logsumexp(logits[m[s]])."""
+    import torch
+    C, V = logits.shape
+    dtype = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_FP32
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise HartsError(-1, "logits must be bf16 or fp32")
+    S = m.numel()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lp(_ptr(logits), C, V, dtype, _ptr(m), _ptr(labels), S, _ptr(logp), _ptr(q), _ptr(lse),
+               _ptr(workspace), ws_bytes, _stream(stream)))

@@ -1,0 +1,400 @@
+// C ABI of the tree-packed chunkwise gated-delta path (declared in include/harts.h).
+// Host calls wrap the C++ planner; device calls upload descriptors and enqueue
+// the per-round HIP kernels on the caller's stream.  No exception crosses the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/harts.h"
+#include "host/plan.hpp"
+#include "kernels/launch.h"
+
+using harts::Error;
+
+struct harts_tree {
+  harts::TreeHost t;
+};
+struct harts_plan {
+  harts::PlanHost p;
+};
+struct harts_dev_plan {
+  harts::PlanHost p;
+  harts::KdaDims dims{};
+  int32_t* vrows = nullptr;
+  harts::SeqDesc* seqs = nullptr;
+  harts::ChunkDesc* chunks = nullptr;
+  int32_t* cons_off = nullptr;
+  int32_t* cons = nullptr;
+  int32_t* fix_rows = nullptr;
+  int32_t* fix_off = nullptr;
+  int32_t* fix_idx = nullptr;
+  // workspace layout (byte offsets)
+  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0,
+         off_dinit = 0, off_rg = 0;
+  size_t ws_fwd = 0, ws_bwd = 0;
+};
+
+namespace {
+thread_local std::string g_err;
+
+int fail(int code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+template <typename F>
+int guarded(F&& f) {
+  try {
+    f();
+    return HARTS_OK;
+  } catch (const Error& e) {
+    return fail(e.code, e.what());
+  } catch (const std::bad_alloc&) {
+    return fail(HARTS_ENOMEM, "host allocation failed");
+  } catch (const std::exception& e) {
+    return fail(HARTS_EINVAL, e.what());
+  }
+}
+
+void hip_check(hipError_t e, const char* what) {
+  if (e != hipSuccess) throw Error(HARTS_EHIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+template <typename T>
+T* upload(const std::vector<T>& v, hipStream_t s) {
+  if (v.empty()) return nullptr;
+  T* p = nullptr;
+  hip_check(hipMalloc(reinterpret_cast<void**>(&p), v.size() * sizeof(T)), "hipMalloc");
+  const hipError_t e = hipMemcpyAsync(p, v.data(), v.size() * sizeof(T), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    hip_check(e, "hipMemcpyAsync");
+  }
+  return p;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+void free_dev(harts_dev_plan* d) {
+  void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx};
+  for (void* p : ptrs)
+    if (p) (void)hipFree(p);
+}
+
+harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int r, char* ws) {
+  const harts::RoundRange& rr = d->p.rounds[r];
+  harts::RoundArgs a{};
+  a.vrows = d->vrows;
+  a.seqs = d->seqs + rr.seq0;
+  a.chunks = d->chunks + rr.chunk0;
+  a.nseq = rr.seq1 - rr.seq0;
+  a.nchunk = rr.chunk1 - rr.chunk0;
+  a.q = io->q;
+  a.k = io->k;
+  a.v = io->v;
+  a.g = io->g;
+  a.beta = io->beta;
+  if (d->p.varlen) {
+    a.init_pool = io->init_states;
+    a.emit_pool = io->states;
+    a.final_pool = io->final_states;
+  } else {
+    a.init_pool = io->states;
+    a.emit_pool = io->states;
+    a.final_pool = nullptr;
+  }
+  a.ws.W = ws + d->off_W;
+  a.ws.UpT = ws + d->off_UpT;
+  a.ws.KhT = ws + d->off_KhT;
+  a.ws.Qt = ws + d->off_Qt;
+  a.ws.Mm = ws + d->off_Mm;
+  a.ws.El = reinterpret_cast<float*>(ws + d->off_El);
+  a.ws.QeffT = ws + d->off_Qe;
+  a.h = ws + d->off_h;
+  return a;
+}
+
+void check_io(const harts_dev_plan* d, const harts_kda_io* io, bool bwd) {
+  if (!io) throw Error(HARTS_EINVAL, "io is NULL");
+  if (!io->q || !io->k || !io->v || !io->g || !io->beta) throw Error(HARTS_EINVAL, "q, k, v, g and beta are required");
+  if (!bwd && !io->o) throw Error(HARTS_EINVAL, "o is required");
+  if (!io->workspace || io->workspace_bytes < (bwd ? d->ws_bwd : d->ws_fwd))
+    throw Error(HARTS_EINVAL, "workspace missing or smaller than harts_kda_workspace_size()");
+  if (!d->p.varlen && d->p.n_slots > 0 && !io->states) throw Error(HARTS_EINVAL, "states (slot pool) is required");
+  if (d->p.varlen) {
+    bool any_init = false;
+    for (auto& s : d->p.seqs) any_init |= s.init >= 0;
+    if (any_init && !io->init_states) throw Error(HARTS_EINVAL, "init_states is required (plan has initial states)");
+    if (d->p.n_boundaries > 0 && !io->states) throw Error(HARTS_EINVAL, "states is required (plan emits boundaries)");
+  }
+}
+}  // namespace
+
+extern "C" {
+
+const char* harts_last_error(void) { return g_err.c_str(); }
+const char* harts_version(void) { return "harts-mi355x 0.1 (gfx950)"; }
+
+int harts_tree_build(const int32_t* tokens, const int64_t* traj_offsets, int64_t n_traj, harts_tree** out) {
+  return guarded([&] {
+    if (!out) throw Error(HARTS_EINVAL, "out is NULL");
+    *out = nullptr;
+    auto* t = new harts_tree{harts::build_tree(tokens, traj_offsets, n_traj)};
+    *out = t;
+  });
+}
+
+int harts_tree_stats(const harts_tree* tree, int64_t* S, int64_t* C, int64_t* n_segments, int64_t* n_forks) {
+  return guarded([&] {
+    if (!tree) throw Error(HARTS_EINVAL, "tree is NULL");
+    if (S) *S = tree->t.S;
+    if (C) *C = tree->t.C;
+    if (n_segments) *n_segments = int64_t(tree->t.seg_first.size());
+    if (n_forks) *n_forks = tree->t.n_forks;
+  });
+}
+
+void harts_tree_free(harts_tree* tree) { delete tree; }
+
+int harts_plan_create(const harts_tree* tree, int32_t chunk_B, harts_plan** out) {
+  return guarded([&] {
+    if (!tree || !out) throw Error(HARTS_EINVAL, "tree and out must be non-NULL");
+    *out = nullptr;
+    *out = new harts_plan{harts::make_plan(tree->t, chunk_B)};
+  });
+}
+
+int harts_plan_create_varlen(const int64_t* cu_seqlens, int64_t n_seq, int32_t chunk_B, const uint8_t* has_init,
+                             int32_t emit_boundaries, harts_plan** out) {
+  return guarded([&] {
+    if (!out) throw Error(HARTS_EINVAL, "out is NULL");
+    *out = nullptr;
+    *out = new harts_plan{harts::make_varlen_plan(cu_seqlens, n_seq, chunk_B, has_init, emit_boundaries != 0)};
+  });
+}
+
+int harts_plan_info(const harts_plan* plan, harts_plan_info_t* o) {
+  return guarded([&] {
+    if (!plan || !o) throw Error(HARTS_EINVAL, "plan and out must be non-NULL");
+    const harts::PlanHost& p = plan->p;
+    o->S = p.S;
+    o->C = p.C;
+    o->chunk_B = p.B;
+    o->n_rounds = p.n_rounds;
+    o->min_calls = p.min_calls;
+    o->n_sequences = int32_t(p.seqs.size());
+    o->n_slots = p.n_slots;
+    o->n_boundaries = p.n_boundaries;
+    o->replay_total = p.replay_total;
+    o->n_chunks = int64_t(p.chunk_desc.size());
+    o->n_vrows = int64_t(p.vrows.size());
+  });
+}
+
+int harts_plan_maps(const harts_plan* plan, int64_t* m, int32_t* q, int64_t* node_to_row) {
+  return guarded([&] {
+    if (!plan) throw Error(HARTS_EINVAL, "plan is NULL");
+    const harts::PlanHost& p = plan->p;
+    if (m) std::memcpy(m, p.m.data(), p.m.size() * sizeof(int64_t));
+    if (q) std::memcpy(q, p.q.data(), p.q.size() * sizeof(int32_t));
+    if (node_to_row) std::memcpy(node_to_row, p.node_to_row.data(), p.node_to_row.size() * sizeof(int64_t));
+  });
+}
+
+int harts_plan_sequences(const harts_plan* plan, harts_seq_view* seqs) {
+  return guarded([&] {
+    if (!plan || !seqs) throw Error(HARTS_EINVAL, "plan and seqs must be non-NULL");
+    for (size_t i = 0; i < plan->p.seqs.size(); ++i) {
+      const harts::SeqHost& s = plan->p.seqs[i];
+      harts_seq_view& v = seqs[i];
+      v.round = s.round;
+      v.init_slot = s.init;
+      v.start = s.start;
+      v.row_begin = s.row_begin;
+      v.row_end = s.row_end;
+      v.replay_off = s.replay_off;
+      v.n_replay = s.n_replay;
+      v.n_emits = s.n_emits;
+      v.emit_off = s.emit_off;
+    }
+  });
+}
+
+int harts_plan_replay_rows(const harts_plan* plan, int64_t* rows) {
+  return guarded([&] {
+    if (!plan || (!rows && !plan->p.replay_rows.empty())) throw Error(HARTS_EINVAL, "plan and rows must be non-NULL");
+    if (!plan->p.replay_rows.empty())
+      std::memcpy(rows, plan->p.replay_rows.data(), plan->p.replay_rows.size() * sizeof(int64_t));
+  });
+}
+
+int harts_plan_emits(const harts_plan* plan, int32_t* boundary, int32_t* target) {
+  return guarded([&] {
+    if (!plan) throw Error(HARTS_EINVAL, "plan is NULL");
+    const size_t n = plan->p.emit_boundary.size();
+    if (n && boundary) std::memcpy(boundary, plan->p.emit_boundary.data(), n * sizeof(int32_t));
+    if (n && target) std::memcpy(target, plan->p.emit_target.data(), n * sizeof(int32_t));
+  });
+}
+
+int harts_plan_boundary_offsets(const harts_plan* plan, int64_t* offsets) {
+  return guarded([&] {
+    if (!plan || !offsets) throw Error(HARTS_EINVAL, "plan and offsets must be non-NULL");
+    if (!plan->p.varlen) throw Error(HARTS_ESTATE, "boundary offsets exist only for varlen plans");
+    std::memcpy(offsets, plan->p.boundary_offsets.data(), plan->p.boundary_offsets.size() * sizeof(int64_t));
+  });
+}
+
+void harts_plan_free(harts_plan* plan) { delete plan; }
+
+int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void* stream,
+                      harts_dev_plan** out) {
+  return guarded([&] {
+    if (!plan || !out) throw Error(HARTS_EINVAL, "plan and out must be non-NULL");
+    *out = nullptr;
+    if (H < 1) throw Error(HARTS_EINVAL, "H must be >= 1");
+    if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+    harts::KdaDims dims{H, dk, dv, plan->p.B, dtype};
+    if (!harts::kda_supported(dims))
+      throw Error(HARTS_EINVAL, "unsupported (dtype, chunk_B, dk, dv) = (" + std::to_string(dtype) + ", " +
+                                    std::to_string(plan->p.B) + ", " + std::to_string(dk) + ", " + std::to_string(dv) +
+                                    ")");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto* d = new harts_dev_plan();
+    try {
+      d->p = plan->p;
+      d->dims = dims;
+      d->vrows = upload(d->p.vrows, s);
+      d->seqs = upload(d->p.seq_desc, s);
+      d->chunks = upload(d->p.chunk_desc, s);
+      d->cons_off = upload(d->p.slot_cons_off, s);
+      d->cons = upload(d->p.slot_cons, s);
+      d->fix_rows = upload(d->p.fix_rows, s);
+      d->fix_off = upload(d->p.fix_off, s);
+      d->fix_idx = upload(d->p.fix_idx, s);
+      // the host vectors must outlive the asynchronous copies
+      hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+      const size_t es = dtype == HARTS_DTYPE_BF16 ? 2 : 4;
+      const size_t MC = size_t(d->p.max_round_chunks) * H, BT = size_t(d->p.B);
+      size_t off = 0;
+      auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align256(off + bytes);
+        return o;
+      };
+      d->off_W = take(MC * BT * dk * es);
+      d->off_UpT = take(MC * dv * BT * es);
+      d->off_KhT = take(MC * dk * BT * es);
+      d->off_Mm = take(MC * BT * BT * es);
+      d->off_El = take(MC * dk * 4);
+      const size_t common = off;
+      d->off_Qt = take(MC * BT * dk * es);
+      d->ws_fwd = off;
+      off = common;
+      d->off_Qe = take(MC * dk * BT * es);
+      d->off_h = take(MC * dv * dk * es);
+      d->off_dh = take(MC * dv * dk * es);
+      d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
+      d->off_rg = take(size_t(d->p.replay_total) * H * (2 * dk + dv + 1) * 4);
+      d->ws_bwd = off;
+      if (d->ws_fwd == 0) d->ws_fwd = 256;
+    } catch (...) {
+      free_dev(d);
+      delete d;
+      throw;
+    }
+    *out = d;
+  });
+}
+
+int harts_kda_workspace_size(const harts_dev_plan* dplan, int32_t backward, size_t* bytes) {
+  return guarded([&] {
+    if (!dplan || !bytes) throw Error(HARTS_EINVAL, "dplan and bytes must be non-NULL");
+    *bytes = backward ? dplan->ws_bwd : dplan->ws_fwd;
+  });
+}
+
+void harts_dev_plan_free(harts_dev_plan* dplan) {
+  if (!dplan) return;
+  free_dev(dplan);
+  delete dplan;
+}
+
+int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream) {
+  return guarded([&] {
+    if (!d) throw Error(HARTS_EINVAL, "dplan is NULL");
+    check_io(d, io, false);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(io->workspace);
+    for (int r = 0; r < d->p.n_rounds; ++r) {
+      harts::RoundArgs a = round_args(d, io, r, ws);
+      a.o = io->o;
+      hip_check(harts::launch_kda_prep(d->dims, a, false, s), "prep kernel launch");
+      hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
+    }
+  });
+}
+
+int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_kda_grad* g, void* stream) {
+  return guarded([&] {
+    if (!d) throw Error(HARTS_EINVAL, "dplan is NULL");
+    check_io(d, io, true);
+    if (!g || !g->dO || !g->dq || !g->dk || !g->dv || !g->dg || !g->dbeta)
+      throw Error(HARTS_EINVAL, "dO, dq, dk, dv, dg and dbeta are required");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(io->workspace);
+    for (int r = d->p.n_rounds - 1; r >= 0; --r) {
+      harts::BwdRoundArgs b{};
+      b.r = round_args(d, io, r, ws);
+      b.r.o = nullptr;
+      b.dO = g->dO;
+      b.dq = g->dq;
+      b.dk = g->dk;
+      b.dv = g->dv;
+      b.dg = g->dg;
+      b.dbeta = g->dbeta;
+      b.dh = ws + d->off_dh;
+      b.dinit = d->p.varlen ? g->dinit : reinterpret_cast<float*>(ws + d->off_dinit);
+      b.dstates = d->p.varlen ? nullptr : g->dstates;
+      b.slot_cons_off = d->p.varlen ? nullptr : d->cons_off;
+      b.slot_cons = d->p.varlen ? nullptr : d->cons;
+      b.replay_grad = reinterpret_cast<float*>(ws + d->off_rg);
+      hip_check(harts::launch_kda_prep(d->dims, b.r, true, s), "prep kernel launch");
+      hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
+      hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
+      hip_check(harts::launch_kda_grad(d->dims, b, s), "gradient kernel launch");
+    }
+    if (!d->p.fix_rows.empty())
+      hip_check(harts::launch_replay_fixup(d->dims, d->fix_rows, d->fix_off, d->fix_idx,
+                                           int32_t(d->p.fix_rows.size()), reinterpret_cast<float*>(ws + d->off_rg),
+                                           g->dk, g->dv, g->dg, g->dbeta, s),
+                "replay fixup launch");
+  });
+}
+
+size_t harts_logprob_workspace_size(int64_t C) { return C > 0 ? align256(size_t(C) * 4) : 256; }
+
+int harts_logprob_gather(const void* logits, int64_t C, int64_t V, int32_t dtype, const int64_t* m,
+                         const int32_t* labels, int64_t S, float* logp_out, int32_t* q_out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    if (C < 0 || V < 1 || S < 0) throw Error(HARTS_EINVAL, "need C >= 0, V >= 1, S >= 0");
+    if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+    if (C > 0 && !logits) throw Error(HARTS_EINVAL, "logits is NULL");
+    if (S > 0 && (!m || !labels || !logp_out)) throw Error(HARTS_EINVAL, "m, labels and logp_out are required");
+    if (C >= (int64_t(1) << 31)) throw Error(HARTS_ERANGE, "C must be < 2^31");
+    float* lse = lse_out;
+    if (!lse) {
+      if (!workspace || workspace_bytes < size_t(C) * 4) throw Error(HARTS_EINVAL, "workspace too small");
+      lse = static_cast<float*>(workspace);
+    }
+    hip_check(harts::launch_logprob(logits, C, V, dtype, m, labels, S, logp_out, q_out, lse,
+                                    static_cast<hipStream_t>(stream)),
+              "log-prob kernel launch");
+  });
+}
+
+}  // extern "C"

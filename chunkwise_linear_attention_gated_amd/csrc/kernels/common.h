@@ -1,0 +1,122 @@
+// Device helpers for gfx950 (CDNA4): MFMA fragment loads and tile layouts.
+//
+// Matrix-core layouts (16x16 output tiles, 64-lane wavefront):
+//   bf16: v_mfma_f32_16x16x32_bf16 -- lane l holds A[l%16][8*(l/16) .. +8) and
+//         B[8*(l/16) .. +8)[l%16]; K step 32.
+//   fp32: v_mfma_f32_16x16x4f32    -- lane l holds A[l%16][l/16] and
+//         B[l/16][l%16]; K step 4.
+//   Both: lane l holds C[4*(l/16) + r][l%16], r = 0..3.
+//
+// An operand is read either from a matrix whose K dimension is contiguous
+// (one 16-byte read per bf16 fragment) or from one stored K-major (the
+// fragment is gathered element by element).  The same helpers serve LDS and
+// global memory.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace harts {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+  static constexpr int KS = 32;
+  using Frag = bf16x8;
+  // element (r, k) at p[r * ld + k]: K contiguous
+  __device__ static __forceinline__ Frag kc(const bf16* p, int ld, int r0, int k0, int lane) {
+    return *reinterpret_cast<const bf16x8*>(p + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+  }
+  // element (r, k) at p[k * ld + r]: gathered
+  __device__ static __forceinline__ Frag rc(const bf16* p, int ld, int r0, int k0, int lane) {
+    Frag f;
+    const bf16* q = p + (k0 + 8 * (lane >> 4)) * ld + r0 + (lane & 15);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = q[t * ld];
+    return f;
+  }
+  __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mma<float> {
+  static constexpr int KS = 4;
+  using Frag = float;
+  __device__ static __forceinline__ Frag kc(const float* p, int ld, int r0, int k0, int lane) {
+    return p[(r0 + (lane & 15)) * ld + k0 + (lane >> 4)];
+  }
+  __device__ static __forceinline__ Frag rc(const float* p, int ld, int r0, int k0, int lane) {
+    return p[(k0 + (lane >> 4)) * ld + r0 + (lane & 15)];
+  }
+  __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// C-layout coordinates of accumulator element r for this lane
+__device__ __forceinline__ int crow(int lane, int r) { return 4 * (lane >> 4) + r; }
+__device__ __forceinline__ int ccol(int lane) { return lane & 15; }
+
+// Store 4 consecutive values (the 4 accumulator rows of one lane) at p[0..3].
+template <typename T> __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *reinterpret_cast<f32x4*>(p) = f32x4{a, b, c, d};
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)a, (bf16)b, (bf16)c, (bf16)d};
+}
+template <typename T> __device__ __forceinline__ void load4(const T* p, float* v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = to_f(p[r]);
+}
+
+// 16-byte vector of T (8 bf16 or 4 fp32) converted to floats
+template <typename T> struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+};
+
+template <typename T> __device__ __forceinline__ void ld16(const T* p, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) out[t] = (float)v[t];
+  } else {
+    f32x4 v = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = v[t];
+  }
+}
+template <typename T> __device__ __forceinline__ void st16(T* p, const float* in) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 v;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] = (bf16)in[t];
+    *reinterpret_cast<bf16x8*>(p) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(p) = f32x4{in[0], in[1], in[2], in[3]};
+  }
+}
+template <typename T> __device__ __forceinline__ void copy16(T* dst, const T* src) {
+  *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
+}
+
+// Blocks of a grid are dealt round-robin to the 8 XCDs; remap so that runs of
+// consecutive logical ids (e.g. the value-column tiles of one sequence-head,
+// which read the same per-chunk operands) land on one XCD and share its L2.
+__device__ __forceinline__ int xcd_logical(int b, int nblocks) {
+  if (nblocks % 8) return b;
+  return (b % 8) * (nblocks / 8) + b / 8;
+}
+
+}  // namespace harts

@@ -1,0 +1,66 @@
+// Host-callable launchers of the HIP kernels (one packed round at a time).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../desc.h"
+
+namespace harts {
+
+// Per-chunk-head workspace produced by the prep kernel and consumed by the
+// serial state / state-gradient passes.  Element offsets are
+// [local chunk][head][...]; every array holds the plan dtype except El.
+struct ChunkWs {
+  void* W;      // [BT][D]   W = T (K * e^G)                      (token-major)
+  void* UpT;    // [DV][BT]  (T V)^T
+  void* KhT;    // [D][BT]   (K * e^{G_last - G})^T
+  void* Qt;     // [BT][D]   Q * e^G                               (forward)
+  void* Mm;     // [BT][BT]  M = lower(gated Q K^T)
+  float* El;    // [D]       e^{G_last}
+  void* QeffT;  // [D][BT]   (Q~ - M W)^T                          (backward)
+};
+
+struct KdaDims {
+  int H, D, DV, BT, dtype;  // dtype: 0 bf16, 1 fp32
+};
+
+struct RoundArgs {
+  const int32_t* vrows;       // global virtual-row table
+  const SeqDesc* seqs;        // this round's sequences
+  const ChunkDesc* chunks;    // this round's chunks
+  int32_t nseq, nchunk;
+  const void *q, *k, *v, *g, *beta;
+  void* o;                    // forward output [N][H][DV] (nullable)
+  const float* init_pool;     // initial states by SeqDesc::init
+  float* emit_pool;           // emitted states by ChunkDesc::emit
+  float* final_pool;          // final states by SeqDesc::final_idx
+  ChunkWs ws;
+  void* h;                    // backward: S_n^T per chunk [chunk][H][DV][D] (nullable)
+};
+
+struct BwdRoundArgs {
+  RoundArgs r;
+  const void* dO;             // [N][H][DV]
+  void *dq, *dk, *dv, *dg, *dbeta;
+  void* dh;                   // dS at chunk ends, [chunk][H][DV][D]
+  float* dinit;               // per-sequence dL/d(initial state) [global seq][H][D][DV]
+  float* dstates;             // per-slot gradient output (nullable)
+  const int32_t* slot_cons_off;  // CSR of consumer sequences per slot (nullable for varlen)
+  const int32_t* slot_cons;
+  float* replay_grad;         // [replay_total][H][3*D + 1] fp32 (dk, dv, dg, dbeta of replayed rows)
+};
+
+hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
+hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
+hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
+hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const int32_t* fix_off,
+                               const int32_t* fix_idx, int32_t nrows, const float* replay_grad, void* dk, void* dv,
+                               void* dg, void* dbeta, hipStream_t s);
+bool kda_supported(const KdaDims& d);
+
+hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
+                          int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
+
+}  // namespace harts

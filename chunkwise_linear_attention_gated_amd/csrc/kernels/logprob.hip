@@ -1,0 +1,148 @@
+// Compact -> semantic log-probabilities on gfx950 (HARTS close-reading blog,
+// section 4.4; paperlayer summary, section 3 "Semantic Preservation"): the
+// vocabulary-wide max and sum-exp are computed once per compact logit row,
+// then every semantic position reads its own target logit in the original
+// order, so vocabulary work is O(C V) + O(S), never O(S V).
+//
+//   row pass:    lse[c] = log sum_v exp(x[c, v])   (one streaming read of each row)
+//   gather pass: logp[s] = x[m[s], label[s]] - lse[m[s]];  q[m[s]] += 1
+//
+// The row pass is a pure HBM stream: 16-byte loads, four in flight per
+// thread, online max / sum-exp in base 2 (one exp2 per element).
+#include "common.h"
+#include "launch.h"
+
+namespace harts {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ void online_add(float& m, float& s, float v2) {
+  // v2 is in base-2 units; (m, s) represents s * 2^m
+  if (v2 > m) {
+    s = s * exp2f(m - v2) + 1.f;
+    m = v2;
+  } else {
+    s += exp2f(v2 - m);
+  }
+}
+
+__device__ __forceinline__ void online_merge(float& m, float& s, float m2, float s2) {
+  if (m2 > m) {
+    s = s * exp2f(m - m2) + s2;
+    m = m2;
+  } else if (s2 > 0.f) {
+    s += s2 * exp2f(m2 - m);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void row_lse_kernel(const T* __restrict__ x, int64_t V, float* __restrict__ lse,
+                                                      bool vec_ok) {
+  constexpr int VN = 16 / sizeof(T);
+  const int64_t c = blockIdx.x;
+  const T* row = x + c * V;
+  float m = -INFINITY, s = 0.f;
+  const int64_t nvec = vec_ok ? V / VN : 0;
+  const f32x4* rv = reinterpret_cast<const f32x4*>(row);
+  int64_t i = threadIdx.x;
+  // four 16-byte loads in flight per thread
+  for (; i + 3 * 256 < nvec; i += 4 * 256) {
+    f32x4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[VN];
+      if constexpr (sizeof(T) == 2) {
+        const bf16x8 b = __builtin_bit_cast(bf16x8, raw[u]);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = (float)b[t] * kLog2e;
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = raw[u][t] * kLog2e;
+      }
+      float vm = v[0];
+#pragma unroll
+      for (int t = 1; t < VN; ++t) vm = fmaxf(vm, v[t]);
+      if (vm > m) {
+        s *= exp2f(m - vm);
+        m = vm;
+      }
+#pragma unroll
+      for (int t = 0; t < VN; ++t) s += exp2f(v[t] - m);
+    }
+  }
+  for (; i < nvec; i += 256) {
+    float v[VN];
+    ld16(row + i * VN, v);
+#pragma unroll
+    for (int t = 0; t < VN; ++t) online_add(m, s, v[t] * kLog2e);
+  }
+  for (int64_t j = nvec * VN + threadIdx.x; j < V; j += 256) online_add(m, s, to_f(row[j]) * kLog2e);
+  // wave reduction, then across the 4 waves
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float m2 = __shfl_xor(m, off, 64);
+    const float s2 = __shfl_xor(s, off, 64);
+    online_merge(m, s, m2, s2);
+  }
+  __shared__ float sm[4], ss[4];
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sm[wave] = m;
+    ss[wave] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float M = sm[0], Sx = ss[0];
+    for (int w = 1; w < 4; ++w) online_merge(M, Sx, sm[w], ss[w]);
+    lse[c] = (M + log2f(Sx)) * kLn2;
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) p[i] = 0;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, int64_t V, const int64_t* __restrict__ m,
+                                                     const int32_t* __restrict__ labels, int64_t S,
+                                                     const float* __restrict__ lse, float* __restrict__ logp,
+                                                     int32_t* __restrict__ q) {
+  for (int64_t s = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; s < S; s += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t c = m[s];
+    logp[s] = to_f(x[c * V + labels[s]]) - lse[c];
+    if (q) atomicAdd(q + c, 1);
+  }
+}
+
+hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
+                          int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s) {
+  if (C <= 0) return hipSuccess;
+  if (q) {
+    hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned((C + 255) / 256 < 4096 ? (C + 255) / 256 : 4096)), dim3(256), 0, s,
+                       q, C);
+  }
+  // rows are read with 16-byte vectors only when every row start is 16-byte aligned
+  const int vn = dtype == 0 ? 8 : 4;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && (V % vn == 0);
+  if (dtype == 0)
+    hipLaunchKernelGGL(row_lse_kernel<bf16>, dim3(unsigned(C)), dim3(256), 0, s, static_cast<const bf16*>(logits), V, lse,
+                       vec_ok);
+  else
+    hipLaunchKernelGGL(row_lse_kernel<float>, dim3(unsigned(C)), dim3(256), 0, s, static_cast<const float*>(logits), V,
+                       lse, vec_ok);
+  if (S > 0) {
+    const unsigned nb = unsigned((S + 255) / 256 < 8192 ? (S + 255) / 256 : 8192);
+    if (dtype == 0)
+      hipLaunchKernelGGL(gather_kernel<bf16>, dim3(nb), dim3(256), 0, s, static_cast<const bf16*>(logits), V, m, labels,
+                         S, lse, logp, q);
+    else
+      hipLaunchKernelGGL(gather_kernel<float>, dim3(nb), dim3(256), 0, s, static_cast<const float*>(logits), V, m,
+                         labels, S, lse, logp, q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace harts

@@ -1,0 +1,241 @@
+/*
+ * harts.h -- C ABI of the MI355X (gfx950) tree-packed chunkwise gated-delta
+ * path: rollout trajectories -> compact tokens -> minimum-call packed rounds
+ * -> per-round chunkwise gated-delta forward / backward with state handoffs
+ * -> per-position log-probabilities.
+ *
+ * Sources (HARTS, arXiv 2608.28158; cited by page and section):
+ *   [blog]   close-reading blog (inkeast.github.io), sections 3.2, 4.2, 4.3, 4.4
+ *   [plsum]  paperlayer.ai summary of v1, sections 3 and 4
+ *   [tla]    thelatestinai.com page: Figures 1, 2, C.1
+ *
+ * Conventions for every entry point
+ *   - Return value: HARTS_OK (0) or a negative HARTS_E* code; nothing is
+ *     thrown across the ABI.  harts_last_error() returns a thread-local
+ *     message describing the last failure of the calling thread.
+ *   - Host calls (tree, plan) are synchronous and thread-safe per handle.
+ *   - Device calls only enqueue work on the caller's HIP stream (hipStream_t
+ *     passed as void*, NULL = the null stream); they never synchronise.
+ *   - Device buffers are allocated by the caller and passed as raw device
+ *     pointers with their sizes; the library never frees them.  Opaque handles
+ *     are owned by the library and released by the matching *_free call.
+ *   - Dense tensors are row-major, token-major: q, k, g [N, H, dk]; v, o
+ *     [N, H, dv]; beta [N, H]; states [n, H, dk, dv] (float32).  N is the
+ *     number of compact rows C for tree plans, the total token count for
+ *     varlen plans.  q and k are used as given (no normalisation, no scale).
+ *   - NaN / Inf in inputs are not checked; they propagate.
+ */
+#ifndef HARTS_H
+#define HARTS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define HARTS_OK 0
+#define HARTS_EINVAL (-1)  /* bad shape, dtype, size or argument */
+#define HARTS_ERANGE (-2)  /* an index or offset outside its range */
+#define HARTS_ENOMEM (-3)  /* host or device allocation failed */
+#define HARTS_EHIP (-4)    /* a HIP runtime call failed */
+#define HARTS_ESTATE (-5)  /* handle in the wrong state for this call */
+
+#define HARTS_DTYPE_BF16 0
+#define HARTS_DTYPE_FP32 1
+
+typedef struct harts_tree harts_tree;
+typedef struct harts_plan harts_plan;
+typedef struct harts_dev_plan harts_dev_plan;
+
+/* ---------------------------------------------------------------- trajectories -> compact tokens
+ * [blog 3.2] semantic positions s = (x, i) and compact tokens C with the map
+ * m: S -> C; [plsum 3] trajectories are sorted lexicographically (stable) and
+ * merged into a compressed trie whose unique nodes are the compact tokens.
+ *
+ * tokens: host int32 [traj_offsets[n_traj]], trajectories concatenated.
+ * traj_offsets: host int64 [n_traj + 1], non-decreasing, traj_offsets[0] = 0.
+ * Trajectories may repeat, be prefixes of one another and come in any order;
+ * the semantic order S is the caller's order.  An empty trajectory, n_traj < 1
+ * or decreasing offsets give HARTS_EINVAL.
+ */
+int harts_tree_build(const int32_t *tokens, const int64_t *traj_offsets, int64_t n_traj, harts_tree **out);
+
+/* S (semantic positions), C (compact tokens), fork-free segments and forks. */
+int harts_tree_stats(const harts_tree *tree, int64_t *S, int64_t *C, int64_t *n_segments, int64_t *n_forks);
+
+void harts_tree_free(harts_tree *tree);
+
+/* ---------------------------------------------------------------- minimum-call round plan
+ * [blog 4.2] segment tree (segment = maximal fork-free token path); packed
+ * chunkwise calls with at most one direct continuation per fork; T_pre/T_in
+ * bottom-up recursion (leaves = 1, minimum calls = T_pre(root)), top-down
+ * recovery; a side branch restarts at a(p) = B*floor(p/B) and replays [a(p), p).
+ * [blog 4.3] compact layout: round-major, sequences contiguous, replay rows
+ * and requested boundary states addressable.  [tla Figure 2] three boundary
+ * cases.
+ *
+ * chunk_B must be 16, 32 or 64 (HARTS_EINVAL otherwise).
+ */
+int harts_plan_create(const harts_tree *tree, int32_t chunk_B, harts_plan **out);
+
+/*
+ * A plan for independent packed sequences (no tree, no replay): one round.
+ * cu_seqlens: host int64 [n_seq + 1] (lengths >= 1).  has_init: host uint8
+ * [n_seq] or NULL; sequence i starts from init_states[i] when has_init[i] != 0,
+ * from zero otherwise.  emit_boundaries != 0 requests the state after every
+ * multiple of chunk_B inside each sequence (in (0, L_i], sequence-major,
+ * chunk order); harts_plan_boundary_offsets() gives where each sequence's
+ * states start.
+ */
+int harts_plan_create_varlen(const int64_t *cu_seqlens, int64_t n_seq, int32_t chunk_B, const uint8_t *has_init,
+                             int32_t emit_boundaries, harts_plan **out);
+
+typedef struct {
+  int64_t S, C;           /* semantic positions, compact rows (= N) */
+  int32_t chunk_B;
+  int32_t n_rounds;       /* packed calls per layer pass = minimum calls for trees */
+  int32_t min_calls;      /* T_pre(root) (trees); 1 for varlen plans */
+  int32_t n_sequences;    /* = number of leaves for trees */
+  int32_t n_slots;        /* handed-off boundary states (trees) */
+  int32_t n_boundaries;   /* emitted boundary states (varlen plans) */
+  int64_t replay_total;   /* sum of replay lengths (= forced replay R) */
+  int64_t n_chunks;       /* chunks over all rounds */
+  int64_t n_vrows;        /* virtual rows (own + replay) over all rounds */
+} harts_plan_info_t;
+
+int harts_plan_info(const harts_plan *plan, harts_plan_info_t *out);
+
+/*
+ * Host copies of the maps [blog 3.2, 4.4]: m int64 [S] (semantic position ->
+ * compact row), q int32 [C] (multiplicity, sum = S), node_to_row int64 [C]
+ * (trie node in DFS preorder, children by token id -> compact row).  Any
+ * pointer may be NULL.  Varlen plans: m and node_to_row are the identity.
+ */
+int harts_plan_maps(const harts_plan *plan, int64_t *m, int32_t *q, int64_t *node_to_row);
+
+/* One packed sequence of the plan (host view). */
+typedef struct {
+  int32_t round;       /* 1-based round (packed call) */
+  int32_t init_slot;   /* slot of the initial state, -1 = zero state (varlen: index into init states) */
+  int64_t start;       /* absolute position of the virtual stream's first token = a(s_head) */
+  int64_t row_begin;   /* own compact rows [row_begin, row_end) */
+  int64_t row_end;
+  int64_t replay_off;  /* replay rows [replay_off, replay_off + n_replay) of harts_plan_replay_rows() */
+  int32_t n_replay;    /* < chunk_B */
+  int32_t n_emits;     /* emitted states [emit_off, emit_off + n_emits) of harts_plan_emits() */
+  int64_t emit_off;
+} harts_seq_view;
+
+/* seqs: host [n_sequences], ordered by round, then head segment DFS preorder. */
+int harts_plan_sequences(const harts_plan *plan, harts_seq_view *seqs);
+/* rows: host int64 [replay_total]: compact rows replayed, per sequence in path order. */
+int harts_plan_replay_rows(const harts_plan *plan, int64_t *rows);
+/* Emitted states: boundary index (local chunk boundary, >= 1) and target
+ * (slot id for trees, boundary-state index for varlen plans); host int32 [total emits]. */
+int harts_plan_emits(const harts_plan *plan, int32_t *boundary, int32_t *target);
+/* Varlen plans with emit_boundaries: host int64 [n_seq + 1]. */
+int harts_plan_boundary_offsets(const harts_plan *plan, int64_t *offsets);
+
+void harts_plan_free(harts_plan *plan);
+
+/* ---------------------------------------------------------------- device plan
+ * Uploads the per-round descriptors (virtual-row gather lists, chunk and
+ * sequence tables, emit targets) for heads H and key / value width dk, dv on
+ * the given stream, and records the workspace size the device calls need.
+ * dk, dv in {16, 32, 64, 128}; dtype HARTS_DTYPE_BF16 (dk = dv = 128 or 64) or
+ * HARTS_DTYPE_FP32 (dk = dv <= 64).  The descriptor memory belongs to the
+ * handle (hipMalloc here, hipFree in harts_dev_plan_free).
+ */
+int harts_plan_upload(const harts_plan *plan, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *stream,
+                      harts_dev_plan **out);
+
+/* Bytes of caller-provided device workspace for harts_kda_fwd (backward = 0)
+ * or harts_kda_bwd (backward = 1). */
+int harts_kda_workspace_size(const harts_dev_plan *dplan, int32_t backward, size_t *bytes);
+
+void harts_dev_plan_free(harts_dev_plan *dplan);
+
+/* ---------------------------------------------------------------- gated-delta forward
+ * [blog 1.2, 4.3] one packed varlen chunkwise call per round: the root starts
+ * from the zero state, other sequences from boundary states returned by
+ * earlier rounds; replay (< B ancestor tokens) updates only the state and
+ * writes no outputs; requested boundary states {S[c]} are materialised
+ * (equation 16, cited not printed).  Per token (equation 1, cited not printed;
+ * KDA-style gated delta rule, per head):
+ *     S'_t = diag(exp(g_t)) S_{t-1};  S_t = S'_t - beta_t k_t (k_t^T S'_t - v_t^T);  o_t = S_t^T q_t
+ *
+ * q, k, g, v, beta, o: device, dtype of the device plan (beta [N, H]).
+ * states: device float32 [n_slots, H, dk, dv] for tree plans (written for
+ *   every produced slot, read for every consumed one); for varlen plans the
+ *   emitted boundary states [n_boundaries, H, dk, dv] (NULL if not requested).
+ * init_states: varlen plans only, device float32 [n_seq, H, dk, dv] read for
+ *   sequences with has_init != 0 (NULL when none).
+ * final_states: varlen plans only, device float32 [n_seq, H, dk, dv] or NULL.
+ * workspace: device, >= harts_kda_workspace_size(dplan, 0, ...) bytes.
+ */
+typedef struct {
+  const void *q, *k, *v, *g, *beta;
+  void *o;
+  float *states;
+  const float *init_states;
+  float *final_states;
+  void *workspace;
+  size_t workspace_bytes;
+} harts_kda_io;
+
+int harts_kda_fwd(const harts_dev_plan *dplan, const harts_kda_io *io, void *stream);
+
+/* ---------------------------------------------------------------- gated-delta backward
+ * [blog 4.3] differentiable handoff: initial-state gradients accumulate back
+ * into the call that produced the boundary; [plsum 4] recomputation under the
+ * fixed plan (same layout, rounds, replay and state links; activations are
+ * recomputed per round, not kept).  Rounds run in reverse order.
+ *
+ * Loss L = sum_rows <dO, o>.  Outputs (device, plan dtype unless noted):
+ *   dq, dk, dg [N, H, dk]; dv [N, H, dv]; dbeta [N, H]: gradients of the compact
+ *   rows, summed over every use (own row and every replay of it);
+ *   dstates (float32 [n_slots, H, dk, dv], tree plans, may be NULL): for every
+ *   slot, the sum over its consumer sequences of dL/d(initial state);
+ *   dinit (float32 [n_seq, H, dk, dv], varlen plans, may be NULL): dL/d(init state).
+ * io->states must hold the slots written by harts_kda_fwd on the same inputs
+ * (tree plans), io->init_states the same initial states (varlen plans).
+ * workspace: >= harts_kda_workspace_size(dplan, 1, ...) bytes.
+ */
+typedef struct {
+  const void *dO;
+  void *dq, *dk, *dv, *dg, *dbeta;
+  float *dstates;
+  float *dinit;
+} harts_kda_grad;
+
+int harts_kda_bwd(const harts_dev_plan *dplan, const harts_kda_io *io, const harts_kda_grad *grad, void *stream);
+
+/* ---------------------------------------------------------------- compact -> semantic log-probs
+ * [blog 4.4; plsum 3] max and sum-exp computed once per compact logit row,
+ * then each semantic position reads its target logit in the original order:
+ *     logp[s] = logits[m[s], labels[s]] - logsumexp(logits[m[s], :])
+ * and the multiplicity q[c] = #{s : m[s] = c}.
+ *
+ * logits: device [C, V] (dtype bf16 or fp32), rows contiguous.
+ * m: device int64 [S] in [0, C); labels: device int32 [S] in [0, V).
+ * logp_out: device float32 [S]; q_out: device int32 [C] (may be NULL);
+ * lse_out: device float32 [C] (may be NULL).
+ * workspace: device, >= harts_logprob_workspace_size(C) bytes.
+ * Out-of-range m or labels are not checked on the device (caller contract).
+ */
+size_t harts_logprob_workspace_size(int64_t C);
+int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype, const int64_t *m,
+                         const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, float *lse_out,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* ---------------------------------------------------------------- misc */
+const char *harts_last_error(void);
+/* Library version string. */
+const char *harts_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* HARTS_H */

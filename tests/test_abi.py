@@ -1,0 +1,53 @@
+"""The C ABI library loads, exports every symbol include/harts.h declares, and
+turns bad host-side inputs into error codes (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import chunkwise_linear_attention_gated_amd as harts
+from chunkwise_linear_attention_gated_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "harts.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(harts_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_lib.library)
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version():
+    assert "gfx950" in harts.version()
+
+
+def test_error_codes():
+    with pytest.raises(harts.HartsError) as e:
+        harts.TreePlan(np.array([1, 2, 3], np.int32), np.array([0, 3, 3], np.int64), 64)
+    assert e.value.code == -1 and "empty trajectory" in str(e.value)
+    with pytest.raises(harts.HartsError) as e:
+        harts.TreePlan(np.array([1, 2, 3], np.int32), np.array([0, 3], np.int64), 48)
+    assert e.value.code == -1 and "chunk_B" in str(e.value)
+    with pytest.raises(harts.HartsError):
+        harts.VarlenPlan(np.array([0, 5, 4], np.int64), 64)
+    with pytest.raises(harts.HartsError):
+        harts.VarlenPlan(np.array([1, 5], np.int64), 64)
+
+
+def test_unsupported_shapes_rejected_before_any_device_work():
+    p = harts.TreePlan(np.array([1, 2, 3], np.int32), np.array([0, 3], np.int64), 64)
+    with pytest.raises(harts.HartsError) as e:
+        harts.DevicePlan(p, 2, 48, 48, harts.DTYPE_BF16, stream=0)
+    assert "unsupported" in str(e.value)
+    with pytest.raises(harts.HartsError):
+        harts.DevicePlan(p, 0, 128, 128, harts.DTYPE_BF16, stream=0)
