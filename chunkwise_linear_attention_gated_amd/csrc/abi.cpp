@@ -33,7 +33,7 @@ struct harts_dev_plan {
   int32_t* fix_idx = nullptr;
   // workspace layout (byte offsets)
   size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0,
-         off_dinit = 0, off_rg = 0;
+         off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
 
@@ -92,6 +92,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.chunks = d->chunks + rr.chunk0;
   a.nseq = rr.seq1 - rr.seq0;
   a.nchunk = rr.chunk1 - rr.chunk0;
+  a.seq0 = rr.seq0;
   a.q = io->q;
   a.k = io->k;
   a.v = io->v;
@@ -113,6 +114,13 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.Mm = ws + d->off_Mm;
   a.ws.El = reinterpret_cast<float*>(ws + d->off_El);
   a.ws.QeffT = ws + d->off_Qe;
+  a.ws.Tm = ws + d->off_Tm;
+  a.ws.Xm = ws + d->off_Xm;
+  a.ws.Am = ws + d->off_Am;
+  a.ws.U = ws + d->off_U;
+  a.ws.dR = ws + d->off_dR;
+  a.ws.dM = ws + d->off_dM;
+  a.ws.dA = ws + d->off_dA;
   a.h = ws + d->off_h;
   return a;
 }
@@ -299,6 +307,13 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_dh = take(MC * dv * dk * es);
       d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
       d->off_rg = take(size_t(d->p.replay_total) * H * (2 * dk + dv + 1) * 4);
+      d->off_Tm = take(MC * BT * BT * es);
+      d->off_Xm = take(MC * BT * BT * es);
+      d->off_Am = take(MC * BT * BT * es);
+      d->off_U = take(MC * BT * dv * es);
+      d->off_dR = take(MC * BT * dv * es);
+      d->off_dM = take(MC * BT * BT * es);
+      d->off_dA = take(MC * BT * BT * es);
       d->ws_bwd = off;
       if (d->ws_fwd == 0) d->ws_fwd = 256;
     } catch (...) {

@@ -1,15 +1,861 @@
-// Chunkwise gated-delta backward on gfx950 (state-gradient pass, per-chunk
-// gradients, replay-gradient fixup).
+// Chunkwise gated-delta backward on gfx950, one packed round at a time, rounds
+// in reverse (HARTS close-reading blog, section 4.3: differentiable state
+// handoff -- initial-state gradients flow back into the call that produced the
+// boundary; paperlayer summary, section 4: recomputation under the fixed plan).
+//
+// Per chunk with start state S0, end-state gradient dS (both known after the
+// serial passes), L = <dO, O> + <dS, S_end>:
+//   dU = M^T dO + K^ dS,  dR = T^T dU  (dV = dR),  dT = dU R^T,  R = V - K~ S0,
+//   dX = dT diag(beta),  dL = -X^T dX X^T,  dA = strict_lower(diag(beta) dL),
+//   dbeta_j = sum_i X_ij dT_ij + sum_k dL_jk A_jk,   dM = lower(dO U^T),
+//   dS_start = diag(e^{G_last}) dS + Qeff^T dO - W^T (K^ dS),  Qeff = Q~ - M W,
+// and the q, k, g gradients through the gated token products (e^{G_i - G_j}
+// factored at 16-row sub-block references, as in the forward):
+//   dq = e^L (rowgated(dM, K) + e^{F_b} dO S0^T)
+//   dk = e^L (rowgated(dA, K) - e^{F_b} dR S0^T) + colgated(dM, Q) + colgated(dA, K) + K^-factor (U dS^T)
+//   dG = q dq + k (row-side terms) - k (column-side terms);  dG_last += sum_i k^ (U dS^T) + e^{G_last} rowsum(dS S0)
+//   dg = reverse cumulative sum of dG over the chunk.
 #include "common.h"
 #include "launch.h"
 
 namespace harts {
 
-hipError_t launch_kda_dstate(const KdaDims&, const BwdRoundArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_kda_grad(const KdaDims&, const BwdRoundArgs&, hipStream_t) { return hipErrorNotSupported; }
-hipError_t launch_replay_fixup(const KdaDims&, const int32_t*, const int32_t*, const int32_t*, int32_t, const float*,
-                               void*, void*, void*, void*, hipStream_t) {
-  return hipErrorNotSupported;
+template <int D> constexpr int dv_tile_b() { return D >= 64 ? 32 : 16; }
+
+// Replay-gradient side buffer: per (replay position, head) dk[D], dv[DV], dg[D], dbeta.
+template <int D, int DV> struct RG {
+  static constexpr int W = 2 * D + DV + 1, DK = 0, DVO = D, DG = D + DV, DB = 2 * D + DV;
+};
+
+// ------------------------------------------------------------------------------------------
+// Serial state-gradient pass, reverse over chunks.  One workgroup per (sequence, head,
+// value-column tile).  dS (fp32) lives in accumulator registers.
+template <typename T, int BT, int D, int DV, int DVT>
+__global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) {
+  using MM = Mma<T>;
+  const RoundArgs& a = b.r;
+  constexpr int NTL = DV / DVT, PAD = 16 / sizeof(T), VN = 16 / sizeof(T);
+  constexpr int LDS_S = D + PAD, LDK = D + PAD, LDJ = BT + PAD, LDO = DVT + PAD;
+  constexpr int MT = D / 16, NTV = DVT / 16, MU = (MT + 3) / 4;
+  __shared__ __attribute__((aligned(16))) T dSt[DVT * LDS_S];
+  __shared__ __attribute__((aligned(16))) T Wl[BT * LDK];
+  __shared__ __attribute__((aligned(16))) T Kl[D * LDJ];
+  __shared__ __attribute__((aligned(16))) T Yt[DVT * LDJ];
+  __shared__ __attribute__((aligned(16))) T dOl[BT * LDO];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lb = xcd_logical(blockIdx.x, gridDim.x);
+  const int tile = lb % NTL, h = (lb / NTL) % H, si = lb / (NTL * H);
+  if (si >= a.nseq) return;
+  const SeqDesc sd = a.seqs[si];
+  const int jvb = tile * DVT;
+  const T* gdo = static_cast<const T*>(b.dO);
+  f32x4 dS[MU][NTV];
+#pragma unroll
+  for (int u = 0; u < MU; ++u)
+#pragma unroll
+    for (int nt = 0; nt < NTV; ++nt) dS[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = sd.n_chunks - 1; n >= 0; --n) {
+    const ChunkDesc cd = a.chunks[sd.chunk_base + n];
+    const size_t wsi = size_t(cd.local) * H + h;
+    __syncthreads();
+    // slot gradient: sum over the consumers of the state emitted after this chunk
+    if (cd.emit >= 0 && b.slot_cons_off) {
+      const int q0 = b.slot_cons_off[cd.emit], q1 = b.slot_cons_off[cd.emit + 1];
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int mt = wave + 4 * u;
+        if (mt < MT)
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int c = 16 * mt + crow(lane, r), jv = jvb + 16 * nt + ccol(lane);
+              float add = 0.f;
+              for (int qq = q0; qq < q1; ++qq)
+                add += b.dinit[((size_t(b.slot_cons[qq]) * H + h) * D + c) * DV + jv];
+              dS[u][nt][r] += add;
+              if (b.dstates) b.dstates[((size_t(cd.emit) * H + h) * D + c) * DV + jv] = add;
+            }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int mt = wave + 4 * u;
+      if (mt < MT)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+          store4(dSt + (16 * nt + ccol(lane)) * LDS_S + 16 * mt + crow(lane, 0), dS[u][nt][0], dS[u][nt][1],
+                 dS[u][nt][2], dS[u][nt][3]);
+    }
+    {
+      const T* wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
+      const T* kg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
+      for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+        const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
+        copy16(Wl + i * LDK + c0, wg + i * D + c0);
+      }
+      for (int idx = tid; idx < D * (BT / VN); idx += 256) {
+        const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
+        copy16(Kl + c * LDJ + i0, kg + c * BT + i0);
+      }
+      for (int idx = tid; idx < BT * (DVT / VN); idx += 256) {
+        const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
+        if (i < cd.len && i >= cd.own_from)
+          copy16(dOl + i * LDO + j0, gdo + (size_t(a.vrows[cd.vbase + i]) * H + h) * DV + jvb + j0);
+        else
+          *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    __syncthreads();
+    {
+      // gradient w.r.t. the chunk-end state, for the per-chunk gradient kernels
+      T* dhg = static_cast<T*>(b.dh) + wsi * DV * D;
+      for (int idx = tid; idx < DVT * (D / VN); idx += 256) {
+        const int jl = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
+        copy16(dhg + (jvb + jl) * D + c0, dSt + jl * LDS_S + c0);
+      }
+    }
+    // Y = K^ dS  (stored transposed)
+    for (int mi = wave; mi < BT / 16; mi += 4) {
+      f32x4 acc[NTV];
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < D; k0 += MM::KS) {
+        const auto af = MM::rc(Kl, LDJ, 16 * mi, k0, lane);
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt) acc[nt] = MM::mma(af, MM::kc(dSt, LDS_S, 16 * nt, k0, lane), acc[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt)
+        store4(Yt + (16 * nt + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[nt][0], acc[nt][1], acc[nt][2],
+               acc[nt][3]);
+    }
+    __syncthreads();
+    // dS <- diag(e^{G_last}) dS + Qeff^T dO - W^T Y
+    {
+      const T* qe = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
+      const float* el = a.ws.El + wsi * D;
+#pragma unroll
+      for (int u = 0; u < MU; ++u) {
+        const int mt = wave + 4 * u;
+        if (mt < MT) {
+          f32x4 a1[NTV], a2[NTV];
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt) a1[nt] = a2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int k0 = 0; k0 < BT; k0 += MM::KS) {
+            const auto f1 = MM::kc(qe, BT, 16 * mt, k0, lane);
+            const auto f2 = MM::rc(Wl, LDK, 16 * mt, k0, lane);
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) {
+              a1[nt] = MM::mma(f1, MM::rc(dOl, LDO, 16 * nt, k0, lane), a1[nt]);
+              a2[nt] = MM::mma(f2, MM::kc(Yt, LDJ, 16 * nt, k0, lane), a2[nt]);
+            }
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = el[16 * mt + crow(lane, r)];
+#pragma unroll
+            for (int nt = 0; nt < NTV; ++nt) dS[u][nt][r] = e * dS[u][nt][r] + a1[nt][r] - a2[nt][r];
+          }
+        }
+      }
+    }
+  }
+  if (b.dinit) {
+    const size_t gs = size_t(a.seq0 + si);
+#pragma unroll
+    for (int u = 0; u < MU; ++u) {
+      const int mt = wave + 4 * u;
+      if (mt < MT)
+#pragma unroll
+        for (int nt = 0; nt < NTV; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int c = 16 * mt + crow(lane, r), jv = jvb + 16 * nt + ccol(lane);
+            b.dinit[((gs * H + h) * D + c) * DV + jv] = dS[u][nt][r];
+          }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// In-chunk cumulative log-decay, block by block (16 rows): Gf = L (block-local cumulative
+// sums), Tv = block totals, Fv = entry log-decays, EF = e^{F}, EH = e^{F_end - F_{b+1}}.
+template <typename T, int BT, int D>
+__device__ void chunk_decay(const T* gg, const int32_t* vr, int len, int H, int h, float* Gf, float* Tv, float* Fv,
+                            float* EF, float* EH, int tid) {
+  constexpr int NB = BT / 16, VN = 16 / sizeof(T), LDF = D + 4;
+  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
+    float v[VN];
+    if (i < len) ld16(gg + (size_t(vr[i]) * H + h) * D + c0, v);
+    else
+#pragma unroll
+      for (int t = 0; t < VN; ++t) v[t] = 0.f;
+#pragma unroll
+    for (int t = 0; t < VN; ++t) Gf[i * LDF + c0 + t] = v[t];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < NB * D; idx += 256) {
+    const int bb = idx / D, c = idx % D;
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      acc += Gf[(16 * bb + t) * LDF + c];
+      Gf[(16 * bb + t) * LDF + c] = acc;
+    }
+    Tv[bb * D + c] = acc;
+  }
+  __syncthreads();
+  for (int c = tid; c < D; c += 256) {
+    float f = 0.f;
+    Fv[c] = 0.f;
+    EF[c] = 1.f;
+    for (int bb = 0; bb < NB; ++bb) {
+      f += Tv[bb * D + c];
+      Fv[(bb + 1) * D + c] = f;
+      EF[(bb + 1) * D + c] = __expf(f);
+    }
+    for (int bb = 0; bb < NB; ++bb) EH[bb * D + c] = __expf(f - Fv[(bb + 1) * D + c]);
+  }
+  __syncthreads();
+}
+
+constexpr size_t al16(size_t x) { return (x + 15) / 16 * 16; }
+constexpr size_t cmx(size_t a, size_t b) { return a > b ? a : b; }
+
+// ------------------------------------------------------------------------------------------
+// Gradient kernel A (token-token side).  One workgroup per (chunk, head).  Produces dv and
+// dbeta, and the intermediates U, dR (value side) and dM, dA (token side) for kernel B.
+template <typename T, int BT, int D, int DV>
+struct GALayout {
+  static constexpr int NB = BT / 16, PAD = 16 / sizeof(T);
+  static constexpr int LDK = D + PAD, LDJ = BT + PAD, LDV = DV + PAD, LDF = D + 4, LDA = BT + 4;
+  static constexpr size_t sJ = size_t(BT) * LDJ * sizeof(T);
+  static constexpr size_t sRt = size_t(DV) * LDJ * sizeof(T);
+  static constexpr size_t R1 = al16(cmx(size_t(BT) * LDF * 4, cmx(2 * sRt, 2 * size_t(BT) * LDA * 4)));
+  static constexpr size_t RA = al16(cmx(size_t(BT) * LDK * sizeof(T), cmx(size_t(BT) * LDV * sizeof(T), size_t(BT) * LDA * 4)));
+  static constexpr size_t RB = al16(cmx(size_t(BT) * LDK * sizeof(T), cmx(size_t(BT) * LDV * sizeof(T), sJ)));
+  static constexpr size_t RT = al16(sJ), RM = al16(sJ);
+  static constexpr size_t RO = al16(cmx(size_t(BT) * LDV * sizeof(T), sJ));
+  static constexpr size_t O_R1 = 0, O_RA = O_R1 + R1, O_RB = O_RA + RA, O_RT = O_RB + RB, O_RM = O_RT + RT,
+                          O_RO = O_RM + RM, O_VEC = O_RO + RO;
+  static constexpr size_t VTV = 0, VFV = VTV + NB * D, VEF = VFV + (NB + 1) * D, VEH = VEF + (NB + 1) * D,
+                          VBET = VEH + NB * D, VDB = VBET + BT, VEND = VDB + BT;
+  static constexpr size_t TOTAL = O_VEC + VEND * 4;
+  static_assert(TOTAL <= 160 * 1024, "gradient kernel A LDS budget");
+};
+
+template <typename T, int BT, int D, int DV>
+__global__ __launch_bounds__(256) void kda_gradA_kernel(BwdRoundArgs b, int H) {
+  using Ly = GALayout<T, BT, D, DV>;
+  using MM = Mma<T>;
+  using G = RG<D, DV>;
+  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDJ = Ly::LDJ, LDV = Ly::LDV, LDF = Ly::LDF, LDA = Ly::LDA;
+  constexpr int VN = 16 / sizeof(T);
+  __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
+  const RoundArgs& a = b.r;
+  float* Gf = reinterpret_cast<float*>(smem + Ly::O_R1);
+  T* Rt = reinterpret_cast<T*>(smem + Ly::O_R1);                    // [DV][LDJ]  R^T
+  T* dUt = reinterpret_cast<T*>(smem + Ly::O_R1 + Ly::sRt);         // [DV][LDJ]  dU^T
+  float* dLf = reinterpret_cast<float*>(smem + Ly::O_R1);           // [BT][LDA]
+  T* Kt = reinterpret_cast<T*>(smem + Ly::O_RA);                    // [BT][LDK]  K~
+  T* Ul = reinterpret_cast<T*>(smem + Ly::O_RA);                    // [BT][LDV]  U
+  float* dTf = reinterpret_cast<float*>(smem + Ly::O_RA);           // [BT][LDA]
+  T* Kh = reinterpret_cast<T*>(smem + Ly::O_RB);                    // [BT][LDK]  K^
+  T* dRl = reinterpret_cast<T*>(smem + Ly::O_RB);                   // [BT][LDV]  dR
+  T* Y1t = reinterpret_cast<T*>(smem + Ly::O_RB);                   // [BT][LDJ]
+  T* Tl = reinterpret_cast<T*>(smem + Ly::O_RT);                    // [BT][LDJ]  T, then A
+  T* Al = Tl;
+  T* Ml = reinterpret_cast<T*>(smem + Ly::O_RM);                    // [BT][LDJ]  M, then X
+  T* Xl = Ml;
+  T* dOl = reinterpret_cast<T*>(smem + Ly::O_RO);                   // [BT][LDV]  dO, then dX
+  T* dXl = dOl;
+  float* vec = reinterpret_cast<float*>(smem + Ly::O_VEC);
+  float *Tv = vec + Ly::VTV, *Fv = vec + Ly::VFV, *EF = vec + Ly::VEF, *EH = vec + Ly::VEH;
+  float *bet = vec + Ly::VBET, *db1 = vec + Ly::VDB;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+  const ChunkDesc cd = a.chunks[chunk];
+  const int len = cd.len, own = cd.own_from;
+  const size_t wsi = size_t(cd.local) * H + h;
+  const int32_t* vr = a.vrows + cd.vbase;
+  const T* gk = static_cast<const T*>(a.k);
+  const T* gv = static_cast<const T*>(a.v);
+  const T* gb = static_cast<const T*>(a.beta);
+  const T* gdo = static_cast<const T*>(b.dO);
+  const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+  const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
+  const size_t BB = size_t(BT) * BT;
+
+  if (tid < BT) bet[tid] = tid < len ? to_f(gb[size_t(vr[tid]) * H + h]) : 0.f;
+  chunk_decay<T, BT, D>(static_cast<const T*>(a.g), vr, len, H, h, Gf, Tv, Fv, EF, EH, tid);
+  // K~ = k e^{G}, K^ = k e^{G_last - G}; T and M from the prep pass; dO (zero on replayed rows)
+  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, bb = i / 16;
+    float kk[VN], kt[VN], kh[VN];
+    if (i < len) ld16(gk + (size_t(vr[i]) * H + h) * D + c0, kk);
+    else
+#pragma unroll
+      for (int t = 0; t < VN; ++t) kk[t] = 0.f;
+#pragma unroll
+    for (int t = 0; t < VN; ++t) {
+      const float L = Gf[i * LDF + c0 + t];
+      kt[t] = kk[t] * __expf(L) * EF[bb * D + c0 + t];
+      kh[t] = kk[t] * __expf(Tv[bb * D + c0 + t] - L) * EH[bb * D + c0 + t];
+    }
+    st16(Kt + i * LDK + c0, kt);
+    st16(Kh + i * LDK + c0, kh);
+  }
+  {
+    const T* tg = static_cast<const T*>(a.ws.Tm) + wsi * BB;
+    const T* mg = static_cast<const T*>(a.ws.Mm) + wsi * BB;
+    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
+      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
+      copy16(Tl + i * LDJ + j0, tg + i * BT + j0);
+      copy16(Ml + i * LDJ + j0, mg + i * BT + j0);
+    }
+    for (int idx = tid; idx < BT * (DV / VN); idx += 256) {
+      const int i = idx / (DV / VN), j0 = (idx % (DV / VN)) * VN;
+      if (i < len && i >= own) copy16(dOl + i * LDV + j0, gdo + (size_t(vr[i]) * H + h) * DV + j0);
+      else *reinterpret_cast<f32x4*>(dOl + i * LDV + j0) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  __syncthreads();
+  // R = V - K~ S0, stored transposed
+  {
+    constexpr int MT = BT / 16, NT = DV / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mi = jb / NT, nj = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < D; k0 += MM::KS)
+        acc = MM::mma(MM::kc(Kt, LDK, 16 * mi, k0, lane), MM::kc(hg, D, 16 * nj, k0, lane), acc);
+      const int jv = 16 * nj + ccol(lane), i0 = 16 * mi + crow(lane, 0);
+      float rv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        rv[r] = (i < len ? to_f(gv[(size_t(vr[i]) * H + h) * DV + jv]) : 0.f) - acc[r];
+      }
+      store4(Rt + jv * LDJ + i0, rv[0], rv[1], rv[2], rv[3]);
+    }
+  }
+  __syncthreads();
+  // U^T = R^T T^T  ->  U [i][jv] (LDS and workspace)
+  {
+    T* ug = static_cast<T*>(a.ws.U) + wsi * BT * DV;
+    constexpr int MT = DV / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mv = jb / NT, ni = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::kc(Rt, LDJ, 16 * mv, k0, lane), MM::kc(Tl, LDJ, 16 * ni, k0, lane), acc);
+      const int i = 16 * ni + ccol(lane), jv0 = 16 * mv + crow(lane, 0);
+      store4(Ul + i * LDV + jv0, acc[0], acc[1], acc[2], acc[3]);
+      store4(ug + i * DV + jv0, acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+  // dU = M^T dO + K^ dS_end, stored transposed
+  {
+    constexpr int MT = BT / 16, NT = DV / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mi = jb / NT, nj = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::rc(Ml, LDJ, 16 * mi, k0, lane), MM::rc(dOl, LDV, 16 * nj, k0, lane), acc);
+      for (int k0 = 0; k0 < D; k0 += MM::KS)
+        acc = MM::mma(MM::kc(Kh, LDK, 16 * mi, k0, lane), MM::kc(dhg, D, 16 * nj, k0, lane), acc);
+      store4(dUt + (16 * nj + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+  __syncthreads();
+  // dM = lower(dO U^T), computed transposed so it stores row-major
+  {
+    T* dmg = static_cast<T*>(a.ws.dM) + wsi * BB;
+    constexpr int MT = BT / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mj = jb / NT, ni = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < DV; k0 += MM::KS)
+        acc = MM::mma(MM::kc(Ul, LDV, 16 * mj, k0, lane), MM::kc(dOl, LDV, 16 * ni, k0, lane), acc);
+      const int i = 16 * ni + ccol(lane), j0 = 16 * mj + crow(lane, 0);
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = j0 + r <= i ? acc[r] : 0.f;
+      store4(dmg + i * BT + j0, v[0], v[1], v[2], v[3]);
+    }
+  }
+  // dR^T = dU^T T  ->  dR [j][jv] (LDS and workspace)
+  {
+    T* drg = static_cast<T*>(a.ws.dR) + wsi * BT * DV;
+    constexpr int MT = DV / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mv = jb / NT, nj = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::kc(dUt, LDJ, 16 * mv, k0, lane), MM::rc(Tl, LDJ, 16 * nj, k0, lane), acc);
+      const int j = 16 * nj + ccol(lane), jv0 = 16 * mv + crow(lane, 0);
+      store4(dRl + j * LDV + jv0, acc[0], acc[1], acc[2], acc[3]);
+      store4(drg + j * DV + jv0, acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+  __syncthreads();  // dM and dR done reading U and T: dT reuses the U region
+  // dT = dU R^T (fp32)
+  {
+    constexpr int MT = BT / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mi = jb / NT, nj = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < DV; k0 += MM::KS)
+        acc = MM::mma(MM::rc(dUt, LDJ, 16 * mi, k0, lane), MM::rc(Rt, LDJ, 16 * nj, k0, lane), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dTf[(16 * mi + crow(lane, r)) * LDA + 16 * nj + ccol(lane)] = acc[r];
+    }
+  }
+  __syncthreads();
+  // dv: own rows to the output, replayed rows to the side buffer
+  {
+    T* gdv = static_cast<T*>(b.dv);
+    for (int idx = tid; idx < BT * (DV / VN); idx += 256) {
+      const int i = idx / (DV / VN), j0 = (idx % (DV / VN)) * VN;
+      if (i >= len) continue;
+      if (i >= own) {
+        copy16(gdv + (size_t(vr[i]) * H + h) * DV + j0, dRl + i * LDV + j0);
+      } else {
+        float* rg = b.replay_grad + (size_t(cd.replay_base + i) * H + h) * G::W + G::DVO + j0;
+#pragma unroll
+        for (int t = 0; t < VN; ++t) rg[t] = to_f(dRl[i * LDV + j0 + t]);
+      }
+    }
+  }
+  // X and A from the prep pass (T, M no longer needed); dbeta_1 = colsum(X .* dT); dX = dT diag(beta)
+  {
+    const T* xg = static_cast<const T*>(a.ws.Xm) + wsi * BB;
+    const T* ag = static_cast<const T*>(a.ws.Am) + wsi * BB;
+    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
+      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
+      copy16(Xl + i * LDJ + j0, xg + i * BT + j0);
+      copy16(Al + i * LDJ + j0, ag + i * BT + j0);
+    }
+  }
+  __syncthreads();
+  for (int j = tid; j < BT; j += 256) {
+    float s = 0.f;
+    for (int i = j; i < BT; ++i) s += to_f(Xl[i * LDJ + j]) * dTf[i * LDA + j];
+    db1[j] = s;
+  }
+  for (int idx = tid; idx < BT * BT; idx += 256) {
+    const int i = idx / BT, j = idx % BT;
+    dXl[i * LDJ + j] = from_f<T>(j <= i ? dTf[i * LDA + j] * bet[j] : 0.f);
+  }
+  __syncthreads();
+  // Y1 = dX X^T, stored transposed (rows of Y1^T in the dR region)
+  {
+    constexpr int MT = BT / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mi = jb / NT, nk = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::kc(dXl, LDJ, 16 * mi, k0, lane), MM::kc(Xl, LDJ, 16 * nk, k0, lane), acc);
+      store4(Y1t + (16 * nk + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
+    }
+  }
+  __syncthreads();
+  // dL = -X^T Y1 (fp32)
+  {
+    constexpr int MT = BT / 16, NT = BT / 16;
+    for (int jb = wave; jb < MT * NT; jb += 4) {
+      const int mi = jb / NT, nk = jb % NT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::rc(Xl, LDJ, 16 * mi, k0, lane), MM::kc(Y1t, LDJ, 16 * nk, k0, lane), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) dLf[(16 * mi + crow(lane, r)) * LDA + 16 * nk + ccol(lane)] = -acc[r];
+    }
+  }
+  __syncthreads();
+  // dA = strict_lower(diag(beta) dL); dbeta = dbeta_1 + rowsum(dL .* A)
+  {
+    T* dag = static_cast<T*>(a.ws.dA) + wsi * BB;
+    for (int idx = tid; idx < BT * BT; idx += 256) {
+      const int i = idx / BT, j = idx % BT;
+      dag[idx] = from_f<T>(j < i ? bet[i] * dLf[i * LDA + j] : 0.f);
+    }
+    T* gdb = static_cast<T*>(b.dbeta);
+    for (int i = tid; i < len; i += 256) {
+      float s = db1[i];
+      for (int j = 0; j < i; ++j) s += dLf[i * LDA + j] * to_f(Al[i * LDJ + j]);
+      if (i >= own) gdb[size_t(vr[i]) * H + h] = from_f<T>(s);
+      else b.replay_grad[(size_t(cd.replay_base + i) * H + h) * G::W + G::DB] = s;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Gradient kernel B (channel side): dq, dk, dg.  One workgroup per (chunk, head); wave w owns
+// token rows [16w, 16w + 16) and accumulates every contribution in registers.
+template <typename T, int BT, int D>
+struct GBLayout {
+  static constexpr int NB = BT / 16, PAD = 16 / sizeof(T);
+  static constexpr int LDK = D + PAD, LDJ = BT + PAD, LDF = D + 4;
+  static constexpr size_t sK = size_t(BT) * LDK * sizeof(T);
+  static constexpr size_t O_GF = 0, O_ARR = al16(size_t(BT) * LDF * 4);
+  static constexpr size_t ARR = al16(cmx(4 * sK, size_t(BT) * LDF * 4));  // Kr, Qr, Kc0, Kcd | staging
+  static constexpr size_t O_DM = O_ARR + ARR, O_DA = O_DM + al16(size_t(BT) * LDJ * sizeof(T));
+  static constexpr size_t O_VEC = O_DA + al16(size_t(BT) * LDJ * sizeof(T));
+  static constexpr size_t VTV = 0, VFV = VTV + NB * D, VEF = VFV + (NB + 1) * D, VEH = VEF + (NB + 1) * D,
+                          VRS = VEH + NB * D, VCS = VRS + D, VEND = VCS + 4 * D;
+  static constexpr size_t TOTAL = O_VEC + VEND * 4;
+  static_assert(TOTAL <= 160 * 1024, "gradient kernel B LDS budget");
+};
+
+// C[16x16] += A[16 x 16] B[16 x 16] over one 16-row sub-block of the contraction.
+// AKC / BKC: operand stored with the contraction index contiguous (else gathered).
+template <typename T, bool AKC, bool BKC>
+__device__ __forceinline__ f32x4 mma_k16(const T* A, int lda, int ar0, const T* Bm, int ldb, int br0, int lane) {
+  using MM = Mma<T>;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 2) {
+    typename MM::Frag af, bf;
+    if ((lane >> 4) < 2) {
+      af = AKC ? MM::kc(A, lda, ar0, 0, lane) : MM::rc(A, lda, ar0, 0, lane);
+      bf = BKC ? MM::kc(Bm, ldb, br0, 0, lane) : MM::rc(Bm, ldb, br0, 0, lane);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) af[t] = bf[t] = (bf16)0.f;
+    }
+    acc = MM::mma(af, bf, acc);
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < 16; k0 += MM::KS)
+      acc = MM::mma(AKC ? MM::kc(A, lda, ar0, k0, lane) : MM::rc(A, lda, ar0, k0, lane),
+                    BKC ? MM::kc(Bm, ldb, br0, k0, lane) : MM::rc(Bm, ldb, br0, k0, lane), acc);
+  }
+  return acc;
+}
+
+template <typename T, int BT, int D, int DV>
+__global__ __launch_bounds__(256) void kda_gradB_kernel(BwdRoundArgs b, int H) {
+  using Ly = GBLayout<T, BT, D>;
+  using MM = Mma<T>;
+  using G = RG<D, DV>;
+  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDJ = Ly::LDJ, LDF = Ly::LDF;
+  constexpr int VN = 16 / sizeof(T), NC = D / 16;
+  __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
+  const RoundArgs& a = b.r;
+  float* Gf = reinterpret_cast<float*>(smem + Ly::O_GF);
+  T* Kr = reinterpret_cast<T*>(smem + Ly::O_ARR);
+  T* Qr = Kr + BT * LDK;
+  T* Kc0 = Qr + BT * LDK;
+  T* Kcd = Kc0 + BT * LDK;
+  float* stage = reinterpret_cast<float*>(smem + Ly::O_ARR);  // [BT][LDF] after the products
+  T* dMl = reinterpret_cast<T*>(smem + Ly::O_DM);
+  T* dAl = reinterpret_cast<T*>(smem + Ly::O_DA);
+  float* vec = reinterpret_cast<float*>(smem + Ly::O_VEC);
+  float *Tv = vec + Ly::VTV, *Fv = vec + Ly::VFV, *EF = vec + Ly::VEF, *EH = vec + Ly::VEH;
+  float *rs = vec + Ly::VRS, *cs = vec + Ly::VCS;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
+  const ChunkDesc cd = a.chunks[chunk];
+  const int len = cd.len, own = cd.own_from;
+  const size_t wsi = size_t(cd.local) * H + h;
+  const int32_t* vr = a.vrows + cd.vbase;
+  const T* gq = static_cast<const T*>(a.q);
+  const T* gk = static_cast<const T*>(a.k);
+  const T* gdo = static_cast<const T*>(b.dO);
+  const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+  const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
+  const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
+  const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
+  const size_t BB = size_t(BT) * BT;
+
+  chunk_decay<T, BT, D>(static_cast<const T*>(a.g), vr, len, H, h, Gf, Tv, Fv, EF, EH, tid);
+  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, bb = i / 16;
+    float kk[VN], qq[VN];
+    if (i < len) {
+      ld16(gk + (size_t(vr[i]) * H + h) * D + c0, kk);
+      ld16(gq + (size_t(vr[i]) * H + h) * D + c0, qq);
+    } else {
+#pragma unroll
+      for (int t = 0; t < VN; ++t) kk[t] = qq[t] = 0.f;
+    }
+    float kr[VN], qr[VN], kc[VN], kd[VN];
+#pragma unroll
+    for (int t = 0; t < VN; ++t) {
+      const float L = Gf[i * LDF + c0 + t];
+      const float er = __expf(L);
+      kr[t] = kk[t] * er;
+      qr[t] = qq[t] * er;
+      kc[t] = kk[t] * __expf(Tv[bb * D + c0 + t] - L);
+      kd[t] = kk[t] * __expf(-L);
+    }
+    st16(Kr + i * LDK + c0, kr);
+    st16(Qr + i * LDK + c0, qr);
+    st16(Kc0 + i * LDK + c0, kc);
+    st16(Kcd + i * LDK + c0, kd);
+  }
+  {
+    const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BB;
+    const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BB;
+    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
+      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
+      copy16(dMl + i * LDJ + j0, dmg + i * BT + j0);
+      copy16(dAl + i * LDJ + j0, dag + i * BT + j0);
+    }
+  }
+  // e^{G_last} rowsum(dS_end .* S0) per channel
+  for (int c = tid; c < D; c += 256) {
+    float s = 0.f;
+    for (int jv = 0; jv < DV; ++jv) s += to_f(dhg[jv * D + c]) * to_f(hg[jv * D + c]);
+    rs[c] = s * EF[NB * D + c];
+  }
+  for (int idx = tid; idx < 4 * D; idx += 256) cs[idx] = 0.f;
+  __syncthreads();
+
+  // per-wave results kept in registers for the staged writes
+  f32x4 dq_o[NC], dk_o[NC], dG_o[NC];
+  const int mi = wave;  // token block owned by this wave
+  const bool active = mi < NB;
+  if (active) {
+    f32x4 dqa[NC], X1[NC], X2[NC], X3[NC], X4[NC];
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) dqa[nc] = X1[nc] = X2[nc] = X3[nc] = X4[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ccl = ccol(lane);
+    // row-gated token products: sum_j P_ij k_j e^{F_mi - G_j}
+    for (int bj = 0; bj <= mi; ++bj) {
+      const T* kcol = (bj == mi ? Kcd : Kc0) + 16 * bj * LDK;
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        const float s = mi - bj >= 2 ? __expf(Fv[mi * D + 16 * nc + ccl] - Fv[(bj + 1) * D + 16 * nc + ccl]) : 1.f;
+        const f32x4 tm = mma_k16<T, true, false>(dMl + 16 * bj, LDJ, 16 * mi, kcol, LDK, 16 * nc, lane);
+        const f32x4 ta = mma_k16<T, true, false>(dAl + 16 * bj, LDJ, 16 * mi, kcol, LDK, 16 * nc, lane);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          dqa[nc][r] += s * tm[r];
+          X1[nc][r] += s * ta[r];
+        }
+      }
+    }
+    // column-gated token products: sum_i P_ij x_i e^{G_i - F_bi}, rows j of block mi
+    for (int bi = mi; bi < NB; ++bi) {
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc) {
+        const f32x4 tm = mma_k16<T, false, false>(dMl + 16 * bi * LDJ, LDJ, 16 * mi, Qr + 16 * bi * LDK, LDK, 16 * nc, lane);
+        const f32x4 ta = mma_k16<T, false, false>(dAl + 16 * bi * LDJ, LDJ, 16 * mi, Kr + 16 * bi * LDK, LDK, 16 * nc, lane);
+        if (bi == mi) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X2[nc][r] += tm[r] + ta[r];
+        } else {
+          const float s = bi - mi >= 2 ? __expf(Fv[bi * D + 16 * nc + ccl] - Fv[(mi + 1) * D + 16 * nc + ccl]) : 1.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) X3[nc][r] += s * (tm[r] + ta[r]);
+        }
+      }
+    }
+    // state-side products over value columns: dO S0^T, -dR S0^T (-> e^{F_b}), U dS^T (-> e^{G_last - F_{b+1}})
+    {
+      const int irow = 16 * mi + (lane & 15);
+      const bool ok = irow < len && irow >= own;
+      const T* dorow = gdo + (size_t(ok ? vr[irow] : 0) * H + h) * DV;
+      for (int k0 = 0; k0 < DV; k0 += MM::KS) {
+        typename MM::Frag fo;
+        if constexpr (sizeof(T) == 2) {
+          if (ok) fo = MM::kc(dorow, 0, 0, k0, lane & 48);
+          else
+#pragma unroll
+            for (int t = 0; t < 8; ++t) fo[t] = (bf16)0.f;
+        } else {
+          fo = ok ? dorow[k0 + (lane >> 4)] : 0.f;
+        }
+        const auto fr = MM::kc(drg, DV, 16 * mi, k0, lane);
+        const auto fu = MM::kc(ug, DV, 16 * mi, k0, lane);
+#pragma unroll
+        for (int nc = 0; nc < NC; ++nc) {
+          const auto fh = MM::rc(hg, D, 16 * nc, k0, lane);
+          const auto fd = MM::rc(dhg, D, 16 * nc, k0, lane);
+          const float ef = EF[mi * D + 16 * nc + ccl], eh = EH[mi * D + 16 * nc + ccl];
+          const f32x4 t1 = MM::mma(fo, fh, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 t2 = MM::mma(fr, fh, f32x4{0.f, 0.f, 0.f, 0.f});
+          const f32x4 t3 = MM::mma(fu, fd, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dqa[nc][r] += ef * t1[r];
+            X1[nc][r] -= ef * t2[r];
+            X4[nc][r] += eh * t3[r];
+          }
+        }
+      }
+    }
+    // assemble dq, dk, dG with exact q, k and fp32 factors
+    float csum[NC];
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      csum[nc] = 0.f;
+      const int c = 16 * nc + ccl;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * mi + crow(lane, r);
+        const float L = Gf[i * LDF + c];
+        const float er = __expf(L), ecd = __expf(-L), ec = __expf(Tv[mi * D + c] - L);
+        float qv = 0.f, kv = 0.f;
+        if (i < len) {
+          qv = to_f(gq[(size_t(vr[i]) * H + h) * D + c]);
+          kv = to_f(gk[(size_t(vr[i]) * H + h) * D + c]);
+        }
+        const float dq = er * dqa[nc][r];
+        const float krow = er * X1[nc][r], kcol = ecd * X2[nc][r] + ec * (X3[nc][r] + X4[nc][r]);
+        dq_o[nc][r] = dq;
+        dk_o[nc][r] = krow + kcol;
+        dG_o[nc][r] = qv * dq + kv * (krow - kcol);
+        csum[nc] += kv * ec * X4[nc][r];
+      }
+    }
+    // column sums of the K^ term: reduce the 4 row groups of the wave, then across waves
+#pragma unroll
+    for (int nc = 0; nc < NC; ++nc) {
+      float v = csum[nc];
+      v += __shfl_xor(v, 16, 64);
+      v += __shfl_xor(v, 32, 64);
+      if (lane < 16) cs[wave * D + 16 * nc + lane] = v;
+    }
+  }
+  __syncthreads();  // products done: the operand arrays become the staging buffer
+  // staged writes: own rows to the outputs, replayed rows to the side buffer
+  auto stage_out = [&](const f32x4* vals) {
+    if (active)
+#pragma unroll
+      for (int nc = 0; nc < NC; ++nc)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) stage[(16 * mi + crow(lane, r)) * LDF + 16 * nc + ccol(lane)] = vals[nc][r];
+  };
+  auto write_rows = [&](void* out, int rg_off, bool replay) {
+    T* o = static_cast<T*>(out);
+    for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+      const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
+      if (i >= len) continue;
+      if (i >= own) {
+        st16(o + (size_t(vr[i]) * H + h) * D + c0, stage + i * LDF + c0);
+      } else if (replay) {
+        float* rg = b.replay_grad + (size_t(cd.replay_base + i) * H + h) * G::W + rg_off + c0;
+#pragma unroll
+        for (int t = 0; t < VN; ++t) rg[t] = stage[i * LDF + c0 + t];
+      }
+    }
+  };
+  stage_out(dq_o);
+  __syncthreads();
+  write_rows(b.dq, 0, false);
+  __syncthreads();
+  stage_out(dk_o);
+  __syncthreads();
+  write_rows(b.dk, G::DK, true);
+  __syncthreads();
+  stage_out(dG_o);
+  __syncthreads();
+  // dG_last terms, then dg = reverse cumulative sum over the chunk
+  for (int c = tid; c < D; c += 256) {
+    float extra = rs[c];
+    for (int w = 0; w < 4; ++w) extra += cs[w * D + c];
+    float run = 0.f;
+    for (int i = BT - 1; i >= 0; --i) {
+      run += stage[i * LDF + c] + (i == BT - 1 ? extra : 0.f);
+      stage[i * LDF + c] = run;
+    }
+  }
+  __syncthreads();
+  write_rows(b.dg, G::DG, true);
+}
+
+// ------------------------------------------------------------------------------------------
+// Replayed rows: add every replay's gradient into the owning compact row, in a fixed order.
+template <typename T, int D, int DV>
+__global__ __launch_bounds__(128) void replay_fixup_kernel(const int32_t* rows, const int32_t* off, const int32_t* idx,
+                                                           const float* rg, T* dk, T* dv, T* dg, T* dbeta, int H) {
+  using G = RG<D, DV>;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const size_t row = size_t(rows[r]);
+  const int q0 = off[r], q1 = off[r + 1];
+  for (int e = threadIdx.x; e < G::W; e += blockDim.x) {
+    float s = 0.f;
+    for (int q = q0; q < q1; ++q) s += rg[(size_t(idx[q]) * H + h) * G::W + e];
+    if (e < D) {
+      T* p = dk + (row * H + h) * D + e;
+      *p = from_f<T>(to_f(*p) + s);
+    } else if (e < D + DV) {
+      T* p = dv + (row * H + h) * DV + (e - D);
+      *p = from_f<T>(to_f(*p) + s);
+    } else if (e < 2 * D + DV) {
+      T* p = dg + (row * H + h) * D + (e - D - DV);
+      *p = from_f<T>(to_f(*p) + s);
+    } else {
+      T* p = dbeta + row * H + h;
+      *p = from_f<T>(to_f(*p) + s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+template <typename T, int BT, int D, int DV>
+static hipError_t dstate_launch(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+  if (b.r.nseq <= 0) return hipSuccess;
+  constexpr int DVT = dv_tile_b<DV>();
+  unsigned n = unsigned(b.r.nseq) * d.H * (DV / DVT);
+  n = (n + 7) / 8 * 8;
+  hipLaunchKernelGGL((kda_dstate_kernel<T, BT, D, DV, DVT>), dim3(n), dim3(256), 0, s, b, d.H);
+  return hipGetLastError();
+}
+
+template <typename T, int BT, int D, int DV>
+static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+  if (b.r.nchunk <= 0) return hipSuccess;
+  dim3 grid(unsigned(b.r.nchunk) * d.H);
+  hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int DV>
+static hipError_t fixup_launch(const KdaDims& d, const int32_t* rows, const int32_t* off, const int32_t* idx,
+                               int32_t n, const float* rg, void* dk, void* dv, void* dg, void* dbeta, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL((replay_fixup_kernel<T, D, DV>), dim3(unsigned(n) * d.H), dim3(128), 0, s, rows, off, idx, rg,
+                     static_cast<T*>(dk), static_cast<T*>(dv), static_cast<T*>(dg), static_cast<T*>(dbeta), d.H);
+  return hipGetLastError();
+}
+
+#define HARTS_KDA_BWD_CONFIGS(X) \
+  X(bf16, 64, 128, 128)          \
+  X(bf16, 64, 64, 64)            \
+  X(bf16, 32, 64, 64)            \
+  X(float, 16, 16, 16)           \
+  X(float, 32, 32, 32)
+
+hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+#define X(T_, B_, D_, V_) \
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return dstate_launch<T_, B_, D_, V_>(d, b, s);
+  HARTS_KDA_BWD_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+#define X(T_, B_, D_, V_) \
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return grad_launch<T_, B_, D_, V_>(d, b, s);
+  HARTS_KDA_BWD_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* rows, const int32_t* off, const int32_t* idx,
+                               int32_t n, const float* rg, void* dk, void* dv, void* dg, void* dbeta, hipStream_t s) {
+#define X(T_, B_, D_, V_) \
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.D == D_ && d.DV == V_) return fixup_launch<T_, D_, V_>(d, rows, off, idx, n, rg, dk, dv, dg, dbeta, s);
+  HARTS_KDA_BWD_CONFIGS(X)
+#undef X
+  return hipErrorInvalidValue;
 }
 
 }  // namespace harts

@@ -255,7 +255,14 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(RoundArgs a, int H) {
   // 6. T = X diag(beta); K~ = Kr e^{F_b}, Q~ = Qr e^{F_b} in place; KhT = (Kc0 e^{F_end - F_{b+1}})^T
   for (int idx = tid; idx < BT * BT; idx += 256) {
     const int i = idx / BT, j = idx % BT;
-    Tm[i * LDJ + j] = from_f<T>(j <= i ? X[i * LDA + j] * bet[j] : 0.f);
+    const float tv = j <= i ? X[i * LDA + j] * bet[j] : 0.f;
+    Tm[i * LDJ + j] = from_f<T>(tv);
+    if (BWD) {
+      // T, X and A for the gradient kernels
+      static_cast<T*>(a.ws.Tm)[wsi * BT * BT + idx] = from_f<T>(tv);
+      static_cast<T*>(a.ws.Xm)[wsi * BT * BT + idx] = from_f<T>(j <= i ? X[i * LDA + j] : 0.f);
+      static_cast<T*>(a.ws.Am)[wsi * BT * BT + idx] = from_f<T>(j < i ? Am[i * LDA + j] : 0.f);
+    }
   }
   for (int idx = tid; idx < BT * (D / VN); idx += 256) {
     const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, b = i / 16;

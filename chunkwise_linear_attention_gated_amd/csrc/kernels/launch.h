@@ -19,6 +19,13 @@ struct ChunkWs {
   void* Mm;     // [BT][BT]  M = lower(gated Q K^T)
   float* El;    // [D]       e^{G_last}
   void* QeffT;  // [D][BT]   (Q~ - M W)^T                          (backward)
+  void* Tm;     // [BT][BT]  T = X diag(beta)                      (backward)
+  void* Xm;     // [BT][BT]  X = (I + diag(beta) A)^{-1}           (backward)
+  void* Am;     // [BT][BT]  A (strictly lower)                    (backward)
+  void* U;      // [BT][DV]  U = T (V - K~ S0)                      (backward)
+  void* dR;     // [BT][DV]  dL/dR = T^T dU                         (backward)
+  void* dM;     // [BT][BT]  dL/dM (lower incl.)                    (backward)
+  void* dA;     // [BT][BT]  dL/dA (strictly lower)                 (backward)
 };
 
 struct KdaDims {
@@ -30,6 +37,7 @@ struct RoundArgs {
   const SeqDesc* seqs;        // this round's sequences
   const ChunkDesc* chunks;    // this round's chunks
   int32_t nseq, nchunk;
+  int32_t seq0;               // global index of this round's first sequence
   const void *q, *k, *v, *g, *beta;
   void* o;                    // forward output [N][H][DV] (nullable)
   const float* init_pool;     // initial states by SeqDesc::init
@@ -48,13 +56,13 @@ struct BwdRoundArgs {
   float* dstates;             // per-slot gradient output (nullable)
   const int32_t* slot_cons_off;  // CSR of consumer sequences per slot (nullable for varlen)
   const int32_t* slot_cons;
-  float* replay_grad;         // [replay_total][H][3*D + 1] fp32 (dk, dv, dg, dbeta of replayed rows)
+  float* replay_grad;         // [replay_total][H][2*D + DV + 1] fp32 (dk, dv, dg, dbeta of replayed rows)
 };
 
 hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
-hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);  // both gradient kernels
 hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const int32_t* fix_off,
                                const int32_t* fix_idx, int32_t nrows, const float* replay_grad, void* dk, void* dv,
                                void* dg, void* dbeta, hipStream_t s);
