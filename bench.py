@@ -1,0 +1,310 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-packed chunkwise gated-delta path on one MI355X.
+
+One step = the whole hot path for one batch: the packed forward over every
+round of the minimum-call plan (with state handoffs) followed by the backward
+over every round in reverse (recompute, state-gradient pass with handoff
+gradients, per-chunk gradients, replay-gradient fixup), on the 64-leaf
+synthetic rollout tree (16384-token root, fan-out 2-4, fork offsets never
+chunk-aligned, leaf lengths log-uniform in [64, 4096]), H=16, d_k=d_v=128,
+B=64, bf16 inputs, fp32 state.  Planning (host, once per batch and reused by
+every layer) and the input upload are outside the timed region and reported
+separately.
+
+Prints ONE JSON line:  metric / value (compact tokens/s) / roofline of the
+dominant kernel / cpu_baseline (the float64 oracle on a bounded sample) /
+the log-prob gather (32768 x 131072 bf16) as an extra HBM measurement.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # MI355X HBM3E, B/s
+RIDGE = PEAK_BF16 / PEAK_HBM
+H, D, B = 16, 128, 64
+ES = 2                  # bf16 bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="only run a plain device copy of known size (for HBM counter calibration)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic work per kernel
+# Multiply-accumulates per chunk of l tokens (replay included) and head, d = d_k = d_v, for the
+# products each kernel performs ("Kernels and their rooflines").
+def macs(kernel, l, d=D):
+    l2d, ld2, l3 = l * l * d, l * d * d, l ** 3
+    return {
+        "kda_prep_fwd": 4 * l2d + l3 / 6,
+        "kda_state_fwd": 3 * ld2 + l2d,
+        "kda_prep_bwd": 5 * l2d + l3 / 6,
+        "kda_state_bwd": 2 * ld2,
+        "kda_dstate": 3 * ld2,
+        "kda_gradA": 5 * l2d + 2 * ld2 + 2 * l3,
+        "kda_gradB": 4 * l2d + 3 * ld2,
+    }[kernel]
+
+
+def hbm_bytes(kernel, l, d=D, bt=B):
+    """Bytes each kernel must move once per chunk-head: its inputs read once and its
+    outputs written once (workspace arrays are chunk-sized)."""
+    tok = l * d * ES        # one [l, d] bf16 tensor of the chunk's rows
+    blk = bt * d * ES       # one [B, d] workspace array
+    sq = bt * bt * ES       # one [B, B] workspace array
+    st = d * d * ES         # one bf16 state [d, d]
+    return {
+        "kda_prep_fwd": 4 * tok + l * ES + 4 * blk + sq + d * 4,
+        "kda_state_fwd": 4 * blk + sq + d * 4 + tok,
+        "kda_prep_bwd": 4 * tok + l * ES + 4 * blk + 4 * sq + d * 4,
+        "kda_state_bwd": 3 * blk + d * 4 + st,
+        "kda_dstate": 3 * blk + d * 4 + tok + st,
+        "kda_gradA": 4 * tok + l * ES + 2 * st + 4 * sq + tok + l * ES + 2 * blk + 2 * sq,
+        "kda_gradB": 4 * tok + 2 * st + 2 * blk + 2 * sq + 3 * tok,
+    }[kernel]
+
+
+def round_chunks(plan):
+    """Chunk lengths (replay included) per round."""
+    seqs = plan.sequences()
+    out = {}
+    for s in seqs:
+        vlen = s["n_replay"] + s["row_end"] - s["row_begin"]
+        lens = [min(B, vlen - c) for c in range(0, vlen, B)]
+        out.setdefault(s["round"], []).extend(lens)
+    return out
+
+
+def path_flops(chunk_lens):
+    """Dense-block algorithmic flops of forward + backward (with recompute) per head
+    for all chunks: forward 4 l^2 d + 3 l d^2 + l^3/6 MAC, backward 11 l^2 d + 8 l d^2
+    + 7/3 l^3 MAC."""
+    tot = 0.0
+    for l in chunk_lens:
+        tot += (4 + 11) * l * l * D + (3 + 8) * l * D * D + (1 / 6 + 7 / 3) * l ** 3
+    return 2 * tot * H
+
+
+def kernel_src_hash():
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "chunkwise_linear_attention_gated_amd", "csrc", "kernels", "*"))):
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        t = json.load(open(path))
+    except ValueError:
+        return None
+    if t.get("kernel_src_hash") != kernel_src_hash():
+        return None
+    k = t.get("kernels", {}).get(kernel)
+    return None if k is None else k.get("bytes_per_launch")
+
+
+def cpu_baseline(t, feats, C, S):
+    """The float64 oracle (trajectory-expanded, token by token, forward + reverse pass)
+    on the shortest trajectory, extrapolated per semantic position to the whole batch."""
+    from oracle.recurrent import Trajectories, default_threads
+    lens = np.diff(t.offsets)
+    x = int(np.argmin(lens))
+    rows = [t.node_of_pos[t.offsets[x]:t.offsets[x + 1]]]
+    F = {n: getattr(feats, n) for n in ("q", "k", "v", "g", "beta", "do")}
+    threads = min(default_threads(), int(os.environ.get("OMP_NUM_THREADS", "16") or 16), H)
+    tr = Trajectories(rows, F["q"], F["k"], F["v"], F["g"], F["beta"])
+    dO = F["do"][rows[0]].astype(np.float64)
+    t0 = time.perf_counter()
+    tr.forward(nthreads=threads)
+    tr.backward(dO, nthreads=threads)
+    dt = time.perf_counter() - t0
+    P = int(lens[x])
+    full = dt * S / P
+    return {"value": C / full, "unit": "compact tokens/s", "cores": threads, "kind": "oracle",
+            "sample": "trajectory %d of %d (%d semantic positions, %d heads), forward + reverse pass in %.1f s; "
+                      "extrapolated per position to all %d semantic positions" % (x, t.n_traj, P, H, dt, S)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only (this build has no multi-GPU path); got --gpus %d" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    from synthetic import tensors, trees
+
+    dev = "cuda"
+    if args.copy_calib:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes": n}))
+        return
+
+    # ---------------------------------------------------------------- workload
+    t = trees.random_rollout_tree(seed=args.seed)
+    feats = tensors.draw_features(t.n_nodes, H, D, D, seed=args.seed, dtype="bf16")
+    t0 = time.perf_counter()
+    plan = harts.TreePlan(t.tokens, t.offsets, B)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info
+    C, S = info.C, info.S
+    m, q_counts, _ = plan.maps()
+    nodes = np.empty(C, np.int64)
+    nodes[m] = t.node_of_pos
+    x = {n: tensors.to_torch(getattr(feats, n)[nodes], "bf16", dev) for n in ("q", "k", "v", "g", "beta", "do")}
+    dp = harts.DevicePlan(plan, H, D, D, harts.DTYPE_BF16)
+    ns = max(1, info.n_slots)
+    o = torch.empty((C, H, D), dtype=torch.bfloat16, device=dev)
+    slots = torch.zeros((ns, H, D, D), dtype=torch.float32, device=dev)
+    dslots = torch.zeros_like(slots)
+    gr = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "g", "beta")}
+    ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True)), dtype=torch.uint8, device=dev)
+
+    def step():
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws)
+        harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"],
+                      gr["g"], gr["beta"], states=slots, dstates=dslots, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # ---------------------------------------------------------------- timed region
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    ev0.record()
+    for _ in range(args.steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    value = C * args.steps / (ms_total / 1e3)
+
+    # ---------------------------------------------------------------- per-kernel timing (same steps, events on)
+    harts.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    prof = harts.profile_collect()
+    harts.profile_enable(False)
+    rch = round_chunks(plan)
+    all_chunks = [l for r in sorted(rch) for l in rch[r]]
+    kernels = {}
+    for name, (launches, tot_ms, units) in prof.items():
+        per_step_launches = launches / args.steps
+        entry = {"launches_per_step": per_step_launches, "avg_ms": tot_ms / launches,
+                 "ms_per_step": tot_ms / args.steps}
+        try:
+            fl = 2 * sum(macs(name, l) for l in all_chunks) * H           # per step
+            by = sum(hbm_bytes(name, l) for l in all_chunks) * H
+            entry["flops_per_launch"] = fl / per_step_launches
+            entry["bytes_per_launch"] = by / per_step_launches
+            sec = entry["avg_ms"] / 1e3
+            entry["tflops"] = entry["flops_per_launch"] / sec / 1e12
+            entry["gbps"] = entry["bytes_per_launch"] / sec / 1e9
+        except KeyError:
+            pass
+        kernels[name] = entry
+    dom = max((k for k in kernels if "flops_per_launch" in kernels[k]), key=lambda k: kernels[k]["ms_per_step"])
+    dk = kernels[dom]
+    intensity = dk["flops_per_launch"] / dk["bytes_per_launch"]
+    if intensity < RIDGE:
+        roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": dk["gbps"] * 1e9 / PEAK_HBM}
+    else:
+        roof = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": dk["tflops"] * 1e12 / PEAK_BF16}
+    roof["kernel"] = dom
+    roof["avg_launch_ms"] = dk["avg_ms"]
+    roof["traffic"] = traffic_for(dom)
+
+    flops_step = path_flops(all_chunks)
+    bytes_step = C * H * (1282 + 2308) + 2 * 2 * info.n_slots * H * D * D * 4
+    out = {
+        "metric": "compact tokens/s, tree-packed chunkwise gated-delta fwd+bwd; MFMA % of peak",
+        "value": value, "unit": "compact tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "64-leaf synthetic rollout tree (seed %d): 16384-token root, fan-out 2-4, "
+                               "leaf lengths log-uniform [64, 4096]; H=16, d_k=d_v=128, B=64; "
+                               "packed forward + backward over all rounds" % args.seed,
+                   "C": C, "S": S, "expansion": S / C, "n_rounds": info.n_rounds, "n_sequences": info.n_sequences,
+                   "n_slots": info.n_slots, "replay_tokens": info.replay_total, "n_chunks": info.n_chunks},
+        "mfma_pct": 100 * flops_step / (ms_step / 1e3) / PEAK_BF16,
+        "hbm_pct_ideal_bytes": 100 * bytes_step / (ms_step / 1e3) / PEAK_HBM,
+        "path_flops_per_step": flops_step,
+        "plan_ms": plan_ms,
+        "wall_s_timed": wall,
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    # ---------------------------------------------------------------- log-prob gather (32768 x 131072 bf16)
+    if not args.no_logprob:
+        del ws
+        torch.cuda.empty_cache()
+        Cl, V = 32768, 131072
+        w = tensors.logprob_map(Cl, V, seed=args.seed)
+        logits = tensors.logits_torch(Cl, V, seed=args.seed, device=dev)
+        mm = torch.from_numpy(w.m).to(dev)
+        lab = torch.from_numpy(w.labels).to(dev)
+        logp = torch.empty(len(w.m), dtype=torch.float32, device=dev)
+        qq = torch.empty(Cl, dtype=torch.int32, device=dev)
+        lws = torch.empty(harts.logprob_workspace_size(Cl), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
+        torch.cuda.synchronize()
+        reps = max(3, min(args.steps, 10))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
+        e1.record()
+        torch.cuda.synchronize()
+        lms = e0.elapsed_time(e1) / reps
+        lbytes = Cl * V * 2 + len(w.m) * (8 + 4 + 4 + 2) + Cl * 8
+        out["logprob_gather"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": lms, "bytes": lbytes,
+                                 "achieved_gbps": lbytes / (lms / 1e3) / 1e9,
+                                 "frac_hbm": lbytes / (lms / 1e3) / PEAK_HBM}
+        del logits
+    # ---------------------------------------------------------------- oracle on the host cores
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(t, feats, C, S)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -49,6 +49,10 @@ class KdaGrad(ctypes.Structure):
     _fields_ = [("dO", P), ("dq", P), ("dk", P), ("dv", P), ("dg", P), ("dbeta", P), ("dstates", P), ("dinit", P)]
 
 
+class ProfileEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 40), ("launches", I64), ("total_ms", ctypes.c_double), ("units", I64)]
+
+
 def _sig(name, res, *args):
     f = getattr(_L, name)
     f.restype = res
@@ -75,6 +79,8 @@ _kda_fwd = _sig("harts_kda_fwd", I32, P, ctypes.POINTER(KdaIO), P)
 _kda_bwd = _sig("harts_kda_bwd", I32, P, ctypes.POINTER(KdaIO), ctypes.POINTER(KdaGrad), P)
 _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
+_prof_enable = _sig("harts_profile_enable", I32, I32)
+_prof_collect = _sig("harts_profile_collect", I32, P, I32, P)
 _last_error = _sig("harts_last_error", ctypes.c_char_p)
 _version = _sig("harts_version", ctypes.c_char_p)
 
@@ -253,3 +259,16 @@ def logprob_gather(logits, m, labels, logp, q=None, lse=None, workspace=None, st
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lp(_ptr(logits), C, V, dtype, _ptr(m), _ptr(labels), S, _ptr(logp), _ptr(q), _ptr(lse),
                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def profile_enable(on: bool = True):
+    """harts_profile_enable: bracket every library kernel with HIP events."""
+    _check(_prof_enable(int(bool(on))))
+
+
+def profile_collect():
+    """harts_profile_collect: {kernel name: (launches, total_ms, units)}."""
+    n = I32()
+    arr = (ProfileEntry * 64)()
+    _check(_prof_collect(arr, 64, ctypes.byref(n)))
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms, arr[i].units) for i in range(min(n.value, 64))}

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -39,6 +41,42 @@ struct harts_dev_plan {
 
 namespace {
 thread_local std::string g_err;
+
+// ---- kernel timing (harts_profile_*): HIP event pairs per launch, on the launch stream
+struct ProfRec {
+  const char* name;
+  hipEvent_t e0, e1;
+  int64_t units;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+
+struct ProfScope {
+  ProfRec rec{};
+  hipStream_t s;
+  bool on;
+  ProfScope(const char* name, hipStream_t st, int64_t units) : s(st) {
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      on = g_prof_on;
+    }
+    if (!on) return;
+    rec.name = name;
+    rec.units = units;
+    if (hipEventCreate(&rec.e0) != hipSuccess || hipEventCreate(&rec.e1) != hipSuccess) {
+      on = false;
+      return;
+    }
+    (void)hipEventRecord(rec.e0, s);
+  }
+  ~ProfScope() {
+    if (!on) return;
+    (void)hipEventRecord(rec.e1, s);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof.push_back(rec);
+  }
+};
 
 int fail(int code, const std::string& msg) {
   g_err = msg;
@@ -347,8 +385,15 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     for (int r = 0; r < d->p.n_rounds; ++r) {
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
-      hip_check(harts::launch_kda_prep(d->dims, a, false, s), "prep kernel launch");
-      hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
+      const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
+      {
+        ProfScope ps("kda_prep_fwd", s, units);
+        hip_check(harts::launch_kda_prep(d->dims, a, false, s), "prep kernel launch");
+      }
+      {
+        ProfScope ps("kda_state_fwd", s, units);
+        hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
+      }
     }
   });
 }
@@ -377,16 +422,35 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       b.slot_cons_off = d->p.varlen ? nullptr : d->cons_off;
       b.slot_cons = d->p.varlen ? nullptr : d->cons;
       b.replay_grad = reinterpret_cast<float*>(ws + d->off_rg);
-      hip_check(harts::launch_kda_prep(d->dims, b.r, true, s), "prep kernel launch");
-      hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
-      hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
-      hip_check(harts::launch_kda_grad(d->dims, b, s), "gradient kernel launch");
+      const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
+      {
+        ProfScope ps("kda_prep_bwd", s, units);
+        hip_check(harts::launch_kda_prep(d->dims, b.r, true, s), "prep kernel launch");
+      }
+      {
+        ProfScope ps("kda_state_bwd", s, units);
+        hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
+      }
+      {
+        ProfScope ps("kda_dstate", s, units);
+        hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
+      }
+      {
+        ProfScope ps("kda_gradA", s, units);
+        hip_check(harts::launch_kda_grad(d->dims, b, 0, s), "gradient kernel launch");
+      }
+      {
+        ProfScope ps("kda_gradB", s, units);
+        hip_check(harts::launch_kda_grad(d->dims, b, 1, s), "gradient kernel launch");
+      }
     }
-    if (!d->p.fix_rows.empty())
+    if (!d->p.fix_rows.empty()) {
+      ProfScope ps("kda_replay_fixup", s, int64_t(d->p.replay_total) * d->dims.H);
       hip_check(harts::launch_replay_fixup(d->dims, d->fix_rows, d->fix_off, d->fix_idx,
                                            int32_t(d->p.fix_rows.size()), reinterpret_cast<float*>(ws + d->off_rg),
                                            g->dk, g->dv, g->dg, g->dbeta, s),
                 "replay fixup launch");
+    }
   });
 }
 
@@ -406,9 +470,58 @@ int harts_logprob_gather(const void* logits, int64_t C, int64_t V, int32_t dtype
       if (!workspace || workspace_bytes < size_t(C) * 4) throw Error(HARTS_EINVAL, "workspace too small");
       lse = static_cast<float*>(workspace);
     }
+    ProfScope ps("logprob_gather", static_cast<hipStream_t>(stream), C);
     hip_check(harts::launch_logprob(logits, C, V, dtype, m, labels, S, logp_out, q_out, lse,
                                     static_cast<hipStream_t>(stream)),
               "log-prob kernel launch");
+  });
+}
+
+int harts_profile_enable(int32_t on) {
+  return guarded([&] {
+    std::vector<ProfRec> old;
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      g_prof_on = on != 0;
+      if (on) old.swap(g_prof);
+    }
+    for (auto& r : old) {
+      (void)hipEventDestroy(r.e0);
+      (void)hipEventDestroy(r.e1);
+    }
+  });
+}
+
+int harts_profile_collect(harts_profile_entry* out, int32_t max_entries, int32_t* n_out) {
+  return guarded([&] {
+    std::vector<ProfRec> recs;
+    {
+      std::lock_guard<std::mutex> lk(g_prof_mu);
+      recs.swap(g_prof);
+    }
+    std::map<std::string, harts_profile_entry> agg;
+    std::vector<std::string> order;
+    hipError_t err = hipSuccess;
+    for (auto& r : recs) {
+      float ms = 0.f;
+      if (err == hipSuccess) err = hipEventSynchronize(r.e1);
+      if (err == hipSuccess) err = hipEventElapsedTime(&ms, r.e0, r.e1);
+      auto it = agg.find(r.name);
+      if (it == agg.end()) {
+        harts_profile_entry e{};
+        std::strncpy(e.name, r.name, sizeof(e.name) - 1);
+        it = agg.emplace(r.name, e).first;
+        order.push_back(r.name);
+      }
+      it->second.launches += 1;
+      it->second.total_ms += ms;
+      it->second.units += r.units;
+      (void)hipEventDestroy(r.e0);
+      (void)hipEventDestroy(r.e1);
+    }
+    hip_check(err, "profile event timing");
+    if (n_out) *n_out = int32_t(order.size());
+    for (size_t i = 0; i < order.size() && out && int32_t(i) < max_entries; ++i) out[i] = agg[order[i]];
   });
 }
 

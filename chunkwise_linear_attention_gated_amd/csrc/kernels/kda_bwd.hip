@@ -809,11 +809,11 @@ static hipError_t dstate_launch(const KdaDims& d, const BwdRoundArgs& b, hipStre
 }
 
 template <typename T, int BT, int D, int DV>
-static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {
   if (b.r.nchunk <= 0) return hipSuccess;
   dim3 grid(unsigned(b.r.nchunk) * d.H);
-  hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
-  hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  if (part == 0) hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  else hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
   return hipGetLastError();
 }
 
@@ -841,9 +841,9 @@ hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& b, hipStream_
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {
 #define X(T_, B_, D_, V_) \
-  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return grad_launch<T_, B_, D_, V_>(d, b, s);
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return grad_launch<T_, B_, D_, V_>(d, b, part, s);
   HARTS_KDA_BWD_CONFIGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -62,7 +62,7 @@ struct BwdRoundArgs {
 hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
-hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);  // both gradient kernels
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, int part, hipStream_t s);  // part 0: token side, 1: channel side
 hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const int32_t* fix_off,
                                const int32_t* fix_idx, int32_t nrows, const float* replay_grad, void* dk, void* dv,
                                void* dg, void* dbeta, hipStream_t s);

@@ -230,6 +230,27 @@ int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype
                          const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, float *lse_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- kernel timing
+ * For benchmarks and profiling.  While enabled, every kernel the library
+ * enqueues is bracketed by two HIP events recorded on the same stream (this
+ * adds event overhead; keep it off in timed production runs).
+ * harts_profile_enable(1) starts a fresh record, (0) stops recording.
+ * harts_profile_collect() waits for the recorded events and reports, per
+ * kernel name, the number of launches, their summed elapsed time and the
+ * summed work units (token-heads processed, replay included; logits rows for
+ * the log-prob kernels).  out: host array of max_entries; *n_out receives the
+ * number of kernel names recorded (may exceed max_entries).
+ */
+typedef struct {
+  char name[40];
+  int64_t launches;
+  double total_ms;
+  int64_t units;
+} harts_profile_entry;
+
+int harts_profile_enable(int32_t on);
+int harts_profile_collect(harts_profile_entry *out, int32_t max_entries, int32_t *n_out);
+
 /* ---------------------------------------------------------------- misc */
 const char *harts_last_error(void);
 /* Library version string. */
