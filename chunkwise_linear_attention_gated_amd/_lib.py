@@ -22,6 +22,13 @@ DTYPE_FP32 = 1
 if not os.path.exists(_SO):
     raise ImportError("HIP library %s is missing: build it with chunkwise_linear_attention_gated_amd.build.build()"
                       % _SO)
+# PyTorch ships its own HIP runtime under the same soname.  Load it first so the
+# library binds to that runtime: device pointers and streams handed over from
+# torch are only valid inside the runtime instance that created them.
+try:
+    import torch  # noqa: F401
+except ImportError:  # host-only use (planner) without torch
+    pass
 _L = ctypes.CDLL(_SO)
 library = _SO
 
