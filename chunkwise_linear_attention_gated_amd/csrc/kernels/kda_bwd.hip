@@ -29,14 +29,72 @@ template <int D, int DV> struct RG {
 
 // ------------------------------------------------------------------------------------------
 // Serial state-gradient pass, reverse over chunks.  One workgroup per (sequence, head,
-// value-column tile).  dS (fp32) lives in accumulator registers.
+// value-column tile).  dS (fp32) lives in accumulator registers.  The per-chunk operands
+// (W, KhT and the dO tile, staged through LDS; Qeff^T fragments and e^{G_last}) are loaded
+// one chunk ahead into registers so only LDS and matrix-core latency sit on the chain.
+template <typename T, int BT, int D, int DV, int DVT>
+struct DStateOps {
+  using MM = Mma<T>;
+  using F = typename MM::Frag;
+  static constexpr int VN = 16 / sizeof(T);
+  static constexpr int NW = (BT * (D / VN) + 255) / 256;   // 16-byte pieces of W per thread
+  static constexpr int NK = (D * (BT / VN) + 255) / 256;   // ... of KhT
+  static constexpr int NO = (BT * (DVT / VN) + 255) / 256; // ... of the dO tile
+  static constexpr int MU = (D / 16 + 3) / 4, KB = BT / MM::KS;
+  f32x4 w[NW], kh[NK], dov[NO];
+  F qe[MU][KB];
+  float el[MU][4];
+};
+
+template <typename T, int BT, int D, int DV, int DVT>
+__device__ __forceinline__ void load_dstate_ops(DStateOps<T, BT, D, DV, DVT>& o, const RoundArgs& a, const T* gdo,
+                                                const ChunkDesc& cd, size_t wsi, int H, int h, int tid, int wave,
+                                                int lane, int jvb) {
+  using Ops = DStateOps<T, BT, D, DV, DVT>;
+  using MM = Mma<T>;
+  constexpr int VN = Ops::VN, MT = D / 16;
+  const T* wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
+  const T* kg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
+#pragma unroll
+  for (int x = 0; x < Ops::NW; ++x) {
+    const int idx = tid + 256 * x;
+    if (idx < BT * (D / VN)) o.w[x] = *reinterpret_cast<const f32x4*>(wg + idx * VN);
+  }
+#pragma unroll
+  for (int x = 0; x < Ops::NK; ++x) {
+    const int idx = tid + 256 * x;
+    if (idx < D * (BT / VN)) o.kh[x] = *reinterpret_cast<const f32x4*>(kg + idx * VN);
+  }
+#pragma unroll
+  for (int x = 0; x < Ops::NO; ++x) {
+    const int idx = tid + 256 * x;
+    const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
+    o.dov[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (idx < BT * (DVT / VN) && i < cd.len && i >= cd.own_from)
+      o.dov[x] = *reinterpret_cast<const f32x4*>(gdo + (size_t(a.vrows[cd.vbase + i]) * H + h) * DV + jvb + j0);
+  }
+  const T* qe = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
+  const float* el = a.ws.El + wsi * D;
+#pragma unroll
+  for (int u = 0; u < Ops::MU; ++u) {
+    const int mt = wave + 4 * u;
+    if (mt < MT) {
+#pragma unroll
+      for (int kk = 0; kk < Ops::KB; ++kk) o.qe[u][kk] = MM::kc(qe, BT, 16 * mt, kk * MM::KS, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mt + crow(lane, r)];
+    }
+  }
+}
+
 template <typename T, int BT, int D, int DV, int DVT>
 __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) {
   using MM = Mma<T>;
+  using Ops = DStateOps<T, BT, D, DV, DVT>;
   const RoundArgs& a = b.r;
   constexpr int NTL = DV / DVT, PAD = 16 / sizeof(T), VN = 16 / sizeof(T);
   constexpr int LDS_S = D + PAD, LDK = D + PAD, LDJ = BT + PAD, LDO = DVT + PAD;
-  constexpr int MT = D / 16, NTV = DVT / 16, MU = (MT + 3) / 4;
+  constexpr int MT = D / 16, NTV = DVT / 16, MU = Ops::MU;
   __shared__ __attribute__((aligned(16))) T dSt[DVT * LDS_S];
   __shared__ __attribute__((aligned(16))) T Wl[BT * LDK];
   __shared__ __attribute__((aligned(16))) T Kl[D * LDJ];
@@ -54,9 +112,14 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
   for (int u = 0; u < MU; ++u)
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) dS[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  Ops cur, nxt;
+  ChunkDesc cd = a.chunks[sd.chunk_base + sd.n_chunks - 1];
+  load_dstate_ops<T, BT, D, DV, DVT>(cur, a, gdo, cd, size_t(cd.local) * H + h, H, h, tid, wave, lane, jvb);
   for (int n = sd.n_chunks - 1; n >= 0; --n) {
-    const ChunkDesc cd = a.chunks[sd.chunk_base + n];
     const size_t wsi = size_t(cd.local) * H + h;
+    const ChunkDesc cdn = a.chunks[sd.chunk_base + (n > 0 ? n - 1 : 0)];
+    if (n > 0)
+      load_dstate_ops<T, BT, D, DV, DVT>(nxt, a, gdo, cdn, size_t(cdn.local) * H + h, H, h, tid, wave, lane, jvb);
     __syncthreads();
     // slot gradient: sum over the consumers of the state emitted after this chunk
     if (cd.emit >= 0 && b.slot_cons_off) {
@@ -87,23 +150,28 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
           store4(dSt + (16 * nt + ccol(lane)) * LDS_S + 16 * mt + crow(lane, 0), dS[u][nt][0], dS[u][nt][1],
                  dS[u][nt][2], dS[u][nt][3]);
     }
-    {
-      const T* wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
-      const T* kg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
-      for (int idx = tid; idx < BT * (D / VN); idx += 256) {
+#pragma unroll
+    for (int x = 0; x < Ops::NW; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < BT * (D / VN)) {
         const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-        copy16(Wl + i * LDK + c0, wg + i * D + c0);
+        *reinterpret_cast<f32x4*>(Wl + i * LDK + c0) = cur.w[x];
       }
-      for (int idx = tid; idx < D * (BT / VN); idx += 256) {
+    }
+#pragma unroll
+    for (int x = 0; x < Ops::NK; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < D * (BT / VN)) {
         const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
-        copy16(Kl + c * LDJ + i0, kg + c * BT + i0);
+        *reinterpret_cast<f32x4*>(Kl + c * LDJ + i0) = cur.kh[x];
       }
-      for (int idx = tid; idx < BT * (DVT / VN); idx += 256) {
+    }
+#pragma unroll
+    for (int x = 0; x < Ops::NO; ++x) {
+      const int idx = tid + 256 * x;
+      if (idx < BT * (DVT / VN)) {
         const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-        if (i < cd.len && i >= cd.own_from)
-          copy16(dOl + i * LDO + j0, gdo + (size_t(a.vrows[cd.vbase + i]) * H + h) * DV + jvb + j0);
-        else
-          *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = cur.dov[x];
       }
     }
     __syncthreads();
@@ -120,6 +188,7 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
       f32x4 acc[NTV];
 #pragma unroll
       for (int nt = 0; nt < NTV; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
       for (int k0 = 0; k0 < D; k0 += MM::KS) {
         const auto af = MM::rc(Kl, LDJ, 16 * mi, k0, lane);
 #pragma unroll
@@ -132,34 +201,30 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
     }
     __syncthreads();
     // dS <- diag(e^{G_last}) dS + Qeff^T dO - W^T Y
-    {
-      const T* qe = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
-      const float* el = a.ws.El + wsi * D;
 #pragma unroll
-      for (int u = 0; u < MU; ++u) {
-        const int mt = wave + 4 * u;
-        if (mt < MT) {
-          f32x4 a1[NTV], a2[NTV];
+    for (int u = 0; u < MU; ++u) {
+      const int mt = wave + 4 * u;
+      if (mt < MT) {
+        f32x4 a1[NTV], a2[NTV];
 #pragma unroll
-          for (int nt = 0; nt < NTV; ++nt) a1[nt] = a2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int k0 = 0; k0 < BT; k0 += MM::KS) {
-            const auto f1 = MM::kc(qe, BT, 16 * mt, k0, lane);
-            const auto f2 = MM::rc(Wl, LDK, 16 * mt, k0, lane);
+        for (int nt = 0; nt < NTV; ++nt) a1[nt] = a2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) {
-              a1[nt] = MM::mma(f1, MM::rc(dOl, LDO, 16 * nt, k0, lane), a1[nt]);
-              a2[nt] = MM::mma(f2, MM::kc(Yt, LDJ, 16 * nt, k0, lane), a2[nt]);
-            }
-          }
+        for (int kk = 0; kk < Ops::KB; ++kk) {
+          const auto f2 = MM::rc(Wl, LDK, 16 * mt, kk * MM::KS, lane);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = el[16 * mt + crow(lane, r)];
-#pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) dS[u][nt][r] = e * dS[u][nt][r] + a1[nt][r] - a2[nt][r];
+          for (int nt = 0; nt < NTV; ++nt) {
+            a1[nt] = MM::mma(cur.qe[u][kk], MM::rc(dOl, LDO, 16 * nt, kk * MM::KS, lane), a1[nt]);
+            a2[nt] = MM::mma(f2, MM::kc(Yt, LDJ, 16 * nt, kk * MM::KS, lane), a2[nt]);
           }
         }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt) dS[u][nt][r] = cur.el[u][r] * dS[u][nt][r] + a1[nt][r] - a2[nt][r];
       }
     }
+    cur = nxt;
+    cd = cdn;
   }
   if (b.dinit) {
     const size_t gs = size_t(a.seq0 + si);

@@ -360,14 +360,74 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(RoundArgs a, int H) {
 // the columns of S evolve independently.  Per chunk:
 //   U = U' - W S;  [forward] O^T = S^T Q~^T + U^T M^T;  S = diag(e^{G_last}) S + KhT U.
 // S lives in accumulator registers (fp32); S^T and U^T are staged in LDS as MFMA operands.
-// Backward mode writes S^T of every chunk start (the recomputed chunk-start states).
+// Every per-chunk operand that does not depend on S (W, U', Q~, M, KhT, e^{G_last}) is
+// loaded one chunk ahead into registers, so the chain S -> U -> S only waits on LDS and
+// the matrix cores.  Backward mode writes S^T of every chunk start (the recomputed
+// chunk-start states).
+template <typename T, int BT, int D, int DV, int DVT, bool FWD>
+struct StateOps {
+  using MM = Mma<T>;
+  using F = typename MM::Frag;
+  static constexpr int NMI = (BT / 16 + 3) / 4, MU = (D / 16 + 3) / 4, NTV = DVT / 16;
+  static constexpr int KD = D / MM::KS, KB = BT / MM::KS;
+  static constexpr int NQ = FWD ? NMI : 1, KQ = FWD ? KD : 1, KM = FWD ? KB : 1;
+  F wa[NMI][KD];        // W fragments (A operand of U = W S), token rows of this wave
+  float up[NMI][NTV][4];  // U' at this lane's accumulator positions
+  F qb[NQ][KQ];         // Q~ fragments (B operand of O^T), forward only
+  F mb[NQ][KM];         // M fragments (B operand of O^T), forward only
+  F ka[MU][KB];         // KhT fragments (A operand of S += KhT U)
+  float el[MU][4];      // e^{G_last} of this lane's state rows
+};
+
+template <typename T, int BT, int D, int DV, int DVT, bool FWD>
+__device__ __forceinline__ void load_state_ops(StateOps<T, BT, D, DV, DVT, FWD>& o, const ChunkWs& ws, size_t wsi,
+                                               int wave, int lane, int jvb) {
+  using Ops = StateOps<T, BT, D, DV, DVT, FWD>;
+  using MM = Mma<T>;
+  constexpr int MT = D / 16;
+  const T* wg = static_cast<const T*>(ws.W) + wsi * BT * D;
+  const T* upg = static_cast<const T*>(ws.UpT) + wsi * DV * BT;
+  const T* khg = static_cast<const T*>(ws.KhT) + wsi * D * BT;
+  const float* el = ws.El + wsi * D;
+#pragma unroll
+  for (int x = 0; x < Ops::NMI; ++x) {
+    const int mi = wave + 4 * x;
+    if (mi < BT / 16) {
+#pragma unroll
+      for (int kk = 0; kk < Ops::KD; ++kk) o.wa[x][kk] = MM::kc(wg, D, 16 * mi, kk * MM::KS, lane);
+#pragma unroll
+      for (int nt = 0; nt < Ops::NTV; ++nt)
+        load4(upg + (jvb + 16 * nt + ccol(lane)) * BT + 16 * mi + crow(lane, 0), o.up[x][nt]);
+      if constexpr (FWD) {
+        const T* qg = static_cast<const T*>(ws.Qt) + wsi * BT * D;
+        const T* mg = static_cast<const T*>(ws.Mm) + wsi * BT * BT;
+#pragma unroll
+        for (int kk = 0; kk < Ops::KD; ++kk) o.qb[x][kk] = MM::kc(qg, D, 16 * mi, kk * MM::KS, lane);
+#pragma unroll
+        for (int kk = 0; kk < Ops::KB; ++kk) o.mb[x][kk] = MM::kc(mg, BT, 16 * mi, kk * MM::KS, lane);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < Ops::MU; ++u) {
+    const int mt = wave + 4 * u;
+    if (mt < MT) {
+#pragma unroll
+      for (int kk = 0; kk < Ops::KB; ++kk) o.ka[u][kk] = MM::kc(khg, BT, 16 * mt, kk * MM::KS, lane);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mt + crow(lane, r)];
+    }
+  }
+}
+
 template <typename T, int BT, int D, int DV, int DVT, bool BWD>
 __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
   using MM = Mma<T>;
+  using Ops = StateOps<T, BT, D, DV, DVT, !BWD>;
   constexpr int NTL = DV / DVT;
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LDS_S = D + PAD, LDS_U = BT + PAD;
-  constexpr int MT = D / 16, NTV = DVT / 16, MU = (MT + 3) / 4;
+  constexpr int MT = D / 16, NTV = DVT / 16, MU = Ops::MU, NMI = Ops::NMI;
   __shared__ __attribute__((aligned(16))) T St[2][DVT * LDS_S];
   __shared__ __attribute__((aligned(16))) T Ut[DVT * LDS_U];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -392,9 +452,14 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
         S[u][nt][r] = v;
       }
     }
+  Ops cur, nxt;
+  ChunkDesc cd = a.chunks[sd.chunk_base];
+  load_state_ops<T, BT, D, DV, DVT, !BWD>(cur, a.ws, size_t(cd.local) * H + h, wave, lane, jvb);
   for (int n = 0; n < sd.n_chunks; ++n) {
-    const ChunkDesc cd = a.chunks[sd.chunk_base + n];
     const size_t wsi = size_t(cd.local) * H + h;
+    const ChunkDesc cdn = a.chunks[sd.chunk_base + (n + 1 < sd.n_chunks ? n + 1 : n)];
+    if (n + 1 < sd.n_chunks)
+      load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a.ws, size_t(cdn.local) * H + h, wave, lane, jvb);
     T* Sb = St[n & 1];
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
@@ -415,76 +480,70 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
       }
     }
     // (a) U = U' - W S
-    {
-      const T* Wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
-      const T* upg = static_cast<const T*>(a.ws.UpT) + wsi * DV * BT;
-      for (int mi = wave; mi < BT / 16; mi += 4) {
+#pragma unroll
+    for (int x = 0; x < NMI; ++x) {
+      const int mi = wave + 4 * x;
+      if (mi < BT / 16) {
         f32x4 acc[NTV];
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < D; k0 += MM::KS) {
-          const auto af = MM::kc(Wg, D, 16 * mi, k0, lane);
 #pragma unroll
-          for (int nt = 0; nt < NTV; ++nt) acc[nt] = MM::mma(af, MM::kc(Sb, LDS_S, 16 * nt, k0, lane), acc[nt]);
-        }
+        for (int kk = 0; kk < Ops::KD; ++kk)
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt)
+            acc[nt] = MM::mma(cur.wa[x][kk], MM::kc(Sb, LDS_S, 16 * nt, kk * MM::KS, lane), acc[nt]);
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           const int jl = 16 * nt + ccol(lane), i0 = 16 * mi + crow(lane, 0);
-          float up[4];
-          load4(upg + (jvb + jl) * BT + i0, up);
-          store4(Ut + jl * LDS_U + i0, up[0] - acc[nt][0], up[1] - acc[nt][1], up[2] - acc[nt][2],
-                 up[3] - acc[nt][3]);
+          store4(Ut + jl * LDS_U + i0, cur.up[x][nt][0] - acc[nt][0], cur.up[x][nt][1] - acc[nt][1],
+                 cur.up[x][nt][2] - acc[nt][2], cur.up[x][nt][3] - acc[nt][3]);
         }
       }
     }
     __syncthreads();
-    if constexpr (!BWD) {
-      // O^T = S^T Q~^T + U^T M^T for own rows
-      const T* qg = static_cast<const T*>(a.ws.Qt) + wsi * BT * D;
-      const T* mg = static_cast<const T*>(a.ws.Mm) + wsi * BT * BT;
-      T* og = static_cast<T*>(a.o);
-      for (int ni = wave; ni < BT / 16; ni += 4) {
-        f32x4 acc[NTV];
+    // (b) S = diag(e^{G_last}) S + KhT U   (the chain: issued before the output products)
 #pragma unroll
-        for (int m = 0; m < NTV; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k0 = 0; k0 < D; k0 += MM::KS) {
-          const auto bf = MM::kc(qg, D, 16 * ni, k0, lane);
+    for (int u = 0; u < MU; ++u) {
+      const int mt = wave + 4 * u;
+      if (mt < MT) {
 #pragma unroll
-          for (int m = 0; m < NTV; ++m) acc[m] = MM::mma(MM::kc(Sb, LDS_S, 16 * m, k0, lane), bf, acc[m]);
-        }
-        for (int k0 = 0; k0 < BT; k0 += MM::KS) {
-          const auto bf = MM::kc(mg, BT, 16 * ni, k0, lane);
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-          for (int m = 0; m < NTV; ++m) acc[m] = MM::mma(MM::kc(Ut, LDS_U, 16 * m, k0, lane), bf, acc[m]);
-        }
-        const int i = 16 * ni + ccol(lane);
-        if (og && i < cd.len && i >= cd.own_from) {
-          const size_t row = size_t(a.vrows[cd.vbase + i]);
+          for (int nt = 0; nt < NTV; ++nt) S[u][nt][r] *= cur.el[u][r];
 #pragma unroll
-          for (int m = 0; m < NTV; ++m)
-            store4(og + (row * H + h) * DV + jvb + 16 * m + crow(lane, 0), acc[m][0], acc[m][1], acc[m][2],
-                   acc[m][3]);
-        }
+        for (int kk = 0; kk < Ops::KB; ++kk)
+#pragma unroll
+          for (int nt = 0; nt < NTV; ++nt)
+            S[u][nt] = MM::mma(cur.ka[u][kk], MM::kc(Ut, LDS_U, 16 * nt, kk * MM::KS, lane), S[u][nt]);
       }
     }
-    // (b) S = diag(e^{G_last}) S + KhT U
-    {
-      const T* khg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
-      const float* el = a.ws.El + wsi * D;
+    if constexpr (!BWD) {
+      // O^T = S^T Q~^T + U^T M^T for own rows
+      T* og = static_cast<T*>(a.o);
 #pragma unroll
-      for (int u = 0; u < MU; ++u) {
-        const int mt = wave + 4 * u;
-        if (mt < MT) {
+      for (int x = 0; x < NMI; ++x) {
+        const int ni = wave + 4 * x;
+        if (ni < BT / 16) {
+          f32x4 acc[NTV];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = el[16 * mt + crow(lane, r)];
+          for (int m = 0; m < NTV; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) S[u][nt][r] *= e;
-          }
-          for (int k0 = 0; k0 < BT; k0 += MM::KS) {
-            const auto af = MM::kc(khg, BT, 16 * mt, k0, lane);
+          for (int kk = 0; kk < Ops::KD; ++kk)
 #pragma unroll
-            for (int nt = 0; nt < NTV; ++nt) S[u][nt] = MM::mma(af, MM::kc(Ut, LDS_U, 16 * nt, k0, lane), S[u][nt]);
+            for (int m = 0; m < NTV; ++m)
+              acc[m] = MM::mma(MM::kc(Sb, LDS_S, 16 * m, kk * MM::KS, lane), cur.qb[x][kk], acc[m]);
+#pragma unroll
+          for (int kk = 0; kk < Ops::KB; ++kk)
+#pragma unroll
+            for (int m = 0; m < NTV; ++m)
+              acc[m] = MM::mma(MM::kc(Ut, LDS_U, 16 * m, kk * MM::KS, lane), cur.mb[x][kk], acc[m]);
+          const int i = 16 * ni + ccol(lane);
+          if (og && i < cd.len && i >= cd.own_from) {
+            const size_t row = size_t(a.vrows[cd.vbase + i]);
+#pragma unroll
+            for (int m = 0; m < NTV; ++m)
+              store4(og + (row * H + h) * DV + jvb + 16 * m + crow(lane, 0), acc[m][0], acc[m][1], acc[m][2],
+                     acc[m][3]);
           }
         }
       }
@@ -503,6 +562,8 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
             }
       }
     }
+    cur = nxt;
+    cd = cdn;
   }
   if (sd.final_idx >= 0 && a.final_pool) {
 #pragma unroll
