@@ -28,6 +28,7 @@ struct harts_dev_plan {
   int32_t* vrows = nullptr;
   harts::SeqDesc* seqs = nullptr;
   harts::ChunkDesc* chunks = nullptr;
+  int32_t* crows = nullptr;
   int32_t* cons_off = nullptr;
   int32_t* cons = nullptr;
   int32_t* fix_rows = nullptr;
@@ -117,7 +118,7 @@ T* upload(const std::vector<T>& v, hipStream_t s) {
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
 void free_dev(harts_dev_plan* d) {
-  void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx};
+  void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->crows, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -128,6 +129,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.vrows = d->vrows;
   a.seqs = d->seqs + rr.seq0;
   a.chunks = d->chunks + rr.chunk0;
+  a.crows = d->crows + size_t(rr.chunk0) * d->p.B;
   a.nseq = rr.seq1 - rr.seq0;
   a.nchunk = rr.chunk1 - rr.chunk0;
   a.seq0 = rr.seq0;
@@ -316,6 +318,18 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->vrows = upload(d->p.vrows, s);
       d->seqs = upload(d->p.seq_desc, s);
       d->chunks = upload(d->p.chunk_desc, s);
+      {
+        // padded per-chunk row table: lets the per-chunk kernels fetch a chunk's rows
+        // without first reading its descriptor
+        const size_t BTc = size_t(d->p.B);
+        std::vector<int32_t> cr(d->p.chunk_desc.size() * BTc, -1);
+        for (size_t c = 0; c < d->p.chunk_desc.size(); ++c) {
+          const harts::ChunkDesc& cd = d->p.chunk_desc[c];
+          for (int i = 0; i < cd.len; ++i) cr[c * BTc + i] = d->p.vrows[size_t(cd.vbase) + i];
+        }
+        d->crows = upload(cr, s);
+        hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+      }
       d->cons_off = upload(d->p.slot_cons_off, s);
       d->cons = upload(d->p.slot_cons, s);
       d->fix_rows = upload(d->p.fix_rows, s);

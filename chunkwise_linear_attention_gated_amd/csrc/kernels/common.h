@@ -111,6 +111,52 @@ template <typename T> __device__ __forceinline__ void copy16(T* dst, const T* sr
   *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(src);
 }
 
+// 16 bytes of T held in a register quad (8 bf16 or 4 fp32), converted to and from floats
+template <typename T> __device__ __forceinline__ void unpack16(f32x4 v, float* out) {
+  if constexpr (sizeof(T) == 2) {
+    const bf16x8 b = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) out[t] = (float)b[t];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) out[t] = v[t];
+  }
+}
+template <typename T> __device__ __forceinline__ f32x4 pack16(const float* in) {
+  if constexpr (sizeof(T) == 2) {
+    bf16x8 b;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) b[t] = (bf16)in[t];
+    return __builtin_bit_cast(f32x4, b);
+  } else {
+    return f32x4{in[0], in[1], in[2], in[3]};
+  }
+}
+__device__ __forceinline__ f32x4 ldq(const void* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void stq(void* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+
+// fp32 16x16 product step with a permuted contraction index: at step s lane l
+// supplies A[l%16][4*(l/16) + s] and B[4*(l/16) + s][l%16].  Over s = 0..3 every
+// k in 0..15 is covered once, the A values of a lane are 4 consecutive row
+// elements (one 16-byte read) and the B values of a lane are exactly the C
+// layout of an earlier product, so results chain without leaving registers.
+__device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], b[s], c, 0, 0, 0);
+  return c;
+}
+
+// for (var = start; var < n; var += step) with a compile-time trip count, fully
+// unrolled: inside the persistent kernels a runtime-bounded loop makes the compiler
+// drain every outstanding load (the fetch-ahead included) before entering it.
+#define HARTS_STRIDED(var, start, n, step)                                              \
+  _Pragma("unroll") for (int var##_u = 0; var##_u < ((n) + (step) - 1) / (step); ++var##_u) \
+    if (const int var = (start) + (step) * var##_u; var < (n))
+
+// Workgroup size of the persistent per-chunk kernels: 8 waves, two per SIMD.
+constexpr int CNT = 512;
+constexpr int CNW = CNT / 64;
+
 // Blocks of a grid are dealt round-robin to the 8 XCDs; remap so that runs of
 // consecutive logical ids (e.g. the value-column tiles of one sequence-head,
 // which read the same per-chunk operands) land on one XCD and share its L2.

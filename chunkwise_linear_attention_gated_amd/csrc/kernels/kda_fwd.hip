@@ -23,335 +23,474 @@ __host__ __device__ constexpr int pair_index(int bi, int bj) { return (bi - 2) *
 
 template <typename T, int BT, int D, int DV>
 struct PrepLayout {
-  static constexpr int NB = BT / 16;
-  static constexpr int PAD = 16 / sizeof(T);
-  static constexpr int LDK = D + PAD, LDJ = BT + PAD, LDV = DV + PAD;
-  static constexpr int LDF = D + 4, LDA = BT + 4;
+  static constexpr int NB = BT / 16, VN = 16 / sizeof(T), PAD = VN;
+  static constexpr int LDK = D + PAD, LDV = DV + PAD, LDJ = BT + PAD, LDF = D + 4, LDA = BT + 4;
   static constexpr int NPX = NB >= 3 ? (NB - 1) * (NB - 2) / 2 : 0;
-  static constexpr size_t szK = size_t(BT) * LDK * sizeof(T);
-  // R1: Gf | X, Tmp | V, W(backward)
-  static constexpr size_t R1 = cmax(cmax(size_t(BT) * LDF * 4, 2 * size_t(BT) * LDA * 4),
-                                    size_t(BT) * LDV * sizeof(T) + szK);
-  static constexpr size_t R1_OFF = 0;
-  // Am: A (fp32) | M (backward, T)
-  static constexpr size_t AM_OFF = R1_OFF + R1;
-  static constexpr size_t AM = cmax(size_t(BT) * LDA * 4, size_t(BT) * LDJ * sizeof(T));
-  // R2: Kr->K~ | Qr->Q~ | Kc0 | Kcd,Kcx -> KhT | Tm
-  static constexpr size_t R2_OFF = AM_OFF + AM;
-  static constexpr size_t KR = 0, QR = KR + szK, KC0 = QR + szK, KCD = KC0 + szK, KCX = KCD + szK;
-  static constexpr size_t AEND = KCX + size_t(NPX) * 16 * LDK * sizeof(T);
-  static constexpr size_t KHT = KCD;
-  static constexpr size_t TM = cmax(AEND, KHT + size_t(D) * LDJ * sizeof(T));
-  static constexpr size_t R2 = TM + size_t(BT) * LDJ * sizeof(T);
+  static constexpr size_t ES = sizeof(T);
+  static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
+  // R1: Gf (fp32 [BT][LDF]) | X (fp32 [BT][LDA]) + M ([BT][LDJ], backward)
+  static constexpr size_t X_SZ = al(size_t(BT) * LDA * 4), ML_SZ = al(size_t(BT) * LDJ * ES);
+  static constexpr size_t R1 = cmax(al(size_t(BT) * LDF * 4), X_SZ + ML_SZ);
+  static constexpr size_t O_GF = 0, O_X = 0, O_ML = X_SZ;
+  // four operand slots, reused after the A/M products:
+  //   S0: Kr -> K~ (-> W, backward)   S1: Qr -> Q~ (backward)   S2: Kc0 -> V   S3: Kcd -> KhT
+  static constexpr size_t SLOT = al(cmax(size_t(BT) * LDK * ES, size_t(BT) * LDV * ES));
+  static constexpr size_t O_S0 = R1, O_S1 = O_S0 + SLOT, O_S2 = O_S1 + SLOT, O_S3 = O_S2 + SLOT, O_SX = O_S3 + SLOT;
+  // SX: Kcx (pair-scaled column operands); afterwards the tail of KhT and T
+  static constexpr size_t KHT_SZ = al(size_t(D) * LDJ * ES), TM_SZ = al(size_t(BT) * LDJ * ES);
+  static constexpr size_t O_TM = O_S3 + KHT_SZ;
+  static constexpr size_t SX = cmax(al(size_t(NPX) * 16 * LDK * ES), O_TM + TM_SZ > O_SX ? O_TM + TM_SZ - O_SX : 0);
+  static constexpr size_t O_A = O_SX + SX;  // A (fp32 [BT][LDA])
+  static constexpr size_t O_VEC = O_A + X_SZ;
   // vectors (fp32): Tv[NB][D], Fv[NB+1][D], EF[NB+1][D], EH[NB][D], Sx[NPX][D], bet[BT]
-  static constexpr size_t VEC_OFF = R2_OFF + R2;
   static constexpr size_t TV = 0, FV = TV + NB * D, EF = FV + (NB + 1) * D, EH = EF + (NB + 1) * D,
-                          SX = EH + NB * D, BET = SX + (NPX > 0 ? NPX : 1) * D;
-  static constexpr size_t VEC = (BET + BT) * 4;
-  static constexpr size_t TOTAL = VEC_OFF + VEC;
+                          SXV = EH + NB * D, BET = SXV + (NPX > 0 ? NPX : 1) * D;
+  static constexpr size_t TOTAL = O_VEC + (BET + BT) * 4;
   static_assert(TOTAL <= 160 * 1024, "prep kernel LDS budget");
 };
 
+// Register-resident global inputs of one (chunk, head) item.  Thread tid owns the
+// 16-byte pieces p = tid + CNT * x of the [BT][D] key/query/gate tiles (row p / NPR)
+// and of the [BT][DV] value tile.  Gates, keys, queries and beta are fetched one item
+// ahead; values are fetched at the start of their own item (first used halfway).
+template <typename T, int BT, int D, int DV>
+struct PrepIn {
+  static constexpr int VN = 16 / sizeof(T);
+  static constexpr int NPR = D / VN, NPK = BT * NPR, NK = (NPK + CNT - 1) / CNT;
+  static constexpr int NPRV = DV / VN, NPV = BT * NPRV, NV = (NPV + CNT - 1) / CNT;
+  static constexpr bool SAMEV = NPR == NPRV;  // value pieces sit on the key pieces' rows
+  f32x4 g[NK], k[NK], q[NK];
+  T beta;
+};
+template <typename T, int BT, int D, int DV>
+struct PrepRows {
+  using P = PrepIn<T, BT, D, DV>;
+  int rk[P::NK], rv_[P::SAMEV ? 1 : P::NV], rb;
+  __device__ __forceinline__ int rv(int x) const {
+    if constexpr (P::SAMEV) return rk[x];
+    else return rv_[x];
+  }
+};
+
+// Loads are unconditional (clamped to a valid row) so that no register of an in-flight
+// load is written on another path, which would force an early wait; padding rows
+// are masked where the values are used.
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void prep_rows(PrepRows<T, BT, D, DV>& r, const int32_t* crows, int chunk, int tid) {
+  using P = PrepIn<T, BT, D, DV>;
+  const int32_t* cr = crows + size_t(chunk) * BT;
+#pragma unroll
+  for (int x = 0; x < P::NK; ++x) {
+    const int p = tid + CNT * x;
+    r.rk[x] = cr[(p < P::NPK ? p : P::NPK - 1) / P::NPR];
+  }
+  if constexpr (!P::SAMEV) {
+#pragma unroll
+    for (int x = 0; x < P::NV; ++x) {
+      const int p = tid + CNT * x;
+      r.rv_[x] = cr[(p < P::NPV ? p : P::NPV - 1) / P::NPRV];
+    }
+  }
+  r.rb = cr[tid < BT ? tid : BT - 1];
+}
+
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void prep_load(PrepIn<T, BT, D, DV>& o, const PrepRows<T, BT, D, DV>& r, const RoundArgs& a,
+                                          int h, int H, int tid) {
+  using P = PrepIn<T, BT, D, DV>;
+#pragma unroll
+  for (int x = 0; x < P::NK; ++x) {
+    const int c0 = ((tid + CNT * x) % P::NPR) * P::VN;
+    const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+    o.q[x] = ldq(static_cast<const T*>(a.q) + off);
+  }
+  o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
+}
+
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void prep_load_v(f32x4* v, const PrepRows<T, BT, D, DV>& r, const RoundArgs& a, int h, int H,
+                                            int tid) {
+  using P = PrepIn<T, BT, D, DV>;
+#pragma unroll
+  for (int x = 0; x < P::NV; ++x) {
+    const int c0 = ((tid + CNT * x) % P::NPRV) * P::VN;
+    const int rr = r.rv(x);
+    v[x] = ldq(static_cast<const T*>(a.v) + (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0);
+  }
+}
+
 // ------------------------------------------------------------------------------------------
-// Per-chunk preparation.  One workgroup (4 waves) per (chunk, head).
+// Per-chunk preparation.  Persistent: one workgroup of CNT threads per CU walks the
+// (chunk, head) items of the round; the next item's rows and inputs are fetched into
+// registers while the current item computes.
 template <typename T, int BT, int D, int DV, bool BWD>
-__global__ __launch_bounds__(256) void kda_prep_kernel(RoundArgs a, int H) {
+__global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   using Ly = PrepLayout<T, BT, D, DV>;
+  using In = PrepIn<T, BT, D, DV>;
+  using Rows = PrepRows<T, BT, D, DV>;
   using MM = Mma<T>;
-  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDJ = Ly::LDJ, LDV = Ly::LDV, LDF = Ly::LDF, LDA = Ly::LDA;
-  constexpr int VN = 16 / sizeof(T);
+  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDV = Ly::LDV, LDJ = Ly::LDJ, LDF = Ly::LDF, LDA = Ly::LDA;
+  constexpr int VN = In::VN, NK = In::NK, NV = In::NV, NPR = In::NPR, NPRV = In::NPRV;
   __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
-  float* Gf = reinterpret_cast<float*>(smem + Ly::R1_OFF);
-  float* X = Gf;
-  float* Tmp = X + BT * LDA;
-  T* Vl = reinterpret_cast<T*>(smem + Ly::R1_OFF);
-  T* Wl = reinterpret_cast<T*>(smem + Ly::R1_OFF + size_t(BT) * LDV * sizeof(T));
-  float* Am = reinterpret_cast<float*>(smem + Ly::AM_OFF);
-  T* Ml = reinterpret_cast<T*>(smem + Ly::AM_OFF);
-  char* r2 = smem + Ly::R2_OFF;
-  T* Kr = reinterpret_cast<T*>(r2 + Ly::KR);
-  T* Qr = reinterpret_cast<T*>(r2 + Ly::QR);
-  T* Kc0 = reinterpret_cast<T*>(r2 + Ly::KC0);
-  T* Kcd = reinterpret_cast<T*>(r2 + Ly::KCD);
-  T* Kcx = reinterpret_cast<T*>(r2 + Ly::KCX);
-  T* KhT = reinterpret_cast<T*>(r2 + Ly::KHT);
-  T* Tm = reinterpret_cast<T*>(r2 + Ly::TM);
-  float* vec = reinterpret_cast<float*>(smem + Ly::VEC_OFF);
+  float* Gf = reinterpret_cast<float*>(smem + Ly::O_GF);
+  float* Xf = reinterpret_cast<float*>(smem + Ly::O_X);
+  T* Ml = reinterpret_cast<T*>(smem + Ly::O_ML);
+  T* Kr = reinterpret_cast<T*>(smem + Ly::O_S0);
+  T* Kt = Kr;  // K~ after the products, then W (backward)
+  T* Qr = reinterpret_cast<T*>(smem + Ly::O_S1);
+  T* Kc0 = reinterpret_cast<T*>(smem + Ly::O_S2);
+  T* Vl = Kc0;
+  T* Kcd = reinterpret_cast<T*>(smem + Ly::O_S3);
+  T* KhT = Kcd;
+  T* Kcx = reinterpret_cast<T*>(smem + Ly::O_SX);
+  T* Tm = reinterpret_cast<T*>(smem + Ly::O_TM);
+  float* Af = reinterpret_cast<float*>(smem + Ly::O_A);
+  float* vec = reinterpret_cast<float*>(smem + Ly::O_VEC);
   float* Tv = vec + Ly::TV;
   float* Fv = vec + Ly::FV;
   float* EF = vec + Ly::EF;
   float* EH = vec + Ly::EH;
-  float* Sx = vec + Ly::SX;
+  float* Sx = vec + Ly::SXV;
   float* bet = vec + Ly::BET;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
-  const ChunkDesc cd = a.chunks[chunk];
-  const int len = cd.len;
-  const size_t wsi = size_t(cd.local) * H + h;
-  const T* gq = static_cast<const T*>(a.q);
-  const T* gk = static_cast<const T*>(a.k);
-  const T* gv = static_cast<const T*>(a.v);
-  const T* gg = static_cast<const T*>(a.g);
-  const T* gb = static_cast<const T*>(a.beta);
-  const int32_t* vr = a.vrows + cd.vbase;
+  const int tid0 = threadIdx.x;
+  const int nitems = a.nchunk * H;
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  Rows rows, rows_n, rows_nn;  // current item (masks), next item, the one after
+  In cur, nxt;
+  prep_rows<T, BT, D, DV>(rows, a.crows, item / H, tid0);
+  prep_load<T, BT, D, DV>(cur, rows, a, item % H, H, tid0);
+  int item_n = item + gridDim.x;
+  prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_n < nitems ? item_n : item) / H, tid0);
 
-  // 1. g -> Gf (fp32), beta
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-    float v[VN];
-    if (i < len) ld16(gg + (size_t(vr[i]) * H + h) * D + c0, v);
-    else
+  for (; item < nitems; item += gridDim.x) {
+    // thread-derived addresses are recomputed per item instead of being held across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int h = item % H;
+    const size_t wsi = size_t(item);  // (round-local chunk) * H + head
+    // this item's values; fetch ahead: inputs of the next item, rows of the one after
+    f32x4 vv[NV];
+    prep_load_v<T, BT, D, DV>(vv, rows, a, h, H, tid);
+    prep_load<T, BT, D, DV>(nxt, rows_n, a, (item_n < nitems ? item_n : item) % H, H, tid);
+    const int item_nn = item_n + gridDim.x;
+    prep_rows<T, BT, D, DV>(rows_nn, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
+
+    // 1. g -> Gf (fp32), beta
 #pragma unroll
-      for (int t = 0; t < VN; ++t) v[t] = 0.f;
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + CNT * x;
+      if (p < In::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN;
+        float gv[VN];
+        unpack16<T>(rows.rk[x] >= 0 ? cur.g[x] : f32x4{0.f, 0.f, 0.f, 0.f}, gv);
 #pragma unroll
-    for (int t = 0; t < VN; ++t) Gf[i * LDF + c0 + t] = v[t];
-  }
-  if (tid < BT) bet[tid] = tid < len ? to_f(gb[size_t(vr[tid]) * H + h]) : 0.f;
-  __syncthreads();
-  // 2. block-local cumulative sums L, block totals, entry log-decays and scale vectors
-  for (int idx = tid; idx < NB * D; idx += 256) {
-    const int b = idx / D, c = idx % D;
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      acc += Gf[(16 * b + t) * LDF + c];
-      Gf[(16 * b + t) * LDF + c] = acc;
+        for (int t = 0; t < VN; t += 4)
+          stq(Gf + i * LDF + c0 + t, f32x4{gv[t], gv[t + 1], gv[t + 2], gv[t + 3]});
+      }
     }
-    Tv[b * D + c] = acc;
-  }
-  __syncthreads();
-  for (int c = tid; c < D; c += 256) {
-    float f = 0.f;
-    Fv[c] = 0.f;
-    EF[c] = 1.f;
-    for (int b = 0; b < NB; ++b) {
-      f += Tv[b * D + c];
-      Fv[(b + 1) * D + c] = f;
-      EF[(b + 1) * D + c] = __expf(f);
-    }
-    for (int b = 0; b < NB; ++b) EH[b * D + c] = __expf(f - Fv[(b + 1) * D + c]);
-  }
-  __syncthreads();
-  if constexpr (Ly::NPX > 0) {
-    for (int idx = tid; idx < Ly::NPX * D; idx += 256) {
-      const int p = idx / D, c = idx % D;
-      int bi = 2, rem = p;
-      while (rem >= bi - 1) { rem -= bi - 1; ++bi; }
-      const int bj = rem;
-      Sx[p * D + c] = __expf(Fv[bi * D + c] - Fv[(bj + 1) * D + c]);
-    }
-  }
-  __syncthreads();
-  // 3. operand arrays: Kr = k e^L, Qr = q e^L, Kc0 = k e^{T_b - L}, Kcd = k e^{-L}, Kcx = Kc0 * pair scale
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, b = i / 16;
-    float kk[VN], qq[VN];
-    if (i < len) {
-      ld16(gk + (size_t(vr[i]) * H + h) * D + c0, kk);
-      ld16(gq + (size_t(vr[i]) * H + h) * D + c0, qq);
-    } else {
+    if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
+    __syncthreads();
+    // 2. block-local cumulative sums L and block totals
+    HARTS_STRIDED(idx, tid, NB * D, CNT) {
+      const int b = idx / D, c = idx % D;
+      float v[16];
 #pragma unroll
-      for (int t = 0; t < VN; ++t) kk[t] = qq[t] = 0.f;
-    }
-    float kr[VN], qr[VN], kc[VN], kd[VN];
+      for (int t = 0; t < 16; ++t) v[t] = Gf[(16 * b + t) * LDF + c];
+      float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < VN; ++t) {
-      const float Lv = Gf[i * LDF + c0 + t];
-      const float er = __expf(Lv);
-      kr[t] = kk[t] * er;
-      qr[t] = qq[t] * er;
-      kc[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lv);
-      kd[t] = kk[t] * __expf(-Lv);
+      for (int t = 0; t < 16; ++t) {
+        acc += v[t];
+        Gf[(16 * b + t) * LDF + c] = acc;
+      }
+      Tv[b * D + c] = acc;
     }
-    st16(Kr + i * LDK + c0, kr);
-    st16(Qr + i * LDK + c0, qr);
-    st16(Kc0 + i * LDK + c0, kc);
-    st16(Kcd + i * LDK + c0, kd);
-    for (int bi = b + 2; bi < NB; ++bi) {
-      const int p = pair_index(bi, b);
-      float x[VN];
+    __syncthreads();
+    // 3. per channel: block entry log-decays F_b, e^{F_b}, e^{F_end - F_{b+1}}, pair scales
+    HARTS_STRIDED(c, tid, D, CNT) {
+      float f = 0.f, fv[NB + 1];
+      fv[0] = 0.f;
+      Fv[c] = 0.f;
+      EF[c] = 1.f;
 #pragma unroll
-      for (int t = 0; t < VN; ++t) x[t] = kc[t] * Sx[p * D + c0 + t];
-      st16(Kcx + (p * 16 + i - 16 * b) * LDK + c0, x);
+      for (int b = 0; b < NB; ++b) {
+        f += Tv[b * D + c];
+        fv[b + 1] = f;
+        Fv[(b + 1) * D + c] = f;
+        EF[(b + 1) * D + c] = __expf(f);
+      }
+#pragma unroll
+      for (int b = 0; b < NB; ++b) EH[b * D + c] = __expf(f - fv[b + 1]);
+#pragma unroll
+      for (int bi = 2; bi < NB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj + 2 <= bi; ++bj) Sx[pair_index(bi, bj) * D + c] = __expf(fv[bi] - fv[bj + 1]);
     }
-  }
-  __syncthreads();
-  // 4. A (strict lower) into Am; M (lower incl.) to global, one 16x16 tile per sub-block pair
-  T* Mg = static_cast<T*>(a.ws.Mm) + wsi * BT * BT;
-  {
-    constexpr int NT = NB * (NB + 1) / 2;
-    for (int jb = wave; jb < 2 * NT; jb += 4) {
-      const bool isM = jb >= NT;
-      const int t = isM ? jb - NT : jb;
-      int bi = 0;
-      while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
-      const int bj = t - bi * (bi + 1) / 2;
-      const T* col = bi == bj ? Kcd + 16 * bj * LDK
-                     : (bi - bj == 1 ? Kc0 + 16 * bj * LDK : Kcx + pair_index(bi, bj) * 16 * LDK);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      if (!isM) {
-        for (int k0 = 0; k0 < D; k0 += MM::KS)
-          acc = MM::mma(MM::kc(Kr + 16 * bi * LDK, LDK, 0, k0, lane), MM::kc(col, LDK, 0, k0, lane), acc);
+    __syncthreads();
+    // 4. operand arrays: Kr = k e^L, Qr = q e^L, Kc0 = k e^{T_b - L}, Kcd = k e^{-L}, Kcx = Kc0 * pair scale.
+    //    L stays in registers for step 6.
+    float Lr[NK][VN];
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int i = 16 * bi + crow(lane, r), j = 16 * bj + ccol(lane);
-          Am[i * LDA + j] = (bi == bj && i <= j) ? 0.f : acc[r];
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + CNT * x;
+      if (p < In::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN, b = i / 16;
+        float kk[VN], qq[VN], kr[VN], qr[VN], kc[VN], kd[VN];
+        unpack16<T>(rows.rk[x] >= 0 ? cur.k[x] : z4, kk);
+        unpack16<T>(rows.rk[x] >= 0 ? cur.q[x] : z4, qq);
+#pragma unroll
+        for (int t = 0; t < VN; ++t) {
+          const float Lv = Gf[i * LDF + c0 + t];
+          Lr[x][t] = Lv;
+          const float er = __expf(Lv);
+          kr[t] = kk[t] * er;
+          qr[t] = qq[t] * er;
+          kc[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lv);
+          kd[t] = kk[t] * __expf(-Lv);
+        }
+        stq(Kr + i * LDK + c0, pack16<T>(kr));
+        stq(Qr + i * LDK + c0, pack16<T>(qr));
+        stq(Kc0 + i * LDK + c0, pack16<T>(kc));
+        stq(Kcd + i * LDK + c0, pack16<T>(kd));
+        for (int bi = b + 2; bi < NB; ++bi) {
+          const int pp = pair_index(bi, b);
+          float xs[VN];
+#pragma unroll
+          for (int t = 0; t < VN; ++t) xs[t] = kc[t] * Sx[pp * D + c0 + t];
+          stq(Kcx + (pp * 16 + i - 16 * b) * LDK + c0, pack16<T>(xs));
         }
       } else {
-        for (int k0 = 0; k0 < D; k0 += MM::KS)
-          acc = MM::mma(MM::kc(col, LDK, 0, k0, lane), MM::kc(Qr + 16 * bi * LDK, LDK, 0, k0, lane), acc);
-        const int i = 16 * bi + ccol(lane), j0 = 16 * bj + crow(lane, 0);
-        float v[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
-        store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
+        for (int t = 0; t < VN; ++t) Lr[x][t] = 0.f;
       }
     }
-    for (int idx = tid; idx < BT * BT; idx += 256) {
-      const int i = idx / BT, j = idx % BT;
-      if (j / 16 > i / 16) Mg[idx] = from_f<T>(0.f);
-    }
-  }
-  __syncthreads();
-  // 5. X = (I + diag(beta) A)^{-1}: diagonal 16x16 blocks by forward substitution,
-  //    then X_{bi,bj} = -X_{bi,bi} sum_{m=bj}^{bi-1} L_{bi,m} X_{m,bj} by increasing distance.
-  for (int idx = tid; idx < BT * LDA; idx += 256) X[idx] = 0.f;
-  __syncthreads();
-  if (tid < NB * 16) {
-    const int b = tid / 16, col = tid % 16;
-    float x[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float s = 0.f;
-#pragma unroll
-      for (int m = 0; m < 16; ++m)
-        if (m < r) s += Am[(16 * b + r) * LDA + 16 * b + m] * x[m];
-      x[r] = r < col ? 0.f : (r == col ? 1.f : -bet[16 * b + r] * s);
-    }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) X[(16 * b + r) * LDA + 16 * b + col] = x[r];
-  }
-  __syncthreads();
-  for (int dd = 1; dd < NB; ++dd) {
-    for (int idx = tid; idx < (NB - dd) * 256; idx += 256) {
-      const int bj = idx / 256, e = idx % 256, bi = bj + dd;
-      const int i = 16 * bi + e / 16, j = 16 * bj + e % 16;
-      float s = 0.f;
-      for (int mm = 16 * bj; mm < 16 * bi; ++mm) s += Am[i * LDA + mm] * X[mm * LDA + j];
-      Tmp[i * LDA + j] = bet[i] * s;
-    }
     __syncthreads();
-    for (int idx = tid; idx < (NB - dd) * 256; idx += 256) {
-      const int bj = idx / 256, e = idx % 256, bi = bj + dd;
-      const int i = 16 * bi + e / 16, j = 16 * bj + e % 16;
-      float s = 0.f;
+    // 5. A (strict lower, fp32) into Af; M (lower incl.) to the workspace (and Ml), one 16x16 tile each
+    T* Mg = static_cast<T*>(a.ws.Mm) + wsi * BT * BT;
+    {
+      constexpr int NTA = NB * (NB + 1) / 2, NTT = NTA + NB * NB;
+      HARTS_STRIDED(jb, wave, NTT, CNW) {
+        if (jb < NTA) {
+          int bi = 0;
+          while ((bi + 1) * (bi + 2) / 2 <= jb) ++bi;
+          const int bj = jb - bi * (bi + 1) / 2;
+          const T* col = bi == bj ? Kcd + 16 * bj * LDK
+                         : (bi - bj == 1 ? Kc0 + 16 * bj * LDK : Kcx + pair_index(bi, bj) * 16 * LDK);
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < 16; ++t) s += X[i * LDA + 16 * bi + t] * Tmp[(16 * bi + t) * LDA + j];
-      X[i * LDA + j] = -s;
-    }
-    __syncthreads();
-  }
-  // 6. T = X diag(beta); K~ = Kr e^{F_b}, Q~ = Qr e^{F_b} in place; KhT = (Kc0 e^{F_end - F_{b+1}})^T
-  for (int idx = tid; idx < BT * BT; idx += 256) {
-    const int i = idx / BT, j = idx % BT;
-    const float tv = j <= i ? X[i * LDA + j] * bet[j] : 0.f;
-    Tm[i * LDJ + j] = from_f<T>(tv);
-    if (BWD) {
-      // T, X and A for the gradient kernels
-      static_cast<T*>(a.ws.Tm)[wsi * BT * BT + idx] = from_f<T>(tv);
-      static_cast<T*>(a.ws.Xm)[wsi * BT * BT + idx] = from_f<T>(j <= i ? X[i * LDA + j] : 0.f);
-      static_cast<T*>(a.ws.Am)[wsi * BT * BT + idx] = from_f<T>(j < i ? Am[i * LDA + j] : 0.f);
-    }
-  }
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, b = i / 16;
-    float kr[VN], qr[VN], kc[VN];
-    ld16(Kr + i * LDK + c0, kr);
-    ld16(Qr + i * LDK + c0, qr);
-    ld16(Kc0 + i * LDK + c0, kc);
+          for (int k0 = 0; k0 < D; k0 += MM::KS)
+            acc = MM::mma(MM::kc(Kr + 16 * bi * LDK, LDK, 0, k0, lane), MM::kc(col, LDK, 0, k0, lane), acc);
 #pragma unroll
-    for (int t = 0; t < VN; ++t) {
-      const float ef = EF[b * D + c0 + t];
-      kr[t] *= ef;
-      qr[t] *= ef;
-      kc[t] *= EH[b * D + c0 + t];
-    }
-    st16(Kr + i * LDK + c0, kr);
-    st16(Qr + i * LDK + c0, qr);
+          for (int r = 0; r < 4; ++r) {
+            const int i = 16 * bi + crow(lane, r), j = 16 * bj + ccol(lane);
+            Af[i * LDA + j] = (bi == bj && i <= j) ? 0.f : acc[r];
+          }
+        } else {
+          const int t = jb - NTA, bi = t / NB, bj = t % NB;
+          const int i = 16 * bi + ccol(lane), j0 = 16 * bj + crow(lane, 0);
+          float v[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bj <= bi) {
+            const T* col = bi == bj ? Kcd + 16 * bj * LDK
+                           : (bi - bj == 1 ? Kc0 + 16 * bj * LDK : Kcx + pair_index(bi, bj) * 16 * LDK);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kc[t]);
-  }
-  __syncthreads();
-  // 7. V into R1; K~ stays in Kr, Q~ in Qr.  Copy KhT, Q~ (forward) and e^{G_last} out.
-  for (int idx = tid; idx < BT * (DV / VN); idx += 256) {
-    const int i = idx / (DV / VN), c0 = (idx % (DV / VN)) * VN;
-    if (i < len) copy16(Vl + i * LDV + c0, gv + (size_t(vr[i]) * H + h) * DV + c0);
-    else *reinterpret_cast<f32x4*>(Vl + i * LDV + c0) = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  {
-    T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
-    for (int idx = tid; idx < D * (BT / VN); idx += 256) {
-      const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
-      copy16(khg + c * BT + i0, KhT + c * LDJ + i0);
-    }
-    if (!BWD) {
-      T* qg = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
-      for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-        const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-        copy16(qg + i * D + c0, Qr + i * LDK + c0);
+            for (int k0 = 0; k0 < D; k0 += MM::KS)
+              acc = MM::mma(MM::kc(col, LDK, 0, k0, lane), MM::kc(Qr + 16 * bi * LDK, LDK, 0, k0, lane), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
+          }
+          store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
+          if (BWD) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
+        }
       }
     }
-    for (int c = tid; c < D; c += 256) a.ws.El[wsi * D + c] = EF[NB * D + c];
-  }
-  __syncthreads();
-  // 8. U' = T V, stored transposed: UpT[jv][i]
-  {
-    T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
-    constexpr int MT = BT / 16, NT = DV / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mt = jb / NT, nt = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
-      store4(upg + (16 * nt + ccol(lane)) * BT + 16 * mt + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  // 9. W^T = K~^T T^T (tile rows = channels), stored token-major: W[i][c]
-  {
-    T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
-    constexpr int MT = D / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mt = jb / NT, nt = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::rc(Kr, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), acc);
-      const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-      store4(wg + i * D + c0, acc[0], acc[1], acc[2], acc[3]);
-      if (BWD) store4(Wl + i * LDK + c0, acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  if constexpr (BWD) {
-    // 10. Qeff = Q~ - M W, stored transposed: QeffT[c][i]
     __syncthreads();
-    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
-      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
-      copy16(Ml + i * LDJ + j0, Mg + i * BT + j0);
-    }
-    __syncthreads();
-    T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
-    constexpr int MT = BT / 16, NT = D / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mt = jb / NT, nt = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Wl, LDK, 16 * nt, k0, lane), acc);
-      const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0);
-      float v[4];
+    // 6a. diagonal 16x16 blocks of X = (I + diag(beta) A)^{-1} by forward substitution
+    if (wave < NB && lane < 16) {
+      const int b = wave, col = lane;
+      float xv[16];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
-      store4(qe + c * BT + i0, v[0], v[1], v[2], v[3]);
+      for (int r = 0; r < 16; ++r) {
+        float s = 0.f;
+#pragma unroll
+        for (int m = 0; m < r; ++m) s += Af[(16 * b + r) * LDA + 16 * b + m] * xv[m];
+        xv[r] = r < col ? 0.f : (r == col ? 1.f : -bet[16 * b + r] * s);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Xf[(16 * b + r) * LDA + 16 * b + col] = xv[r];
     }
+    // 6b. K~ = k e^G, K^ = k e^{G_last - G} (transposed), Q~ = q e^G, V; e^{G_last}
+#pragma unroll
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + CNT * x;
+      if (p < In::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN, b = i / 16;
+        float kk[VN], qq[VN], kt[VN], qt[VN], kh[VN];
+        unpack16<T>(rows.rk[x] >= 0 ? cur.k[x] : z4, kk);
+        unpack16<T>(rows.rk[x] >= 0 ? cur.q[x] : z4, qq);
+#pragma unroll
+        for (int t = 0; t < VN; ++t) {
+          const float er = __expf(Lr[x][t]), ef = EF[b * D + c0 + t];
+          kt[t] = kk[t] * er * ef;
+          qt[t] = qq[t] * er * ef;
+          kh[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lr[x][t]) * EH[b * D + c0 + t];
+        }
+        stq(Kt + i * LDK + c0, pack16<T>(kt));
+        if (BWD) stq(Qr + i * LDK + c0, pack16<T>(qt));
+        else stq(static_cast<T*>(a.ws.Qt) + wsi * BT * D + i * D + c0, pack16<T>(qt));
+#pragma unroll
+        for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kh[t]);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int p = tid + CNT * x;
+      if (p < In::NPV) stq(Vl + (p / NPRV) * LDV + (p % NPRV) * VN, rows.rv(x) >= 0 ? vv[x] : z4);
+    }
+    HARTS_STRIDED(c, tid, D, CNT) a.ws.El[wsi * D + c] = EF[NB * D + c];
+    __syncthreads();
+    // 7. off-diagonal blocks of X, column block j per wave, with fp32 matrix cores:
+    //    X_ij = -X_ii sum_{m=j}^{i-1} diag(beta_i) A_im X_mj; then T = X diag(beta) (bf16/fp32) into Tm.
+    if (wave < NB) {
+      const int j = wave, lr = lane & 15, lg = lane >> 4;
+      f32x4 xb[NB];
+#pragma unroll
+      for (int m = 0; m < NB; ++m) xb[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xb[j][s] = Xf[(16 * j + 4 * lg + s) * LDA + 16 * j + lr];
+#pragma unroll
+      for (int i = 1; i < NB; ++i) {
+        if (i <= j) continue;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const float bi = bet[16 * i + lr];
+#pragma unroll
+        for (int m = 0; m < NB; ++m) {
+          if (m < j || m >= i) continue;
+          f32x4 pa = ldq(Af + (16 * i + lr) * LDA + 16 * m + 4 * lg);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) pa[s] *= bi;
+          acc = mma16_f32(pa, xb[m], acc);
+        }
+        const f32x4 pd = ldq(Xf + (16 * i + lr) * LDA + 16 * i + 4 * lg);
+        const f32x4 r2 = mma16_f32(pd, acc, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          xb[i][s] = -r2[s];
+          Xf[(16 * i + 4 * lg + s) * LDA + 16 * j + lr] = -r2[s];
+        }
+      }
+      const float bc = bet[16 * j + lr];
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          Tm[(16 * i + 4 * lg + s) * LDJ + 16 * j + lr] = from_f<T>(i < j ? 0.f : xb[i][s] * bc);
+    }
+    __syncthreads();
+    // 8. U' = T V (stored transposed), W = T K~ (token-major), KhT out; backward: T, X, A out
+    {
+      T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
+      T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
+      constexpr int NU = (BT / 16) * (DV / 16), NW = (D / 16) * (BT / 16);
+      constexpr int NWW = BWD ? (NW + CNW - 1) / CNW : 1;
+      f32x4 wacc[NWW];  // backward keeps W for the Qeff product
+      HARTS_STRIDED(jb, wave, NU, CNW) {
+        constexpr int NT = DV / 16;
+        const int mt = jb / NT, nt = jb % NT;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k0 = 0; k0 < BT; k0 += MM::KS)
+          acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
+        store4(upg + (16 * nt + ccol(lane)) * BT + 16 * mt + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
+      }
+      if constexpr (BWD) {
+#pragma unroll
+        for (int u = 0; u < NWW; ++u) {
+          const int jb = wave + CNW * u;
+          wacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (jb < NW) {
+            constexpr int NT = BT / 16;
+            const int mt = jb / NT, nt = jb % NT;
+#pragma unroll
+            for (int k0 = 0; k0 < BT; k0 += MM::KS)
+              wacc[u] = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), wacc[u]);
+            const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
+            store4(wg + i * D + c0, wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]);
+          }
+        }
+      } else {
+        HARTS_STRIDED(jb, wave, NW, CNW) {
+          constexpr int NT = BT / 16;
+          const int mt = jb / NT, nt = jb % NT;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k0 = 0; k0 < BT; k0 += MM::KS)
+            acc = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), acc);
+          const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
+          store4(wg + i * D + c0, acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+      T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
+      HARTS_STRIDED(idx, tid, D * (BT / VN), CNT) {
+        const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
+        copy16(khg + c * BT + i0, KhT + c * LDJ + i0);
+      }
+      if constexpr (BWD) {
+        const size_t BB = size_t(BT) * BT;
+        T* tg = static_cast<T*>(a.ws.Tm) + wsi * BB;
+        T* xg = static_cast<T*>(a.ws.Xm) + wsi * BB;
+        T* ag = static_cast<T*>(a.ws.Am) + wsi * BB;
+        HARTS_STRIDED(idx, tid, BT * (BT / VN), CNT) {
+          const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
+          copy16(tg + i * BT + j0, Tm + i * LDJ + j0);
+          float xv[VN], av[VN];
+#pragma unroll
+          for (int t = 0; t < VN; ++t) {
+            xv[t] = j0 + t <= i ? Xf[i * LDA + j0 + t] : 0.f;
+            av[t] = j0 + t < i ? Af[i * LDA + j0 + t] : 0.f;
+          }
+          stq(xg + i * BT + j0, pack16<T>(xv));
+          stq(ag + i * BT + j0, pack16<T>(av));
+        }
+        __syncthreads();  // every wave is done reading K~: W takes its place
+#pragma unroll
+        for (int u = 0; u < NWW; ++u) {
+          const int jb = wave + CNW * u;
+          if (jb < NW) {
+            constexpr int NT = BT / 16;
+            const int mt = jb / NT, nt = jb % NT;
+            const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
+            store4(Kt + i * LDK + c0, wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]);
+          }
+        }
+        __syncthreads();
+        // 9. Qeff = Q~ - M W, stored transposed: QeffT[c][i]
+        T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
+        constexpr int MT = BT / 16, NT = D / 16;
+        HARTS_STRIDED(jb, wave, MT * NT, CNW) {
+          const int mt = jb / NT, nt = jb % NT;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k0 = 0; k0 < BT; k0 += MM::KS)
+            acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
+          const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0);
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
+          store4(qe + c * BT + i0, v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+    __syncthreads();  // the next item overwrites every region
+    cur = nxt;
+    rows = rows_n;
+    rows_n = rows_nn;
+    item_n = item_nn;
   }
 }
 
@@ -585,7 +724,7 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
 template <typename T, int BT, int D, int DV>
 static hipError_t prep_launch(const KdaDims& d, const RoundArgs& a, bool bwd, hipStream_t s) {
   if (a.nchunk <= 0) return hipSuccess;
-  dim3 grid(unsigned(a.nchunk) * d.H), block(256);
+  dim3 grid(persistent_grid(unsigned(a.nchunk) * d.H)), block(CNT);
   if (bwd) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, true>), grid, block, 0, s, a, d.H);
   else hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, false>), grid, block, 0, s, a, d.H);
   return hipGetLastError();

@@ -36,6 +36,7 @@ struct RoundArgs {
   const int32_t* vrows;       // global virtual-row table
   const SeqDesc* seqs;        // this round's sequences
   const ChunkDesc* chunks;    // this round's chunks
+  const int32_t* crows;       // [chunk][BT] compact row of every chunk row, -1 past the chunk's end
   int32_t nseq, nchunk;
   int32_t seq0;               // global index of this round's first sequence
   const void *q, *k, *v, *g, *beta;
@@ -58,6 +59,20 @@ struct BwdRoundArgs {
   const int32_t* slot_cons;
   float* replay_grad;         // [replay_total][H][2*D + DV + 1] fp32 (dk, dv, dg, dbeta of replayed rows)
 };
+
+// Grid of a persistent per-chunk kernel: one workgroup per compute unit of the
+// current device (at most one item per workgroup when there are fewer items).
+inline unsigned persistent_grid(unsigned items) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return items < unsigned(cus[dev]) ? items : unsigned(cus[dev]);
+}
 
 hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
