@@ -35,7 +35,7 @@ struct harts_dev_plan {
   int32_t* fix_off = nullptr;
   int32_t* fix_idx = nullptr;
   // workspace layout (byte offsets)
-  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0,
+  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0,
          off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
@@ -162,6 +162,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.dM = ws + d->off_dM;
   a.ws.dA = ws + d->off_dA;
   a.h = ws + d->off_h;
+  a.hc = ws + d->off_hc;
   return a;
 }
 
@@ -357,6 +358,8 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_Qe = take(MC * dk * BT * es);
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
+      d->off_hc = take(MC * dv * dk * es);
+      d->off_dhc = take(MC * dv * dk * es);
       d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
       d->off_rg = take(size_t(d->p.replay_total) * H * (2 * dk + dv + 1) * 4);
       d->off_Tm = take(MC * BT * BT * es);
@@ -431,6 +434,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       b.dg = g->dg;
       b.dbeta = g->dbeta;
       b.dh = ws + d->off_dh;
+      b.dhc = ws + d->off_dhc;
       b.dinit = d->p.varlen ? g->dinit : reinterpret_cast<float*>(ws + d->off_dinit);
       b.dstates = d->p.varlen ? nullptr : g->dstates;
       b.slot_cons_off = d->p.varlen ? nullptr : d->cons_off;

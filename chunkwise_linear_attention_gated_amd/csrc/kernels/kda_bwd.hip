@@ -176,11 +176,20 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
     }
     __syncthreads();
     {
-      // gradient w.r.t. the chunk-end state, for the per-chunk gradient kernels
+      // gradient w.r.t. the chunk-end state, for the per-chunk gradient kernels:
+      // value-major (dS^T) and channel-major (dS)
       T* dhg = static_cast<T*>(b.dh) + wsi * DV * D;
+      T* dhcg = static_cast<T*>(b.dhc) + wsi * D * DV;
       for (int idx = tid; idx < DVT * (D / VN); idx += 256) {
         const int jl = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
         copy16(dhg + (jvb + jl) * D + c0, dSt + jl * LDS_S + c0);
+      }
+      for (int idx = tid; idx < D * (DVT / VN); idx += 256) {
+        const int c = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
+        float v[VN];
+#pragma unroll
+        for (int t = 0; t < VN; ++t) v[t] = to_f(dSt[(j0 + t) * LDS_S + c]);
+        stq(dhcg + c * DV + jvb + j0, pack16<T>(v));
       }
     }
     // Y = K^ dS  (stored transposed)
@@ -558,280 +567,387 @@ __global__ __launch_bounds__(256) void kda_gradA_kernel(BwdRoundArgs b, int H) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Gradient kernel B (channel side): dq, dk, dg.  One workgroup per (chunk, head); wave w owns
-// token rows [16w, 16w + 16) and accumulates every contribution in registers.
-template <typename T, int BT, int D>
-struct GBLayout {
-  static constexpr int NB = BT / 16, PAD = 16 / sizeof(T);
-  static constexpr int LDK = D + PAD, LDJ = BT + PAD, LDF = D + 4;
-  static constexpr size_t sK = size_t(BT) * LDK * sizeof(T);
-  static constexpr size_t O_GF = 0, O_ARR = al16(size_t(BT) * LDF * 4);
-  static constexpr size_t ARR = al16(cmx(4 * sK, size_t(BT) * LDF * 4));  // Kr, Qr, Kc0, Kcd | staging
-  static constexpr size_t O_DM = O_ARR + ARR, O_DA = O_DM + al16(size_t(BT) * LDJ * sizeof(T));
-  static constexpr size_t O_VEC = O_DA + al16(size_t(BT) * LDJ * sizeof(T));
-  static constexpr size_t VTV = 0, VFV = VTV + NB * D, VEF = VFV + (NB + 1) * D, VEH = VEF + (NB + 1) * D,
-                          VRS = VEH + NB * D, VCS = VRS + D, VEND = VCS + 4 * D;
-  static constexpr size_t TOTAL = O_VEC + VEND * 4;
+// Gradient kernel B (channel side): dq, dk, dg.  Persistent, one workgroup of D/16 waves
+// per compute unit walking the (chunk, head) items of the round.  Wave w owns channels
+// [16w, 16w + 16) for every token of the chunk, with lane l holding, for each 16-token
+// block b, tokens 16b + 4(l/16) + r (r = 0..3) of channel 16w + l%16 -- the accumulator
+// layout of the matrix cores.  The in-chunk decay, the 16-token block products (whose
+// right operand is the lane's own values), the state products and the final reverse
+// cumulative sum of dg all stay inside the wave.  The next item's inputs (and this
+// wave's slices of S_n and dS_n) are fetched into registers while the current item computes.
+template <typename T, int BT, int D, int DV>
+struct GBCfg {
+  using MM = Mma<T>;
+  static constexpr int NW = D / 16, NT = 64 * NW, NB = BT / 16, VN = 16 / sizeof(T), PAD = VN;
+  static constexpr int NPR = D / VN, NPK = BT * NPR, NK = (NPK + NT - 1) / NT;
+  static constexpr int NPRV = DV / VN, NPV = BT * NPRV, NV = (NPV + NT - 1) / NT;
+  static constexpr int NPJ = BT * BT / VN, NJ = (NPJ + NT - 1) / NT;
+  static constexpr int NKS = DV / MM::KS;
+  static constexpr bool SAMEV = NPR == NPRV;
+  static constexpr int LDK = D + PAD, LDV = DV + PAD, LDJ = BT + PAD, LDF = D + 4;
+  static constexpr size_t ES = sizeof(T);
+  static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
+  // staged inputs (bf16/fp32): Q, K, g [BT][LDK]; dO, U, dR [BT][LDV]; dM, dA [BT][LDJ]
+  static constexpr size_t SK = al(size_t(BT) * LDK * ES), SV = al(size_t(BT) * LDV * ES), SJ = al(size_t(BT) * LDJ * ES);
+  static constexpr size_t O_Q = 0, O_K = SK, O_G = 2 * SK, O_DO = 3 * SK, O_U = O_DO + SV, O_DR = O_U + SV,
+                          O_DM = O_DR + SV, O_DA = O_DM + SJ, IN_END = O_DA + SJ;
+  // output staging (fp32 [BT][LDF] for dq, dk, dg) over the inputs once they are consumed
+  static constexpr size_t SF = al(size_t(BT) * LDF * 4);
+  static constexpr size_t TOTAL = cmx(IN_END, 3 * SF);
   static_assert(TOTAL <= 160 * 1024, "gradient kernel B LDS budget");
 };
 
-// C[16x16] += A[16 x 16] B[16 x 16] over one 16-row sub-block of the contraction.
-// AKC / BKC: operand stored with the contraction index contiguous (else gathered).
-template <typename T, bool AKC, bool BKC>
-__device__ __forceinline__ f32x4 mma_k16(const T* A, int lda, int ar0, const T* Bm, int ldb, int br0, int lane) {
-  using MM = Mma<T>;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (sizeof(T) == 2) {
-    typename MM::Frag af, bf;
-    if ((lane >> 4) < 2) {
-      af = AKC ? MM::kc(A, lda, ar0, 0, lane) : MM::rc(A, lda, ar0, 0, lane);
-      bf = BKC ? MM::kc(Bm, ldb, br0, 0, lane) : MM::rc(Bm, ldb, br0, 0, lane);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 8; ++t) af[t] = bf[t] = (bf16)0.f;
-    }
-    acc = MM::mma(af, bf, acc);
-  } else {
-#pragma unroll
-    for (int k0 = 0; k0 < 16; k0 += MM::KS)
-      acc = MM::mma(AKC ? MM::kc(A, lda, ar0, k0, lane) : MM::rc(A, lda, ar0, k0, lane),
-                    BKC ? MM::kc(Bm, ldb, br0, k0, lane) : MM::rc(Bm, ldb, br0, k0, lane), acc);
+template <typename T, int BT, int D, int DV>
+struct GBRows {
+  using C = GBCfg<T, BT, D, DV>;
+  int rk[C::NK], rv_[C::SAMEV ? 1 : C::NV], own, rbase;
+  __device__ __forceinline__ int rv(int x) const {
+    if constexpr (C::SAMEV) return rk[x];
+    else return rv_[x];
   }
-  return acc;
+};
+
+template <typename T, int BT, int D, int DV>
+struct GBIn {
+  using C = GBCfg<T, BT, D, DV>;
+  using F = typename C::MM::Frag;
+  f32x4 q[C::NK], k[C::NK], g[C::NK], dO[C::NV], u[C::NV], dr[C::NV], dm[C::NJ], da[C::NJ];
+  F hc[C::NKS], dhc[C::NKS];  // this wave's rows of S_n and dS_n as matrix-core B operands
+};
+
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void gb_rows(GBRows<T, BT, D, DV>& r, const RoundArgs& a, int chunk, int tid) {
+  using C = GBCfg<T, BT, D, DV>;
+  const int32_t* cr = a.crows + size_t(chunk) * BT;
+#pragma unroll
+  for (int x = 0; x < C::NK; ++x) {
+    const int p = tid + C::NT * x;
+    r.rk[x] = cr[(p < C::NPK ? p : C::NPK - 1) / C::NPR];
+  }
+  if constexpr (!C::SAMEV) {
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const int p = tid + C::NT * x;
+      r.rv_[x] = cr[(p < C::NPV ? p : C::NPV - 1) / C::NPRV];
+    }
+  }
+  r.own = a.chunks[chunk].own_from;
+  r.rbase = a.chunks[chunk].replay_base;
+}
+
+// Unconditional loads from clamped addresses: padding is masked where the values are used.
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, BT, D, DV>& r, const BwdRoundArgs& b,
+                                        size_t wsi, int h, int H, int tid, int wave, int lane) {
+  using C = GBCfg<T, BT, D, DV>;
+  using MM = typename C::MM;
+  const RoundArgs& a = b.r;
+#pragma unroll
+  for (int x = 0; x < C::NK; ++x) {
+    const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
+    const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+    o.q[x] = ldq(static_cast<const T*>(a.q) + off);
+    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+  }
+  const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
+  const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
+#pragma unroll
+  for (int x = 0; x < C::NV; ++x) {
+    const int p = tid + C::NT * x, pc = p < C::NPV ? p : C::NPV - 1;
+    const int c0 = (p % C::NPRV) * C::VN;
+    const int rr = r.rv(x);
+    o.dO[x] = ldq(static_cast<const T*>(b.dO) + (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0);
+    o.u[x] = ldq(ug + size_t(pc) * C::VN);
+    o.dr[x] = ldq(drg + size_t(pc) * C::VN);
+  }
+  const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BT * BT;
+  const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BT * BT;
+#pragma unroll
+  for (int x = 0; x < C::NJ; ++x) {
+    const int p = tid + C::NT * x, pc = p < C::NPJ ? p : C::NPJ - 1;
+    o.dm[x] = ldq(dmg + size_t(pc) * C::VN);
+    o.da[x] = ldq(dag + size_t(pc) * C::VN);
+  }
+  const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
+  const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    o.hc[ks] = MM::kc(hcg, DV, 16 * wave, ks * MM::KS, lane);
+    o.dhc[ks] = MM::kc(dhcg, DV, 16 * wave, ks * MM::KS, lane);
+  }
+}
+
+// C[16x16] += A B over a 16-long contraction: lane l supplies A[l%16][4(l/16) + t] and
+// B[4(l/16) + t][l%16], t = 0..3 (B is then a 16-token block of the accumulator layout).
+template <typename T>
+__device__ __forceinline__ f32x4 mma_k16(const float* av, const float* bv, f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s4;
+    const bf16x4 a4 = {(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
+    const bf16x4 b4 = {(bf16)bv[0], (bf16)bv[1], (bf16)bv[2], (bf16)bv[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a4), __builtin_bit_cast(s4, b4), c, 0, 0,
+                                                     0);
+  } else {
+    return mma16_f32(f32x4{av[0], av[1], av[2], av[3]}, f32x4{bv[0], bv[1], bv[2], bv[3]}, c);
+  }
 }
 
 template <typename T, int BT, int D, int DV>
-__global__ __launch_bounds__(256) void kda_gradB_kernel(BwdRoundArgs b, int H) {
-  using Ly = GBLayout<T, BT, D>;
-  using MM = Mma<T>;
+__global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b, int H) {
+  using C = GBCfg<T, BT, D, DV>;
+  using MM = typename C::MM;
   using G = RG<D, DV>;
-  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDJ = Ly::LDJ, LDF = Ly::LDF;
-  constexpr int VN = 16 / sizeof(T), NC = D / 16;
-  __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
+  using In = GBIn<T, BT, D, DV>;
+  using Rows = GBRows<T, BT, D, DV>;
+  constexpr int NT = C::NT, NB = C::NB, VN = C::VN, NK = C::NK, NV = C::NV, NJ = C::NJ;
+  constexpr int LDK = C::LDK, LDV = C::LDV, LDJ = C::LDJ, LDF = C::LDF, NPR = C::NPR, NPRV = C::NPRV;
+  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
+  T* Qs = reinterpret_cast<T*>(smem + C::O_Q);
+  T* Ks = reinterpret_cast<T*>(smem + C::O_K);
+  T* Gs = reinterpret_cast<T*>(smem + C::O_G);
+  T* dOs = reinterpret_cast<T*>(smem + C::O_DO);
+  T* Us = reinterpret_cast<T*>(smem + C::O_U);
+  T* dRs = reinterpret_cast<T*>(smem + C::O_DR);
+  T* dMs = reinterpret_cast<T*>(smem + C::O_DM);
+  T* dAs = reinterpret_cast<T*>(smem + C::O_DA);
+  float* stg = reinterpret_cast<float*>(smem);  // [3][BT][LDF] after the products
   const RoundArgs& a = b.r;
-  float* Gf = reinterpret_cast<float*>(smem + Ly::O_GF);
-  T* Kr = reinterpret_cast<T*>(smem + Ly::O_ARR);
-  T* Qr = Kr + BT * LDK;
-  T* Kc0 = Qr + BT * LDK;
-  T* Kcd = Kc0 + BT * LDK;
-  float* stage = reinterpret_cast<float*>(smem + Ly::O_ARR);  // [BT][LDF] after the products
-  T* dMl = reinterpret_cast<T*>(smem + Ly::O_DM);
-  T* dAl = reinterpret_cast<T*>(smem + Ly::O_DA);
-  float* vec = reinterpret_cast<float*>(smem + Ly::O_VEC);
-  float *Tv = vec + Ly::VTV, *Fv = vec + Ly::VFV, *EF = vec + Ly::VEF, *EH = vec + Ly::VEH;
-  float *rs = vec + Ly::VRS, *cs = vec + Ly::VCS;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
-  const ChunkDesc cd = a.chunks[chunk];
-  const int len = cd.len, own = cd.own_from;
-  const size_t wsi = size_t(cd.local) * H + h;
-  const int32_t* vr = a.vrows + cd.vbase;
-  const T* gq = static_cast<const T*>(a.q);
-  const T* gk = static_cast<const T*>(a.k);
-  const T* gdo = static_cast<const T*>(b.dO);
-  const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
-  const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
-  const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
-  const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
-  const size_t BB = size_t(BT) * BT;
+  const int nitems = a.nchunk * H;
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  const int tid0 = threadIdx.x;
+  Rows rows, rows_n, rows_nn;
+  In cur, nxt;
+  gb_rows<T, BT, D, DV>(rows, a, item / H, tid0);
+  gb_load<T, BT, D, DV>(cur, rows, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
+  int item_n = item + gridDim.x;
+  gb_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
 
-  chunk_decay<T, BT, D>(static_cast<const T*>(a.g), vr, len, H, h, Gf, Tv, Fv, EF, EH, tid);
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, bb = i / 16;
-    float kk[VN], qq[VN];
-    if (i < len) {
-      ld16(gk + (size_t(vr[i]) * H + h) * D + c0, kk);
-      ld16(gq + (size_t(vr[i]) * H + h) * D + c0, qq);
-    } else {
-#pragma unroll
-      for (int t = 0; t < VN; ++t) kk[t] = qq[t] = 0.f;
-    }
-    float kr[VN], qr[VN], kc[VN], kd[VN];
-#pragma unroll
-    for (int t = 0; t < VN; ++t) {
-      const float L = Gf[i * LDF + c0 + t];
-      const float er = __expf(L);
-      kr[t] = kk[t] * er;
-      qr[t] = qq[t] * er;
-      kc[t] = kk[t] * __expf(Tv[bb * D + c0 + t] - L);
-      kd[t] = kk[t] * __expf(-L);
-    }
-    st16(Kr + i * LDK + c0, kr);
-    st16(Qr + i * LDK + c0, qr);
-    st16(Kc0 + i * LDK + c0, kc);
-    st16(Kcd + i * LDK + c0, kd);
-  }
-  {
-    const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BB;
-    const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BB;
-    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
-      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
-      copy16(dMl + i * LDJ + j0, dmg + i * BT + j0);
-      copy16(dAl + i * LDJ + j0, dag + i * BT + j0);
-    }
-  }
-  // e^{G_last} rowsum(dS_end .* S0) per channel
-  for (int c = tid; c < D; c += 256) {
-    float s = 0.f;
-    for (int jv = 0; jv < DV; ++jv) s += to_f(dhg[jv * D + c]) * to_f(hg[jv * D + c]);
-    rs[c] = s * EF[NB * D + c];
-  }
-  for (int idx = tid; idx < 4 * D; idx += 256) cs[idx] = 0.f;
-  __syncthreads();
-
-  // per-wave results kept in registers for the staged writes
-  f32x4 dq_o[NC], dk_o[NC], dG_o[NC];
-  const int mi = wave;  // token block owned by this wave
-  const bool active = mi < NB;
-  if (active) {
-    f32x4 dqa[NC], X1[NC], X2[NC], X3[NC], X4[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) dqa[nc] = X1[nc] = X2[nc] = X3[nc] = X4[nc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ccl = ccol(lane);
-    // row-gated token products: sum_j P_ij k_j e^{F_mi - G_j}
-    for (int bj = 0; bj <= mi; ++bj) {
-      const T* kcol = (bj == mi ? Kcd : Kc0) + 16 * bj * LDK;
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        const float s = mi - bj >= 2 ? __expf(Fv[mi * D + 16 * nc + ccl] - Fv[(bj + 1) * D + 16 * nc + ccl]) : 1.f;
-        const f32x4 tm = mma_k16<T, true, false>(dMl + 16 * bj, LDJ, 16 * mi, kcol, LDK, 16 * nc, lane);
-        const f32x4 ta = mma_k16<T, true, false>(dAl + 16 * bj, LDJ, 16 * mi, kcol, LDK, 16 * nc, lane);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          dqa[nc][r] += s * tm[r];
-          X1[nc][r] += s * ta[r];
-        }
-      }
-    }
-    // column-gated token products: sum_i P_ij x_i e^{G_i - F_bi}, rows j of block mi
-    for (int bi = mi; bi < NB; ++bi) {
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc) {
-        const f32x4 tm = mma_k16<T, false, false>(dMl + 16 * bi * LDJ, LDJ, 16 * mi, Qr + 16 * bi * LDK, LDK, 16 * nc, lane);
-        const f32x4 ta = mma_k16<T, false, false>(dAl + 16 * bi * LDJ, LDJ, 16 * mi, Kr + 16 * bi * LDK, LDK, 16 * nc, lane);
-        if (bi == mi) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) X2[nc][r] += tm[r] + ta[r];
-        } else {
-          const float s = bi - mi >= 2 ? __expf(Fv[bi * D + 16 * nc + ccl] - Fv[(mi + 1) * D + 16 * nc + ccl]) : 1.f;
-#pragma unroll
-          for (int r = 0; r < 4; ++r) X3[nc][r] += s * (tm[r] + ta[r]);
-        }
-      }
-    }
-    // state-side products over value columns: dO S0^T, -dR S0^T (-> e^{F_b}), U dS^T (-> e^{G_last - F_{b+1}})
+  for (; item < nitems; item += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
+    const int h = item % H;
+    const size_t wsi = size_t(item);
     {
-      const int irow = 16 * mi + (lane & 15);
-      const bool ok = irow < len && irow >= own;
-      const T* dorow = gdo + (size_t(ok ? vr[irow] : 0) * H + h) * DV;
-      for (int k0 = 0; k0 < DV; k0 += MM::KS) {
-        typename MM::Frag fo;
-        if constexpr (sizeof(T) == 2) {
-          if (ok) fo = MM::kc(dorow, 0, 0, k0, lane & 48);
-          else
+      const int itn = item_n < nitems ? item_n : item;
+      gb_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
+    }
+    const int item_nn = item_n + gridDim.x;
+    gb_rows<T, BT, D, DV>(rows_nn, a, (item_nn < nitems ? item_nn : item) / H, tid);
+
+    // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int t = 0; t < 8; ++t) fo[t] = (bf16)0.f;
-        } else {
-          fo = ok ? dorow[k0 + (lane >> 4)] : 0.f;
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN;
+        const bool ok = rows.rk[x] >= 0;
+        stq(Qs + i * LDK + c0, ok ? cur.q[x] : z4);
+        stq(Ks + i * LDK + c0, ok ? cur.k[x] : z4);
+        stq(Gs + i * LDK + c0, ok ? cur.g[x] : z4);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NV; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPV) {
+        const int i = p / NPRV, c0 = (p % NPRV) * VN;
+        stq(dOs + i * LDV + c0, rows.rv(x) >= 0 && i >= rows.own ? cur.dO[x] : z4);
+        stq(Us + i * LDV + c0, cur.u[x]);
+        stq(dRs + i * LDV + c0, cur.dr[x]);
+      }
+    }
+#pragma unroll
+    for (int x = 0; x < NJ; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPJ) {
+        const int i = p / (BT / VN), j0 = (p % (BT / VN)) * VN;
+        stq(dMs + i * LDJ + j0, cur.dm[x]);
+        stq(dAs + i * LDJ + j0, cur.da[x]);
+      }
+    }
+    __syncthreads();
+
+    const int c = 16 * wave + cc;
+    // 2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
+    f32x4 dqa[NB], X1[NB], X23[NB], X4[NB];
+    float rs = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) rs += (float)cur.hc[ks][t] * (float)cur.dhc[ks][t];
+      } else {
+        rs += cur.hc[ks] * cur.dhc[ks];
+      }
+    }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
+        X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
+        X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
+      }
+    }
+    // 3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),
+    //    block totals Tb and block entry values F (F[NB] = G_last)
+    float L[NB][4], Tb[NB], F[NB + 1];
+    F[0] = 0.f;
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s += to_f(Gs[(16 * bb + 4 * g4 + r) * LDK + c]);
+        L[bb][r] = s;
+      }
+      float tot[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) tot[q] = __shfl(s, cc + 16 * q, 64);
+      float ex = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ex += q < g4 ? tot[q] : 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) L[bb][r] += ex;
+      Tb[bb] = tot[0] + tot[1] + tot[2] + tot[3];
+      F[bb + 1] = F[bb] + Tb[bb];
+    }
+    rs *= __expf(F[NB]);
+    // state-product factors: dq gets e^{F_b}, dk (row side) -e^{F_b}, dk (through K^) e^{G_last - F_{b+1}}
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const float ef = __expf(F[bb]), eh = __expf(F[NB] - F[bb + 1]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        dqa[bb][r] *= ef;
+        X1[bb][r] *= -ef;
+        X4[bb][r] *= eh;
+      }
+    }
+    // 4. 16-token block products with the gated masks factored per block pair:
+    //    row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
+    //    col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA; times e^{-L_j} later)
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj <= bi; ++bj) {
+        // row side: output block bi, contraction over block bj
+        float am[4], aa[4], bk[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          am[t] = to_f(dMs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
+          aa[t] = to_f(dAs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
+          bk[t] = to_f(Ks[(16 * bj + 4 * g4 + t) * LDK + c]) * __expf(F[bi] - F[bj] - L[bj][t]);
         }
-        const auto fr = MM::kc(drg, DV, 16 * mi, k0, lane);
-        const auto fu = MM::kc(ug, DV, 16 * mi, k0, lane);
+        dqa[bi] = mma_k16<T>(am, bk, dqa[bi]);
+        X1[bi] = mma_k16<T>(aa, bk, X1[bi]);
+        // col side: output block bj, contraction over block bi
+        float cm[4], ca[4], bq[4], bk2[4];
 #pragma unroll
-        for (int nc = 0; nc < NC; ++nc) {
-          const auto fh = MM::rc(hg, D, 16 * nc, k0, lane);
-          const auto fd = MM::rc(dhg, D, 16 * nc, k0, lane);
-          const float ef = EF[mi * D + 16 * nc + ccl], eh = EH[mi * D + 16 * nc + ccl];
-          const f32x4 t1 = MM::mma(fo, fh, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 t2 = MM::mma(fr, fh, f32x4{0.f, 0.f, 0.f, 0.f});
-          const f32x4 t3 = MM::mma(fu, fd, f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int t = 0; t < 4; ++t) {
+          cm[t] = to_f(dMs[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);
+          ca[t] = to_f(dAs[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);
+          const float e = __expf(L[bi][t] + F[bi] - F[bj]);
+          bq[t] = to_f(Qs[(16 * bi + 4 * g4 + t) * LDK + c]) * e;
+          bk2[t] = to_f(Ks[(16 * bi + 4 * g4 + t) * LDK + c]) * e;
+        }
+        X23[bj] = mma_k16<T>(cm, bq, X23[bj]);
+        X23[bj] = mma_k16<T>(ca, bk2, X23[bj]);
+        __builtin_amdgcn_sched_barrier(0);  // one block pair's operands live at a time
+      }
+    // 5. assemble dq, dk, dG with exact q, k and fp32 factors
+    float csum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            dqa[nc][r] += ef * t1[r];
-            X1[nc][r] -= ef * t2[r];
-            X4[nc][r] += eh * t3[r];
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float Lv = L[bb][r];
+        const float er = __expf(Lv), ecd = __expf(-Lv), ec = __expf(Tb[bb] - Lv);
+        const float dq = er * dqa[bb][r];
+        const float krow = er * X1[bb][r], kcol = ecd * X23[bb][r] + ec * X4[bb][r];
+        const int i = 16 * bb + 4 * g4 + r;
+        const float kv = to_f(Ks[i * LDK + c]), qv = to_f(Qs[i * LDK + c]);
+        dqa[bb][r] = dq;
+        X1[bb][r] = krow + kcol;                        // dk
+        X23[bb][r] = qv * dq + kv * (krow - kcol);      // dG
+        csum += kv * ec * X4[bb][r];
+      }
+    csum += __shfl_xor(csum, 16, 64);
+    csum += __shfl_xor(csum, 32, 64);
+    // 6. dg = reverse cumulative sum of dG over the chunk, dG_last added at the last row
+    {
+      float gt[NB], after_blk = rs + csum;
+      float suf[NB][4];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        float s = 0.f;
+#pragma unroll
+        for (int r = 3; r >= 0; --r) {
+          s += X23[bb][r];
+          suf[bb][r] = s;
+        }
+        gt[bb] = s;
+      }
+#pragma unroll
+      for (int bb = NB - 1; bb >= 0; --bb) {
+        float tot[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tot[q] = __shfl(gt[bb], cc + 16 * q, 64);
+        float later = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) later += q > g4 ? tot[q] : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) X23[bb][r] = suf[bb][r] + later + after_blk;
+        after_blk += tot[0] + tot[1] + tot[2] + tot[3];
+      }
+    }
+    __syncthreads();  // staged inputs consumed: the output staging takes their place
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * bb + 4 * g4 + r;
+        stg[i * LDF + c] = dqa[bb][r];
+        stg[BT * LDF + i * LDF + c] = X1[bb][r];
+        stg[2 * BT * LDF + i * LDF + c] = X23[bb][r];
+      }
+    __syncthreads();
+    // 7. own rows to dq, dk, dg; replayed rows (dk, dg) to the side buffer
+#pragma unroll
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + NT * x;
+      const int row = rows.rk[x];
+      if (p < C::NPK && row >= 0) {
+        const int i = p / NPR, c0 = (p % NPR) * VN;
+        if (i >= rows.own) {
+          const size_t off = (size_t(row) * H + h) * D + c0;
+          stq(static_cast<T*>(b.dq) + off, pack16<T>(stg + i * LDF + c0));
+          stq(static_cast<T*>(b.dk) + off, pack16<T>(stg + BT * LDF + i * LDF + c0));
+          stq(static_cast<T*>(b.dg) + off, pack16<T>(stg + 2 * BT * LDF + i * LDF + c0));
+        } else {
+          float* rg = b.replay_grad + (size_t(rows.rbase + i) * H + h) * G::W;  // odd row stride: scalar stores
+#pragma unroll
+          for (int t = 0; t < VN; ++t) {
+            rg[G::DK + c0 + t] = stg[BT * LDF + i * LDF + c0 + t];
+            rg[G::DG + c0 + t] = stg[2 * BT * LDF + i * LDF + c0 + t];
           }
         }
       }
     }
-    // assemble dq, dk, dG with exact q, k and fp32 factors
-    float csum[NC];
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      csum[nc] = 0.f;
-      const int c = 16 * nc + ccl;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * mi + crow(lane, r);
-        const float L = Gf[i * LDF + c];
-        const float er = __expf(L), ecd = __expf(-L), ec = __expf(Tv[mi * D + c] - L);
-        float qv = 0.f, kv = 0.f;
-        if (i < len) {
-          qv = to_f(gq[(size_t(vr[i]) * H + h) * D + c]);
-          kv = to_f(gk[(size_t(vr[i]) * H + h) * D + c]);
-        }
-        const float dq = er * dqa[nc][r];
-        const float krow = er * X1[nc][r], kcol = ecd * X2[nc][r] + ec * (X3[nc][r] + X4[nc][r]);
-        dq_o[nc][r] = dq;
-        dk_o[nc][r] = krow + kcol;
-        dG_o[nc][r] = qv * dq + kv * (krow - kcol);
-        csum[nc] += kv * ec * X4[nc][r];
-      }
-    }
-    // column sums of the K^ term: reduce the 4 row groups of the wave, then across waves
-#pragma unroll
-    for (int nc = 0; nc < NC; ++nc) {
-      float v = csum[nc];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      if (lane < 16) cs[wave * D + 16 * nc + lane] = v;
-    }
+    __syncthreads();  // the next item restages every region
+    cur = nxt;
+    rows = rows_n;
+    rows_n = rows_nn;
+    item_n = item_nn;
   }
-  __syncthreads();  // products done: the operand arrays become the staging buffer
-  // staged writes: own rows to the outputs, replayed rows to the side buffer
-  auto stage_out = [&](const f32x4* vals) {
-    if (active)
-#pragma unroll
-      for (int nc = 0; nc < NC; ++nc)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) stage[(16 * mi + crow(lane, r)) * LDF + 16 * nc + ccol(lane)] = vals[nc][r];
-  };
-  auto write_rows = [&](void* out, int rg_off, bool replay) {
-    T* o = static_cast<T*>(out);
-    for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-      const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-      if (i >= len) continue;
-      if (i >= own) {
-        st16(o + (size_t(vr[i]) * H + h) * D + c0, stage + i * LDF + c0);
-      } else if (replay) {
-        float* rg = b.replay_grad + (size_t(cd.replay_base + i) * H + h) * G::W + rg_off + c0;
-#pragma unroll
-        for (int t = 0; t < VN; ++t) rg[t] = stage[i * LDF + c0 + t];
-      }
-    }
-  };
-  stage_out(dq_o);
-  __syncthreads();
-  write_rows(b.dq, 0, false);
-  __syncthreads();
-  stage_out(dk_o);
-  __syncthreads();
-  write_rows(b.dk, G::DK, true);
-  __syncthreads();
-  stage_out(dG_o);
-  __syncthreads();
-  // dG_last terms, then dg = reverse cumulative sum over the chunk
-  for (int c = tid; c < D; c += 256) {
-    float extra = rs[c];
-    for (int w = 0; w < 4; ++w) extra += cs[w * D + c];
-    float run = 0.f;
-    for (int i = BT - 1; i >= 0; --i) {
-      run += stage[i * LDF + c] + (i == BT - 1 ? extra : 0.f);
-      stage[i * LDF + c] = run;
-    }
-  }
-  __syncthreads();
-  write_rows(b.dg, G::DG, true);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -878,7 +994,9 @@ static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, int part,
   if (b.r.nchunk <= 0) return hipSuccess;
   dim3 grid(unsigned(b.r.nchunk) * d.H);
   if (part == 0) hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
-  else hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  else
+    hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
+                       dim3(GBCfg<T, BT, D, DV>::NT), 0, s, b, d.H);
   return hipGetLastError();
 }
 

@@ -611,11 +611,20 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
     }
     __syncthreads();
     if constexpr (BWD) {
+      // chunk-start state, value-major (S^T) and channel-major (S)
       T* hg = static_cast<T*>(a.h) + wsi * DV * D;
+      T* hcg = static_cast<T*>(a.hc) + wsi * D * DV;
       constexpr int VN = 16 / sizeof(T);
       for (int idx = tid; idx < DVT * (D / VN); idx += 256) {
         const int jl = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
         copy16(hg + (jvb + jl) * D + c0, Sb + jl * LDS_S + c0);
+      }
+      for (int idx = tid; idx < D * (DVT / VN); idx += 256) {
+        const int c = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
+        float v[VN];
+#pragma unroll
+        for (int t = 0; t < VN; ++t) v[t] = to_f(Sb[(j0 + t) * LDS_S + c]);
+        stq(hcg + c * DV + jvb + j0, pack16<T>(v));
       }
     }
     // (a) U = U' - W S

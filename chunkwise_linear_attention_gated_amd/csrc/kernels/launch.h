@@ -46,6 +46,7 @@ struct RoundArgs {
   float* final_pool;          // final states by SeqDesc::final_idx
   ChunkWs ws;
   void* h;                    // backward: S_n^T per chunk [chunk][H][DV][D] (nullable)
+  void* hc;                   // backward: S_n per chunk, channel-major [chunk][H][D][DV] (nullable)
 };
 
 struct BwdRoundArgs {
@@ -53,6 +54,7 @@ struct BwdRoundArgs {
   const void* dO;             // [N][H][DV]
   void *dq, *dk, *dv, *dg, *dbeta;
   void* dh;                   // dS at chunk ends, [chunk][H][DV][D]
+  void* dhc;                  // dS at chunk ends, channel-major [chunk][H][D][DV]
   float* dinit;               // per-sequence dL/d(initial state) [global seq][H][D][DV]
   float* dstates;             // per-slot gradient output (nullable)
   const int32_t* slot_cons_off;  // CSR of consumer sequences per slot (nullable for varlen)
