@@ -252,317 +252,460 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
   }
 }
 
-// ------------------------------------------------------------------------------------------
-// In-chunk cumulative log-decay, block by block (16 rows): Gf = L (block-local cumulative
-// sums), Tv = block totals, Fv = entry log-decays, EF = e^{F}, EH = e^{F_end - F_{b+1}}.
-template <typename T, int BT, int D>
-__device__ void chunk_decay(const T* gg, const int32_t* vr, int len, int H, int h, float* Gf, float* Tv, float* Fv,
-                            float* EF, float* EH, int tid) {
-  constexpr int NB = BT / 16, VN = 16 / sizeof(T), LDF = D + 4;
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-    float v[VN];
-    if (i < len) ld16(gg + (size_t(vr[i]) * H + h) * D + c0, v);
-    else
-#pragma unroll
-      for (int t = 0; t < VN; ++t) v[t] = 0.f;
-#pragma unroll
-    for (int t = 0; t < VN; ++t) Gf[i * LDF + c0 + t] = v[t];
-  }
-  __syncthreads();
-  for (int idx = tid; idx < NB * D; idx += 256) {
-    const int bb = idx / D, c = idx % D;
-    float acc = 0.f;
-#pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      acc += Gf[(16 * bb + t) * LDF + c];
-      Gf[(16 * bb + t) * LDF + c] = acc;
-    }
-    Tv[bb * D + c] = acc;
-  }
-  __syncthreads();
-  for (int c = tid; c < D; c += 256) {
-    float f = 0.f;
-    Fv[c] = 0.f;
-    EF[c] = 1.f;
-    for (int bb = 0; bb < NB; ++bb) {
-      f += Tv[bb * D + c];
-      Fv[(bb + 1) * D + c] = f;
-      EF[(bb + 1) * D + c] = __expf(f);
-    }
-    for (int bb = 0; bb < NB; ++bb) EH[bb * D + c] = __expf(f - Fv[(bb + 1) * D + c]);
-  }
-  __syncthreads();
-}
-
 constexpr size_t al16(size_t x) { return (x + 15) / 16 * 16; }
 constexpr size_t cmx(size_t a, size_t b) { return a > b ? a : b; }
 
 // ------------------------------------------------------------------------------------------
-// Gradient kernel A (token-token side).  One workgroup per (chunk, head).  Produces dv and
-// dbeta, and the intermediates U, dR (value side) and dM, dA (token side) for kernel B.
+// C[16x16] += A B over a 16-long contraction: lane l supplies A[l%16][4(l/16) + t] and
+// B[4(l/16) + t][l%16], t = 0..3 (B is then a 16-token block of the accumulator layout).
+template <typename T>
+__device__ __forceinline__ f32x4 mma_k16(const float* av, const float* bv, f32x4 c) {
+  if constexpr (sizeof(T) == 2) {
+    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s4;
+    const bf16x4 a4 = {(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
+    const bf16x4 b4 = {(bf16)bv[0], (bf16)bv[1], (bf16)bv[2], (bf16)bv[3]};
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a4), __builtin_bit_cast(s4, b4), c, 0, 0,
+                                                     0);
+  } else {
+    return mma16_f32(f32x4{av[0], av[1], av[2], av[3]}, f32x4{bv[0], bv[1], bv[2], bv[3]}, c);
+  }
+}
+
+// Gradient kernel A (token side): dv, dbeta, and U, dR, dM, dA for kernel B.  Persistent,
+// one workgroup of DV/16 waves per compute unit walking the (chunk, head) items of the
+// round.  Wave w owns value columns [16w, 16w + 16): R = V - K~ S0, dU = M^T dO + K^ dS,
+// U = T R and dR = T^T dU are chained in the accumulator layout (lane l holds tokens
+// 16b + 4(l/16) + r of column 16w + l%16), the 16-token block products taking the lane's
+// own values as their right operand.  The token-token tail (dM, dT, dX, dL, dA, dbeta)
+// runs on tiles staged in LDS.  The next item's inputs (and this wave's slices of S_n^T
+// and dS_n^T) are fetched into registers while the current item computes.
 template <typename T, int BT, int D, int DV>
-struct GALayout {
-  static constexpr int NB = BT / 16, PAD = 16 / sizeof(T);
-  static constexpr int LDK = D + PAD, LDJ = BT + PAD, LDV = DV + PAD, LDF = D + 4, LDA = BT + 4;
-  static constexpr size_t sJ = size_t(BT) * LDJ * sizeof(T);
-  static constexpr size_t sRt = size_t(DV) * LDJ * sizeof(T);
-  static constexpr size_t R1 = al16(cmx(size_t(BT) * LDF * 4, cmx(2 * sRt, 2 * size_t(BT) * LDA * 4)));
-  static constexpr size_t RA = al16(cmx(size_t(BT) * LDK * sizeof(T), cmx(size_t(BT) * LDV * sizeof(T), size_t(BT) * LDA * 4)));
-  static constexpr size_t RB = al16(cmx(size_t(BT) * LDK * sizeof(T), cmx(size_t(BT) * LDV * sizeof(T), sJ)));
-  static constexpr size_t RT = al16(sJ), RM = al16(sJ);
-  static constexpr size_t RO = al16(cmx(size_t(BT) * LDV * sizeof(T), sJ));
-  static constexpr size_t O_R1 = 0, O_RA = O_R1 + R1, O_RB = O_RA + RA, O_RT = O_RB + RB, O_RM = O_RT + RT,
-                          O_RO = O_RM + RM, O_VEC = O_RO + RO;
-  static constexpr size_t VTV = 0, VFV = VTV + NB * D, VEF = VFV + (NB + 1) * D, VEH = VEF + (NB + 1) * D,
-                          VBET = VEH + NB * D, VDB = VBET + BT, VEND = VDB + BT;
-  static constexpr size_t TOTAL = O_VEC + VEND * 4;
+struct GACfg {
+  using MM = Mma<T>;
+  static constexpr int NW = DV / 16, NT = 64 * NW, NB = BT / 16, VN = 16 / sizeof(T), PAD = VN;
+  static constexpr int NPR = D / VN, NPK = BT * NPR, NK = (NPK + NT - 1) / NT;
+  static constexpr int NPRV = DV / VN, NPV = BT * NPRV, NV = (NPV + NT - 1) / NT;
+  static constexpr int NPJ = BT * BT / VN, NJ = (NPJ + NT - 1) / NT;
+  static constexpr int NKS = D / MM::KS;
+  static constexpr bool SAMEV = NPR == NPRV;
+  static constexpr int NPART = NT / BT;  // row groups of the dbeta_1 column sums
+  static constexpr int LDK = D + PAD, LDV = DV + PAD, LDJ = BT + PAD, LDA = BT + 4;
+  static constexpr size_t ES = sizeof(T);
+  static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
+  static constexpr size_t SKV = al(cmx(size_t(BT) * LDK * ES, size_t(BT) * LDV * ES));
+  static constexpr size_t SJ = al(size_t(BT) * LDJ * ES);
+  // R0: g -> K~ -> R -> Y1^T   R1: k -> K^ -> U -> dX   R2: v -> dU   R3: dO   R4: dR
+  static constexpr size_t O_R0 = 0, O_R1 = SKV, O_R2 = 2 * SKV, O_R3 = 3 * SKV, O_R4 = 4 * SKV;
+  // T, M (-> dT fp32 over both), X, A
+  static constexpr size_t O_T = 5 * SKV, O_M = O_T + SJ, O_X = O_M + SJ, O_A = O_X + SJ;
+  static constexpr size_t O_VEC = O_A + SJ;
+  static_assert(2 * SJ >= size_t(BT) * LDA * 4, "dT fits over T and M");
+  // vectors (fp32): beta[BT], block totals[NB][D], dbeta_1 parts[NPART][BT], dbeta_2 parts[NB][BT]
+  static constexpr size_t V_BET = 0, V_TB = BT, V_DB1 = V_TB + NB * D, V_DB2 = V_DB1 + NPART * BT,
+                          V_END = V_DB2 + NB * BT;
+  static constexpr size_t TOTAL = O_VEC + V_END * 4;
   static_assert(TOTAL <= 160 * 1024, "gradient kernel A LDS budget");
+  static_assert(NB * D <= NT, "one (block, channel) decay item per thread");
+  static_assert(NPART >= 1 && BT % NPART == 0, "dbeta_1 row groups");
 };
 
 template <typename T, int BT, int D, int DV>
-__global__ __launch_bounds__(256) void kda_gradA_kernel(BwdRoundArgs b, int H) {
-  using Ly = GALayout<T, BT, D, DV>;
-  using MM = Mma<T>;
-  using G = RG<D, DV>;
-  constexpr int NB = Ly::NB, LDK = Ly::LDK, LDJ = Ly::LDJ, LDV = Ly::LDV, LDF = Ly::LDF, LDA = Ly::LDA;
-  constexpr int VN = 16 / sizeof(T);
-  __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
-  const RoundArgs& a = b.r;
-  float* Gf = reinterpret_cast<float*>(smem + Ly::O_R1);
-  T* Rt = reinterpret_cast<T*>(smem + Ly::O_R1);                    // [DV][LDJ]  R^T
-  T* dUt = reinterpret_cast<T*>(smem + Ly::O_R1 + Ly::sRt);         // [DV][LDJ]  dU^T
-  float* dLf = reinterpret_cast<float*>(smem + Ly::O_R1);           // [BT][LDA]
-  T* Kt = reinterpret_cast<T*>(smem + Ly::O_RA);                    // [BT][LDK]  K~
-  T* Ul = reinterpret_cast<T*>(smem + Ly::O_RA);                    // [BT][LDV]  U
-  float* dTf = reinterpret_cast<float*>(smem + Ly::O_RA);           // [BT][LDA]
-  T* Kh = reinterpret_cast<T*>(smem + Ly::O_RB);                    // [BT][LDK]  K^
-  T* dRl = reinterpret_cast<T*>(smem + Ly::O_RB);                   // [BT][LDV]  dR
-  T* Y1t = reinterpret_cast<T*>(smem + Ly::O_RB);                   // [BT][LDJ]
-  T* Tl = reinterpret_cast<T*>(smem + Ly::O_RT);                    // [BT][LDJ]  T, then A
-  T* Al = Tl;
-  T* Ml = reinterpret_cast<T*>(smem + Ly::O_RM);                    // [BT][LDJ]  M, then X
-  T* Xl = Ml;
-  T* dOl = reinterpret_cast<T*>(smem + Ly::O_RO);                   // [BT][LDV]  dO, then dX
-  T* dXl = dOl;
-  float* vec = reinterpret_cast<float*>(smem + Ly::O_VEC);
-  float *Tv = vec + Ly::VTV, *Fv = vec + Ly::VFV, *EF = vec + Ly::VEF, *EH = vec + Ly::VEH;
-  float *bet = vec + Ly::VBET, *db1 = vec + Ly::VDB;
+struct GARows {
+  using C = GACfg<T, BT, D, DV>;
+  int rk[C::NK], rv_[C::SAMEV ? 1 : C::NV], rb, own, rbase;
+  __device__ __forceinline__ int rv(int x) const {
+    if constexpr (C::SAMEV) return rk[x];
+    else return rv_[x];
+  }
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int chunk = blockIdx.x / H, h = blockIdx.x % H;
-  const ChunkDesc cd = a.chunks[chunk];
-  const int len = cd.len, own = cd.own_from;
-  const size_t wsi = size_t(cd.local) * H + h;
-  const int32_t* vr = a.vrows + cd.vbase;
-  const T* gk = static_cast<const T*>(a.k);
-  const T* gv = static_cast<const T*>(a.v);
-  const T* gb = static_cast<const T*>(a.beta);
-  const T* gdo = static_cast<const T*>(b.dO);
+template <typename T, int BT, int D, int DV>
+struct GAIn {
+  using C = GACfg<T, BT, D, DV>;
+  using F = typename C::MM::Frag;
+  f32x4 k[C::NK], g[C::NK], v[C::NV], dO[C::NV], tm[C::NJ], mm[C::NJ], xm[C::NJ], am[C::NJ];
+  T beta;
+  F hf[C::NKS], dhf[C::NKS];  // this wave's rows of S_n^T and dS_n^T as matrix-core B operands
+};
+
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void ga_rows(GARows<T, BT, D, DV>& r, const RoundArgs& a, int chunk, int tid) {
+  using C = GACfg<T, BT, D, DV>;
+  const int32_t* cr = a.crows + size_t(chunk) * BT;
+#pragma unroll
+  for (int x = 0; x < C::NK; ++x) {
+    const int p = tid + C::NT * x;
+    r.rk[x] = cr[(p < C::NPK ? p : C::NPK - 1) / C::NPR];
+  }
+  if constexpr (!C::SAMEV) {
+#pragma unroll
+    for (int x = 0; x < C::NV; ++x) {
+      const int p = tid + C::NT * x;
+      r.rv_[x] = cr[(p < C::NPV ? p : C::NPV - 1) / C::NPRV];
+    }
+  }
+  r.rb = cr[tid < BT ? tid : BT - 1];
+  r.own = a.chunks[chunk].own_from;
+  r.rbase = a.chunks[chunk].replay_base;
+}
+
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, BT, D, DV>& r, const BwdRoundArgs& b,
+                                        size_t wsi, int h, int H, int tid, int wave, int lane) {
+  using C = GACfg<T, BT, D, DV>;
+  using MM = typename C::MM;
+  const RoundArgs& a = b.r;
+#pragma unroll
+  for (int x = 0; x < C::NK; ++x) {
+    const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
+    const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+  }
+#pragma unroll
+  for (int x = 0; x < C::NV; ++x) {
+    const int c0 = ((tid + C::NT * x) % C::NPRV) * C::VN;
+    const int rr = r.rv(x);
+    const size_t off = (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0;
+    o.v[x] = ldq(static_cast<const T*>(a.v) + off);
+    o.dO[x] = ldq(static_cast<const T*>(b.dO) + off);
+  }
+  const size_t BB = size_t(BT) * BT;
+#pragma unroll
+  for (int x = 0; x < C::NJ; ++x) {
+    const int p = tid + C::NT * x;
+    const size_t off = wsi * BB + size_t(p < C::NPJ ? p : C::NPJ - 1) * C::VN;
+    o.tm[x] = ldq(static_cast<const T*>(a.ws.Tm) + off);
+    o.mm[x] = ldq(static_cast<const T*>(a.ws.Mm) + off);
+    o.xm[x] = ldq(static_cast<const T*>(a.ws.Xm) + off);
+    o.am[x] = ldq(static_cast<const T*>(a.ws.Am) + off);
+  }
+  o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
   const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
   const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
-  const size_t BB = size_t(BT) * BT;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) {
+    o.hf[ks] = MM::kc(hg, D, 16 * wave, ks * MM::KS, lane);
+    o.dhf[ks] = MM::kc(dhg, D, 16 * wave, ks * MM::KS, lane);
+  }
+}
 
-  if (tid < BT) bet[tid] = tid < len ? to_f(gb[size_t(vr[tid]) * H + h]) : 0.f;
-  chunk_decay<T, BT, D>(static_cast<const T*>(a.g), vr, len, H, h, Gf, Tv, Fv, EF, EH, tid);
-  // K~ = k e^{G}, K^ = k e^{G_last - G}; T and M from the prep pass; dO (zero on replayed rows)
-  for (int idx = tid; idx < BT * (D / VN); idx += 256) {
-    const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN, bb = i / 16;
-    float kk[VN], kt[VN], kh[VN];
-    if (i < len) ld16(gk + (size_t(vr[i]) * H + h) * D + c0, kk);
-    else
+template <typename T, int BT, int D, int DV>
+__global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs b, int H) {
+  using C = GACfg<T, BT, D, DV>;
+  using MM = typename C::MM;
+  using G = RG<D, DV>;
+  using In = GAIn<T, BT, D, DV>;
+  using Rows = GARows<T, BT, D, DV>;
+  constexpr int NT = C::NT, NW = C::NW, NB = C::NB, VN = C::VN, NK = C::NK, NV = C::NV, NJ = C::NJ;
+  constexpr int LDK = C::LDK, LDV = C::LDV, LDJ = C::LDJ, LDA = C::LDA, NPR = C::NPR, NPRV = C::NPRV;
+  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
+  T* Gs = reinterpret_cast<T*>(smem + C::O_R0);   // g, then K~ in place
+  T* Kt = Gs;
+  T* Rs = Gs;                                      // R after the chained products
+  T* Y1t = Gs;                                     // Y1^T at the end
+  T* Ks = reinterpret_cast<T*>(smem + C::O_R1);   // k, then K^ in place
+  T* Kh = Ks;
+  T* Us = Ks;
+  T* dXs = Ks;
+  T* Vs = reinterpret_cast<T*>(smem + C::O_R2);
+  T* dUs = Vs;
+  T* dOs = reinterpret_cast<T*>(smem + C::O_R3);
+  T* dRs = reinterpret_cast<T*>(smem + C::O_R4);
+  T* Tl = reinterpret_cast<T*>(smem + C::O_T);
+  T* Ml = reinterpret_cast<T*>(smem + C::O_M);
+  float* dTf = reinterpret_cast<float*>(smem + C::O_T);
+  T* Xl = reinterpret_cast<T*>(smem + C::O_X);
+  T* Al = reinterpret_cast<T*>(smem + C::O_A);
+  float* vec = reinterpret_cast<float*>(smem + C::O_VEC);
+  float* bet = vec + C::V_BET;
+  float* Tbv = vec + C::V_TB;
+  float* db1 = vec + C::V_DB1;
+  float* db2 = vec + C::V_DB2;
+  const RoundArgs& a = b.r;
+
+  const int nitems = a.nchunk * H;
+  int item = blockIdx.x;
+  if (item >= nitems) return;
+  const int tid0 = threadIdx.x;
+  Rows rows, rows_n, rows_nn;
+  In cur, nxt;
+  ga_rows<T, BT, D, DV>(rows, a, item / H, tid0);
+  ga_load<T, BT, D, DV>(cur, rows, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
+  int item_n = item + gridDim.x;
+  ga_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
+
+  for (; item < nitems; item += gridDim.x) {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
+    const int h = item % H;
+    const size_t wsi = size_t(item);
+    {
+      const int itn = item_n < nitems ? item_n : item;
+      ga_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
+    }
+    const int item_nn = item_n + gridDim.x;
+    ga_rows<T, BT, D, DV>(rows_nn, a, (item_nn < nitems ? item_nn : item) / H, tid);
+
+    // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
+    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int t = 0; t < VN; ++t) kk[t] = 0.f;
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN;
+        const bool ok = rows.rk[x] >= 0;
+        stq(Gs + i * LDK + c0, ok ? cur.g[x] : z4);
+        stq(Ks + i * LDK + c0, ok ? cur.k[x] : z4);
+      }
+    }
 #pragma unroll
-    for (int t = 0; t < VN; ++t) {
-      const float L = Gf[i * LDF + c0 + t];
-      kt[t] = kk[t] * __expf(L) * EF[bb * D + c0 + t];
-      kh[t] = kk[t] * __expf(Tv[bb * D + c0 + t] - L) * EH[bb * D + c0 + t];
+    for (int x = 0; x < NV; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPV) {
+        const int i = p / NPRV, c0 = (p % NPRV) * VN;
+        const bool ok = rows.rv(x) >= 0;
+        stq(Vs + i * LDV + c0, ok ? cur.v[x] : z4);
+        stq(dOs + i * LDV + c0, ok && i >= rows.own ? cur.dO[x] : z4);
+      }
     }
-    st16(Kt + i * LDK + c0, kt);
-    st16(Kh + i * LDK + c0, kh);
-  }
-  {
-    const T* tg = static_cast<const T*>(a.ws.Tm) + wsi * BB;
-    const T* mg = static_cast<const T*>(a.ws.Mm) + wsi * BB;
-    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
-      const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
-      copy16(Tl + i * LDJ + j0, tg + i * BT + j0);
-      copy16(Ml + i * LDJ + j0, mg + i * BT + j0);
+#pragma unroll
+    for (int x = 0; x < NJ; ++x) {
+      const int p = tid + NT * x;
+      if (p < C::NPJ) {
+        const int i = p / (BT / VN), j0 = (p % (BT / VN)) * VN;
+        stq(Tl + i * LDJ + j0, cur.tm[x]);
+        stq(Ml + i * LDJ + j0, cur.mm[x]);
+        stq(Xl + i * LDJ + j0, cur.xm[x]);
+        stq(Al + i * LDJ + j0, cur.am[x]);
+      }
     }
-    for (int idx = tid; idx < BT * (DV / VN); idx += 256) {
-      const int i = idx / (DV / VN), j0 = (idx % (DV / VN)) * VN;
-      if (i < len && i >= own) copy16(dOl + i * LDV + j0, gdo + (size_t(vr[i]) * H + h) * DV + j0);
-      else *reinterpret_cast<f32x4*>(dOl + i * LDV + j0) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
+    __syncthreads();
+    // 2. decay per (16-row block, channel): block-local cumulative L, block totals
+    float Lr[16];
+    HARTS_STRIDED(idx, tid, NB * D, NT) {
+      const int bb = idx / D, c = idx % D;
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        s += to_f(Gs[(16 * bb + t) * LDK + c]);
+        Lr[t] = s;
+      }
+      Tbv[bb * D + c] = s;
     }
-  }
-  __syncthreads();
-  // R = V - K~ S0, stored transposed
-  {
-    constexpr int MT = BT / 16, NT = DV / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mi = jb / NT, nj = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < D; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Kt, LDK, 16 * mi, k0, lane), MM::kc(hg, D, 16 * nj, k0, lane), acc);
-      const int jv = 16 * nj + ccol(lane), i0 = 16 * mi + crow(lane, 0);
-      float rv[4];
+    __syncthreads();
+    // 3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k (each thread its own entries)
+    HARTS_STRIDED(idx, tid, NB * D, NT) {
+      const int bb = idx / D, c = idx % D;
+      float fb = 0.f, fe = 0.f;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        const float tq = Tbv[q * D + c];
+        fb += q < bb ? tq : 0.f;
+        fe += tq;
+      }
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int i = 16 * bb + t;
+        const float kv = to_f(Ks[i * LDK + c]);
+        Kt[i * LDK + c] = from_f<T>(kv * __expf(fb + Lr[t]));
+        Kh[i * LDK + c] = from_f<T>(kv * __expf(fe - fb - Lr[t]));
+      }
+    }
+    __syncthreads();
+    // 4. R = V - K~ S0 and dU = K^ dS + M^T dO for this wave's value columns
+    const int jv = 16 * wave + cc;
+    f32x4 R[NB], dU[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      f32x4 r1 = z4, r2 = z4;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        r1 = MM::mma(MM::kc(Kt, LDK, 16 * bb, ks * MM::KS, lane), cur.hf[ks], r1);
+        r2 = MM::mma(MM::kc(Kh, LDK, 16 * bb, ks * MM::KS, lane), cur.dhf[ks], r2);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) R[bb][r] = to_f(Vs[(16 * bb + 4 * g4 + r) * LDV + jv]) - r1[r];
+      dU[bb] = r2;
+    }
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int br = 0; br < NB; ++br) {
+        if (br < bi) continue;
+        // dU block bi += sum over rows of block br of M[r][i] dO[r][jv]
+        float am[4], bo[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          am[t] = to_f(Ml[(16 * br + 4 * g4 + t) * LDJ + 16 * bi + cc]);
+          bo[t] = to_f(dOs[(16 * br + 4 * g4 + t) * LDV + jv]);
+        }
+        dU[bi] = mma_k16<T>(am, bo, dU[bi]);
+      }
+    __syncthreads();  // K~, K^ and V consumed
+    // 5. U = T R, dR = T^T dU (16-token blocks, right operand in registers); stage R, U, dU, dR
+    f32x4 U[NB], dR[NB];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) U[bb] = dR[bb] = z4;
+#pragma unroll
+    for (int bi = 0; bi < NB; ++bi)
+#pragma unroll
+      for (int bj = 0; bj <= bi; ++bj) {
+        float ta[4], tb[4], rb[4], ub[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          ta[t] = to_f(Tl[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);  // T[i][j], i in bi, j in bj
+          tb[t] = to_f(Tl[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);  // T[i][j] as (j, i)
+          rb[t] = R[bj][t];
+          ub[t] = dU[bi][t];
+        }
+        U[bi] = mma_k16<T>(ta, rb, U[bi]);
+        dR[bj] = mma_k16<T>(tb, ub, dR[bj]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        rv[r] = (i < len ? to_f(gv[(size_t(vr[i]) * H + h) * DV + jv]) : 0.f) - acc[r];
+        const int i = 16 * bb + 4 * g4 + r;
+        Rs[i * LDV + jv] = from_f<T>(R[bb][r]);
+        Us[i * LDV + jv] = from_f<T>(U[bb][r]);
+        dUs[i * LDV + jv] = from_f<T>(dU[bb][r]);
+        dRs[i * LDV + jv] = from_f<T>(dR[bb][r]);
       }
-      store4(Rt + jv * LDJ + i0, rv[0], rv[1], rv[2], rv[3]);
-    }
-  }
-  __syncthreads();
-  // U^T = R^T T^T  ->  U [i][jv] (LDS and workspace)
-  {
-    T* ug = static_cast<T*>(a.ws.U) + wsi * BT * DV;
-    constexpr int MT = DV / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mv = jb / NT, ni = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Rt, LDJ, 16 * mv, k0, lane), MM::kc(Tl, LDJ, 16 * ni, k0, lane), acc);
-      const int i = 16 * ni + ccol(lane), jv0 = 16 * mv + crow(lane, 0);
-      store4(Ul + i * LDV + jv0, acc[0], acc[1], acc[2], acc[3]);
-      store4(ug + i * DV + jv0, acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  // dU = M^T dO + K^ dS_end, stored transposed
-  {
-    constexpr int MT = BT / 16, NT = DV / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mi = jb / NT, nj = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::rc(Ml, LDJ, 16 * mi, k0, lane), MM::rc(dOl, LDV, 16 * nj, k0, lane), acc);
-      for (int k0 = 0; k0 < D; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Kh, LDK, 16 * mi, k0, lane), MM::kc(dhg, D, 16 * nj, k0, lane), acc);
-      store4(dUt + (16 * nj + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  __syncthreads();
-  // dM = lower(dO U^T), computed transposed so it stores row-major
-  {
-    T* dmg = static_cast<T*>(a.ws.dM) + wsi * BB;
-    constexpr int MT = BT / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mj = jb / NT, ni = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < DV; k0 += MM::KS)
-        acc = MM::mma(MM::kc(Ul, LDV, 16 * mj, k0, lane), MM::kc(dOl, LDV, 16 * ni, k0, lane), acc);
-      const int i = 16 * ni + ccol(lane), j0 = 16 * mj + crow(lane, 0);
-      float v[4];
+    __syncthreads();
+    // 6. dM = lower(dO U^T) (computed transposed) to the workspace; dT = dU R^T (fp32) over T, M;
+    //    U and dR to the workspace; dv of own rows to the output, of replayed rows to the side buffer
+    {
+      constexpr int NTRI = NB * (NB + 1) / 2;
+      T* dmg = static_cast<T*>(a.ws.dM) + wsi * BT * BT;
+      HARTS_STRIDED(jb, wave, 2 * NTRI, NW) {
+        const int t = jb < NTRI ? jb : jb - NTRI;
+        int bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= t) ++bi;
+        const int bj = t - bi * (bi + 1) / 2;
+        f32x4 acc = z4;
+        if (jb < NTRI) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = j0 + r <= i ? acc[r] : 0.f;
-      store4(dmg + i * BT + j0, v[0], v[1], v[2], v[3]);
-    }
-  }
-  // dR^T = dU^T T  ->  dR [j][jv] (LDS and workspace)
-  {
-    T* drg = static_cast<T*>(a.ws.dR) + wsi * BT * DV;
-    constexpr int MT = DV / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mv = jb / NT, nj = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::kc(dUt, LDJ, 16 * mv, k0, lane), MM::rc(Tl, LDJ, 16 * nj, k0, lane), acc);
-      const int j = 16 * nj + ccol(lane), jv0 = 16 * mv + crow(lane, 0);
-      store4(dRl + j * LDV + jv0, acc[0], acc[1], acc[2], acc[3]);
-      store4(drg + j * DV + jv0, acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  __syncthreads();  // dM and dR done reading U and T: dT reuses the U region
-  // dT = dU R^T (fp32)
-  {
-    constexpr int MT = BT / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mi = jb / NT, nj = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < DV; k0 += MM::KS)
-        acc = MM::mma(MM::rc(dUt, LDJ, 16 * mi, k0, lane), MM::rc(Rt, LDJ, 16 * nj, k0, lane), acc);
+          for (int k0 = 0; k0 < DV; k0 += MM::KS)
+            acc = MM::mma(MM::kc(Us, LDV, 16 * bj, k0, lane), MM::kc(dOs, LDV, 16 * bi, k0, lane), acc);
+          const int i = 16 * bi + cc, j0 = 16 * bj + 4 * g4;
+          float v[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dTf[(16 * mi + crow(lane, r)) * LDA + 16 * nj + ccol(lane)] = acc[r];
-    }
-  }
-  __syncthreads();
-  // dv: own rows to the output, replayed rows to the side buffer
-  {
-    T* gdv = static_cast<T*>(b.dv);
-    for (int idx = tid; idx < BT * (DV / VN); idx += 256) {
-      const int i = idx / (DV / VN), j0 = (idx % (DV / VN)) * VN;
-      if (i >= len) continue;
-      if (i >= own) {
-        copy16(gdv + (size_t(vr[i]) * H + h) * DV + j0, dRl + i * LDV + j0);
-      } else {
-        float* rg = b.replay_grad + (size_t(cd.replay_base + i) * H + h) * G::W + G::DVO + j0;
+          for (int r = 0; r < 4; ++r) v[r] = j0 + r <= i ? acc[r] : 0.f;
+          store4(dmg + i * BT + j0, v[0], v[1], v[2], v[3]);
+        } else {
 #pragma unroll
-        for (int t = 0; t < VN; ++t) rg[t] = to_f(dRl[i * LDV + j0 + t]);
+          for (int k0 = 0; k0 < DV; k0 += MM::KS)
+            acc = MM::mma(MM::kc(dUs, LDV, 16 * bi, k0, lane), MM::kc(Rs, LDV, 16 * bj, k0, lane), acc);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) dTf[(16 * bi + 4 * g4 + r) * LDA + 16 * bj + cc] = acc[r];
+        }
+      }
+      T* ug = static_cast<T*>(a.ws.U) + wsi * BT * DV;
+      T* drg = static_cast<T*>(a.ws.dR) + wsi * BT * DV;
+#pragma unroll
+      for (int x = 0; x < NV; ++x) {
+        const int p = tid + NT * x;
+        if (p < C::NPV) {
+          const int i = p / NPRV, c0 = (p % NPRV) * VN;
+          const f32x4 drv = ldq(dRs + i * LDV + c0);
+          stq(ug + i * DV + c0, ldq(Us + i * LDV + c0));
+          stq(drg + i * DV + c0, drv);
+          const int row = rows.rv(x);
+          if (row >= 0) {
+            if (i >= rows.own) {
+              stq(static_cast<T*>(b.dv) + (size_t(row) * H + h) * DV + c0, drv);
+            } else {
+              float f[VN];
+              unpack16<T>(drv, f);
+              float* rg = b.replay_grad + (size_t(rows.rbase + i) * H + h) * G::W + G::DVO + c0;
+#pragma unroll
+              for (int t = 0; t < VN; ++t) rg[t] = f[t];
+            }
+          }
+        }
       }
     }
-  }
-  // X and A from the prep pass (T, M no longer needed); dbeta_1 = colsum(X .* dT); dX = dT diag(beta)
-  {
-    const T* xg = static_cast<const T*>(a.ws.Xm) + wsi * BB;
-    const T* ag = static_cast<const T*>(a.ws.Am) + wsi * BB;
-    for (int idx = tid; idx < BT * (BT / VN); idx += 256) {
+    __syncthreads();
+    // 7. dX = dT diag(beta) (lower incl.) over U; column partial sums of X .* dT for dbeta_1
+    HARTS_STRIDED(idx, tid, BT * (BT / VN), NT) {
       const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
-      copy16(Xl + i * LDJ + j0, xg + i * BT + j0);
-      copy16(Al + i * LDJ + j0, ag + i * BT + j0);
-    }
-  }
-  __syncthreads();
-  for (int j = tid; j < BT; j += 256) {
-    float s = 0.f;
-    for (int i = j; i < BT; ++i) s += to_f(Xl[i * LDJ + j]) * dTf[i * LDA + j];
-    db1[j] = s;
-  }
-  for (int idx = tid; idx < BT * BT; idx += 256) {
-    const int i = idx / BT, j = idx % BT;
-    dXl[i * LDJ + j] = from_f<T>(j <= i ? dTf[i * LDA + j] * bet[j] : 0.f);
-  }
-  __syncthreads();
-  // Y1 = dX X^T, stored transposed (rows of Y1^T in the dR region)
-  {
-    constexpr int MT = BT / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mi = jb / NT, nk = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::kc(dXl, LDJ, 16 * mi, k0, lane), MM::kc(Xl, LDJ, 16 * nk, k0, lane), acc);
-      store4(Y1t + (16 * nk + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
-    }
-  }
-  __syncthreads();
-  // dL = -X^T Y1 (fp32)
-  {
-    constexpr int MT = BT / 16, NT = BT / 16;
-    for (int jb = wave; jb < MT * NT; jb += 4) {
-      const int mi = jb / NT, nk = jb % NT;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int k0 = 0; k0 < BT; k0 += MM::KS)
-        acc = MM::mma(MM::rc(Xl, LDJ, 16 * mi, k0, lane), MM::kc(Y1t, LDJ, 16 * nk, k0, lane), acc);
+      float v[VN];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) dLf[(16 * mi + crow(lane, r)) * LDA + 16 * nk + ccol(lane)] = -acc[r];
+      for (int t = 0; t < VN; ++t) v[t] = j0 + t <= i ? dTf[i * LDA + j0 + t] * bet[j0 + t] : 0.f;
+      stq(dXs + i * LDJ + j0, pack16<T>(v));
     }
-  }
-  __syncthreads();
-  // dA = strict_lower(diag(beta) dL); dbeta = dbeta_1 + rowsum(dL .* A)
-  {
-    T* dag = static_cast<T*>(a.ws.dA) + wsi * BB;
-    for (int idx = tid; idx < BT * BT; idx += 256) {
-      const int i = idx / BT, j = idx % BT;
-      dag[idx] = from_f<T>(j < i ? bet[i] * dLf[i * LDA + j] : 0.f);
+    {
+      constexpr int RPP = BT / C::NPART;
+      const int j = tid % BT, part = tid / BT;
+      float s = 0.f;
+#pragma unroll
+      for (int u = 0; u < RPP; ++u) {
+        const int i = part * RPP + u;
+        s += i >= j ? to_f(Xl[i * LDJ + j]) * dTf[i * LDA + j] : 0.f;
+      }
+      db1[part * BT + j] = s;
     }
-    T* gdb = static_cast<T*>(b.dbeta);
-    for (int i = tid; i < len; i += 256) {
-      float s = db1[i];
-      for (int j = 0; j < i; ++j) s += dLf[i * LDA + j] * to_f(Al[i * LDJ + j]);
-      if (i >= own) gdb[size_t(vr[i]) * H + h] = from_f<T>(s);
-      else b.replay_grad[(size_t(cd.replay_base + i) * H + h) * G::W + G::DB] = s;
+    __syncthreads();
+    // 8. Y1 = dX X^T, stored transposed over R
+    HARTS_STRIDED(jb, wave, NB * NB, NW) {
+      const int mi = jb / NB, nk = jb % NB;
+      f32x4 acc = z4;
+#pragma unroll
+      for (int k0 = 0; k0 < BT; k0 += MM::KS)
+        acc = MM::mma(MM::kc(dXs, LDJ, 16 * mi, k0, lane), MM::kc(Xl, LDJ, 16 * nk, k0, lane), acc);
+      store4(Y1t + (16 * nk + cc) * LDJ + 16 * mi + 4 * g4, acc[0], acc[1], acc[2], acc[3]);
     }
+    __syncthreads();
+    // 9. dL = -X^T Y1 (lower tiles, computed transposed): dA = strict_lower(diag(beta) dL) to the
+    //    workspace, row partial sums of dL .* A for dbeta_2
+    {
+      constexpr int NTRI = NB * (NB + 1) / 2;
+      T* dag = static_cast<T*>(a.ws.dA) + wsi * BT * BT;
+      HARTS_STRIDED(jb, wave, NTRI, NW) {
+        int bi = 0;
+        while ((bi + 1) * (bi + 2) / 2 <= jb) ++bi;
+        const int bj = jb - bi * (bi + 1) / 2;
+        f32x4 acc = z4;
+#pragma unroll
+        for (int k0 = 0; k0 < BT; k0 += MM::KS)
+          acc = MM::mma(MM::kc(Y1t, LDJ, 16 * bj, k0, lane), MM::rc(Xl, LDJ, 16 * bi, k0, lane), acc);
+        const int i = 16 * bi + cc, j0 = 16 * bj + 4 * g4;
+        const float bi_ = bet[i];
+        float v[4], p2 = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int j = j0 + r;
+          const float dl = -acc[r];
+          v[r] = j < i ? bi_ * dl : 0.f;
+          p2 += j < i ? dl * to_f(Al[i * LDJ + j]) : 0.f;
+        }
+        store4(dag + i * BT + j0, v[0], v[1], v[2], v[3]);
+        p2 += __shfl_xor(p2, 16, 64);
+        p2 += __shfl_xor(p2, 32, 64);
+        if (g4 == 0) db2[bj * BT + i] = p2;
+      }
+    }
+    __syncthreads();
+    // 10. dbeta = dbeta_1 + dbeta_2: own rows to the output, replayed rows to the side buffer
+    if (tid < BT && rows.rb >= 0) {
+      const int i = tid;
+      float s = 0.f;
+#pragma unroll
+      for (int part = 0; part < C::NPART; ++part) s += db1[part * BT + i];
+#pragma unroll
+      for (int bj = 0; bj < NB; ++bj) s += bj <= i / 16 ? db2[bj * BT + i] : 0.f;
+      if (i >= rows.own) static_cast<T*>(b.dbeta)[size_t(rows.rb) * H + h] = from_f<T>(s);
+      else b.replay_grad[(size_t(rows.rbase + i) * H + h) * G::W + G::DB] = s;
+    }
+    __syncthreads();  // the next item restages every region
+    cur = nxt;
+    rows = rows_n;
+    rows_n = rows_nn;
+    item_n = item_nn;
   }
 }
 
@@ -675,21 +818,6 @@ __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, B
   for (int ks = 0; ks < C::NKS; ++ks) {
     o.hc[ks] = MM::kc(hcg, DV, 16 * wave, ks * MM::KS, lane);
     o.dhc[ks] = MM::kc(dhcg, DV, 16 * wave, ks * MM::KS, lane);
-  }
-}
-
-// C[16x16] += A B over a 16-long contraction: lane l supplies A[l%16][4(l/16) + t] and
-// B[4(l/16) + t][l%16], t = 0..3 (B is then a 16-token block of the accumulator layout).
-template <typename T>
-__device__ __forceinline__ f32x4 mma_k16(const float* av, const float* bv, f32x4 c) {
-  if constexpr (sizeof(T) == 2) {
-    typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s4;
-    const bf16x4 a4 = {(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
-    const bf16x4 b4 = {(bf16)bv[0], (bf16)bv[1], (bf16)bv[2], (bf16)bv[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a4), __builtin_bit_cast(s4, b4), c, 0, 0,
-                                                     0);
-  } else {
-    return mma16_f32(f32x4{av[0], av[1], av[2], av[3]}, f32x4{bv[0], bv[1], bv[2], bv[3]}, c);
   }
 }
 
@@ -992,8 +1120,9 @@ static hipError_t dstate_launch(const KdaDims& d, const BwdRoundArgs& b, hipStre
 template <typename T, int BT, int D, int DV>
 static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {
   if (b.r.nchunk <= 0) return hipSuccess;
-  dim3 grid(unsigned(b.r.nchunk) * d.H);
-  if (part == 0) hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), grid, dim3(256), 0, s, b, d.H);
+  if (part == 0)
+    hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
+                       dim3(GACfg<T, BT, D, DV>::NT), 0, s, b, d.H);
   else
     hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
                        dim3(GBCfg<T, BT, D, DV>::NT), 0, s, b, d.H);
