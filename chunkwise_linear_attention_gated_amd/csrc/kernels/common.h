@@ -153,6 +153,16 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
   _Pragma("unroll") for (int var##_u = 0; var##_u < ((n) + (step) - 1) / (step); ++var##_u) \
     if (const int var = (start) + (step) * var##_u; var < (n))
 
+// A zero the compiler cannot see through.  Loads of per-chunk descriptor fields are
+// indexed with it so their values stay per-lane: a value the compiler knows to be
+// uniform is moved to a scalar register right where it is loaded, which waits for
+// that load (and, counters being in order, for every fetch issued before it).
+__device__ __forceinline__ int lane_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
 // Workgroup size of the persistent per-chunk kernels: 8 waves, two per SIMD.
 constexpr int CNT = 512;
 constexpr int CNW = CNT / 64;

@@ -44,35 +44,58 @@ struct DStateOps {
   f32x4 w[NW], kh[NK], dov[NO];
   F qe[MU][KB];
   float el[MU][4];
+  int own, emit;
+};
+// compact rows of this thread's dO pieces (-1: padding), fetched one step before the dO itself
+template <typename T, int BT, int D, int DV, int DVT>
+struct DStateRows {
+  int r[DStateOps<T, BT, D, DV, DVT>::NO];
 };
 
 template <typename T, int BT, int D, int DV, int DVT>
-__device__ __forceinline__ void load_dstate_ops(DStateOps<T, BT, D, DV, DVT>& o, const RoundArgs& a, const T* gdo,
-                                                const ChunkDesc& cd, size_t wsi, int H, int h, int tid, int wave,
-                                                int lane, int jvb) {
+__device__ __forceinline__ void load_dstate_rows(DStateRows<T, BT, D, DV, DVT>& o, const RoundArgs& a, int chunk,
+                                                 int tid) {
+  using Ops = DStateOps<T, BT, D, DV, DVT>;
+#pragma unroll
+  for (int x = 0; x < Ops::NO; ++x) {
+    const int idx = tid + 256 * x;
+    const int i = idx / (DVT / Ops::VN);
+    o.r[x] = a.crows[size_t(chunk) * BT + (i < BT ? i : BT - 1)];
+  }
+}
+
+// Operands of one chunk step, addressed from the chunk's round-local index and its
+// (already fetched) rows only, so none of these loads waits on another.  Loads are
+// unconditional from clamped addresses; padding and replayed rows are masked at use.
+template <typename T, int BT, int D, int DV, int DVT>
+__device__ __forceinline__ void load_dstate_ops(DStateOps<T, BT, D, DV, DVT>& o, const DStateRows<T, BT, D, DV, DVT>& rw,
+                                                const RoundArgs& a, const T* gdo, int chunk, int H, int h, int tid,
+                                                int wave, int lane, int jvb, int z) {
   using Ops = DStateOps<T, BT, D, DV, DVT>;
   using MM = Mma<T>;
   constexpr int VN = Ops::VN, MT = D / 16;
+  const size_t wsi = size_t(chunk) * H + h;
   const T* wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
   const T* kg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
 #pragma unroll
   for (int x = 0; x < Ops::NW; ++x) {
     const int idx = tid + 256 * x;
-    if (idx < BT * (D / VN)) o.w[x] = *reinterpret_cast<const f32x4*>(wg + idx * VN);
+    o.w[x] = ldq(wg + (idx < BT * (D / VN) ? idx : 0) * VN);
   }
 #pragma unroll
   for (int x = 0; x < Ops::NK; ++x) {
     const int idx = tid + 256 * x;
-    if (idx < D * (BT / VN)) o.kh[x] = *reinterpret_cast<const f32x4*>(kg + idx * VN);
+    o.kh[x] = ldq(kg + (idx < D * (BT / VN) ? idx : 0) * VN);
   }
 #pragma unroll
   for (int x = 0; x < Ops::NO; ++x) {
     const int idx = tid + 256 * x;
-    const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-    o.dov[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (idx < BT * (DVT / VN) && i < cd.len && i >= cd.own_from)
-      o.dov[x] = *reinterpret_cast<const f32x4*>(gdo + (size_t(a.vrows[cd.vbase + i]) * H + h) * DV + jvb + j0);
+    const int j0 = (idx % (DVT / VN)) * VN;
+    const int row = rw.r[x] >= 0 ? rw.r[x] : 0;
+    o.dov[x] = ldq(gdo + (size_t(row) * H + h) * DV + jvb + j0);
   }
+  o.own = a.chunks[chunk + z].own_from;
+  o.emit = a.chunks[chunk + z].emit;
   const T* qe = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
   const float* el = a.ws.El + wsi * D;
 #pragma unroll
@@ -112,18 +135,32 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
   for (int u = 0; u < MU; ++u)
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) dS[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  using Rows = DStateRows<T, BT, D, DV, DVT>;
   Ops cur, nxt;
-  ChunkDesc cd = a.chunks[sd.chunk_base + sd.n_chunks - 1];
-  load_dstate_ops<T, BT, D, DV, DVT>(cur, a, gdo, cd, size_t(cd.local) * H + h, H, h, tid, wave, lane, jvb);
+  // cur_rows: rows of chunk n; rows_x: rows of the chunk whose operands are in nxt;
+  // rows_n: rows of the chunk before that.  cur is taken from nxt at the top of each
+  // step, before the next fetch is issued.
+  Rows cur_rows, rows_x, rows_n;
+  const int z = lane_zero();
+  {
+    const int last = sd.chunk_base + sd.n_chunks - 1;
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_x, a, last, tid);
+    load_dstate_ops<T, BT, D, DV, DVT>(nxt, rows_x, a, gdo, last, H, h, tid, wave, lane, jvb, z);
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, sd.chunk_base + (sd.n_chunks > 1 ? sd.n_chunks - 2 : 0), tid);
+  }
   for (int n = sd.n_chunks - 1; n >= 0; --n) {
-    const size_t wsi = size_t(cd.local) * H + h;
-    const ChunkDesc cdn = a.chunks[sd.chunk_base + (n > 0 ? n - 1 : 0)];
-    if (n > 0)
-      load_dstate_ops<T, BT, D, DV, DVT>(nxt, a, gdo, cdn, size_t(cdn.local) * H + h, H, h, tid, wave, lane, jvb);
+    const size_t wsi = size_t(sd.chunk_base + n) * H + h;
+    cur = nxt;
+    cur_rows = rows_x;
+    // fetch ahead: operands of chunk n-1 (its rows are already here), rows of chunk n-2
+    load_dstate_ops<T, BT, D, DV, DVT>(nxt, rows_n, a, gdo, sd.chunk_base + (n > 0 ? n - 1 : 0), H, h, tid, wave,
+                                       lane, jvb, z);
+    rows_x = rows_n;
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, sd.chunk_base + (n > 1 ? n - 2 : 0), tid);
     __syncthreads();
     // slot gradient: sum over the consumers of the state emitted after this chunk
-    if (cd.emit >= 0 && b.slot_cons_off) {
-      const int q0 = b.slot_cons_off[cd.emit], q1 = b.slot_cons_off[cd.emit + 1];
+    if (cur.emit >= 0 && b.slot_cons_off) {
+      const int q0 = b.slot_cons_off[cur.emit], q1 = b.slot_cons_off[cur.emit + 1];
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
         const int mt = wave + 4 * u;
@@ -137,7 +174,7 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
               for (int qq = q0; qq < q1; ++qq)
                 add += b.dinit[((size_t(b.slot_cons[qq]) * H + h) * D + c) * DV + jv];
               dS[u][nt][r] += add;
-              if (b.dstates) b.dstates[((size_t(cd.emit) * H + h) * D + c) * DV + jv] = add;
+              if (b.dstates) b.dstates[((size_t(cur.emit) * H + h) * D + c) * DV + jv] = add;
             }
       }
     }
@@ -171,7 +208,8 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
       const int idx = tid + 256 * x;
       if (idx < BT * (DVT / VN)) {
         const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-        *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = cur.dov[x];
+        const bool ok = cur_rows.r[x] >= 0 && i >= cur.own;
+        *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = ok ? cur.dov[x] : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     __syncthreads();
@@ -232,8 +270,6 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
           for (int nt = 0; nt < NTV; ++nt) dS[u][nt][r] = cur.el[u][r] * dS[u][nt][r] + a1[nt][r] - a2[nt][r];
       }
     }
-    cur = nxt;
-    cd = cdn;
   }
   if (b.dinit) {
     const size_t gs = size_t(a.seq0 + si);
@@ -428,10 +464,12 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
   int item = blockIdx.x;
   if (item >= nitems) return;
   const int tid0 = threadIdx.x;
-  Rows rows, rows_n, rows_nn;
+  // rows_x: rows of the item whose inputs are in nxt; rows_n: rows of the item after it.
+  // cur is taken from nxt at the top of each iteration, before the next fetch is issued.
+  Rows rows, rows_x, rows_n;
   In cur, nxt;
-  ga_rows<T, BT, D, DV>(rows, a, item / H, tid0);
-  ga_load<T, BT, D, DV>(cur, rows, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
+  ga_rows<T, BT, D, DV>(rows_x, a, item / H, tid0);
+  ga_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
   int item_n = item + gridDim.x;
   ga_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
 
@@ -441,12 +479,15 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
     const int h = item % H;
     const size_t wsi = size_t(item);
+    cur = nxt;
+    rows = rows_x;
     {
       const int itn = item_n < nitems ? item_n : item;
       ga_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     }
+    rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
-    ga_rows<T, BT, D, DV>(rows_nn, a, (item_nn < nitems ? item_nn : item) / H, tid);
+    ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
 
     // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -702,9 +743,6 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       else b.replay_grad[(size_t(rows.rbase + i) * H + h) * G::W + G::DB] = s;
     }
     __syncthreads();  // the next item restages every region
-    cur = nxt;
-    rows = rows_n;
-    rows_n = rows_nn;
     item_n = item_nn;
   }
 }
@@ -846,10 +884,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
   int item = blockIdx.x;
   if (item >= nitems) return;
   const int tid0 = threadIdx.x;
-  Rows rows, rows_n, rows_nn;
+  // rows_x: rows of the item whose inputs are in nxt; rows_n: rows of the item after it.
+  // cur is taken from nxt at the top of each iteration, before the next fetch is issued.
+  Rows rows, rows_x, rows_n;
   In cur, nxt;
-  gb_rows<T, BT, D, DV>(rows, a, item / H, tid0);
-  gb_load<T, BT, D, DV>(cur, rows, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
+  gb_rows<T, BT, D, DV>(rows_x, a, item / H, tid0);
+  gb_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
   int item_n = item + gridDim.x;
   gb_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
 
@@ -859,12 +899,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
     const int h = item % H;
     const size_t wsi = size_t(item);
+    cur = nxt;
+    rows = rows_x;
     {
       const int itn = item_n < nitems ? item_n : item;
       gb_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     }
+    rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
-    gb_rows<T, BT, D, DV>(rows_nn, a, (item_nn < nitems ? item_nn : item) / H, tid);
+    gb_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
 
     // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -1071,9 +1114,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       }
     }
     __syncthreads();  // the next item restages every region
-    cur = nxt;
-    rows = rows_n;
-    rows_n = rows_nn;
     item_n = item_nn;
   }
 }

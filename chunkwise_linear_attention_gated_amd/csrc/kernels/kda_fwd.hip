@@ -13,6 +13,8 @@
 // e^{G_i - G_j} = e^{G_i - F_bi} * e^{F_bi - G_j}, F_b the log-decay before
 // block b; both factors are <= 1 off the diagonal blocks, and within a
 // diagonal block the pair is bounded by one 16-row gate sum.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -159,10 +161,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   const int nitems = a.nchunk * H;
   int item = blockIdx.x;
   if (item >= nitems) return;
-  Rows rows, rows_n, rows_nn;  // current item (masks), next item, the one after
+  // rows_x: rows of the item whose inputs are in nxt; rows_n: rows of the item after it.
+  // cur is taken from nxt at the top of each iteration, before the next fetch is issued.
+  Rows rows, rows_x, rows_n;
   In cur, nxt;
-  prep_rows<T, BT, D, DV>(rows, a.crows, item / H, tid0);
-  prep_load<T, BT, D, DV>(cur, rows, a, item % H, H, tid0);
+  prep_rows<T, BT, D, DV>(rows_x, a.crows, item / H, tid0);
+  prep_load<T, BT, D, DV>(nxt, rows_x, a, item % H, H, tid0);
   int item_n = item + gridDim.x;
   prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_n < nitems ? item_n : item) / H, tid0);
 
@@ -173,12 +177,15 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     const int lane = tid & 63, wave = tid >> 6;
     const int h = item % H;
     const size_t wsi = size_t(item);  // (round-local chunk) * H + head
+    cur = nxt;
+    rows = rows_x;
     // this item's values; fetch ahead: inputs of the next item, rows of the one after
     f32x4 vv[NV];
     prep_load_v<T, BT, D, DV>(vv, rows, a, h, H, tid);
     prep_load<T, BT, D, DV>(nxt, rows_n, a, (item_n < nitems ? item_n : item) % H, H, tid);
+    rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
-    prep_rows<T, BT, D, DV>(rows_nn, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
+    prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
 
     // 1. g -> Gf (fp32), beta
 #pragma unroll
@@ -487,9 +494,6 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     __syncthreads();  // the next item overwrites every region
-    cur = nxt;
-    rows = rows_n;
-    rows_n = rows_nn;
     item_n = item_nn;
   }
 }
@@ -510,20 +514,37 @@ struct StateOps {
   static constexpr int NMI = (BT / 16 + 3) / 4, MU = (D / 16 + 3) / 4, NTV = DVT / 16;
   static constexpr int KD = D / MM::KS, KB = BT / MM::KS;
   static constexpr int NQ = FWD ? NMI : 1, KQ = FWD ? KD : 1, KM = FWD ? KB : 1;
+  using Raw4 = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
   F wa[NMI][KD];        // W fragments (A operand of U = W S), token rows of this wave
-  float up[NMI][NTV][4];  // U' at this lane's accumulator positions
+  Raw4 up[NMI][NTV];    // U' at this lane's accumulator positions (converted at use)
   F qb[NQ][KQ];         // Q~ fragments (B operand of O^T), forward only
   F mb[NQ][KM];         // M fragments (B operand of O^T), forward only
   F ka[MU][KB];         // KhT fragments (A operand of S += KhT U)
   float el[MU][4];      // e^{G_last} of this lane's state rows
+  int own, emit;        // first own row, emitted slot (-1: none)
+  int orow[NQ];         // forward: compact row of this lane's output token per token block (-1: padding)
 };
 
+// Everything a chunk step needs that does not depend on the state, addressed from the
+// chunk's round-local index alone (a sequence's chunks are consecutive), so the loads of
+// the next step never wait on a descriptor.
 template <typename T, int BT, int D, int DV, int DVT, bool FWD>
-__device__ __forceinline__ void load_state_ops(StateOps<T, BT, D, DV, DVT, FWD>& o, const ChunkWs& ws, size_t wsi,
-                                               int wave, int lane, int jvb) {
+__device__ __forceinline__ void load_state_ops(StateOps<T, BT, D, DV, DVT, FWD>& o, const RoundArgs& a, int chunk,
+                                               int h, int H, int wave, int lane, int jvb, int z) {
   using Ops = StateOps<T, BT, D, DV, DVT, FWD>;
   using MM = Mma<T>;
   constexpr int MT = D / 16;
+  const ChunkWs& ws = a.ws;
+  const size_t wsi = size_t(chunk) * H + h;
+  o.own = a.chunks[chunk + z].own_from;
+  o.emit = a.chunks[chunk + z].emit;
+  if constexpr (FWD) {
+#pragma unroll
+    for (int x = 0; x < Ops::NQ; ++x) {
+      const int mi = wave + 4 * x;
+      o.orow[x] = a.crows[size_t(chunk) * BT + (mi < BT / 16 ? 16 * mi : 0) + (lane & 15)];
+    }
+  }
   const T* wg = static_cast<const T*>(ws.W) + wsi * BT * D;
   const T* upg = static_cast<const T*>(ws.UpT) + wsi * DV * BT;
   const T* khg = static_cast<const T*>(ws.KhT) + wsi * D * BT;
@@ -536,7 +557,8 @@ __device__ __forceinline__ void load_state_ops(StateOps<T, BT, D, DV, DVT, FWD>&
       for (int kk = 0; kk < Ops::KD; ++kk) o.wa[x][kk] = MM::kc(wg, D, 16 * mi, kk * MM::KS, lane);
 #pragma unroll
       for (int nt = 0; nt < Ops::NTV; ++nt)
-        load4(upg + (jvb + 16 * nt + ccol(lane)) * BT + 16 * mi + crow(lane, 0), o.up[x][nt]);
+        o.up[x][nt] = *reinterpret_cast<const typename Ops::Raw4*>(upg + (jvb + 16 * nt + ccol(lane)) * BT + 16 * mi +
+                                                                  crow(lane, 0));
       if constexpr (FWD) {
         const T* qg = static_cast<const T*>(ws.Qt) + wsi * BT * D;
         const T* mg = static_cast<const T*>(ws.Mm) + wsi * BT * BT;
@@ -591,14 +613,16 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
         S[u][nt][r] = v;
       }
     }
+  // cur is taken from nxt at the top of each step, before the next fetch is issued, so
+  // no path into the loop leaves a load pending on cur's registers
   Ops cur, nxt;
-  ChunkDesc cd = a.chunks[sd.chunk_base];
-  load_state_ops<T, BT, D, DV, DVT, !BWD>(cur, a.ws, size_t(cd.local) * H + h, wave, lane, jvb);
+  const int z = lane_zero();
+  load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a, sd.chunk_base, h, H, wave, lane, jvb, z);
   for (int n = 0; n < sd.n_chunks; ++n) {
-    const size_t wsi = size_t(cd.local) * H + h;
-    const ChunkDesc cdn = a.chunks[sd.chunk_base + (n + 1 < sd.n_chunks ? n + 1 : n)];
-    if (n + 1 < sd.n_chunks)
-      load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a.ws, size_t(cdn.local) * H + h, wave, lane, jvb);
+    const size_t wsi = size_t(sd.chunk_base + n) * H + h;
+    cur = nxt;
+    load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a, sd.chunk_base + (n + 1 < sd.n_chunks ? n + 1 : n), h, H, wave,
+                                            lane, jvb, z);
     T* Sb = St[n & 1];
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
@@ -643,8 +667,8 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt) {
           const int jl = 16 * nt + ccol(lane), i0 = 16 * mi + crow(lane, 0);
-          store4(Ut + jl * LDS_U + i0, cur.up[x][nt][0] - acc[nt][0], cur.up[x][nt][1] - acc[nt][1],
-                 cur.up[x][nt][2] - acc[nt][2], cur.up[x][nt][3] - acc[nt][3]);
+          store4(Ut + jl * LDS_U + i0, to_f(cur.up[x][nt][0]) - acc[nt][0], to_f(cur.up[x][nt][1]) - acc[nt][1],
+                 to_f(cur.up[x][nt][2]) - acc[nt][2], to_f(cur.up[x][nt][3]) - acc[nt][3]);
         }
       }
     }
@@ -686,8 +710,8 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
             for (int m = 0; m < NTV; ++m)
               acc[m] = MM::mma(MM::kc(Ut, LDS_U, 16 * m, kk * MM::KS, lane), cur.mb[x][kk], acc[m]);
           const int i = 16 * ni + ccol(lane);
-          if (og && i < cd.len && i >= cd.own_from) {
-            const size_t row = size_t(a.vrows[cd.vbase + i]);
+          if (og && cur.orow[x] >= 0 && i >= cur.own) {
+            const size_t row = size_t(cur.orow[x]);
 #pragma unroll
             for (int m = 0; m < NTV; ++m)
               store4(og + (row * H + h) * DV + jvb + 16 * m + crow(lane, 0), acc[m][0], acc[m][1], acc[m][2],
@@ -696,7 +720,7 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
         }
       }
     }
-    if (cd.emit >= 0 && a.emit_pool) {
+    if (cur.emit >= 0 && a.emit_pool) {
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
         const int mt = wave + 4 * u;
@@ -706,12 +730,10 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int c = 16 * mt + crow(lane, r), jv = jvb + 16 * nt + ccol(lane);
-              a.emit_pool[((size_t(cd.emit) * H + h) * D + c) * DV + jv] = S[u][nt][r];
+              a.emit_pool[((size_t(cur.emit) * H + h) * D + c) * DV + jv] = S[u][nt][r];
             }
       }
     }
-    cur = nxt;
-    cd = cdn;
   }
   if (sd.final_idx >= 0 && a.final_pool) {
 #pragma unroll
