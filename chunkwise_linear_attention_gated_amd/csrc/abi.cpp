@@ -35,7 +35,7 @@ struct harts_dev_plan {
   int32_t* fix_off = nullptr;
   int32_t* fix_idx = nullptr;
   // workspace layout (byte offsets)
-  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0,
+  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
          off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
@@ -117,6 +117,10 @@ T* upload(const std::vector<T>& v, hipStream_t s) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Write-only region of the workspace that masked-off lanes store into, so that a
+// kernel's stores are unconditional (see RoundArgs::sink).
+constexpr size_t kSinkBytes = 64 * 1024;
+
 void free_dev(harts_dev_plan* d) {
   void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->crows, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx};
   for (void* p : ptrs)
@@ -153,7 +157,10 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.Qt = ws + d->off_Qt;
   a.ws.Mm = ws + d->off_Mm;
   a.ws.El = reinterpret_cast<float*>(ws + d->off_El);
+  a.sink = ws + d->off_sink;
   a.ws.QeffT = ws + d->off_Qe;
+  a.ws.WT = ws + d->off_WT;
+  a.ws.Kh = ws + d->off_Kh;
   a.ws.Tm = ws + d->off_Tm;
   a.ws.Xm = ws + d->off_Xm;
   a.ws.Am = ws + d->off_Am;
@@ -351,6 +358,7 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_KhT = take(MC * dk * BT * es);
       d->off_Mm = take(MC * BT * BT * es);
       d->off_El = take(MC * dk * 4);
+      d->off_sink = take(kSinkBytes);
       const size_t common = off;
       d->off_Qt = take(MC * BT * dk * es);
       d->ws_fwd = off;
@@ -360,6 +368,8 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_dh = take(MC * dv * dk * es);
       d->off_hc = take(MC * dv * dk * es);
       d->off_dhc = take(MC * dv * dk * es);
+      d->off_WT = take(MC * dk * BT * es);
+      d->off_Kh = take(MC * BT * dk * es);
       d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
       d->off_rg = take(size_t(d->p.replay_total) * H * (2 * dk + dv + 1) * 4);
       d->off_Tm = take(MC * BT * BT * es);

@@ -163,6 +163,46 @@ __device__ __forceinline__ int lane_zero() {
   return z;
 }
 
+// ---- workspace layouts read by the matrix cores -------------------------------------------
+// Fragment-major ("FM") layout of an [R][K] matrix used as a matrix-core operand with rows R
+// (the A operand's m or the B operand's n) and contraction K: every 16 x KS block is stored
+// as the 64 lanes' register contents, lane after lane, so loading an operand fragment is one
+// contiguous read per wavefront.  Lane l holds row l%16, contraction indices
+// LE*(l/16) .. LE*(l/16) + LE - 1 of its block, LE = KS/4.
+template <typename T> __host__ __device__ constexpr int fm_le() { return Mma<T>::KS / 4; }
+template <typename T> __device__ __forceinline__ size_t fm_off(int r, int k, int K) {
+  constexpr int KS = Mma<T>::KS, LE = KS / 4;
+  return ((size_t(r >> 4) * (K / KS) + k / KS) * 64 + (r & 15) + 16 * ((k % KS) / LE)) * LE + (k % LE);
+}
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag fm_frag(const T* p, int K, int rt, int kt, int lane) {
+  constexpr int KS = Mma<T>::KS, LE = KS / 4;
+  const T* q = p + ((size_t(rt) * (K / KS) + kt) * 64 + lane) * LE;
+  if constexpr (sizeof(T) == 2) return *reinterpret_cast<const bf16x8*>(q);
+  else return *q;
+}
+// store n consecutive contraction entries k0 .. k0+n-1 of row r (n = 4 or 16/sizeof(T))
+template <typename T> __device__ __forceinline__ void fm_store(T* p, int K, int r, int k0, const float* v, int n) {
+  constexpr int LE = fm_le<T>();
+  if (LE >= 4 && n <= LE) {  // the n entries are contiguous in one lane's run
+    if (n == 8) stq(p + fm_off<T>(r, k0, K), pack16<T>(v));
+    else store4(p + fm_off<T>(r, k0, K), v[0], v[1], v[2], v[3]);
+  } else {
+    for (int t = 0; t < n; ++t) p[fm_off<T>(r, k0 + t, K)] = from_f<T>(v[t]);
+  }
+}
+// Accumulator-major ("CM") layout of an [R][C] matrix of 16 x 16 result tiles: tile after
+// tile, each as the 64 lanes' four accumulator values (rows 4(l/16)..+3 of column l%16).
+__device__ __forceinline__ size_t cm_off(int r, int c, int C) {
+  return ((size_t(r >> 4) * (C / 16) + (c >> 4)) * 64 + (c & 15) + 16 * ((r & 15) >> 2)) * 4 + (r & 3);
+}
+
+// Elements of T in the store sink (RoundArgs::sink, 64 KiB)
+template <typename T> __host__ __device__ constexpr int kSinkElems() { return 64 * 1024 / sizeof(T); }
+
+// Waves of a serial state-pass workgroup: one per 16 state rows, at most 8.
+template <int D> constexpr int state_waves() { return D / 16 < 8 ? D / 16 : 8; }
+
 // Workgroup size of the persistent per-chunk kernels: 8 waves, two per SIMD.
 constexpr int CNT = 512;
 constexpr int CNW = CNT / 64;

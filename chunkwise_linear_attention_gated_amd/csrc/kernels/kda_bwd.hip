@@ -17,10 +17,11 @@
 //   dg = reverse cumulative sum of dG over the chunk.
 #include "common.h"
 #include "launch.h"
+#include "state_common.h"
 
 namespace harts {
 
-template <int D> constexpr int dv_tile_b() { return D >= 64 ? 32 : 16; }
+template <int DV> constexpr int dv_tile_b() { return DV; }  // one workgroup per (sequence, head)
 
 // Replay-gradient side buffer: per (replay position, head) dk[D], dv[DV], dg[D], dbeta.
 template <int D, int DV> struct RG {
@@ -28,25 +29,28 @@ template <int D, int DV> struct RG {
 };
 
 // ------------------------------------------------------------------------------------------
-// Serial state-gradient pass, reverse over chunks.  One workgroup per (sequence, head,
-// value-column tile).  dS (fp32) lives in accumulator registers.  The per-chunk operands
-// (W, KhT and the dO tile, staged through LDS; Qeff^T fragments and e^{G_last}) are loaded
-// one chunk ahead into registers so only LDS and matrix-core latency sit on the chain.
+// Serial state-gradient pass, reverse over chunks.  One workgroup of SNW waves per
+// (sequence, head, value-column tile of DVT).  dS (fp32) lives in accumulator registers
+// (wave w owns rows 16w..).  Per chunk:  Y = K^ dS;  dS <- diag(e^{G_last}) dS + Qeff^T dO - W^T Y.
+// The left operands (K^, W^T, Qeff^T) are register fragments read from their fragment-major
+// workspace layouts one chunk ahead; dO is staged transposed into LDS one chunk ahead
+// (double-buffered), so Qeff^T dO is formed off the chain and a step is
+// dS -> LDS -> barrier -> Y -> LDS -> barrier -> dS.
 template <typename T, int BT, int D, int DV, int DVT>
 struct DStateOps {
   using MM = Mma<T>;
   using F = typename MM::Frag;
-  static constexpr int VN = 16 / sizeof(T);
-  static constexpr int NW = (BT * (D / VN) + 255) / 256;   // 16-byte pieces of W per thread
-  static constexpr int NK = (D * (BT / VN) + 255) / 256;   // ... of KhT
-  static constexpr int NO = (BT * (DVT / VN) + 255) / 256; // ... of the dO tile
-  static constexpr int MU = (D / 16 + 3) / 4, KB = BT / MM::KS;
-  f32x4 w[NW], kh[NK], dov[NO];
-  F qe[MU][KB];
-  float el[MU][4];
-  int own, emit;
+  using TL = StateTiles<BT, D, DVT>;
+  static constexpr int NTH = 64 * TL::NW, VN = 16 / sizeof(T);
+  static constexpr int KD = D / MM::KS, KB = BT / MM::KS;
+  static constexpr int NO = (BT * (DVT / VN) + NTH - 1) / NTH;  // dO pieces per thread
+  F kh[KD];                // K^ (token-major) fragments of this wave's token block
+  F wt[TL::MU][KB];        // W^T fragments of this wave's dS rows
+  F qe[TL::MU][KB];        // Qeff^T fragments of this wave's dS rows
+  float el[TL::MU][4];     // e^{G_last} of this lane's dS rows
+  int emit;                // slot emitted after this chunk (-1: none)
+  f32x4 dov[NO];           // dO pieces of the chunk before this one (staged one step ahead)
 };
-// compact rows of this thread's dO pieces (-1: padding), fetched one step before the dO itself
 template <typename T, int BT, int D, int DV, int DVT>
 struct DStateRows {
   int r[DStateOps<T, BT, D, DV, DVT>::NO];
@@ -58,112 +62,144 @@ __device__ __forceinline__ void load_dstate_rows(DStateRows<T, BT, D, DV, DVT>& 
   using Ops = DStateOps<T, BT, D, DV, DVT>;
 #pragma unroll
   for (int x = 0; x < Ops::NO; ++x) {
-    const int idx = tid + 256 * x;
-    const int i = idx / (DVT / Ops::VN);
+    const int i = (tid + Ops::NTH * x) / (DVT / Ops::VN);
     o.r[x] = a.crows[size_t(chunk) * BT + (i < BT ? i : BT - 1)];
   }
 }
 
-// Operands of one chunk step, addressed from the chunk's round-local index and its
-// (already fetched) rows only, so none of these loads waits on another.  Loads are
-// unconditional from clamped addresses; padding and replayed rows are masked at use.
 template <typename T, int BT, int D, int DV, int DVT>
-__device__ __forceinline__ void load_dstate_ops(DStateOps<T, BT, D, DV, DVT>& o, const DStateRows<T, BT, D, DV, DVT>& rw,
-                                                const RoundArgs& a, const T* gdo, int chunk, int H, int h, int tid,
-                                                int wave, int lane, int jvb, int z) {
+__device__ __forceinline__ void load_dstate_dov(f32x4* dov, const DStateRows<T, BT, D, DV, DVT>& rw, const T* gdo,
+                                                int H, int h, int tid, int jvb) {
   using Ops = DStateOps<T, BT, D, DV, DVT>;
-  using MM = Mma<T>;
-  constexpr int VN = Ops::VN, MT = D / 16;
-  const size_t wsi = size_t(chunk) * H + h;
-  const T* wg = static_cast<const T*>(a.ws.W) + wsi * BT * D;
-  const T* kg = static_cast<const T*>(a.ws.KhT) + wsi * D * BT;
-#pragma unroll
-  for (int x = 0; x < Ops::NW; ++x) {
-    const int idx = tid + 256 * x;
-    o.w[x] = ldq(wg + (idx < BT * (D / VN) ? idx : 0) * VN);
-  }
-#pragma unroll
-  for (int x = 0; x < Ops::NK; ++x) {
-    const int idx = tid + 256 * x;
-    o.kh[x] = ldq(kg + (idx < D * (BT / VN) ? idx : 0) * VN);
-  }
 #pragma unroll
   for (int x = 0; x < Ops::NO; ++x) {
-    const int idx = tid + 256 * x;
-    const int j0 = (idx % (DVT / VN)) * VN;
+    const int j0 = ((tid + Ops::NTH * x) % (DVT / Ops::VN)) * Ops::VN;
     const int row = rw.r[x] >= 0 ? rw.r[x] : 0;
-    o.dov[x] = ldq(gdo + (size_t(row) * H + h) * DV + jvb + j0);
+    dov[x] = ldq(gdo + (size_t(row) * H + h) * DV + jvb + j0);
   }
-  o.own = a.chunks[chunk + z].own_from;
-  o.emit = a.chunks[chunk + z].emit;
-  const T* qe = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
+}
+
+// Unconditional loads from clamped addresses; padding and replayed rows are masked at use.
+template <typename T, int BT, int D, int DV, int DVT>
+__device__ __forceinline__ void load_dstate_ops(DStateOps<T, BT, D, DV, DVT>& o, const RoundArgs& a, int chunk, int H,
+                                                int h, int wave, int lane, int z) {
+  using Ops = DStateOps<T, BT, D, DV, DVT>;
+  using TL = typename Ops::TL;
+  const size_t wsi = size_t(chunk) * H + h;
+  const T* khg = static_cast<const T*>(a.ws.Kh) + wsi * BT * D;
+  const T* wtg = static_cast<const T*>(a.ws.WT) + wsi * D * BT;
+  const T* qeg = static_cast<const T*>(a.ws.QeffT) + wsi * D * BT;
   const float* el = a.ws.El + wsi * D;
+  const int mi = wave / TL::WPB;
+  o.emit = a.chunks[chunk + z].emit;
 #pragma unroll
-  for (int u = 0; u < Ops::MU; ++u) {
-    const int mt = wave + 4 * u;
-    if (mt < MT) {
+  for (int kk = 0; kk < Ops::KD; ++kk) o.kh[kk] = fm_frag<T>(khg, D, mi, kk, lane);
 #pragma unroll
-      for (int kk = 0; kk < Ops::KB; ++kk) o.qe[u][kk] = MM::kc(qe, BT, 16 * mt, kk * MM::KS, lane);
+  for (int u = 0; u < TL::MU; ++u) {
+    const int mt = wave + TL::NW * u, mc = mt < TL::MT ? mt : 0;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mt + crow(lane, r)];
+    for (int kk = 0; kk < Ops::KB; ++kk) {
+      o.wt[u][kk] = fm_frag<T>(wtg, BT, mc, kk, lane);
+      o.qe[u][kk] = fm_frag<T>(qeg, BT, mc, kk, lane);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mc + crow(lane, r)];
   }
 }
 
 template <typename T, int BT, int D, int DV, int DVT>
-__global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) {
+__global__ __launch_bounds__(64 * state_waves<D>()) void kda_dstate_kernel(BwdRoundArgs b, int H) {
   using MM = Mma<T>;
   using Ops = DStateOps<T, BT, D, DV, DVT>;
+  using TL = typename Ops::TL;
+  using Rows = DStateRows<T, BT, D, DV, DVT>;
   const RoundArgs& a = b.r;
-  constexpr int NTL = DV / DVT, PAD = 16 / sizeof(T), VN = 16 / sizeof(T);
-  constexpr int LDS_S = D + PAD, LDK = D + PAD, LDJ = BT + PAD, LDO = DVT + PAD;
-  constexpr int MT = D / 16, NTV = DVT / 16, MU = Ops::MU;
+  constexpr int NW = TL::NW, NTH = Ops::NTH, NTL = DV / DVT, PAD = 16 / sizeof(T), VN = Ops::VN;
+  constexpr int LDS_S = D + PAD, LDJ = BT + PAD;
+  constexpr int MT = TL::MT, NTV = TL::NTV, MU = TL::MU, NTU = TL::NTU, NO = Ops::NO;
   __shared__ __attribute__((aligned(16))) T dSt[DVT * LDS_S];
-  __shared__ __attribute__((aligned(16))) T Wl[BT * LDK];
-  __shared__ __attribute__((aligned(16))) T Kl[D * LDJ];
   __shared__ __attribute__((aligned(16))) T Yt[DVT * LDJ];
-  __shared__ __attribute__((aligned(16))) T dOl[BT * LDO];
+  __shared__ __attribute__((aligned(16))) T dOt[2][DVT * LDJ];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lb = xcd_logical(blockIdx.x, gridDim.x);
   const int tile = lb % NTL, h = (lb / NTL) % H, si = lb / (NTL * H);
   if (si >= a.nseq) return;
   const SeqDesc sd = a.seqs[si];
   const int jvb = tile * DVT;
+  const int mi = wave / TL::WPB, nt0 = (wave % TL::WPB) * NTU;  // this wave's token block and tile columns
   const T* gdo = static_cast<const T*>(b.dO);
+  const int N = sd.n_chunks, c0 = sd.chunk_base;
+  auto chunk_at = [&](int n) { return c0 + (n > 0 ? n : 0); };
+  // dO of chunk m, transposed into dOt[m & 1]; replayed (and padding) rows are zero
+  auto stage_dO = [&](const f32x4* dov, const Rows& rw, int m, int tid) {
+    T* dst = dOt[m & 1];
+    const int own = sd.n_replay - m * BT;
+#pragma unroll
+    for (int x = 0; x < NO; ++x) {
+      const int idx = tid + NTH * x;
+      if (idx < BT * (DVT / VN)) {
+        const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
+        float v[VN];
+        unpack16<T>(rw.r[x] >= 0 && i >= own ? dov[x] : f32x4{0.f, 0.f, 0.f, 0.f}, v);
+#pragma unroll
+        for (int t = 0; t < VN; ++t) dst[(j0 + t) * LDJ + i] = from_f<T>(v[t]);
+      }
+    }
+  };
   f32x4 dS[MU][NTV];
 #pragma unroll
   for (int u = 0; u < MU; ++u)
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) dS[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  using Rows = DStateRows<T, BT, D, DV, DVT>;
-  Ops cur, nxt;
-  // cur_rows: rows of chunk n; rows_x: rows of the chunk whose operands are in nxt;
-  // rows_n: rows of the chunk before that.  cur is taken from nxt at the top of each
-  // step, before the next fetch is issued.
-  Rows cur_rows, rows_x, rows_n;
+  // nxt: operands of chunk n with the dO of chunk n-1; rows_x: rows of the chunk whose
+  // dO is in nxt; rows_n: rows of the chunk before that.  cur is taken from nxt at the
+  // top of each step, before the next fetch is issued.
   const int z = lane_zero();
+  Ops cur, nxt;
+  Rows cur_rows, rows_x, rows_n;
   {
-    const int last = sd.chunk_base + sd.n_chunks - 1;
-    load_dstate_rows<T, BT, D, DV, DVT>(rows_x, a, last, tid);
-    load_dstate_ops<T, BT, D, DV, DVT>(nxt, rows_x, a, gdo, last, H, h, tid, wave, lane, jvb, z);
-    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, sd.chunk_base + (sd.n_chunks > 1 ? sd.n_chunks - 2 : 0), tid);
+    Rows r0;
+    f32x4 d0[NO];
+    load_dstate_rows<T, BT, D, DV, DVT>(r0, a, chunk_at(N - 1), tid);
+    load_dstate_dov<T, BT, D, DV, DVT>(d0, r0, gdo, H, h, tid, jvb);
+    stage_dO(d0, r0, N - 1, tid);
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_x, a, chunk_at(N - 2), tid);
+    load_dstate_ops<T, BT, D, DV, DVT>(nxt, a, chunk_at(N - 1), H, h, wave, lane, z);
+    load_dstate_dov<T, BT, D, DV, DVT>(nxt.dov, rows_x, gdo, H, h, tid, jvb);
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, chunk_at(N - 3), tid);
   }
-  for (int n = sd.n_chunks - 1; n >= 0; --n) {
-    const size_t wsi = size_t(sd.chunk_base + n) * H + h;
+  __syncthreads();
+  for (int n = N - 1; n >= 0; --n) {
+    // thread-derived addresses are recomputed per step instead of being held across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
+    const size_t wsi = size_t(c0 + n) * H + h;
     cur = nxt;
     cur_rows = rows_x;
-    // fetch ahead: operands of chunk n-1 (its rows are already here), rows of chunk n-2
-    load_dstate_ops<T, BT, D, DV, DVT>(nxt, rows_n, a, gdo, sd.chunk_base + (n > 0 ? n - 1 : 0), H, h, tid, wave,
-                                       lane, jvb, z);
+    // fetch ahead: operands of chunk n-1, dO of chunk n-2 (its rows are here), rows of chunk n-3
+    load_dstate_ops<T, BT, D, DV, DVT>(nxt, a, chunk_at(n - 1), H, h, wave, lane, z);
+    load_dstate_dov<T, BT, D, DV, DVT>(nxt.dov, rows_n, gdo, H, h, tid, jvb);
     rows_x = rows_n;
-    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, sd.chunk_base + (n > 1 ? n - 2 : 0), tid);
-    __syncthreads();
+    load_dstate_rows<T, BT, D, DV, DVT>(rows_n, a, chunk_at(n - 3), tid);
+    // Qeff^T dO (independent of dS)
+    f32x4 a1[MU][NTV];
+    const T* dOc = dOt[n & 1];
+#pragma unroll
+    for (int u = 0; u < MU; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NTV; ++nt) {
+        a1[u][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < Ops::KB; ++kk)
+          a1[u][nt] = MM::mma(cur.qe[u][kk], MM::kc(dOc, LDJ, 16 * nt, kk * MM::KS, lane), a1[u][nt]);
+      }
     // slot gradient: sum over the consumers of the state emitted after this chunk
     if (cur.emit >= 0 && b.slot_cons_off) {
       const int q0 = b.slot_cons_off[cur.emit], q1 = b.slot_cons_off[cur.emit + 1];
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
-        const int mt = wave + 4 * u;
+        const int mt = wave + NW * u;
         if (mt < MT)
 #pragma unroll
           for (int nt = 0; nt < NTV; ++nt)
@@ -180,94 +216,44 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
     }
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
           store4(dSt + (16 * nt + ccol(lane)) * LDS_S + 16 * mt + crow(lane, 0), dS[u][nt][0], dS[u][nt][1],
                  dS[u][nt][2], dS[u][nt][3]);
     }
-#pragma unroll
-    for (int x = 0; x < Ops::NW; ++x) {
-      const int idx = tid + 256 * x;
-      if (idx < BT * (D / VN)) {
-        const int i = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-        *reinterpret_cast<f32x4*>(Wl + i * LDK + c0) = cur.w[x];
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < Ops::NK; ++x) {
-      const int idx = tid + 256 * x;
-      if (idx < D * (BT / VN)) {
-        const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
-        *reinterpret_cast<f32x4*>(Kl + c * LDJ + i0) = cur.kh[x];
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < Ops::NO; ++x) {
-      const int idx = tid + 256 * x;
-      if (idx < BT * (DVT / VN)) {
-        const int i = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-        const bool ok = cur_rows.r[x] >= 0 && i >= cur.own;
-        *reinterpret_cast<f32x4*>(dOl + i * LDO + j0) = ok ? cur.dov[x] : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-    }
+    if (n > 0) stage_dO(cur.dov, cur_rows, n - 1, tid);
     __syncthreads();
-    {
-      // gradient w.r.t. the chunk-end state, for the per-chunk gradient kernels:
-      // value-major (dS^T) and channel-major (dS)
-      T* dhg = static_cast<T*>(b.dh) + wsi * DV * D;
-      T* dhcg = static_cast<T*>(b.dhc) + wsi * D * DV;
-      for (int idx = tid; idx < DVT * (D / VN); idx += 256) {
-        const int jl = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-        copy16(dhg + (jvb + jl) * D + c0, dSt + jl * LDS_S + c0);
-      }
-      for (int idx = tid; idx < D * (DVT / VN); idx += 256) {
-        const int c = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-        float v[VN];
+    // Y = K^ dS  (stored transposed; this wave: token block mi, value tiles nt0 ..)
 #pragma unroll
-        for (int t = 0; t < VN; ++t) v[t] = to_f(dSt[(j0 + t) * LDS_S + c]);
-        stq(dhcg + c * DV + jvb + j0, pack16<T>(v));
-      }
+    for (int j = 0; j < NTU; ++j) {
+      const int nt = nt0 + j;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < Ops::KD; ++kk)
+        acc = MM::mma(cur.kh[kk], MM::kc(dSt, LDS_S, 16 * nt, kk * MM::KS, lane), acc);
+      store4(Yt + (16 * nt + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
     }
-    // Y = K^ dS  (stored transposed)
-    for (int mi = wave; mi < BT / 16; mi += 4) {
-      f32x4 acc[NTV];
-#pragma unroll
-      for (int nt = 0; nt < NTV; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < D; k0 += MM::KS) {
-        const auto af = MM::rc(Kl, LDJ, 16 * mi, k0, lane);
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) acc[nt] = MM::mma(af, MM::kc(dSt, LDS_S, 16 * nt, k0, lane), acc[nt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTV; ++nt)
-        store4(Yt + (16 * nt + ccol(lane)) * LDJ + 16 * mi + crow(lane, 0), acc[nt][0], acc[nt][1], acc[nt][2],
-               acc[nt][3]);
-    }
+    // gradient w.r.t. the chunk-end state for the per-chunk gradient kernels (dS^T and dS,
+    // fragment-major); dSt is rewritten only after the next barrier
+    store_state_fm<T, D, DV, DVT, NTH>(static_cast<T*>(b.dh) + wsi * DV * D, static_cast<T*>(b.dhc) + wsi * D * DV,
+                                       dSt, LDS_S, jvb, tid);
     __syncthreads();
     // dS <- diag(e^{G_last}) dS + Qeff^T dO - W^T Y
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT) {
-        f32x4 a1[NTV], a2[NTV];
 #pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) a1[nt] = a2[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int nt = 0; nt < NTV; ++nt) {
+          f32x4 a2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < Ops::KB; ++kk) {
-          const auto f2 = MM::rc(Wl, LDK, 16 * mt, kk * MM::KS, lane);
+          for (int kk = 0; kk < Ops::KB; ++kk)
+            a2 = MM::mma(cur.wt[u][kk], MM::kc(Yt, LDJ, 16 * nt, kk * MM::KS, lane), a2);
 #pragma unroll
-          for (int nt = 0; nt < NTV; ++nt) {
-            a1[nt] = MM::mma(cur.qe[u][kk], MM::rc(dOl, LDO, 16 * nt, kk * MM::KS, lane), a1[nt]);
-            a2[nt] = MM::mma(f2, MM::kc(Yt, LDJ, 16 * nt, kk * MM::KS, lane), a2[nt]);
-          }
+          for (int r = 0; r < 4; ++r) dS[u][nt][r] = cur.el[u][r] * dS[u][nt][r] + a1[u][nt][r] - a2[r];
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int nt = 0; nt < NTV; ++nt) dS[u][nt][r] = cur.el[u][r] * dS[u][nt][r] + a1[nt][r] - a2[nt][r];
       }
     }
   }
@@ -275,7 +261,7 @@ __global__ __launch_bounds__(256) void kda_dstate_kernel(BwdRoundArgs b, int H) 
     const size_t gs = size_t(a.seq0 + si);
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
@@ -421,8 +407,8 @@ __device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, B
   const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
-    o.hf[ks] = MM::kc(hg, D, 16 * wave, ks * MM::KS, lane);
-    o.dhf[ks] = MM::kc(dhg, D, 16 * wave, ks * MM::KS, lane);
+    o.hf[ks] = fm_frag<T>(hg, D, wave, ks, lane);
+    o.dhf[ks] = fm_frag<T>(dhg, D, wave, ks, lane);
   }
 }
 
@@ -517,9 +503,20 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       if (p < C::NPJ) {
         const int i = p / (BT / VN), j0 = (p % (BT / VN)) * VN;
         stq(Tl + i * LDJ + j0, cur.tm[x]);
-        stq(Ml + i * LDJ + j0, cur.mm[x]);
         stq(Xl + i * LDJ + j0, cur.xm[x]);
         stq(Al + i * LDJ + j0, cur.am[x]);
+        // M arrives fragment-major: element o of the piece is row r, column k of M
+        {
+          constexpr int LE = fm_le<T>(), KS = MM::KS;
+          float mv[VN];
+          unpack16<T>(cur.mm[x], mv);
+#pragma unroll
+          for (int e = 0; e < VN; ++e) {
+            const int o = p * VN + e, li = o / LE, f = li / 64, l = li % 64;
+            const int r = (f / (BT / KS)) * 16 + (l & 15), k = (f % (BT / KS)) * KS + LE * (l >> 4) + o % LE;
+            Ml[r * LDJ + k] = from_f<T>(mv[e]);
+          }
+        }
       }
     }
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
@@ -854,8 +851,8 @@ __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, B
   const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) {
-    o.hc[ks] = MM::kc(hcg, DV, 16 * wave, ks * MM::KS, lane);
-    o.dhc[ks] = MM::kc(dhcg, DV, 16 * wave, ks * MM::KS, lane);
+    o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
+    o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
   }
 }
 
@@ -1153,7 +1150,7 @@ static hipError_t dstate_launch(const KdaDims& d, const BwdRoundArgs& b, hipStre
   constexpr int DVT = dv_tile_b<DV>();
   unsigned n = unsigned(b.r.nseq) * d.H * (DV / DVT);
   n = (n + 7) / 8 * 8;
-  hipLaunchKernelGGL((kda_dstate_kernel<T, BT, D, DV, DVT>), dim3(n), dim3(256), 0, s, b, d.H);
+  hipLaunchKernelGGL((kda_dstate_kernel<T, BT, D, DV, DVT>), dim3(n), dim3(64 * state_waves<D>()), 0, s, b, d.H);
   return hipGetLastError();
 }
 

@@ -17,6 +17,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "state_common.h"
 
 namespace harts {
 
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
-          store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
+          fm_store<T>(Mg, BT, i, j0, v, 4);
           if (BWD) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         }
       }
@@ -348,8 +349,9 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           kh[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lr[x][t]) * EH[b * D + c0 + t];
         }
         stq(Kt + i * LDK + c0, pack16<T>(kt));
+        if (BWD) fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
         if (BWD) stq(Qr + i * LDK + c0, pack16<T>(qt));
-        else stq(static_cast<T*>(a.ws.Qt) + wsi * BT * D + i * D + c0, pack16<T>(qt));
+        else fm_store<T>(static_cast<T*>(a.ws.Qt) + wsi * BT * D, D, i, c0, qt, VN);
 #pragma unroll
         for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kh[t]);
       }
@@ -413,7 +415,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
         for (int k0 = 0; k0 < BT; k0 += MM::KS)
           acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
-        store4(upg + (16 * nt + ccol(lane)) * BT + 16 * mt + crow(lane, 0), acc[0], acc[1], acc[2], acc[3]);
+        store4(upg + cm_off(16 * mt + crow(lane, 0), 16 * nt + ccol(lane), DV), acc[0], acc[1], acc[2], acc[3]);
       }
       if constexpr (BWD) {
 #pragma unroll
@@ -427,7 +429,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             for (int k0 = 0; k0 < BT; k0 += MM::KS)
               wacc[u] = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), wacc[u]);
             const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-            store4(wg + i * D + c0, wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]);
+            const float wv[4] = {wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]};
+            fm_store<T>(wg, D, i, c0, wv, 4);
+            T* wtg = static_cast<T*>(a.ws.WT) + wsi * D * BT;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
           }
         }
       } else {
@@ -439,13 +445,16 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           for (int k0 = 0; k0 < BT; k0 += MM::KS)
             acc = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), acc);
           const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-          store4(wg + i * D + c0, acc[0], acc[1], acc[2], acc[3]);
+          const float wv[4] = {acc[0], acc[1], acc[2], acc[3]};
+          fm_store<T>(wg, D, i, c0, wv, 4);
         }
       }
       T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
       HARTS_STRIDED(idx, tid, D * (BT / VN), CNT) {
         const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
-        copy16(khg + c * BT + i0, KhT + c * LDJ + i0);
+        float kv[VN];
+        ld16(KhT + c * LDJ + i0, kv);
+        fm_store<T>(khg, BT, c, i0, kv, VN);
       }
       if constexpr (BWD) {
         const size_t BB = size_t(BT) * BT;
@@ -489,7 +498,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
-          store4(qe + c * BT + i0, v[0], v[1], v[2], v[3]);
+          fm_store<T>(qe, BT, c, i0, v, 4);
         }
       }
     }
@@ -499,96 +508,79 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Serial state pass.  One workgroup (4 waves) per (sequence, head, value-column tile of DVT):
-// the columns of S evolve independently.  Per chunk:
+// Serial state pass.  One workgroup of SNW waves per (sequence, head, value-column tile of
+// DVT): the columns of S evolve independently.  Per chunk:
 //   U = U' - W S;  [forward] O^T = S^T Q~^T + U^T M^T;  S = diag(e^{G_last}) S + KhT U.
-// S lives in accumulator registers (fp32); S^T and U^T are staged in LDS as MFMA operands.
-// Every per-chunk operand that does not depend on S (W, U', Q~, M, KhT, e^{G_last}) is
-// loaded one chunk ahead into registers, so the chain S -> U -> S only waits on LDS and
-// the matrix cores.  Backward mode writes S^T of every chunk start (the recomputed
-// chunk-start states).
+// S lives in accumulator registers (fp32; wave w owns state rows 16w..); S^T and U^T are
+// staged in LDS as matrix-core operands.  Every per-chunk operand that does not depend on S
+// (W, U', Q~, M, KhT, e^{G_last}, the output rows) is read from its fragment-major
+// workspace layout one chunk ahead into registers, so a step is
+// S -> LDS -> barrier -> U -> LDS -> barrier -> S on the matrix cores.  Backward mode
+// writes the chunk-start states (S^T and S, fragment-major) after the second barrier.
 template <typename T, int BT, int D, int DV, int DVT, bool FWD>
 struct StateOps {
   using MM = Mma<T>;
   using F = typename MM::Frag;
-  static constexpr int NMI = (BT / 16 + 3) / 4, MU = (D / 16 + 3) / 4, NTV = DVT / 16;
-  static constexpr int KD = D / MM::KS, KB = BT / MM::KS;
-  static constexpr int NQ = FWD ? NMI : 1, KQ = FWD ? KD : 1, KM = FWD ? KB : 1;
   using Raw4 = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
-  F wa[NMI][KD];        // W fragments (A operand of U = W S), token rows of this wave
-  Raw4 up[NMI][NTV];    // U' at this lane's accumulator positions (converted at use)
-  F qb[NQ][KQ];         // Q~ fragments (B operand of O^T), forward only
-  F mb[NQ][KM];         // M fragments (B operand of O^T), forward only
-  F ka[MU][KB];         // KhT fragments (A operand of S += KhT U)
-  float el[MU][4];      // e^{G_last} of this lane's state rows
-  int own, emit;        // first own row, emitted slot (-1: none)
-  int orow[NQ];         // forward: compact row of this lane's output token per token block (-1: padding)
+  using TL = StateTiles<BT, D, DVT>;
+  static constexpr int KD = D / MM::KS, KB = BT / MM::KS;
+  static constexpr int KQ = FWD ? KD : 1, KM = FWD ? KB : 1;
+  F wa[KD];               // W fragments of this wave's token block (A operand of W S)
+  Raw4 up[TL::NTU];       // U' at this lane's accumulator positions of its U tiles
+  F qb[KQ];               // forward: Q~ fragments of the token block (B operand of the output)
+  F mb[KM];               // forward: M fragments of the token block (B operand of the output)
+  F ka[TL::MU][KB];       // KhT fragments (A operand of S += KhT U)
+  float el[TL::MU][4];    // e^{G_last} of this lane's state rows
+  int emit;               // emitted slot (-1: none)
+  int orow;               // forward: compact row of this lane's output token (-1: padding)
 };
 
-// Everything a chunk step needs that does not depend on the state, addressed from the
-// chunk's round-local index alone (a sequence's chunks are consecutive), so the loads of
-// the next step never wait on a descriptor.
 template <typename T, int BT, int D, int DV, int DVT, bool FWD>
 __device__ __forceinline__ void load_state_ops(StateOps<T, BT, D, DV, DVT, FWD>& o, const RoundArgs& a, int chunk,
                                                int h, int H, int wave, int lane, int jvb, int z) {
   using Ops = StateOps<T, BT, D, DV, DVT, FWD>;
-  using MM = Mma<T>;
-  constexpr int MT = D / 16;
+  using TL = typename Ops::TL;
   const ChunkWs& ws = a.ws;
   const size_t wsi = size_t(chunk) * H + h;
-  o.own = a.chunks[chunk + z].own_from;
-  o.emit = a.chunks[chunk + z].emit;
-  if constexpr (FWD) {
-#pragma unroll
-    for (int x = 0; x < Ops::NQ; ++x) {
-      const int mi = wave + 4 * x;
-      o.orow[x] = a.crows[size_t(chunk) * BT + (mi < BT / 16 ? 16 * mi : 0) + (lane & 15)];
-    }
-  }
+  const int mi = wave / TL::WPB, nt0 = jvb / 16 + (wave % TL::WPB) * TL::NTU;
   const T* wg = static_cast<const T*>(ws.W) + wsi * BT * D;
-  const T* upg = static_cast<const T*>(ws.UpT) + wsi * DV * BT;
+  const T* upg = static_cast<const T*>(ws.UpT) + wsi * BT * DV;
   const T* khg = static_cast<const T*>(ws.KhT) + wsi * D * BT;
   const float* el = ws.El + wsi * D;
+  o.emit = a.chunks[chunk + z].emit;
 #pragma unroll
-  for (int x = 0; x < Ops::NMI; ++x) {
-    const int mi = wave + 4 * x;
-    if (mi < BT / 16) {
+  for (int kk = 0; kk < Ops::KD; ++kk) o.wa[kk] = fm_frag<T>(wg, D, mi, kk, lane);
 #pragma unroll
-      for (int kk = 0; kk < Ops::KD; ++kk) o.wa[x][kk] = MM::kc(wg, D, 16 * mi, kk * MM::KS, lane);
+  for (int j = 0; j < TL::NTU; ++j)
+    o.up[j] = *reinterpret_cast<const typename Ops::Raw4*>(upg + ((size_t(mi) * (DV / 16) + nt0 + j) * 64 + lane) * 4);
+  if constexpr (FWD) {
+    const T* qg = static_cast<const T*>(ws.Qt) + wsi * BT * D;
+    const T* mg = static_cast<const T*>(ws.Mm) + wsi * BT * BT;
 #pragma unroll
-      for (int nt = 0; nt < Ops::NTV; ++nt)
-        o.up[x][nt] = *reinterpret_cast<const typename Ops::Raw4*>(upg + (jvb + 16 * nt + ccol(lane)) * BT + 16 * mi +
-                                                                  crow(lane, 0));
-      if constexpr (FWD) {
-        const T* qg = static_cast<const T*>(ws.Qt) + wsi * BT * D;
-        const T* mg = static_cast<const T*>(ws.Mm) + wsi * BT * BT;
+    for (int kk = 0; kk < Ops::KD; ++kk) o.qb[kk] = fm_frag<T>(qg, D, mi, kk, lane);
 #pragma unroll
-        for (int kk = 0; kk < Ops::KD; ++kk) o.qb[x][kk] = MM::kc(qg, D, 16 * mi, kk * MM::KS, lane);
-#pragma unroll
-        for (int kk = 0; kk < Ops::KB; ++kk) o.mb[x][kk] = MM::kc(mg, BT, 16 * mi, kk * MM::KS, lane);
-      }
-    }
+    for (int kk = 0; kk < Ops::KB; ++kk) o.mb[kk] = fm_frag<T>(mg, BT, mi, kk, lane);
+    o.orow = a.crows[size_t(chunk) * BT + 16 * mi + ccol(lane)];
   }
 #pragma unroll
-  for (int u = 0; u < Ops::MU; ++u) {
-    const int mt = wave + 4 * u;
-    if (mt < MT) {
+  for (int u = 0; u < TL::MU; ++u) {
+    const int mt = wave + TL::NW * u, mc = mt < TL::MT ? mt : 0;
 #pragma unroll
-      for (int kk = 0; kk < Ops::KB; ++kk) o.ka[u][kk] = MM::kc(khg, BT, 16 * mt, kk * MM::KS, lane);
+    for (int kk = 0; kk < Ops::KB; ++kk) o.ka[u][kk] = fm_frag<T>(khg, BT, mc, kk, lane);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mt + crow(lane, r)];
-    }
+    for (int r = 0; r < 4; ++r) o.el[u][r] = el[16 * mc + crow(lane, r)];
   }
 }
 
 template <typename T, int BT, int D, int DV, int DVT, bool BWD>
-__global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
+__global__ __launch_bounds__(64 * state_waves<D>()) void kda_state_kernel(RoundArgs a, int H) {
   using MM = Mma<T>;
   using Ops = StateOps<T, BT, D, DV, DVT, !BWD>;
-  constexpr int NTL = DV / DVT;
+  using TL = typename Ops::TL;
+  constexpr int NW = TL::NW, NTL = DV / DVT, NTV = TL::NTV, MT = TL::MT, MU = TL::MU, NTU = TL::NTU;
   constexpr int PAD = 16 / sizeof(T);
   constexpr int LDS_S = D + PAD, LDS_U = BT + PAD;
-  constexpr int MT = D / 16, NTV = DVT / 16, MU = Ops::MU, NMI = Ops::NMI;
+  constexpr int NTH = 64 * NW;
   __shared__ __attribute__((aligned(16))) T St[2][DVT * LDS_S];
   __shared__ __attribute__((aligned(16))) T Ut[DVT * LDS_U];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -597,12 +589,13 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
   if (si >= a.nseq) return;
   const SeqDesc sd = a.seqs[si];
   const int jvb = tile * DVT;
+  const int mi = wave / TL::WPB, nt0 = (wave % TL::WPB) * NTU;  // this wave's token block and tile columns
   f32x4 S[MU][NTV];
 #pragma unroll
   for (int u = 0; u < MU; ++u)
 #pragma unroll
     for (int nt = 0; nt < NTV; ++nt) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float v = 0.f;
@@ -619,14 +612,19 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
   const int z = lane_zero();
   load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a, sd.chunk_base, h, H, wave, lane, jvb, z);
   for (int n = 0; n < sd.n_chunks; ++n) {
+    // thread-derived addresses are recomputed per step instead of being held across the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63;
     const size_t wsi = size_t(sd.chunk_base + n) * H + h;
+    const int own = sd.n_replay - n * BT;  // replayed rows sit at the front of the first chunk
     cur = nxt;
     load_state_ops<T, BT, D, DV, DVT, !BWD>(nxt, a, sd.chunk_base + (n + 1 < sd.n_chunks ? n + 1 : n), h, H, wave,
                                             lane, jvb, z);
     T* Sb = St[n & 1];
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
@@ -634,49 +632,22 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
                  S[u][nt][2], S[u][nt][3]);
     }
     __syncthreads();
-    if constexpr (BWD) {
-      // chunk-start state, value-major (S^T) and channel-major (S)
-      T* hg = static_cast<T*>(a.h) + wsi * DV * D;
-      T* hcg = static_cast<T*>(a.hc) + wsi * D * DV;
-      constexpr int VN = 16 / sizeof(T);
-      for (int idx = tid; idx < DVT * (D / VN); idx += 256) {
-        const int jl = idx / (D / VN), c0 = (idx % (D / VN)) * VN;
-        copy16(hg + (jvb + jl) * D + c0, Sb + jl * LDS_S + c0);
-      }
-      for (int idx = tid; idx < D * (DVT / VN); idx += 256) {
-        const int c = idx / (DVT / VN), j0 = (idx % (DVT / VN)) * VN;
-        float v[VN];
+    // (a) U = U' - W S  (this wave: token block mi, value tiles nt0 ..)
 #pragma unroll
-        for (int t = 0; t < VN; ++t) v[t] = to_f(Sb[(j0 + t) * LDS_S + c]);
-        stq(hcg + c * DV + jvb + j0, pack16<T>(v));
-      }
-    }
-    // (a) U = U' - W S
+    for (int j = 0; j < NTU; ++j) {
+      const int nt = nt0 + j;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int x = 0; x < NMI; ++x) {
-      const int mi = wave + 4 * x;
-      if (mi < BT / 16) {
-        f32x4 acc[NTV];
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < Ops::KD; ++kk)
-#pragma unroll
-          for (int nt = 0; nt < NTV; ++nt)
-            acc[nt] = MM::mma(cur.wa[x][kk], MM::kc(Sb, LDS_S, 16 * nt, kk * MM::KS, lane), acc[nt]);
-#pragma unroll
-        for (int nt = 0; nt < NTV; ++nt) {
-          const int jl = 16 * nt + ccol(lane), i0 = 16 * mi + crow(lane, 0);
-          store4(Ut + jl * LDS_U + i0, to_f(cur.up[x][nt][0]) - acc[nt][0], to_f(cur.up[x][nt][1]) - acc[nt][1],
-                 to_f(cur.up[x][nt][2]) - acc[nt][2], to_f(cur.up[x][nt][3]) - acc[nt][3]);
-        }
-      }
+      for (int kk = 0; kk < Ops::KD; ++kk)
+        acc = MM::mma(cur.wa[kk], MM::kc(Sb, LDS_S, 16 * nt, kk * MM::KS, lane), acc);
+      store4(Ut + (16 * nt + ccol(lane)) * LDS_U + 16 * mi + crow(lane, 0), to_f(cur.up[j][0]) - acc[0],
+             to_f(cur.up[j][1]) - acc[1], to_f(cur.up[j][2]) - acc[2], to_f(cur.up[j][3]) - acc[3]);
     }
     __syncthreads();
-    // (b) S = diag(e^{G_last}) S + KhT U   (the chain: issued before the output products)
+    // (b) S = diag(e^{G_last}) S + KhT U   (the chain: issued before the side work below)
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -689,41 +660,34 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
             S[u][nt] = MM::mma(cur.ka[u][kk], MM::kc(Ut, LDS_U, 16 * nt, kk * MM::KS, lane), S[u][nt]);
       }
     }
-    if constexpr (!BWD) {
-      // O^T = S^T Q~^T + U^T M^T for own rows
+    if constexpr (BWD) {
+      // chunk-start state for the per-chunk gradient kernels; Sb is next written two steps on
+      store_state_fm<T, D, DV, DVT, NTH>(static_cast<T*>(a.h) + wsi * DV * D, static_cast<T*>(a.hc) + wsi * D * DV,
+                                         Sb, LDS_S, jvb, tid);
+    } else {
+      // O^T = S^T Q~^T + U^T M^T for own rows; lanes without a row store into the sink
       T* og = static_cast<T*>(a.o);
+      const int i = 16 * mi + ccol(lane);
+      const bool ok = og && cur.orow >= 0 && i >= own;
 #pragma unroll
-      for (int x = 0; x < NMI; ++x) {
-        const int ni = wave + 4 * x;
-        if (ni < BT / 16) {
-          f32x4 acc[NTV];
+      for (int j = 0; j < NTU; ++j) {
+        const int m = nt0 + j;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int m = 0; m < NTV; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < Ops::KD; ++kk)
+          acc = MM::mma(MM::kc(Sb, LDS_S, 16 * m, kk * MM::KS, lane), cur.qb[kk], acc);
 #pragma unroll
-          for (int kk = 0; kk < Ops::KD; ++kk)
-#pragma unroll
-            for (int m = 0; m < NTV; ++m)
-              acc[m] = MM::mma(MM::kc(Sb, LDS_S, 16 * m, kk * MM::KS, lane), cur.qb[x][kk], acc[m]);
-#pragma unroll
-          for (int kk = 0; kk < Ops::KB; ++kk)
-#pragma unroll
-            for (int m = 0; m < NTV; ++m)
-              acc[m] = MM::mma(MM::kc(Ut, LDS_U, 16 * m, kk * MM::KS, lane), cur.mb[x][kk], acc[m]);
-          const int i = 16 * ni + ccol(lane);
-          if (og && cur.orow[x] >= 0 && i >= cur.own) {
-            const size_t row = size_t(cur.orow[x]);
-#pragma unroll
-            for (int m = 0; m < NTV; ++m)
-              store4(og + (row * H + h) * DV + jvb + 16 * m + crow(lane, 0), acc[m][0], acc[m][1], acc[m][2],
-                     acc[m][3]);
-          }
-        }
+        for (int kk = 0; kk < Ops::KB; ++kk)
+          acc = MM::mma(MM::kc(Ut, LDS_U, 16 * m, kk * MM::KS, lane), cur.mb[kk], acc);
+        T* dst = ok ? og + (size_t(cur.orow) * H + h) * DV + jvb + 16 * m + crow(lane, 0)
+                    : static_cast<T*>(a.sink) + (tid * 4) % kSinkElems<T>();
+        store4(dst, acc[0], acc[1], acc[2], acc[3]);
       }
     }
     if (cur.emit >= 0 && a.emit_pool) {
 #pragma unroll
       for (int u = 0; u < MU; ++u) {
-        const int mt = wave + 4 * u;
+        const int mt = wave + NW * u;
         if (mt < MT)
 #pragma unroll
           for (int nt = 0; nt < NTV; ++nt)
@@ -738,7 +702,7 @@ __global__ __launch_bounds__(256) void kda_state_kernel(RoundArgs a, int H) {
   if (sd.final_idx >= 0 && a.final_pool) {
 #pragma unroll
     for (int u = 0; u < MU; ++u) {
-      const int mt = wave + 4 * u;
+      const int mt = wave + NW * u;
       if (mt < MT)
 #pragma unroll
         for (int nt = 0; nt < NTV; ++nt)
@@ -761,7 +725,7 @@ static hipError_t prep_launch(const KdaDims& d, const RoundArgs& a, bool bwd, hi
   return hipGetLastError();
 }
 
-template <int D> constexpr int dv_tile() { return D >= 64 ? 32 : 16; }
+template <int DV> constexpr int dv_tile() { return DV; }  // one workgroup per (sequence, head)
 
 template <typename T, int BT, int D, int DV>
 static hipError_t state_launch(const KdaDims& d, const RoundArgs& a, bool bwd, hipStream_t s) {
@@ -769,7 +733,7 @@ static hipError_t state_launch(const KdaDims& d, const RoundArgs& a, bool bwd, h
   constexpr int DVT = dv_tile<DV>();
   unsigned n = unsigned(a.nseq) * d.H * (DV / DVT);
   n = (n + 7) / 8 * 8;
-  dim3 grid(n), block(256);
+  dim3 grid(n), block(64 * state_waves<D>());
   if (bwd) hipLaunchKernelGGL((kda_state_kernel<T, BT, D, DV, DVT, true>), grid, block, 0, s, a, d.H);
   else hipLaunchKernelGGL((kda_state_kernel<T, BT, D, DV, DVT, false>), grid, block, 0, s, a, d.H);
   return hipGetLastError();

@@ -19,6 +19,8 @@ struct ChunkWs {
   void* Mm;     // [BT][BT]  M = lower(gated Q K^T)
   float* El;    // [D]       e^{G_last}
   void* QeffT;  // [D][BT]   (Q~ - M W)^T                          (backward)
+  void* WT;     // [D][BT]   W^T                                   (backward)
+  void* Kh;     // [BT][D]   K * e^{G_last - G}                    (backward, token-major)
   void* Tm;     // [BT][BT]  T = X diag(beta)                      (backward)
   void* Xm;     // [BT][BT]  X = (I + diag(beta) A)^{-1}           (backward)
   void* Am;     // [BT][BT]  A (strictly lower)                    (backward)
@@ -45,6 +47,8 @@ struct RoundArgs {
   float* emit_pool;           // emitted states by ChunkDesc::emit
   float* final_pool;          // final states by SeqDesc::final_idx
   ChunkWs ws;
+  void* sink;                 // >= 64 KiB that lanes with nothing to store write into: stores stay
+                              // unconditional, so the wait counters see the same count on every path
   void* h;                    // backward: S_n^T per chunk [chunk][H][DV][D] (nullable)
   void* hc;                   // backward: S_n per chunk, channel-major [chunk][H][D][DV] (nullable)
 };
