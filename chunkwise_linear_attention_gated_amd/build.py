@@ -19,7 +19,9 @@ ARCH = os.environ.get("HARTS_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc")]
 # device code: no packed-fp32 instructions (they are not used on this target)
-DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+DEVICE = ["--offload-arch=" + ARCH, "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # matrix-core accumulators in VGPRs: avoids accumulator shuffles across loop iterations
+          "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def _compile(src: str, obj: str, device: bool) -> str:

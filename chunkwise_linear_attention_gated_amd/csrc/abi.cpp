@@ -34,9 +34,11 @@ struct harts_dev_plan {
   int32_t* fix_rows = nullptr;
   int32_t* fix_off = nullptr;
   int32_t* fix_idx = nullptr;
+  int32_t* rslots = nullptr;           // slots produced per round (concatenated)
+  std::vector<int32_t> rslot_off;      // [n_rounds + 1] offsets into rslots
   // workspace layout (byte offsets)
-  size_t off_W = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
-         off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0;
+  size_t off_W = 0, off_Op = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
+         off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0, off_dslot = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
 };
 
@@ -122,7 +124,8 @@ size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 constexpr size_t kSinkBytes = 64 * 1024;
 
 void free_dev(harts_dev_plan* d) {
-  void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->crows, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx};
+  void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->crows, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx,
+                  d->rslots};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -168,6 +171,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.dR = ws + d->off_dR;
   a.ws.dM = ws + d->off_dM;
   a.ws.dA = ws + d->off_dA;
+  a.ws.Op = ws + d->off_Op;
   a.h = ws + d->off_h;
   a.hc = ws + d->off_hc;
   return a;
@@ -343,6 +347,15 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->fix_rows = upload(d->p.fix_rows, s);
       d->fix_off = upload(d->p.fix_off, s);
       d->fix_idx = upload(d->p.fix_idx, s);
+      std::vector<int32_t> rsl;
+      d->rslot_off.assign(1, 0);
+      for (const harts::RoundRange& rr : d->p.rounds) {
+        if (!d->p.varlen)
+          for (int32_t c = rr.chunk0; c < rr.chunk1; ++c)
+            if (d->p.chunk_desc[size_t(c)].emit >= 0) rsl.push_back(d->p.chunk_desc[size_t(c)].emit);
+        d->rslot_off.push_back(int32_t(rsl.size()));
+      }
+      d->rslots = upload(rsl, s);
       // the host vectors must outlive the asynchronous copies
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       const size_t es = dtype == HARTS_DTYPE_BF16 ? 2 : 4;
@@ -361,6 +374,7 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_sink = take(kSinkBytes);
       const size_t common = off;
       d->off_Qt = take(MC * BT * dk * es);
+      d->off_Op = take(MC * BT * dv * es);
       d->ws_fwd = off;
       off = common;
       d->off_Qe = take(MC * dk * BT * es);
@@ -379,6 +393,7 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_dR = take(MC * BT * dv * es);
       d->off_dM = take(MC * BT * BT * es);
       d->off_dA = take(MC * BT * BT * es);
+      d->off_dslot = take(size_t(d->p.n_slots) * H * dk * dv * 4);
       d->ws_bwd = off;
       if (d->ws_fwd == 0) d->ws_fwd = 256;
     } catch (...) {
@@ -419,7 +434,13 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
       }
       {
         ProfScope ps("kda_state_fwd", s, units);
-        hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
+        if (harts::kda_slab_supported(d->dims)) {
+          harts::BwdRoundArgs b{};
+          b.r = a;
+          hip_check(harts::launch_kda_slab(d->dims, b, 0, d->p.rounds[r].max_chunks, s), "state kernel launch");
+        } else {
+          hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
+        }
       }
     }
   });
@@ -455,13 +476,25 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
         ProfScope ps("kda_prep_bwd", s, units);
         hip_check(harts::launch_kda_prep(d->dims, b.r, true, s), "prep kernel launch");
       }
+      const bool slab = harts::kda_slab_supported(d->dims);
+      if (slab && !d->p.varlen) {
+        // gradients of the states this round hands off: complete, since every consumer runs later
+        float* dslot = g->dstates ? g->dstates : reinterpret_cast<float*>(ws + d->off_dslot);
+        const int32_t n0 = d->rslot_off[size_t(r)], n1 = d->rslot_off[size_t(r) + 1];
+        ProfScope ps("kda_slot_grad", s, int64_t(n1 - n0));
+        hip_check(harts::launch_slot_grad(d->dims, d->rslots + n0, n1 - n0, d->cons_off, d->cons, b.dinit, dslot, s),
+                  "slot gradient launch");
+        b.dslot = dslot;
+      }
       {
         ProfScope ps("kda_state_bwd", s, units);
-        hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
+        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 1, d->p.rounds[r].max_chunks, s), "state kernel launch");
+        else hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
       }
       {
         ProfScope ps("kda_dstate", s, units);
-        hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
+        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 2, d->p.rounds[r].max_chunks, s), "state-gradient kernel launch");
+        else hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
       }
       {
         ProfScope ps("kda_gradA", s, units);

@@ -197,6 +197,50 @@ __device__ __forceinline__ size_t cm_off(int r, int c, int C) {
   return ((size_t(r >> 4) * (C / 16) + (c >> 4)) * 64 + (c & 15) + 16 * ((r & 15) >> 2)) * 4 + (r & 3);
 }
 
+// Permuted fragment-major ("PF") layout of a bf16 [R][K] matrix-core operand (K a multiple
+// of 32).  Every 16 x 32 block is stored as the 64 lanes' 16-byte operand registers, lane
+// after lane (1 KiB per block, blocks row-tile-major).  Lane l holds row l%16 and the
+// contraction indices 4(l/16) + {0..3} and 16 + 4(l/16) + {0..3} of its block.  Those are
+// exactly the rows at which a lane holds the accumulators of two stacked 16 x 16 result
+// tiles, so a pair of result tiles is, converted in registers, the other operand of the next
+// product over that contraction; the matrix core sums over the contraction in any order as
+// long as both operands use the same one.
+__host__ __device__ constexpr size_t pf_off(int r, int k, int K) {
+  return ((size_t(r >> 4) * (K >> 5) + (k >> 5)) * 64 + (((k & 15) >> 2) << 4) + (r & 15)) * 8 +
+         (((k >> 4) & 1) << 2) + (k & 3);
+}
+// The 8 contraction indices lane-group gq (= lane/16) holds in a PF block, slot order.
+__host__ __device__ constexpr int pf_k(int gq, int s) { return s < 4 ? 4 * gq + s : 16 + 4 * gq + (s - 4); }
+// Operand fragment from a pair of accumulator tiles (rows 0-15 and 16-31 of a contraction block).
+__device__ __forceinline__ bf16x8 pf_pair(f32x4 lo, f32x4 hi) {
+  return bf16x8{(bf16)lo[0], (bf16)lo[1], (bf16)lo[2], (bf16)lo[3], (bf16)hi[0], (bf16)hi[1], (bf16)hi[2], (bf16)hi[3]};
+}
+
+// A-operand fragment of an [R][K] bf16 matrix with K contiguous (row stride ld), in the PF
+// contraction order: rows r0 + l%16, contraction k0 + pf_k(l/16, 0..7).
+__device__ __forceinline__ bf16x8 pf_kc(const bf16* p, int ld, int r0, int k0, int lane) {
+  const bf16* q = p + (r0 + (lane & 15)) * ld + k0 + 4 * (lane >> 4);
+  const bf16x4 lo = *reinterpret_cast<const bf16x4*>(q), hi = *reinterpret_cast<const bf16x4*>(q + 16);
+  return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// 4 x 4 transpose across each group of 4 consecutive lanes (DPP quad permutes): lane q of a
+// group holds x[r] = M[r][q] on entry and M[q][r] on return.
+__device__ __forceinline__ float dpp_xor1(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+}
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int lane) {
+  const bool lo = (lane & 2) == 0, ev = (lane & 1) == 0;
+  float r0 = dpp_xor2(lo ? x[2] : x[0]), r1 = dpp_xor2(lo ? x[3] : x[1]);
+  const f32x4 y = lo ? f32x4{x[0], x[1], r0, r1} : f32x4{r0, r1, x[2], x[3]};
+  r0 = dpp_xor1(ev ? y[1] : y[0]);
+  r1 = dpp_xor1(ev ? y[3] : y[2]);
+  return ev ? f32x4{y[0], r0, y[2], r1} : f32x4{r0, y[1], r1, y[3]};
+}
+
 // Elements of T in the store sink (RoundArgs::sink, 64 KiB)
 template <typename T> __host__ __device__ constexpr int kSinkElems() { return 64 * 1024 / sizeof(T); }
 

@@ -960,9 +960,16 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
-        dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
-        X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
-        X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
+        if constexpr (sizeof(T) == 2) {
+          // S_n and dS_n come in the permuted contraction order of the slab passes
+          dqa[bb] = MM::mma(pf_kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
+          X1[bb] = MM::mma(pf_kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
+          X4[bb] = MM::mma(pf_kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
+        } else {
+          dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
+          X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
+          X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
+        }
       }
     }
     // 3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),

@@ -134,6 +134,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   using In = PrepIn<T, BT, D, DV>;
   using Rows = PrepRows<T, BT, D, DV>;
   using MM = Mma<T>;
+  // bf16: operands of the slab-parallel serial passes in the permuted fragment-major layout
+  constexpr bool PF = sizeof(T) == 2;
   constexpr int NB = Ly::NB, LDK = Ly::LDK, LDV = Ly::LDV, LDJ = Ly::LDJ, LDF = Ly::LDF, LDA = Ly::LDA;
   constexpr int VN = In::VN, NK = In::NK, NV = In::NV, NPR = In::NPR, NPRV = In::NPRV;
   __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
@@ -312,8 +314,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
-          fm_store<T>(Mg, BT, i, j0, v, 4);
-          if (BWD) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
+          if (BWD || !PF) fm_store<T>(Mg, BT, i, j0, v, 4);
+          if (BWD || PF) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -349,8 +351,14 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           kh[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lr[x][t]) * EH[b * D + c0 + t];
         }
         stq(Kt + i * LDK + c0, pack16<T>(kt));
-        if (BWD) fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
-        if (BWD) stq(Qr + i * LDK + c0, pack16<T>(qt));
+        if constexpr (BWD && PF) {
+          T* khp = static_cast<T*>(a.ws.Kh) + wsi * BT * D;
+          store4(khp + pf_off(i, c0, D), kh[0], kh[1], kh[2], kh[3]);
+          store4(khp + pf_off(i, c0 + 4, D), kh[4], kh[5], kh[6], kh[7]);
+        } else if constexpr (BWD) {
+          fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
+        }
+        if (BWD || PF) stq(Qr + i * LDK + c0, pack16<T>(qt));
         else fm_store<T>(static_cast<T*>(a.ws.Qt) + wsi * BT * D, D, i, c0, qt, VN);
 #pragma unroll
         for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kh[t]);
@@ -401,13 +409,17 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           Tm[(16 * i + 4 * lg + s) * LDJ + 16 * j + lr] = from_f<T>(i < j ? 0.f : xb[i][s] * bc);
     }
     __syncthreads();
-    // 8. U' = T V (stored transposed), W = T K~ (token-major), KhT out; backward: T, X, A out
+    // 8. U' = T V (accumulator tiles), W = T K~, KhT out; backward: T, X, A out.
+    //    PF: W (and W^T) are stored negated; W stays in registers for Qeff = Q~ - M W.
     {
       T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
       T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
+      T* Ul = reinterpret_cast<T*>(smem + Ly::O_A);  // PF forward: U' for O' = M U' (A is dead here)
+      static_assert(size_t(BT) * LDV * sizeof(T) <= Ly::X_SZ, "U' fits over A");
       constexpr int NU = (BT / 16) * (DV / 16), NW = (D / 16) * (BT / 16);
-      constexpr int NWW = BWD ? (NW + CNW - 1) / CNW : 1;
-      f32x4 wacc[NWW];  // backward keeps W for the Qeff product
+      constexpr bool KEEPW = BWD || PF;
+      constexpr int NWW = KEEPW ? (NW + CNW - 1) / CNW : 1;
+      f32x4 wacc[NWW];
       HARTS_STRIDED(jb, wave, NU, CNW) {
         constexpr int NT = DV / 16;
         const int mt = jb / NT, nt = jb % NT;
@@ -416,8 +428,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         for (int k0 = 0; k0 < BT; k0 += MM::KS)
           acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
         store4(upg + cm_off(16 * mt + crow(lane, 0), 16 * nt + ccol(lane), DV), acc[0], acc[1], acc[2], acc[3]);
+        if constexpr (PF && !BWD) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) Ul[(16 * mt + crow(lane, r)) * LDV + 16 * nt + ccol(lane)] = from_f<T>(acc[r]);
+        }
       }
-      if constexpr (BWD) {
+      if constexpr (KEEPW) {
 #pragma unroll
         for (int u = 0; u < NWW; ++u) {
           const int jb = wave + CNW * u;
@@ -429,11 +445,20 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             for (int k0 = 0; k0 < BT; k0 += MM::KS)
               wacc[u] = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), wacc[u]);
             const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-            const float wv[4] = {wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]};
-            fm_store<T>(wg, D, i, c0, wv, 4);
-            T* wtg = static_cast<T*>(a.ws.WT) + wsi * D * BT;
+            if constexpr (PF) {
+              store4(wg + pf_off(i, c0, D), -wacc[u][0], -wacc[u][1], -wacc[u][2], -wacc[u][3]);
+            } else {
+              const float wv[4] = {wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]};
+              fm_store<T>(wg, D, i, c0, wv, 4);
+            }
+            if constexpr (BWD) {
+              T* wtg = static_cast<T*>(a.ws.WT) + wsi * D * BT;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
+              for (int r = 0; r < 4; ++r) {
+                if constexpr (PF) wtg[pf_off(c0 + r, i, BT)] = from_f<T>(-wacc[u][r]);
+                else wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
+              }
+            }
           }
         }
       } else {
@@ -450,11 +475,22 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
       }
       T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
-      HARTS_STRIDED(idx, tid, D * (BT / VN), CNT) {
-        const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
-        float kv[VN];
-        ld16(KhT + c * LDJ + i0, kv);
-        fm_store<T>(khg, BT, c, i0, kv, VN);
+      if constexpr (PF) {
+        // K^^T [D][BT] permuted fragment-major: two 8-byte row pieces per 16-byte lane slot
+        HARTS_STRIDED(pc, tid, D * BT / 8, CNT) {
+          const int blk = pc / 64, l = pc % 64;
+          const int c = 16 * (blk / (BT / 32)) + (l & 15), k0 = 32 * (blk % (BT / 32)) + 4 * (l >> 4);
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(KhT + c * LDJ + k0);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(KhT + c * LDJ + k0 + 16);
+          *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      } else {
+        HARTS_STRIDED(idx, tid, D * (BT / VN), CNT) {
+          const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
+          float kv[VN];
+          ld16(KhT + c * LDJ + i0, kv);
+          fm_store<T>(khg, BT, c, i0, kv, VN);
+        }
       }
       if constexpr (BWD) {
         const size_t BB = size_t(BT) * BT;
@@ -473,6 +509,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           stq(xg + i * BT + j0, pack16<T>(xv));
           stq(ag + i * BT + j0, pack16<T>(av));
         }
+      }
+      if constexpr (KEEPW) {
         __syncthreads();  // every wave is done reading K~: W takes its place
 #pragma unroll
         for (int u = 0; u < NWW; ++u) {
@@ -485,20 +523,48 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           }
         }
         __syncthreads();
-        // 9. Qeff = Q~ - M W, stored transposed: QeffT[c][i]
-        T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
-        constexpr int MT = BT / 16, NT = D / 16;
-        HARTS_STRIDED(jb, wave, MT * NT, CNW) {
-          const int mt = jb / NT, nt = jb % NT;
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (BWD) {
+          // 9. Qeff = Q~ - M W, stored as Qeff^T [D][BT]
+          T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
+          constexpr int MT = BT / 16, NT = D / 16;
+          HARTS_STRIDED(jb, wave, MT * NT, CNW) {
+            const int mt = jb / NT, nt = jb % NT;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int k0 = 0; k0 < BT; k0 += MM::KS)
-            acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
-          const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0);
-          float v[4];
+            for (int k0 = 0; k0 < BT; k0 += MM::KS)
+              acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
+            const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0);
+            float v[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
-          fm_store<T>(qe, BT, c, i0, v, 4);
+            for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
+            if constexpr (PF) store4(qe + pf_off(c, i0, BT), v[0], v[1], v[2], v[3]);
+            else fm_store<T>(qe, BT, c, i0, v, 4);
+          }
+        } else {
+          // 9. forward (PF): Qeff = Q~ - M W as [BT][D] (tiles of Qeff^T: rows are channels),
+          //    and O' = M U' as accumulator tiles of O'^T (value rows, token columns)
+          T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
+          HARTS_STRIDED(jb, wave, (D / 16) * (BT / 16), CNW) {
+            const int mt = jb / (BT / 16), nt = jb % (BT / 16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < BT; k0 += MM::KS)
+              acc = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Ml, LDJ, 16 * nt, k0, lane), acc);
+            const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[i * LDK + c0 + r]) - acc[r];
+            store4(qe + pf_off(i, c0, D), v[0], v[1], v[2], v[3]);
+          }
+          T* opg = static_cast<T*>(a.ws.Op) + wsi * BT * DV;
+          HARTS_STRIDED(jb, wave, (DV / 16) * (BT / 16), CNW) {
+            const int jt = jb / (BT / 16), it = jb % (BT / 16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < BT; k0 += MM::KS)
+              acc = MM::mma(MM::rc(Ul, LDV, 16 * jt, k0, lane), MM::kc(Ml, LDJ, 16 * it, k0, lane), acc);
+            store4(opg + ((size_t(jt) * (BT / 16) + it) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+          }
         }
       }
     }

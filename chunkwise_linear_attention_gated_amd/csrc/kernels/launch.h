@@ -28,6 +28,7 @@ struct ChunkWs {
   void* dR;     // [BT][DV]  dL/dR = T^T dU                         (backward)
   void* dM;     // [BT][BT]  dL/dM (lower incl.)                    (backward)
   void* dA;     // [BT][BT]  dL/dA (strictly lower)                 (backward)
+  void* Op;     // O'^T = (M U')^T as accumulator tiles             (forward, slab passes)
 };
 
 struct KdaDims {
@@ -64,6 +65,8 @@ struct BwdRoundArgs {
   const int32_t* slot_cons_off;  // CSR of consumer sequences per slot (nullable for varlen)
   const int32_t* slot_cons;
   float* replay_grad;         // [replay_total][H][2*D + DV + 1] fp32 (dk, dv, dg, dbeta of replayed rows)
+  const float* dslot;         // slab passes: gradient of every handed-off state, summed over its
+                              // consumers before the producing round runs (nullable)
 };
 
 // Grid of a persistent per-chunk kernel: one workgroup per compute unit of the
@@ -82,6 +85,13 @@ inline unsigned persistent_grid(unsigned items) {
 
 hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
+// Slab-parallel serial passes (bf16 operands): mode 0 forward, 1 backward state recompute,
+// 2 state gradient.  Returns hipErrorNotSupported for configurations they do not cover.
+bool kda_slab_supported(const KdaDims& d);
+// out[slot] = sum over the slot's consumer sequences of dinit[consumer], for the listed slots
+hipError_t launch_slot_grad(const KdaDims& d, const int32_t* slots, int32_t nslots, const int32_t* cons_off,
+                            const int32_t* cons, const float* dinit, float* out, hipStream_t s);
+hipError_t launch_kda_slab(const KdaDims& d, const BwdRoundArgs& b, int mode, int round_max_chunks, hipStream_t s);
 hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
 hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, int part, hipStream_t s);  // part 0: token side, 1: channel side
 hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const int32_t* fix_off,
