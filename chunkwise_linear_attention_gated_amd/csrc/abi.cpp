@@ -130,6 +130,46 @@ void free_dev(harts_dev_plan* d) {
     if (p) (void)hipFree(p);
 }
 
+// Auxiliary streams of the current device, created once at the default priority and kept
+// for the life of the process; work is forked onto them from the caller's stream and joined
+// back with events, so every entry point still only enqueues on the caller's stream.
+hipStream_t aux_stream(int i) {
+  static std::mutex mu;
+  static std::map<int, std::pair<hipStream_t, hipStream_t>> streams;
+  int dev = 0;
+  hip_check(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = streams.find(dev);
+  if (it == streams.end()) {
+    hipStream_t a = nullptr, b = nullptr;
+    hip_check(hipStreamCreateWithFlags(&a, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    hip_check(hipStreamCreateWithFlags(&b, hipStreamNonBlocking), "hipStreamCreateWithFlags");
+    it = streams.emplace(dev, std::make_pair(a, b)).first;
+  }
+  return i == 0 ? it->second.first : it->second.second;
+}
+
+// Events recorded while enqueueing one call; released when the call returns (a recorded
+// event's resources outlive it until the device reaches it).
+struct Events {
+  std::vector<hipEvent_t> ev;
+  hipEvent_t record(hipStream_t s) {
+    hipEvent_t e = nullptr;
+    hip_check(hipEventCreateWithFlags(&e, hipEventDisableTiming), "hipEventCreateWithFlags");
+    ev.push_back(e);
+    hip_check(hipEventRecord(e, s), "hipEventRecord");
+    return e;
+  }
+  ~Events() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+  }
+};
+
+// stream `to` continues after the work enqueued so far on `from`
+void fork(hipStream_t from, hipStream_t to, Events& ev) {
+  hip_check(hipStreamWaitEvent(to, ev.record(from), 0), "hipStreamWaitEvent");
+}
+
 harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int r, char* ws) {
   const harts::RoundRange& rr = d->p.rounds[r];
   harts::RoundArgs a{};
@@ -154,26 +194,30 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
     a.emit_pool = io->states;
     a.final_pool = nullptr;
   }
-  a.ws.W = ws + d->off_W;
-  a.ws.UpT = ws + d->off_UpT;
-  a.ws.KhT = ws + d->off_KhT;
-  a.ws.Qt = ws + d->off_Qt;
-  a.ws.Mm = ws + d->off_Mm;
-  a.ws.El = reinterpret_cast<float*>(ws + d->off_El);
+  // every per-chunk workspace array holds all rounds, so rounds may run concurrently
+  const size_t H = size_t(d->dims.H), BT = size_t(d->p.B), dk = size_t(d->dims.D), dv = size_t(d->dims.DV);
+  const size_t es = d->dims.dtype == HARTS_DTYPE_BF16 ? 2 : 4, item0 = size_t(rr.chunk0) * H;
+  auto at = [&](size_t off, size_t elems, size_t esz) { return ws + off + item0 * elems * esz; };
+  a.ws.W = at(d->off_W, BT * dk, es);
+  a.ws.UpT = at(d->off_UpT, dv * BT, es);
+  a.ws.KhT = at(d->off_KhT, dk * BT, es);
+  a.ws.Qt = at(d->off_Qt, BT * dk, es);
+  a.ws.Mm = at(d->off_Mm, BT * BT, es);
+  a.ws.El = reinterpret_cast<float*>(at(d->off_El, dk, 4));
   a.sink = ws + d->off_sink;
-  a.ws.QeffT = ws + d->off_Qe;
-  a.ws.WT = ws + d->off_WT;
-  a.ws.Kh = ws + d->off_Kh;
-  a.ws.Tm = ws + d->off_Tm;
-  a.ws.Xm = ws + d->off_Xm;
-  a.ws.Am = ws + d->off_Am;
-  a.ws.U = ws + d->off_U;
-  a.ws.dR = ws + d->off_dR;
-  a.ws.dM = ws + d->off_dM;
-  a.ws.dA = ws + d->off_dA;
-  a.ws.Op = ws + d->off_Op;
-  a.h = ws + d->off_h;
-  a.hc = ws + d->off_hc;
+  a.ws.QeffT = at(d->off_Qe, dk * BT, es);
+  a.ws.WT = at(d->off_WT, dk * BT, es);
+  a.ws.Kh = at(d->off_Kh, BT * dk, es);
+  a.ws.Tm = at(d->off_Tm, BT * BT, es);
+  a.ws.Xm = at(d->off_Xm, BT * BT, es);
+  a.ws.Am = at(d->off_Am, BT * BT, es);
+  a.ws.U = at(d->off_U, BT * dv, es);
+  a.ws.dR = at(d->off_dR, BT * dv, es);
+  a.ws.dM = at(d->off_dM, BT * BT, es);
+  a.ws.dA = at(d->off_dA, BT * BT, es);
+  a.ws.Op = at(d->off_Op, BT * dv, es);
+  a.h = at(d->off_h, dv * dk, es);
+  a.hc = at(d->off_hc, dv * dk, es);
   return a;
 }
 
@@ -359,7 +403,8 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       // the host vectors must outlive the asynchronous copies
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       const size_t es = dtype == HARTS_DTYPE_BF16 ? 2 : 4;
-      const size_t MC = size_t(d->p.max_round_chunks) * H, BT = size_t(d->p.B);
+      // per-chunk arrays are sized for every chunk of the plan (rounds may run concurrently)
+      const size_t MC = d->p.chunk_desc.size() * size_t(H), BT = size_t(d->p.B);
       size_t off = 0;
       auto take = [&](size_t bytes) {
         const size_t o = off;
@@ -422,25 +467,34 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
   return guarded([&] {
     if (!d) throw Error(HARTS_EINVAL, "dplan is NULL");
     check_io(d, io, false);
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s0 = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(io->workspace);
+    // Preparation of every round runs ahead on an auxiliary stream (it depends on the inputs
+    // only); the serial passes follow in round order on the caller's stream.
+    Events ev;
+    hipStream_t s1 = aux_stream(0);
+    fork(s0, s1, ev);
+    const bool slab = harts::kda_slab_supported(d->dims);
+    std::vector<hipEvent_t> prepped(size_t(d->p.n_rounds));
+    for (int r = 0; r < d->p.n_rounds; ++r) {
+      harts::RoundArgs a = round_args(d, io, r, ws);
+      const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
+      ProfScope ps("kda_prep_fwd", s1, units);
+      hip_check(harts::launch_kda_prep(d->dims, a, false, s1), "prep kernel launch");
+      prepped[size_t(r)] = ev.record(s1);
+    }
     for (int r = 0; r < d->p.n_rounds; ++r) {
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
       const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
-      {
-        ProfScope ps("kda_prep_fwd", s, units);
-        hip_check(harts::launch_kda_prep(d->dims, a, false, s), "prep kernel launch");
-      }
-      {
-        ProfScope ps("kda_state_fwd", s, units);
-        if (harts::kda_slab_supported(d->dims)) {
-          harts::BwdRoundArgs b{};
-          b.r = a;
-          hip_check(harts::launch_kda_slab(d->dims, b, 0, d->p.rounds[r].max_chunks, s), "state kernel launch");
-        } else {
-          hip_check(harts::launch_kda_state(d->dims, a, false, s), "state kernel launch");
-        }
+      hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
+      ProfScope ps("kda_state_fwd", s0, units);
+      if (slab) {
+        harts::BwdRoundArgs b{};
+        b.r = a;
+        hip_check(harts::launch_kda_slab(d->dims, b, 0, d->p.rounds[r].max_chunks, s0), "state kernel launch");
+      } else {
+        hip_check(harts::launch_kda_state(d->dims, a, false, s0), "state kernel launch");
       }
     }
   });
@@ -452,9 +506,21 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     check_io(d, io, true);
     if (!g || !g->dO || !g->dq || !g->dk || !g->dv || !g->dg || !g->dbeta)
       throw Error(HARTS_EINVAL, "dO, dq, dk, dv, dg and dbeta are required");
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStream_t s0 = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(io->workspace);
-    for (int r = d->p.n_rounds - 1; r >= 0; --r) {
+    const bool slab = harts::kda_slab_supported(d->dims);
+    const int R = d->p.n_rounds;
+    // Three streams, rounds in reverse:
+    //   s1: preparation and state recompute of every round (they need no gradient);
+    //   s0: the state-gradient chain (each round needs the initial-state gradients of the
+    //       later rounds that consume its handed-off states);
+    //   s2: the per-chunk gradient kernels of a round once its recompute and state
+    //       gradient are done.
+    Events ev;
+    hipStream_t s1 = aux_stream(0), s2 = aux_stream(1);
+    fork(s0, s1, ev);
+    fork(s0, s2, ev);
+    auto round = [&](int r) {
       harts::BwdRoundArgs b{};
       b.r = round_args(d, io, r, ws);
       b.r.o = nullptr;
@@ -464,52 +530,69 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       b.dv = g->dv;
       b.dg = g->dg;
       b.dbeta = g->dbeta;
-      b.dh = ws + d->off_dh;
-      b.dhc = ws + d->off_dhc;
+      const size_t item0 = size_t(d->p.rounds[r].chunk0) * d->dims.H;
+      const size_t sz = size_t(d->dims.D) * d->dims.DV * (d->dims.dtype == HARTS_DTYPE_BF16 ? 2 : 4);
+      b.dh = ws + d->off_dh + item0 * sz;
+      b.dhc = ws + d->off_dhc + item0 * sz;
       b.dinit = d->p.varlen ? g->dinit : reinterpret_cast<float*>(ws + d->off_dinit);
       b.dstates = d->p.varlen ? nullptr : g->dstates;
       b.slot_cons_off = d->p.varlen ? nullptr : d->cons_off;
       b.slot_cons = d->p.varlen ? nullptr : d->cons;
       b.replay_grad = reinterpret_cast<float*>(ws + d->off_rg);
-      const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
+      if (slab && !d->p.varlen) b.dslot = g->dstates ? g->dstates : reinterpret_cast<float*>(ws + d->off_dslot);
+      return b;
+    };
+    auto units = [&](int r) { return int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H; };
+    std::vector<hipEvent_t> prepped(R, nullptr), recomputed(R, nullptr);
+    for (int r = R - 1; r >= 0; --r) {
+      harts::BwdRoundArgs b = round(r);
       {
-        ProfScope ps("kda_prep_bwd", s, units);
-        hip_check(harts::launch_kda_prep(d->dims, b.r, true, s), "prep kernel launch");
+        ProfScope ps("kda_prep_bwd", s1, units(r));
+        hip_check(harts::launch_kda_prep(d->dims, b.r, true, s1), "prep kernel launch");
       }
-      const bool slab = harts::kda_slab_supported(d->dims);
-      if (slab && !d->p.varlen) {
+      prepped[size_t(r)] = ev.record(s1);
+      {
+        ProfScope ps("kda_state_bwd", s1, units(r));
+        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 1, d->p.rounds[r].max_chunks, s1), "state kernel launch");
+        else hip_check(harts::launch_kda_state(d->dims, b.r, true, s1), "state kernel launch");
+      }
+      recomputed[size_t(r)] = ev.record(s1);
+    }
+    for (int r = R - 1; r >= 0; --r) {
+      harts::BwdRoundArgs b = round(r);
+      hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
+      if (b.dslot) {
         // gradients of the states this round hands off: complete, since every consumer runs later
-        float* dslot = g->dstates ? g->dstates : reinterpret_cast<float*>(ws + d->off_dslot);
         const int32_t n0 = d->rslot_off[size_t(r)], n1 = d->rslot_off[size_t(r) + 1];
-        ProfScope ps("kda_slot_grad", s, int64_t(n1 - n0));
-        hip_check(harts::launch_slot_grad(d->dims, d->rslots + n0, n1 - n0, d->cons_off, d->cons, b.dinit, dslot, s),
+        ProfScope ps("kda_slot_grad", s0, int64_t(n1 - n0));
+        hip_check(harts::launch_slot_grad(d->dims, d->rslots + n0, n1 - n0, d->cons_off, d->cons, b.dinit,
+                                          const_cast<float*>(b.dslot), s0),
                   "slot gradient launch");
-        b.dslot = dslot;
       }
       {
-        ProfScope ps("kda_state_bwd", s, units);
-        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 1, d->p.rounds[r].max_chunks, s), "state kernel launch");
-        else hip_check(harts::launch_kda_state(d->dims, b.r, true, s), "state kernel launch");
+        ProfScope ps("kda_dstate", s0, units(r));
+        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 2, d->p.rounds[r].max_chunks, s0), "state-gradient kernel launch");
+        else hip_check(harts::launch_kda_dstate(d->dims, b, s0), "state-gradient kernel launch");
+      }
+      hip_check(hipStreamWaitEvent(s2, ev.record(s0), 0), "hipStreamWaitEvent");
+      hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
+      {
+        ProfScope ps("kda_gradA", s2, units(r));
+        hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");
       }
       {
-        ProfScope ps("kda_dstate", s, units);
-        if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 2, d->p.rounds[r].max_chunks, s), "state-gradient kernel launch");
-        else hip_check(harts::launch_kda_dstate(d->dims, b, s), "state-gradient kernel launch");
-      }
-      {
-        ProfScope ps("kda_gradA", s, units);
-        hip_check(harts::launch_kda_grad(d->dims, b, 0, s), "gradient kernel launch");
-      }
-      {
-        ProfScope ps("kda_gradB", s, units);
-        hip_check(harts::launch_kda_grad(d->dims, b, 1, s), "gradient kernel launch");
+        ProfScope ps("kda_gradB", s2, units(r));
+        hip_check(harts::launch_kda_grad(d->dims, b, 1, s2), "gradient kernel launch");
       }
     }
+    // join: the caller's stream continues after every round's gradients
+    hip_check(hipStreamWaitEvent(s0, ev.record(s2), 0), "hipStreamWaitEvent");
+    hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
     if (!d->p.fix_rows.empty()) {
-      ProfScope ps("kda_replay_fixup", s, int64_t(d->p.replay_total) * d->dims.H);
+      ProfScope ps("kda_replay_fixup", s0, int64_t(d->p.replay_total) * d->dims.H);
       hip_check(harts::launch_replay_fixup(d->dims, d->fix_rows, d->fix_off, d->fix_idx,
                                            int32_t(d->p.fix_rows.size()), reinterpret_cast<float*>(ws + d->off_rg),
-                                           g->dk, g->dv, g->dg, g->dbeta, s),
+                                           g->dk, g->dv, g->dg, g->dbeta, s0),
                 "replay fixup launch");
     }
   });

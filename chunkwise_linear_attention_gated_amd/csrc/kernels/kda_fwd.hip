@@ -222,19 +222,23 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     __syncthreads();
     // 3. per channel: block entry log-decays F_b, e^{F_b}, e^{F_end - F_{b+1}}, pair scales
     HARTS_STRIDED(c, tid, D, CNT) {
-      float f = 0.f, fv[NB + 1];
+      float f = 0.f, fv[NB + 1], tb[NB];
       fv[0] = 0.f;
       Fv[c] = 0.f;
       EF[c] = 1.f;
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        f += Tv[b * D + c];
+        tb[b] = Tv[b * D + c];
+        f += tb[b];
         fv[b + 1] = f;
         Fv[(b + 1) * D + c] = f;
         EF[(b + 1) * D + c] = __expf(f);
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) EH[b * D + c] = __expf(f - fv[b + 1]);
+      // block totals become e^{T_b}: e^{T_b - L} = e^{T_b} e^{-L} below
+#pragma unroll
+      for (int b = 0; b < NB; ++b) Tv[b * D + c] = __expf(tb[b]);
 #pragma unroll
       for (int bi = 2; bi < NB; ++bi)
 #pragma unroll
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     __syncthreads();
     // 4. operand arrays: Kr = k e^L, Qr = q e^L, Kc0 = k e^{T_b - L}, Kcd = k e^{-L}, Kcx = Kc0 * pair scale.
     //    L stays in registers for step 6.
-    float Lr[NK][VN];
+    float Er[NK][VN], En[NK][VN];  // e^{L}, e^{-L} of this thread's elements
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
@@ -256,12 +260,13 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
         for (int t = 0; t < VN; ++t) {
           const float Lv = Gf[i * LDF + c0 + t];
-          Lr[x][t] = Lv;
-          const float er = __expf(Lv);
+          const float er = __expf(Lv), en = __expf(-Lv);
+          Er[x][t] = er;
+          En[x][t] = en;
           kr[t] = kk[t] * er;
           qr[t] = qq[t] * er;
-          kc[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lv);
-          kd[t] = kk[t] * __expf(-Lv);
+          kc[t] = kk[t] * (Tv[b * D + c0 + t] * en);
+          kd[t] = kk[t] * en;
         }
         stq(Kr + i * LDK + c0, pack16<T>(kr));
         stq(Qr + i * LDK + c0, pack16<T>(qr));
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
       } else {
 #pragma unroll
-        for (int t = 0; t < VN; ++t) Lr[x][t] = 0.f;
+        for (int t = 0; t < VN; ++t) Er[x][t] = En[x][t] = 1.f;
       }
     }
     __syncthreads();
@@ -345,10 +350,10 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         unpack16<T>(rows.rk[x] >= 0 ? cur.q[x] : z4, qq);
 #pragma unroll
         for (int t = 0; t < VN; ++t) {
-          const float er = __expf(Lr[x][t]), ef = EF[b * D + c0 + t];
+          const float er = Er[x][t], ef = EF[b * D + c0 + t];
           kt[t] = kk[t] * er * ef;
           qt[t] = qq[t] * er * ef;
-          kh[t] = kk[t] * __expf(Tv[b * D + c0 + t] - Lr[x][t]) * EH[b * D + c0 + t];
+          kh[t] = kk[t] * (Tv[b * D + c0 + t] * En[x][t]) * EH[b * D + c0 + t];
         }
         stq(Kt + i * LDK + c0, pack16<T>(kt));
         if constexpr (BWD && PF) {
