@@ -52,13 +52,16 @@ def parse():
 
 # ------------------------------------------------------------------ algorithmic work per kernel
 # Multiply-accumulates per chunk of l tokens (replay included) and head, d = d_k = d_v, for the
-# products each kernel performs ("Kernels and their rooflines").
+# products each kernel performs ("Kernels and their rooflines").  The benchmark
+# runs the forward that keeps the backward's operands: kda_prep_fwd is then the preparation of
+# both directions (A and M, W, U', Qeff, O', the diagonal-block inverse), kda_state_fwd also
+# writes the chunk-start states, and the backward runs no kda_prep_bwd or kda_state_bwd.
 def macs(kernel, l, d=D):
     l2d, ld2, l3 = l * l * d, l * d * d, l ** 3
     return {
-        "kda_prep_fwd": 4 * l2d + l3 / 6,
-        "kda_state_fwd": 3 * ld2 + l2d,
-        "kda_prep_bwd": 5 * l2d + l3 / 6,
+        "kda_prep_fwd": 5 * l2d + l3 / 6,
+        "kda_state_fwd": 3 * ld2,
+        "kda_prep_bwd": 4 * l2d + l3 / 6,
         "kda_state_bwd": 2 * ld2,
         "kda_dstate": 3 * ld2,
         "kda_gradA": 5 * l2d + 2 * ld2 + 2 * l3,
@@ -74,11 +77,11 @@ def hbm_bytes(kernel, l, d=D, bt=B):
     sq = bt * bt * ES       # one [B, B] workspace array
     st = d * d * ES         # one bf16 state [d, d]
     return {
-        "kda_prep_fwd": 4 * tok + l * ES + 4 * blk + sq + d * 4,
-        "kda_state_fwd": 4 * blk + sq + d * 4 + tok,
-        "kda_prep_bwd": 4 * tok + l * ES + 4 * blk + 4 * sq + d * 4,
-        "kda_state_bwd": 3 * blk + d * 4 + st,
-        "kda_dstate": 3 * blk + d * 4 + tok + st,
+        "kda_prep_fwd": 4 * tok + l * ES + 8 * blk + 4 * sq + d * 4,
+        "kda_state_fwd": 5 * blk + d * 4 + tok + 2 * st,
+        "kda_prep_bwd": 4 * tok + l * ES + 6 * blk + 4 * sq + d * 4,
+        "kda_state_bwd": 3 * blk + d * 4 + 2 * st,
+        "kda_dstate": 3 * blk + d * 4 + tok + 2 * st,
         "kda_gradA": 4 * tok + l * ES + 2 * st + 4 * sq + tok + l * ES + 2 * blk + 2 * sq,
         "kda_gradB": 4 * tok + 2 * st + 2 * blk + 2 * sq + 3 * tok,
     }[kernel]
@@ -196,12 +199,13 @@ def main():
     slots = torch.zeros((ns, H, D, D), dtype=torch.float32, device=dev)
     dslots = torch.zeros_like(slots)
     gr = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "g", "beta")}
-    ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True)), dtype=torch.uint8, device=dev)
+    ws = torch.empty(dp.workspace_size(2), dtype=torch.uint8, device=dev)
 
     def step():
-        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws)
+        # the forward keeps the backward's per-chunk operands and chunk-start states
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=True)
         harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"],
-                      gr["g"], gr["beta"], states=slots, dstates=dslots, workspace=ws)
+                      gr["g"], gr["beta"], states=slots, dstates=dslots, workspace=ws, keep=True)
 
     for _ in range(args.warmup):
         step()

@@ -49,7 +49,8 @@ class SeqView(ctypes.Structure):
 
 class KdaIO(ctypes.Structure):
     _fields_ = [("q", P), ("k", P), ("v", P), ("g", P), ("beta", P), ("o", P), ("states", P),
-                ("init_states", P), ("final_states", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t)]
+                ("init_states", P), ("final_states", P), ("workspace", P), ("workspace_bytes", ctypes.c_size_t),
+                ("keep", I32)]
 
 
 class KdaGrad(ctypes.Structure):
@@ -220,9 +221,10 @@ class DevicePlan:
         _check(_plan_upload(plan._h, H, dk, dv, dtype, _stream(stream), ctypes.byref(h)))
         self._h = h
 
-    def workspace_size(self, backward: bool) -> int:
+    def workspace_size(self, backward) -> int:
+        """backward: False/0 forward, True/1 backward, 2 a forward/backward pair with keep."""
         n = ctypes.c_size_t()
-        _check(_ws_size(self._h, int(bool(backward)), ctypes.byref(n)))
+        _check(_ws_size(self._h, int(backward), ctypes.byref(n)))
         return n.value
 
     def __del__(self):
@@ -231,22 +233,25 @@ class DevicePlan:
             self._h = None
 
 
-def _io(q, k, v, g, beta, o, states, init_states, final_states, workspace):
+def _io(q, k, v, g, beta, o, states, init_states, final_states, workspace, keep):
     return KdaIO(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(o), _ptr(states), _ptr(init_states),
-                 _ptr(final_states), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size())
+                 _ptr(final_states), _ptr(workspace), 0 if workspace is None else workspace.numel() * workspace.element_size(),
+                 int(bool(keep)))
 
 
 def kda_fwd(dplan: DevicePlan, q, k, v, g, beta, o, states=None, init_states=None, final_states=None,
-            workspace=None, stream=None):
-    """harts_kda_fwd over every round of the plan."""
-    io = _io(q, k, v, g, beta, o, states, init_states, final_states, workspace)
+            workspace=None, stream=None, keep=False):
+    """harts_kda_fwd over every round of the plan (keep: also leave the backward's operands
+    and chunk-start states in the workspace for kda_bwd(..., keep=True))."""
+    io = _io(q, k, v, g, beta, o, states, init_states, final_states, workspace, keep)
     _check(_kda_fwd(dplan._h, ctypes.byref(io), _stream(stream)))
 
 
 def kda_bwd(dplan: DevicePlan, q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta, states=None, init_states=None,
-            dstates=None, dinit=None, workspace=None, stream=None):
-    """harts_kda_bwd over every round of the plan, in reverse."""
-    io = _io(q, k, v, g, beta, None, states, init_states, None, workspace)
+            dstates=None, dinit=None, workspace=None, stream=None, keep=False):
+    """harts_kda_bwd over every round of the plan, in reverse (keep: read what
+    kda_fwd(..., keep=True) left in the same workspace instead of recomputing it)."""
+    io = _io(q, k, v, g, beta, None, states, init_states, None, workspace, keep)
     gr = KdaGrad(_ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta), _ptr(dstates), _ptr(dinit))
     _check(_kda_bwd(dplan._h, ctypes.byref(io), ctypes.byref(gr), _stream(stream)))
 

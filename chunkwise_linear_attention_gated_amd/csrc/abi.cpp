@@ -225,7 +225,8 @@ void check_io(const harts_dev_plan* d, const harts_kda_io* io, bool bwd) {
   if (!io) throw Error(HARTS_EINVAL, "io is NULL");
   if (!io->q || !io->k || !io->v || !io->g || !io->beta) throw Error(HARTS_EINVAL, "q, k, v, g and beta are required");
   if (!bwd && !io->o) throw Error(HARTS_EINVAL, "o is required");
-  if (!io->workspace || io->workspace_bytes < (bwd ? d->ws_bwd : d->ws_fwd))
+  if (io->keep != 0 && io->keep != 1) throw Error(HARTS_EINVAL, "keep must be 0 or 1");
+  if (!io->workspace || io->workspace_bytes < (bwd || io->keep ? d->ws_bwd : d->ws_fwd))
     throw Error(HARTS_EINVAL, "workspace missing or smaller than harts_kda_workspace_size()");
   if (!d->p.varlen && d->p.n_slots > 0 && !io->states) throw Error(HARTS_EINVAL, "states (slot pool) is required");
   if (d->p.varlen) {
@@ -417,11 +418,11 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_Mm = take(MC * BT * BT * es);
       d->off_El = take(MC * dk * 4);
       d->off_sink = take(kSinkBytes);
-      const size_t common = off;
       d->off_Qt = take(MC * BT * dk * es);
       d->off_Op = take(MC * BT * dv * es);
       d->ws_fwd = off;
-      off = common;
+      // the backward arrays follow the forward's, so that a forward that keeps them for the
+      // backward (harts_kda_io::keep) leaves its own outputs intact
       d->off_Qe = take(MC * dk * BT * es);
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
@@ -453,6 +454,7 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
 int harts_kda_workspace_size(const harts_dev_plan* dplan, int32_t backward, size_t* bytes) {
   return guarded([&] {
     if (!dplan || !bytes) throw Error(HARTS_EINVAL, "dplan and bytes must be non-NULL");
+    if (backward < 0 || backward > 2) throw Error(HARTS_EINVAL, "backward must be 0, 1 or 2");
     *bytes = backward ? dplan->ws_bwd : dplan->ws_fwd;
   });
 }
@@ -475,24 +477,29 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     hipStream_t s1 = aux_stream(0);
     fork(s0, s1, ev);
     const bool slab = harts::kda_slab_supported(d->dims);
+    // keep: the preparation also writes the backward's per-chunk operands and the serial pass
+    // every chunk-start state, so that the backward neither prepares nor recomputes
+    const bool keep = io->keep && slab;
     std::vector<hipEvent_t> prepped(size_t(d->p.n_rounds));
     for (int r = 0; r < d->p.n_rounds; ++r) {
       harts::RoundArgs a = round_args(d, io, r, ws);
       const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
       ProfScope ps("kda_prep_fwd", s1, units);
-      hip_check(harts::launch_kda_prep(d->dims, a, false, s1), "prep kernel launch");
+      hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, s1), "prep kernel launch");
       prepped[size_t(r)] = ev.record(s1);
     }
     for (int r = 0; r < d->p.n_rounds; ++r) {
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
+      if (!keep) a.h = a.hc = nullptr;
       const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
       hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       ProfScope ps("kda_state_fwd", s0, units);
       if (slab) {
         harts::BwdRoundArgs b{};
         b.r = a;
-        hip_check(harts::launch_kda_slab(d->dims, b, 0, d->p.rounds[r].max_chunks, s0), "state kernel launch");
+        hip_check(harts::launch_kda_slab(d->dims, b, keep ? 3 : 0, d->p.rounds[r].max_chunks, s0),
+                  "state kernel launch");
       } else {
         hip_check(harts::launch_kda_state(d->dims, a, false, s0), "state kernel launch");
       }
@@ -509,6 +516,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     hipStream_t s0 = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(io->workspace);
     const bool slab = harts::kda_slab_supported(d->dims);
+    const bool keep = io->keep && slab;  // operands and chunk-start states are in the workspace
     const int R = d->p.n_rounds;
     // Three streams, rounds in reverse:
     //   s1: preparation and state recompute of every round (they need no gradient);
@@ -544,11 +552,11 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     };
     auto units = [&](int r) { return int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H; };
     std::vector<hipEvent_t> prepped(R, nullptr), recomputed(R, nullptr);
-    for (int r = R - 1; r >= 0; --r) {
+    for (int r = R - 1; r >= 0 && !keep; --r) {
       harts::BwdRoundArgs b = round(r);
       {
         ProfScope ps("kda_prep_bwd", s1, units(r));
-        hip_check(harts::launch_kda_prep(d->dims, b.r, true, s1), "prep kernel launch");
+        hip_check(harts::launch_kda_prep(d->dims, b.r, 1, s1), "prep kernel launch");
       }
       prepped[size_t(r)] = ev.record(s1);
       {
@@ -560,7 +568,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     }
     for (int r = R - 1; r >= 0; --r) {
       harts::BwdRoundArgs b = round(r);
-      hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
+      if (!keep) hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       if (b.dslot) {
         // gradients of the states this round hands off: complete, since every consumer runs later
         const int32_t n0 = d->rslot_off[size_t(r)], n1 = d->rslot_off[size_t(r) + 1];
@@ -575,7 +583,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
         else hip_check(harts::launch_kda_dstate(d->dims, b, s0), "state-gradient kernel launch");
       }
       hip_check(hipStreamWaitEvent(s2, ev.record(s0), 0), "hipStreamWaitEvent");
-      hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
+      if (!keep) hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
       {
         ProfScope ps("kda_gradA", s2, units(r));
         hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");

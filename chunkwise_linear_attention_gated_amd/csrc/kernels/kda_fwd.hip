@@ -128,7 +128,9 @@ __device__ __forceinline__ void prep_load_v(f32x4* v, const PrepRows<T, BT, D, D
 // Per-chunk preparation.  Persistent: one workgroup of CNT threads per CU walks the
 // (chunk, head) items of the round; the next item's rows and inputs are fetched into
 // registers while the current item computes.
-template <typename T, int BT, int D, int DV, bool BWD>
+// PM: 0 forward operands, 1 backward operands, 2 both (bf16 only: a forward that keeps
+// everything the backward needs).
+template <typename T, int BT, int D, int DV, int PM>
 __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   using Ly = PrepLayout<T, BT, D, DV>;
   using In = PrepIn<T, BT, D, DV>;
@@ -136,6 +138,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   using MM = Mma<T>;
   // bf16: operands of the slab-parallel serial passes in the permuted fragment-major layout
   constexpr bool PF = sizeof(T) == 2;
+  constexpr bool BWD = PM != 0, FO = PM != 1;
+  static_assert(PM != 2 || PF, "kept backward operands need the fragment-major layouts");
   constexpr int NB = Ly::NB, LDK = Ly::LDK, LDV = Ly::LDV, LDJ = Ly::LDJ, LDF = Ly::LDF, LDA = Ly::LDA;
   constexpr int VN = In::VN, NK = In::NK, NV = In::NV, NPR = In::NPR, NPRV = In::NPRV;
   __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
@@ -419,23 +423,24 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     {
       T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
       T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
-      T* Ul = reinterpret_cast<T*>(smem + Ly::O_A);  // PF forward: U' for O' = M U' (A is dead here)
-      static_assert(size_t(BT) * LDV * sizeof(T) <= Ly::X_SZ, "U' fits over A");
+      // PF forward outputs: U' kept in registers, staged over V once every wave has read V
+      T* Ul = Vl;
       constexpr int NU = (BT / 16) * (DV / 16), NW = (D / 16) * (BT / 16);
-      constexpr bool KEEPW = BWD || PF;
-      constexpr int NWW = KEEPW ? (NW + CNW - 1) / CNW : 1;
-      f32x4 wacc[NWW];
-      HARTS_STRIDED(jb, wave, NU, CNW) {
-        constexpr int NT = DV / 16;
-        const int mt = jb / NT, nt = jb % NT;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      constexpr bool KEEPW = BWD || PF, KEEPU = PF && FO;
+      constexpr int NWW = KEEPW ? (NW + CNW - 1) / CNW : 1, NUW = (NU + CNW - 1) / CNW;
+      f32x4 wacc[NWW], uacc[KEEPU ? NUW : 1];
 #pragma unroll
-        for (int k0 = 0; k0 < BT; k0 += MM::KS)
-          acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
-        store4(upg + cm_off(16 * mt + crow(lane, 0), 16 * nt + ccol(lane), DV), acc[0], acc[1], acc[2], acc[3]);
-        if constexpr (PF && !BWD) {
+      for (int u = 0; u < NUW; ++u) {
+        const int jb = wave + CNW * u;
+        if (jb < NU) {
+          constexpr int NT = DV / 16;
+          const int mt = jb / NT, nt = jb % NT;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) Ul[(16 * mt + crow(lane, r)) * LDV + 16 * nt + ccol(lane)] = from_f<T>(acc[r]);
+          for (int k0 = 0; k0 < BT; k0 += MM::KS)
+            acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
+          store4(upg + cm_off(16 * mt + crow(lane, 0), 16 * nt + ccol(lane), DV), acc[0], acc[1], acc[2], acc[3]);
+          if constexpr (KEEPU) uacc[u] = acc;
         }
       }
       if constexpr (KEEPW) {
@@ -516,7 +521,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
       }
       if constexpr (KEEPW) {
-        __syncthreads();  // every wave is done reading K~: W takes its place
+        __syncthreads();  // every wave is done reading K~ and V: W and U' take their places
 #pragma unroll
         for (int u = 0; u < NWW; ++u) {
           const int jb = wave + CNW * u;
@@ -525,6 +530,19 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             const int mt = jb / NT, nt = jb % NT;
             const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
             store4(Kt + i * LDK + c0, wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]);
+          }
+        }
+        if constexpr (KEEPU) {
+#pragma unroll
+          for (int u = 0; u < NUW; ++u) {
+            const int jb = wave + CNW * u;
+            if (jb < NU) {
+              constexpr int NT = DV / 16;
+              const int mt = jb / NT, nt = jb % NT;
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                Ul[(16 * mt + crow(lane, r)) * LDV + 16 * nt + ccol(lane)] = from_f<T>(uacc[u][r]);
+            }
           }
         }
         __syncthreads();
@@ -545,7 +563,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             if constexpr (PF) store4(qe + pf_off(c, i0, BT), v[0], v[1], v[2], v[3]);
             else fm_store<T>(qe, BT, c, i0, v, 4);
           }
-        } else {
+        }
+        if constexpr (PF && FO) {
           // 9. forward (PF): Qeff = Q~ - M W as [BT][D] (tiles of Qeff^T: rows are channels),
           //    and O' = M U' as accumulator tiles of O'^T (value rows, token columns)
           T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
@@ -788,11 +807,13 @@ __global__ __launch_bounds__(64 * state_waves<D>()) void kda_state_kernel(RoundA
 
 // ------------------------------------------------------------------------------------------
 template <typename T, int BT, int D, int DV>
-static hipError_t prep_launch(const KdaDims& d, const RoundArgs& a, bool bwd, hipStream_t s) {
+static hipError_t prep_launch(const KdaDims& d, const RoundArgs& a, int mode, hipStream_t s) {
   if (a.nchunk <= 0) return hipSuccess;
   dim3 grid(persistent_grid(unsigned(a.nchunk) * d.H)), block(CNT);
-  if (bwd) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, true>), grid, block, 0, s, a, d.H);
-  else hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, false>), grid, block, 0, s, a, d.H);
+  if (mode == 1) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 1>), grid, block, 0, s, a, d.H);
+  else if (mode == 0) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 0>), grid, block, 0, s, a, d.H);
+  else if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 2>), grid, block, 0, s, a, d.H);
+  else return hipErrorNotSupported;
   return hipGetLastError();
 }
 
@@ -825,9 +846,9 @@ bool kda_supported(const KdaDims& d) {
   return false;
 }
 
-hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s) {
+hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, int mode, hipStream_t s) {
 #define X(T_, B_, D_, V_) \
-  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return prep_launch<T_, B_, D_, V_>(d, a, backward, s);
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return prep_launch<T_, B_, D_, V_>(d, a, mode, s);
   HARTS_KDA_CONFIGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -32,17 +32,19 @@
 
 namespace harts {
 
-enum : int { SLAB_FWD = 0, SLAB_REC = 1, SLAB_DST = 2 };
+// SLAB_FWDS: the forward that also writes every chunk-start state (what SLAB_REC writes)
+enum : int { SLAB_FWD = 0, SLAB_REC = 1, SLAB_DST = 2, SLAB_FWDS = 3 };
 
 template <int MODE, int BT, int D, int DV, int NC, int NS, int RD>
 struct SlabCfg {
   static constexpr int KBD = D / 32, KBT = BT / 32, NTT = BT / 16, NTS = D / 16;
   static constexpr int BD = BT * D / 512;                // 1 KiB operand blocks per shared array
+  static constexpr bool FO = MODE == SLAB_FWD || MODE == SLAB_FWDS;  // forward outputs
   static constexpr int NARR = MODE == SLAB_REC ? 2 : 3;  // shared arrays
   static constexpr int EOFF = NARR * BD * 1024;          // E (fp32 [D]), then the chunk descriptor
   static constexpr int SOFF = EOFF + 1024;               // per-slab inputs
   static constexpr int PA = BT * 32;                     // bytes of one per-slab array (BT x 16 x 2 B)
-  static constexpr int NPA = MODE == SLAB_FWD ? 2 : 1;   // per-slab arrays: U', O' | U' | dO
+  static constexpr int NPA = FO ? 2 : 1;             // per-slab arrays: U', O' | U' | dO
   static constexpr int SLABS = NC * NS, NGRP = DV / (16 * SLABS);
   static constexpr int BUF = SOFF + SLABS * NPA * PA;    // bytes per ring buffer
   // producer loads per chunk: shared blocks, E, descriptor, per-slab blocks
@@ -83,6 +85,7 @@ template <int MODE, int BT, int D, int DV, int NC, int NS, int RD>
 struct SlabPass {
   using C = SlabCfg<MODE, BT, D, DV, NC, NS, RD>;
   static constexpr int KBD = C::KBD, KBT = C::KBT, NTT = C::NTT, NTS = C::NTS, BD = C::BD;
+  static constexpr bool FO = C::FO, SAVE = MODE == SLAB_REC || MODE == SLAB_FWDS;
 
   const BwdRoundArgs& b;
   int H, h, si, lane, wave, g4, n16, grp;
@@ -111,10 +114,10 @@ struct SlabPass {
       r.dO = buf_rsrc(b.dO, size_t(0x7fffffff));
     } else {
       r.arr[0] = buf_rsrc(a.ws.W, opb);
-      r.arr[1] = buf_rsrc(MODE == SLAB_FWD ? a.ws.Qt : a.ws.KhT, opb);
+      r.arr[1] = buf_rsrc(FO ? a.ws.Qt : a.ws.KhT, opb);
       r.arr[2] = buf_rsrc(a.ws.KhT, opb);
       r.up = buf_rsrc(a.ws.UpT, items * BT * DV * 2);
-      r.op = buf_rsrc(MODE == SLAB_FWD ? a.ws.Op : a.ws.UpT, items * BT * DV * 2);
+      r.op = buf_rsrc(FO ? a.ws.Op : a.ws.UpT, items * BT * DV * 2);
     }
     r.el = buf_rsrc(a.ws.El, items * D * 4);
     r.desc = buf_rsrc(a.chunks, size_t(a.nchunk) * sizeof(ChunkDesc));
@@ -154,7 +157,7 @@ struct SlabPass {
           const int i = 2 * x + (lane >> 5);
           lds_load16(r.up, sdst + x * 1024, (i * (DV / 16) + j) * 512 + (lane & 31) * 16, int(w * BT * DV * 2));
         }
-        if constexpr (MODE == SLAB_FWD) {
+        if constexpr (FO) {
           // O'^T accumulator tiles (slab j, token block i): contiguous per slab
 #pragma unroll
           for (int x = 0; x < C::PA / 1024; ++x)
@@ -267,18 +270,18 @@ struct SlabPass {
 
   __device__ __forceinline__ void compute_fwd(int c, const char* p) {
     const RoundArgs& a = b.r;
-    const int emit = MODE == SLAB_FWD ? emit_of(p) : -1;
+    const int emit = FO ? emit_of(p) : -1;
     bf16x8 Sf[NS][KBD];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) Sf[s][kb] = pf_pair(S[s][2 * kb], S[s][2 * kb + 1]);
-    if constexpr (MODE == SLAB_REC) {
+    if constexpr (SAVE) {
       const size_t w = wsi(c);
       store_state(static_cast<bf16*>(a.h) + w * DV * D, static_cast<bf16*>(a.hc) + w * D * DV, Sf);
     }
     f32x4 U[NS][NTT];
-    f32x4 O[MODE == SLAB_FWD ? NS : 1][NTT];
+    f32x4 O[FO ? NS : 1][NTT];
     bf16x8 Uf[NS][KBT];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -286,7 +289,7 @@ struct SlabPass {
 #pragma unroll
       for (int i = 0; i < NTT; ++i) {
         U[s][i] = f4_of(*reinterpret_cast<const bf16x4*>(in + i * 512 + lane * 8));
-        if constexpr (MODE == SLAB_FWD) O[s][i] = f4_of(*reinterpret_cast<const bf16x4*>(in + C::PA + i * 512 + lane * 8));
+        if constexpr (FO) O[s][i] = f4_of(*reinterpret_cast<const bf16x4*>(in + C::PA + i * 512 + lane * 8));
       }
     }
     walk(
@@ -332,7 +335,7 @@ struct SlabPass {
                 for (int s = 0; s < NS; ++s) S[s][t] = mfma_bf16(g.f[kb * NTS + t], Uf[s][kb], S[s][t]);
           }
         });
-    if constexpr (MODE == SLAB_FWD) {
+    if constexpr (FO) {
       // own rows only (replayed rows and padding store into the sink)
       bf16* og = static_cast<bf16*>(a.o);
 #pragma unroll
@@ -512,7 +515,7 @@ __global__ __launch_bounds__(64 * (NC + 1)) void kda_slab_kernel(BwdRoundArgs b,
     if constexpr (MODE == SLAB_DST) x.compute_dst(chunk_of(k), p);
     else x.compute_fwd(chunk_of(k), p);
   }
-  if constexpr (MODE == SLAB_FWD) {
+  if constexpr (P::FO) {
     if (x.sd.final_idx >= 0 && a.final_pool) x.store_f32(a.final_pool, x.sd.final_idx);
   }
   if constexpr (MODE == SLAB_DST) {
@@ -570,6 +573,7 @@ template <int BT, int D, int DV>
 static hipError_t slab_mode(const KdaDims& d, const BwdRoundArgs& b, int mode, hipStream_t s) {
   if (b.r.nseq <= 0) return hipSuccess;
   if (mode == SLAB_FWD) return slab_pick<SLAB_FWD, BT, D, DV>(d, b, s);
+  if (mode == SLAB_FWDS) return slab_pick<SLAB_FWDS, BT, D, DV>(d, b, s);
   if (mode == SLAB_REC) return slab_pick<SLAB_REC, BT, D, DV>(d, b, s);
   return slab_pick<SLAB_DST, BT, D, DV>(d, b, s);
 }

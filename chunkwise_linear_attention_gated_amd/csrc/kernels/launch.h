@@ -83,10 +83,11 @@ inline unsigned persistent_grid(unsigned items) {
   return items < unsigned(cus[dev]) ? items : unsigned(cus[dev]);
 }
 
-hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
+// mode 0 forward operands, 1 backward operands, 2 both (bf16)
+hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, int mode, hipStream_t s);
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s);
 // Slab-parallel serial passes (bf16 operands): mode 0 forward, 1 backward state recompute,
-// 2 state gradient.  Returns hipErrorNotSupported for configurations they do not cover.
+// 2 state gradient, 3 forward that also writes every chunk-start state (a.h, a.hc).  Returns hipErrorNotSupported for configurations they do not cover.
 bool kda_slab_supported(const KdaDims& d);
 // out[slot] = sum over the slot's consumer sequences of dinit[consumer], for the listed slots
 hipError_t launch_slot_grad(const KdaDims& d, const int32_t* slots, int32_t nslots, const int32_t* cons_off,

@@ -151,8 +151,9 @@ void harts_plan_free(harts_plan *plan);
 int harts_plan_upload(const harts_plan *plan, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *stream,
                       harts_dev_plan **out);
 
-/* Bytes of caller-provided device workspace for harts_kda_fwd (backward = 0)
- * or harts_kda_bwd (backward = 1). */
+/* Bytes of caller-provided device workspace for harts_kda_fwd (backward = 0),
+ * harts_kda_bwd (backward = 1), or a forward/backward pair with keep = 1
+ * (backward = 2; the same size as 1).  Other values: HARTS_EINVAL. */
 int harts_kda_workspace_size(const harts_dev_plan *dplan, int32_t backward, size_t *bytes);
 
 void harts_dev_plan_free(harts_dev_plan *dplan);
@@ -173,7 +174,13 @@ void harts_dev_plan_free(harts_dev_plan *dplan);
  * init_states: varlen plans only, device float32 [n_seq, H, dk, dv] read for
  *   sequences with has_init != 0 (NULL when none).
  * final_states: varlen plans only, device float32 [n_seq, H, dk, dv] or NULL.
- * workspace: device, >= harts_kda_workspace_size(dplan, 0, ...) bytes.
+ * workspace: device, >= harts_kda_workspace_size(dplan, keep ? 2 : 0, ...) bytes.
+ * keep (0 or 1): 1 makes the forward also write, into the workspace, every
+ *   round's per-chunk backward operands and every chunk-start state, so that a
+ *   following harts_kda_bwd with keep = 1 on the same inputs, states and
+ *   workspace (untouched in between) skips the per-round preparation and state
+ *   recompute.  Results are the same either way.  Honoured for the bf16
+ *   configurations; elsewhere both calls recompute as with keep = 0.
  */
 typedef struct {
   const void *q, *k, *v, *g, *beta;
@@ -183,6 +190,7 @@ typedef struct {
   float *final_states;
   void *workspace;
   size_t workspace_bytes;
+  int32_t keep;
 } harts_kda_io;
 
 int harts_kda_fwd(const harts_dev_plan *dplan, const harts_kda_io *io, void *stream);
@@ -191,7 +199,8 @@ int harts_kda_fwd(const harts_dev_plan *dplan, const harts_kda_io *io, void *str
  * [blog 4.3] differentiable handoff: initial-state gradients accumulate back
  * into the call that produced the boundary; [plsum 4] recomputation under the
  * fixed plan (same layout, rounds, replay and state links; activations are
- * recomputed per round, not kept).  Rounds run in reverse order.
+ * recomputed per round unless the forward kept them, see keep above).  Rounds
+ * run in reverse order.
  *
  * Loss L = sum_rows <dO, o>.  Outputs (device, plan dtype unless noted):
  *   dq, dk, dg [N, H, dk]; dv [N, H, dv]; dbeta [N, H]: gradients of the compact

@@ -19,7 +19,7 @@ from gpu_util import TOL, device_inputs, harts_dtype, node_of_row, oracle_feats,
 NAMES = ("q", "k", "v", "g", "beta")
 
 
-def run_tree_bwd(t, feats, B, H, D, dt):
+def run_tree_bwd(t, feats, B, H, D, dt, keep=False):
     hp = harts.TreePlan(t.tokens, t.offsets, B)
     m, q, _ = hp.maps()
     C = hp.info.C
@@ -29,21 +29,24 @@ def run_tree_bwd(t, feats, B, H, D, dt):
     ns = max(1, hp.info.n_slots)
     o = torch.zeros((C, H, D), dtype=torch_dtype(dt), device="cuda")
     slots = torch.zeros((ns, H, D, D), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True)), dtype=torch.uint8, device="cuda")
-    harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws)
+    ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True), dp.workspace_size(2)),
+                     dtype=torch.uint8, device="cuda")
+    harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=keep)
     gr = {n: torch.full_like(x[n], float("nan")) for n in NAMES}
     dslots = torch.full_like(slots, float("nan"))
     harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"], gr["g"],
-                  gr["beta"], states=slots, dstates=dslots, workspace=ws)
+                  gr["beta"], states=slots, dstates=dslots, workspace=ws, keep=keep)
     torch.cuda.synchronize()
     out = {"d" + n: gr[n].float().cpu().numpy() for n in NAMES}
     out["dslots"] = dslots[:hp.info.n_slots].cpu().numpy()
+    out["o"] = o.float().cpu().numpy()
+    out["slots"] = slots[:hp.info.n_slots].cpu().numpy()
     return hp, nodes, out, q
 
 
-def compare_tree_bwd(t, B, H, D, dt, seed=0):
+def compare_tree_bwd(t, B, H, D, dt, seed=0, keep=False):
     feats = tensors.draw_features(t.n_nodes, H, D, D, seed=seed, dtype=dt)
-    hp, nodes_h, got, _ = run_tree_bwd(t, feats, B, H, D, dt)
+    hp, nodes_h, got, _ = run_tree_bwd(t, feats, B, H, D, dt, keep=keep)
     op = planner.make_plan(t.tokens, t.offsets, B)
     F = oracle_feats(feats)
     ot = TreeOracle(op, t.offsets, t.node_of_pos, F)
@@ -128,6 +131,33 @@ def test_varlen_backward_initial_state_gradient():
     assert rel_err(dinit.cpu().numpy(), ref["dS0"]) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64)])
+def test_kept_forward_operands_backward_bf16(B, D):
+    # the forward keeps the backward's per-chunk operands and chunk-start states
+    rng = np.random.default_rng(57 + B + D)
+    for _ in range(3):
+        t = trees.random_small_tree(rng, max_segments=7, max_len=3 * B, forest=True)
+        compare_tree_bwd(t, B, 3, D, "bf16", seed=int(rng.integers(1000)), keep=True)
+
+
+def test_kept_operands_equal_recompute_bitwise():
+    # the kept operands are computed by the same arithmetic as the recomputed ones
+    for seed, t in [(3, trees.figure2_tree()),
+                    (4, trees.random_small_tree(np.random.default_rng(4), max_segments=9, max_len=300, forest=True)),
+                    (5, trees.GenTree(parent=[-1, 0, 0, 0, 0], length=[100, 30, 40, 50, 60]).finalize(seed=2))]:
+        feats = tensors.draw_features(t.n_nodes, 2, 128, 128, seed=seed, dtype="bf16")
+        a = run_tree_bwd(t, feats, 64, 2, 128, "bf16")[2]
+        b = run_tree_bwd(t, feats, 64, 2, 128, "bf16", keep=True)[2]
+        for k in a:
+            assert np.array_equal(a[k], b[k], equal_nan=True), k
+
+
+def test_kept_operands_fp32_fall_back_to_recompute():
+    t = trees.random_small_tree(np.random.default_rng(78), max_segments=6, max_len=90)
+    errs = compare_tree_bwd(t, 32, 2, 32, "fp32", seed=3, keep=True)
+    assert max(errs.values()) < 1e-4
+
+
 def test_backward_repeat_runs_are_identical():
     t = trees.random_small_tree(np.random.default_rng(9), max_segments=7, max_len=200)
     feats = tensors.draw_features(t.n_nodes, 2, 128, 128, seed=2, dtype="bf16")
@@ -138,14 +168,18 @@ def test_backward_repeat_runs_are_identical():
 
 
 def test_rollout_tree_backward_sampled():
-    """Full 64-leaf tree, H=16, d=128: every compact row's gradient checked on
-    the leaf-only rows (multiplicity 1) of the two trajectories with the most of
-    them, whose
-    gradients depend only on their own trajectory."""
+    """Full 64-leaf tree, H=16, d=128, in the benchmark's configuration (the forward keeps
+    the backward's operands): every compact row's gradient checked on the leaf-only rows
+    (multiplicity 1) of the two trajectories with the most of them, whose gradients depend
+    only on their own trajectory; the recomputing backward must agree bit for bit."""
     H, D, B = 16, 128, 64
     t = trees.random_rollout_tree(seed=0)
     feats = tensors.draw_features(t.n_nodes, H, D, D, seed=1, dtype="bf16")
-    hp, nodes_h, got, q = run_tree_bwd(t, feats, B, H, D, "bf16")
+    hp, nodes_h, got, q = run_tree_bwd(t, feats, B, H, D, "bf16", keep=True)
+    rec = run_tree_bwd(t, feats, B, H, D, "bf16")[2]
+    for k in got:
+        assert np.array_equal(got[k], rec[k], equal_nan=True), k
+    del rec
     for n in ("dq", "dk", "dv", "dg", "dbeta"):
         assert not np.isnan(got[n]).any(), n
     m, _, _ = hp.maps()
@@ -160,9 +194,9 @@ def test_rollout_tree_backward_sampled():
     base = 0
     for x in which:
         mm = m[t.offsets[x]:t.offsets[x + 1]]
-        keep = np.nonzero(q[mm] == 1)[0]
-        sel_pos.append(base + keep)
-        sel_rows.append(mm[keep])
+        own = np.nonzero(q[mm] == 1)[0]
+        sel_pos.append(base + own)
+        sel_rows.append(mm[own])
         base += len(mm)
     sel_pos = np.concatenate(sel_pos)
     sel_rows = np.concatenate(sel_rows)
