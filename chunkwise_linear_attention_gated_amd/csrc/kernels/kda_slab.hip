@@ -73,6 +73,13 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// transposing LDS read of four 16-bit values (gfx950 ds_read_b64_tr_b16)
+__device__ __forceinline__ bf16x4 ds_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -236,15 +243,23 @@ struct SlabPass {
 
   // Chunk-start state (or chunk-end state gradient) as bf16: S^T fragment-major [DV][D] and
   // S in permuted fragment-major [D][DV] (4 x 4 lane transposes), for the gradient kernels.
-  __device__ __forceinline__ void store_state(bf16* hT, bf16* hP, const bf16x8 (&Sf)[NS][KBD]) {
+  // state_rows takes the transposed rows while S still holds the state; state_store issues
+  // the stores once the chunk's products are under way, off the serial chain.
+  __device__ __forceinline__ void state_rows(bf16x4 (&hq)[NS][NTS]) const {
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int t = 0; t < NTS; ++t) hq[s][t] = b4_of(quad_transpose(S[s][t], lane));
+  }
+  __device__ __forceinline__ void state_store(bf16* hT, bf16* hP, const bf16x8 (&Sf)[NS][KBD],
+                                              const bf16x4 (&hq)[NS][NTS]) const {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int t = 0; t < NTS; ++t) {
         const bf16x4 v = (t & 1) ? hi4(Sf[s][t / 2]) : lo4(Sf[s][t / 2]);
         *reinterpret_cast<bf16x4*>(hT + fm_off<bf16>(jv0[s] + n16, 16 * t + 4 * g4, D)) = v;
-        const f32x4 y = quad_transpose(S[s][t], lane);
-        *reinterpret_cast<bf16x4*>(hP + pf_off(16 * t + 4 * g4 + (lane & 3), jv0[s] + 4 * (n16 >> 2), DV)) = b4_of(y);
+        *reinterpret_cast<bf16x4*>(hP + pf_off(16 * t + 4 * g4 + (lane & 3), jv0[s] + 4 * (n16 >> 2), DV)) = hq[s][t];
       }
   }
 
@@ -276,10 +291,8 @@ struct SlabPass {
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) Sf[s][kb] = pf_pair(S[s][2 * kb], S[s][2 * kb + 1]);
-    if constexpr (SAVE) {
-      const size_t w = wsi(c);
-      store_state(static_cast<bf16*>(a.h) + w * DV * D, static_cast<bf16*>(a.hc) + w * D * DV, Sf);
-    }
+    bf16x4 hq[SAVE ? NS : 1][SAVE ? NTS : 1];
+    if constexpr (SAVE) state_rows(hq);
     f32x4 U[NS][NTT];
     f32x4 O[FO ? NS : 1][NTT];
     bf16x8 Uf[NS][KBT];
@@ -335,6 +348,10 @@ struct SlabPass {
                 for (int s = 0; s < NS; ++s) S[s][t] = mfma_bf16(g.f[kb * NTS + t], Uf[s][kb], S[s][t]);
           }
         });
+    if constexpr (SAVE) {
+      const size_t w = wsi(c);
+      state_store(static_cast<bf16*>(a.h) + w * DV * D, static_cast<bf16*>(a.hc) + w * D * DV, Sf, hq);
+    }
     if constexpr (FO) {
       // own rows only (replayed rows and padding store into the sink)
       bf16* og = static_cast<bf16*>(a.o);
@@ -378,24 +395,30 @@ struct SlabPass {
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) Sf[s][kb] = pf_pair(S[s][2 * kb], S[s][2 * kb + 1]);
-    {
-      const size_t w = wsi(c);
-      store_state(static_cast<bf16*>(b.dh) + w * DV * D, static_cast<bf16*>(b.dhc) + w * D * DV, Sf);
-    }
-    // dO fragments: tokens 32 kb + pf_k(g4, t) at the slab's column n16; replayed rows carry
-    // no output gradient here, padding rows none at all
+    bf16x4 hq[NS][NTS];
+    state_rows(hq);
+    // dO fragments: tokens 32 kb + pf_k(g4, t) at the slab's column n16, by two transposing
+    // LDS reads per 32-token block (within each 16-lane group, result element j of lane s is
+    // element s % 4 of the 8 bytes that lane 4 j + s / 4 points at); replayed rows carry no
+    // output gradient here, padding rows none at all
     bf16x8 dof[NS][KBT];
+    const bool masked = c * BT < sd.n_replay || (c + 1) * BT > sd.vlen;  // uniform
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      const bf16* rows = reinterpret_cast<const bf16*>(slab_in(p, s));
+      const char* rows = slab_in(p, s);
 #pragma unroll
-      for (int kb = 0; kb < KBT; ++kb)
+      for (int kb = 0; kb < KBT; ++kb) {
+        const int o = kb * 1024 + (4 * g4 + (n16 >> 2)) * 32 + (n16 & 3) * 8;
+        const bf16x4 lo = ds_tr16(rows + o), hi = ds_tr16(rows + o + 16 * 32);
+        dof[s][kb] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if (masked) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-          const int tok = 32 * kb + pf_k(g4, t), v = c * BT + tok;
-          const bf16 x = rows[tok * 16 + n16];
-          dof[s][kb][t] = v >= sd.n_replay && v < sd.vlen ? x : (bf16)0.f;
+          for (int t = 0; t < 8; ++t) {
+            const int v = c * BT + 32 * kb + pf_k(g4, t);
+            if (!(v >= sd.n_replay && v < sd.vlen)) dof[s][kb][t] = (bf16)0.f;
+          }
         }
+      }
     }
     f32x4 Y[NS][NTT];
     bf16x8 Yf[NS][KBT];
@@ -447,6 +470,8 @@ struct SlabPass {
                 for (int s = 0; s < NS; ++s) S[s][t] = mfma_bf16(g.f[kb * NTS + t], Yf[s][kb], S[s][t]);
           }
         });
+    const size_t w = wsi(c);
+    state_store(static_cast<bf16*>(b.dh) + w * DV * D, static_cast<bf16*>(b.dhc) + w * D * DV, Sf, hq);
   }
 };
 
