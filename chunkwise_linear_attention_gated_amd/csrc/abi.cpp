@@ -566,6 +566,21 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       }
       recomputed[size_t(r)] = ev.record(s1);
     }
+    // The per-chunk gradients of round r + 1 are enqueued behind the start of round r's
+    // state-gradient pass, so that the serial pass takes its compute units before the
+    // gradient kernels fill the chip.
+    auto grads = [&](int r) {
+      harts::BwdRoundArgs b = round(r);
+      if (!keep) hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
+      {
+        ProfScope ps("kda_gradA", s2, units(r));
+        hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");
+      }
+      {
+        ProfScope ps("kda_gradB", s2, units(r));
+        hip_check(harts::launch_kda_grad(d->dims, b, 1, s2), "gradient kernel launch");
+      }
+    };
     for (int r = R - 1; r >= 0; --r) {
       harts::BwdRoundArgs b = round(r);
       if (!keep) hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
@@ -577,22 +592,20 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
                                           const_cast<float*>(b.dslot), s0),
                   "slot gradient launch");
       }
+      // round r + 1's state gradient (and everything before it on s0) is complete here
+      hipEvent_t ready = ev.record(s0);
       {
         ProfScope ps("kda_dstate", s0, units(r));
         if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 2, d->p.rounds[r].max_chunks, s0), "state-gradient kernel launch");
         else hip_check(harts::launch_kda_dstate(d->dims, b, s0), "state-gradient kernel launch");
       }
-      hip_check(hipStreamWaitEvent(s2, ev.record(s0), 0), "hipStreamWaitEvent");
-      if (!keep) hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
-      {
-        ProfScope ps("kda_gradA", s2, units(r));
-        hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");
-      }
-      {
-        ProfScope ps("kda_gradB", s2, units(r));
-        hip_check(harts::launch_kda_grad(d->dims, b, 1, s2), "gradient kernel launch");
+      if (r + 1 < R) {
+        hip_check(hipStreamWaitEvent(s2, ready, 0), "hipStreamWaitEvent");
+        grads(r + 1);
       }
     }
+    hip_check(hipStreamWaitEvent(s2, ev.record(s0), 0), "hipStreamWaitEvent");
+    grads(0);
     // join: the caller's stream continues after every round's gradients
     hip_check(hipStreamWaitEvent(s0, ev.record(s2), 0), "hipStreamWaitEvent");
     hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");

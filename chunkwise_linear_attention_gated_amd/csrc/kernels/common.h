@@ -28,6 +28,15 @@ template <typename T> __device__ __forceinline__ T from_f(float x);
 template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
 template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
 
+// transposing LDS read of four 16-bit values (gfx950 ds_read_b64_tr_b16); p is an LDS
+// address, 8-byte aligned
+__device__ __forceinline__ bf16x4 ds_tr16(const void* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) const char*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16> {
@@ -37,13 +46,14 @@ template <> struct Mma<bf16> {
   __device__ static __forceinline__ Frag kc(const bf16* p, int ld, int r0, int k0, int lane) {
     return *reinterpret_cast<const bf16x8*>(p + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
   }
-  // element (r, k) at p[k * ld + r]: gathered
+  // element (r, k) at p[k * ld + r], p in LDS, ld and r0 multiples of 4: two transposing
+  // reads (in each 16-lane group, result element j of lane s is element s % 4 of the four
+  // that lane 4 j + s / 4 points at), each lane pointing at 4 consecutive r of one k
   __device__ static __forceinline__ Frag rc(const bf16* p, int ld, int r0, int k0, int lane) {
-    Frag f;
-    const bf16* q = p + (k0 + 8 * (lane >> 4)) * ld + r0 + (lane & 15);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) f[t] = q[t * ld];
-    return f;
+    const int s = lane & 15;
+    const bf16* q = p + (k0 + 8 * (lane >> 4) + (s >> 2)) * ld + r0 + 4 * (s & 3);
+    const bf16x4 lo = ds_tr16(q), hi = ds_tr16(q + 4 * ld);
+    return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
   __device__ static __forceinline__ f32x4 mma(Frag a, Frag b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);

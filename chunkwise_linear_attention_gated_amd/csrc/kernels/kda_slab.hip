@@ -73,13 +73,6 @@ __device__ __forceinline__ void lds_load16(__amdgpu_buffer_rsrc_t r, char* dst, 
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
-// transposing LDS read of four 16-bit values (gfx950 ds_read_b64_tr_b16)
-__device__ __forceinline__ bf16x4 ds_tr16(const char* p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(__attribute__((address_space(3))) char*)(p));
-  return __builtin_bit_cast(bf16x4, r);
-}
 __device__ __forceinline__ void wg_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
