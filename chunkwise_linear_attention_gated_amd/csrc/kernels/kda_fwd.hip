@@ -140,6 +140,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   constexpr bool PF = sizeof(T) == 2;
   constexpr bool BWD = PM != 0, FO = PM != 1;
   static_assert(PM != 2 || PF, "kept backward operands need the fragment-major layouts");
+  static_assert(!PF || size_t(BT) * Ly::LDK * sizeof(T) <= Ly::KHT_SZ, "token-major K^ fits its slot");
   constexpr int NB = Ly::NB, LDK = Ly::LDK, LDV = Ly::LDV, LDJ = Ly::LDJ, LDF = Ly::LDF, LDA = Ly::LDA;
   constexpr int VN = In::VN, NK = In::NK, NV = In::NV, NPR = In::NPR, NPRV = In::NPRV;
   __shared__ __attribute__((aligned(16))) char smem[Ly::TOTAL];
@@ -152,7 +153,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   T* Kc0 = reinterpret_cast<T*>(smem + Ly::O_S2);
   T* Vl = Kc0;
   T* Kcd = reinterpret_cast<T*>(smem + Ly::O_S3);
-  T* KhT = Kcd;
+  T* KhT = Kcd;  // fp32: K^^T [D][LDJ]; bf16: K^ token-major [BT][LDK] (read back transposed)
   T* Kcx = reinterpret_cast<T*>(smem + Ly::O_SX);
   T* Tm = reinterpret_cast<T*>(smem + Ly::O_TM);
   float* Af = reinterpret_cast<float*>(smem + Ly::O_A);
@@ -329,19 +330,32 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     __syncthreads();
-    // 6a. diagonal 16x16 blocks of X = (I + diag(beta) A)^{-1} by forward substitution
-    if (wave < NB && lane < 16) {
-      const int b = wave, col = lane;
-      float xv[16];
+    // 6a. diagonal 16x16 blocks of X = (I + N)^{-1}, N = diag(beta) A_bb strictly lower and so
+    //     nilpotent: (I + N)^{-1} = (I - N)(I + N^2)(I + N^4)(I + N^8).  fp32 matrix cores, each
+    //     operand kept with its transpose in accumulator layout (mma16_f32(c(Z^T), c(Y)) = Z Y).
+    if (wave < NB) {
+      const int b = wave, lr = lane & 15, lg = lane >> 4;
+      const float bl = bet[16 * b + lr];
+      const f32x4 arow = ldq(Af + (16 * b + lr) * LDA + 16 * b + 4 * lg);
+      f32x4 n, nt, q, qt;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float s = 0.f;
-#pragma unroll
-        for (int m = 0; m < r; ++m) s += Af[(16 * b + r) * LDA + 16 * b + m] * xv[m];
-        xv[r] = r < col ? 0.f : (r == col ? 1.f : -bet[16 * b + r] * s);
+      for (int r = 0; r < 4; ++r) {
+        const int i = 4 * lg + r;
+        n[r] = bet[16 * b + i] * Af[(16 * b + i) * LDA + 16 * b + lr];
+        nt[r] = bl * arow[r];
+        const float id = i == lr ? 1.f : 0.f;
+        q[r] = id - n[r];
+        qt[r] = id - nt[r];
       }
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 n2 = mma16_f32(nt, n, z), n2t = mma16_f32(n, nt, z);
+      const f32x4 n4 = mma16_f32(n2t, n2, z), n4t = mma16_f32(n2, n2t, z);
+      const f32x4 n8 = mma16_f32(n4t, n4, z);
+      const f32x4 p1 = mma16_f32(qt, n2, q), p1t = mma16_f32(n2, qt, qt);
+      const f32x4 p2 = mma16_f32(p1t, n4, p1), p2t = mma16_f32(n4, p1t, p1t);
+      const f32x4 x = mma16_f32(p2t, n8, p2);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Xf[(16 * b + r) * LDA + 16 * b + col] = xv[r];
+      for (int r = 0; r < 4; ++r) Xf[(16 * b + 4 * lg + r) * LDA + 16 * b + lr] = x[r];
     }
     // 6b. K~ = k e^G, K^ = k e^{G_last - G} (transposed), Q~ = q e^G, V; e^{G_last}
 #pragma unroll
@@ -369,8 +383,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
         if (BWD || PF) stq(Qr + i * LDK + c0, pack16<T>(qt));
         else fm_store<T>(static_cast<T*>(a.ws.Qt) + wsi * BT * D, D, i, c0, qt, VN);
+        if constexpr (PF) {
+          stq(KhT + i * LDK + c0, pack16<T>(kh));
+        } else {
 #pragma unroll
-        for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kh[t]);
+          for (int t = 0; t < VN; ++t) KhT[(c0 + t) * LDJ + i] = from_f<T>(kh[t]);
+        }
       }
     }
 #pragma unroll
@@ -463,10 +481,13 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             }
             if constexpr (BWD) {
               T* wtg = static_cast<T*>(a.ws.WT) + wsi * D * BT;
+              if constexpr (PF) {
+                // 4 x 4 lane transpose: channel c0 + lane % 4, tokens 16 nt + 4 (lane % 16 / 4) + {0..3}
+                const f32x4 y = quad_transpose(wacc[u], lane);
+                store4(wtg + pf_off(c0 + (lane & 3), 16 * nt + 4 * ((lane & 15) >> 2), BT), -y[0], -y[1], -y[2], -y[3]);
+              } else {
 #pragma unroll
-              for (int r = 0; r < 4; ++r) {
-                if constexpr (PF) wtg[pf_off(c0 + r, i, BT)] = from_f<T>(-wacc[u][r]);
-                else wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
+                for (int r = 0; r < 4; ++r) wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
               }
             }
           }
@@ -486,12 +507,15 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
       T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
       if constexpr (PF) {
-        // K^^T [D][BT] permuted fragment-major: two 8-byte row pieces per 16-byte lane slot
+        // K^^T [D][BT] permuted fragment-major from the token-major K^: block (channel block cb,
+        // token block kb), lane l: channel 16 cb + l % 16, tokens 32 kb + 4 (l / 16) + {0..3} and
+        // the same + 16, by two transposing reads (lane q of a 16-lane group points at 4
+        // consecutive channels of token 4 (q / 4) + ...)
         HARTS_STRIDED(pc, tid, D * BT / 8, CNT) {
-          const int blk = pc / 64, l = pc % 64;
-          const int c = 16 * (blk / (BT / 32)) + (l & 15), k0 = 32 * (blk % (BT / 32)) + 4 * (l >> 4);
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(KhT + c * LDJ + k0);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(KhT + c * LDJ + k0 + 16);
+          const int blk = pc / 64, l = pc % 64, q = l & 15;
+          const int cb = blk / (BT / 32), kb = blk % (BT / 32);
+          const T* src = KhT + (32 * kb + 4 * (l >> 4) + (q >> 2)) * LDK + 16 * cb + 4 * (q & 3);
+          const bf16x4 lo = ds_tr16(src), hi = ds_tr16(src + 16 * LDK);
           *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       } else {
