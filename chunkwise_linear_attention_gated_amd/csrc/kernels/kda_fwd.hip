@@ -570,7 +570,31 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           }
         }
         __syncthreads();
-        if constexpr (BWD) {
+        if constexpr (PF) {
+          // 9. Qeff = Q~ - M W once, in tiles of token rows and channel columns: Qeff^T [D][BT]
+          //    (backward) straight from the tile, Qeff [BT][D] (forward) after a 4 x 4 lane
+          //    transpose; Q~ of the tile by one transposing read
+          T* qeT = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
+          T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
+          constexpr int MT = BT / 16, NT = D / 16;
+          HARTS_STRIDED(jb, wave, MT * NT, CNW) {
+            const int mt = jb / NT, nt = jb % NT;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k0 = 0; k0 < BT; k0 += MM::KS)
+              acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
+            const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0), q = lane & 15;
+            const bf16x4 qv = ds_tr16(Qr + (16 * mt + 4 * (lane >> 4) + (q >> 2)) * LDK + 16 * nt + 4 * (q & 3));
+            f32x4 v;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = (float)qv[r] - acc[r];
+            if constexpr (BWD) store4(qeT + pf_off(c, i0, BT), v[0], v[1], v[2], v[3]);
+            if constexpr (FO) {
+              const f32x4 y = quad_transpose(v, lane);
+              store4(qe + pf_off(i0 + (lane & 3), 16 * nt + 4 * (q >> 2), D), y[0], y[1], y[2], y[3]);
+            }
+          }
+        } else if constexpr (BWD) {
           // 9. Qeff = Q~ - M W, stored as Qeff^T [D][BT]
           T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
           constexpr int MT = BT / 16, NT = D / 16;
@@ -584,26 +608,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
-            if constexpr (PF) store4(qe + pf_off(c, i0, BT), v[0], v[1], v[2], v[3]);
-            else fm_store<T>(qe, BT, c, i0, v, 4);
+            fm_store<T>(qe, BT, c, i0, v, 4);
           }
         }
         if constexpr (PF && FO) {
-          // 9. forward (PF): Qeff = Q~ - M W as [BT][D] (tiles of Qeff^T: rows are channels),
-          //    and O' = M U' as accumulator tiles of O'^T (value rows, token columns)
-          T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
-          HARTS_STRIDED(jb, wave, (D / 16) * (BT / 16), CNW) {
-            const int mt = jb / (BT / 16), nt = jb % (BT / 16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BT; k0 += MM::KS)
-              acc = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Ml, LDJ, 16 * nt, k0, lane), acc);
-            const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[i * LDK + c0 + r]) - acc[r];
-            store4(qe + pf_off(i, c0, D), v[0], v[1], v[2], v[3]);
-          }
+          // O' = M U' as accumulator tiles of O'^T (value rows, token columns)
           T* opg = static_cast<T*>(a.ws.Op) + wsi * BT * DV;
           HARTS_STRIDED(jb, wave, (DV / 16) * (BT / 16), CNW) {
             const int jt = jb / (BT / 16), it = jb % (BT / 16);
