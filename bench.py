@@ -131,10 +131,10 @@ def traffic_for(kernel):
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(t, feats, C, S, target_positions=60000, seed=0):
+def cpu_baseline(t, feats, C, S, target_positions=250000, seed=0):
     """The float64 oracle (trajectory-expanded, token by token, forward + reverse pass)
     on a bounded sample: whole trajectories in a seeded random order until about
-    ``target_positions`` semantic positions (about 10 s on 16 cores), extrapolated per
+    ``target_positions`` semantic positions (about 12 s on 16 cores), extrapolated per
     semantic position to the whole batch."""
     from oracle.recurrent import Trajectories, default_threads
     lens = np.diff(t.offsets)
