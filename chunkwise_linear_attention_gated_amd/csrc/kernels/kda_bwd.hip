@@ -371,44 +371,55 @@ __device__ __forceinline__ void ga_rows(GARows<T, BT, D, DV>& r, const RoundArgs
   r.rbase = a.chunks[chunk].replay_base;
 }
 
-template <typename T, int BT, int D, int DV>
+// P selects a part of the fetch (-1: all): 0 k, g; 1 v, dO; 2 T, M, X, A, beta; 3 the state
+// slices.  The persistent loop issues the parts between phases, so that a workgroup's loads
+// are spread over the item instead of queueing behind each other at its top.
+template <typename T, int BT, int D, int DV, int P = -1>
 __device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, BT, D, DV>& r, const BwdRoundArgs& b,
                                         size_t wsi, int h, int H, int tid, int wave, int lane) {
   using C = GACfg<T, BT, D, DV>;
   using MM = typename C::MM;
   const RoundArgs& a = b.r;
+  if constexpr (P < 0 || P == 0) {
 #pragma unroll
-  for (int x = 0; x < C::NK; ++x) {
-    const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
-    const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
-    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
-    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    for (int x = 0; x < C::NK; ++x) {
+      const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
+      const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+      o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+      o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    }
   }
+  if constexpr (P < 0 || P == 1) {
 #pragma unroll
-  for (int x = 0; x < C::NV; ++x) {
-    const int c0 = ((tid + C::NT * x) % C::NPRV) * C::VN;
-    const int rr = r.rv(x);
-    const size_t off = (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0;
-    o.v[x] = ldq(static_cast<const T*>(a.v) + off);
-    o.dO[x] = ldq(static_cast<const T*>(b.dO) + off);
+    for (int x = 0; x < C::NV; ++x) {
+      const int c0 = ((tid + C::NT * x) % C::NPRV) * C::VN;
+      const int rr = r.rv(x);
+      const size_t off = (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0;
+      o.v[x] = ldq(static_cast<const T*>(a.v) + off);
+      o.dO[x] = ldq(static_cast<const T*>(b.dO) + off);
+    }
   }
-  const size_t BB = size_t(BT) * BT;
+  if constexpr (P < 0 || P == 2) {
+    const size_t BB = size_t(BT) * BT;
 #pragma unroll
-  for (int x = 0; x < C::NJ; ++x) {
-    const int p = tid + C::NT * x;
-    const size_t off = wsi * BB + size_t(p < C::NPJ ? p : C::NPJ - 1) * C::VN;
-    o.tm[x] = ldq(static_cast<const T*>(a.ws.Tm) + off);
-    o.mm[x] = ldq(static_cast<const T*>(a.ws.Mm) + off);
-    o.xm[x] = ldq(static_cast<const T*>(a.ws.Xm) + off);
-    o.am[x] = ldq(static_cast<const T*>(a.ws.Am) + off);
+    for (int x = 0; x < C::NJ; ++x) {
+      const int p = tid + C::NT * x;
+      const size_t off = wsi * BB + size_t(p < C::NPJ ? p : C::NPJ - 1) * C::VN;
+      o.tm[x] = ldq(static_cast<const T*>(a.ws.Tm) + off);
+      o.mm[x] = ldq(static_cast<const T*>(a.ws.Mm) + off);
+      o.xm[x] = ldq(static_cast<const T*>(a.ws.Xm) + off);
+      o.am[x] = ldq(static_cast<const T*>(a.ws.Am) + off);
+    }
+    o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
   }
-  o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
-  const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
-  const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
+  if constexpr (P < 0 || P == 3) {
+    const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+    const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    o.hf[ks] = fm_frag<T>(hg, D, wave, ks, lane);
-    o.dhf[ks] = fm_frag<T>(dhg, D, wave, ks, lane);
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      o.hf[ks] = fm_frag<T>(hg, D, wave, ks, lane);
+      o.dhf[ks] = fm_frag<T>(dhg, D, wave, ks, lane);
+    }
   }
 }
 
@@ -467,10 +478,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     const size_t wsi = size_t(item);
     cur = nxt;
     rows = rows_x;
-    {
-      const int itn = item_n < nitems ? item_n : item;
-      ga_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
-    }
+    const int itn = item_n < nitems ? item_n : item;
+    ga_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
     ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
@@ -534,6 +543,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       Tbv[bb * D + c] = s;
     }
     __syncthreads();
+    ga_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k (each thread its own entries)
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
@@ -583,6 +593,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         dU[bi] = mma_k16<T>(am, bo, dU[bi]);
       }
     __syncthreads();  // K~, K^ and V consumed
+    ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 5. U = T R, dR = T^T dU (16-token blocks, right operand in registers); stage R, U, dU, dR
     f32x4 U[NB], dR[NB];
 #pragma unroll
@@ -668,6 +679,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       }
     }
     __syncthreads();
+    ga_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 7. dX = dT diag(beta) (lower incl.) over U; column partial sums of X .* dT for dbeta_1
     HARTS_STRIDED(idx, tid, BT * (BT / VN), NT) {
       const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
@@ -814,45 +826,55 @@ __device__ __forceinline__ void gb_rows(GBRows<T, BT, D, DV>& r, const RoundArgs
 }
 
 // Unconditional loads from clamped addresses: padding is masked where the values are used.
-template <typename T, int BT, int D, int DV>
+// P selects a part of the fetch (-1: all): 0 q, k, g; 1 dO, U, dR; 2 dM, dA; 3 the state
+// slices (issued between phases by the persistent loop, as in kernel A).
+template <typename T, int BT, int D, int DV, int P = -1>
 __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, BT, D, DV>& r, const BwdRoundArgs& b,
                                         size_t wsi, int h, int H, int tid, int wave, int lane) {
   using C = GBCfg<T, BT, D, DV>;
   using MM = typename C::MM;
   const RoundArgs& a = b.r;
+  if constexpr (P < 0 || P == 0) {
 #pragma unroll
-  for (int x = 0; x < C::NK; ++x) {
-    const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
-    const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
-    o.q[x] = ldq(static_cast<const T*>(a.q) + off);
-    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
-    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    for (int x = 0; x < C::NK; ++x) {
+      const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
+      const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+      o.q[x] = ldq(static_cast<const T*>(a.q) + off);
+      o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+      o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    }
   }
-  const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
-  const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
+  if constexpr (P < 0 || P == 1) {
+    const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
+    const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
 #pragma unroll
-  for (int x = 0; x < C::NV; ++x) {
-    const int p = tid + C::NT * x, pc = p < C::NPV ? p : C::NPV - 1;
-    const int c0 = (p % C::NPRV) * C::VN;
-    const int rr = r.rv(x);
-    o.dO[x] = ldq(static_cast<const T*>(b.dO) + (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0);
-    o.u[x] = ldq(ug + size_t(pc) * C::VN);
-    o.dr[x] = ldq(drg + size_t(pc) * C::VN);
+    for (int x = 0; x < C::NV; ++x) {
+      const int p = tid + C::NT * x, pc = p < C::NPV ? p : C::NPV - 1;
+      const int c0 = (p % C::NPRV) * C::VN;
+      const int rr = r.rv(x);
+      o.dO[x] = ldq(static_cast<const T*>(b.dO) + (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0);
+      o.u[x] = ldq(ug + size_t(pc) * C::VN);
+      o.dr[x] = ldq(drg + size_t(pc) * C::VN);
+    }
   }
-  const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BT * BT;
-  const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BT * BT;
+  if constexpr (P < 0 || P == 2) {
+    const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BT * BT;
+    const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BT * BT;
 #pragma unroll
-  for (int x = 0; x < C::NJ; ++x) {
-    const int p = tid + C::NT * x, pc = p < C::NPJ ? p : C::NPJ - 1;
-    o.dm[x] = ldq(dmg + size_t(pc) * C::VN);
-    o.da[x] = ldq(dag + size_t(pc) * C::VN);
+    for (int x = 0; x < C::NJ; ++x) {
+      const int p = tid + C::NT * x, pc = p < C::NPJ ? p : C::NPJ - 1;
+      o.dm[x] = ldq(dmg + size_t(pc) * C::VN);
+      o.da[x] = ldq(dag + size_t(pc) * C::VN);
+    }
   }
-  const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
-  const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
+  if constexpr (P < 0 || P == 3) {
+    const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
+    const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) {
-    o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
-    o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
+    for (int ks = 0; ks < C::NKS; ++ks) {
+      o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
+      o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
+    }
   }
 }
 
@@ -898,10 +920,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     const size_t wsi = size_t(item);
     cur = nxt;
     rows = rows_x;
-    {
-      const int itn = item_n < nitems ? item_n : item;
-      gb_load<T, BT, D, DV>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
-    }
+    const int itn = item_n < nitems ? item_n : item;
+    gb_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
     gb_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
@@ -972,6 +992,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         }
       }
     }
+    gb_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),
     //    block totals Tb and block entry values F (F[NB] = G_last)
     float L[NB][4], Tb[NB], F[NB + 1];
@@ -1007,6 +1028,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         X4[bb][r] *= eh;
       }
     }
+    gb_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 4. 16-token block products with the gated masks factored per block pair:
     //    row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
     //    col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA; times e^{-L_j} later)
@@ -1038,6 +1060,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         X23[bj] = mma_k16<T>(ca, bk2, X23[bj]);
         __builtin_amdgcn_sched_barrier(0);  // one block pair's operands live at a time
       }
+    gb_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 5. assemble dq, dk, dG with exact q, k and fp32 factors
     float csum = 0.f;
 #pragma unroll

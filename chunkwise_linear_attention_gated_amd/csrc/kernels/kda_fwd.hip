@@ -97,7 +97,9 @@ __device__ __forceinline__ void prep_rows(PrepRows<T, BT, D, DV>& r, const int32
   r.rb = cr[tid < BT ? tid : BT - 1];
 }
 
-template <typename T, int BT, int D, int DV>
+// PART selects a part of the fetch (-1: all): 0 g and beta, 1 k, 2 q.  The persistent loop
+// issues the parts between phases so that a workgroup's loads do not queue at its top.
+template <typename T, int BT, int D, int DV, int PART = -1>
 __device__ __forceinline__ void prep_load(PrepIn<T, BT, D, DV>& o, const PrepRows<T, BT, D, DV>& r, const RoundArgs& a,
                                           int h, int H, int tid) {
   using P = PrepIn<T, BT, D, DV>;
@@ -105,11 +107,11 @@ __device__ __forceinline__ void prep_load(PrepIn<T, BT, D, DV>& o, const PrepRow
   for (int x = 0; x < P::NK; ++x) {
     const int c0 = ((tid + CNT * x) % P::NPR) * P::VN;
     const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
-    o.g[x] = ldq(static_cast<const T*>(a.g) + off);
-    o.k[x] = ldq(static_cast<const T*>(a.k) + off);
-    o.q[x] = ldq(static_cast<const T*>(a.q) + off);
+    if constexpr (PART < 0 || PART == 0) o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    if constexpr (PART < 0 || PART == 1) o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+    if constexpr (PART < 0 || PART == 2) o.q[x] = ldq(static_cast<const T*>(a.q) + off);
   }
-  o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
+  if constexpr (PART < 0 || PART == 0) o.beta = static_cast<const T*>(a.beta)[size_t(r.rb >= 0 ? r.rb : 0) * H + h];
 }
 
 template <typename T, int BT, int D, int DV>
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     // this item's values; fetch ahead: inputs of the next item, rows of the one after
     f32x4 vv[NV];
     prep_load_v<T, BT, D, DV>(vv, rows, a, h, H, tid);
-    prep_load<T, BT, D, DV>(nxt, rows_n, a, (item_n < nitems ? item_n : item) % H, H, tid);
+    const int hn = (item_n < nitems ? item_n : item) % H;
+    prep_load<T, BT, D, DV, 0>(nxt, rows_n, a, hn, H, tid);
     rows_x = rows_n;
     const int item_nn = item_n + gridDim.x;
     prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
@@ -225,6 +228,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       Tv[b * D + c] = acc;
     }
     __syncthreads();
+    prep_load<T, BT, D, DV, 1>(nxt, rows_x, a, hn, H, tid);
     // 3. per channel: block entry log-decays F_b, e^{F_b}, e^{F_end - F_{b+1}}, pair scales
     HARTS_STRIDED(c, tid, D, CNT) {
       float f = 0.f, fv[NB + 1], tb[NB];
@@ -290,6 +294,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     __syncthreads();
+    prep_load<T, BT, D, DV, 2>(nxt, rows_x, a, hn, H, tid);
     // 5. A (strict lower, fp32) into Af; M (lower incl.) to the workspace (and Ml), one 16x16 tile each
     T* Mg = static_cast<T*>(a.ws.Mm) + wsi * BT * BT;
     {
