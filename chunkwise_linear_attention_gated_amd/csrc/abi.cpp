@@ -40,6 +40,7 @@ struct harts_dev_plan {
   size_t off_W = 0, off_Op = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
          off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0, off_dslot = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
+  size_t off_ctr = 0;
 };
 
 namespace {
@@ -218,6 +219,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.Op = at(d->off_Op, BT * dv, es);
   a.h = at(d->off_h, dv * dk, es);
   a.hc = at(d->off_hc, dv * dk, es);
+  a.ctr = nullptr;
   return a;
 }
 
@@ -418,6 +420,9 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_Mm = take(MC * BT * BT * es);
       d->off_El = take(MC * dk * 4);
       d->off_sink = take(kSinkBytes);
+      // item counters of the persistent per-chunk kernels: per round, forward preparation,
+      // backward preparation, gradient kernels A and B; zeroed at the start of every call
+      d->off_ctr = take(size_t(4) * d->p.rounds.size() * sizeof(int32_t));
       d->off_Qt = take(MC * BT * dk * es);
       d->off_Op = take(MC * BT * dv * es);
       d->ws_fwd = off;
@@ -471,29 +476,35 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     check_io(d, io, false);
     hipStream_t s0 = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(io->workspace);
-    // Preparation of every round runs ahead on an auxiliary stream (it depends on the inputs
-    // only); the serial passes follow in round order on the caller's stream.
+    // Preparation runs on an auxiliary stream (it depends on the inputs only); the serial
+    // passes follow in round order on the caller's stream.
     Events ev;
     hipStream_t s1 = aux_stream(0);
-    fork(s0, s1, ev);
     const bool slab = harts::kda_slab_supported(d->dims);
     // keep: the preparation also writes the backward's per-chunk operands and the serial pass
     // every chunk-start state, so that the backward neither prepares nor recomputes
     const bool keep = io->keep && slab;
-    std::vector<hipEvent_t> prepped(size_t(d->p.n_rounds));
+    int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
+    hip_check(harts::launch_zero_i32(ctr, 4 * int64_t(d->p.n_rounds), s0), "counter reset");
+    fork(s0, s1, ev);
+    // Round r + 1's preparation is enqueued behind the start of round r's serial pass, so that
+    // the serial pass takes its compute units first; the preparation's workgroups draw items
+    // from a counter and fill the rest of the chip as it frees up.
+    hipEvent_t started = nullptr;
     for (int r = 0; r < d->p.n_rounds; ++r) {
-      harts::RoundArgs a = round_args(d, io, r, ws);
       const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
-      ProfScope ps("kda_prep_fwd", s1, units);
-      hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, s1), "prep kernel launch");
-      prepped[size_t(r)] = ev.record(s1);
-    }
-    for (int r = 0; r < d->p.n_rounds; ++r) {
+      if (started) hip_check(hipStreamWaitEvent(s1, started, 0), "hipStreamWaitEvent");
+      {
+        harts::RoundArgs a = round_args(d, io, r, ws);
+        a.ctr = ctr + 4 * r;
+        ProfScope ps("kda_prep_fwd", s1, units);
+        hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, s1), "prep kernel launch");
+      }
+      hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
+      started = ev.record(s0);
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
       if (!keep) a.h = a.hc = nullptr;
-      const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
-      hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       ProfScope ps("kda_state_fwd", s0, units);
       if (slab) {
         harts::BwdRoundArgs b{};
@@ -504,6 +515,7 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
         hip_check(harts::launch_kda_state(d->dims, a, false, s0), "state kernel launch");
       }
     }
+    // join: every preparation precedes the last serial pass on the caller's stream
   });
 }
 
@@ -526,6 +538,8 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     //       gradient are done.
     Events ev;
     hipStream_t s1 = aux_stream(0), s2 = aux_stream(1);
+    int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
+    hip_check(harts::launch_zero_i32(ctr, 4 * int64_t(R), s0), "counter reset");
     fork(s0, s1, ev);
     fork(s0, s2, ev);
     auto round = [&](int r) {
@@ -556,7 +570,9 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       harts::BwdRoundArgs b = round(r);
       {
         ProfScope ps("kda_prep_bwd", s1, units(r));
-        hip_check(harts::launch_kda_prep(d->dims, b.r, 1, s1), "prep kernel launch");
+        harts::RoundArgs a = b.r;
+        a.ctr = ctr + 4 * r + 1;
+        hip_check(harts::launch_kda_prep(d->dims, a, 1, s1), "prep kernel launch");
       }
       prepped[size_t(r)] = ev.record(s1);
       {
@@ -574,10 +590,12 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       if (!keep) hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
       {
         ProfScope ps("kda_gradA", s2, units(r));
+        b.r.ctr = ctr + 4 * r + 2;
         hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");
       }
       {
         ProfScope ps("kda_gradB", s2, units(r));
+        b.r.ctr = ctr + 4 * r + 3;
         hip_check(harts::launch_kda_grad(d->dims, b, 1, s2), "gradient kernel launch");
       }
     };

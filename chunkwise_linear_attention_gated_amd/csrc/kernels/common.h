@@ -163,6 +163,16 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
   _Pragma("unroll") for (int var##_u = 0; var##_u < ((n) + (step) - 1) / (step); ++var##_u) \
     if (const int var = (start) + (step) * var##_u; var < (n))
 
+// Item order of a persistent per-chunk kernel.  Workgroup b takes items b and b + G (G = grid
+// size) statically, then items 2G + t for tickets t drawn from a per-launch counter that starts
+// at zero.  Thread 0 draws a ticket at the top of each item and publishes it through one LDS
+// word at the top of the next item; the workgroup reads it after that item's first barrier, so a
+// ticket is drawn two items before it is processed.  A workgroup that starts late (its compute
+// unit was busy with another kernel) simply draws fewer tickets.  Each workgroup's draws
+// increase, so once its item is past the end so are all its later draws, and every ticket below
+// the end is processed by the workgroup that drew it.
+__device__ __forceinline__ int draw_ticket(int* ctr) { return atomicAdd(ctr, 1); }
+
 // A zero the compiler cannot see through.  Loads of per-chunk descriptor fields are
 // indexed with it so their values stay per-lane: a value the compiler knows to be
 // uniform is moved to a scalar register right where it is loaded, which waits for

@@ -469,8 +469,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
   ga_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
   int item_n = item + gridDim.x;
   ga_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
+  __shared__ int tk_slot;
+  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
+  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
 
-  for (; item < nitems; item += gridDim.x) {
+  while (item < nitems) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
@@ -481,8 +484,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     const int itn = item_n < nitems ? item_n : item;
     ga_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     rows_x = rows_n;
-    const int item_nn = item_n + gridDim.x;
-    ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
+    if (a.ctr && tid == 0) {
+      tk_slot = tk;
+      tk = draw_ticket(a.ctr);
+    }
 
     // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -530,6 +535,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     }
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
     __syncthreads();
+    // the item after the next one: its rows are fetched a whole item ahead of their use
+    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
+    ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
     // 2. decay per (16-row block, channel): block-local cumulative L, block totals
     float Lr[16];
     HARTS_STRIDED(idx, tid, NB * D, NT) {
@@ -752,6 +760,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       else b.replay_grad[(size_t(rows.rbase + i) * H + h) * G::W + G::DB] = s;
     }
     __syncthreads();  // the next item restages every region
+    item = item_n;
     item_n = item_nn;
   }
 }
@@ -911,8 +920,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
   gb_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
   int item_n = item + gridDim.x;
   gb_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
+  __shared__ int tk_slot;
+  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
+  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
 
-  for (; item < nitems; item += gridDim.x) {
+  while (item < nitems) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
     const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
@@ -923,8 +935,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     const int itn = item_n < nitems ? item_n : item;
     gb_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     rows_x = rows_n;
-    const int item_nn = item_n + gridDim.x;
-    gb_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
+    if (a.ctr && tid == 0) {
+      tk_slot = tk;
+      tk = draw_ticket(a.ctr);
+    }
 
     // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
@@ -959,6 +973,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       }
     }
     __syncthreads();
+    // the item after the next one: its rows are fetched a whole item ahead of their use
+    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
+    gb_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
 
     const int c = 16 * wave + cc;
     // 2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
@@ -1141,6 +1158,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       }
     }
     __syncthreads();  // the next item restages every region
+    item = item_n;
     item_n = item_nn;
   }
 }

@@ -179,8 +179,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   prep_load<T, BT, D, DV>(nxt, rows_x, a, item % H, H, tid0);
   int item_n = item + gridDim.x;
   prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_n < nitems ? item_n : item) / H, tid0);
+  __shared__ int tk_slot;
+  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
+  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
 
-  for (; item < nitems; item += gridDim.x) {
+  while (item < nitems) {
     // thread-derived addresses are recomputed per item instead of being held across the loop
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
@@ -195,8 +198,10 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     const int hn = (item_n < nitems ? item_n : item) % H;
     prep_load<T, BT, D, DV, 0>(nxt, rows_n, a, hn, H, tid);
     rows_x = rows_n;
-    const int item_nn = item_n + gridDim.x;
-    prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
+    if (a.ctr && tid == 0) {
+      tk_slot = tk;
+      tk = draw_ticket(a.ctr);
+    }
 
     // 1. g -> Gf (fp32), beta
 #pragma unroll
@@ -213,6 +218,9 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     }
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
     __syncthreads();
+    // the item after the next one: its rows are fetched a whole item ahead of their use
+    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
+    prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
     // 2. block-local cumulative sums L and block totals
     HARTS_STRIDED(idx, tid, NB * D, CNT) {
       const int b = idx / D, c = idx % D;
@@ -631,6 +639,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     __syncthreads();  // the next item overwrites every region
+    item = item_n;
     item_n = item_nn;
   }
 }

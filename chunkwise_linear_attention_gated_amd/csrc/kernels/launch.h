@@ -52,6 +52,8 @@ struct RoundArgs {
                               // unconditional, so the wait counters see the same count on every path
   void* h;                    // backward: S_n^T per chunk [chunk][H][DV][D] (nullable)
   void* hc;                   // backward: S_n per chunk, channel-major [chunk][H][D][DV] (nullable)
+  int* ctr;                   // zeroed item counter of this launch of a persistent per-chunk kernel
+                              // (nullable: static item order)
 };
 
 struct BwdRoundArgs {
@@ -100,6 +102,8 @@ hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const 
                                void* dg, void* dbeta, hipStream_t s);
 bool kda_supported(const KdaDims& d);
 
+// p[0..n) = 0 on stream s
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
                           int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
 

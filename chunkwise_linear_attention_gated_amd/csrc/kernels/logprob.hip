@@ -105,6 +105,12 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n) {
   for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < n; i += int64_t(gridDim.x) * blockDim.x) p[i] = 0;
 }
 
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(unsigned((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096)), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, int64_t V, const int64_t* __restrict__ m,
                                                      const int32_t* __restrict__ labels, int64_t S,
