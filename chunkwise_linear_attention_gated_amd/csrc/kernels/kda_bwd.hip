@@ -582,8 +582,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         r1 = MM::mma(MM::kc(Kt, LDK, 16 * bb, ks * MM::KS, lane), cur.hf[ks], r1);
         r2 = MM::mma(MM::kc(Kh, LDK, 16 * bb, ks * MM::KS, lane), cur.dhf[ks], r2);
       }
+      float vv[4];
+      col4_load<T>(Vs, LDV, 16 * bb, 16 * wave, lane, vv);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) R[bb][r] = to_f(Vs[(16 * bb + 4 * g4 + r) * LDV + jv]) - r1[r];
+      for (int r = 0; r < 4; ++r) R[bb][r] = vv[r] - r1[r];
       dU[bb] = r2;
     }
 #pragma unroll
@@ -593,11 +595,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         if (br < bi) continue;
         // dU block bi += sum over rows of block br of M[r][i] dO[r][jv]
         float am[4], bo[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          am[t] = to_f(Ml[(16 * br + 4 * g4 + t) * LDJ + 16 * bi + cc]);
-          bo[t] = to_f(dOs[(16 * br + 4 * g4 + t) * LDV + jv]);
-        }
+        col4_load<T>(Ml, LDJ, 16 * br, 16 * bi, lane, am);
+        col4_load<T>(dOs, LDV, 16 * br, 16 * wave, lane, bo);
         dU[bi] = mma_k16<T>(am, bo, dU[bi]);
       }
     __syncthreads();  // K~, K^ and V consumed
@@ -611,10 +610,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
         float ta[4], tb[4], rb[4], ub[4];
+        col4_load<T>(Tl, LDJ, 16 * bi, 16 * bj, lane, tb);  // T[i][j] as (j, i)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           ta[t] = to_f(Tl[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);  // T[i][j], i in bi, j in bj
-          tb[t] = to_f(Tl[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);  // T[i][j] as (j, i)
           rb[t] = R[bj][t];
           ub[t] = dU[bi][t];
         }
@@ -623,15 +622,12 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = 16 * bb + 4 * g4 + r;
-        Rs[i * LDV + jv] = from_f<T>(R[bb][r]);
-        Us[i * LDV + jv] = from_f<T>(U[bb][r]);
-        dUs[i * LDV + jv] = from_f<T>(dU[bb][r]);
-        dRs[i * LDV + jv] = from_f<T>(dR[bb][r]);
-      }
+    for (int bb = 0; bb < NB; ++bb) {
+      col4_store<T>(Rs, LDV, 16 * bb, 16 * wave, lane, R[bb]);
+      col4_store<T>(Us, LDV, 16 * bb, 16 * wave, lane, U[bb]);
+      col4_store<T>(dUs, LDV, 16 * bb, 16 * wave, lane, dU[bb]);
+      col4_store<T>(dRs, LDV, 16 * bb, 16 * wave, lane, dR[bb]);
+    }
     __syncthreads();
     // 6. dM = lower(dO U^T) (computed transposed) to the workspace; dT = dU R^T (fp32) over T, M;
     //    U and dR to the workspace; dv of own rows to the output, of replayed rows to the side buffer
@@ -1016,10 +1012,11 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     F[0] = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
-      float s = 0.f;
+      float s = 0.f, gv[4];
+      col4_load<T>(Gs, LDK, 16 * bb, 16 * wave, lane, gv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        s += to_f(Gs[(16 * bb + 4 * g4 + r) * LDK + c]);
+        s += gv[r];
         L[bb][r] = s;
       }
       float tot[4];
@@ -1055,23 +1052,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       for (int bj = 0; bj <= bi; ++bj) {
         // row side: output block bi, contraction over block bj
         float am[4], aa[4], bk[4];
+        col4_load<T>(Ks, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           am[t] = to_f(dMs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
           aa[t] = to_f(dAs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
-          bk[t] = to_f(Ks[(16 * bj + 4 * g4 + t) * LDK + c]) * __expf(F[bi] - F[bj] - L[bj][t]);
+          bk[t] *= __expf(F[bi] - F[bj] - L[bj][t]);
         }
         dqa[bi] = mma_k16<T>(am, bk, dqa[bi]);
         X1[bi] = mma_k16<T>(aa, bk, X1[bi]);
         // col side: output block bj, contraction over block bi
         float cm[4], ca[4], bq[4], bk2[4];
+        col4_load<T>(dMs, LDJ, 16 * bi, 16 * bj, lane, cm);
+        col4_load<T>(dAs, LDJ, 16 * bi, 16 * bj, lane, ca);
+        col4_load<T>(Qs, LDK, 16 * bi, 16 * wave, lane, bq);
+        col4_load<T>(Ks, LDK, 16 * bi, 16 * wave, lane, bk2);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          cm[t] = to_f(dMs[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);
-          ca[t] = to_f(dAs[(16 * bi + 4 * g4 + t) * LDJ + 16 * bj + cc]);
           const float e = __expf(L[bi][t] + F[bi] - F[bj]);
-          bq[t] = to_f(Qs[(16 * bi + 4 * g4 + t) * LDK + c]) * e;
-          bk2[t] = to_f(Ks[(16 * bi + 4 * g4 + t) * LDK + c]) * e;
+          bq[t] *= e;
+          bk2[t] *= e;
         }
         X23[bj] = mma_k16<T>(cm, bq, X23[bj]);
         X23[bj] = mma_k16<T>(ca, bk2, X23[bj]);
@@ -1081,20 +1081,23 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     // 5. assemble dq, dk, dG with exact q, k and fp32 factors
     float csum = 0.f;
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
+    for (int bb = 0; bb < NB; ++bb) {
+      float kvv[4], qvv[4];
+      col4_load<T>(Ks, LDK, 16 * bb, 16 * wave, lane, kvv);
+      col4_load<T>(Qs, LDK, 16 * bb, 16 * wave, lane, qvv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float Lv = L[bb][r];
         const float er = __expf(Lv), ecd = __expf(-Lv), ec = __expf(Tb[bb] - Lv);
         const float dq = er * dqa[bb][r];
         const float krow = er * X1[bb][r], kcol = ecd * X23[bb][r] + ec * X4[bb][r];
-        const int i = 16 * bb + 4 * g4 + r;
-        const float kv = to_f(Ks[i * LDK + c]), qv = to_f(Qs[i * LDK + c]);
+        const float kv = kvv[r], qv = qvv[r];
         dqa[bb][r] = dq;
         X1[bb][r] = krow + kcol;                        // dk
         X23[bb][r] = qv * dq + kv * (krow - kcol);      // dG
         csum += kv * ec * X4[bb][r];
       }
+    }
     csum += __shfl_xor(csum, 16, 64);
     csum += __shfl_xor(csum, 32, 64);
     // 6. dg = reverse cumulative sum of dG over the chunk, dG_last added at the last row
