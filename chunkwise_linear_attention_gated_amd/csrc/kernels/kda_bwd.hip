@@ -619,7 +619,6 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         }
         U[bi] = mma_k16<T>(ta, rb, U[bi]);
         dR[bj] = mma_k16<T>(tb, ub, dR[bj]);
-        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
@@ -1043,6 +1042,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       }
     }
     gb_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
+    // e^{L} and e^{-L} at this lane's tokens, shared by the block products and the assembly
+    float eL[NB][4], enL[NB][4];
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        eL[bb][r] = __expf(L[bb][r]);
+        enL[bb][r] = __expf(-L[bb][r]);
+      }
     // 4. 16-token block products with the gated masks factored per block pair:
     //    row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
     //    col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA; times e^{-L_j} later)
@@ -1051,13 +1059,14 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
         // row side: output block bi, contraction over block bj
+        const float epf = bi == bj ? 1.f : __expf(F[bi] - F[bj]);  // <= 1
         float am[4], aa[4], bk[4];
         col4_load<T>(Ks, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           am[t] = to_f(dMs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
           aa[t] = to_f(dAs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
-          bk[t] *= __expf(F[bi] - F[bj] - L[bj][t]);
+          bk[t] *= epf * enL[bj][t];
         }
         dqa[bi] = mma_k16<T>(am, bk, dqa[bi]);
         X1[bi] = mma_k16<T>(aa, bk, X1[bi]);
@@ -1069,13 +1078,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         col4_load<T>(Ks, LDK, 16 * bi, 16 * wave, lane, bk2);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float e = __expf(L[bi][t] + F[bi] - F[bj]);
+          const float e = eL[bi][t] * epf;
           bq[t] *= e;
           bk2[t] *= e;
         }
         X23[bj] = mma_k16<T>(cm, bq, X23[bj]);
         X23[bj] = mma_k16<T>(ca, bk2, X23[bj]);
-        __builtin_amdgcn_sched_barrier(0);  // one block pair's operands live at a time
       }
     gb_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 5. assemble dq, dk, dG with exact q, k and fp32 factors
@@ -1085,10 +1093,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       float kvv[4], qvv[4];
       col4_load<T>(Ks, LDK, 16 * bb, 16 * wave, lane, kvv);
       col4_load<T>(Qs, LDK, 16 * bb, 16 * wave, lane, qvv);
+      const float eT = __expf(Tb[bb]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float Lv = L[bb][r];
-        const float er = __expf(Lv), ecd = __expf(-Lv), ec = __expf(Tb[bb] - Lv);
+        const float er = eL[bb][r], ecd = enL[bb][r], ec = eT * ecd;
         const float dq = er * dqa[bb][r];
         const float krow = er * X1[bb][r], kcol = ecd * X23[bb][r] + ec * X4[bb][r];
         const float kv = kvv[r], qv = qvv[r];
