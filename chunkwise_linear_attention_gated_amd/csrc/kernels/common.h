@@ -261,10 +261,9 @@ __device__ __forceinline__ f32x4 quad_transpose(f32x4 x, int lane) {
   return ev ? f32x4{y[0], r0, y[2], r1} : f32x4{r0, y[1], r1, y[3]};
 }
 
-// Column slices of row-major LDS tiles in the accumulator layout: lane l handles column
-// c0 + l % 16 and rows r0 + 4 (l / 16) + t, t = 0..3 (ld and c0 multiples of 4, bf16 tiles 8-byte
-// aligned).  bf16 reads are one transposing read, bf16 writes one 4 x 4 lane transpose and one
-// 8-byte store.
+// Column slice of a row-major LDS tile in the accumulator layout: lane l reads column
+// c0 + l % 16, rows r0 + 4 (l / 16) + t, t = 0..3 (ld and c0 multiples of 4, bf16 tiles 8-byte
+// aligned); bf16 by one transposing read.
 template <typename T>
 __device__ __forceinline__ void col4_load(const T* p, int ld, int r0, int c0, int lane, float (&v)[4]) {
   if constexpr (sizeof(T) == 2) {
@@ -277,18 +276,6 @@ __device__ __forceinline__ void col4_load(const T* p, int ld, int r0, int c0, in
     for (int t = 0; t < 4; ++t) v[t] = p[(r0 + 4 * (lane >> 4) + t) * ld + c0 + (lane & 15)];
   }
 }
-template <typename T>
-__device__ __forceinline__ void col4_store(T* p, int ld, int r0, int c0, int lane, f32x4 v) {
-  if constexpr (sizeof(T) == 2) {
-    const f32x4 y = quad_transpose(v, lane);
-    *reinterpret_cast<bf16x4*>(p + (r0 + 4 * (lane >> 4) + (lane & 3)) * ld + c0 + 4 * ((lane & 15) >> 2)) =
-        bf16x4{(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
-  } else {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) p[(r0 + 4 * (lane >> 4) + t) * ld + c0 + (lane & 15)] = v[t];
-  }
-}
-
 // Elements of T in the store sink (RoundArgs::sink, 64 KiB)
 template <typename T> __host__ __device__ constexpr int kSinkElems() { return 64 * 1024 / sizeof(T); }
 

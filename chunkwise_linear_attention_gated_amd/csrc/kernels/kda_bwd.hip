@@ -476,7 +476,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
   while (item < nitems) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
+    // the wave index is uniform: tile selection and addressing derived from it stay scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), cc = lane & 15, g4 = lane >> 4;
     const int h = item % H;
     const size_t wsi = size_t(item);
     cur = nxt;
@@ -620,13 +621,17 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         U[bi] = mma_k16<T>(ta, rb, U[bi]);
         dR[bj] = mma_k16<T>(tb, ub, dR[bj]);
       }
+    // scalar stores: the LDS pipe takes them, where a lane transpose would cost vector ALU time
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      col4_store<T>(Rs, LDV, 16 * bb, 16 * wave, lane, R[bb]);
-      col4_store<T>(Us, LDV, 16 * bb, 16 * wave, lane, U[bb]);
-      col4_store<T>(dUs, LDV, 16 * bb, 16 * wave, lane, dU[bb]);
-      col4_store<T>(dRs, LDV, 16 * bb, 16 * wave, lane, dR[bb]);
-    }
+    for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * bb + 4 * g4 + r;
+        Rs[i * LDV + jv] = from_f<T>(R[bb][r]);
+        Us[i * LDV + jv] = from_f<T>(U[bb][r]);
+        dUs[i * LDV + jv] = from_f<T>(dU[bb][r]);
+        dRs[i * LDV + jv] = from_f<T>(dR[bb][r]);
+      }
     __syncthreads();
     // 6. dM = lower(dO U^T) (computed transposed) to the workspace; dT = dU R^T (fp32) over T, M;
     //    U and dR to the workspace; dv of own rows to the output, of replayed rows to the side buffer
@@ -922,7 +927,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
   while (item < nitems) {
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6, cc = lane & 15, g4 = lane >> 4;
+    // the wave index is uniform: tile selection and addressing derived from it stay scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), cc = lane & 15, g4 = lane >> 4;
     const int h = item % H;
     const size_t wsi = size_t(item);
     cur = nxt;

@@ -187,7 +187,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     // thread-derived addresses are recomputed per item instead of being held across the loop
     int tid = threadIdx.x;
     asm volatile("" : "+v"(tid));
-    const int lane = tid & 63, wave = tid >> 6;
+    // the wave index is uniform: tile selection and addressing derived from it stay scalar
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = item % H;
     const size_t wsi = size_t(item);  // (round-local chunk) * H + head
     cur = nxt;
