@@ -371,8 +371,8 @@ __device__ __forceinline__ void ga_rows(GARows<T, BT, D, DV>& r, const RoundArgs
   r.rbase = a.chunks[chunk].replay_base;
 }
 
-// P selects a part of the fetch (-1: all): 0 k, g; 1 v, dO; 2 T, M, X, A, beta; 3 the state
-// slices.  The persistent loop issues the parts between phases, so that a workgroup's loads
+// P selects a part of the fetch (-1: all): 0 k, g; 1 v, dO; 2 T, M, X, A, beta; 3 and 4 the
+// state and state-gradient slices.  The persistent loop issues the parts between phases, so that a workgroup's loads
 // are spread over the item instead of queueing behind each other at its top.
 template <typename T, int BT, int D, int DV, int P = -1>
 __device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, BT, D, DV>& r, const BwdRoundArgs& b,
@@ -414,12 +414,13 @@ __device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, B
   }
   if constexpr (P < 0 || P == 3) {
     const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) o.hf[ks] = fm_frag<T>(hg, D, wave, ks, lane);
+  }
+  if constexpr (P < 0 || P == 4) {
     const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      o.hf[ks] = fm_frag<T>(hg, D, wave, ks, lane);
-      o.dhf[ks] = fm_frag<T>(dhg, D, wave, ks, lane);
-    }
+    for (int ks = 0; ks < C::NKS; ++ks) o.dhf[ks] = fm_frag<T>(dhg, D, wave, ks, lane);
   }
 }
 
@@ -520,8 +521,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         stq(Tl + i * LDJ + j0, cur.tm[x]);
         stq(Xl + i * LDJ + j0, cur.xm[x]);
         stq(Al + i * LDJ + j0, cur.am[x]);
-        // M arrives fragment-major: element o of the piece is row r, column k of M
-        {
+        if constexpr (sizeof(T) == 2) {
+          stq(Ml + i * LDJ + j0, cur.mm[x]);  // row-major from the bf16 preparation
+        } else {
+          // M arrives fragment-major: element o of the piece is row r, column k of M
           constexpr int LE = fm_le<T>(), KS = MM::KS;
           float mv[VN];
           unpack16<T>(cur.mm[x], mv);
@@ -718,6 +721,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       store4(Y1t + (16 * nk + cc) * LDJ + 16 * mi + 4 * g4, acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
+    ga_load<T, BT, D, DV, 4>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 9. dL = -X^T Y1 (lower tiles, computed transposed): dA = strict_lower(diag(beta) dL) to the
     //    workspace, row partial sums of dL .* A for dbeta_2
     {
@@ -1247,12 +1251,14 @@ static hipError_t fixup_launch(const KdaDims& d, const int32_t* rows, const int3
   X(float, 16, 16, 16)           \
   X(float, 32, 32, 32)
 
+// fp32 configurations only: bf16 runs the slab passes (kda_slab.hip)
 hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
-#define X(T_, B_, D_, V_) \
-  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return dstate_launch<T_, B_, D_, V_>(d, b, s);
+#define X(T_, B_, D_, V_)                                                             \
+  if constexpr (sizeof(T_) == 4)                                                      \
+    if (d.dtype == 1 && d.BT == B_ && d.D == D_ && d.DV == V_) return dstate_launch<T_, B_, D_, V_>(d, b, s);
   HARTS_KDA_BWD_CONFIGS(X)
 #undef X
-  return hipErrorInvalidValue;
+  return hipErrorNotSupported;
 }
 
 hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {

@@ -338,7 +338,13 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
-          if (BWD || !PF) fm_store<T>(Mg, BT, i, j0, v, 4);
+          // M to the workspace: row-major for the bf16 gradient kernel, fragment-major for the
+          // fp32 serial pass
+          if constexpr (PF) {
+            if constexpr (BWD) store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
+          } else {
+            fm_store<T>(Mg, BT, i, j0, v, 4);
+          }
           if (BWD || PF) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         }
       }
@@ -902,12 +908,14 @@ hipError_t launch_kda_prep(const KdaDims& d, const RoundArgs& a, int mode, hipSt
   return hipErrorInvalidValue;
 }
 
+// fp32 configurations only: bf16 runs the slab passes (kda_slab.hip)
 hipError_t launch_kda_state(const KdaDims& d, const RoundArgs& a, bool backward, hipStream_t s) {
-#define X(T_, B_, D_, V_) \
-  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return state_launch<T_, B_, D_, V_>(d, a, backward, s);
+#define X(T_, B_, D_, V_)                                                             \
+  if constexpr (sizeof(T_) == 4)                                                      \
+    if (d.dtype == 1 && d.BT == B_ && d.D == D_ && d.DV == V_) return state_launch<T_, B_, D_, V_>(d, a, backward, s);
   HARTS_KDA_CONFIGS(X)
 #undef X
-  return hipErrorInvalidValue;
+  return hipErrorNotSupported;
 }
 
 }  // namespace harts
