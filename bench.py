@@ -78,10 +78,10 @@ def hbm_bytes(kernel, l, d=D, bt=B):
     st = d * d * ES         # one bf16 state [d, d]
     return {
         "kda_prep_fwd": 4 * tok + l * ES + 8 * blk + 4 * sq + d * 4,
-        "kda_state_fwd": 5 * blk + d * 4 + tok + 2 * st,
+        "kda_state_fwd": 5 * blk + d * 4 + tok + st,
         "kda_prep_bwd": 4 * tok + l * ES + 6 * blk + 4 * sq + d * 4,
-        "kda_state_bwd": 3 * blk + d * 4 + 2 * st,
-        "kda_dstate": 3 * blk + d * 4 + tok + 2 * st,
+        "kda_state_bwd": 3 * blk + d * 4 + st,
+        "kda_dstate": 3 * blk + d * 4 + tok + st,
         "kda_gradA": 4 * tok + l * ES + 2 * st + 4 * sq + tok + l * ES + 2 * blk + 2 * sq,
         "kda_gradB": 4 * tok + 2 * st + 2 * blk + 2 * sq + 3 * tok,
     }[kernel]

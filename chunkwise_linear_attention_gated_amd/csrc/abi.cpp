@@ -218,7 +218,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.dA = at(d->off_dA, BT * BT, es);
   a.ws.Op = at(d->off_Op, BT * dv, es);
   a.h = at(d->off_h, dv * dk, es);
-  a.hc = at(d->off_hc, dv * dk, es);
+  a.hc = d->dims.dtype == HARTS_DTYPE_FP32 ? at(d->off_hc, dv * dk, es) : nullptr;
   a.ctr = nullptr;
   return a;
 }
@@ -431,8 +431,12 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_Qe = take(MC * dk * BT * es);
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
-      d->off_hc = take(MC * dv * dk * es);
-      d->off_dhc = take(MC * dv * dk * es);
+      // channel-major copies of the chunk-start states and their gradients: fp32 path only
+      // (the bf16 gradient kernel transposes its slices in LDS)
+      if (dtype == HARTS_DTYPE_FP32) {
+        d->off_hc = take(MC * dv * dk * es);
+        d->off_dhc = take(MC * dv * dk * es);
+      }
       d->off_WT = take(MC * dk * BT * es);
       d->off_Kh = take(MC * BT * dk * es);
       d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
@@ -555,7 +559,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       const size_t item0 = size_t(d->p.rounds[r].chunk0) * d->dims.H;
       const size_t sz = size_t(d->dims.D) * d->dims.DV * (d->dims.dtype == HARTS_DTYPE_BF16 ? 2 : 4);
       b.dh = ws + d->off_dh + item0 * sz;
-      b.dhc = ws + d->off_dhc + item0 * sz;
+      b.dhc = d->dims.dtype == HARTS_DTYPE_FP32 ? ws + d->off_dhc + item0 * sz : nullptr;
       b.dinit = d->p.varlen ? g->dinit : reinterpret_cast<float*>(ws + d->off_dinit);
       b.dstates = d->p.varlen ? nullptr : g->dstates;
       b.slot_cons_off = d->p.varlen ? nullptr : d->cons_off;

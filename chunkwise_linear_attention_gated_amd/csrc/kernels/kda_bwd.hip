@@ -796,7 +796,10 @@ struct GBCfg {
                           O_DM = O_DR + SV, O_DA = O_DM + SJ, IN_END = O_DA + SJ;
   // output staging (fp32 [BT][LDF] for dq, dk, dg) over the inputs once they are consumed
   static constexpr size_t SF = al(size_t(BT) * LDF * 4);
-  static constexpr size_t TOTAL = cmx(IN_END, 3 * SF);
+  // bf16: per wave, its 16 channels of S_n (then of dS_n) as [DV][16], read back transposed
+  static constexpr size_t O_HS = cmx(IN_END, 3 * SF), HS = sizeof(T) == 2 ? al(size_t(NW) * DV * 16 * ES) : 0;
+  static constexpr size_t TOTAL = O_HS + HS;
+  static constexpr int NHP = DV / 32;  // 16-byte pieces per lane of one wave's slice
   static_assert(TOTAL <= 160 * 1024, "gradient kernel B LDS budget");
 };
 
@@ -815,7 +818,12 @@ struct GBIn {
   using C = GBCfg<T, BT, D, DV>;
   using F = typename C::MM::Frag;
   f32x4 q[C::NK], k[C::NK], g[C::NK], dO[C::NV], u[C::NV], dr[C::NV], dm[C::NJ], da[C::NJ];
-  F hc[C::NKS], dhc[C::NKS];  // this wave's rows of S_n and dS_n as matrix-core B operands
+  // bf16: this wave's channels of S_n and dS_n, read from their S_n^T fragment-major copies
+  // (16-byte pieces, staged in LDS and read back as matrix-core B operands); fp32: the B
+  // operands from the channel-major copies
+  static constexpr bool BF = sizeof(T) == 2;
+  f32x4 hp[BF ? C::NHP : 1], dp[BF ? C::NHP : 1];
+  F hc[BF ? 1 : C::NKS], dhc[BF ? 1 : C::NKS];
 };
 
 template <typename T, int BT, int D, int DV>
@@ -881,12 +889,26 @@ __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, B
     }
   }
   if constexpr (P < 0 || P == 3) {
-    const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
-    const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
+    if constexpr (sizeof(T) == 2) {
+      // piece x of lane l: value rows 16 (2x + l/32) + l%16, channels 16 wave + 8 ((l/16)%2) + 0..7
+      // of the [DV][D] fragment-major S_n^T (block (v tile, channel block wave/2), lane 32 (wave%2)
+      // + l%32)
+      const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+      const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
-      o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
+      for (int x = 0; x < C::NHP; ++x) {
+        const size_t off = ((size_t(2 * x + (lane >> 5)) * (D / 32) + (wave >> 1)) * 64 + 32 * (wave & 1) + (lane & 31)) * 8;
+        o.hp[x] = ldq(hg + off);
+        o.dp[x] = ldq(dhg + off);
+      }
+    } else {
+      const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
+      const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
+        o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
+      }
     }
   }
 }
@@ -986,34 +1008,58 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
     // 2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
     f32x4 dqa[NB], X1[NB], X23[NB], X4[NB];
     float rs = 0.f;
+    if constexpr (sizeof(T) == 2) {
+      // this wave's channels of S_n, then of dS_n, through its LDS slice [DV][16]; B operands
+      // (channel n = lane % 16, values 32 ks + 8 (lane / 16) + 0..7) by two transposing reads
+      T* hs = reinterpret_cast<T*>(smem + C::O_HS) + wave * (DV * 16);
+      const int cl0 = 8 * ((lane >> 4) & 1), q = lane & 15;
+      auto stage = [&](const f32x4 (&pc)[C::NHP]) {
 #pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      if constexpr (sizeof(T) == 2) {
+        for (int x = 0; x < C::NHP; ++x) stq(hs + (16 * (2 * x + (lane >> 5)) + (lane & 15)) * 16 + cl0, pc[x]);
+      };
+      auto frag = [&](int ks) {
+        const T* src = hs + (32 * ks + 8 * (lane >> 4) + (q >> 2)) * 16 + 4 * (q & 3);
+        const bf16x4 lo = ds_tr16(src), hi = ds_tr16(src + 4 * 16);
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      bf16x8 hf[C::NKS];
+      stage(cur.hp);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) rs += (float)cur.hc[ks][t] * (float)cur.dhc[ks][t];
-      } else {
-        rs += cur.hc[ks] * cur.dhc[ks];
+      for (int ks = 0; ks < C::NKS; ++ks) hf[ks] = frag(ks);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), hf[ks], dqa[bb]);
+          X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), hf[ks], X1[bb]);
+        }
       }
-    }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+      stage(cur.dp);  // in order behind this wave's reads of the S_n slice
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
-        if constexpr (sizeof(T) == 2) {
-          // S_n and dS_n come in the permuted contraction order of the slab passes
-          dqa[bb] = MM::mma(pf_kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
-          X1[bb] = MM::mma(pf_kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
-          X4[bb] = MM::mma(pf_kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
-        } else {
+        const bf16x8 df = frag(ks);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) rs += (float)hf[ks][t] * (float)df[t];
+#pragma unroll
+        for (int bb = 0; bb < NB; ++bb) X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), df, X4[bb]);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) rs += cur.hc[ks] * cur.dhc[ks];
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
           dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
           X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
           X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
         }
       }
     }
+    rs += __shfl_xor(rs, 16, 64);
+    rs += __shfl_xor(rs, 32, 64);
     gb_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),
     //    block totals Tb and block entry values F (F[NB] = G_last)

@@ -234,25 +234,15 @@ struct SlabPass {
     }
   }
 
-  // Chunk-start state (or chunk-end state gradient) as bf16: S^T fragment-major [DV][D] and
-  // S in permuted fragment-major [D][DV] (4 x 4 lane transposes), for the gradient kernels.
-  // state_rows takes the transposed rows while S still holds the state; state_store issues
-  // the stores once the chunk's products are under way, off the serial chain.
-  __device__ __forceinline__ void state_rows(bf16x4 (&hq)[NS][NTS]) const {
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-#pragma unroll
-      for (int t = 0; t < NTS; ++t) hq[s][t] = b4_of(quad_transpose(S[s][t], lane));
-  }
-  __device__ __forceinline__ void state_store(bf16* hT, bf16* hP, const bf16x8 (&Sf)[NS][KBD],
-                                              const bf16x4 (&hq)[NS][NTS]) const {
+  // Chunk-start state (or chunk-end state gradient) as bf16 S^T, fragment-major [DV][D], for
+  // the gradient kernels; issued once the chunk's products are under way, off the serial chain.
+  __device__ __forceinline__ void state_store(bf16* hT, const bf16x8 (&Sf)[NS][KBD]) const {
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int t = 0; t < NTS; ++t) {
         const bf16x4 v = (t & 1) ? hi4(Sf[s][t / 2]) : lo4(Sf[s][t / 2]);
         *reinterpret_cast<bf16x4*>(hT + fm_off<bf16>(jv0[s] + n16, 16 * t + 4 * g4, D)) = v;
-        *reinterpret_cast<bf16x4*>(hP + pf_off(16 * t + 4 * g4 + (lane & 3), jv0[s] + 4 * (n16 >> 2), DV)) = hq[s][t];
       }
   }
 
@@ -284,8 +274,6 @@ struct SlabPass {
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) Sf[s][kb] = pf_pair(S[s][2 * kb], S[s][2 * kb + 1]);
-    bf16x4 hq[SAVE ? NS : 1][SAVE ? NTS : 1];
-    if constexpr (SAVE) state_rows(hq);
     f32x4 U[NS][NTT];
     f32x4 O[FO ? NS : 1][NTT];
     bf16x8 Uf[NS][KBT];
@@ -343,7 +331,7 @@ struct SlabPass {
         });
     if constexpr (SAVE) {
       const size_t w = wsi(c);
-      state_store(static_cast<bf16*>(a.h) + w * DV * D, static_cast<bf16*>(a.hc) + w * D * DV, Sf, hq);
+      state_store(static_cast<bf16*>(a.h) + w * DV * D, Sf);
     }
     if constexpr (FO) {
       // own rows only (replayed rows and padding store into the sink)
@@ -388,8 +376,6 @@ struct SlabPass {
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb) Sf[s][kb] = pf_pair(S[s][2 * kb], S[s][2 * kb + 1]);
-    bf16x4 hq[NS][NTS];
-    state_rows(hq);
     // dO fragments: tokens 32 kb + pf_k(g4, t) at the slab's column n16, by two transposing
     // LDS reads per 32-token block (within each 16-lane group, result element j of lane s is
     // element s % 4 of the 8 bytes that lane 4 j + s / 4 points at); replayed rows carry no
@@ -464,7 +450,7 @@ struct SlabPass {
           }
         });
     const size_t w = wsi(c);
-    state_store(static_cast<bf16*>(b.dh) + w * DV * D, static_cast<bf16*>(b.dhc) + w * D * DV, Sf, hq);
+    state_store(static_cast<bf16*>(b.dh) + w * DV * D, Sf);
   }
 };
 
