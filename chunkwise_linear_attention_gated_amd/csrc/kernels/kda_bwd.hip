@@ -15,6 +15,8 @@
 //   dk = e^L (rowgated(dA, K) - e^{F_b} dR S0^T) + colgated(dM, Q) + colgated(dA, K) + K^-factor (U dS^T)
 //   dG = q dq + k (row-side terms) - k (column-side terms);  dG_last += sum_i k^ (U dS^T) + e^{G_last} rowsum(dS S0)
 //   dg = reverse cumulative sum of dG over the chunk.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 #include "state_common.h"
@@ -279,17 +281,40 @@ constexpr size_t cmx(size_t a, size_t b) { return a > b ? a : b; }
 
 // ------------------------------------------------------------------------------------------
 // C[16x16] += A B over a 16-long contraction: lane l supplies A[l%16][4(l/16) + t] and
-// B[4(l/16) + t][l%16], t = 0..3 (B is then a 16-token block of the accumulator layout).
+// B[4(l/16) + t][l%16], t = 0..3 (B is then a 16-token block of the accumulator layout), as four
+// values of the matrix-core element type, so that staged bf16 tiles feed it without a round
+// trip through fp32.
 template <typename T>
-__device__ __forceinline__ f32x4 mma_k16(const float* av, const float* bv, f32x4 c) {
+using k16_t = typename std::conditional<sizeof(T) == 2, bf16x4, f32x4>::type;
+template <typename T> __device__ __forceinline__ k16_t<T> k16_pack(const float* v) {
+  if constexpr (sizeof(T) == 2) return bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+  else return f32x4{v[0], v[1], v[2], v[3]};
+}
+template <typename T> __device__ __forceinline__ k16_t<T> k16_pack(f32x4 v) {
+  const float a[4] = {v[0], v[1], v[2], v[3]};
+  return k16_pack<T>(a);
+}
+// four consecutive elements p[0..3]
+template <typename T> __device__ __forceinline__ k16_t<T> k16_row(const T* p) {
+  return *reinterpret_cast<const k16_t<T>*>(p);
+}
+// column slice of a row-major LDS tile (as col4_load)
+template <typename T> __device__ __forceinline__ k16_t<T> k16_col(const T* p, int ld, int r0, int c0, int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int q = lane & 15;
+    return ds_tr16(p + (r0 + 4 * (lane >> 4) + (q >> 2)) * ld + c0 + 4 * (q & 3));
+  } else {
+    float v[4];
+    col4_load<T>(p, ld, r0, c0, lane, v);
+    return f32x4{v[0], v[1], v[2], v[3]};
+  }
+}
+template <typename T> __device__ __forceinline__ f32x4 mma_k16r(k16_t<T> a, k16_t<T> b, f32x4 c) {
   if constexpr (sizeof(T) == 2) {
     typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s4;
-    const bf16x4 a4 = {(bf16)av[0], (bf16)av[1], (bf16)av[2], (bf16)av[3]};
-    const bf16x4 b4 = {(bf16)bv[0], (bf16)bv[1], (bf16)bv[2], (bf16)bv[3]};
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a4), __builtin_bit_cast(s4, b4), c, 0, 0,
-                                                     0);
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s4, a), __builtin_bit_cast(s4, b), c, 0, 0, 0);
   } else {
-    return mma16_f32(f32x4{av[0], av[1], av[2], av[3]}, f32x4{bv[0], bv[1], bv[2], bv[3]}, c);
+    return mma16_f32(a, b, c);
   }
 }
 
@@ -598,10 +623,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       for (int br = 0; br < NB; ++br) {
         if (br < bi) continue;
         // dU block bi += sum over rows of block br of M[r][i] dO[r][jv]
-        float am[4], bo[4];
-        col4_load<T>(Ml, LDJ, 16 * br, 16 * bi, lane, am);
-        col4_load<T>(dOs, LDV, 16 * br, 16 * wave, lane, bo);
-        dU[bi] = mma_k16<T>(am, bo, dU[bi]);
+        dU[bi] = mma_k16r<T>(k16_col<T>(Ml, LDJ, 16 * br, 16 * bi, lane), k16_col<T>(dOs, LDV, 16 * br, 16 * wave, lane),
+                             dU[bi]);
       }
     __syncthreads();  // K~, K^ and V consumed
     ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
@@ -609,20 +632,20 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     f32x4 U[NB], dR[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) U[bb] = dR[bb] = z4;
+    k16_t<T> Rk[NB], dUk[NB];  // the right operands, converted once
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      Rk[bb] = k16_pack<T>(R[bb]);
+      dUk[bb] = k16_pack<T>(dU[bb]);
+    }
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
-        float ta[4], tb[4], rb[4], ub[4];
-        col4_load<T>(Tl, LDJ, 16 * bi, 16 * bj, lane, tb);  // T[i][j] as (j, i)
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          ta[t] = to_f(Tl[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);  // T[i][j], i in bi, j in bj
-          rb[t] = R[bj][t];
-          ub[t] = dU[bi][t];
-        }
-        U[bi] = mma_k16<T>(ta, rb, U[bi]);
-        dR[bj] = mma_k16<T>(tb, ub, dR[bj]);
+        const k16_t<T> ta = k16_row<T>(Tl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);  // T[i][j], i in bi, j in bj
+        const k16_t<T> tb = k16_col<T>(Tl, LDJ, 16 * bi, 16 * bj, lane);               // T[i][j] as (j, i)
+        U[bi] = mma_k16r<T>(ta, Rk[bj], U[bi]);
+        dR[bj] = mma_k16r<T>(tb, dUk[bi], dR[bj]);
       }
     // scalar stores: the LDS pipe takes them, where a lane transpose would cost vector ALU time
 #pragma unroll
@@ -1116,20 +1139,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       for (int bj = 0; bj <= bi; ++bj) {
         // row side: output block bi, contraction over block bj
         const float epf = bi == bj ? 1.f : __expf(F[bi] - F[bj]);  // <= 1
-        float am[4], aa[4], bk[4];
+        float bk[4];
         col4_load<T>(Ks, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          am[t] = to_f(dMs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
-          aa[t] = to_f(dAs[(16 * bi + cc) * LDJ + 16 * bj + 4 * g4 + t]);
-          bk[t] *= epf * enL[bj][t];
-        }
-        dqa[bi] = mma_k16<T>(am, bk, dqa[bi]);
-        X1[bi] = mma_k16<T>(aa, bk, X1[bi]);
+        for (int t = 0; t < 4; ++t) bk[t] *= epf * enL[bj][t];
+        const k16_t<T> bkk = k16_pack<T>(bk);
+        dqa[bi] = mma_k16r<T>(k16_row<T>(dMs + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, dqa[bi]);
+        X1[bi] = mma_k16r<T>(k16_row<T>(dAs + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, X1[bi]);
         // col side: output block bj, contraction over block bi
-        float cm[4], ca[4], bq[4], bk2[4];
-        col4_load<T>(dMs, LDJ, 16 * bi, 16 * bj, lane, cm);
-        col4_load<T>(dAs, LDJ, 16 * bi, 16 * bj, lane, ca);
+        float bq[4], bk2[4];
         col4_load<T>(Qs, LDK, 16 * bi, 16 * wave, lane, bq);
         col4_load<T>(Ks, LDK, 16 * bi, 16 * wave, lane, bk2);
 #pragma unroll
@@ -1138,8 +1156,8 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
           bq[t] *= e;
           bk2[t] *= e;
         }
-        X23[bj] = mma_k16<T>(cm, bq, X23[bj]);
-        X23[bj] = mma_k16<T>(ca, bk2, X23[bj]);
+        X23[bj] = mma_k16r<T>(k16_col<T>(dMs, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bq), X23[bj]);
+        X23[bj] = mma_k16r<T>(k16_col<T>(dAs, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bk2), X23[bj]);
       }
     gb_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // 5. assemble dq, dk, dG with exact q, k and fp32 factors
