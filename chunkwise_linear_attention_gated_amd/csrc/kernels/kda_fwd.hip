@@ -454,9 +454,37 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
         for (int s = 0; s < 4; ++s)
           Tm[(16 * i + 4 * lg + s) * LDJ + 16 * j + lr] = from_f<T>(i < j ? 0.f : xb[i][s] * bc);
+    } else {
+      // the other waves export what does not depend on T: K^^T (bf16) and A (backward)
+      constexpr int HN = CNT - 64 * NB;
+      const int ht = tid - 64 * NB;
+      if constexpr (PF) {
+        // K^^T [D][BT] permuted fragment-major from the token-major K^: block (channel block cb,
+        // token block kb), lane l: channel 16 cb + l % 16, tokens 32 kb + 4 (l / 16) + {0..3} and
+        // the same + 16, by two transposing reads (lane q of a 16-lane group points at 4
+        // consecutive channels of token 4 (q / 4) + ...)
+        T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
+        HARTS_STRIDED(pc, ht, D * BT / 8, HN) {
+          const int blk = pc / 64, l = pc % 64, q = l & 15;
+          const int cb = blk / (BT / 32), kb = blk % (BT / 32);
+          const T* src = KhT + (32 * kb + 4 * (l >> 4) + (q >> 2)) * LDK + 16 * cb + 4 * (q & 3);
+          const bf16x4 lo = ds_tr16(src), hi = ds_tr16(src + 16 * LDK);
+          *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+      }
+      if constexpr (BWD) {
+        T* ag = static_cast<T*>(a.ws.Am) + wsi * size_t(BT) * BT;
+        HARTS_STRIDED(idx, ht, BT * (BT / VN), HN) {
+          const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
+          float av[VN];
+#pragma unroll
+          for (int t = 0; t < VN; ++t) av[t] = j0 + t < i ? Af[i * LDA + j0 + t] : 0.f;
+          stq(ag + i * BT + j0, pack16<T>(av));
+        }
+      }
     }
     __syncthreads();
-    // 8. U' = T V (accumulator tiles), W = T K~, KhT out; backward: T, X, A out.
+    // 8. U' = T V (accumulator tiles), W = T K~; backward: T, X out.
     //    PF: W (and W^T) are stored negated; W stays in registers for Qeff = Q~ - M W.
     {
       T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
@@ -525,20 +553,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           fm_store<T>(wg, D, i, c0, wv, 4);
         }
       }
-      T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
-      if constexpr (PF) {
-        // K^^T [D][BT] permuted fragment-major from the token-major K^: block (channel block cb,
-        // token block kb), lane l: channel 16 cb + l % 16, tokens 32 kb + 4 (l / 16) + {0..3} and
-        // the same + 16, by two transposing reads (lane q of a 16-lane group points at 4
-        // consecutive channels of token 4 (q / 4) + ...)
-        HARTS_STRIDED(pc, tid, D * BT / 8, CNT) {
-          const int blk = pc / 64, l = pc % 64, q = l & 15;
-          const int cb = blk / (BT / 32), kb = blk % (BT / 32);
-          const T* src = KhT + (32 * kb + 4 * (l >> 4) + (q >> 2)) * LDK + 16 * cb + 4 * (q & 3);
-          const bf16x4 lo = ds_tr16(src), hi = ds_tr16(src + 16 * LDK);
-          *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        }
-      } else {
+      if constexpr (!PF) {  // (bf16: exported during step 7)
+        T* khg = static_cast<T*>(a.ws.KhT) + wsi * D * BT;
         HARTS_STRIDED(idx, tid, D * (BT / VN), CNT) {
           const int c = idx / (BT / VN), i0 = (idx % (BT / VN)) * VN;
           float kv[VN];
@@ -550,18 +566,13 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         const size_t BB = size_t(BT) * BT;
         T* tg = static_cast<T*>(a.ws.Tm) + wsi * BB;
         T* xg = static_cast<T*>(a.ws.Xm) + wsi * BB;
-        T* ag = static_cast<T*>(a.ws.Am) + wsi * BB;
         HARTS_STRIDED(idx, tid, BT * (BT / VN), CNT) {
           const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
           copy16(tg + i * BT + j0, Tm + i * LDJ + j0);
-          float xv[VN], av[VN];
+          float xv[VN];
 #pragma unroll
-          for (int t = 0; t < VN; ++t) {
-            xv[t] = j0 + t <= i ? Xf[i * LDA + j0 + t] : 0.f;
-            av[t] = j0 + t < i ? Af[i * LDA + j0 + t] : 0.f;
-          }
+          for (int t = 0; t < VN; ++t) xv[t] = j0 + t <= i ? Xf[i * LDA + j0 + t] : 0.f;
           stq(xg + i * BT + j0, pack16<T>(xv));
-          stq(ag + i * BT + j0, pack16<T>(av));
         }
       }
       if constexpr (KEEPW) {
