@@ -564,13 +564,14 @@ static hipError_t slab_go(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s
 }
 
 // One compute wave (one slab) per workgroup while the round's slabs fit the chip one
-// workgroup per compute unit (latency-bound long chains); otherwise four compute waves of
-// one slab each sharing one ring, which cuts the shared-operand traffic per slab fourfold.
+// workgroup per compute unit (latency-bound long chains); otherwise two compute waves of two
+// slabs each sharing one ring: every wave has a SIMD (and its registers) to itself, and the
+// shared operands are read from LDS once per two slabs.
 template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
   if (slabs <= persistent_grid(1u << 30)) return slab_go<MODE, BT, D, DV, 1, 1, 3>(d, b, s);
-  return slab_go<MODE, BT, D, DV, 4, 1, 2>(d, b, s);
+  return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
 }
 
 template <int BT, int D, int DV>
