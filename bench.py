@@ -64,8 +64,7 @@ def macs(kernel, l, d=D):
         "kda_prep_bwd": 4 * l2d + l3 / 6,
         "kda_state_bwd": 2 * ld2,
         "kda_dstate": 3 * ld2,
-        "kda_gradA": 5 * l2d + 2 * ld2 + 2 * l3,
-        "kda_gradB": 4 * l2d + 3 * ld2,
+        "kda_grad": 9 * l2d + 5 * ld2 + 2 * l3,
     }[kernel]
 
 
@@ -82,8 +81,8 @@ def hbm_bytes(kernel, l, d=D, bt=B):
         "kda_prep_bwd": 4 * tok + l * ES + 6 * blk + 4 * sq + d * 4,
         "kda_state_bwd": 3 * blk + d * 4 + st,
         "kda_dstate": 3 * blk + d * 4 + tok + st,
-        "kda_gradA": 4 * tok + l * ES + 2 * st + 4 * sq + tok + l * ES + 2 * blk + 2 * sq,
-        "kda_gradB": 4 * tok + 2 * st + 2 * blk + 2 * sq + 3 * tok,
+        # q, k, v, g, dO, beta, S, dS, T, M, X, A in; dq, dk, dv, dg, dbeta out
+        "kda_grad": 5 * tok + l * ES + 2 * st + 4 * sq + 4 * tok + l * ES,
     }[kernel]
 
 

@@ -38,7 +38,7 @@ struct harts_dev_plan {
   std::vector<int32_t> rslot_off;      // [n_rounds + 1] offsets into rslots
   // workspace layout (byte offsets)
   size_t off_W = 0, off_Op = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
-         off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_U = 0, off_dR = 0, off_dM = 0, off_dA = 0, off_dslot = 0;
+         off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_dslot = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
   size_t off_ctr = 0;
 };
@@ -212,10 +212,6 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.Tm = at(d->off_Tm, BT * BT, es);
   a.ws.Xm = at(d->off_Xm, BT * BT, es);
   a.ws.Am = at(d->off_Am, BT * BT, es);
-  a.ws.U = at(d->off_U, BT * dv, es);
-  a.ws.dR = at(d->off_dR, BT * dv, es);
-  a.ws.dM = at(d->off_dM, BT * BT, es);
-  a.ws.dA = at(d->off_dA, BT * BT, es);
   a.ws.Op = at(d->off_Op, BT * dv, es);
   a.h = at(d->off_h, dv * dk, es);
   a.hc = d->dims.dtype == HARTS_DTYPE_FP32 ? at(d->off_hc, dv * dk, es) : nullptr;
@@ -421,8 +417,8 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_El = take(MC * dk * 4);
       d->off_sink = take(kSinkBytes);
       // item counters of the persistent per-chunk kernels: per round, forward preparation,
-      // backward preparation, gradient kernels A and B; zeroed at the start of every call
-      d->off_ctr = take(size_t(4) * d->p.rounds.size() * sizeof(int32_t));
+      // backward preparation and the gradient kernel; zeroed at the start of every call
+      d->off_ctr = take(size_t(3) * d->p.rounds.size() * sizeof(int32_t));
       d->off_Qt = take(MC * BT * dk * es);
       d->off_Op = take(MC * BT * dv * es);
       d->ws_fwd = off;
@@ -444,10 +440,6 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->off_Tm = take(MC * BT * BT * es);
       d->off_Xm = take(MC * BT * BT * es);
       d->off_Am = take(MC * BT * BT * es);
-      d->off_U = take(MC * BT * dv * es);
-      d->off_dR = take(MC * BT * dv * es);
-      d->off_dM = take(MC * BT * BT * es);
-      d->off_dA = take(MC * BT * BT * es);
       d->off_dslot = take(size_t(d->p.n_slots) * H * dk * dv * 4);
       d->ws_bwd = off;
       if (d->ws_fwd == 0) d->ws_fwd = 256;
@@ -489,7 +481,7 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     // every chunk-start state, so that the backward neither prepares nor recomputes
     const bool keep = io->keep && slab;
     int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
-    hip_check(harts::launch_zero_i32(ctr, 4 * int64_t(d->p.n_rounds), s0), "counter reset");
+    hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(d->p.n_rounds), s0), "counter reset");
     fork(s0, s1, ev);
     // Round r + 1's preparation is enqueued behind the start of round r's serial pass, so that
     // the serial pass takes its compute units first; the preparation's workgroups draw items
@@ -500,7 +492,7 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
       if (started) hip_check(hipStreamWaitEvent(s1, started, 0), "hipStreamWaitEvent");
       {
         harts::RoundArgs a = round_args(d, io, r, ws);
-        a.ctr = ctr + 4 * r;
+        a.ctr = ctr + 3 * r;
         ProfScope ps("kda_prep_fwd", s1, units);
         hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, s1), "prep kernel launch");
       }
@@ -543,7 +535,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     Events ev;
     hipStream_t s1 = aux_stream(0), s2 = aux_stream(1);
     int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
-    hip_check(harts::launch_zero_i32(ctr, 4 * int64_t(R), s0), "counter reset");
+    hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(R), s0), "counter reset");
     fork(s0, s1, ev);
     fork(s0, s2, ev);
     auto round = [&](int r) {
@@ -575,7 +567,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       {
         ProfScope ps("kda_prep_bwd", s1, units(r));
         harts::RoundArgs a = b.r;
-        a.ctr = ctr + 4 * r + 1;
+        a.ctr = ctr + 3 * r + 1;
         hip_check(harts::launch_kda_prep(d->dims, a, 1, s1), "prep kernel launch");
       }
       prepped[size_t(r)] = ev.record(s1);
@@ -593,14 +585,9 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       harts::BwdRoundArgs b = round(r);
       if (!keep) hip_check(hipStreamWaitEvent(s2, recomputed[size_t(r)], 0), "hipStreamWaitEvent");
       {
-        ProfScope ps("kda_gradA", s2, units(r));
-        b.r.ctr = ctr + 4 * r + 2;
-        hip_check(harts::launch_kda_grad(d->dims, b, 0, s2), "gradient kernel launch");
-      }
-      {
-        ProfScope ps("kda_gradB", s2, units(r));
-        b.r.ctr = ctr + 4 * r + 3;
-        hip_check(harts::launch_kda_grad(d->dims, b, 1, s2), "gradient kernel launch");
+        ProfScope ps("kda_grad", s2, units(r));
+        b.r.ctr = ctr + 3 * r + 2;
+        hip_check(harts::launch_kda_grad(d->dims, b, s2), "gradient kernel launch");
       }
     };
     for (int r = R - 1; r >= 0; --r) {

@@ -318,14 +318,14 @@ template <typename T> __device__ __forceinline__ f32x4 mma_k16r(k16_t<T> a, k16_
   }
 }
 
-// Gradient kernel A (token side): dv, dbeta, and U, dR, dM, dA for kernel B.  Persistent,
-// one workgroup of DV/16 waves per compute unit walking the (chunk, head) items of the
-// round.  Wave w owns value columns [16w, 16w + 16): R = V - K~ S0, dU = M^T dO + K^ dS,
-// U = T R and dR = T^T dU are chained in the accumulator layout (lane l holds tokens
-// 16b + 4(l/16) + r of column 16w + l%16), the 16-token block products taking the lane's
-// own values as their right operand.  The token-token tail (dM, dT, dX, dL, dA, dbeta)
-// runs on tiles staged in LDS.  The next item's inputs (and this wave's slices of S_n^T
-// and dS_n^T) are fetched into registers while the current item computes.
+// Per-chunk gradients: one persistent kernel, one workgroup per compute unit walking the
+// (chunk, head) items of the round, each item in two halves.
+//
+// Token side (configuration GACfg): dv, dbeta, and U, dR, dM, dA for the channel side.  Wave
+// w owns value columns [16w, 16w + 16): R = V - K~ S0, dU = M^T dO + K^ dS, U = T R and
+// dR = T^T dU are chained in the accumulator layout (lane l holds tokens 16b + 4(l/16) + r of
+// column 16w + l%16), the 16-token block products taking the lane's own values as their
+// right operand.  The token-token tail (dM, dT, dX, dL, dA, dbeta) runs on tiles staged in LDS.
 template <typename T, int BT, int D, int DV>
 struct GACfg {
   using MM = Mma<T>;
@@ -351,7 +351,7 @@ struct GACfg {
   static constexpr size_t V_BET = 0, V_TB = BT, V_DB1 = V_TB + NB * D, V_DB2 = V_DB1 + NPART * BT,
                           V_END = V_DB2 + NB * BT;
   static constexpr size_t TOTAL = O_VEC + V_END * 4;
-  static_assert(TOTAL <= 160 * 1024, "gradient kernel A LDS budget");
+  static_assert(TOTAL <= 160 * 1024, "token side LDS budget");
   static_assert(NB * D <= NT, "one (block, channel) decay item per thread");
   static_assert(NPART >= 1 && BT % NPART == 0, "dbeta_1 row groups");
 };
@@ -449,48 +449,177 @@ __device__ __forceinline__ void ga_load(GAIn<T, BT, D, DV>& o, const GARows<T, B
   }
 }
 
+// ------------------------------------------------------------------------------------------
+// Channel side (configuration GBCfg): dq, dk, dg.  Wave w owns channels [16w, 16w + 16) for
+// every token of the chunk, with lane l holding, for each 16-token block b, tokens
+// 16b + 4(l/16) + r (r = 0..3) of channel 16w + l%16 -- the accumulator layout of the matrix
+// cores.  The in-chunk decay, the 16-token block products (whose right operand is the lane's
+// own values), the state products and the final reverse cumulative sum of dg all stay inside
+// the wave.
 template <typename T, int BT, int D, int DV>
-__global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs b, int H) {
-  using C = GACfg<T, BT, D, DV>;
+struct GBCfg {
+  using MM = Mma<T>;
+  static constexpr int NW = D / 16, NT = 64 * NW, NB = BT / 16, VN = 16 / sizeof(T), PAD = VN;
+  static constexpr int NPR = D / VN, NPK = BT * NPR, NK = (NPK + NT - 1) / NT;
+  static constexpr int NPRV = DV / VN, NPV = BT * NPRV, NV = (NPV + NT - 1) / NT;
+  static constexpr int NPJ = BT * BT / VN, NJ = (NPJ + NT - 1) / NT;
+  static constexpr int NKS = DV / MM::KS;
+  static constexpr bool SAMEV = NPR == NPRV;
+  static constexpr int LDK = D + PAD, LDV = DV + PAD, LDJ = BT + PAD, LDF = D + 4;
+  static constexpr size_t ES = sizeof(T);
+  static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
+  // staged inputs (bf16/fp32): Q, K, g [BT][LDK]; dO, U, dR [BT][LDV]; dM, dA [BT][LDJ]
+  static constexpr size_t SK = al(size_t(BT) * LDK * ES), SV = al(size_t(BT) * LDV * ES), SJ = al(size_t(BT) * LDJ * ES);
+  static constexpr size_t O_Q = 0, O_K = SK, O_G = 2 * SK, O_DO = 3 * SK, O_U = O_DO + SV, O_DR = O_U + SV,
+                          O_DM = O_DR + SV, O_DA = O_DM + SJ, IN_END = O_DA + SJ;
+  // output staging (fp32 [BT][LDF] for dq, dk, dg) over the inputs once they are consumed
+  static constexpr size_t SF = al(size_t(BT) * LDF * 4);
+  // bf16: per wave, its 16 channels of S_n (then of dS_n) as [DV][16], read back transposed
+  static constexpr size_t O_HS = cmx(IN_END, 3 * SF), HS = sizeof(T) == 2 ? al(size_t(NW) * DV * 16 * ES) : 0;
+  static constexpr size_t TOTAL = O_HS + HS;
+  static constexpr int NHP = DV / 32;  // 16-byte pieces per lane of one wave's slice
+  static_assert(TOTAL <= 160 * 1024, "channel side LDS budget");
+};
+
+template <typename T, int BT, int D, int DV>
+struct GBIn {
+  using C = GBCfg<T, BT, D, DV>;
+  using F = typename C::MM::Frag;
+  f32x4 q[C::NK], k[C::NK], g[C::NK];
+  // bf16: this wave's channels of S_n and dS_n, read from their S_n^T fragment-major copies
+  // (16-byte pieces, staged in LDS and read back as matrix-core B operands); fp32: the B
+  // operands from the channel-major copies
+  static constexpr bool BF = sizeof(T) == 2;
+  f32x4 hp[BF ? C::NHP : 1], dp[BF ? C::NHP : 1];
+  F hc[BF ? 1 : C::NKS], dhc[BF ? 1 : C::NKS];
+};
+
+// Unconditional loads from clamped addresses: padding is masked where the values are used.
+// P selects a part of the fetch: 0 q, k, g; 1 the state slices.
+template <typename T, int BT, int D, int DV, int P>
+__device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GARows<T, BT, D, DV>& r, const BwdRoundArgs& b,
+                                        size_t wsi, int h, int H, int tid, int wave, int lane) {
+  using C = GBCfg<T, BT, D, DV>;
   using MM = typename C::MM;
+  const RoundArgs& a = b.r;
+  if constexpr (P == 0) {
+#pragma unroll
+    for (int x = 0; x < C::NK; ++x) {
+      const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
+      const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
+      o.q[x] = ldq(static_cast<const T*>(a.q) + off);
+      o.k[x] = ldq(static_cast<const T*>(a.k) + off);
+      o.g[x] = ldq(static_cast<const T*>(a.g) + off);
+    }
+  }
+  if constexpr (P == 1) {
+    if constexpr (sizeof(T) == 2) {
+      // piece x of lane l: value rows 16 (2x + l/32) + l%16, channels 16 wave + 8 ((l/16)%2) + 0..7
+      // of the [DV][D] fragment-major S_n^T (block (v tile, channel block wave/2), lane 32 (wave%2)
+      // + l%32)
+      const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
+      const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
+#pragma unroll
+      for (int x = 0; x < C::NHP; ++x) {
+        const size_t off = ((size_t(2 * x + (lane >> 5)) * (D / 32) + (wave >> 1)) * 64 + 32 * (wave & 1) + (lane & 31)) * 8;
+        o.hp[x] = ldq(hg + off);
+        o.dp[x] = ldq(dhg + off);
+      }
+    } else {
+      const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
+      const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
+        o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// The gradient kernel: a workgroup takes each (chunk, head) item through the token side and
+// then the channel side.  U, dR, dM and dA stay in LDS between the halves and dO is staged
+// once for both, so the intermediates never reach HBM and the shared inputs are read once.  The channel side's own
+// inputs (q, k, g and its state slices) are fetched while the token side computes, the next
+// item's token-side inputs while the channel side computes.
+template <typename T, int BT, int D, int DV>
+struct GFCfg {
+  using A = GACfg<T, BT, D, DV>;
+  using B = GBCfg<T, BT, D, DV>;
+  static_assert(D == DV, "one thread layout serves both halves");
+  static_assert(DV >= BT, "token-token tiles fit in the token-channel regions");
+  static constexpr size_t SKV = A::SKV, SJ = A::SJ;
+  // dO | k -> K^ -> U | dR | dM | T (-> dT over T and M -> dA) | M | X | A |
+  // R0: g -> K~ -> R -> Y1^T | R2: v -> dU -> dX | token-side vectors
+  static constexpr size_t O_DO = 0, O_U = SKV, O_DR = 2 * SKV, O_DM = 3 * SKV, O_T = O_DM + SJ, O_M = O_T + SJ,
+                          O_X = O_M + SJ, O_A = O_X + SJ, O_R0 = O_A + SJ, O_R2 = O_R0 + SKV, O_VEC = O_R2 + SKV;
+  static constexpr size_t A_END = O_VEC + A::V_END * 4;
+  // channel side: per-wave state slices over R0 and R2, then q, k, g from M on; the fp32
+  // output staging over everything once the inputs are consumed
+  static constexpr size_t O_HS = O_R0, O_Q = O_M, O_K = O_M + B::SK, O_G = O_M + 2 * B::SK;
+  static constexpr size_t TOTAL = cmx(A_END, 3 * B::SF);
+  static_assert(2 * SJ >= size_t(BT) * A::LDA * 4, "dT fits over T and M");
+  static_assert(O_HS + B::HS <= O_VEC, "state slices clear of the token-side vectors");
+  static_assert(O_G + B::SK <= TOTAL, "q, k, g");
+  static_assert(B::SV <= SKV && B::SJ == SJ && A::LDV == B::LDV && A::LDJ == B::LDJ && A::LDK == B::LDK &&
+                    A::NK == B::NK && A::NV == B::NV && A::NT == B::NT,
+                "shared tiles and thread mapping");
+  static_assert(TOTAL <= 160 * 1024, "fused gradient kernel LDS budget");
+};
+
+template <typename T, int BT, int D, int DV>
+__global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b, int H) {
+  using C = GFCfg<T, BT, D, DV>;
+  using CA = GACfg<T, BT, D, DV>;
+  using CB = GBCfg<T, BT, D, DV>;
+  using MM = typename CA::MM;
   using G = RG<D, DV>;
   using In = GAIn<T, BT, D, DV>;
+  using InB = GBIn<T, BT, D, DV>;
   using Rows = GARows<T, BT, D, DV>;
-  constexpr int NT = C::NT, NW = C::NW, NB = C::NB, VN = C::VN, NK = C::NK, NV = C::NV, NJ = C::NJ;
-  constexpr int LDK = C::LDK, LDV = C::LDV, LDJ = C::LDJ, LDA = C::LDA, NPR = C::NPR, NPRV = C::NPRV;
+  constexpr int NT = CA::NT, NW = CA::NW, NB = CA::NB, VN = CA::VN, NK = CA::NK, NV = CA::NV, NJ = CA::NJ;
+  constexpr int LDK = CA::LDK, LDV = CA::LDV, LDJ = CA::LDJ, LDA = CA::LDA, LDF = CB::LDF, NPR = CA::NPR,
+                NPRV = CA::NPRV;
   __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  T* Gs = reinterpret_cast<T*>(smem + C::O_R0);   // g, then K~ in place
-  T* Kt = Gs;
-  T* Rs = Gs;                                      // R after the chained products
-  T* Y1t = Gs;                                     // Y1^T at the end
-  T* Ks = reinterpret_cast<T*>(smem + C::O_R1);   // k, then K^ in place
+  T* dOs = reinterpret_cast<T*>(smem + C::O_DO);
+  T* Ks = reinterpret_cast<T*>(smem + C::O_U);  // k, then K^ in place, then U
   T* Kh = Ks;
   T* Us = Ks;
-  T* dXs = Ks;
-  T* Vs = reinterpret_cast<T*>(smem + C::O_R2);
-  T* dUs = Vs;
-  T* dOs = reinterpret_cast<T*>(smem + C::O_R3);
-  T* dRs = reinterpret_cast<T*>(smem + C::O_R4);
+  T* dRs = reinterpret_cast<T*>(smem + C::O_DR);
+  T* dMl = reinterpret_cast<T*>(smem + C::O_DM);
   T* Tl = reinterpret_cast<T*>(smem + C::O_T);
-  T* Ml = reinterpret_cast<T*>(smem + C::O_M);
   float* dTf = reinterpret_cast<float*>(smem + C::O_T);
+  T* dAl = Tl;
+  T* Ml = reinterpret_cast<T*>(smem + C::O_M);
   T* Xl = reinterpret_cast<T*>(smem + C::O_X);
   T* Al = reinterpret_cast<T*>(smem + C::O_A);
+  T* Gs = reinterpret_cast<T*>(smem + C::O_R0);  // g, then K~ in place, then R, then Y1^T
+  T* Kt = Gs;
+  T* Rs = Gs;
+  T* Y1t = Gs;
+  T* Vs = reinterpret_cast<T*>(smem + C::O_R2);  // v, then dU, then dX
+  T* dUs = Vs;
+  T* dXs = Vs;
   float* vec = reinterpret_cast<float*>(smem + C::O_VEC);
-  float* bet = vec + C::V_BET;
-  float* Tbv = vec + C::V_TB;
-  float* db1 = vec + C::V_DB1;
-  float* db2 = vec + C::V_DB2;
+  float* bet = vec + CA::V_BET;
+  float* Tbv = vec + CA::V_TB;
+  float* db1 = vec + CA::V_DB1;
+  float* db2 = vec + CA::V_DB2;
+  T* Qb = reinterpret_cast<T*>(smem + C::O_Q);
+  T* Kb = reinterpret_cast<T*>(smem + C::O_K);
+  T* Gb = reinterpret_cast<T*>(smem + C::O_G);
+  float* stg = reinterpret_cast<float*>(smem);  // [3][BT][LDF] at the end of the channel side
   const RoundArgs& a = b.r;
 
   const int nitems = a.nchunk * H;
   int item = blockIdx.x;
   if (item >= nitems) return;
   const int tid0 = threadIdx.x;
-  // rows_x: rows of the item whose inputs are in nxt; rows_n: rows of the item after it.
-  // cur is taken from nxt at the top of each iteration, before the next fetch is issued.
+  // rows_x: rows of the item whose token-side inputs are in nxt; rows_n: rows of the item after it
   Rows rows, rows_x, rows_n;
   In cur, nxt;
+  InB cb;  // channel-side inputs of the current item
   ga_rows<T, BT, D, DV>(rows_x, a, item / H, tid0);
   ga_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
   int item_n = item + gridDim.x;
@@ -509,19 +638,20 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     cur = nxt;
     rows = rows_x;
     const int itn = item_n < nitems ? item_n : item;
-    ga_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
     rows_x = rows_n;
+    gb_load<T, BT, D, DV, 0>(cb, rows, b, wsi, h, H, tid, wave, lane);  // q, k, g of this item
     if (a.ctr && tid == 0) {
       tk_slot = tk;
       tk = draw_ticket(a.ctr);
     }
 
-    // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
+    // ---------------- token side ----------------
+    // A1. stage the inputs (padding rows zero; dO zero on replayed rows)
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
       const int p = tid + NT * x;
-      if (p < C::NPK) {
+      if (p < CA::NPK) {
         const int i = p / NPR, c0 = (p % NPR) * VN;
         const bool ok = rows.rk[x] >= 0;
         stq(Gs + i * LDK + c0, ok ? cur.g[x] : z4);
@@ -531,7 +661,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
 #pragma unroll
     for (int x = 0; x < NV; ++x) {
       const int p = tid + NT * x;
-      if (p < C::NPV) {
+      if (p < CA::NPV) {
         const int i = p / NPRV, c0 = (p % NPRV) * VN;
         const bool ok = rows.rv(x) >= 0;
         stq(Vs + i * LDV + c0, ok ? cur.v[x] : z4);
@@ -541,7 +671,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
 #pragma unroll
     for (int x = 0; x < NJ; ++x) {
       const int p = tid + NT * x;
-      if (p < C::NPJ) {
+      if (p < CA::NPJ) {
         const int i = p / (BT / VN), j0 = (p % (BT / VN)) * VN;
         stq(Tl + i * LDJ + j0, cur.tm[x]);
         stq(Xl + i * LDJ + j0, cur.xm[x]);
@@ -567,7 +697,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     // the item after the next one: its rows are fetched a whole item ahead of their use
     const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
     ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
-    // 2. decay per (16-row block, channel): block-local cumulative L, block totals
+    // A2. decay per (16-row block, channel): block-local cumulative L, block totals
     float Lr[16];
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
@@ -580,8 +710,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       Tbv[bb * D + c] = s;
     }
     __syncthreads();
-    ga_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k (each thread its own entries)
+    // A3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
       float fb = 0.f, fe = 0.f;
@@ -600,14 +729,14 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       }
     }
     __syncthreads();
-    // 4. R = V - K~ S0 and dU = K^ dS + M^T dO for this wave's value columns
+    // A4. R = V - K~ S0 and dU = K^ dS + M^T dO for this wave's value columns
     const int jv = 16 * wave + cc;
     f32x4 R[NB], dU[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       f32x4 r1 = z4, r2 = z4;
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
+      for (int ks = 0; ks < CA::NKS; ++ks) {
         r1 = MM::mma(MM::kc(Kt, LDK, 16 * bb, ks * MM::KS, lane), cur.hf[ks], r1);
         r2 = MM::mma(MM::kc(Kh, LDK, 16 * bb, ks * MM::KS, lane), cur.dhf[ks], r2);
       }
@@ -622,17 +751,16 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
 #pragma unroll
       for (int br = 0; br < NB; ++br) {
         if (br < bi) continue;
-        // dU block bi += sum over rows of block br of M[r][i] dO[r][jv]
         dU[bi] = mma_k16r<T>(k16_col<T>(Ml, LDJ, 16 * br, 16 * bi, lane), k16_col<T>(dOs, LDV, 16 * br, 16 * wave, lane),
                              dU[bi]);
       }
     __syncthreads();  // K~, K^ and V consumed
-    ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 5. U = T R, dR = T^T dU (16-token blocks, right operand in registers); stage R, U, dU, dR
+    gb_load<T, BT, D, DV, 1>(cb, rows, b, wsi, h, H, tid, wave, lane);  // the channel side's state slices
+    // A5. U = T R, dR = T^T dU; stage R, U, dU, dR
     f32x4 U[NB], dR[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) U[bb] = dR[bb] = z4;
-    k16_t<T> Rk[NB], dUk[NB];  // the right operands, converted once
+    k16_t<T> Rk[NB], dUk[NB];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       Rk[bb] = k16_pack<T>(R[bb]);
@@ -642,12 +770,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
-        const k16_t<T> ta = k16_row<T>(Tl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);  // T[i][j], i in bi, j in bj
-        const k16_t<T> tb = k16_col<T>(Tl, LDJ, 16 * bi, 16 * bj, lane);               // T[i][j] as (j, i)
+        const k16_t<T> ta = k16_row<T>(Tl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);
+        const k16_t<T> tb = k16_col<T>(Tl, LDJ, 16 * bi, 16 * bj, lane);
         U[bi] = mma_k16r<T>(ta, Rk[bj], U[bi]);
         dR[bj] = mma_k16r<T>(tb, dUk[bi], dR[bj]);
       }
-    // scalar stores: the LDS pipe takes them, where a lane transpose would cost vector ALU time
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
@@ -659,11 +786,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
         dRs[i * LDV + jv] = from_f<T>(dR[bb][r]);
       }
     __syncthreads();
-    // 6. dM = lower(dO U^T) (computed transposed) to the workspace; dT = dU R^T (fp32) over T, M;
-    //    U and dR to the workspace; dv of own rows to the output, of replayed rows to the side buffer
+    // A6. dM = lower(dO U^T) (computed transposed) into LDS; dT = dU R^T (fp32) over T, M;
+    //     dv of own rows to the output, of replayed rows to the side buffer
     {
       constexpr int NTRI = NB * (NB + 1) / 2;
-      T* dmg = static_cast<T*>(a.ws.dM) + wsi * BT * BT;
       HARTS_STRIDED(jb, wave, 2 * NTRI, NW) {
         const int t = jb < NTRI ? jb : jb - NTRI;
         int bi = 0;
@@ -678,7 +804,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
           float v[4];
 #pragma unroll
           for (int r = 0; r < 4; ++r) v[r] = j0 + r <= i ? acc[r] : 0.f;
-          store4(dmg + i * BT + j0, v[0], v[1], v[2], v[3]);
+          store4(dMl + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         } else {
 #pragma unroll
           for (int k0 = 0; k0 < DV; k0 += MM::KS)
@@ -687,34 +813,27 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
           for (int r = 0; r < 4; ++r) dTf[(16 * bi + 4 * g4 + r) * LDA + 16 * bj + cc] = acc[r];
         }
       }
-      T* ug = static_cast<T*>(a.ws.U) + wsi * BT * DV;
-      T* drg = static_cast<T*>(a.ws.dR) + wsi * BT * DV;
 #pragma unroll
       for (int x = 0; x < NV; ++x) {
         const int p = tid + NT * x;
-        if (p < C::NPV) {
+        const int row = rows.rv(x);
+        if (p < CA::NPV && row >= 0) {
           const int i = p / NPRV, c0 = (p % NPRV) * VN;
           const f32x4 drv = ldq(dRs + i * LDV + c0);
-          stq(ug + i * DV + c0, ldq(Us + i * LDV + c0));
-          stq(drg + i * DV + c0, drv);
-          const int row = rows.rv(x);
-          if (row >= 0) {
-            if (i >= rows.own) {
-              stq(static_cast<T*>(b.dv) + (size_t(row) * H + h) * DV + c0, drv);
-            } else {
-              float f[VN];
-              unpack16<T>(drv, f);
-              float* rg = b.replay_grad + (size_t(rows.rbase + i) * H + h) * G::W + G::DVO + c0;
+          if (i >= rows.own) {
+            stq(static_cast<T*>(b.dv) + (size_t(row) * H + h) * DV + c0, drv);
+          } else {
+            float f[VN];
+            unpack16<T>(drv, f);
+            float* rg = b.replay_grad + (size_t(rows.rbase + i) * H + h) * G::W + G::DVO + c0;
 #pragma unroll
-              for (int t = 0; t < VN; ++t) rg[t] = f[t];
-            }
+            for (int t = 0; t < VN; ++t) rg[t] = f[t];
           }
         }
       }
     }
     __syncthreads();
-    ga_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 7. dX = dT diag(beta) (lower incl.) over U; column partial sums of X .* dT for dbeta_1
+    // A7. dX = dT diag(beta) (lower incl.) over dU; column partial sums of X .* dT for dbeta_1
     HARTS_STRIDED(idx, tid, BT * (BT / VN), NT) {
       const int i = idx / (BT / VN), j0 = (idx % (BT / VN)) * VN;
       float v[VN];
@@ -723,7 +842,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       stq(dXs + i * LDJ + j0, pack16<T>(v));
     }
     {
-      constexpr int RPP = BT / C::NPART;
+      constexpr int RPP = BT / CA::NPART;
       const int j = tid % BT, part = tid / BT;
       float s = 0.f;
 #pragma unroll
@@ -734,7 +853,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       db1[part * BT + j] = s;
     }
     __syncthreads();
-    // 8. Y1 = dX X^T, stored transposed over R
+    // A8. Y1 = dX X^T, stored transposed over R
     HARTS_STRIDED(jb, wave, NB * NB, NW) {
       const int mi = jb / NB, nk = jb % NB;
       f32x4 acc = z4;
@@ -744,12 +863,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
       store4(Y1t + (16 * nk + cc) * LDJ + 16 * mi + 4 * g4, acc[0], acc[1], acc[2], acc[3]);
     }
     __syncthreads();
-    ga_load<T, BT, D, DV, 4>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 9. dL = -X^T Y1 (lower tiles, computed transposed): dA = strict_lower(diag(beta) dL) to the
-    //    workspace, row partial sums of dL .* A for dbeta_2
+    // A9. dL = -X^T Y1 (lower tiles, computed transposed): dA = strict_lower(diag(beta) dL) into
+    //     LDS over T, row partial sums of dL .* A for dbeta_2
     {
       constexpr int NTRI = NB * (NB + 1) / 2;
-      T* dag = static_cast<T*>(a.ws.dA) + wsi * BT * BT;
       HARTS_STRIDED(jb, wave, NTRI, NW) {
         int bi = 0;
         while ((bi + 1) * (bi + 2) / 2 <= jb) ++bi;
@@ -768,299 +885,60 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_gradA_kernel(BwdRoundArgs 
           v[r] = j < i ? bi_ * dl : 0.f;
           p2 += j < i ? dl * to_f(Al[i * LDJ + j]) : 0.f;
         }
-        store4(dag + i * BT + j0, v[0], v[1], v[2], v[3]);
+        store4(dAl + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         p2 += __shfl_xor(p2, 16, 64);
         p2 += __shfl_xor(p2, 32, 64);
         if (g4 == 0) db2[bj * BT + i] = p2;
       }
     }
     __syncthreads();
-    // 10. dbeta = dbeta_1 + dbeta_2: own rows to the output, replayed rows to the side buffer
+    // A10. dbeta = dbeta_1 + dbeta_2: own rows to the output, replayed rows to the side buffer
     if (tid < BT && rows.rb >= 0) {
       const int i = tid;
       float s = 0.f;
 #pragma unroll
-      for (int part = 0; part < C::NPART; ++part) s += db1[part * BT + i];
+      for (int part = 0; part < CA::NPART; ++part) s += db1[part * BT + i];
 #pragma unroll
       for (int bj = 0; bj < NB; ++bj) s += bj <= i / 16 ? db2[bj * BT + i] : 0.f;
       if (i >= rows.own) static_cast<T*>(b.dbeta)[size_t(rows.rb) * H + h] = from_f<T>(s);
       else b.replay_grad[(size_t(rows.rbase + i) * H + h) * G::W + G::DB] = s;
     }
-    __syncthreads();  // the next item restages every region
-    item = item_n;
-    item_n = item_nn;
-  }
-}
 
-// ------------------------------------------------------------------------------------------
-// Gradient kernel B (channel side): dq, dk, dg.  Persistent, one workgroup of D/16 waves
-// per compute unit walking the (chunk, head) items of the round.  Wave w owns channels
-// [16w, 16w + 16) for every token of the chunk, with lane l holding, for each 16-token
-// block b, tokens 16b + 4(l/16) + r (r = 0..3) of channel 16w + l%16 -- the accumulator
-// layout of the matrix cores.  The in-chunk decay, the 16-token block products (whose
-// right operand is the lane's own values), the state products and the final reverse
-// cumulative sum of dg all stay inside the wave.  The next item's inputs (and this
-// wave's slices of S_n and dS_n) are fetched into registers while the current item computes.
-template <typename T, int BT, int D, int DV>
-struct GBCfg {
-  using MM = Mma<T>;
-  static constexpr int NW = D / 16, NT = 64 * NW, NB = BT / 16, VN = 16 / sizeof(T), PAD = VN;
-  static constexpr int NPR = D / VN, NPK = BT * NPR, NK = (NPK + NT - 1) / NT;
-  static constexpr int NPRV = DV / VN, NPV = BT * NPRV, NV = (NPV + NT - 1) / NT;
-  static constexpr int NPJ = BT * BT / VN, NJ = (NPJ + NT - 1) / NT;
-  static constexpr int NKS = DV / MM::KS;
-  static constexpr bool SAMEV = NPR == NPRV;
-  static constexpr int LDK = D + PAD, LDV = DV + PAD, LDJ = BT + PAD, LDF = D + 4;
-  static constexpr size_t ES = sizeof(T);
-  static constexpr size_t al(size_t x) { return (x + 15) / 16 * 16; }
-  // staged inputs (bf16/fp32): Q, K, g [BT][LDK]; dO, U, dR [BT][LDV]; dM, dA [BT][LDJ]
-  static constexpr size_t SK = al(size_t(BT) * LDK * ES), SV = al(size_t(BT) * LDV * ES), SJ = al(size_t(BT) * LDJ * ES);
-  static constexpr size_t O_Q = 0, O_K = SK, O_G = 2 * SK, O_DO = 3 * SK, O_U = O_DO + SV, O_DR = O_U + SV,
-                          O_DM = O_DR + SV, O_DA = O_DM + SJ, IN_END = O_DA + SJ;
-  // output staging (fp32 [BT][LDF] for dq, dk, dg) over the inputs once they are consumed
-  static constexpr size_t SF = al(size_t(BT) * LDF * 4);
-  // bf16: per wave, its 16 channels of S_n (then of dS_n) as [DV][16], read back transposed
-  static constexpr size_t O_HS = cmx(IN_END, 3 * SF), HS = sizeof(T) == 2 ? al(size_t(NW) * DV * 16 * ES) : 0;
-  static constexpr size_t TOTAL = O_HS + HS;
-  static constexpr int NHP = DV / 32;  // 16-byte pieces per lane of one wave's slice
-  static_assert(TOTAL <= 160 * 1024, "gradient kernel B LDS budget");
-};
-
-template <typename T, int BT, int D, int DV>
-struct GBRows {
-  using C = GBCfg<T, BT, D, DV>;
-  int rk[C::NK], rv_[C::SAMEV ? 1 : C::NV], own, rbase;
-  __device__ __forceinline__ int rv(int x) const {
-    if constexpr (C::SAMEV) return rk[x];
-    else return rv_[x];
-  }
-};
-
-template <typename T, int BT, int D, int DV>
-struct GBIn {
-  using C = GBCfg<T, BT, D, DV>;
-  using F = typename C::MM::Frag;
-  f32x4 q[C::NK], k[C::NK], g[C::NK], dO[C::NV], u[C::NV], dr[C::NV], dm[C::NJ], da[C::NJ];
-  // bf16: this wave's channels of S_n and dS_n, read from their S_n^T fragment-major copies
-  // (16-byte pieces, staged in LDS and read back as matrix-core B operands); fp32: the B
-  // operands from the channel-major copies
-  static constexpr bool BF = sizeof(T) == 2;
-  f32x4 hp[BF ? C::NHP : 1], dp[BF ? C::NHP : 1];
-  F hc[BF ? 1 : C::NKS], dhc[BF ? 1 : C::NKS];
-};
-
-template <typename T, int BT, int D, int DV>
-__device__ __forceinline__ void gb_rows(GBRows<T, BT, D, DV>& r, const RoundArgs& a, int chunk, int tid) {
-  using C = GBCfg<T, BT, D, DV>;
-  const int32_t* cr = a.crows + size_t(chunk) * BT;
-#pragma unroll
-  for (int x = 0; x < C::NK; ++x) {
-    const int p = tid + C::NT * x;
-    r.rk[x] = cr[(p < C::NPK ? p : C::NPK - 1) / C::NPR];
-  }
-  if constexpr (!C::SAMEV) {
-#pragma unroll
-    for (int x = 0; x < C::NV; ++x) {
-      const int p = tid + C::NT * x;
-      r.rv_[x] = cr[(p < C::NPV ? p : C::NPV - 1) / C::NPRV];
-    }
-  }
-  r.own = a.chunks[chunk].own_from;
-  r.rbase = a.chunks[chunk].replay_base;
-}
-
-// Unconditional loads from clamped addresses: padding is masked where the values are used.
-// P selects a part of the fetch (-1: all): 0 q, k, g; 1 dO, U, dR; 2 dM, dA; 3 the state
-// slices (issued between phases by the persistent loop, as in kernel A).
-template <typename T, int BT, int D, int DV, int P = -1>
-__device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GBRows<T, BT, D, DV>& r, const BwdRoundArgs& b,
-                                        size_t wsi, int h, int H, int tid, int wave, int lane) {
-  using C = GBCfg<T, BT, D, DV>;
-  using MM = typename C::MM;
-  const RoundArgs& a = b.r;
-  if constexpr (P < 0 || P == 0) {
-#pragma unroll
-    for (int x = 0; x < C::NK; ++x) {
-      const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
-      const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
-      o.q[x] = ldq(static_cast<const T*>(a.q) + off);
-      o.k[x] = ldq(static_cast<const T*>(a.k) + off);
-      o.g[x] = ldq(static_cast<const T*>(a.g) + off);
-    }
-  }
-  if constexpr (P < 0 || P == 1) {
-    const T* ug = static_cast<const T*>(a.ws.U) + wsi * BT * DV;
-    const T* drg = static_cast<const T*>(a.ws.dR) + wsi * BT * DV;
-#pragma unroll
-    for (int x = 0; x < C::NV; ++x) {
-      const int p = tid + C::NT * x, pc = p < C::NPV ? p : C::NPV - 1;
-      const int c0 = (p % C::NPRV) * C::VN;
-      const int rr = r.rv(x);
-      o.dO[x] = ldq(static_cast<const T*>(b.dO) + (size_t(rr >= 0 ? rr : 0) * H + h) * DV + c0);
-      o.u[x] = ldq(ug + size_t(pc) * C::VN);
-      o.dr[x] = ldq(drg + size_t(pc) * C::VN);
-    }
-  }
-  if constexpr (P < 0 || P == 2) {
-    const T* dmg = static_cast<const T*>(a.ws.dM) + wsi * BT * BT;
-    const T* dag = static_cast<const T*>(a.ws.dA) + wsi * BT * BT;
-#pragma unroll
-    for (int x = 0; x < C::NJ; ++x) {
-      const int p = tid + C::NT * x, pc = p < C::NPJ ? p : C::NPJ - 1;
-      o.dm[x] = ldq(dmg + size_t(pc) * C::VN);
-      o.da[x] = ldq(dag + size_t(pc) * C::VN);
-    }
-  }
-  if constexpr (P < 0 || P == 3) {
-    if constexpr (sizeof(T) == 2) {
-      // piece x of lane l: value rows 16 (2x + l/32) + l%16, channels 16 wave + 8 ((l/16)%2) + 0..7
-      // of the [DV][D] fragment-major S_n^T (block (v tile, channel block wave/2), lane 32 (wave%2)
-      // + l%32)
-      const T* hg = static_cast<const T*>(a.h) + wsi * DV * D;
-      const T* dhg = static_cast<const T*>(b.dh) + wsi * DV * D;
-#pragma unroll
-      for (int x = 0; x < C::NHP; ++x) {
-        const size_t off = ((size_t(2 * x + (lane >> 5)) * (D / 32) + (wave >> 1)) * 64 + 32 * (wave & 1) + (lane & 31)) * 8;
-        o.hp[x] = ldq(hg + off);
-        o.dp[x] = ldq(dhg + off);
-      }
-    } else {
-      const T* hcg = static_cast<const T*>(a.hc) + wsi * D * DV;
-      const T* dhcg = static_cast<const T*>(b.dhc) + wsi * D * DV;
-#pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
-        o.hc[ks] = fm_frag<T>(hcg, DV, wave, ks, lane);
-        o.dhc[ks] = fm_frag<T>(dhcg, DV, wave, ks, lane);
-      }
-    }
-  }
-}
-
-template <typename T, int BT, int D, int DV>
-__global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b, int H) {
-  using C = GBCfg<T, BT, D, DV>;
-  using MM = typename C::MM;
-  using G = RG<D, DV>;
-  using In = GBIn<T, BT, D, DV>;
-  using Rows = GBRows<T, BT, D, DV>;
-  constexpr int NT = C::NT, NB = C::NB, VN = C::VN, NK = C::NK, NV = C::NV, NJ = C::NJ;
-  constexpr int LDK = C::LDK, LDV = C::LDV, LDJ = C::LDJ, LDF = C::LDF, NPR = C::NPR, NPRV = C::NPRV;
-  __shared__ __attribute__((aligned(16))) char smem[C::TOTAL];
-  T* Qs = reinterpret_cast<T*>(smem + C::O_Q);
-  T* Ks = reinterpret_cast<T*>(smem + C::O_K);
-  T* Gs = reinterpret_cast<T*>(smem + C::O_G);
-  T* dOs = reinterpret_cast<T*>(smem + C::O_DO);
-  T* Us = reinterpret_cast<T*>(smem + C::O_U);
-  T* dRs = reinterpret_cast<T*>(smem + C::O_DR);
-  T* dMs = reinterpret_cast<T*>(smem + C::O_DM);
-  T* dAs = reinterpret_cast<T*>(smem + C::O_DA);
-  float* stg = reinterpret_cast<float*>(smem);  // [3][BT][LDF] after the products
-  const RoundArgs& a = b.r;
-
-  const int nitems = a.nchunk * H;
-  int item = blockIdx.x;
-  if (item >= nitems) return;
-  const int tid0 = threadIdx.x;
-  // rows_x: rows of the item whose inputs are in nxt; rows_n: rows of the item after it.
-  // cur is taken from nxt at the top of each iteration, before the next fetch is issued.
-  Rows rows, rows_x, rows_n;
-  In cur, nxt;
-  gb_rows<T, BT, D, DV>(rows_x, a, item / H, tid0);
-  gb_load<T, BT, D, DV>(nxt, rows_x, b, size_t(item), item % H, H, tid0, tid0 >> 6, tid0 & 63);
-  int item_n = item + gridDim.x;
-  gb_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
-  __shared__ int tk_slot;
-  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
-  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
-
-  while (item < nitems) {
-    int tid = threadIdx.x;
-    asm volatile("" : "+v"(tid));
-    // the wave index is uniform: tile selection and addressing derived from it stay scalar
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6), cc = lane & 15, g4 = lane >> 4;
-    const int h = item % H;
-    const size_t wsi = size_t(item);
-    cur = nxt;
-    rows = rows_x;
-    const int itn = item_n < nitems ? item_n : item;
-    gb_load<T, BT, D, DV, 0>(nxt, rows_n, b, size_t(itn), itn % H, H, tid, wave, lane);
-    rows_x = rows_n;
-    if (a.ctr && tid == 0) {
-      tk_slot = tk;
-      tk = draw_ticket(a.ctr);
-    }
-
-    // 1. stage the inputs (padding rows zero; dO zero on replayed rows)
-    const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int x = 0; x < NK; ++x) {
-      const int p = tid + NT * x;
-      if (p < C::NPK) {
-        const int i = p / NPR, c0 = (p % NPR) * VN;
-        const bool ok = rows.rk[x] >= 0;
-        stq(Qs + i * LDK + c0, ok ? cur.q[x] : z4);
-        stq(Ks + i * LDK + c0, ok ? cur.k[x] : z4);
-        stq(Gs + i * LDK + c0, ok ? cur.g[x] : z4);
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < NV; ++x) {
-      const int p = tid + NT * x;
-      if (p < C::NPV) {
-        const int i = p / NPRV, c0 = (p % NPRV) * VN;
-        stq(dOs + i * LDV + c0, rows.rv(x) >= 0 && i >= rows.own ? cur.dO[x] : z4);
-        stq(Us + i * LDV + c0, cur.u[x]);
-        stq(dRs + i * LDV + c0, cur.dr[x]);
-      }
-    }
-#pragma unroll
-    for (int x = 0; x < NJ; ++x) {
-      const int p = tid + NT * x;
-      if (p < C::NPJ) {
-        const int i = p / (BT / VN), j0 = (p % (BT / VN)) * VN;
-        stq(dMs + i * LDJ + j0, cur.dm[x]);
-        stq(dAs + i * LDJ + j0, cur.da[x]);
-      }
-    }
-    __syncthreads();
-    // the item after the next one: its rows are fetched a whole item ahead of their use
-    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
-    gb_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
-
+    // ---------------- channel side ----------------
     const int c = 16 * wave + cc;
-    // 2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
+    // B2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
     f32x4 dqa[NB], X1[NB], X23[NB], X4[NB];
     float rs = 0.f;
     if constexpr (sizeof(T) == 2) {
-      // this wave's channels of S_n, then of dS_n, through its LDS slice [DV][16]; B operands
-      // (channel n = lane % 16, values 32 ks + 8 (lane / 16) + 0..7) by two transposing reads
+      // this wave's channels of S_n, then of dS_n, through its LDS slice [DV][16] (over R0 and
+      // R2, whose last readers passed the barrier above); B operands by two transposing reads
       T* hs = reinterpret_cast<T*>(smem + C::O_HS) + wave * (DV * 16);
       const int cl0 = 8 * ((lane >> 4) & 1), q = lane & 15;
-      auto stage = [&](const f32x4 (&pc)[C::NHP]) {
+      auto stage = [&](const f32x4 (&pc)[CB::NHP]) {
 #pragma unroll
-        for (int x = 0; x < C::NHP; ++x) stq(hs + (16 * (2 * x + (lane >> 5)) + (lane & 15)) * 16 + cl0, pc[x]);
+        for (int x = 0; x < CB::NHP; ++x) stq(hs + (16 * (2 * x + (lane >> 5)) + (lane & 15)) * 16 + cl0, pc[x]);
       };
       auto frag = [&](int ks) {
         const T* src = hs + (32 * ks + 8 * (lane >> 4) + (q >> 2)) * 16 + 4 * (q & 3);
         const bf16x4 lo = ds_tr16(src), hi = ds_tr16(src + 4 * 16);
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
-      bf16x8 hf[C::NKS];
-      stage(cur.hp);
+      bf16x8 hf[CB::NKS];
+      stage(cb.hp);
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) hf[ks] = frag(ks);
+      for (int ks = 0; ks < CB::NKS; ++ks) hf[ks] = frag(ks);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
+        for (int ks = 0; ks < CB::NKS; ++ks) {
           dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), hf[ks], dqa[bb]);
           X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), hf[ks], X1[bb]);
         }
       }
-      stage(cur.dp);  // in order behind this wave's reads of the S_n slice
+      stage(cb.dp);  // in order behind this wave's reads of the S_n slice
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) {
+      for (int ks = 0; ks < CB::NKS; ++ks) {
         const bf16x8 df = frag(ks);
 #pragma unroll
         for (int t = 0; t < 8; ++t) rs += (float)hf[ks][t] * (float)df[t];
@@ -1069,29 +947,43 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       }
     } else {
 #pragma unroll
-      for (int ks = 0; ks < C::NKS; ++ks) rs += cur.hc[ks] * cur.dhc[ks];
+      for (int ks = 0; ks < CB::NKS; ++ks) rs += cb.hc[ks] * cb.dhc[ks];
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
         dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], dqa[bb]);
-          X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cur.hc[ks], X1[bb]);
-          X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cur.dhc[ks], X4[bb]);
+        for (int ks = 0; ks < CB::NKS; ++ks) {
+          dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cb.hc[ks], dqa[bb]);
+          X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cb.hc[ks], X1[bb]);
+          X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cb.dhc[ks], X4[bb]);
         }
       }
     }
     rs += __shfl_xor(rs, 16, 64);
     rs += __shfl_xor(rs, 32, 64);
-    gb_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),
-    //    block totals Tb and block entry values F (F[NB] = G_last)
+    ga_load<T, BT, D, DV, 0>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
+    __syncthreads();  // state slices read: q, k, g take their place
+#pragma unroll
+    for (int x = 0; x < NK; ++x) {
+      const int p = tid + NT * x;
+      if (p < CA::NPK) {
+        const int i = p / NPR, c0 = (p % NPR) * VN;
+        const bool ok = rows.rk[x] >= 0;
+        stq(Qb + i * LDK + c0, ok ? cb.q[x] : z4);
+        stq(Kb + i * LDK + c0, ok ? cb.k[x] : z4);
+        stq(Gb + i * LDK + c0, ok ? cb.g[x] : z4);
+      }
+    }
+    __syncthreads();
+    ga_load<T, BT, D, DV, 1>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
+    // B3. in-chunk decay of channel c at this lane's tokens: L (block-local cumulative),
+    //     block totals Tb and block entry values F (F[NB] = G_last)
     float L[NB][4], Tb[NB], F[NB + 1];
     F[0] = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       float s = 0.f, gv[4];
-      col4_load<T>(Gs, LDK, 16 * bb, 16 * wave, lane, gv);
+      col4_load<T>(Gb, LDK, 16 * bb, 16 * wave, lane, gv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         s += gv[r];
@@ -1109,7 +1001,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
       F[bb + 1] = F[bb] + Tb[bb];
     }
     rs *= __expf(F[NB]);
-    // state-product factors: dq gets e^{F_b}, dk (row side) -e^{F_b}, dk (through K^) e^{G_last - F_{b+1}}
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       const float ef = __expf(F[bb]), eh = __expf(F[NB] - F[bb + 1]);
@@ -1120,8 +1011,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         X4[bb][r] *= eh;
       }
     }
-    gb_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // e^{L} and e^{-L} at this lane's tokens, shared by the block products and the assembly
+    ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     float eL[NB][4], enL[NB][4];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
@@ -1130,43 +1020,41 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         eL[bb][r] = __expf(L[bb][r]);
         enL[bb][r] = __expf(-L[bb][r]);
       }
-    // 4. 16-token block products with the gated masks factored per block pair:
-    //    row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
-    //    col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA; times e^{-L_j} later)
+    // B4. 16-token block products with the gated masks factored per block pair:
+    //     row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
+    //     col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA)
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
-        // row side: output block bi, contraction over block bj
         const float epf = bi == bj ? 1.f : __expf(F[bi] - F[bj]);  // <= 1
         float bk[4];
-        col4_load<T>(Ks, LDK, 16 * bj, 16 * wave, lane, bk);
+        col4_load<T>(Kb, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
         for (int t = 0; t < 4; ++t) bk[t] *= epf * enL[bj][t];
         const k16_t<T> bkk = k16_pack<T>(bk);
-        dqa[bi] = mma_k16r<T>(k16_row<T>(dMs + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, dqa[bi]);
-        X1[bi] = mma_k16r<T>(k16_row<T>(dAs + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, X1[bi]);
-        // col side: output block bj, contraction over block bi
+        dqa[bi] = mma_k16r<T>(k16_row<T>(dMl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, dqa[bi]);
+        X1[bi] = mma_k16r<T>(k16_row<T>(dAl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, X1[bi]);
         float bq[4], bk2[4];
-        col4_load<T>(Qs, LDK, 16 * bi, 16 * wave, lane, bq);
-        col4_load<T>(Ks, LDK, 16 * bi, 16 * wave, lane, bk2);
+        col4_load<T>(Qb, LDK, 16 * bi, 16 * wave, lane, bq);
+        col4_load<T>(Kb, LDK, 16 * bi, 16 * wave, lane, bk2);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float e = eL[bi][t] * epf;
           bq[t] *= e;
           bk2[t] *= e;
         }
-        X23[bj] = mma_k16r<T>(k16_col<T>(dMs, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bq), X23[bj]);
-        X23[bj] = mma_k16r<T>(k16_col<T>(dAs, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bk2), X23[bj]);
+        X23[bj] = mma_k16r<T>(k16_col<T>(dMl, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bq), X23[bj]);
+        X23[bj] = mma_k16r<T>(k16_col<T>(dAl, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bk2), X23[bj]);
       }
-    gb_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // 5. assemble dq, dk, dG with exact q, k and fp32 factors
+    ga_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
+    // B5. assemble dq, dk, dG with exact q, k and fp32 factors
     float csum = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       float kvv[4], qvv[4];
-      col4_load<T>(Ks, LDK, 16 * bb, 16 * wave, lane, kvv);
-      col4_load<T>(Qs, LDK, 16 * bb, 16 * wave, lane, qvv);
+      col4_load<T>(Kb, LDK, 16 * bb, 16 * wave, lane, kvv);
+      col4_load<T>(Qb, LDK, 16 * bb, 16 * wave, lane, qvv);
       const float eT = __expf(Tb[bb]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -1175,14 +1063,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         const float krow = er * X1[bb][r], kcol = ecd * X23[bb][r] + ec * X4[bb][r];
         const float kv = kvv[r], qv = qvv[r];
         dqa[bb][r] = dq;
-        X1[bb][r] = krow + kcol;                        // dk
-        X23[bb][r] = qv * dq + kv * (krow - kcol);      // dG
+        X1[bb][r] = krow + kcol;                    // dk
+        X23[bb][r] = qv * dq + kv * (krow - kcol);  // dG
         csum += kv * ec * X4[bb][r];
       }
     }
     csum += __shfl_xor(csum, 16, 64);
     csum += __shfl_xor(csum, 32, 64);
-    // 6. dg = reverse cumulative sum of dG over the chunk, dG_last added at the last row
+    ga_load<T, BT, D, DV, 4>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
+    // B6. dg = reverse cumulative sum of dG over the chunk, dG_last added at the last row
     {
       float gt[NB], after_blk = rs + csum;
       float suf[NB][4];
@@ -1220,12 +1109,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void kda_gradB_kernel(BwdRoundArgs b
         stg[2 * BT * LDF + i * LDF + c] = X23[bb][r];
       }
     __syncthreads();
-    // 7. own rows to dq, dk, dg; replayed rows (dk, dg) to the side buffer
+    // B7. own rows to dq, dk, dg; replayed rows (dk, dg) to the side buffer
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
       const int p = tid + NT * x;
       const int row = rows.rk[x];
-      if (p < C::NPK && row >= 0) {
+      if (p < CA::NPK && row >= 0) {
         const int i = p / NPR, c0 = (p % NPR) * VN;
         if (i >= rows.own) {
           const size_t off = (size_t(row) * H + h) * D + c0;
@@ -1288,14 +1177,10 @@ static hipError_t dstate_launch(const KdaDims& d, const BwdRoundArgs& b, hipStre
 }
 
 template <typename T, int BT, int D, int DV>
-static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {
+static hipError_t grad_launch(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   if (b.r.nchunk <= 0) return hipSuccess;
-  if (part == 0)
-    hipLaunchKernelGGL((kda_gradA_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
-                       dim3(GACfg<T, BT, D, DV>::NT), 0, s, b, d.H);
-  else
-    hipLaunchKernelGGL((kda_gradB_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
-                       dim3(GBCfg<T, BT, D, DV>::NT), 0, s, b, d.H);
+  hipLaunchKernelGGL((kda_grad_kernel<T, BT, D, DV>), dim3(persistent_grid(unsigned(b.r.nchunk) * d.H)),
+                     dim3(GACfg<T, BT, D, DV>::NT), 0, s, b, d.H);
   return hipGetLastError();
 }
 
@@ -1325,9 +1210,9 @@ hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& b, hipStream_
   return hipErrorNotSupported;
 }
 
-hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, int part, hipStream_t s) {
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
 #define X(T_, B_, D_, V_) \
-  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return grad_launch<T_, B_, D_, V_>(d, b, part, s);
+  if (d.dtype == (sizeof(T_) == 2 ? 0 : 1) && d.BT == B_ && d.D == D_ && d.DV == V_) return grad_launch<T_, B_, D_, V_>(d, b, s);
   HARTS_KDA_BWD_CONFIGS(X)
 #undef X
   return hipErrorInvalidValue;

@@ -24,10 +24,6 @@ struct ChunkWs {
   void* Tm;     // [BT][BT]  T = X diag(beta)                      (backward)
   void* Xm;     // [BT][BT]  X = (I + diag(beta) A)^{-1}           (backward)
   void* Am;     // [BT][BT]  A (strictly lower)                    (backward)
-  void* U;      // [BT][DV]  U = T (V - K~ S0)                      (backward)
-  void* dR;     // [BT][DV]  dL/dR = T^T dU                         (backward)
-  void* dM;     // [BT][BT]  dL/dM (lower incl.)                    (backward)
-  void* dA;     // [BT][BT]  dL/dA (strictly lower)                 (backward)
   void* Op;     // O'^T = (M U')^T as accumulator tiles             (forward, slab passes)
 };
 
@@ -96,7 +92,7 @@ hipError_t launch_slot_grad(const KdaDims& d, const int32_t* slots, int32_t nslo
                             const int32_t* cons, const float* dinit, float* out, hipStream_t s);
 hipError_t launch_kda_slab(const KdaDims& d, const BwdRoundArgs& b, int mode, int round_max_chunks, hipStream_t s);
 hipError_t launch_kda_dstate(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
-hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, int part, hipStream_t s);  // part 0: token side, 1: channel side
+hipError_t launch_kda_grad(const KdaDims& d, const BwdRoundArgs& a, hipStream_t s);
 hipError_t launch_replay_fixup(const KdaDims& d, const int32_t* fix_rows, const int32_t* fix_off,
                                const int32_t* fix_idx, int32_t nrows, const float* replay_grad, void* dk, void* dv,
                                void* dg, void* dbeta, hipStream_t s);
