@@ -3,6 +3,7 @@
 // the per-round HIP kernels on the caller's stream.  No exception crosses the ABI.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -35,6 +36,7 @@ struct harts_dev_plan {
   int32_t* fix_off = nullptr;
   int32_t* fix_idx = nullptr;
   int32_t* rslots = nullptr;           // slots produced per round (concatenated)
+  int32_t* units = nullptr;            // per round, (sequence, head) launch order of the serial passes
   std::vector<int32_t> rslot_off;      // [n_rounds + 1] offsets into rslots
   // workspace layout (byte offsets)
   size_t off_W = 0, off_Op = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
@@ -120,13 +122,42 @@ T* upload(const std::vector<T>& v, hipStream_t s) {
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
+// Launch order of a round's (sequence, head) pairs in the serial passes.  Workgroup b runs on
+// XCD b mod 8, and the kernels map the pairs to contiguous eighths of the grid, one eighth per
+// XCD, so that the workgroups of one pair share an L2.  Each chain takes its sequence's chunk
+// count in steps: the pairs are dealt to the eighths longest first, each to the least loaded
+// eighth with room, and each eighth lists its pairs longest first, so that every XCD starts its
+// long chains early and the XCDs carry equal work.  Returns u = s * H + h per launch slot.
+std::vector<int32_t> slab_unit_order(const std::vector<int32_t>& chunks, int32_t H) {
+  const size_t n = chunks.size() * size_t(H);
+  std::vector<int32_t> id(n);
+  for (size_t u = 0; u < n; ++u) id[u] = int32_t(u);
+  if (n % 8) return id;  // the eighths would split pairs: natural order
+  auto wt = [&](int32_t u) { return int64_t(chunks[size_t(u / H)]) + 1; };
+  std::stable_sort(id.begin(), id.end(), [&](int32_t x, int32_t y) { return wt(x) > wt(y); });
+  const size_t cap = n / 8;
+  std::vector<std::vector<int32_t>> bin(8);
+  std::vector<int64_t> load(8, 0);
+  for (int32_t u : id) {
+    int best = -1;
+    for (int x = 0; x < 8; ++x)
+      if (bin[size_t(x)].size() < cap && (best < 0 || load[size_t(x)] < load[size_t(best)])) best = x;
+    bin[size_t(best)].push_back(u);
+    load[size_t(best)] += wt(u);
+  }
+  std::vector<int32_t> out;
+  out.reserve(n);
+  for (const std::vector<int32_t>& b : bin) out.insert(out.end(), b.begin(), b.end());
+  return out;
+}
+
 // Write-only region of the workspace that masked-off lanes store into, so that a
 // kernel's stores are unconditional (see RoundArgs::sink).
 constexpr size_t kSinkBytes = 64 * 1024;
 
 void free_dev(harts_dev_plan* d) {
   void* ptrs[] = {d->vrows, d->seqs, d->chunks, d->crows, d->cons_off, d->cons, d->fix_rows, d->fix_off, d->fix_idx,
-                  d->rslots};
+                  d->rslots, d->units};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
 }
@@ -181,6 +212,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.nseq = rr.seq1 - rr.seq0;
   a.nchunk = rr.chunk1 - rr.chunk0;
   a.seq0 = rr.seq0;
+  a.units = d->units + size_t(rr.seq0) * size_t(d->dims.H);
   a.q = io->q;
   a.k = io->k;
   a.v = io->v;
@@ -399,6 +431,14 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
         d->rslot_off.push_back(int32_t(rsl.size()));
       }
       d->rslots = upload(rsl, s);
+      std::vector<int32_t> units;
+      for (const harts::RoundRange& rr : d->p.rounds) {
+        std::vector<int32_t> w;
+        for (int32_t q = rr.seq0; q < rr.seq1; ++q) w.push_back(d->p.seq_desc[size_t(q)].n_chunks);
+        const std::vector<int32_t> u = slab_unit_order(w, H);
+        units.insert(units.end(), u.begin(), u.end());
+      }
+      d->units = upload(units, s);
       // the host vectors must outlive the asynchronous copies
       hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
       const size_t es = dtype == HARTS_DTYPE_BF16 ? 2 : 4;

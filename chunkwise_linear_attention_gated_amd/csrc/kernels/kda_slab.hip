@@ -461,11 +461,14 @@ __global__ __launch_bounds__(64 * (NC + 1)) void kda_slab_kernel(BwdRoundArgs b,
   __shared__ __attribute__((aligned(1024))) char ring[RD * C::BUF];
   const RoundArgs& a = b.r;
   P x(b, H);
+  // the workgroups of one (sequence, head) pair sit on one XCD; the pairs in the round's launch order
   const int lb = xcd_logical(blockIdx.x, gridDim.x);
   x.grp = lb % C::NGRP;
-  x.h = (lb / C::NGRP) % H;
-  x.si = lb / (C::NGRP * H);
-  if (x.si >= a.nseq) return;
+  const int us = lb / C::NGRP;
+  if (us >= a.nseq * H) return;
+  const int u = a.units ? a.units[us] : us;
+  x.h = u % H;
+  x.si = u / H;
   x.lane = threadIdx.x & 63;
   x.wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   x.g4 = x.lane >> 4;

@@ -50,6 +50,8 @@ struct RoundArgs {
   void* hc;                   // backward: S_n per chunk, channel-major [chunk][H][D][DV] (nullable)
   int* ctr;                   // zeroed item counter of this launch of a persistent per-chunk kernel
                               // (nullable: static item order)
+  const int32_t* units;       // serial passes: this round's (sequence, head) pairs s * H + h in
+                              // launch order (nullable: natural order)
 };
 
 struct BwdRoundArgs {
