@@ -566,14 +566,16 @@ static hipError_t slab_go(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s
   return hipGetLastError();
 }
 
-// One compute wave (one slab) per workgroup while the round's slabs fit the chip one
-// workgroup per compute unit (latency-bound long chains); otherwise two compute waves of two
-// slabs each sharing one ring: every wave has a SIMD (and its registers) to itself, and the
-// shared operands are read from LDS once per two slabs.
+// Two compute waves of two slabs each per workgroup, sharing one ring: every wave has a SIMD
+// (and its registers) to itself, the shared operands are read from LDS once per two slabs, and a
+// (sequence, head) pair takes two compute units.  Only a round too small to matter for the rest
+// of the chip (at most a quarter of the compute units' worth of slabs) runs one slab per
+// workgroup, for the shortest chain latency; a larger round shares the chip with the per-chunk
+// kernels of other rounds, and packing its chains onto fewer compute units leaves them more.
 template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
-  if (slabs <= persistent_grid(1u << 30)) return slab_go<MODE, BT, D, DV, 1, 1, 3>(d, b, s);
+  if (4 * slabs <= persistent_grid(1u << 30)) return slab_go<MODE, BT, D, DV, 1, 1, 3>(d, b, s);
   return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
 }
 

@@ -205,3 +205,54 @@ def test_rollout_tree_backward_sampled():
         e = rel_err(got[n][sel_rows], ref[n][sel_pos])
         print(n, "rows", len(sel_rows), "rel err", e)
         assert e <= TOL["bf16"], (n, e)
+
+
+def test_graph_replay_equals_eager():
+    """The forward + backward step captured into a HIP graph (its work forked onto the
+    library's own streams joins the capture) replays bit for bit what the eager calls
+    produce, replay after replay, with eager work between the replays."""
+    t = trees.random_small_tree(np.random.default_rng(31), max_segments=9, max_len=300, forest=True)
+    H, D, B = 4, 128, 64
+    feats = tensors.draw_features(t.n_nodes, H, D, D, seed=8, dtype="bf16")
+    hp = harts.TreePlan(t.tokens, t.offsets, B)
+    m, _, _ = hp.maps()
+    C = hp.info.C
+    x = device_inputs(feats, node_of_row(m, t.node_of_pos, C))
+    dp = harts.DevicePlan(hp, H, D, D, harts.DTYPE_BF16)
+    ns = max(1, hp.info.n_slots)
+    o = torch.zeros((C, H, D), dtype=torch.bfloat16, device="cuda")
+    slots = torch.zeros((ns, H, D, D), dtype=torch.float32, device="cuda")
+    dslots = torch.zeros_like(slots)
+    gr = {n: torch.zeros_like(x[n]) for n in NAMES}
+    ws = torch.empty(dp.workspace_size(2), dtype=torch.uint8, device="cuda")
+
+    def step():
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=True)
+        harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"], gr["g"],
+                      gr["beta"], states=slots, dstates=dslots, workspace=ws, keep=True)
+
+    n_slots = hp.info.n_slots
+    outs = lambda: [o.clone(), slots[:n_slots].clone(), dslots[:n_slots].clone()] + [gr[n].clone() for n in NAMES]  # noqa: E731
+    step()
+    torch.cuda.synchronize()
+    ref = outs()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for r in range(3):
+        for z in [o, dslots[:n_slots]] + list(gr.values()):
+            z.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(ref, outs()):
+            assert torch.equal(a, b), "replay %d" % r
+        step()  # eager work between replays
+        torch.cuda.synchronize()
