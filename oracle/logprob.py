@@ -9,6 +9,12 @@ For semantic position s with compact row m(s) and target label y_s
 computed in float64 per semantic position (the expanded definition: no
 per-row sharing), with the usual max shift inside the log-sum-exp.  The
 occurrence count q_c is the number of semantic positions with m(s) = c.
+
+Backward (blog section 4.4, equation 19): for L = sum_s g_s log p_s, every
+semantic position forms its own gradient g_s (onehot(y_s) - softmax(x[m(s)]))
+and the gradients of all positions that read one compact row are summed into
+that row -- a sum of independently formed terms, not a reuse count times one
+term, so positions with different labels or weights keep their own parts.
 """
 from __future__ import annotations
 
@@ -37,3 +43,34 @@ def counts(m: np.ndarray, C: int) -> np.ndarray:
     for c in np.asarray(m, dtype=np.int64):
         q[c] += 1
     return q.astype(np.int32)
+
+
+def logprob_backward(rows_fp64: np.ndarray, row_index: np.ndarray, labels: np.ndarray,
+                     dlogp: np.ndarray) -> np.ndarray:
+    """dL/dx [R, V] for L = sum_s dlogp[s] * logp[s]: the expanded definition, one semantic
+    position at a time (a Python loop: small cases only)."""
+    rows = np.asarray(rows_fp64, dtype=np.float64)
+    row_index = np.asarray(row_index, dtype=np.int64)
+    labels = np.asarray(labels, dtype=np.int64)
+    dlogp = np.asarray(dlogp, dtype=np.float64)
+    out = np.zeros_like(rows)
+    for s in range(row_index.shape[0]):
+        x = rows[row_index[s]]
+        e = np.exp(x - x.max())
+        g = -dlogp[s] * (e / e.sum())
+        g[labels[s]] += dlogp[s]
+        out[row_index[s]] += g
+    return out
+
+
+def rows_of_map(m: np.ndarray, C: int):
+    """The semantic positions of every compact row in increasing order, as CSR offsets [C + 1]
+    and positions [S]."""
+    m = np.asarray(m, dtype=np.int64)
+    off = np.zeros(C + 1, dtype=np.int64)
+    pos = []
+    for c in range(C):
+        mine = [s for s in range(m.shape[0]) if m[s] == c]
+        pos.extend(mine)
+        off[c + 1] = off[c] + len(mine)
+    return off, np.asarray(pos, dtype=np.int64)

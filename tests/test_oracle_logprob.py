@@ -1,5 +1,8 @@
 """Pins of the float64 log-prob oracle: a constant row, a library
-log-softmax, brute-force counts, and the workload generator's invariants."""
+log-softmax, brute-force counts, and the workload generator's invariants;
+for its backward, central finite differences of the forward, the zero row
+sum, a library cross-entropy gradient and the additivity of repeated
+positions."""
 import numpy as np
 import scipy.special
 
@@ -41,3 +44,66 @@ def test_counts_and_generator_invariants():
         lab = w.labels[w.m == c]
         assert len(np.unique(lab)) == len(lab)
     assert 4.5 < len(w.m) / w.C < 6.8
+
+
+def _fd_grad(x, m, y, w, c, v, h=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp[c, v] += h
+    xm[c, v] -= h
+    return (w @ logprob.logprob(xp, m, y) - w @ logprob.logprob(xm, m, y)) / (2 * h)
+
+
+def test_backward_matches_finite_differences():
+    rng = np.random.default_rng(5)
+    C, V, S = 4, 37, 11
+    x = rng.standard_normal((C, V)) * 1.5
+    m = rng.integers(0, C, size=S)
+    y = rng.integers(0, V, size=S)
+    y[3], m[3] = y[2], m[2]  # a repeated (row, label) pair
+    w = rng.standard_normal(S)
+    g = logprob.logprob_backward(x, m, y, w)
+    for c in range(C):
+        for v in list(rng.integers(0, V, size=6)) + [int(y[s]) for s in range(S) if m[s] == c]:
+            assert abs(g[c, v] - _fd_grad(x, m, y, w, c, v)) < 1e-7
+
+
+def test_backward_rows_sum_to_zero_and_unread_rows_are_zero():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((6, 50))
+    m = np.array([0, 0, 2, 3, 3, 3])
+    y = np.array([1, 1, 7, 0, 49, 2])
+    g = logprob.logprob_backward(x, m, y, rng.standard_normal(6))
+    np.testing.assert_allclose(g.sum(axis=1), 0.0, atol=1e-12)
+    assert not g[[1, 4, 5]].any()
+
+
+def test_backward_single_positions_match_library_cross_entropy():
+    torch = __import__("pytest").importorskip("torch")
+    rng = np.random.default_rng(7)
+    C, V = 5, 64
+    x = rng.standard_normal((C, V))
+    y = rng.integers(0, V, size=C)
+    xt = torch.tensor(x, requires_grad=True)
+    torch.nn.functional.cross_entropy(xt, torch.tensor(y), reduction="sum").backward()
+    # L = sum log p = -cross entropy: the gradient is the negated library one
+    np.testing.assert_allclose(logprob.logprob_backward(x, np.arange(C), y, np.ones(C)), -xt.grad.numpy(),
+                               rtol=0, atol=1e-12)
+
+
+def test_backward_repeated_positions_add():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((2, 20))
+    one = logprob.logprob_backward(x, np.array([1]), np.array([4]), np.array([0.7]))
+    two = logprob.logprob_backward(x, np.array([1, 1]), np.array([4, 4]), np.array([0.7, 0.7]))
+    np.testing.assert_allclose(two, 2 * one, rtol=0, atol=1e-14)
+    mixed = logprob.logprob_backward(x, np.array([1, 1]), np.array([4, 9]), np.array([0.7, -0.2]))
+    np.testing.assert_allclose(mixed, one + logprob.logprob_backward(x, np.array([1]), np.array([9]), np.array([-0.2])),
+                               rtol=0, atol=1e-14)
+
+
+def test_rows_of_map_is_the_stable_inverse():
+    rng = np.random.default_rng(9)
+    m = rng.integers(0, 7, size=40)
+    off, pos = logprob.rows_of_map(m, 9)
+    assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(m, minlength=9))]))
+    assert np.array_equal(pos, np.argsort(m, kind="stable"))
