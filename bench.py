@@ -307,7 +307,27 @@ def main():
         out["logprob_gather"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": lms, "bytes": lbytes,
                                  "achieved_gbps": lbytes / (lms / 1e3) / 1e9,
                                  "frac_hbm": lbytes / (lms / 1e3) / PEAK_HBM}
-        del logits
+        # backward (equation 19): one read of the logits and one write of their gradient
+        lse = torch.empty(Cl, dtype=torch.float32, device=dev)
+        harts.logprob_gather(logits, mm, lab, logp, lse=lse)
+        off, pos = harts.logprob_rows(w.m, Cl)
+        offd, posd = torch.from_numpy(off).to(dev), torch.from_numpy(pos).to(dev)
+        gl = torch.from_numpy(np.random.default_rng(args.seed).standard_normal(len(w.m)).astype(np.float32)).to(dev)
+        dlog = torch.empty_like(logits)
+        for _ in range(2):
+            harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / reps
+        bbytes = 2 * Cl * V * 2 + len(w.m) * (8 + 4 + 4) + Cl * (8 + 4)
+        out["logprob_backward"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": bms, "bytes": bbytes,
+                                   "achieved_gbps": bbytes / (bms / 1e3) / 1e9,
+                                   "frac_hbm": bbytes / (bms / 1e3) / PEAK_HBM}
+        del logits, dlog
     # ---------------------------------------------------------------- oracle on the host cores
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(t, feats, C, S)

@@ -87,6 +87,8 @@ _kda_fwd = _sig("harts_kda_fwd", I32, P, ctypes.POINTER(KdaIO), P)
 _kda_bwd = _sig("harts_kda_bwd", I32, P, ctypes.POINTER(KdaIO), ctypes.POINTER(KdaGrad), P)
 _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
+_lpb = _sig("harts_logprob_backward", I32, P, I64, I64, I32, P, P, P, P, P, I64, P, P)
+_lp_rows = _sig("harts_logprob_rows", I32, P, I64, I64, P, P)
 _prof_enable = _sig("harts_profile_enable", I32, I32)
 _prof_collect = _sig("harts_profile_collect", I32, P, I32, P)
 _last_error = _sig("harts_last_error", ctypes.c_char_p)
@@ -271,6 +273,28 @@ def logprob_gather(logits, m, labels, logp, q=None, lse=None, workspace=None, st
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lp(_ptr(logits), C, V, dtype, _ptr(m), _ptr(labels), S, _ptr(logp), _ptr(q), _ptr(lse),
                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def logprob_backward(logits, lse, row_off, row_pos, labels, dlogp, dlogits, stream=None):
+    """harts_logprob_backward: dlogits[c] = sum over row c's positions of
+    dlogp[s] (onehot(labels[s]) - softmax(logits[c]))."""
+    import torch
+    C, V = logits.shape
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise HartsError(-1, "logits must be bf16 or fp32")
+    dtype = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_FP32
+    _check(_lpb(_ptr(logits), C, V, dtype, _ptr(lse), _ptr(row_off), _ptr(row_pos), _ptr(labels), _ptr(dlogp),
+                labels.numel(), _ptr(dlogits), _stream(stream)))
+
+
+def logprob_rows(m, C: int):
+    """harts_logprob_rows (host): CSR offsets [C + 1] and positions [S] of every compact
+    row's semantic positions, in increasing order."""
+    m = np.ascontiguousarray(m, dtype=np.int64)
+    off = np.empty(C + 1, dtype=np.int64)
+    pos = np.empty(m.shape[0], dtype=np.int64)
+    _check(_lp_rows(m.ctypes.data, m.shape[0], C, off.ctypes.data, pos.ctypes.data))
+    return off, pos
 
 
 def profile_enable(on: bool = True):

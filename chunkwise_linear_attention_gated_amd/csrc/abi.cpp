@@ -691,6 +691,43 @@ int harts_logprob_gather(const void* logits, int64_t C, int64_t V, int32_t dtype
   });
 }
 
+int harts_logprob_backward(const void* logits, int64_t C, int64_t V, int32_t dtype, const float* lse,
+                           const int64_t* row_off, const int64_t* row_pos, const int32_t* labels, const float* dlogp,
+                           int64_t S, void* dlogits_out, void* stream) {
+  return guarded([&] {
+    if (C < 0 || V < 1 || S < 0) throw Error(HARTS_EINVAL, "need C >= 0, V >= 1, S >= 0");
+    if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+    if (C >= (int64_t(1) << 31)) throw Error(HARTS_ERANGE, "C must be < 2^31");
+    if (C == 0) return;
+    if (!logits || !lse || !row_off || !dlogits_out) throw Error(HARTS_EINVAL, "logits, lse, row_off and dlogits_out are required");
+    if (S > 0 && (!row_pos || !labels || !dlogp)) throw Error(HARTS_EINVAL, "row_pos, labels and dlogp are required");
+    const size_t es = dtype == HARTS_DTYPE_BF16 ? 2 : 4;
+    const char* a = static_cast<const char*>(logits);
+    const char* b = static_cast<const char*>(dlogits_out);
+    const size_t bytes = size_t(C) * size_t(V) * es;
+    if (a < b + bytes && b < a + bytes) throw Error(HARTS_EINVAL, "dlogits_out overlaps logits");
+    ProfScope ps("logprob_backward", static_cast<hipStream_t>(stream), C);
+    hip_check(harts::launch_logprob_bwd(logits, C, V, dtype, lse, row_off, row_pos, labels, dlogp, dlogits_out,
+                                        static_cast<hipStream_t>(stream)),
+              "log-prob backward kernel launch");
+  });
+}
+
+int harts_logprob_rows(const int64_t* m, int64_t S, int64_t C, int64_t* row_off, int64_t* row_pos) {
+  return guarded([&] {
+    if (S < 0 || C < 0) throw Error(HARTS_EINVAL, "need S >= 0, C >= 0");
+    if (!row_off || (S > 0 && (!m || !row_pos))) throw Error(HARTS_EINVAL, "m, row_off and row_pos are required");
+    std::vector<int64_t> cnt(size_t(C) + 1, 0);
+    for (int64_t s = 0; s < S; ++s) {
+      if (m[s] < 0 || m[s] >= C) throw Error(HARTS_EINVAL, "m[" + std::to_string(s) + "] is outside [0, C)");
+      ++cnt[size_t(m[s]) + 1];
+    }
+    for (int64_t c = 0; c < C; ++c) cnt[size_t(c) + 1] += cnt[size_t(c)];
+    std::copy(cnt.begin(), cnt.end(), row_off);
+    for (int64_t s = 0; s < S; ++s) row_pos[cnt[size_t(m[s])]++] = s;  // stable: positions in increasing s
+  });
+}
+
 int harts_profile_enable(int32_t on) {
   return guarded([&] {
     std::vector<ProfRec> old;

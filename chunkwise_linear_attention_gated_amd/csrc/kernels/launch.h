@@ -104,5 +104,8 @@ bool kda_supported(const KdaDims& d);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
                           int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
+hipError_t launch_logprob_bwd(const void* logits, int64_t C, int64_t V, int dtype, const float* lse,
+                              const int64_t* row_off, const int64_t* row_pos, const int32_t* labels, const float* dlogp,
+                              void* dlogits, hipStream_t s);
 
 }  // namespace harts

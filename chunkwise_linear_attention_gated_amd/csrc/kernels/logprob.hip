@@ -7,6 +7,12 @@
 //   row pass:    lse[c] = log sum_v exp(x[c, v])   (one streaming read of each row)
 //   gather pass: logp[s] = x[m[s], label[s]] - lse[m[s]];  q[m[s]] += 1
 //
+// Backward (equation 19 of the same section): for L = sum_s g_s logp[s], each compact row
+// takes the sum of its semantic positions' own gradients g_s (onehot(label_s) - softmax(x[c])):
+//   dx[c, v] = sum_{s in c, label_s = v} g_s - (sum_{s in c} g_s) softmax(x[c])[v]
+// in one streaming read and write of the row; the positions of a row come from the CSR inverse
+// of m and are summed in increasing s, so the result does not depend on scheduling.
+//
 // The row pass is a pure HBM stream: 16-byte loads, four in flight per
 // thread, online max / sum-exp in base 2 (one exp2 per element).
 #include "common.h"
@@ -121,6 +127,103 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, in
     logp[s] = to_f(x[c * V + labels[s]]) - lse[c];
     if (q) atomicAdd(q + c, 1);
   }
+}
+
+// One workgroup per compact row: the row's positions (label, weight) staged in LDS, their weight
+// sum G, a streaming pass writing -G softmax(x[c]), then the label entries rewritten with their
+// positions' weights added (a wait for the streamed stores and a barrier order them after).
+// Rows with more than KPOS positions read their lists from global memory instead.
+constexpr int KPOS = 512;
+
+template <typename T>
+__global__ __launch_bounds__(256) void logprob_bwd_kernel(const T* __restrict__ x, int64_t V, const float* __restrict__ lse,
+                                                          const int64_t* __restrict__ row_off,
+                                                          const int64_t* __restrict__ row_pos,
+                                                          const int32_t* __restrict__ labels,
+                                                          const float* __restrict__ dlogp, T* __restrict__ dx,
+                                                          bool vec_ok) {
+  constexpr int VN = 16 / sizeof(T);
+  const int64_t c = blockIdx.x;
+  const int64_t b = row_off[c], n = row_off[c + 1] - b;
+  __shared__ int32_t plab[KPOS];
+  __shared__ float pw[KPOS];
+  __shared__ float wsum;
+  const bool staged = n <= KPOS;
+  if (staged)
+    for (int64_t t = threadIdx.x; t < n; t += 256) {
+      const int64_t s = row_pos[b + t];
+      plab[t] = labels[s];
+      pw[t] = dlogp[s];
+    }
+  auto lab_of = [&](int64_t t) { return staged ? plab[t] : labels[row_pos[b + t]]; };
+  auto w_of = [&](int64_t t) { return staged ? pw[t] : dlogp[row_pos[b + t]]; };
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float g = 0.f;
+    for (int64_t t = 0; t < n; ++t) g += w_of(t);
+    wsum = g;
+  }
+  __syncthreads();
+  const float ng = 0.f - wsum;  // +0 for a row no position reads
+  const float l2 = lse[c] * kLog2e;
+  const T* row = x + c * V;
+  T* out = dx + c * V;
+  const int64_t nvec = vec_ok ? V / VN : 0;
+  const f32x4* rv = reinterpret_cast<const f32x4*>(row);
+  int64_t i = threadIdx.x;
+  for (; i + 3 * 256 < nvec; i += 4 * 256) {
+    f32x4 raw[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      float v[VN];
+      unpack16<T>(raw[u], v);
+#pragma unroll
+      for (int t = 0; t < VN; ++t) v[t] = ng * exp2f(v[t] * kLog2e - l2);
+      __builtin_nontemporal_store(pack16<T>(v), reinterpret_cast<f32x4*>(out) + i + u * 256);
+    }
+  }
+  for (; i < nvec; i += 256) {
+    float v[VN];
+    unpack16<T>(rv[i], v);
+#pragma unroll
+    for (int t = 0; t < VN; ++t) v[t] = ng * exp2f(v[t] * kLog2e - l2);
+    st16<T>(out + i * VN, v);
+  }
+  for (int64_t j = nvec * VN + threadIdx.x; j < V; j += 256) out[j] = from_f<T>(ng * exp2f(to_f(row[j]) * kLog2e - l2));
+  // every streamed store has completed (acknowledged by the L2 that holds its line) before any
+  // label entry is rewritten: a plain wait, where a device-scope fence would write the L2 back
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  // label entries: the first position of each distinct label in the row writes the sum of the
+  // weights of all its positions with that label, in increasing s
+  for (int64_t k = threadIdx.x; k < n; k += 256) {
+    const int32_t y = lab_of(k);
+    bool first = true;
+    for (int64_t j = 0; j < k && first; ++j) first = lab_of(j) != y;
+    if (!first) continue;
+    float g = 0.f;
+    for (int64_t j = k; j < n; ++j)
+      if (lab_of(j) == y) g += w_of(j);
+    out[y] = from_f<T>(g + ng * exp2f(to_f(row[y]) * kLog2e - l2));
+  }
+}
+
+hipError_t launch_logprob_bwd(const void* logits, int64_t C, int64_t V, int dtype, const float* lse,
+                              const int64_t* row_off, const int64_t* row_pos, const int32_t* labels, const float* dlogp,
+                              void* dlogits, hipStream_t s) {
+  if (C <= 0) return hipSuccess;
+  const int vn = dtype == 0 ? 8 : 4;
+  const bool vec_ok = (reinterpret_cast<uintptr_t>(logits) % 16 == 0) && (reinterpret_cast<uintptr_t>(dlogits) % 16 == 0) &&
+                      (V % vn == 0);
+  if (dtype == 0)
+    hipLaunchKernelGGL(logprob_bwd_kernel<bf16>, dim3(unsigned(C)), dim3(256), 0, s, static_cast<const bf16*>(logits), V,
+                       lse, row_off, row_pos, labels, dlogp, static_cast<bf16*>(dlogits), vec_ok);
+  else
+    hipLaunchKernelGGL(logprob_bwd_kernel<float>, dim3(unsigned(C)), dim3(256), 0, s, static_cast<const float*>(logits),
+                       V, lse, row_off, row_pos, labels, dlogp, static_cast<float*>(dlogits), vec_ok);
+  return hipGetLastError();
 }
 
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,

@@ -239,6 +239,36 @@ int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype
                          const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, float *lse_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- log-prob gradient
+ * [blog 4.4, equation 19] For L = sum_s dlogp[s] * logp[s], every semantic
+ * position forms its own gradient and the positions that read one compact row
+ * are summed into it (never a reuse count times one term):
+ *     dlogits[c, v] = sum_{s : m[s] = c, labels[s] = v} dlogp[s]
+ *                     - (sum_{s : m[s] = c} dlogp[s]) * softmax(logits[c, :])[v]
+ * each row's positions summed in increasing s (results do not depend on the
+ * schedule); the S x V expansion is never formed.  One streaming read of the
+ * logits and one write of the gradient.
+ *
+ * logits: device [C, V] (dtype bf16 or fp32), as given to harts_logprob_gather.
+ * lse: device float32 [C], that call's lse_out on the same logits.
+ * row_off: device int64 [C + 1]; row_pos: device int64 [S]: the semantic
+ *   positions of row c are row_pos[row_off[c] .. row_off[c + 1]) in increasing
+ *   order (harts_logprob_rows builds both from m on the host).
+ * labels: device int32 [S] in [0, V); dlogp: device float32 [S].
+ * dlogits_out: device [C, V], the logits' dtype, every element written; must
+ *   not overlap logits.
+ * Offsets, positions and labels are not checked on the device (caller contract).
+ */
+int harts_logprob_backward(const void *logits, int64_t C, int64_t V, int32_t dtype, const float *lse,
+                           const int64_t *row_off, const int64_t *row_pos, const int32_t *labels,
+                           const float *dlogp, int64_t S, void *dlogits_out, void *stream);
+
+/* Host: the inverse of the semantic map m (host int64 [S], values in [0, C)) as
+ * CSR arrays: row_off (host int64 [C + 1]) and row_pos (host int64 [S]), each
+ * row's positions in increasing order.  HARTS_EINVAL if some m[s] is outside
+ * [0, C). */
+int harts_logprob_rows(const int64_t *m, int64_t S, int64_t C, int64_t *row_off, int64_t *row_pos);
+
 /* ---------------------------------------------------------------- kernel timing
  * For benchmarks and profiling.  While enabled, every kernel the library
  * enqueues is bracketed by two HIP events recorded on the same stream (this

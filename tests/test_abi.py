@@ -51,3 +51,25 @@ def test_unsupported_shapes_rejected_before_any_device_work():
     assert "unsupported" in str(e.value)
     with pytest.raises(harts.HartsError):
         harts.DevicePlan(p, 0, 128, 128, harts.DTYPE_BF16, stream=0)
+
+
+def test_logprob_rows_is_the_stable_inverse_of_m():
+    from oracle import logprob as olp
+    rng = np.random.default_rng(3)
+    for C, S in [(1, 0), (5, 1), (9, 60), (40, 300)]:
+        m = rng.integers(0, C, size=S)
+        off, pos = harts.logprob_rows(m, C)
+        want_off, want_pos = olp.rows_of_map(m, C)
+        assert np.array_equal(off, want_off) and np.array_equal(pos, want_pos)
+    with pytest.raises(harts.HartsError) as e:
+        harts.logprob_rows(np.array([0, 3, 1]), 3)
+    assert e.value.code == -1 and "outside" in str(e.value)
+
+
+def test_logprob_backward_rejects_bad_arguments_before_any_device_work():
+    f = _lib._lpb
+    assert f(None, 4, 0, 0, None, None, None, None, None, 0, None, None) == -1  # V < 1
+    assert f(None, 4, 8, 7, None, None, None, None, None, 0, None, None) == -1  # unknown dtype
+    assert f(None, 4, 8, 0, None, None, None, None, None, 0, None, None) == -1  # missing arrays
+    assert b"required" in _lib._last_error()
+    assert f(None, 0, 8, 0, None, None, None, None, None, 0, None, None) == 0  # no rows: nothing to do

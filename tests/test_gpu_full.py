@@ -95,3 +95,34 @@ def test_logprob_full_size_sampled():
     ref = olp.logprob(xr, remap[w.m[sel]], w.labels[sel])
     assert np.abs(logp.cpu().numpy()[sel] - ref).max() <= 1e-3
     del x
+
+
+def test_logprob_backward_full_size_sampled():
+    """C = 32768 rows of V = 131072 bf16 logits (the log-prob workload): the gradient of
+    sum_s g_s logp_s with respect to the logits, checked on 32 sampled rows (every position of
+    those rows) against the float64 per-position definition."""
+    C, V = 32768, 131072
+    w = tensors.logprob_map(C, V, seed=1)
+    x = tensors.logits_torch(C, V, seed=1, device="cuda")
+    g = np.random.default_rng(1).standard_normal(len(w.m)).astype(np.float32)
+    m = torch.from_numpy(w.m).cuda()
+    lab = torch.from_numpy(w.labels).cuda()
+    lp = torch.empty(len(w.m), dtype=torch.float32, device="cuda")
+    lse = torch.empty(C, dtype=torch.float32, device="cuda")
+    harts.logprob_gather(x, m, lab, lp, lse=lse)
+    off, pos = harts.logprob_rows(w.m, C)
+    dx = torch.empty_like(x)
+    harts.logprob_backward(x, lse, torch.from_numpy(off).cuda(), torch.from_numpy(pos).cuda(), lab,
+                           torch.from_numpy(g).cuda(), dx)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(2).choice(C, size=32, replace=False))
+    sel = np.nonzero(np.isin(w.m, rows))[0]
+    remap = np.full(C, -1, np.int64)
+    remap[rows] = np.arange(len(rows))
+    ri = torch.from_numpy(rows).cuda()
+    ref = olp.logprob_backward(x[ri].double().cpu().numpy(), remap[w.m[sel]], w.labels[sel], g[sel])
+    got = dx[ri].double().cpu().numpy()
+    scale = np.zeros(len(rows))
+    np.add.at(scale, remap[w.m[sel]], np.abs(g[sel].astype(np.float64)))
+    assert (np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6 * scale[:, None]).all()
+    del x, dx
