@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--only-logprob", action="store_true",
+                    help="only the log-prob gather and its backward (for profiling them alone)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     return ap.parse_args()
@@ -159,6 +161,59 @@ def cpu_baseline(t, feats, C, S, target_positions=250000, seed=0):
                       "%.1f s; extrapolated per semantic position" % (len(which), t.n_traj, P, S, H, dt)}
 
 
+def logprob_bench(args, out):
+    """The log-prob workload (32768 compact rows x 131072 bf16 logits): forward gather and its
+    backward, each timed with HIP events, into ``out``."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    from synthetic import tensors
+    dev = "cuda"
+    Cl, V = 32768, 131072
+    w = tensors.logprob_map(Cl, V, seed=args.seed)
+    logits = tensors.logits_torch(Cl, V, seed=args.seed, device=dev)
+    mm = torch.from_numpy(w.m).to(dev)
+    lab = torch.from_numpy(w.labels).to(dev)
+    logp = torch.empty(len(w.m), dtype=torch.float32, device=dev)
+    qq = torch.empty(Cl, dtype=torch.int32, device=dev)
+    lws = torch.empty(harts.logprob_workspace_size(Cl), dtype=torch.uint8, device=dev)
+    for _ in range(2):
+        harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
+    torch.cuda.synchronize()
+    reps = max(3, min(args.steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
+    e1.record()
+    torch.cuda.synchronize()
+    lms = e0.elapsed_time(e1) / reps
+    lbytes = Cl * V * 2 + len(w.m) * (8 + 4 + 4 + 2) + Cl * 8
+    out["logprob_gather"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": lms, "bytes": lbytes,
+                             "achieved_gbps": lbytes / (lms / 1e3) / 1e9,
+                             "frac_hbm": lbytes / (lms / 1e3) / PEAK_HBM}
+    # backward (equation 19): one read of the logits and one write of their gradient
+    lse = torch.empty(Cl, dtype=torch.float32, device=dev)
+    harts.logprob_gather(logits, mm, lab, logp, lse=lse)
+    off, pos = harts.logprob_rows(w.m, Cl)
+    offd, posd = torch.from_numpy(off).to(dev), torch.from_numpy(pos).to(dev)
+    gl = torch.from_numpy(np.random.default_rng(args.seed).standard_normal(len(w.m)).astype(np.float32)).to(dev)
+    dlog = torch.empty_like(logits)
+    for _ in range(2):
+        harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
+    e1.record()
+    torch.cuda.synchronize()
+    bms = e0.elapsed_time(e1) / reps
+    bbytes = 2 * Cl * V * 2 + len(w.m) * (8 + 4 + 4) + Cl * (8 + 4)
+    out["logprob_backward"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": bms, "bytes": bbytes,
+                               "achieved_gbps": bbytes / (bms / 1e3) / 1e9,
+                               "frac_hbm": bbytes / (bms / 1e3) / PEAK_HBM}
+    del logits, dlog
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -178,6 +233,12 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes": n}))
+        return
+
+    if args.only_logprob:
+        out = {}
+        logprob_bench(args, out)
+        print(json.dumps(out))
         return
 
     # ---------------------------------------------------------------- workload
@@ -280,54 +341,11 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
-    # ---------------------------------------------------------------- log-prob gather (32768 x 131072 bf16)
+    # ---------------------------------------------------------------- log-prob gather and its backward
     if not args.no_logprob:
         del ws
         torch.cuda.empty_cache()
-        Cl, V = 32768, 131072
-        w = tensors.logprob_map(Cl, V, seed=args.seed)
-        logits = tensors.logits_torch(Cl, V, seed=args.seed, device=dev)
-        mm = torch.from_numpy(w.m).to(dev)
-        lab = torch.from_numpy(w.labels).to(dev)
-        logp = torch.empty(len(w.m), dtype=torch.float32, device=dev)
-        qq = torch.empty(Cl, dtype=torch.int32, device=dev)
-        lws = torch.empty(harts.logprob_workspace_size(Cl), dtype=torch.uint8, device=dev)
-        for _ in range(2):
-            harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
-        torch.cuda.synchronize()
-        reps = max(3, min(args.steps, 10))
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            harts.logprob_gather(logits, mm, lab, logp, q=qq, workspace=lws)
-        e1.record()
-        torch.cuda.synchronize()
-        lms = e0.elapsed_time(e1) / reps
-        lbytes = Cl * V * 2 + len(w.m) * (8 + 4 + 4 + 2) + Cl * 8
-        out["logprob_gather"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": lms, "bytes": lbytes,
-                                 "achieved_gbps": lbytes / (lms / 1e3) / 1e9,
-                                 "frac_hbm": lbytes / (lms / 1e3) / PEAK_HBM}
-        # backward (equation 19): one read of the logits and one write of their gradient
-        lse = torch.empty(Cl, dtype=torch.float32, device=dev)
-        harts.logprob_gather(logits, mm, lab, logp, lse=lse)
-        off, pos = harts.logprob_rows(w.m, Cl)
-        offd, posd = torch.from_numpy(off).to(dev), torch.from_numpy(pos).to(dev)
-        gl = torch.from_numpy(np.random.default_rng(args.seed).standard_normal(len(w.m)).astype(np.float32)).to(dev)
-        dlog = torch.empty_like(logits)
-        for _ in range(2):
-            harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(reps):
-            harts.logprob_backward(logits, lse, offd, posd, lab, gl, dlog)
-        e1.record()
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / reps
-        bbytes = 2 * Cl * V * 2 + len(w.m) * (8 + 4 + 4) + Cl * (8 + 4)
-        out["logprob_backward"] = {"C": Cl, "V": V, "S": int(len(w.m)), "ms": bms, "bytes": bbytes,
-                                   "achieved_gbps": bbytes / (bms / 1e3) / 1e9,
-                                   "frac_hbm": bbytes / (bms / 1e3) / PEAK_HBM}
-        del logits, dlog
+        logprob_bench(args, out)
     # ---------------------------------------------------------------- oracle on the host cores
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(t, feats, C, S)
