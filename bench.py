@@ -78,9 +78,9 @@ def hbm_bytes(kernel, l, d=D, bt=B):
     sq = bt * bt * ES       # one [B, B] workspace array
     st = d * d * ES         # one bf16 state [d, d]
     return {
-        "kda_prep_fwd": 4 * tok + l * ES + 8 * blk + 4 * sq + d * 4,
+        "kda_prep_fwd": 4 * tok + l * ES + 5 * blk + 4 * sq + d * 4,
         "kda_state_fwd": 5 * blk + d * 4 + tok + st,
-        "kda_prep_bwd": 4 * tok + l * ES + 6 * blk + 4 * sq + d * 4,
+        "kda_prep_bwd": 4 * tok + l * ES + 4 * blk + 4 * sq + d * 4,
         "kda_state_bwd": 3 * blk + d * 4 + st,
         "kda_dstate": 3 * blk + d * 4 + tok + st,
         # q, k, v, g, dO, beta, S, dS, T, M, X, A in; dq, dk, dv, dg, dbeta out

@@ -238,9 +238,10 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.Mm = at(d->off_Mm, BT * BT, es);
   a.ws.El = reinterpret_cast<float*>(at(d->off_El, dk, 4));
   a.sink = ws + d->off_sink;
-  a.ws.QeffT = at(d->off_Qe, dk * BT, es);
-  a.ws.WT = at(d->off_WT, dk * BT, es);
-  a.ws.Kh = at(d->off_Kh, BT * dk, es);
+  const bool f32 = d->dims.dtype == HARTS_DTYPE_FP32;
+  a.ws.QeffT = f32 ? at(d->off_Qe, dk * BT, es) : nullptr;
+  a.ws.WT = f32 ? at(d->off_WT, dk * BT, es) : nullptr;
+  a.ws.Kh = f32 ? at(d->off_Kh, BT * dk, es) : nullptr;
   a.ws.Tm = at(d->off_Tm, BT * BT, es);
   a.ws.Xm = at(d->off_Xm, BT * BT, es);
   a.ws.Am = at(d->off_Am, BT * BT, es);
@@ -464,17 +465,18 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       d->ws_fwd = off;
       // the backward arrays follow the forward's, so that a forward that keeps them for the
       // backward (harts_kda_io::keep) leaves its own outputs intact
-      d->off_Qe = take(MC * dk * BT * es);
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
-      // channel-major copies of the chunk-start states and their gradients: fp32 path only
-      // (the bf16 gradient kernel transposes its slices in LDS)
+      // fp32 path only: channel-major copies of the chunk-start states and their gradients, and
+      // the state-gradient operands Qeff^T, W^T, K^ (the bf16 gradient kernel transposes its state
+      // slices in LDS, and the bf16 state-gradient pass reads the forward's operands transposed)
       if (dtype == HARTS_DTYPE_FP32) {
         d->off_hc = take(MC * dv * dk * es);
         d->off_dhc = take(MC * dv * dk * es);
+        d->off_Qe = take(MC * dk * BT * es);
+        d->off_WT = take(MC * dk * BT * es);
+        d->off_Kh = take(MC * BT * dk * es);
       }
-      d->off_WT = take(MC * dk * BT * es);
-      d->off_Kh = take(MC * BT * dk * es);
       d->off_dinit = take(size_t(d->p.seqs.size()) * H * dk * dv * 4);
       d->off_rg = take(size_t(d->p.replay_total) * H * (2 * dk + dv + 1) * 4);
       d->off_Tm = take(MC * BT * BT * es);

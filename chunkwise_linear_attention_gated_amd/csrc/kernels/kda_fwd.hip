@@ -394,13 +394,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           kh[t] = kk[t] * (Tv[b * D + c0 + t] * En[x][t]) * EH[b * D + c0 + t];
         }
         stq(Kt + i * LDK + c0, pack16<T>(kt));
-        if constexpr (BWD && PF) {
-          T* khp = static_cast<T*>(a.ws.Kh) + wsi * BT * D;
-          store4(khp + pf_off(i, c0, D), kh[0], kh[1], kh[2], kh[3]);
-          store4(khp + pf_off(i, c0 + 4, D), kh[4], kh[5], kh[6], kh[7]);
-        } else if constexpr (BWD) {
-          fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
-        }
+        if constexpr (BWD && !PF) fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
         if (BWD || PF) stq(Qr + i * LDK + c0, pack16<T>(qt));
         else fm_store<T>(static_cast<T*>(a.ws.Qt) + wsi * BT * D, D, i, c0, qt, VN);
         if constexpr (PF) {
@@ -527,16 +521,10 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
               const float wv[4] = {wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]};
               fm_store<T>(wg, D, i, c0, wv, 4);
             }
-            if constexpr (BWD) {
+            if constexpr (BWD && !PF) {
               T* wtg = static_cast<T*>(a.ws.WT) + wsi * D * BT;
-              if constexpr (PF) {
-                // 4 x 4 lane transpose: channel c0 + lane % 4, tokens 16 nt + 4 (lane % 16 / 4) + {0..3}
-                const f32x4 y = quad_transpose(wacc[u], lane);
-                store4(wtg + pf_off(c0 + (lane & 3), 16 * nt + 4 * ((lane & 15) >> 2), BT), -y[0], -y[1], -y[2], -y[3]);
-              } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
-              }
+              for (int r = 0; r < 4; ++r) wtg[fm_off<T>(c0 + r, i, BT)] = from_f<T>(wacc[u][r]);
             }
           }
         }
@@ -602,10 +590,9 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
         __syncthreads();
         if constexpr (PF) {
-          // 9. Qeff = Q~ - M W once, in tiles of token rows and channel columns: Qeff^T [D][BT]
-          //    (backward) straight from the tile, Qeff [BT][D] (forward) after a 4 x 4 lane
-          //    transpose; Q~ of the tile by one transposing read
-          T* qeT = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
+          // 9. Qeff = Q~ - M W, in tiles of token rows and channel columns, stored as Qeff [BT][D]
+          //    after a 4 x 4 lane transpose (the state-gradient pass reads it back transposed);
+          //    Q~ of the tile by one transposing read
           T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
           constexpr int MT = BT / 16, NT = D / 16;
           HARTS_STRIDED(jb, wave, MT * NT, CNW) {
@@ -614,16 +601,13 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int k0 = 0; k0 < BT; k0 += MM::KS)
               acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
-            const int c = 16 * nt + ccol(lane), i0 = 16 * mt + crow(lane, 0), q = lane & 15;
+            const int i0 = 16 * mt + crow(lane, 0), q = lane & 15;
             const bf16x4 qv = ds_tr16(Qr + (16 * mt + 4 * (lane >> 4) + (q >> 2)) * LDK + 16 * nt + 4 * (q & 3));
             f32x4 v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (float)qv[r] - acc[r];
-            if constexpr (BWD) store4(qeT + pf_off(c, i0, BT), v[0], v[1], v[2], v[3]);
-            if constexpr (FO) {
-              const f32x4 y = quad_transpose(v, lane);
-              store4(qe + pf_off(i0 + (lane & 3), 16 * nt + 4 * (q >> 2), D), y[0], y[1], y[2], y[3]);
-            }
+            const f32x4 y = quad_transpose(v, lane);
+            store4(qe + pf_off(i0 + (lane & 3), 16 * nt + 4 * (q >> 2), D), y[0], y[1], y[2], y[3]);
           }
         } else if constexpr (BWD) {
           // 9. Qeff = Q~ - M W, stored as Qeff^T [D][BT]

@@ -108,9 +108,10 @@ struct SlabPass {
     const size_t items = size_t(a.nchunk) * H;
     const size_t opb = items * BT * D * 2;
     if constexpr (MODE == SLAB_DST) {
-      r.arr[0] = buf_rsrc(a.ws.Kh, opb);
-      r.arr[1] = buf_rsrc(a.ws.QeffT, opb);
-      r.arr[2] = buf_rsrc(a.ws.WT, opb);
+      // the forward's operand layouts, read back transposed (see read_phase)
+      r.arr[0] = buf_rsrc(a.ws.KhT, opb);
+      r.arr[1] = buf_rsrc(a.ws.Qt, opb);
+      r.arr[2] = buf_rsrc(a.ws.W, opb);
       r.dO = buf_rsrc(b.dO, size_t(0x7fffffff));
     } else {
       r.arr[0] = buf_rsrc(a.ws.W, opb);
@@ -198,7 +199,30 @@ struct SlabPass {
       arr = p + (ph == NP - 1 ? NP - 1 : ph) * BD * 1024;  // W, [Qeff], K^^T
       with_e = ph == NP - 1;
     }
-    if (phase_kind(ph) == 0) {
+    if constexpr (MODE == SLAB_DST) {
+      // The gradient's operands are the transposes of the forward's: K^ from K^^T [D][BT], Qeff^T
+      // and -W^T from Qeff and -W [BT][D], all in the permuted fragment-major layout.  A
+      // transposed fragment (rows r0 + lane % 16, contraction k0 + pf_k(lane / 16, 0..7)) is two
+      // transposing reads: lane q of a 16-lane group points at 4 consecutive columns r0 + 4 (q % 4)
+      // of source row k0 + 4 (lane / 16) + q / 4 (then + 16), and receives column r0 + q of the
+      // four rows the group's lanes point at.
+      const int q = lane & 15, k4 = 4 * g4 + (q >> 2), r4 = 4 * (q & 3);
+      auto tr = [&](int k, int r, int K) {
+        const bf16x4 lo = ds_tr16(arr + 2 * pf_off(k, r, K)), hi = ds_tr16(arr + 2 * pf_off(k + 16, r, K));
+        return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      };
+      if (phase_kind(ph) == 0) {
+#pragma unroll
+        for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+          for (int i = 0; i < NTT; ++i) g.f[kb * NTT + i] = tr(32 * kb + k4, 16 * i + r4, BT);
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+          for (int t = 0; t < NTS; ++t) g.f[kb * NTS + t] = tr(32 * kb + k4, 16 * t + r4, D);
+      }
+    } else if (phase_kind(ph) == 0) {
 #pragma unroll
       for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
@@ -227,8 +251,8 @@ struct SlabPass {
       mma(ph, g[ph & 1]);
 #pragma unroll
       for (int x = 0; x < NFM * NS; ++x) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one matrix-core op
+        __builtin_amdgcn_sched_group_barrier(0x100, MODE == SLAB_DST ? 2 : 1, 0);  // its share of LDS reads
       }
       sched_fence();
     }
