@@ -99,6 +99,12 @@ struct SlabPass {
   __device__ __forceinline__ size_t wsi(int c) const { return wbase + size_t(c) * H; }
   __device__ __forceinline__ int jv0_of(int sl) const { return 16 * (grp * C::SLABS + sl); }
 
+  // Slot of 16-byte piece L (0..63) of a 1 KiB operand block in the gradient pass's ring: bits 2-3
+  // of L flipped by bits 4-5 (an involution).  A transposing read of a fragment touches pieces
+  // 16 a + 4 g + b (a, b = 0..3) for each 16-lane group g; unswizzled, the four pieces with the
+  // same b share their banks.
+  __device__ __forceinline__ static int swz(int L) { return L ^ ((L >> 4) << 2); }
+
   // ---- producer ---------------------------------------------------------------------------
   struct Src {
     __amdgpu_buffer_rsrc_t arr[3], el, up, op, dO, desc;
@@ -128,10 +134,13 @@ struct SlabPass {
   __device__ __forceinline__ void produce(const Src& r, int c, char* dst) const {
     const size_t w = wsi(c);
     const int vo = lane * 16;
+    // the gradient pass reads its operands transposed: its copies place 16-byte piece L of each
+    // 1 KiB block at slot swz(L) (see read_phase), so that those reads spread over the banks
+    const int vs = (MODE == SLAB_DST ? swz(lane) : lane) * 16;
 #pragma unroll
     for (int ar = 0; ar < C::NARR; ++ar)
 #pragma unroll
-      for (int q = 0; q < BD; ++q) lds_load16(r.arr[ar], dst + (ar * BD + q) * 1024, vo, int(w * BT * D * 2) + q * 1024);
+      for (int q = 0; q < BD; ++q) lds_load16(r.arr[ar], dst + (ar * BD + q) * 1024, vs, int(w * BT * D * 2) + q * 1024);
     // E in lanes [0, D/4), the chunk descriptor (32 bytes) in the next two lanes
     constexpr int NE = D / 4;
     if (lane < NE) lds_load16(r.el, dst + C::EOFF, vo, int(w * D * 4));
@@ -207,8 +216,12 @@ struct SlabPass {
       // of source row k0 + 4 (lane / 16) + q / 4 (then + 16), and receives column r0 + q of the
       // four rows the group's lanes point at.
       const int q = lane & 15, k4 = 4 * g4 + (q >> 2), r4 = 4 * (q & 3);
+      auto at = [&](int k, int r, int K) {
+        const int o = 2 * int(pf_off(k, r, K));  // byte offset: 1 KiB block, 16-byte piece, half
+        return arr + (o & ~1023) + 16 * swz((o >> 4) & 63) + (o & 15);
+      };
       auto tr = [&](int k, int r, int K) {
-        const bf16x4 lo = ds_tr16(arr + 2 * pf_off(k, r, K)), hi = ds_tr16(arr + 2 * pf_off(k + 16, r, K));
+        const bf16x4 lo = ds_tr16(at(k, r, K)), hi = ds_tr16(at(k + 16, r, K));
         return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       };
       if (phase_kind(ph) == 0) {
