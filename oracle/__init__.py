@@ -18,8 +18,11 @@ Contents, each written from the pages (HARTS, arXiv 2608.28158):
   hand-derived reverse pass (C, OpenMP; ``recurrent.c``).
 * ``oracle.chunkwise`` -- float64 chunkwise form of the same rule, and a tree
   execution with bounded replay built on it (used only for self-checks).
-* ``oracle.logprob``   -- float64 log-softmax gather from its definition, and
-  occurrence counts.
+* ``oracle.logprob``   -- float64 log-softmax gather from its definition, its
+  gradient (per-position terms summed into their compact row), occurrence
+  counts.
+* ``oracle.conv``      -- float64 depthwise causal convolution over each
+  trajectory's own tokens (ancestor context), and its gradients.
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force or a library routine.
