@@ -12,5 +12,6 @@ from __future__ import annotations
 from .build import build  # noqa: F401
 from ._lib import (  # noqa: F401
     DTYPE_BF16, DTYPE_FP32, HartsError, TreePlan, VarlenPlan, DevicePlan, kda_fwd, kda_bwd, logprob_gather,
-    logprob_workspace_size, logprob_backward, logprob_rows, library, version, profile_enable, profile_collect,
+    logprob_workspace_size, logprob_backward, logprob_rows, conv_tables, conv_workspace_size, conv_fwd,
+    conv_bwd, library, version, profile_enable, profile_collect,
 )

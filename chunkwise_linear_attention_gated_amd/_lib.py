@@ -89,6 +89,10 @@ _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
 _lpb = _sig("harts_logprob_backward", I32, P, I64, I64, I32, P, P, P, P, P, I64, P, P)
 _lp_rows = _sig("harts_logprob_rows", I32, P, I64, I64, P, P)
+_conv_tables = _sig("harts_conv_tables", I32, P, P, I64, I64, I32, P, P, P)
+_conv_ws = _sig("harts_conv_workspace_size", ctypes.c_size_t, I64, I32, I32)
+_conv_fwd = _sig("harts_conv_fwd", I32, P, P, P, I64, I32, I32, I32, P, P)
+_conv_bwd = _sig("harts_conv_bwd", I32, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P, ctypes.c_size_t, P)
 _prof_enable = _sig("harts_profile_enable", I32, I32)
 _prof_collect = _sig("harts_profile_collect", I32, P, I32, P)
 _last_error = _sig("harts_last_error", ctypes.c_char_p)
@@ -295,6 +299,46 @@ def logprob_rows(m, C: int):
     pos = np.empty(m.shape[0], dtype=np.int64)
     _check(_lp_rows(m.ctypes.data, m.shape[0], C, off.ctypes.data, pos.ctypes.data))
     return off, pos
+
+
+def conv_tables(m, traj_offsets, C: int, w: int):
+    """harts_conv_tables (host): ancestor table [C, w - 1] (int32) and the gather lists
+    (offsets [C + 1], entries 8 t + j) of the tree causal convolution."""
+    m = np.ascontiguousarray(m, dtype=np.int64)
+    off = np.ascontiguousarray(traj_offsets, dtype=np.int64)
+    anc = np.empty((C, w - 1), dtype=np.int32)
+    goff = np.empty(C + 1, dtype=np.int64)
+    gl = np.empty(max(1, C * (w - 1)), dtype=np.int64)
+    _check(_conv_tables(m.ctypes.data, off.ctypes.data, off.shape[0] - 1, C, w, anc.ctypes.data, goff.ctypes.data,
+                        gl.ctypes.data))
+    return anc, goff, gl  # gl holds goff[-1] entries (at least one slot, so never empty)
+
+
+def conv_workspace_size(C: int, channels: int, w: int) -> int:
+    return int(_conv_ws(C, channels, w))
+
+
+def _act_dtype(x):
+    import torch
+    if x.dtype not in (torch.bfloat16, torch.float32):
+        raise HartsError(-1, "activations must be bf16 or fp32")
+    return DTYPE_BF16 if x.dtype == torch.bfloat16 else DTYPE_FP32
+
+
+def conv_fwd(x, weight, anc, out, stream=None):
+    """harts_conv_fwd: out[t] = sum_j weight[:, j] * x[anc_j(t)] over the compact rows."""
+    C, ch = x.shape
+    _check(_conv_fwd(_ptr(x), _ptr(weight), _ptr(anc), C, ch, weight.shape[1], _act_dtype(x), _ptr(out),
+                     _stream(stream)))
+
+
+def conv_bwd(x, weight, anc, gather_off, gather, dout, dx=None, dweight=None, workspace=None, stream=None):
+    """harts_conv_bwd: dx and dweight of sum_t <dout[t], out[t]>."""
+    C, ch = x.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_conv_bwd(_ptr(x), _ptr(weight), _ptr(anc), _ptr(gather_off), _ptr(gather), _ptr(dout), C, ch,
+                     weight.shape[1], _act_dtype(x), _ptr(dx), _ptr(dweight), _ptr(workspace), ws_bytes,
+                     _stream(stream)))
 
 
 def profile_enable(on: bool = True):

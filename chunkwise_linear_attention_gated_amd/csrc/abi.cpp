@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -727,6 +728,100 @@ int harts_logprob_rows(const int64_t* m, int64_t S, int64_t C, int64_t* row_off,
     for (int64_t c = 0; c < C; ++c) cnt[size_t(c) + 1] += cnt[size_t(c)];
     std::copy(cnt.begin(), cnt.end(), row_off);
     for (int64_t s = 0; s < S; ++s) row_pos[cnt[size_t(m[s])]++] = s;  // stable: positions in increasing s
+  });
+}
+
+int harts_conv_tables(const int64_t* m, const int64_t* traj_offsets, int64_t n_traj, int64_t C, int32_t w,
+                      int32_t* anc, int64_t* gather_off, int64_t* gather) {
+  return guarded([&] {
+    if (n_traj < 0 || C < 0) throw Error(HARTS_EINVAL, "need n_traj >= 0, C >= 0");
+    if (w < 2 || w > 8) throw Error(HARTS_EINVAL, "w must be in [2, 8]");
+    if (!traj_offsets || !gather_off || (C > 0 && (!anc || !gather))) throw Error(HARTS_EINVAL, "missing arrays");
+    if (traj_offsets[0] != 0) throw Error(HARTS_EINVAL, "traj_offsets[0] must be 0");
+    for (int64_t i = 0; i < n_traj; ++i)
+      if (traj_offsets[i + 1] < traj_offsets[i]) throw Error(HARTS_EINVAL, "traj_offsets must be non-decreasing");
+    if (traj_offsets[n_traj] > 0 && !m) throw Error(HARTS_EINVAL, "m is NULL");
+    const int K = w - 1;
+    constexpr int32_t kUnset = INT32_MIN;
+    std::fill(anc, anc + size_t(C) * K, kUnset);
+    for (int64_t i = 0; i < n_traj; ++i) {
+      const int64_t o = traj_offsets[i], L = traj_offsets[i + 1] - o;
+      for (int64_t p = 0; p < L; ++p) {
+        const int64_t t = m[o + p];
+        if (t < 0 || t >= C) throw Error(HARTS_EINVAL, "m[" + std::to_string(o + p) + "] is outside [0, C)");
+        for (int j = 1; j <= K; ++j) {
+          const int32_t a = p >= j ? int32_t(m[o + p - j]) : -1;
+          int32_t& slot = anc[size_t(t) * K + j - 1];
+          if (slot == kUnset) slot = a;
+          else if (slot != a)
+            throw Error(HARTS_EINVAL, "m is not the map of a prefix tree: row " + std::to_string(t) +
+                                          " has two different predecessors");
+        }
+      }
+    }
+    std::vector<int64_t> cnt(size_t(C) + 1, 0);
+    for (int64_t t = 0; t < C; ++t)
+      for (int j = 1; j <= K; ++j) {
+        const int32_t a = anc[size_t(t) * K + j - 1];
+        if (a == kUnset) throw Error(HARTS_EINVAL, "row " + std::to_string(t) + " is on no trajectory");
+        if (a >= 0) ++cnt[size_t(a) + 1];
+      }
+    for (int64_t c = 0; c < C; ++c) cnt[size_t(c) + 1] += cnt[size_t(c)];
+    std::copy(cnt.begin(), cnt.end(), gather_off);
+    for (int j = 1; j <= K; ++j)  // increasing (j, t) within each row's list
+      for (int64_t t = 0; t < C; ++t) {
+        const int32_t a = anc[size_t(t) * K + j - 1];
+        if (a >= 0) gather[cnt[size_t(a)]++] = t * 8 + j;
+      }
+  });
+}
+
+size_t harts_conv_workspace_size(int64_t C, int32_t channels, int32_t w) {
+  return C > 0 && channels > 0 && w > 0 ? align256(harts::conv_workspace_bytes(C, channels, w)) : 256;
+}
+
+namespace {
+void conv_check(const void* x, int64_t C, int32_t channels, int32_t w, int32_t dtype) {
+  if (C < 0) throw Error(HARTS_EINVAL, "need C >= 0");
+  if (C >= (int64_t(1) << 31)) throw Error(HARTS_ERANGE, "C must be < 2^31");
+  if (channels <= 0 || channels % 8) throw Error(HARTS_EINVAL, "channels must be a positive multiple of 8");
+  if (w < 2 || w > 8) throw Error(HARTS_EINVAL, "w must be in [2, 8]");
+  if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+  if (C > 0 && (!x || reinterpret_cast<uintptr_t>(x) % 16)) throw Error(HARTS_EINVAL, "x must be 16-byte aligned");
+}
+}  // namespace
+
+int harts_conv_fwd(const void* x, const float* weight, const int32_t* anc, int64_t C, int32_t channels, int32_t w,
+                   int32_t dtype, void* out, void* stream) {
+  return guarded([&] {
+    conv_check(x, C, channels, w, dtype);
+    if (C == 0) return;
+    if (!weight || !anc || !out || reinterpret_cast<uintptr_t>(out) % 16)
+      throw Error(HARTS_EINVAL, "weight, anc and a 16-byte aligned out are required");
+    const size_t bytes = size_t(C) * size_t(channels) * (dtype == HARTS_DTYPE_BF16 ? 2 : 4);
+    const char *a = static_cast<const char*>(x), *b = static_cast<const char*>(out);
+    if (a < b + bytes && b < a + bytes) throw Error(HARTS_EINVAL, "out overlaps x");
+    ProfScope ps("conv_fwd", static_cast<hipStream_t>(stream), C);
+    hip_check(harts::launch_conv_fwd(x, weight, anc, C, channels, w, dtype, out, static_cast<hipStream_t>(stream)),
+              "convolution kernel launch");
+  });
+}
+
+int harts_conv_bwd(const void* x, const float* weight, const int32_t* anc, const int64_t* gather_off,
+                   const int64_t* gather, const void* dout, int64_t C, int32_t channels, int32_t w, int32_t dtype,
+                   void* dx, float* dweight, void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    conv_check(x, C, channels, w, dtype);
+    if (C == 0) return;
+    if (!weight || !dout || reinterpret_cast<uintptr_t>(dout) % 16) throw Error(HARTS_EINVAL, "weight and a 16-byte aligned dout are required");
+    if (dx && (!gather_off || !gather || reinterpret_cast<uintptr_t>(dx) % 16))
+      throw Error(HARTS_EINVAL, "dx needs gather_off, gather and 16-byte alignment");
+    if (dweight && (!anc || !workspace || workspace_bytes < harts::conv_workspace_bytes(C, channels, w)))
+      throw Error(HARTS_EINVAL, "dweight needs anc and a workspace of harts_conv_workspace_size bytes");
+    ProfScope ps("conv_bwd", static_cast<hipStream_t>(stream), C);
+    hip_check(harts::launch_conv_bwd(x, weight, anc, gather_off, gather, dout, C, channels, w, dtype, dx, dweight,
+                                     static_cast<float*>(workspace), static_cast<hipStream_t>(stream)),
+              "convolution gradient kernel launch");
   });
 }
 

@@ -1,0 +1,189 @@
+// Depthwise causal convolution over the compact rows of a rollout tree on gfx950 (HARTS
+// close-reading blog, section 4.3: the convolution's context for a branch is built from its real
+// ancestors' last w - 1 projected activations, and windows never cross into another
+// trajectory).  Each row's window is read through a per-row ancestor table (row of the token j
+// places earlier on the row's trajectories, -1 before the first token), so a fork's branches
+// all see their common prefix and no row is expanded:
+//
+//   out[t, c] = sum_{j<w} weight[c, j] x[anc_j(t), c]                         (anc_0(t) = t)
+//   dx[s, c]  = weight[c, 0] dout[s, c] + sum_{(t, j): anc_j(t) = s} weight[c, j] dout[t, c]
+//   dweight[c, j] = sum_t dout[t, c] x[anc_j(t), c]
+//
+// Every pass moves 16-byte pieces of 8 channels; dx gathers over a per-row list of (t, j) in a
+// fixed order and dweight sums fixed row blocks, then the blocks in order, so the results do not
+// depend on scheduling.  The windows' reads of earlier rows mostly hit the L2 (rows of one
+// branch are contiguous).
+#include "common.h"
+#include "launch.h"
+
+namespace harts {
+
+constexpr int kConvRowBlock = 256;  // rows per partial sum of dweight
+
+template <typename T>
+__device__ __forceinline__ void ld8(const T* p, float* v) {
+  if constexpr (sizeof(T) == 2) {
+    unpack16<T>(*reinterpret_cast<const f32x4*>(p), v);
+  } else {
+    unpack16<T>(*reinterpret_cast<const f32x4*>(p), v);
+    unpack16<T>(*reinterpret_cast<const f32x4*>(p + 4), v + 4);
+  }
+}
+template <typename T>
+__device__ __forceinline__ void st8(T* p, const float* v) {
+  if constexpr (sizeof(T) == 2) {
+    *reinterpret_cast<f32x4*>(p) = pack16<T>(v);
+  } else {
+    *reinterpret_cast<f32x4*>(p) = pack16<T>(v);
+    *reinterpret_cast<f32x4*>(p + 4) = pack16<T>(v + 4);
+  }
+}
+
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ wt,
+                                                       const int32_t* __restrict__ anc, int64_t C, int32_t ch,
+                                                       T* __restrict__ out) {
+  const int64_t pieces = C * (ch / 8);
+  for (int64_t p = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; p < pieces; p += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t t = p / (ch / 8);
+    const int c0 = int(p % (ch / 8)) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int64_t r = j == 0 ? t : anc[t * (W - 1) + j - 1];
+      if (r < 0) continue;
+      float v[8];
+      ld8<T>(x + r * ch + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wt[(c0 + e) * W + j] * v[e];
+    }
+    st8<T>(out + t * ch + c0, acc);
+  }
+}
+
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_dx_kernel(const T* __restrict__ dout, const float* __restrict__ wt,
+                                                      const int64_t* __restrict__ goff, const int64_t* __restrict__ gl,
+                                                      int64_t C, int32_t ch, T* __restrict__ dx) {
+  const int64_t pieces = C * (ch / 8);
+  for (int64_t p = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; p < pieces; p += int64_t(gridDim.x) * blockDim.x) {
+    const int64_t s = p / (ch / 8);
+    const int c0 = int(p % (ch / 8)) * 8;
+    float acc[8], v[8];
+    ld8<T>(dout + s * ch + c0, v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = wt[(c0 + e) * W] * v[e];
+    for (int64_t i = goff[s]; i < goff[s + 1]; ++i) {
+      const int64_t t = gl[i] >> 3;
+      const int j = int(gl[i] & 7);
+      ld8<T>(dout + t * ch + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wt[(c0 + e) * W + j] * v[e];
+    }
+    st8<T>(dx + s * ch + c0, acc);
+  }
+}
+
+// partial[b][c][j] = sum over rows t of block b of dout[t, c] x[anc_j(t), c]; grid (channel
+// pieces / 256, row blocks)
+template <typename T, int W>
+__global__ __launch_bounds__(256) void conv_dw_partial_kernel(const T* __restrict__ x, const T* __restrict__ dout,
+                                                              const int32_t* __restrict__ anc, int64_t C, int32_t ch,
+                                                              float* __restrict__ part) {
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (c0 >= ch) return;
+  const int64_t t0 = int64_t(blockIdx.y) * kConvRowBlock, t1 = t0 + kConvRowBlock < C ? t0 + kConvRowBlock : C;
+  float acc[W][8];
+#pragma unroll
+  for (int j = 0; j < W; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  for (int64_t t = t0; t < t1; ++t) {
+    float g[8];
+    ld8<T>(dout + t * ch + c0, g);
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+      const int64_t r = j == 0 ? t : anc[t * (W - 1) + j - 1];
+      if (r < 0) continue;
+      float v[8];
+      ld8<T>(x + r * ch + c0, v);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] += g[e] * v[e];
+    }
+  }
+  float* pb = part + (size_t(blockIdx.y) * ch + c0) * W;
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < W; ++j) pb[e * W + j] = acc[j][e];
+}
+
+__global__ __launch_bounds__(256) void conv_dw_sum_kernel(const float* __restrict__ part, int64_t nblk, int64_t n,
+                                                          float* __restrict__ dw) {
+  const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int64_t b = 0; b < nblk; ++b) s += part[b * n + i];
+  dw[i] = s;
+}
+
+size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w) {
+  const int64_t nblk = (C + kConvRowBlock - 1) / kConvRowBlock;
+  return size_t(nblk > 0 ? nblk : 1) * size_t(ch) * size_t(w) * 4;
+}
+
+static unsigned conv_grid(int64_t pieces) {
+  const int64_t b = (pieces + 255) / 256;
+  return unsigned(b < 65536 ? (b > 0 ? b : 1) : 65536);
+}
+
+template <typename T, int W>
+static hipError_t conv_fwd_t(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, void* out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL((conv_fwd_kernel<T, W>), dim3(conv_grid(C * (ch / 8))), dim3(256), 0, s, static_cast<const T*>(x),
+                     wt, anc, C, ch, static_cast<T*>(out));
+  return hipGetLastError();
+}
+
+template <typename T, int W>
+static hipError_t conv_bwd_t(const void* x, const float* wt, const int32_t* anc, const int64_t* goff, const int64_t* gl,
+                             const void* dout, int64_t C, int32_t ch, void* dx, float* dw, float* part, hipStream_t s) {
+  if (dx)
+    hipLaunchKernelGGL((conv_dx_kernel<T, W>), dim3(conv_grid(C * (ch / 8))), dim3(256), 0, s,
+                       static_cast<const T*>(dout), wt, goff, gl, C, ch, static_cast<T*>(dx));
+  if (dw) {
+    const int64_t nblk = (C + kConvRowBlock - 1) / kConvRowBlock;
+    hipLaunchKernelGGL((conv_dw_partial_kernel<T, W>), dim3(unsigned((ch / 8 + 255) / 256), unsigned(nblk)), dim3(256), 0,
+                       s, static_cast<const T*>(x), static_cast<const T*>(dout), anc, C, ch, part);
+    const int64_t n = int64_t(ch) * W;
+    hipLaunchKernelGGL(conv_dw_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part, nblk, n, dw);
+  }
+  return hipGetLastError();
+}
+
+#define HARTS_CONV_W(X) X(2) X(3) X(4) X(5) X(6) X(7) X(8)
+
+hipError_t launch_conv_fwd(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, int32_t w,
+                           int dtype, void* out, hipStream_t s) {
+  if (C <= 0) return hipSuccess;
+#define X(W_)                                                                                   \
+  if (w == W_) return dtype == 0 ? conv_fwd_t<bf16, W_>(x, wt, anc, C, ch, out, s)             \
+                                 : conv_fwd_t<float, W_>(x, wt, anc, C, ch, out, s);
+  HARTS_CONV_W(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_conv_bwd(const void* x, const float* wt, const int32_t* anc, const int64_t* goff, const int64_t* gl,
+                           const void* dout, int64_t C, int32_t ch, int32_t w, int dtype, void* dx, float* dw,
+                           float* part, hipStream_t s) {
+  if (C <= 0) return hipSuccess;
+#define X(W_)                                                                                        \
+  if (w == W_) return dtype == 0 ? conv_bwd_t<bf16, W_>(x, wt, anc, goff, gl, dout, C, ch, dx, dw, part, s) \
+                                 : conv_bwd_t<float, W_>(x, wt, anc, goff, gl, dout, C, ch, dx, dw, part, s);
+  HARTS_CONV_W(X)
+#undef X
+  return hipErrorInvalidValue;
+}
+
+}  // namespace harts

@@ -104,6 +104,12 @@ bool kda_supported(const KdaDims& d);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
                           int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
+size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w);
+hipError_t launch_conv_fwd(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, int32_t w,
+                           int dtype, void* out, hipStream_t s);
+hipError_t launch_conv_bwd(const void* x, const float* wt, const int32_t* anc, const int64_t* goff, const int64_t* gl,
+                           const void* dout, int64_t C, int32_t ch, int32_t w, int dtype, void* dx, float* dw,
+                           float* part, hipStream_t s);
 hipError_t launch_logprob_bwd(const void* logits, int64_t C, int64_t V, int dtype, const float* lse,
                               const int64_t* row_off, const int64_t* row_pos, const int32_t* labels, const float* dlogp,
                               void* dlogits, hipStream_t s);

@@ -269,6 +269,44 @@ int harts_logprob_backward(const void *logits, int64_t C, int64_t V, int32_t dty
  * [0, C). */
 int harts_logprob_rows(const int64_t *m, int64_t S, int64_t C, int64_t *row_off, int64_t *row_pos);
 
+/* ---------------------------------------------------------------- tree causal convolution
+ * [blog 4.3] The KDA layer's depthwise causal convolution over the compact
+ * rows: a branch's window reaches into its real ancestors' last w - 1 tokens,
+ * never into another trajectory, and no row is expanded:
+ *     out[t, c] = sum_{j < w} weight[c, j] * x[anc_j(t), c],   anc_0(t) = t,
+ * anc_j(t) the row of the token j places before t on the trajectories through
+ * t (they share t's prefix), zero before a trajectory's first token.
+ *
+ * Host: harts_conv_tables builds, from m (host int64 [S], semantic -> compact,
+ * as harts_plan_maps returns it) and the trajectory offsets (host int64
+ * [n_traj + 1], offsets[0] = 0):
+ *   anc: int32 [C][w - 1], anc[t][j - 1] = anc_j(t) or -1;
+ *   gather_off: int64 [C + 1]; gather: int64 [C * (w - 1)]: for each row s the
+ *     pairs (t, j) with anc_j(t) = s encoded as 8 t + j, in increasing (j, t).
+ * HARTS_EINVAL if m is not the map of a prefix tree (a row with two different
+ * predecessors), a row is on no trajectory, or w is outside [2, 8].
+ */
+int harts_conv_tables(const int64_t *m, const int64_t *traj_offsets, int64_t n_traj, int64_t C, int32_t w,
+                      int32_t *anc, int64_t *gather_off, int64_t *gather);
+
+/* x: device [C, channels] (dtype bf16 or fp32), rows contiguous, 16-byte aligned;
+ * weight: device float32 [channels, w]; anc: device copy of the table above;
+ * out: device [C, channels], x's dtype, must not overlap x.  channels a
+ * positive multiple of 8.  fp32 accumulation. */
+int harts_conv_fwd(const void *x, const float *weight, const int32_t *anc, int64_t C, int32_t channels, int32_t w,
+                   int32_t dtype, void *out, void *stream);
+
+/* Gradients of L = sum_t <dout[t], out[t]>:
+ *   dx[s, c] = weight[c, 0] dout[s, c] + sum over the gather entries (t, j) of s of weight[c, j] dout[t, c]
+ *   dweight[c, j] = sum_t dout[t, c] x[anc_j(t), c]   (fixed-order block sums)
+ * dx: device [C, channels] in x's dtype, or NULL; dweight: device float32
+ * [channels, w], or NULL (then no workspace is needed).
+ * workspace: device, >= harts_conv_workspace_size(C, channels, w) bytes. */
+size_t harts_conv_workspace_size(int64_t C, int32_t channels, int32_t w);
+int harts_conv_bwd(const void *x, const float *weight, const int32_t *anc, const int64_t *gather_off,
+                   const int64_t *gather, const void *dout, int64_t C, int32_t channels, int32_t w, int32_t dtype,
+                   void *dx, float *dweight, void *workspace, size_t workspace_bytes, void *stream);
+
 /* ---------------------------------------------------------------- kernel timing
  * For benchmarks and profiling.  While enabled, every kernel the library
  * enqueues is bracketed by two HIP events recorded on the same stream (this

@@ -73,3 +73,24 @@ def test_logprob_backward_rejects_bad_arguments_before_any_device_work():
     assert f(None, 4, 8, 0, None, None, None, None, None, 0, None, None) == -1  # missing arrays
     assert b"required" in _lib._last_error()
     assert f(None, 0, 8, 0, None, None, None, None, None, 0, None, None) == 0  # no rows: nothing to do
+
+
+def test_conv_tables_follow_each_trajectory():
+    # trajectories [a b c d e] [a b c f] [a b g h]: rows a..h = 0..7
+    m = np.array([0, 1, 2, 3, 4, 0, 1, 2, 5, 0, 1, 6, 7])
+    off = np.array([0, 5, 9, 13])
+    anc, goff, gl = harts.conv_tables(m, off, 8, 3)
+    want = np.array([[-1, -1], [0, -1], [1, 0], [2, 1], [3, 2], [2, 1], [1, 0], [6, 1]])
+    assert np.array_equal(anc, want)
+    # gather lists: the (t, j) with anc_j(t) = s, increasing (j, t)
+    got = {s: [(int(e) >> 3, int(e) & 7) for e in gl[goff[s]:goff[s + 1]]] for s in range(8)}
+    assert got[1] == [(2, 1), (6, 1), (3, 2), (5, 2), (7, 2)]
+    assert got[0] == [(1, 1), (2, 2), (6, 2)] and got[4] == [] and got[7] == []
+    with pytest.raises(harts.HartsError) as e:  # row 2 preceded by 1 on one trajectory and by 0 on another
+        harts.conv_tables(np.array([0, 1, 2, 0, 2]), np.array([0, 3, 5]), 3, 2)
+    assert "prefix tree" in str(e.value)
+    with pytest.raises(harts.HartsError) as e:
+        harts.conv_tables(np.array([0, 1]), np.array([0, 2]), 3, 2)
+    assert "no trajectory" in str(e.value)
+    with pytest.raises(harts.HartsError):
+        harts.conv_tables(m, off, 8, 9)
