@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--only-logprob", action="store_true",
                     help="only the log-prob gather and its backward (for profiling them alone)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -159,6 +160,45 @@ def cpu_baseline(t, feats, C, S, target_positions=250000, seed=0):
     return {"value": C / full, "unit": "compact tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d trajectories (%d of %d semantic positions, %d heads), forward + reverse pass in "
                       "%.1f s; extrapolated per semantic position" % (len(which), t.n_traj, P, S, H, dt)}
+
+
+def conv_bench(args, out, t, plan, C):
+    """The tree causal convolution of the KDA layer's q, k, v projections (3 H d = 6144 channels,
+    window 4, bf16) over the benchmark tree's compact rows: forward and both gradients, timed with
+    HIP events, into ``out``."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    dev = "cuda"
+    ch, w = 3 * H * D, 4
+    m = np.asarray(plan.maps()[0], np.int64)
+    anc, goff, gl = harts.conv_tables(m, np.asarray(t.offsets, np.int64), C, w)
+    ancd, goffd, gld = (torch.from_numpy(a).to(dev) for a in (anc, goff, gl))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    x = torch.randn((C, ch), generator=gen, device=dev).to(torch.bfloat16)
+    dout = torch.randn((C, ch), generator=gen, device=dev).to(torch.bfloat16)
+    wt = torch.randn((ch, w), generator=gen, device=dev) / w
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dw = torch.empty((ch, w), device=dev)
+    ws = torch.empty(harts.conv_workspace_size(C, ch, w), dtype=torch.uint8, device=dev)
+    reps = max(3, min(args.steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"C": C, "channels": ch, "w": w}
+    for name, fn, by in (("fwd", lambda: harts.conv_fwd(x, wt, ancd, y), 2 * C * ch * 2),
+                         ("bwd", lambda: harts.conv_bwd(x, wt, ancd, goffd, gld, dout, dx=dx, dweight=dw, workspace=ws),
+                          4 * C * ch * 2)):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": ms, "bytes": by, "achieved_gbps": by / (ms / 1e3) / 1e9, "frac_hbm": by / (ms / 1e3) / PEAK_HBM}
+    out["tree_conv"] = res
+    del x, dout, y, dx
 
 
 def logprob_bench(args, out):
@@ -341,6 +381,9 @@ def main():
         "roofline": roof,
         "kernels": kernels,
     }
+    # ---------------------------------------------------------------- tree causal convolution
+    if not args.no_conv:
+        conv_bench(args, out, t, plan, C)
     # ---------------------------------------------------------------- log-prob gather and its backward
     if not args.no_logprob:
         del ws

@@ -783,7 +783,7 @@ size_t harts_conv_workspace_size(int64_t C, int32_t channels, int32_t w) {
 namespace {
 void conv_check(const void* x, int64_t C, int32_t channels, int32_t w, int32_t dtype) {
   if (C < 0) throw Error(HARTS_EINVAL, "need C >= 0");
-  if (C >= (int64_t(1) << 31)) throw Error(HARTS_ERANGE, "C must be < 2^31");
+  if (C > int64_t(65535) * 64) throw Error(HARTS_ERANGE, "C must be <= 65535 * 64 rows");
   if (channels <= 0 || channels % 8) throw Error(HARTS_EINVAL, "channels must be a positive multiple of 8");
   if (w < 2 || w > 8) throw Error(HARTS_EINVAL, "w must be in [2, 8]");
   if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");

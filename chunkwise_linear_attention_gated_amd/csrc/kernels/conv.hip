@@ -9,9 +9,10 @@
 //   dx[s, c]  = weight[c, 0] dout[s, c] + sum_{(t, j): anc_j(t) = s} weight[c, j] dout[t, c]
 //   dweight[c, j] = sum_t dout[t, c] x[anc_j(t), c]
 //
-// Every pass moves 16-byte pieces of 8 channels; dx gathers over a per-row list of (t, j) in a
-// fixed order and dweight sums fixed row blocks, then the blocks in order, so the results do not
-// depend on scheduling.  The windows' reads of earlier rows mostly hit the L2 (rows of one
+// Every pass moves 16-byte pieces of 8 channels, a thread keeping its channels' weights in
+// registers over a block of rows; dx gathers over a per-row list of (t, j) in a fixed order and
+// dweight sums fixed row blocks, then the blocks in order, so the results do not depend on
+// scheduling.  The windows' reads of earlier rows mostly hit the L2 (rows of one
 // branch are contiguous).
 #include "common.h"
 #include "launch.h"
@@ -39,25 +40,61 @@ __device__ __forceinline__ void st8(T* p, const float* v) {
   }
 }
 
+// Forward and dx: grid (channel pieces / 256, row blocks of kConvRows); a thread keeps its 8
+// channels' weights in registers and walks the block's rows, whose ancestor rows and gather
+// lists are uniform over the workgroup (scalar loads).
+constexpr int kConvRows = 64;
+
+template <typename T, int W>
+__device__ __forceinline__ void conv_weights(const float* __restrict__ wt, int c0, float (&wv)[W][8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int j = 0; j < W; ++j) wv[j][e] = wt[(c0 + e) * W + j];
+}
+
 template <typename T, int W>
 __global__ __launch_bounds__(256) void conv_fwd_kernel(const T* __restrict__ x, const float* __restrict__ wt,
                                                        const int32_t* __restrict__ anc, int64_t C, int32_t ch,
                                                        T* __restrict__ out) {
-  const int64_t pieces = C * (ch / 8);
-  for (int64_t p = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; p < pieces; p += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t t = p / (ch / 8);
-    const int c0 = int(p % (ch / 8)) * 8;
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  float wv[W][8];
+  conv_weights<T, W>(wt, c0 < ch ? c0 : 0, wv);
+  const int64_t t0 = int64_t(blockIdx.y) * kConvRows, t1 = t0 + kConvRows < C ? t0 + kConvRows : C;
+  // the block's ancestor rows, staged once
+  __shared__ int32_t sa[kConvRows * (W - 1)];
+  for (int i = threadIdx.x; i < int(t1 - t0) * (W - 1); i += 256) sa[i] = anc[t0 * (W - 1) + i];
+  __syncthreads();
+  if (c0 >= ch) return;
+  // hist[j - 1]: this thread's channels of row t - j, read in an earlier iteration (a branch's
+  // rows are contiguous, so most windows are the previous rows)
+  float hist[W - 1][8];
+  for (int64_t t = t0; t < t1; ++t) {
+    float acc[8], cur[8];
+    ld8<T>(x + t * ch + c0, cur);
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const int64_t r = j == 0 ? t : anc[t * (W - 1) + j - 1];
+    for (int e = 0; e < 8; ++e) acc[e] = wv[0][e] * cur[e];
+#pragma unroll
+    for (int j = 1; j < W; ++j) {
+      const int64_t r = sa[(t - t0) * (W - 1) + j - 1];
       if (r < 0) continue;
       float v[8];
-      ld8<T>(x + r * ch + c0, v);
+      if (r == t - j && t - j >= t0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wt[(c0 + e) * W + j] * v[e];
+        for (int e = 0; e < 8; ++e) v[e] = hist[j - 1][e];
+      } else {
+        ld8<T>(x + r * ch + c0, v);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wv[j][e] * v[e];
     }
     st8<T>(out + t * ch + c0, acc);
+#pragma unroll
+    for (int j = W - 2; j > 0; --j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hist[j][e] = hist[j - 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hist[0][e] = cur[e];
   }
 }
 
@@ -65,22 +102,57 @@ template <typename T, int W>
 __global__ __launch_bounds__(256) void conv_dx_kernel(const T* __restrict__ dout, const float* __restrict__ wt,
                                                       const int64_t* __restrict__ goff, const int64_t* __restrict__ gl,
                                                       int64_t C, int32_t ch, T* __restrict__ dx) {
-  const int64_t pieces = C * (ch / 8);
-  for (int64_t p = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; p < pieces; p += int64_t(gridDim.x) * blockDim.x) {
-    const int64_t s = p / (ch / 8);
-    const int c0 = int(p % (ch / 8)) * 8;
-    float acc[8], v[8];
-    ld8<T>(dout + s * ch + c0, v);
+  constexpr int KG = 4 * kConvRows;  // gather entries staged per block (the rest read from memory)
+  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  float wv[W][8];
+  conv_weights<T, W>(wt, c0 < ch ? c0 : 0, wv);
+  const int64_t s0 = int64_t(blockIdx.y) * kConvRows, s1 = s0 + kConvRows < C ? s0 + kConvRows : C;
+  __shared__ int64_t so[kConvRows + 1], sg[KG];
+  for (int i = threadIdx.x; i <= int(s1 - s0); i += 256) so[i] = goff[s0 + i];
+  __syncthreads();
+  const int64_t g0 = so[0], ng = so[s1 - s0] - g0;
+  for (int i = threadIdx.x; i < (ng < KG ? ng : KG); i += 256) sg[i] = gl[g0 + i];
+  __syncthreads();
+  if (c0 >= ch) return;
+  // rows in reverse; next[j - 1]: this thread's channels of dout[s + j], read in an earlier
+  // iteration (most gather entries of a row are the rows just after it)
+  float next[W - 1][8];
+  for (int64_t s = s1 - 1; s >= s0; --s) {
+    float acc[8], cur[8], v[8];
+    ld8<T>(dout + s * ch + c0, cur);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] = wt[(c0 + e) * W] * v[e];
-    for (int64_t i = goff[s]; i < goff[s + 1]; ++i) {
-      const int64_t t = gl[i] >> 3;
-      const int j = int(gl[i] & 7);
-      ld8<T>(dout + t * ch + c0, v);
+    for (int e = 0; e < 8; ++e) acc[e] = wv[0][e] * cur[e];
+    for (int64_t i = so[s - s0]; i < so[s - s0 + 1]; ++i) {
+      const int64_t ge = i - g0 < KG ? sg[i - g0] : gl[i];
+      const int64_t t = ge >> 3;
+      const int j = int(ge & 7);
+      const int64_t k = t - s;  // in 1 .. W - 1 when t is one of the rows held
+      bool held = false;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += wt[(c0 + e) * W + j] * v[e];
+      for (int q = 1; q < W; ++q)
+        if (k == q && s + q < s1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = next[q - 1][e];
+          held = true;
+        }
+      if (!held) ld8<T>(dout + t * ch + c0, v);
+      float wj[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wj[e] = wv[1][e];
+#pragma unroll
+        for (int q = 2; q < W; ++q) wj[e] = j == q ? wv[q][e] : wj[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += wj[e] * v[e];
     }
     st8<T>(dx + s * ch + c0, acc);
+#pragma unroll
+    for (int q = W - 2; q > 0; --q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) next[q][e] = next[q - 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) next[0][e] = cur[e];
   }
 }
 
@@ -91,25 +163,43 @@ __global__ __launch_bounds__(256) void conv_dw_partial_kernel(const T* __restric
                                                               const int32_t* __restrict__ anc, int64_t C, int32_t ch,
                                                               float* __restrict__ part) {
   const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
-  if (c0 >= ch) return;
   const int64_t t0 = int64_t(blockIdx.y) * kConvRowBlock, t1 = t0 + kConvRowBlock < C ? t0 + kConvRowBlock : C;
+  __shared__ int32_t sa[kConvRowBlock * (W - 1)];
+  for (int i = threadIdx.x; i < int(t1 - t0) * (W - 1); i += 256) sa[i] = anc[t0 * (W - 1) + i];
+  __syncthreads();
+  if (c0 >= ch) return;
   float acc[W][8];
 #pragma unroll
   for (int j = 0; j < W; ++j)
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[j][e] = 0.f;
+  float hist[W - 1][8];  // x of rows t - j read in earlier iterations (as in the forward)
   for (int64_t t = t0; t < t1; ++t) {
-    float g[8];
+    float g[8], cur[8];
     ld8<T>(dout + t * ch + c0, g);
+    ld8<T>(x + t * ch + c0, cur);
 #pragma unroll
-    for (int j = 0; j < W; ++j) {
-      const int64_t r = j == 0 ? t : anc[t * (W - 1) + j - 1];
+    for (int e = 0; e < 8; ++e) acc[0][e] += g[e] * cur[e];
+#pragma unroll
+    for (int j = 1; j < W; ++j) {
+      const int64_t r = sa[(t - t0) * (W - 1) + j - 1];
       if (r < 0) continue;
       float v[8];
-      ld8<T>(x + r * ch + c0, v);
+      if (r == t - j && t - j >= t0) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = hist[j - 1][e];
+      } else {
+        ld8<T>(x + r * ch + c0, v);
+      }
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[j][e] += g[e] * v[e];
     }
+#pragma unroll
+    for (int j = W - 2; j > 0; --j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) hist[j][e] = hist[j - 1][e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hist[0][e] = cur[e];
   }
   float* pb = part + (size_t(blockIdx.y) * ch + c0) * W;
 #pragma unroll
@@ -132,15 +222,14 @@ size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w) {
   return size_t(nblk > 0 ? nblk : 1) * size_t(ch) * size_t(w) * 4;
 }
 
-static unsigned conv_grid(int64_t pieces) {
-  const int64_t b = (pieces + 255) / 256;
-  return unsigned(b < 65536 ? (b > 0 ? b : 1) : 65536);
+static dim3 conv_grid(int64_t C, int32_t ch) {
+  return dim3(unsigned((ch / 8 + 255) / 256), unsigned((C + kConvRows - 1) / kConvRows));
 }
 
 template <typename T, int W>
 static hipError_t conv_fwd_t(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, void* out,
                              hipStream_t s) {
-  hipLaunchKernelGGL((conv_fwd_kernel<T, W>), dim3(conv_grid(C * (ch / 8))), dim3(256), 0, s, static_cast<const T*>(x),
+  hipLaunchKernelGGL((conv_fwd_kernel<T, W>), conv_grid(C, ch), dim3(256), 0, s, static_cast<const T*>(x),
                      wt, anc, C, ch, static_cast<T*>(out));
   return hipGetLastError();
 }
@@ -149,7 +238,7 @@ template <typename T, int W>
 static hipError_t conv_bwd_t(const void* x, const float* wt, const int32_t* anc, const int64_t* goff, const int64_t* gl,
                              const void* dout, int64_t C, int32_t ch, void* dx, float* dw, float* part, hipStream_t s) {
   if (dx)
-    hipLaunchKernelGGL((conv_dx_kernel<T, W>), dim3(conv_grid(C * (ch / 8))), dim3(256), 0, s,
+    hipLaunchKernelGGL((conv_dx_kernel<T, W>), conv_grid(C, ch), dim3(256), 0, s,
                        static_cast<const T*>(dout), wt, goff, gl, C, ch, static_cast<T*>(dx));
   if (dw) {
     const int64_t nblk = (C + kConvRowBlock - 1) / kConvRowBlock;

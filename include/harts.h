@@ -292,7 +292,7 @@ int harts_conv_tables(const int64_t *m, const int64_t *traj_offsets, int64_t n_t
 /* x: device [C, channels] (dtype bf16 or fp32), rows contiguous, 16-byte aligned;
  * weight: device float32 [channels, w]; anc: device copy of the table above;
  * out: device [C, channels], x's dtype, must not overlap x.  channels a
- * positive multiple of 8.  fp32 accumulation. */
+ * positive multiple of 8; C <= 65535 * 64 (HARTS_ERANGE).  fp32 accumulation. */
 int harts_conv_fwd(const void *x, const float *weight, const int32_t *anc, int64_t C, int32_t channels, int32_t w,
                    int32_t dtype, void *out, void *stream);
 
