@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--only-conv", action="store_true",
+                    help="only the tree causal convolution (for profiling it alone)")
     ap.add_argument("--only-logprob", action="store_true",
                     help="only the log-prob gather and its backward (for profiling them alone)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -278,6 +280,13 @@ def main():
     if args.only_logprob:
         out = {}
         logprob_bench(args, out)
+        print(json.dumps(out))
+        return
+    if args.only_conv:
+        t = trees.random_rollout_tree(seed=args.seed)
+        plan = harts.TreePlan(t.tokens, t.offsets, B)
+        out = {}
+        conv_bench(args, out, t, plan, plan.info.C)
         print(json.dumps(out))
         return
 
