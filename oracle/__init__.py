@@ -23,6 +23,9 @@ Contents, each written from the pages (HARTS, arXiv 2608.28158):
   counts.
 * ``oracle.conv``      -- float64 depthwise causal convolution over each
   trajectory's own tokens (ancestor context), and its gradients.
+* ``oracle.attention`` -- float64 softmax attention of every compact row over
+  its own root-to-row path (the tree form of the MLA layer's ancestor-KV
+  views with bottom-right causal alignment), and its gradients.
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force or a library routine.
