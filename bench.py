@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--only-conv", action="store_true",
                     help="only the tree causal convolution (for profiling it alone)")
+    ap.add_argument("--no-attn", action="store_true")
+    ap.add_argument("--only-attn", action="store_true",
+                    help="only the tree softmax attention (for profiling it alone)")
     ap.add_argument("--only-logprob", action="store_true",
                     help="only the log-prob gather and its backward (for profiling them alone)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -203,6 +206,51 @@ def conv_bench(args, out, t, plan, C):
     del x, dout, y, dx
 
 
+def attn_bench(args, out, t, plan, C):
+    """Tree softmax attention of the full-attention (MLA) layer over the benchmark tree's compact
+    rows: 16 heads, q/k head dim 192 (128 + 64 rotary), v head dim 128, bf16.  Forward and
+    backward timed with HIP events; algorithmic flops count only the visible (query, key) pairs:
+    forward 2 (dqk + dv), backward 2 (3 dqk + 2 dv) per pair and head."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    dev = "cuda"
+    Ha, dqk, dv = 16, 192, 128
+    m = np.asarray(plan.maps()[0], np.int64)
+    tb = harts.attn_tables(m, np.asarray(t.offsets, np.int64), C)
+    qt, kv, kt, ql = (torch.from_numpy(tb[k]).to(dev) for k in ("qtiles", "kv_list", "ktiles", "q_list"))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    mk = lambda d: torch.randn((C, Ha, d), generator=gen, device=dev).to(torch.bfloat16)
+    q, k, v, do = mk(dqk), mk(dqk), mk(dv), mk(dv)
+    o = torch.empty_like(v)
+    lse = torch.empty((C, Ha), device=dev)
+    dq, dk, dvv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(harts.attn_workspace_size(C, Ha), dtype=torch.uint8, device=dev)
+    scale = dqk ** -0.5
+    pairs = tb["info"]["pairs"]
+    reps = max(3, min(args.steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"C": C, "H": Ha, "dqk": dqk, "dv": dv, "pairs_per_head": pairs, "max_depth": tb["info"]["max_depth"],
+           "n_segments": tb["info"]["n_segments"]}
+    for name, fn, fl in (("fwd", lambda: harts.attn_fwd(q, k, v, qt, kv, scale, o, lse), 2 * (dqk + dv)),
+                         ("bwd", lambda: harts.attn_bwd(q, k, v, o, lse, do, qt, kv, kt, ql, scale, dq, dk, dvv, ws),
+                          2 * (3 * dqk + 2 * dv))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = fl * pairs * Ha
+        res[name] = {"ms": ms, "flops": flops, "tflops": flops / (ms / 1e3) / 1e12,
+                     "frac_mfma": flops / (ms / 1e3) / PEAK_BF16}
+    out["tree_attention"] = res
+    del q, k, v, do, o, dq, dk, dvv
+
+
 def logprob_bench(args, out):
     """The log-prob workload (32768 compact rows x 131072 bf16 logits): forward gather and its
     backward, each timed with HIP events, into ``out``."""
@@ -280,6 +328,13 @@ def main():
     if args.only_logprob:
         out = {}
         logprob_bench(args, out)
+        print(json.dumps(out))
+        return
+    if args.only_attn:
+        t = trees.random_rollout_tree(seed=args.seed)
+        plan = harts.TreePlan(t.tokens, t.offsets, B)
+        out = {}
+        attn_bench(args, out, t, plan, plan.info.C)
         print(json.dumps(out))
         return
     if args.only_conv:
@@ -393,6 +448,9 @@ def main():
     # ---------------------------------------------------------------- tree causal convolution
     if not args.no_conv:
         conv_bench(args, out, t, plan, C)
+    # ---------------------------------------------------------------- tree softmax attention
+    if not args.no_attn:
+        attn_bench(args, out, t, plan, C)
     # ---------------------------------------------------------------- log-prob gather and its backward
     if not args.no_logprob:
         del ws

@@ -92,6 +92,14 @@ _lp_rows = _sig("harts_logprob_rows", I32, P, I64, I64, P, P)
 _conv_tables = _sig("harts_conv_tables", I32, P, P, I64, I64, I32, P, P, P)
 _conv_ws = _sig("harts_conv_workspace_size", ctypes.c_size_t, I64, I32, I32)
 _conv_fwd = _sig("harts_conv_fwd", I32, P, P, P, I64, I32, I32, I32, P, P)
+_attn_build = _sig("harts_attn_tables_build", I32, P, P, I64, I64, ctypes.POINTER(P))
+_attn_info = _sig("harts_attn_info", I32, P, P)
+_attn_copy = _sig("harts_attn_tables_copy", I32, P, P, P, P, P, P)
+_attn_free = _sig("harts_attn_tables_free", None, P)
+_attn_ws = _sig("harts_attn_workspace_size", ctypes.c_size_t, I64, I32)
+_attn_fwd = _sig("harts_attn_fwd", I32, P, P, P, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P)
+_attn_bwd = _sig("harts_attn_bwd", I32, P, P, P, P, P, P, P, I64, P, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
+                 P, P, P, P, ctypes.c_size_t, P)
 _conv_bwd = _sig("harts_conv_bwd", I32, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P, ctypes.c_size_t, P)
 _prof_enable = _sig("harts_profile_enable", I32, I32)
 _prof_collect = _sig("harts_profile_collect", I32, P, I32, P)
@@ -339,6 +347,68 @@ def conv_bwd(x, weight, anc, gather_off, gather, dout, dx=None, dweight=None, wo
     _check(_conv_bwd(_ptr(x), _ptr(weight), _ptr(anc), _ptr(gather_off), _ptr(gather), _ptr(dout), C, ch,
                      weight.shape[1], _act_dtype(x), _ptr(dx), _ptr(dweight), _ptr(workspace), ws_bytes,
                      _stream(stream)))
+
+
+class AttnInfo(ctypes.Structure):
+    _fields_ = [("C", I64), ("n_segments", I64), ("n_qtiles", I64), ("n_ktiles", I64), ("kv_list_len", I64),
+                ("q_list_len", I64), ("pairs", I64), ("max_depth", I32)]
+
+
+def attn_tables(m, traj_offsets, C: int):
+    """harts_attn_tables_build + harts_attn_tables_copy (host): the tree-attention tiles and
+    row lists as numpy int32 arrays {qtiles [n, 4], kv_list, ktiles [n, 4], q_list, pos [C]}
+    plus the table sizes ("info", a dict)."""
+    m = np.ascontiguousarray(m, dtype=np.int64)
+    off = np.ascontiguousarray(traj_offsets, dtype=np.int64)
+    h = P()
+    _check(_attn_build(m.ctypes.data, off.ctypes.data, off.shape[0] - 1, C, ctypes.byref(h)))
+    try:
+        info = AttnInfo()
+        _check(_attn_info(h, ctypes.byref(info)))
+        out = {
+            "qtiles": np.empty((info.n_qtiles, 4), dtype=np.int32),
+            "kv_list": np.empty(max(1, info.kv_list_len), dtype=np.int32),
+            "ktiles": np.empty((info.n_ktiles, 4), dtype=np.int32),
+            "q_list": np.empty(max(1, info.q_list_len), dtype=np.int32),
+            "pos": np.empty(max(1, C), dtype=np.int32),
+        }
+        _check(_attn_copy(h, *(out[k].ctypes.data for k in ("qtiles", "kv_list", "ktiles", "q_list", "pos"))))
+    finally:
+        _attn_free(h)
+    out["pos"] = out["pos"][:C]
+    out["info"] = {f: getattr(info, f) for f, _ in AttnInfo._fields_}
+    return out
+
+
+def attn_workspace_size(C: int, H: int) -> int:
+    return int(_attn_ws(C, H))
+
+
+def _bf16(*xs):
+    import torch
+    for x in xs:
+        if x.dtype != torch.bfloat16 or not x.is_contiguous():
+            raise HartsError(-1, "attention operands must be contiguous bf16")
+
+
+def attn_fwd(q, k, v, qtiles, kv_list, scale: float, o, lse, stream=None):
+    """harts_attn_fwd: o[t] = softmax over the rows of t's root path of scale <q[t], k[a]>, times v;
+    lse[t] its natural-log denominator.  q, k: [C, H, dqk]; v, o: [C, H, dv] bf16."""
+    _bf16(q, k, v, o)
+    C, H, dqk = q.shape
+    _check(_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(qtiles), qtiles.shape[0], _ptr(kv_list), C, H, dqk,
+                     v.shape[2], float(scale), _ptr(o), _ptr(lse), _stream(stream)))
+
+
+def attn_bwd(q, k, v, o, lse, dout, qtiles, kv_list, ktiles, q_list, scale: float, dq, dk, dv, workspace,
+             stream=None):
+    """harts_attn_bwd: dq, dk, dv of sum_t <dout[t], o[t]>."""
+    _bf16(q, k, v, o, dout, dq, dk, dv)
+    C, H, dqk = q.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(qtiles), qtiles.shape[0],
+                     _ptr(kv_list), _ptr(ktiles), ktiles.shape[0], _ptr(q_list), C, H, dqk, v.shape[2],
+                     float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
 
 
 def profile_enable(on: bool = True):

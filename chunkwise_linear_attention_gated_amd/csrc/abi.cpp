@@ -13,11 +13,15 @@
 #include <vector>
 
 #include "../../include/harts.h"
+#include "host/attn_tables.hpp"
 #include "host/plan.hpp"
 #include "kernels/launch.h"
 
 using harts::Error;
 
+struct harts_attn_tables {
+  harts::AttnTables t;
+};
 struct harts_tree {
   harts::TreeHost t;
 };
@@ -822,6 +826,158 @@ int harts_conv_bwd(const void* x, const float* weight, const int32_t* anc, const
     hip_check(harts::launch_conv_bwd(x, weight, anc, gather_off, gather, dout, C, channels, w, dtype, dx, dweight,
                                      static_cast<float*>(workspace), static_cast<hipStream_t>(stream)),
               "convolution gradient kernel launch");
+  });
+}
+
+int harts_attn_tables_build(const int64_t* m, const int64_t* traj_offsets, int64_t n_traj, int64_t C,
+                            harts_attn_tables** out) {
+  return guarded([&] {
+    if (!out) throw Error(HARTS_EINVAL, "out is NULL");
+    *out = nullptr;
+    auto* t = new harts_attn_tables{harts::build_attn_tables(m, traj_offsets, n_traj, C)};
+    *out = t;
+  });
+}
+
+int harts_attn_info(const harts_attn_tables* t, harts_attn_info_t* info) {
+  return guarded([&] {
+    if (!t || !info) throw Error(HARTS_EINVAL, "NULL argument");
+    info->C = t->t.C;
+    info->n_segments = t->t.n_segments;
+    info->n_qtiles = int64_t(t->t.qtiles.size() / 4);
+    info->n_ktiles = int64_t(t->t.ktiles.size() / 4);
+    info->kv_list_len = int64_t(t->t.kv_list.size());
+    info->q_list_len = int64_t(t->t.q_list.size());
+    info->pairs = t->t.pairs;
+    info->max_depth = t->t.max_depth;
+  });
+}
+
+int harts_attn_tables_copy(const harts_attn_tables* t, int32_t* qtiles, int32_t* kv_list, int32_t* ktiles,
+                           int32_t* q_list, int32_t* pos) {
+  return guarded([&] {
+    if (!t) throw Error(HARTS_EINVAL, "NULL tables");
+    auto cp = [](const std::vector<int32_t>& v, int32_t* dst) {
+      if (!v.empty()) {
+        if (!dst) throw Error(HARTS_EINVAL, "missing output array");
+        std::memcpy(dst, v.data(), v.size() * sizeof(int32_t));
+      }
+    };
+    cp(t->t.qtiles, qtiles);
+    cp(t->t.kv_list, kv_list);
+    cp(t->t.ktiles, ktiles);
+    cp(t->t.q_list, q_list);
+    if (pos) std::copy(t->t.pos.begin(), t->t.pos.end(), pos);
+  });
+}
+
+void harts_attn_tables_free(harts_attn_tables* t) { delete t; }
+
+size_t harts_attn_workspace_size(int64_t C, int32_t H) { return C > 0 && H > 0 ? align256(size_t(C) * H * 4) : 256; }
+
+namespace {
+void attn_check(const void* q, const void* k, const void* v, const int32_t* tiles, int64_t n_tiles,
+                const int32_t* list, int64_t C, int32_t H, int32_t dqk, int32_t dv) {
+  if (C < 0 || H <= 0 || n_tiles < 0) throw Error(HARTS_EINVAL, "need C >= 0, H > 0, n_tiles >= 0");
+  if (C > INT32_MAX) throw Error(HARTS_ERANGE, "C must fit int32 row indices");
+  if (!harts::attn_dims_supported(dqk, dv))
+    throw Error(HARTS_EINVAL, "(dqk, dv) must be (192, 128), (128, 128) or (64, 64)");
+  if (n_tiles * int64_t(H) > INT32_MAX) throw Error(HARTS_ERANGE, "too many tiles x heads for one grid");
+  if (C > 0 && n_tiles == 0) throw Error(HARTS_EINVAL, "no tiles for a non-empty set of rows");
+  for (const void* p : {q, k, v})
+    if (C > 0 && (!p || reinterpret_cast<uintptr_t>(p) % 16)) throw Error(HARTS_EINVAL, "q, k, v must be 16-byte aligned");
+  if (n_tiles > 0 && (!tiles || !list || reinterpret_cast<uintptr_t>(tiles) % 16))
+    throw Error(HARTS_EINVAL, "tiles (16-byte aligned) and list are required");
+}
+void no_overlap(const void* a, size_t na, const void* b, size_t nb, const char* what) {
+  const char *x = static_cast<const char*>(a), *y = static_cast<const char*>(b);
+  if (x < y + nb && y < x + na) throw Error(HARTS_EINVAL, what);
+}
+}  // namespace
+
+int harts_attn_fwd(const void* q, const void* k, const void* v, const int32_t* qtiles, int64_t n_qtiles,
+                   const int32_t* kv_list, int64_t C, int32_t H, int32_t dqk, int32_t dv, float scale, void* o,
+                   float* lse, void* stream) {
+  return guarded([&] {
+    attn_check(q, k, v, qtiles, n_qtiles, kv_list, C, H, dqk, dv);
+    if (C == 0) return;
+    if (!o || !lse || reinterpret_cast<uintptr_t>(o) % 16) throw Error(HARTS_EINVAL, "o (16-byte aligned) and lse are required");
+    const size_t no = size_t(C) * H * dv * 2, nq = size_t(C) * H * dqk * 2;
+    no_overlap(o, no, q, nq, "o overlaps q");
+    no_overlap(o, no, k, nq, "o overlaps k");
+    no_overlap(o, no, v, no, "o overlaps v");
+    harts::AttnArgs a{};
+    a.q = static_cast<const __bf16*>(q);
+    a.k = static_cast<const __bf16*>(k);
+    a.v = static_cast<const __bf16*>(v);
+    a.tiles = qtiles;
+    a.list = kv_list;
+    a.o_out = static_cast<__bf16*>(o);
+    a.lse_out = lse;
+    a.C = C;
+    a.H = H;
+    a.scale = scale;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope ps("attn_fwd", s, C);
+    hip_check(harts::launch_attn(0, a, n_qtiles, dqk, dv, s), "attention forward launch");
+  });
+}
+
+int harts_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                   const int32_t* qtiles, int64_t n_qtiles, const int32_t* kv_list, const int32_t* ktiles,
+                   int64_t n_ktiles, const int32_t* q_list, int64_t C, int32_t H, int32_t dqk, int32_t dv,
+                   float scale, void* dq, void* dk, void* dv_out, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return guarded([&] {
+    attn_check(q, k, v, qtiles, n_qtiles, kv_list, C, H, dqk, dv);
+    attn_check(q, k, v, ktiles, n_ktiles, q_list, C, H, dqk, dv);
+    if (C == 0) return;
+    for (const void* p : {o, dout, static_cast<const void*>(dq), static_cast<const void*>(dk), static_cast<const void*>(dv_out)})
+      if (!p || reinterpret_cast<uintptr_t>(p) % 16) throw Error(HARTS_EINVAL, "o, dout, dq, dk, dv must be 16-byte aligned");
+    if (!lse) throw Error(HARTS_EINVAL, "lse is required");
+    if (!workspace || workspace_bytes < size_t(C) * H * 4)
+      throw Error(HARTS_EINVAL, "workspace must hold harts_attn_workspace_size bytes");
+    const size_t nqb = size_t(C) * H * dqk * 2, nvb = size_t(C) * H * dv * 2;
+    const void* ins[] = {q, k, v, o, dout};
+    const size_t insz[] = {nqb, nqb, nvb, nvb, nvb};
+    const void* outs[] = {dq, dk, dv_out};
+    const size_t outsz[] = {nqb, nqb, nvb};
+    for (int i = 0; i < 3; ++i) {
+      for (int j = 0; j < 5; ++j) no_overlap(outs[i], outsz[i], ins[j], insz[j], "a gradient overlaps an input");
+      for (int j = 0; j < i; ++j) no_overlap(outs[i], outsz[i], outs[j], outsz[j], "gradients overlap");
+    }
+    harts::AttnArgs a{};
+    a.q = static_cast<const __bf16*>(q);
+    a.k = static_cast<const __bf16*>(k);
+    a.v = static_cast<const __bf16*>(v);
+    a.o = static_cast<const __bf16*>(o);
+    a.dout = static_cast<const __bf16*>(dout);
+    a.lse = lse;
+    a.delta = static_cast<const float*>(workspace);
+    a.delta_out = static_cast<float*>(workspace);
+    a.dq = static_cast<__bf16*>(dq);
+    a.dk = static_cast<__bf16*>(dk);
+    a.dv = static_cast<__bf16*>(dv_out);
+    a.C = C;
+    a.H = H;
+    a.scale = scale;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    {
+      ProfScope ps("attn_delta", s, C);
+      hip_check(harts::launch_attn(1, a, 0, dqk, dv, s), "attention delta launch");
+    }
+    {
+      a.tiles = qtiles;
+      a.list = kv_list;
+      ProfScope ps("attn_dq", s, C);
+      hip_check(harts::launch_attn(2, a, n_qtiles, dqk, dv, s), "attention dq launch");
+    }
+    {
+      a.tiles = ktiles;
+      a.list = q_list;
+      ProfScope ps("attn_dkv", s, C);
+      hip_check(harts::launch_attn(3, a, n_ktiles, dqk, dv, s), "attention dk/dv launch");
+    }
   });
 }
 

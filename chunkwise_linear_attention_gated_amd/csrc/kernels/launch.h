@@ -104,6 +104,20 @@ bool kda_supported(const KdaDims& d);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
                           int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
+// Tree softmax attention (attn.hip).  which: 0 forward, 1 delta = <dout, o>, 2 dq, 3 dk and dv.
+struct AttnArgs {
+  const __bf16 *q, *k, *v, *o, *dout;
+  const float *lse, *delta;
+  const int32_t *tiles, *list;  // query tiles + kv lists (0, 2) or key tiles + q lists (3)
+  __bf16 *o_out, *dq, *dk, *dv;
+  float *lse_out, *delta_out;
+  int64_t C;
+  int32_t H;
+  float scale;
+};
+bool attn_dims_supported(int dqk, int dv);
+hipError_t launch_attn(int which, const AttnArgs& a, int64_t n_tiles, int dqk, int dv, hipStream_t s);
+
 size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w);
 hipError_t launch_conv_fwd(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, int32_t w,
                            int dtype, void* out, hipStream_t s);

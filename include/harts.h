@@ -307,6 +307,68 @@ int harts_conv_bwd(const void *x, const float *weight, const int32_t *anc, const
                    const int64_t *gather, const void *dout, int64_t C, int32_t channels, int32_t w, int32_t dtype,
                    void *dx, float *dweight, void *workspace, size_t workspace_bytes, void *stream);
 
+/* ---------------------------------------------------------------- tree attention
+ * Softmax attention of the hybrid model's full-attention (MLA) layer on compact
+ * rows (HARTS, section 4 "MLA execution"; blog section 4.3, MLA paragraph;
+ * Figure C.1(c)): a branch's queries read the keys and values of its ancestor
+ * prefix and its own earlier rows (bottom-right causal alignment), so a compact
+ * row t attends over the rows of its root-to-t path, t included:
+ *   o[t, h] = sum_{a in path(t)} softmax_a(scale <q[t, h], k[a, h]>) v[a, h]
+ * The ancestor view is read through row-index lists; no key or value row is
+ * copied.
+ *
+ * Host: harts_attn_tables_build derives the paths from m (host int64 [S],
+ * semantic -> compact) and the trajectory offsets (host int64 [n_traj + 1]),
+ * cuts the rows into fork-free segments and those into tiles of 64 rows.
+ * harts_attn_tables_copy fills caller arrays (sizes from harts_attn_info):
+ *   qtiles  int32 [n_qtiles][4]   {row0, n, off, base}: query rows row0..row0+n-1,
+ *           keys kv_list[off + v] for v < base + n; query row0 + i sees v iff v <= base + i
+ *   kv_list int32 [kv_list_len]   per segment: ancestor rows (root first), own rows
+ *   ktiles  int32 [n_ktiles][4]   {row0, n, off, nq}: key rows row0..row0+n-1,
+ *           queries q_list[off + u] for u < nq; key row0 + j is seen by u iff u >= j
+ *   q_list  int32 [q_list_len]    per segment: own rows, rows of every segment below
+ *   pos     int32 [C]             position of the row on its trajectories (the RoPE
+ *                                 position id of the row), may be NULL
+ * Tiles come longest first.  HARTS_EINVAL if m is not the map of a prefix tree
+ * (a row with two different prefixes) or a row is on no trajectory; HARTS_ERANGE
+ * if a list outgrows int32 offsets. */
+typedef struct harts_attn_tables harts_attn_tables;
+typedef struct {
+  int64_t C, n_segments, n_qtiles, n_ktiles, kv_list_len, q_list_len;
+  int64_t pairs;     /* sum over rows of the path length: visible (query, key) pairs per head */
+  int32_t max_depth; /* longest path */
+} harts_attn_info_t;
+int harts_attn_tables_build(const int64_t *m, const int64_t *traj_offsets, int64_t n_traj, int64_t C,
+                            harts_attn_tables **out);
+int harts_attn_info(const harts_attn_tables *t, harts_attn_info_t *info);
+int harts_attn_tables_copy(const harts_attn_tables *t, int32_t *qtiles, int32_t *kv_list, int32_t *ktiles,
+                           int32_t *q_list, int32_t *pos);
+void harts_attn_tables_free(harts_attn_tables *t);
+
+/* Forward.  q, k: device bf16 [C, H, dqk]; v: device bf16 [C, H, dv]; rows
+ * contiguous, 16-byte aligned; (dqk, dv) in {(192, 128), (128, 128), (64, 64)}.
+ * qtiles / kv_list: device copies of the tables above.  Outputs: o device bf16
+ * [C, H, dv] (must not overlap the inputs); lse device float32 [C, H], the natural
+ * log of each softmax denominator (needed by the backward).  P is rounded to bf16
+ * for the value product; fp32 accumulation. */
+int harts_attn_fwd(const void *q, const void *k, const void *v, const int32_t *qtiles, int64_t n_qtiles,
+                   const int32_t *kv_list, int64_t C, int32_t H, int32_t dqk, int32_t dv, float scale, void *o,
+                   float *lse, void *stream);
+
+/* Gradients of L = sum_t <dout[t], o[t]> (each compact row counted once):
+ *   dq[t] = scale sum_a ds[t, a] k[a],  dk[a] = scale sum_t ds[t, a] q[t],
+ *   dv[a] = sum_t p[t, a] dout[t],  ds = p (dout v^T - <dout[t], o[t]>)
+ * o, lse: the forward's outputs; dout: device bf16 [C, H, dv]; dq, dk, dv_out:
+ * device bf16, shapes of q, k, v (each row written once, no accumulation);
+ * workspace: device, >= harts_attn_workspace_size(C, H) bytes.  dq is computed
+ * by query tiles, dk and dv by key tiles: no atomics, deterministic. */
+size_t harts_attn_workspace_size(int64_t C, int32_t H);
+int harts_attn_bwd(const void *q, const void *k, const void *v, const void *o, const float *lse, const void *dout,
+                   const int32_t *qtiles, int64_t n_qtiles, const int32_t *kv_list, const int32_t *ktiles,
+                   int64_t n_ktiles, const int32_t *q_list, int64_t C, int32_t H, int32_t dqk, int32_t dv,
+                   float scale, void *dq, void *dk, void *dv_out, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
 /* ---------------------------------------------------------------- kernel timing
  * For benchmarks and profiling.  While enabled, every kernel the library
  * enqueues is bracketed by two HIP events recorded on the same stream (this

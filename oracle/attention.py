@@ -25,25 +25,59 @@ from __future__ import annotations
 import numpy as np
 
 
-def paths(m, offsets, C):
-    """For every compact row, the rows of its root-to-row path (root first, the row last),
-    taken from a trajectory through it; checks that every trajectory through a row gives the
-    same path (m is the map of a prefix tree)."""
+def parent_rows(m, offsets, C):
+    """For every compact row, the row of the token before it on its trajectories (-1 for a
+    first token); checks that every trajectory through a row agrees (m is the map of a prefix
+    tree) and that every row is on some trajectory."""
     m = np.asarray(m, dtype=np.int64)
-    out = [None] * C
+    parent = np.full(C, -2, dtype=np.int64)
+    depth = np.full(C, -1, dtype=np.int64)
     for tr in range(len(offsets) - 1):
         rows = m[offsets[tr]:offsets[tr + 1]]
         for p in range(len(rows)):
             t = int(rows[p])
-            path = rows[:p + 1]
-            if out[t] is None:
-                out[t] = path.copy()
-            elif len(out[t]) != len(path) or np.any(out[t] != path):
+            a = int(rows[p - 1]) if p else -1
+            if parent[t] == -2:
+                parent[t], depth[t] = a, p
+            elif parent[t] != a or depth[t] != p:
                 raise ValueError(f"row {t} has two different prefixes: not a prefix tree")
-    for t in range(C):
-        if out[t] is None:
-            raise ValueError(f"row {t} is on no trajectory")
-    return out
+    if (parent == -2).any():
+        raise ValueError(f"row {int(np.argmax(parent == -2))} is on no trajectory")
+    return parent
+
+
+def path_of(parent, t):
+    """Rows of the root-to-t path, root first, t last."""
+    out = []
+    while t >= 0:
+        out.append(t)
+        t = int(parent[t])
+    return np.array(out[::-1], dtype=np.int64)
+
+
+def paths(m, offsets, C):
+    """For every compact row, the rows of its root-to-row path (root first, the row last)."""
+    parent = parent_rows(m, offsets, C)
+    return [path_of(parent, t) for t in range(C)]
+
+
+def row_terms(q, k, v, dout, path, t, h, scale):
+    """One query row t of head h over its path (row indices, root first), float64:
+    (o [Dv], lse, p [len(path)], ds [len(path)]); ds is None when dout is None.  The
+    per-key gradient terms are dk[a] += scale ds[a] q[t] and dv[a] += p[a] dout[t]."""
+    qt = np.asarray(q[t, h], dtype=np.float64)
+    ka = np.asarray(k[path, h], dtype=np.float64)
+    va = np.asarray(v[path, h], dtype=np.float64)
+    s = scale * (ka @ qt)
+    mx = s.max()
+    e = np.exp(s - mx)
+    p = e / e.sum()
+    o = p @ va
+    ds = None
+    if dout is not None:
+        g = np.asarray(dout[t, h], dtype=np.float64)
+        ds = p * (va @ g - g @ o)
+    return o, mx + np.log(e.sum()), p, ds
 
 
 def attention_forward(q, k, v, m, offsets, scale):

@@ -9,6 +9,7 @@ import pytest
 
 import chunkwise_linear_attention_gated_amd as harts
 from chunkwise_linear_attention_gated_amd import _lib
+from synthetic import trees
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -94,3 +95,59 @@ def test_conv_tables_follow_each_trajectory():
     assert "no trajectory" in str(e.value)
     with pytest.raises(harts.HartsError):
         harts.conv_tables(m, off, 8, 9)
+
+
+def _attn_check_tables(m, off, C):
+    from oracle import attention as oatt
+    tb = harts.attn_tables(m, off, C)
+    P = oatt.paths(m, off, C)
+    qt, kv, kt, ql = tb["qtiles"], tb["kv_list"], tb["ktiles"], tb["q_list"]
+    seen_q = np.zeros(C, np.int64)
+    for row0, n, o, base in qt:
+        assert 1 <= n <= 64
+        for i in range(n):
+            seen_q[row0 + i] += 1
+            assert list(kv[o:o + base + i + 1]) == list(P[row0 + i])  # the path, root first
+    assert (seen_q == 1).all()
+    lens = qt[:, 3] + qt[:, 1]
+    assert (np.diff(lens) <= 0).all()  # longest first
+    readers = {a: set() for a in range(C)}
+    for t in range(C):
+        for a in P[t]:
+            readers[int(a)].add(t)
+    seen_k = np.zeros(C, np.int64)
+    for row0, n, o, nq in kt:
+        for j in range(n):
+            seen_k[row0 + j] += 1
+            got = list(ql[o + j:o + nq])
+            assert len(got) == len(set(got)) and set(got) == readers[row0 + j]
+    assert (seen_k == 1).all()
+    assert (np.diff(kt[:, 3]) <= 0).all()
+    assert tb["info"]["pairs"] == sum(len(p) for p in P)
+    assert list(tb["pos"]) == [len(p) - 1 for p in P]
+    return tb
+
+
+def test_attn_tables_are_the_root_paths():
+    m, off, C = np.array([0, 1, 2, 3, 4, 0, 1, 2, 5, 0, 1, 6, 7]), np.array([0, 5, 9, 13]), 8
+    tb = _attn_check_tables(m, off, C)
+    assert tb["info"]["n_segments"] == 5  # a b | c | d e | f | g h
+    rng = np.random.default_rng(11)
+    for i in range(6):
+        t = trees.random_small_tree(rng, max_segments=9, max_len=150, forest=i % 2 == 1)
+        hp = harts.TreePlan(t.tokens, t.offsets, 64)
+        _attn_check_tables(np.asarray(hp.maps()[0], np.int64), np.asarray(t.offsets, np.int64), hp.info.C)
+    with pytest.raises(harts.HartsError) as e:
+        harts.attn_tables(np.array([0, 1, 2, 0, 2]), np.array([0, 3, 5]), 3)
+    assert "prefix tree" in str(e.value)
+    with pytest.raises(harts.HartsError) as e:
+        harts.attn_tables(np.array([0, 1]), np.array([0, 2]), 3)
+    assert "no trajectory" in str(e.value)
+
+
+def test_attn_entry_points_reject_bad_arguments():
+    f = harts._lib._attn_fwd
+    # unsupported head dims, before any device pointer is touched
+    assert f(None, None, None, None, 0, None, 0, 2, 96, 64, 1.0, None, None, None) == -1
+    assert f(None, None, None, None, 0, None, 0, 2, 64, 64, 1.0, None, None, None) == 0  # no rows: nothing to do
+    assert f(None, None, None, None, 0, None, 4, 2, 64, 64, 1.0, None, None, None) < 0  # rows but no tiles

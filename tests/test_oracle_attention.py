@@ -109,3 +109,31 @@ def test_rejects_a_row_with_two_prefixes():
         att.paths(np.array([0, 1, 2, 1]), np.array([0, 2, 4]), 3)
     with pytest.raises(ValueError):
         att.paths(np.array([0, 1]), np.array([0, 2]), 3)
+
+
+def test_row_terms_assemble_the_library_gradients():
+    m, off, C = _tree()
+    H, dqk, dv, scale = 2, 4, 3, 0.9
+    q, k, v = _inputs(C, H, dqk, dv, 9)
+    dout = np.random.default_rng(10).standard_normal((C, H, dv))
+    P = att.paths(m, off, C)
+    o = np.zeros((C, H, dv))
+    dq, dk, dvv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for t in range(C):
+        for h in range(H):
+            o[t, h], _, p, ds = att.row_terms(q, k, v, dout, P[t], t, h, scale)
+            dq[t, h] = scale * ds @ k[P[t], h]
+            for a, pa, dsa in zip(P[t], p, ds):
+                dk[a, h] += scale * dsa * q[t, h]
+                dvv[a, h] += pa * dout[t, h]
+    qc = np.bincount(m, minlength=C).astype(np.float64)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    loss = 0
+    for tr in range(len(off) - 1):
+        rows = torch.from_numpy(m[off[tr]:off[tr + 1]])
+        out = _sdpa(tq[rows], tk[rows], tv[rows], scale)
+        np.testing.assert_allclose(o[rows.numpy()], out.detach().numpy(), rtol=0, atol=1e-12)
+        loss = loss + (out * torch.from_numpy(dout)[rows] / torch.from_numpy(qc)[rows][:, None, None]).sum()
+    loss.backward()
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dvv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=0, atol=1e-11)
