@@ -26,6 +26,9 @@ Contents, each written from the pages (HARTS, arXiv 2608.28158):
 * ``oracle.attention`` -- float64 softmax attention of every compact row over
   its own root-to-row path (the tree form of the MLA layer's ancestor-KV
   views with bottom-right causal alignment), and its gradients.
+* ``oracle.moe``      -- float64 router statistics of compact rows weighted by
+  their multiplicities (z-loss, load-balance mass and top-k counts, bias
+  update) and the logits' gradient.
 
 Parity status: every function above is pinned by ``tests/test_oracle_*.py``
 against closed forms, invariants, brute force or a library routine.
