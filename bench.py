@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-attn", action="store_true")
     ap.add_argument("--only-attn", action="store_true",
                     help="only the tree softmax attention (for profiling it alone)")
+    ap.add_argument("--no-moe", action="store_true")
+    ap.add_argument("--only-moe", action="store_true",
+                    help="only the router statistics (for profiling them alone)")
     ap.add_argument("--only-logprob", action="store_true",
                     help="only the log-prob gather and its backward (for profiling them alone)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -251,6 +254,48 @@ def attn_bench(args, out, t, plan, C):
     del q, k, v, do, o, dq, dk, dvv
 
 
+def moe_bench(args, out, plan, C):
+    """Multiplicity-weighted router statistics of the benchmark tree's compact rows: 128 experts,
+    top-8, fp32 router logits; statistics and the logits' gradient timed with HIP events.
+    Algorithmic bytes: statistics read the logits and q and write top-k and lse (C (4E + 4 + 4k + 4));
+    the gradient reads the logits and q and writes the gradient (C (8E + 4))."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    dev = "cuda"
+    E, k = 128, 8
+    m = np.asarray(plan.maps()[0], np.int64)
+    q = torch.from_numpy(np.bincount(m, minlength=C).astype(np.int32)).to(dev)
+    S = len(m)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed)
+    z = torch.randn((C, E), generator=gen, device=dev) * 2.0
+    bias = torch.randn((E,), generator=gen, device=dev) * 0.01
+    top = torch.empty((C, k), dtype=torch.int32, device=dev)
+    lse = torch.empty((C,), device=dev)
+    counts = torch.empty((E,), dtype=torch.int32, device=dev)
+    mass = torch.empty((E,), device=dev)
+    losses = torch.empty((2,), device=dev)
+    dz = torch.empty_like(z)
+    ws = torch.empty(harts.moe_workspace_size(C, E), dtype=torch.uint8, device=dev)
+    reps = max(3, min(args.steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = {"C": C, "S": S, "E": E, "k": k}
+    for name, fn, by in (("stats", lambda: harts.moe_stats(z, q, k, S, top, lse, counts, mass, losses, ws, bias=bias),
+                          C * (4 * E + 8 + 4 * k)),
+                         ("grad", lambda: harts.moe_grad(z, q, counts, k, S, 1e-3, 1e-2, dz), C * (8 * E + 4))):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[name] = {"ms": ms, "bytes": by, "achieved_gbps": by / (ms / 1e3) / 1e9, "frac_hbm": by / (ms / 1e3) / PEAK_HBM}
+    out["moe_stats"] = res
+
+
 def logprob_bench(args, out):
     """The log-prob workload (32768 compact rows x 131072 bf16 logits): forward gather and its
     backward, each timed with HIP events, into ``out``."""
@@ -328,6 +373,13 @@ def main():
     if args.only_logprob:
         out = {}
         logprob_bench(args, out)
+        print(json.dumps(out))
+        return
+    if args.only_moe:
+        t = trees.random_rollout_tree(seed=args.seed)
+        plan = harts.TreePlan(t.tokens, t.offsets, B)
+        out = {}
+        moe_bench(args, out, plan, plan.info.C)
         print(json.dumps(out))
         return
     if args.only_attn:
@@ -451,6 +503,9 @@ def main():
     # ---------------------------------------------------------------- tree softmax attention
     if not args.no_attn:
         attn_bench(args, out, t, plan, C)
+    # ---------------------------------------------------------------- router statistics
+    if not args.no_moe:
+        moe_bench(args, out, plan, C)
     # ---------------------------------------------------------------- log-prob gather and its backward
     if not args.no_logprob:
         del ws

@@ -100,6 +100,10 @@ _attn_ws = _sig("harts_attn_workspace_size", ctypes.c_size_t, I64, I32)
 _attn_fwd = _sig("harts_attn_fwd", I32, P, P, P, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P)
 _attn_bwd = _sig("harts_attn_bwd", I32, P, P, P, P, P, P, P, I64, P, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
                  P, P, P, P, ctypes.c_size_t, P)
+_moe_ws = _sig("harts_moe_workspace_size", ctypes.c_size_t, I64, I32)
+_moe_stats = _sig("harts_moe_stats", I32, P, P, P, I64, I32, I32, I64, P, P, P, P, P, P, ctypes.c_size_t, P)
+_moe_grad = _sig("harts_moe_grad", I32, P, P, P, I64, I32, I32, I64, ctypes.c_float, ctypes.c_float, P, P)
+_moe_bias = _sig("harts_moe_bias_update", I32, P, I32, ctypes.c_float, P, P)
 _conv_bwd = _sig("harts_conv_bwd", I32, P, P, P, P, P, P, I64, I32, I32, I32, P, P, P, ctypes.c_size_t, P)
 _prof_enable = _sig("harts_profile_enable", I32, I32)
 _prof_collect = _sig("harts_profile_collect", I32, P, I32, P)
@@ -409,6 +413,29 @@ def attn_bwd(q, k, v, o, lse, dout, qtiles, kv_list, ktiles, q_list, scale: floa
     _check(_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(qtiles), qtiles.shape[0],
                      _ptr(kv_list), _ptr(ktiles), ktiles.shape[0], _ptr(q_list), C, H, dqk, v.shape[2],
                      float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def moe_workspace_size(C: int, E: int) -> int:
+    return int(_moe_ws(C, E))
+
+
+def moe_stats(logits, q, k: int, S: int, topk, lse, counts, mass, losses, workspace, bias=None, stream=None):
+    """harts_moe_stats: q-weighted router statistics of the compact rows (logits fp32 [C, E])."""
+    C, E = logits.shape
+    _check(_moe_stats(_ptr(logits), _ptr(bias), _ptr(q), C, E, k, S, _ptr(topk), _ptr(lse), _ptr(counts), _ptr(mass),
+                      _ptr(losses), _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def moe_grad(logits, q, counts, k: int, S: int, z_coef: float, aux_coef: float, dlogits, stream=None):
+    """harts_moe_grad: d(z_coef L_z + aux_coef L_aux)/d logits, counts held fixed."""
+    C, E = logits.shape
+    _check(_moe_grad(_ptr(logits), _ptr(q), _ptr(counts), C, E, k, S, float(z_coef), float(aux_coef), _ptr(dlogits),
+                     _stream(stream)))
+
+
+def moe_bias_update(counts, gamma: float, bias, stream=None):
+    """harts_moe_bias_update: bias[e] += gamma sign(mean(counts) - counts[e])."""
+    _check(_moe_bias(_ptr(counts), counts.shape[0], float(gamma), _ptr(bias), _stream(stream)))
 
 
 def profile_enable(on: bool = True):

@@ -981,6 +981,84 @@ int harts_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
   });
 }
 
+size_t harts_moe_workspace_size(int64_t C, int32_t E) {
+  return C >= 0 && E > 0 ? align256(size_t(harts::moe_partial_rows(C)) * size_t(2 * E + 1) * 4) : 256;
+}
+
+namespace {
+void moe_check(int64_t C, int32_t E, int32_t k, int64_t S) {
+  if (C < 0 || S < 0) throw Error(HARTS_EINVAL, "need C >= 0, S >= 0");
+  if (E != 64 && E != 128 && E != 256 && E != 512) throw Error(HARTS_EINVAL, "E must be 64, 128, 256 or 512");
+  if (k < 1 || k > 8 || k > E) throw Error(HARTS_EINVAL, "k must be in [1, 8]");
+  if (C > 0 && S < C) throw Error(HARTS_EINVAL, "S (the sum of q) must be >= C");
+  if (S > int64_t(INT32_MAX) / k) throw Error(HARTS_ERANGE, "S * k must fit int32 counts");
+  if (C > int64_t(INT32_MAX) * 64) throw Error(HARTS_ERANGE, "C too large");
+}
+}  // namespace
+
+int harts_moe_stats(const float* logits, const float* bias, const int32_t* q, int64_t C, int32_t E, int32_t k,
+                    int64_t S, int32_t* topk, float* lse, int32_t* counts, float* mass, float* losses,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  return guarded([&] {
+    moe_check(C, E, k, S);
+    if (!counts || !mass || !losses) throw Error(HARTS_EINVAL, "counts, mass and losses are required");
+    if (C > 0 && (!logits || !q || !topk || !lse)) throw Error(HARTS_EINVAL, "logits, q, topk and lse are required");
+    if (!workspace || workspace_bytes < size_t(harts::moe_partial_rows(C)) * size_t(2 * E + 1) * 4)
+      throw Error(HARTS_EINVAL, "workspace must hold harts_moe_workspace_size bytes");
+    harts::MoeArgs a{};
+    a.z = logits;
+    a.bias = bias;
+    a.q = q;
+    a.top = topk;
+    a.lse = lse;
+    a.counts = counts;
+    a.part = static_cast<float*>(workspace);
+    a.mass = mass;
+    a.losses = losses;
+    a.C = C;
+    a.S = S;
+    a.E = E;
+    a.k = k;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope ps("moe_stats", s, C);
+    hip_check(harts::launch_moe(0, a, s), "router statistics launch");
+  });
+}
+
+int harts_moe_grad(const float* logits, const int32_t* q, const int32_t* counts, int64_t C, int32_t E, int32_t k,
+                   int64_t S, float z_coef, float aux_coef, float* dlogits, void* stream) {
+  return guarded([&] {
+    moe_check(C, E, k, S);
+    if (C == 0) return;
+    if (!logits || !q || !counts || !dlogits) throw Error(HARTS_EINVAL, "logits, q, counts and dlogits are required");
+    const size_t nb = size_t(C) * E * 4;
+    const char *x = reinterpret_cast<const char*>(logits), *y = reinterpret_cast<const char*>(dlogits);
+    if (x < y + nb && y < x + nb) throw Error(HARTS_EINVAL, "dlogits overlaps logits");
+    harts::MoeArgs a{};
+    a.z = logits;
+    a.q = q;
+    a.counts = const_cast<int32_t*>(counts);
+    a.dz = dlogits;
+    a.C = C;
+    a.S = S;
+    a.E = E;
+    a.k = k;
+    a.z_coef = z_coef;
+    a.aux_coef = aux_coef;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ProfScope ps("moe_grad", s, C);
+    hip_check(harts::launch_moe(1, a, s), "router gradient launch");
+  });
+}
+
+int harts_moe_bias_update(const int32_t* counts, int32_t E, float gamma, float* bias, void* stream) {
+  return guarded([&] {
+    if (E <= 0) throw Error(HARTS_EINVAL, "need E > 0");
+    if (!counts || !bias) throw Error(HARTS_EINVAL, "counts and bias are required");
+    hip_check(harts::launch_moe_bias(counts, E, gamma, bias, static_cast<hipStream_t>(stream)), "bias update launch");
+  });
+}
+
 int harts_profile_enable(int32_t on) {
   return guarded([&] {
     std::vector<ProfRec> old;

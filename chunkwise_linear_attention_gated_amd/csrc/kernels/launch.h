@@ -118,6 +118,26 @@ struct AttnArgs {
 bool attn_dims_supported(int dqk, int dv);
 hipError_t launch_attn(int which, const AttnArgs& a, int64_t n_tiles, int dqk, int dv, hipStream_t s);
 
+// Multiplicity-weighted router statistics (moe.hip).  which: 0 statistics, 1 gradient.
+struct MoeArgs {
+  const float* z;      // [C][E] router logits
+  const float* bias;   // [E] or null
+  const int32_t* q;    // [C] multiplicities
+  int32_t* top;        // [C][k]
+  float* lse;          // [C]
+  int32_t* counts;     // [E] (statistics: written; gradient: read)
+  float* part;         // workspace: [moe_partial_rows(C)][E + 1] float, then [..][E] int32
+  float* mass;         // [E]
+  float* losses;       // [2]: L_z, L_aux
+  float* dz;           // [C][E]
+  int64_t C, S;
+  int32_t E, k;
+  float z_coef, aux_coef;
+};
+int64_t moe_partial_rows(int64_t C);
+hipError_t launch_moe(int which, const MoeArgs& a, hipStream_t s);
+hipError_t launch_moe_bias(const int32_t* counts, int E, float gamma, float* bias, hipStream_t s);
+
 size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w);
 hipError_t launch_conv_fwd(const void* x, const float* wt, const int32_t* anc, int64_t C, int32_t ch, int32_t w,
                            int dtype, void* out, hipStream_t s);

@@ -369,6 +369,35 @@ int harts_attn_bwd(const void *q, const void *k, const void *v, const void *o, c
                    float scale, void *dq, void *dk, void *dv_out, void *workspace, size_t workspace_bytes,
                    void *stream);
 
+/* ---------------------------------------------------------------- MoE router statistics
+ * A compact row is routed once; its multiplicity q_c (semantic positions that
+ * read row c, sum_c q_c = S; harts_plan_maps returns it) restores the training
+ * weights (HARTS blog sections 4.3-4.4; arXiv summary, section 4 "MoE
+ * execution"; Figure C.1(d)):
+ *   p[c] = softmax(z[c]), lse_c = log sum_e exp z[c, e]
+ *   top_c = the k experts with the largest p[c, e] + bias[e] (ties: lower index)
+ *   counts[e] = sum_c q_c [e in top_c]      mass[e] = sum_c q_c p[c, e]
+ *   losses[0] = L_z = sum_c q_c lse_c^2 / S
+ *   losses[1] = L_aux = E / (k S^2) sum_e counts[e] mass[e]
+ * logits: device float32 [C, E]; bias: device float32 [E] or NULL (zero);
+ * q: device int32 [C]; outputs (device): topk int32 [C, k] (decreasing score),
+ * lse float32 [C], counts int32 [E], mass float32 [E], losses float32 [2].
+ * E in {64, 128, 256, 512}, k in [1, 8], S >= C; counts are exact integers,
+ * mass and losses are fixed-order fp32 sums (run to run identical).
+ * workspace: device, >= harts_moe_workspace_size(C, E) bytes. */
+size_t harts_moe_workspace_size(int64_t C, int32_t E);
+int harts_moe_stats(const float *logits, const float *bias, const int32_t *q, int64_t C, int32_t E, int32_t k,
+                    int64_t S, int32_t *topk, float *lse, int32_t *counts, float *mass, float *losses,
+                    void *workspace, size_t workspace_bytes, void *stream);
+/* Gradient of z_coef L_z + aux_coef L_aux with respect to the logits, the counts
+ * of harts_moe_stats held fixed:
+ *   dlogits[c, e] = q_c p[c, e] (z_coef 2 lse_c / S + aux_coef E / (k S^2) (counts[e] - <counts, p[c]>))
+ * dlogits: device float32 [C, E], must not overlap logits. */
+int harts_moe_grad(const float *logits, const int32_t *q, const int32_t *counts, int64_t C, int32_t E, int32_t k,
+                   int64_t S, float z_coef, float aux_coef, float *dlogits, void *stream);
+/* Expert-bias update from the weighted counts: bias[e] += gamma sign(mean_j counts[j] - counts[e]). */
+int harts_moe_bias_update(const int32_t *counts, int32_t E, float gamma, float *bias, void *stream);
+
 /* ---------------------------------------------------------------- kernel timing
  * For benchmarks and profiling.  While enabled, every kernel the library
  * enqueues is bracketed by two HIP events recorded on the same stream (this
