@@ -100,10 +100,12 @@ AttnTables build_attn_tables(const int64_t* m, const int64_t* off, int64_t n_tra
       stack.insert(stack.end(), kids[size_t(d)].rbegin(), kids[size_t(d)].rend());
     }
     const int64_t below = int64_t(t.q_list.size()) - q_off - len;
-    for (int64_t a0 = r0; a0 < r1; a0 += kAttnTile) {
-      const int32_t n = int32_t(std::min<int64_t>(kAttnTile, r1 - a0));
-      const int32_t base = int32_t(h + (a0 - r0));
-      t.qtiles.insert(t.qtiles.end(), {int32_t(a0), n, int32_t(kv_off), base});
+    for (int64_t a0 = r0; a0 < r1; a0 += kAttnQTile) {
+      const int32_t n = int32_t(std::min<int64_t>(kAttnQTile, r1 - a0));
+      t.qtiles.insert(t.qtiles.end(), {int32_t(a0), n, int32_t(kv_off), int32_t(h + (a0 - r0))});
+    }
+    for (int64_t a0 = r0; a0 < r1; a0 += kAttnKTile) {
+      const int32_t n = int32_t(std::min<int64_t>(kAttnKTile, r1 - a0));
       t.ktiles.insert(t.ktiles.end(), {int32_t(a0), n, int32_t(q_off + (a0 - r0)), int32_t(r1 - a0 + below)});
     }
   }

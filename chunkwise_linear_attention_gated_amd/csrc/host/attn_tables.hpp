@@ -7,7 +7,7 @@
 // with h ancestor rows gets two row lists:
 //   kv list: its h ancestor rows (root first), then its own rows;
 //   q list:  its own rows, then the rows of every segment below it.
-// and is cut into tiles of kAttnTile rows:
+// and is cut into query tiles of kAttnQTile rows and key tiles of kAttnKTile rows:
 //   query tile {row0, n, off, base}: rows row0 .. row0+n-1; keys are
 //     kv_list[off + v] for v < base + n, and query row0 + i sees key v iff
 //     v <= base + i;
@@ -20,7 +20,8 @@
 
 namespace harts {
 
-constexpr int kAttnTile = 64;
+constexpr int kAttnQTile = 128;
+constexpr int kAttnKTile = 64;
 
 struct AttnTables {
   int64_t C = 0;

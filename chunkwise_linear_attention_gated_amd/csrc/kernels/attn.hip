@@ -5,9 +5,11 @@
 // through the segment's row list (ancestors, then own rows, bottom-right causal),
 // and key tiles read queries through the list of the rows below the segment.
 //
-// Every workgroup is 4 waves and owns a tile of 64 rows of one head; wave w owns
-// rows 16w .. 16w+15.  The gathered operand tile (64 rows) goes through LDS with a
-// register prefetch of the next tile; products run on v_mfma_f32_16x16x32_bf16.
+// A workgroup owns one tile of one head: a 128-row query tile (forward: 4 waves of
+// 32 queries, so every key/value fragment read from LDS feeds two products; dq: 8
+// waves of 16) or a 64-row key tile (dk/dv: 4 waves of 16 keys).  The gathered
+// operand tile (64 rows) goes through LDS with a register prefetch of the next
+// tile; products run on v_mfma_f32_16x16x32_bf16.
 //
 //   forward / dq (query tiles): S^T = K Q^T puts the 16 queries of a wave in the
 //     accumulator columns and 4 keys per lane in its rows; the online softmax is a
@@ -24,14 +26,14 @@
 namespace harts {
 namespace {
 
-constexpr int AT = 64;      // rows per tile
-constexpr int ATHR = 256;   // 4 waves of 16 rows
+constexpr int AT = 64;      // rows per gathered operand tile (and per key tile)
+constexpr int ATHR = 256;   // 4 waves
+constexpr int QT = 128;     // rows per query tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <int DA, int DB> struct AttnCfg {
-  static_assert(DA % 32 == 0 && DB % 32 == 0, "head dims must be multiples of 32");
+  static_assert(DA % 64 == 0 && DB % 64 == 0, "head dims must be multiples of 64");
   static constexpr int LA = DA + 16, LB = DB + 16;   // LDS row strides in elements (32-byte pad)
-  static constexpr int NA = DA / 32, NB = DB / 32;   // 16-byte chunks per loader thread
 };
 
 // A-operand fragment of M^T where M is an LDS matrix stored [k][r] (row stride ld): rows
@@ -43,31 +45,34 @@ __device__ __forceinline__ bf16x8 pf_rc(const bf16* p, int ld, int r0, int k0, i
   return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Tile of 64 gathered rows of two row-major arrays (widths DA and DB).  Thread t loads row
-// t/4, 16-byte chunks t%4 + 4i; a row index < 0 loads zeros.
-template <int DA, int DB> struct RowLoad {
+// Tile of 64 gathered rows of two row-major arrays (widths DA and DB) loaded by 64 TPR
+// threads: thread t loads row t/TPR, 16-byte chunks t%TPR + TPR i; a row index < 0 loads zeros.
+template <int DA, int DB, int TPR> struct RowLoad {
   using Cf = AttnCfg<DA, DB>;
-  f32x4 a[Cf::NA], b[Cf::NB];
+  struct N {
+    static constexpr int NA = DA / (8 * TPR), NB = DB / (8 * TPR);
+  };
+  f32x4 a[N::NA], b[N::NB];
   __device__ __forceinline__ void issue(const bf16* A, const bf16* B, int64_t lda, int64_t ldb, int row, int p) {
     if (row >= 0) {
       const bf16* pa = A + row * lda + 8 * p;
       const bf16* pb = B + row * ldb + 8 * p;
 #pragma unroll
-      for (int i = 0; i < Cf::NA; ++i) a[i] = ldq(pa + 32 * i);
+      for (int i = 0; i < N::NA; ++i) a[i] = ldq(pa + 8 * TPR * i);
 #pragma unroll
-      for (int i = 0; i < Cf::NB; ++i) b[i] = ldq(pb + 32 * i);
+      for (int i = 0; i < N::NB; ++i) b[i] = ldq(pb + 8 * TPR * i);
     } else {
 #pragma unroll
-      for (int i = 0; i < Cf::NA; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < N::NA; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < Cf::NB; ++i) b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < N::NB; ++i) b[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
   __device__ __forceinline__ void put(bf16* sA, bf16* sB, int r, int p) const {
 #pragma unroll
-    for (int i = 0; i < Cf::NA; ++i) stq(sA + r * Cf::LA + 8 * p + 32 * i, a[i]);
+    for (int i = 0; i < N::NA; ++i) stq(sA + r * Cf::LA + 8 * p + 8 * TPR * i, a[i]);
 #pragma unroll
-    for (int i = 0; i < Cf::NB; ++i) stq(sB + r * Cf::LB + 8 * p + 32 * i, b[i]);
+    for (int i = 0; i < N::NB; ++i) stq(sB + r * Cf::LB + 8 * p + 8 * TPR * i, b[i]);
   }
 };
 
@@ -93,10 +98,11 @@ __device__ __forceinline__ void scores_t(const bf16* sK, const bf16x8 (&qf)[DQ /
   }
 }
 
-// three workgroups per CU (<= 168 registers, no spills): the extra waves hide the gathered loads'
-// latency behind the other workgroups' products (-7 % at dims 192/128)
+// two waves per SIMD (<= 256 registers; one spilled): at the unconstrained 320 registers one
+// wave per SIMD leaves the gathered loads' latency exposed (16.3 ms against 9.5 ms at dims
+// 192/128 on the rollout tree)
 template <int DQ, int DV>
-__global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(3))) void attn_fwd_kernel(AttnArgs g) {
+__global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void attn_fwd_kernel(AttnArgs g) {
   using Cf = AttnCfg<DQ, DV>;
   __shared__ __align__(16) bf16 sK[AT * Cf::LA];
   __shared__ __align__(16) bf16 sV[AT * Cf::LB];
@@ -104,66 +110,96 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(3))) void 
   const int4 T = reinterpret_cast<const int4*>(g.tiles)[tile];
   const int row0 = T.x, nr = T.y, base = T.w, nkv = base + nr, nt = (nkv + AT - 1) / AT;
   const int32_t* lst = g.list + T.z;
-  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, qi = 16 * (tid >> 6) + (lane & 15);
-  const int qrow = row0 + min(qi, nr - 1);
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
+  // the wave's two query halves: qi[n] = 32 w + 16 n + l % 16
+  int qi[2], qrow[2];
+#pragma unroll
+  for (int n = 0; n < 2; ++n) {
+    qi[n] = 32 * (tid >> 6) + 16 * n + (lane & 15);
+    qrow[n] = row0 + min(qi[n], nr - 1);
+  }
   const int64_t ldq = int64_t(H) * DQ, ldv = int64_t(H) * DV;
   const bf16* kh = g.k + h * DQ;
   const bf16* vh = g.v + h * DV;
-  bf16x8 qf[DQ / 32];
-  {
-    const bf16* qp = g.q + qrow * ldq + h * DQ + 8 * gq;
+  bf16x8 qf[2][DQ / 32];
 #pragma unroll
-    for (int s = 0; s < DQ / 32; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
+  for (int n = 0; n < 2; ++n) {
+    const bf16* qp = g.q + qrow[n] * ldq + h * DQ + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < DQ / 32; ++s) qf[n][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
   }
   const int lr = tid >> 2, lp = tid & 3;
-  RowLoad<DQ, DV> ld;
+  RowLoad<DQ, DV, 4> ld;
   ld.issue(kh, vh, ldq, ldv, lr < nkv ? lst[lr] : -1, lp);
   int nxt = AT + lr < nkv ? lst[AT + lr] : -1;
   ld.put(sK, sV, lr, lp);
   __syncthreads();
 
   const float c = g.scale * kLog2e;
-  float mrun = -INFINITY, lsum = 0.f;
-  f32x4 acc[DV / 16];
+  float mrun[2] = {-INFINITY, -INFINITY}, lsum[2] = {0.f, 0.f};
+  f32x4 acc[2][DV / 16];
 #pragma unroll
-  for (int d = 0; d < DV / 16; ++d) acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < 2; ++n)
+#pragma unroll
+    for (int d = 0; d < DV / 16; ++d) acc[n][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nt; ++j) {
     if (j + 1 < nt) {
       ld.issue(kh, vh, ldq, ldv, nxt, lp);
       const int u = (j + 2) * AT + lr;
       nxt = u < nkv ? lst[u] : -1;
     }
-    f32x4 sc[4];
-    scores_t<DQ, Cf::LA>(sK, qf, lane, sc);
-    const int lim = base + qi - j * AT;  // keys of this tile with index <= lim are visible
-    float mx = -INFINITY;
+    f32x4 sc[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 4; ++kb) {
+      f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = 16 * kb + 4 * gq + i <= lim ? sc[kb][i] * c : -INFINITY;
-        sc[kb][i] = x;
-        mx = fmaxf(mx, x);
+      for (int s = 0; s < DQ / 32; ++s) {
+        const bf16x8 kf = Mma<bf16>::kc(sK, Cf::LA, 16 * kb, 32 * s, lane);
+        a0 = Mma<bf16>::mma(kf, qf[0][s], a0);
+        a1 = Mma<bf16>::mma(kf, qf[1][s], a1);
       }
-    const float mnew = fmaxf(mrun, wave_quad_max(mx));
-    const float alpha = exp2f(mrun - mnew);
-    mrun = mnew;
-    float ps = 0.f;
+      sc[0][kb] = a0;
+      sc[1][kb] = a1;
+    }
+    bf16x8 pb[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int n = 0; n < 2; ++n) {
+      const int lim = base + qi[n] - j * AT;  // keys of this tile with index <= lim are visible
+      float mx = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(sc[kb][i] - mnew);
-        sc[kb][i] = p;
-        ps += p;
-      }
-    lsum = lsum * alpha + ps;
-    const bf16x8 p0 = pf_pair(sc[0], sc[1]), p1 = pf_pair(sc[2], sc[3]);
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = 16 * kb + 4 * gq + i <= lim ? sc[n][kb][i] * c : -INFINITY;
+          sc[n][kb][i] = x;
+          mx = fmaxf(mx, x);
+        }
+      const float mnew = fmaxf(mrun[n], wave_quad_max(mx));
+      const float alpha = exp2f(mrun[n] - mnew);
+      mrun[n] = mnew;
+      float ps = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = exp2f(sc[n][kb][i] - mnew);
+          sc[n][kb][i] = p;
+          ps += p;
+        }
+      lsum[n] = lsum[n] * alpha + ps;
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d) acc[n][d] *= alpha;
+      pb[n][0] = pf_pair(sc[n][0], sc[n][1]);
+      pb[n][1] = pf_pair(sc[n][2], sc[n][3]);
+    }
 #pragma unroll
     for (int d = 0; d < DV / 16; ++d) {
-      acc[d] *= alpha;
-      acc[d] = Mma<bf16>::mma(pf_rc(sV, Cf::LB, 16 * d, 0, lane), p0, acc[d]);
-      acc[d] = Mma<bf16>::mma(pf_rc(sV, Cf::LB, 16 * d, 32, lane), p1, acc[d]);
+      const bf16x8 v0 = pf_rc(sV, Cf::LB, 16 * d, 0, lane), v1 = pf_rc(sV, Cf::LB, 16 * d, 32, lane);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        acc[n][d] = Mma<bf16>::mma(v0, pb[n][0], acc[n][d]);
+        acc[n][d] = Mma<bf16>::mma(v1, pb[n][1], acc[n][d]);
+      }
     }
     if (j + 1 < nt) {
       __syncthreads();
@@ -171,14 +207,17 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(3))) void 
       __syncthreads();
     }
   }
-  lsum = wave_quad_sum(lsum);
-  if (qi < nr) {
-    const float inv = 1.f / lsum;
-    bf16* op = g.o_out + qrow * ldv + h * DV + 4 * gq;
 #pragma unroll
-    for (int d = 0; d < DV / 16; ++d)
-      store4<bf16>(op + 16 * d, acc[d][0] * inv, acc[d][1] * inv, acc[d][2] * inv, acc[d][3] * inv);
-    if (gq == 0) g.lse_out[int64_t(qrow) * H + h] = (mrun + log2f(lsum)) * (1.f / kLog2e);
+  for (int n = 0; n < 2; ++n) {
+    const float l = wave_quad_sum(lsum[n]);
+    if (qi[n] < nr) {
+      const float inv = 1.f / l;
+      bf16* op = g.o_out + qrow[n] * ldv + h * DV + 4 * gq;
+#pragma unroll
+      for (int d = 0; d < DV / 16; ++d)
+        store4<bf16>(op + 16 * d, acc[n][d][0] * inv, acc[n][d][1] * inv, acc[n][d][2] * inv, acc[n][d][3] * inv);
+      if (gq == 0) g.lse_out[int64_t(qrow[n]) * H + h] = (mrun[n] + log2f(l)) * (1.f / kLog2e);
+    }
   }
 }
 
@@ -202,7 +241,7 @@ __global__ __launch_bounds__(256) void attn_delta_kernel(const bf16* o, const bf
 }
 
 template <int DQ, int DV>
-__global__ __launch_bounds__(ATHR) void attn_dq_kernel(AttnArgs g) {
+__global__ __launch_bounds__(2 * ATHR) void attn_dq_kernel(AttnArgs g) {
   using Cf = AttnCfg<DQ, DV>;
   __shared__ __align__(16) bf16 sK[AT * Cf::LA];
   __shared__ __align__(16) bf16 sV[AT * Cf::LB];
@@ -225,8 +264,8 @@ __global__ __launch_bounds__(ATHR) void attn_dq_kernel(AttnArgs g) {
     for (int s = 0; s < DV / 32; ++s) df[s] = *reinterpret_cast<const bf16x8*>(dp + 32 * s);
   }
   const float lse2 = g.lse[int64_t(qrow) * H + h] * kLog2e, dlt = g.delta[int64_t(qrow) * H + h];
-  const int lr = tid >> 2, lp = tid & 3;
-  RowLoad<DQ, DV> ld;
+  const int lr = tid >> 3, lp = tid & 7;
+  RowLoad<DQ, DV, 8> ld;
   ld.issue(kh, vh, ldq, ldv, lr < nkv ? lst[lr] : -1, lp);
   int nxt = AT + lr < nkv ? lst[AT + lr] : -1;
   ld.put(sK, sV, lr, lp);
@@ -305,7 +344,7 @@ __global__ __launch_bounds__(ATHR) void attn_dkv_kernel(AttnArgs g) {
     for (int s = 0; s < DV / 32; ++s) vf[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
   }
   const int lr = tid >> 2, lp = tid & 3;
-  RowLoad<DQ, DV> ld;
+  RowLoad<DQ, DV, 4> ld;
   float xl = 0.f, xd = 0.f;
   auto issue = [&](int row) {
     ld.issue(qh, oh, ldq, ldv, row, lp);
@@ -397,7 +436,7 @@ hipError_t attn_dispatch(int which, const AttnArgs& a, int64_t n_tiles, hipStrea
   }
   const dim3 grid(unsigned(n_tiles * a.H)), block(ATHR);
   if (which == 0) hipLaunchKernelGGL((attn_fwd_kernel<DQ, DV>), grid, block, 0, s, a);
-  else if (which == 2) hipLaunchKernelGGL((attn_dq_kernel<DQ, DV>), grid, block, 0, s, a);
+  else if (which == 2) hipLaunchKernelGGL((attn_dq_kernel<DQ, DV>), grid, dim3(2 * ATHR), 0, s, a);
   else hipLaunchKernelGGL((attn_dkv_kernel<DQ, DV>), grid, block, 0, s, a);
   return hipGetLastError();
 }

@@ -104,7 +104,7 @@ def _attn_check_tables(m, off, C):
     qt, kv, kt, ql = tb["qtiles"], tb["kv_list"], tb["ktiles"], tb["q_list"]
     seen_q = np.zeros(C, np.int64)
     for row0, n, o, base in qt:
-        assert 1 <= n <= 64
+        assert 1 <= n <= 128
         for i in range(n):
             seen_q[row0 + i] += 1
             assert list(kv[o:o + base + i + 1]) == list(P[row0 + i])  # the path, root first
@@ -117,6 +117,7 @@ def _attn_check_tables(m, off, C):
             readers[int(a)].add(t)
     seen_k = np.zeros(C, np.int64)
     for row0, n, o, nq in kt:
+        assert 1 <= n <= 64
         for j in range(n):
             seen_k[row0 + j] += 1
             got = list(ql[o + j:o + nq])
