@@ -45,6 +45,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--no-flat", action="store_true", help="skip the flat packed call (32 sequences, all states)")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--only-conv", action="store_true",
                     help="only the tree causal convolution (for profiling it alone)")
@@ -63,14 +64,15 @@ def parse():
 
 # ------------------------------------------------------------------ algorithmic work per kernel
 # Multiply-accumulates per chunk of l tokens (replay included) and head, d = d_k = d_v, for the
-# products each kernel performs ("Kernels and their rooflines").  The benchmark
-# runs the forward that keeps the backward's operands: kda_prep_fwd is then the preparation of
-# both directions (A and M, W, U', Qeff, O', the diagonal-block inverse), kda_state_fwd also
-# writes the chunk-start states, and the backward runs no kda_prep_bwd or kda_state_bwd.
-def macs(kernel, l, d=D):
+# products each kernel performs ("Kernels, data layout, rooflines").  In the
+# recompute mode (the headline) the forward runs kda_prep_fwd + kda_state_fwd per round and the
+# backward kda_prep_bwd + kda_state_bwd (recompute) + kda_dstate + kda_grad per round.  With keep
+# the forward's preparation also produces the backward's operands (kda_prep_fwd counts both) and
+# the backward runs no preparation or recompute.
+def macs(kernel, l, d=D, keep=False):
     l2d, ld2, l3 = l * l * d, l * d * d, l ** 3
     return {
-        "kda_prep_fwd": 5 * l2d + l3 / 6,
+        "kda_prep_fwd": (5 * l2d + l3 / 6) if keep else (4 * l2d + l3 / 6),
         "kda_state_fwd": 3 * ld2,
         "kda_prep_bwd": 4 * l2d + l3 / 6,
         "kda_state_bwd": 2 * ld2,
@@ -79,22 +81,26 @@ def macs(kernel, l, d=D):
     }[kernel]
 
 
-def hbm_bytes(kernel, l, d=D, bt=B):
-    """Bytes each kernel must move once per chunk-head: its inputs read once and its
-    outputs written once (workspace arrays are chunk-sized)."""
-    tok = l * d * ES        # one [l, d] bf16 tensor of the chunk's rows
-    blk = bt * d * ES       # one [B, d] workspace array
-    sq = bt * bt * ES       # one [B, B] workspace array
-    st = d * d * ES         # one bf16 state [d, d]
-    return {
-        "kda_prep_fwd": 4 * tok + l * ES + 5 * blk + 4 * sq + d * 4,
-        "kda_state_fwd": 5 * blk + d * 4 + tok + st,
-        "kda_prep_bwd": 4 * tok + l * ES + 4 * blk + 4 * sq + d * 4,
-        "kda_state_bwd": 3 * blk + d * 4 + st,
-        "kda_dstate": 3 * blk + d * 4 + tok + st,
-        # q, k, v, g, dO, beta, S, dS, T, M, X, A in; dq, dk, dv, dg, dbeta out
-        "kda_grad": 5 * tok + l * ES + 2 * st + 4 * sq + 4 * tok + l * ES,
-    }[kernel]
+# Algorithmic HBM bytes per token-head (ideal single pass over the path's own inputs and outputs,
+# bf16, d = 128): forward 1282 B = q, k, v, g read (4 x 256) + beta (2) + o written (256); backward
+# 2308 B = the five inputs read (1026) + dO read (256) + dq, dk, dv, dg (4 x 256) and dbeta (2)
+# written.  They are attributed to the kernels that must move them: the forward preparation reads
+# the inputs, the forward serial pass writes o (and the handed-off states), and the gradient
+# kernel reads the inputs and dO and writes every gradient.  Recompute and state-gradient passes
+# only move intermediates, which are not algorithmic bytes.
+ALG_BYTES_PER_TOKEN_HEAD = {"kda_prep_fwd": 4 * D * ES + ES, "kda_state_fwd": D * ES,
+                            "kda_grad": 8 * D * ES + D * ES + 2 * ES}
+
+
+def alg_bytes(kernel, tokens, own_tokens, slot_bytes):
+    """Algorithmic bytes of one step of ``kernel``: ``tokens`` chunk rows (replay included) and
+    ``own_tokens`` compact rows, times heads; the forward serial pass also writes the handed-off
+    states (``slot_bytes``)."""
+    if kernel == "kda_state_fwd":
+        return own_tokens * H * ALG_BYTES_PER_TOKEN_HEAD[kernel] + slot_bytes
+    if kernel in ALG_BYTES_PER_TOKEN_HEAD:
+        return tokens * H * ALG_BYTES_PER_TOKEN_HEAD[kernel]
+    return None
 
 
 def round_chunks(plan):
@@ -168,6 +174,71 @@ def cpu_baseline(t, feats, C, S, target_positions=250000, seed=0):
     return {"value": C / full, "unit": "compact tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d of %d trajectories (%d of %d semantic positions, %d heads), forward + reverse pass in "
                       "%.1f s; extrapolated per semantic position" % (len(which), t.n_traj, P, S, H, dt)}
+
+
+def device_features(N, seed, dev):
+    """q, k (unit norm per token-head), v, g = -softplus(N(0,1)), beta = sigmoid(N(0,1)), bf16, drawn by
+    torch's generator on the device (the benchmark's distributions, without the host round trip)."""
+    import torch
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    r = lambda *s: torch.randn(s, generator=gen, device=dev, dtype=torch.float32)
+    q = torch.nn.functional.normalize(r(N, H, D), dim=-1).to(torch.bfloat16)
+    k = torch.nn.functional.normalize(r(N, H, D), dim=-1).to(torch.bfloat16)
+    v = r(N, H, D).to(torch.bfloat16)
+    g = (-torch.nn.functional.softplus(r(N, H, D))).to(torch.bfloat16)
+    beta = torch.sigmoid(r(N, H)).to(torch.bfloat16)
+    return q, k, v, g, beta
+
+
+def flat_bench(args, out):
+    """The flat packed call: 32 independent sequences (lengths uniform in [1024, 4096], multiples of
+    64 rejected), even ones from the zero state and odd ones from an fp32 N(0, 0.1^2) state, one
+    forward call writing o, every chunk-boundary state and the final states.  HBM-bound: algorithmic
+    bytes = 1282 per token-head + initial states read + boundary and final states written."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    from synthetic import trees
+    dev = "cuda"
+    lens = trees.flat_varlen_lengths(seed=args.seed, n=32)
+    n = len(lens)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    has = (np.arange(n) % 2 == 1).astype(np.uint8)
+    vp = harts.VarlenPlan(cu, B, has_init=has, emit_boundaries=True)
+    dp = harts.DevicePlan(vp, H, D, D, harts.DTYPE_BF16)
+    N = int(cu[-1])
+    q, k, v, g, beta = device_features(N, args.seed + 1, dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed + 2)
+    init = torch.randn((n, H, D, D), generator=gen, device=dev) * 0.1
+    o = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+    nb = vp.info.n_boundaries
+    bst = torch.empty((max(nb, 1), H, D, D), dtype=torch.float32, device=dev)
+    fin = torch.empty((n, H, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(dp.workspace_size(False), dtype=torch.uint8, device=dev)
+
+    def call():
+        harts.kda_fwd(dp, q, k, v, g, beta, o, states=bst, init_states=init, final_states=fin, workspace=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    reps = max(3, min(args.steps, 10))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    st = H * D * D * 4
+    by = N * H * 1282 + int(has.sum()) * st + nb * st + n * st
+    chunks = [min(B, int(L) - c) for L in lens for c in range(0, int(L), B)]
+    fl = sum(2 * (4 * l * l * D + 3 * l * D * D + l ** 3 / 6) * H for l in chunks)
+    out["flat_varlen"] = {"n_seq": n, "tokens": N, "boundary_states": nb, "ms": ms, "value": N / (ms / 1e3),
+                          "unit": "tokens/s", "alg_bytes": by, "achieved_gbps": by / (ms / 1e3) / 1e9,
+                          "frac_hbm": by / (ms / 1e3) / PEAK_HBM, "mfma_pct": 100 * fl / (ms / 1e3) / PEAK_BF16}
+    del q, k, v, g, beta, init, o, bst, fin, ws
 
 
 def conv_bench(args, out, t, plan, C):
@@ -417,86 +488,137 @@ def main():
     gr = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "g", "beta")}
     ws = torch.empty(dp.workspace_size(2), dtype=torch.uint8, device=dev)
 
-    def step():
-        # the forward keeps the backward's per-chunk operands and chunk-start states
-        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=True)
+    def fwd(keep):
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=keep)
+
+    def step(keep=False):
+        # recompute (keep=False): the backward prepares each round again and recomputes its
+        # chunk-start states from the round's initial states; keep=True: the forward leaves the
+        # backward's per-chunk operands and chunk-start states in the workspace
+        fwd(keep)
         harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"],
-                      gr["g"], gr["beta"], states=slots, dstates=dslots, workspace=ws, keep=True)
+                      gr["g"], gr["beta"], states=slots, dstates=dslots, workspace=ws, keep=keep)
+
+    def timed(fn, steps):
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        ev0.record()
+        for _ in range(steps):
+            fn()
+        ev1.record()
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1), time.perf_counter() - w0
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # ---------------------------------------------------------------- timed region
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    ev0.record()
-    for _ in range(args.steps):
-        step()
-    ev1.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = ev0.elapsed_time(ev1)
+    # ---------------------------------------------------------------- timed region (headline)
+    ms_total, wall = timed(step, args.steps)
     ms_step = ms_total / args.steps
     value = C * args.steps / (ms_total / 1e3)
 
-    # ---------------------------------------------------------------- per-kernel timing (same steps, events on)
-    harts.profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    prof = harts.profile_collect()
-    harts.profile_enable(False)
     rch = round_chunks(plan)
     all_chunks = [l for r in sorted(rch) for l in rch[r]]
-    kernels = {}
-    for name, (launches, tot_ms, units) in prof.items():
-        per_step_launches = launches / args.steps
-        entry = {"launches_per_step": per_step_launches, "avg_ms": tot_ms / launches,
-                 "ms_per_step": tot_ms / args.steps}
-        try:
-            fl = 2 * sum(macs(name, l) for l in all_chunks) * H           # per step
-            by = sum(hbm_bytes(name, l) for l in all_chunks) * H
-            entry["flops_per_launch"] = fl / per_step_launches
-            entry["bytes_per_launch"] = by / per_step_launches
-            sec = entry["avg_ms"] / 1e3
-            entry["tflops"] = entry["flops_per_launch"] / sec / 1e12
-            entry["gbps"] = entry["bytes_per_launch"] / sec / 1e9
-        except KeyError:
-            pass
-        kernels[name] = entry
-    dom = max((k for k in kernels if "flops_per_launch" in kernels[k]), key=lambda k: kernels[k]["ms_per_step"])
+    tokens_step = sum(all_chunks)           # chunk rows per head, replay included
+    slot_bytes = info.n_slots * H * D * D * 4
+    flops_step = path_flops(all_chunks)
+    bytes_step = C * H * (1282 + 2308) + 2 * 2 * slot_bytes
+
+    # ---------------------------------------------------------------- per-kernel timing (same steps, events on)
+    def kernel_table(keep):
+        harts.profile_collect()  # drop anything recorded before
+        harts.profile_enable(True)
+        for _ in range(args.steps):
+            step(keep)
+        torch.cuda.synchronize()
+        prof = harts.profile_collect()
+        harts.profile_enable(False)
+        kernels = {}
+        for name, (launches, tot_ms, units) in prof.items():
+            per_step_launches = launches / args.steps
+            entry = {"launches_per_step": per_step_launches, "avg_ms": tot_ms / launches,
+                     "ms_per_step": tot_ms / args.steps}
+            try:
+                fl = 2 * sum(macs(name, l, keep=keep) for l in all_chunks) * H           # per step
+                entry["flops_per_launch"] = fl / per_step_launches
+                entry["tflops"] = entry["flops_per_launch"] / (entry["avg_ms"] / 1e3) / 1e12
+            except KeyError:
+                pass
+            by = alg_bytes(name, tokens_step, C, slot_bytes)
+            if by is not None:
+                entry["alg_bytes_per_launch"] = by / per_step_launches
+                entry["alg_gbps"] = entry["alg_bytes_per_launch"] / (entry["avg_ms"] / 1e3) / 1e9
+            kernels[name] = entry
+        return kernels
+
+    kernels = kernel_table(False)
+    dom = max((k for k in kernels if "alg_bytes_per_launch" in kernels[k]), key=lambda k: kernels[k]["ms_per_step"])
     dk = kernels[dom]
-    intensity = dk["flops_per_launch"] / dk["bytes_per_launch"]
+    intensity = dk["flops_per_launch"] / dk["alg_bytes_per_launch"]
     if intensity < RIDGE:
-        roof = {"bound": "hbm", "achieved": dk["gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
-                "frac": dk["gbps"] * 1e9 / PEAK_HBM}
+        roof = {"bound": "hbm", "achieved": dk["alg_gbps"], "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                "frac": dk["alg_gbps"] * 1e9 / PEAK_HBM}
     else:
         roof = {"bound": "mfma", "achieved": dk["tflops"], "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                 "frac": dk["tflops"] * 1e12 / PEAK_BF16}
+    roof["traffic"] = traffic_for(dom)
     roof["kernel"] = dom
     roof["avg_launch_ms"] = dk["avg_ms"]
-    roof["traffic"] = traffic_for(dom)
+    roof["alg_bytes_per_launch"] = dk["alg_bytes_per_launch"]
+    roof["bytes_per_token_head"] = ALG_BYTES_PER_TOKEN_HEAD[dom]
 
-    flops_step = path_flops(all_chunks)
-    bytes_step = C * H * (1282 + 2308) + 2 * 2 * info.n_slots * H * D * D * 4
+    # ---------------------------------------------------------------- the keep variant (same step, more memory)
+    for _ in range(2):
+        step(True)
+    ms_keep, _ = timed(lambda: step(True), args.steps)
+    keep_kernels = kernel_table(True)
+    keep_variant = {"ms_per_step": ms_keep / args.steps, "value": C * args.steps / (ms_keep / 1e3),
+                    "workspace_bytes": dp.workspace_size(2),
+                    "mfma_pct": 100 * flops_step / (ms_keep / args.steps / 1e3) / PEAK_BF16,
+                    "kernels": keep_kernels}
+
+    # ---------------------------------------------------------------- tree forward alone (C / t_fwd)
+    for _ in range(2):
+        fwd(False)
+    ms_f, _ = timed(lambda: fwd(False), args.steps)
+    ms_f /= args.steps
+    fwd_flops = 0.0
+    for l in all_chunks:
+        fwd_flops += 2 * (4 * l * l * D + 3 * l * D * D + l ** 3 / 6) * H
+    fwd_bytes = C * H * 1282 + slot_bytes
+    tree_forward = {"ms": ms_f, "value": C / (ms_f / 1e3), "unit": "compact tokens/s",
+                    "mfma_pct": 100 * fwd_flops / (ms_f / 1e3) / PEAK_BF16,
+                    "hbm_pct_alg_bytes": 100 * fwd_bytes / (ms_f / 1e3) / PEAK_HBM}
+
     out = {
         "metric": "compact tokens/s, tree-packed chunkwise gated-delta fwd+bwd; MFMA % of peak",
         "value": value, "unit": "compact tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "64-leaf synthetic rollout tree (seed %d): 16384-token root, fan-out 2-4, "
-                               "leaf lengths log-uniform [64, 4096]; H=16, d_k=d_v=128, B=64; "
-                               "packed forward + backward over all rounds" % args.seed,
+                               "leaf lengths log-uniform [64, 4096]; H=16, d_k=d_v=128, B=64, bf16 inputs, fp32 "
+                               "state; packed forward + backward over all rounds, activations recomputed in the "
+                               "backward (no operands kept between the two)" % args.seed,
+                   "mode": "recompute",
                    "C": C, "S": S, "expansion": S / C, "n_rounds": info.n_rounds, "n_sequences": info.n_sequences,
                    "n_slots": info.n_slots, "replay_tokens": info.replay_total, "n_chunks": info.n_chunks},
         "mfma_pct": 100 * flops_step / (ms_step / 1e3) / PEAK_BF16,
-        "hbm_pct_ideal_bytes": 100 * bytes_step / (ms_step / 1e3) / PEAK_HBM,
+        "hbm_pct_alg_bytes": 100 * bytes_step / (ms_step / 1e3) / PEAK_HBM,
         "path_flops_per_step": flops_step,
+        "path_alg_bytes_per_step": bytes_step,
         "plan_ms": plan_ms,
         "wall_s_timed": wall,
         "roofline": roof,
         "kernels": kernels,
+        "keep_variant": keep_variant,
+        "tree_forward": tree_forward,
     }
+    del ws
+    torch.cuda.empty_cache()
+    # ---------------------------------------------------------------- flat packed call (forward, all states)
+    if not args.no_flat:
+        flat_bench(args, out)
     # ---------------------------------------------------------------- tree causal convolution
     if not args.no_conv:
         conv_bench(args, out, t, plan, C)
@@ -508,7 +630,6 @@ def main():
         moe_bench(args, out, plan, C)
     # ---------------------------------------------------------------- log-prob gather and its backward
     if not args.no_logprob:
-        del ws
         torch.cuda.empty_cache()
         logprob_bench(args, out)
     # ---------------------------------------------------------------- oracle on the host cores

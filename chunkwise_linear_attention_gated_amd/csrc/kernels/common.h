@@ -279,6 +279,12 @@ __device__ __forceinline__ void col4_load(const T* p, int ld, int r0, int c0, in
 // Elements of T in the store sink (RoundArgs::sink, 64 KiB)
 template <typename T> __host__ __device__ constexpr int kSinkElems() { return 64 * 1024 / sizeof(T); }
 
+// In-chunk decay products e^{L_i - L_j} inside a 16-token block factor as e^{L_i} e^{-L_j} (L the
+// block-local cumulative log-decay) only for channels whose block gate sum is at least
+// -kSteepGate: then no factor exceeds e^{kSteepGate}, far inside fp32 and bf16 range, and none
+// underflows to a subnormal for unit-scale keys.  Steeper channels take the pairwise form.
+constexpr float kSteepGate = 60.f;
+
 // Waves of a serial state-pass workgroup: one per 16 state rows, at most 8.
 template <int D> constexpr int state_waves() { return D / 16 < 8 ? D / 16 : 8; }
 

@@ -318,6 +318,21 @@ template <typename T> __device__ __forceinline__ f32x4 mma_k16r(k16_t<T> a, k16_
   }
 }
 
+// c + a b with a right operand b given in fp32: for bf16 operands b is split into a bf16 head
+// and the bf16 rounding of its remainder, two products, so b carries about 16 significant bits.
+// The gated 16-token block products need them: with steep gates dg is a small difference of
+// large terms that the row side and the column side compute from differently scaled operands,
+// and one bf16 rounding of each would not cancel.
+template <typename T> __device__ __forceinline__ f32x4 mma_k16r_split(k16_t<T> a, const float (&b)[4], f32x4 c) {
+  const k16_t<T> hi = k16_pack<T>(b);
+  c = mma_k16r<T>(a, hi, c);
+  if constexpr (sizeof(T) == 2) {
+    const float lo[4] = {b[0] - (float)hi[0], b[1] - (float)hi[1], b[2] - (float)hi[2], b[3] - (float)hi[3]};
+    c = mma_k16r<T>(a, k16_pack<T>(lo), c);
+  }
+  return c;
+}
+
 // Per-chunk gradients: one persistent kernel, one workgroup per compute unit walking the
 // (chunk, head) items of the round, each item in two halves.
 //
@@ -570,6 +585,41 @@ struct GFCfg {
   static_assert(TOTAL <= 160 * 1024, "fused gradient kernel LDS budget");
 };
 
+// Pairwise diagonal-block terms of block bb for a steep channel c (block gate sum below
+// -kSteepGate), this lane's rows i = 16 bb + 4 g4 + r:
+//   dq_i += sum_{j <= i} dM_ij k_jc e^{L_ic - L_jc},   dk_i (row) += sum_{j < i} dA_ij k_jc e^{L_ic - L_jc},
+//   dk_i (col) += sum_{j >= i} (dM_ji q_jc + dA_ji k_jc) e^{L_jc - L_ic},
+// L the block-local cumulative log-decays, taken from the lanes that hold them (lane cc + 16 q
+// holds rows 4 q .. 4 q + 3 of channel c), so the j = i terms carry exactly e^0.  Called by the
+// whole wave.
+template <typename T, int LDK, int LDJ>
+__device__ __forceinline__ void steep_diag_grad(const T* Qb, const T* Kb, const T* dMl, const T* dAl, int bb, int c,
+                                                int cc, int g4, const float (&Li)[4], bool mine, f32x4& dq, f32x4& kr,
+                                                f32x4& kc) {
+  // a rolled loop over j keeps this rarely taken path from raising the register demand of the
+  // kernel around it; lanes whose channel is not steep add nothing
+  const float w = mine ? 1.f : 0.f;
+#pragma unroll 1
+  for (int j = 0; j < 16; ++j) {
+    const int t = j & 3;
+    const float lsrc = t == 0 ? Li[0] : t == 1 ? Li[1] : t == 2 ? Li[2] : Li[3];
+    const float lj = __shfl(lsrc, cc + 16 * (j >> 2), 64);
+    const int rj = 16 * bb + j;
+    const float kj = w * to_f(Kb[rj * LDK + c]), qj = w * to_f(Qb[rj * LDK + c]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * g4 + r, ri = 16 * bb + i;
+      if (j <= i) {
+        const float e = __expf(fminf(Li[r] - lj, 0.f));
+        dq[r] += to_f(dMl[ri * LDJ + rj]) * kj * e;
+        if (j < i) kr[r] += to_f(dAl[ri * LDJ + rj]) * kj * e;
+      }
+      if (j >= i)
+        kc[r] += (to_f(dMl[rj * LDJ + ri]) * qj + to_f(dAl[rj * LDJ + ri]) * kj) * __expf(fminf(lj - Li[r], 0.f));
+    }
+  }
+}
+
 template <typename T, int BT, int D, int DV>
 __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b, int H) {
   using C = GFCfg<T, BT, D, DV>;
@@ -699,20 +749,17 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
     // the item after the next one: its rows are fetched a whole item ahead of their use
     const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
     ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
-    // A2. decay per (16-row block, channel): block-local cumulative L, block totals
-    float Lr[16];
+    // A2. decay per (16-row block, channel): block totals
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
       float s = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        s += to_f(Gs[(16 * bb + t) * LDK + c]);
-        Lr[t] = s;
-      }
+      for (int t = 0; t < 16; ++t) s += to_f(Gs[(16 * bb + t) * LDK + c]);
       Tbv[bb * D + c] = s;
     }
     __syncthreads();
-    // A3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k
+    // A3. K~ = k e^{F_b + L} over g, K^ = k e^{G_last - F_b - L} over k, L the block-local
+    //     cumulative log-decay (summed again rather than held across the barrier)
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
       float fb = 0.f, fe = 0.f;
@@ -722,12 +769,14 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
         fb += q < bb ? tq : 0.f;
         fe += tq;
       }
+      float Lr = 0.f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const int i = 16 * bb + t;
+        Lr += to_f(Gs[i * LDK + c]);
         const float kv = to_f(Ks[i * LDK + c]);
-        Kt[i * LDK + c] = from_f<T>(kv * __expf(fb + Lr[t]));
-        Kh[i * LDK + c] = from_f<T>(kv * __expf(fe - fb - Lr[t]));
+        Kt[i * LDK + c] = from_f<T>(kv * __expf(fb + Lr));
+        Kh[i * LDK + c] = from_f<T>(kv * __expf(fe - fb - Lr));
       }
     }
     __syncthreads();
@@ -908,8 +957,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
 
     // ---------------- channel side ----------------
     const int c = 16 * wave + cc;
-    // B2. state products (raw): dO S0^T, dR S0^T, U dS^T; rowsum(dS .* S0) for dG_last
-    f32x4 dqa[NB], X1[NB], X23[NB], X4[NB];
+    // B2. state products (raw): dO S0^T, dR S0^T, U dS^T (into X23, where the column side of the
+    //     block products accumulates on top of it: both take the factor e^{F_{b+1} - G_j}, B4);
+    //     rowsum(dS .* S0) for dG_last
+    f32x4 dqa[NB], X1[NB], X23[NB];
     float rs = 0.f;
     if constexpr (sizeof(T) == 2) {
       // this wave's channels of S_n, then of dS_n, through its LDS slice [DV][16] (over R0 and
@@ -931,7 +982,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       for (int ks = 0; ks < CB::NKS; ++ks) hf[ks] = frag(ks);
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+        dqa[bb] = X1[bb] = X23[bb] = z4;
 #pragma unroll
         for (int ks = 0; ks < CB::NKS; ++ks) {
           dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), hf[ks], dqa[bb]);
@@ -945,19 +996,19 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
 #pragma unroll
         for (int t = 0; t < 8; ++t) rs += (float)hf[ks][t] * (float)df[t];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), df, X4[bb]);
+        for (int bb = 0; bb < NB; ++bb) X23[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), df, X23[bb]);
       }
     } else {
 #pragma unroll
       for (int ks = 0; ks < CB::NKS; ++ks) rs += cb.hc[ks] * cb.dhc[ks];
 #pragma unroll
       for (int bb = 0; bb < NB; ++bb) {
-        dqa[bb] = X1[bb] = X4[bb] = X23[bb] = z4;
+        dqa[bb] = X1[bb] = X23[bb] = z4;
 #pragma unroll
         for (int ks = 0; ks < CB::NKS; ++ks) {
           dqa[bb] = MM::mma(MM::kc(dOs, LDV, 16 * bb, ks * MM::KS, lane), cb.hc[ks], dqa[bb]);
           X1[bb] = MM::mma(MM::kc(dRs, LDV, 16 * bb, ks * MM::KS, lane), cb.hc[ks], X1[bb]);
-          X4[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cb.dhc[ks], X4[bb]);
+          X23[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), cb.dhc[ks], X23[bb]);
         }
       }
     }
@@ -1002,72 +1053,90 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       Tb[bb] = tot[0] + tot[1] + tot[2] + tot[3];
       F[bb + 1] = F[bb] + Tb[bb];
     }
+    // gated state products; csum = sum over this lane's rows of k e^{G_last - G} (U dS^T), the
+    // K^ part of dG_last
     rs *= __expf(F[NB]);
+    float csum = 0.f;
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       const float ef = __expf(F[bb]), eh = __expf(F[NB] - F[bb + 1]);
+      float kvv[4];
+      col4_load<T>(Kb, LDK, 16 * bb, 16 * wave, lane, kvv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         dqa[bb][r] *= ef;
         X1[bb][r] *= -ef;
-        X4[bb][r] *= eh;
+        X23[bb][r] *= eh;
+        csum += kvv[r] * __expf(Tb[bb] - L[bb][r]) * X23[bb][r];
       }
     }
     ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    float eL[NB][4], enL[NB][4];
+    float eL[NB][4];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        eL[bb][r] = __expf(L[bb][r]);
-        enL[bb][r] = __expf(-L[bb][r]);
-      }
-    // B4. 16-token block products with the gated masks factored per block pair:
-    //     row side  sum_j P_ij k_j e^{F_bi - G_j}                  (P = dM -> dq, P = dA -> dk)
-    //     col side  sum_i P_ij x_i e^{G_i - F_bi} e^{F_bi - F_bj}  (x = q for dM, k for dA)
+      for (int r = 0; r < 4; ++r) eL[bb][r] = __expf(L[bb][r]);
+    // B4. 16-token block products with the gated masks factored per block pair, every
+    //     exponent <= 0 off the diagonal blocks (P = dM with x = q, P = dA with x = k):
+    //     row side  sum_j P_ij k_j e^{F_bi - G_j}      (F_bi - G_j = F_bi - F_bj - L_j <= T_bj - L_j <= 0)
+    //     col side  sum_i P_ij x_i e^{G_i - F_{bj+1}},  e^{G_i - F_{bj+1}} = e^{L_i} e^{F_bi - F_{bj+1}}
+    //     and on a diagonal block e^{-L_j} and e^{L_i - T_b} = e^{L_i} e^{-T_b}, both at most
+    //     e^{kSteepGate}; a steep block (gate sum below -kSteepGate) takes 0 here and its
+    //     diagonal terms pairwise in B5
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
-        const float epf = bi == bj ? 1.f : __expf(F[bi] - F[bj]);  // <= 1
+        const bool dg = bi == bj, stp = Tb[bi] < -kSteepGate;
+        const float ep = dg ? (stp ? 0.f : __expf(-Tb[bi])) : __expf(F[bi] - F[bj + 1]);
         float bk[4];
         col4_load<T>(Kb, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bk[t] *= epf * enL[bj][t];
-        const k16_t<T> bkk = k16_pack<T>(bk);
-        dqa[bi] = mma_k16r<T>(k16_row<T>(dMl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, dqa[bi]);
-        X1[bi] = mma_k16r<T>(k16_row<T>(dAl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4), bkk, X1[bi]);
+        for (int t = 0; t < 4; ++t) bk[t] *= (dg && stp) ? 0.f : __expf(F[bi] - F[bj] - L[bj][t]);
+        const k16_t<T> dMr = k16_row<T>(dMl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);
+        const k16_t<T> dAr = k16_row<T>(dAl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);
+        dqa[bi] = mma_k16r_split<T>(dMr, bk, dqa[bi]);
+        X1[bi] = mma_k16r_split<T>(dAr, bk, X1[bi]);
         float bq[4], bk2[4];
         col4_load<T>(Qb, LDK, 16 * bi, 16 * wave, lane, bq);
         col4_load<T>(Kb, LDK, 16 * bi, 16 * wave, lane, bk2);
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const float e = eL[bi][t] * epf;
+          const float e = eL[bi][t] * ep;
           bq[t] *= e;
           bk2[t] *= e;
         }
-        X23[bj] = mma_k16r<T>(k16_col<T>(dMl, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bq), X23[bj]);
-        X23[bj] = mma_k16r<T>(k16_col<T>(dAl, LDJ, 16 * bi, 16 * bj, lane), k16_pack<T>(bk2), X23[bj]);
+        X23[bj] = mma_k16r_split<T>(k16_col<T>(dMl, LDJ, 16 * bi, 16 * bj, lane), bq, X23[bj]);
+        X23[bj] = mma_k16r_split<T>(k16_col<T>(dAl, LDJ, 16 * bi, 16 * bj, lane), bk2, X23[bj]);
       }
     ga_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    // B5. assemble dq, dk, dG with exact q, k and fp32 factors
-    float csum = 0.f;
+    // B5. assemble dq, dk, dG with exact q, k and fp32 factors: dq into dqa, the row and column
+    //     parts of dk into X1 and X23, then the steep blocks' pairwise diagonal terms, then dk and dG
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float er = eL[bb][r];
+        dqa[bb][r] *= er;
+        X1[bb][r] *= er;
+        X23[bb][r] *= __expf(Tb[bb] - L[bb][r]);
+      }
+    }
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      const bool steep = Tb[bb] < -kSteepGate;
+      if (__any(steep)) steep_diag_grad<T, LDK, LDJ>(Qb, Kb, dMl, dAl, bb, 16 * wave + cc, cc, g4, L[bb], steep, dqa[bb], X1[bb], X23[bb]);
+    }
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       float kvv[4], qvv[4];
       col4_load<T>(Kb, LDK, 16 * bb, 16 * wave, lane, kvv);
       col4_load<T>(Qb, LDK, 16 * bb, 16 * wave, lane, qvv);
-      const float eT = __expf(Tb[bb]);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float er = eL[bb][r], ecd = enL[bb][r], ec = eT * ecd;
-        const float dq = er * dqa[bb][r];
-        const float krow = er * X1[bb][r], kcol = ecd * X23[bb][r] + ec * X4[bb][r];
-        const float kv = kvv[r], qv = qvv[r];
-        dqa[bb][r] = dq;
-        X1[bb][r] = krow + kcol;                    // dk
-        X23[bb][r] = qv * dq + kv * (krow - kcol);  // dG
-        csum += kv * ec * X4[bb][r];
+        const float dq = dqa[bb][r], krow = X1[bb][r], kcol = X23[bb][r];
+        X1[bb][r] = krow + kcol;                            // dk
+        X23[bb][r] = qvv[r] * dq + kvv[r] * (krow - kcol);  // dG
       }
     }
     csum += __shfl_xor(csum, 16, 64);

@@ -9,10 +9,18 @@
 //   W = T (K e^G), U' = T V,
 //   U = U' - W S0,  O = (Q e^G) S0 + M U,  S = diag(e^{G_last}) S0 + (K e^{G_last - G})^T U.
 // "gated" products use e^{G_i - G_j} factored through 16-row sub-block
-// reference points: for rows i in block bi and j in block bj <= bi,
-// e^{G_i - G_j} = e^{G_i - F_bi} * e^{F_bi - G_j}, F_b the log-decay before
-// block b; both factors are <= 1 off the diagonal blocks, and within a
-// diagonal block the pair is bounded by one 16-row gate sum.
+// reference points: for rows i in block bi and j in block bj < bi,
+// e^{G_i - G_j} = e^{G_i - F_bi} * e^{F_bi - F_{bj+1}} * e^{F_{bj+1} - G_j}, F_b the
+// log-decay before block b; every factor is an exponential of a non-positive
+// number, formed directly.  Within a diagonal block the pair (i, j <= i) factors
+// as e^{L_i} * e^{-L_j} (L the block-local cumulative log-decay) when
+// L_i >= -kSteepGate, which bounds both factors by e^{kSteepGate}; the terms of
+// the "steep" (row, channel) elements with L_i < -kSteepGate are masked out of
+// the matrix-core product and summed pairwise, e^{L_i - L_j} directly, in a
+// separate step.  The decision depends on row i alone, so a row's results never
+// depend on the rows after it (tree and expanded execution stay bitwise equal),
+// and the result is exact (to fp32 rounding) for every g <= 0, including the
+// g -> -inf limit.
 #include <type_traits>
 
 #include "common.h"
@@ -45,10 +53,20 @@ struct PrepLayout {
   static constexpr size_t SX = cmax(al(size_t(NPX) * 16 * LDK * ES), O_TM + TM_SZ > O_SX ? O_TM + TM_SZ - O_SX : 0);
   static constexpr size_t O_A = O_SX + SX;  // A (fp32 [BT][LDA])
   static constexpr size_t O_VEC = O_A + X_SZ;
-  // vectors (fp32): Tv[NB][D], Fv[NB+1][D], EF[NB+1][D], EH[NB][D], Sx[NPX][D], bet[BT]
+  // vectors (fp32): Tv[NB][D], Fv[NB+1][D], EF[NB+1][D], EH[NB][D], Sx[NPX][D], bet[BT],
+  // DA[NB][16][16] and DM[NB][16][16] (pairwise diagonal-block sums of the steep elements),
+  // stf[NB + 1] (int: block b has a steep element; [NB]: any block has), then the steep mask
+  // (bytes [BT][D / VN]: bit t of byte (i, g) marks element (i, VN g + t))
   static constexpr size_t TV = 0, FV = TV + NB * D, EF = FV + (NB + 1) * D, EH = EF + (NB + 1) * D,
-                          SXV = EH + NB * D, BET = SXV + (NPX > 0 ? NPX : 1) * D;
-  static constexpr size_t TOTAL = O_VEC + (BET + BT) * 4;
+                          SXV = EH + NB * D, BET = SXV + (NPX > 0 ? NPX : 1) * D, DAV = BET + BT,
+                          DMV = DAV + NB * 256, STF = DMV + NB * 256, SMK = STF + NB + 1;
+  static constexpr int MKR = D / VN;  // mask bytes per row
+  // raw k and q of one 16-row block for the pairwise steep terms ([16][LDK] each): over A, which
+  // is first written after that step, when it fits there
+  static constexpr size_t STG_SZ = al(size_t(2) * 16 * LDK * ES);
+  static constexpr bool STG_IN_A = STG_SZ <= X_SZ;
+  static constexpr size_t O_STG = STG_IN_A ? O_A : O_VEC + SMK * 4 + al(size_t(BT) * MKR);
+  static constexpr size_t TOTAL = O_VEC + SMK * 4 + al(size_t(BT) * MKR) + (STG_IN_A ? 0 : STG_SZ);
   static_assert(TOTAL <= 160 * 1024, "prep kernel LDS budget");
 };
 
@@ -126,6 +144,81 @@ __device__ __forceinline__ void prep_load_v(f32x4* v, const PrepRows<T, BT, D, D
   }
 }
 
+// An operand fragment of rows r0 + lane % 16 (contraction = channels k0 + ..., as Mma<T>::kc reads
+// them) with the steep elements of its row zeroed; mrow is the row's mask (bit t of byte g marks
+// channel VN g + t, VN = 16 / sizeof(T)).
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::Frag steep_masked(typename Mma<T>::Frag f, const uint8_t* mrow, int k0,
+                                                              int lane) {
+  if constexpr (sizeof(T) == 2) {
+    const int bits = mrow[(k0 + 8 * (lane >> 4)) / 8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((bits >> e) & 1) f[e] = bf16(0.f);
+    return f;
+  } else {
+    const int c = k0 + (lane >> 4);
+    return ((mrow[c / 4] >> (c % 4)) & 1) ? 0.f : f;
+  }
+}
+
+// Pairwise diagonal-block terms of the steep elements (row i, channel c with L_ic < -kSteepGate,
+// marked in the mask), block after block for the blocks that have one: the raw k and q of the
+// block's rows are staged from the registers that hold them (PrepIn, thread-owned pieces) into
+// Sk, Sq ([16][LDK]), then thread tid takes entry (i, j) = (tid / 16 % 16, tid % 16) of A
+// (tid < 256) or M (tid >= 256) and sums x_ic k_jc e^{L_ic - L_jc} over row i's steep channels,
+// x = k for A (i > j) and q for M (i >= j), L the block-local cumulative log-decays in Gf.  No
+// global memory is read, so the loads in flight for the next item are not waited for.  Called
+// by the whole workgroup; ends with a barrier.
+template <typename T, int BT, int D, int DV>
+__device__ __forceinline__ void steep_diag_sums(float* DA, float* DM, T* Sk, T* Sq, const float* Gf,
+                                                const uint8_t* smask, const int* stf,
+                                                const PrepIn<T, BT, D, DV>& cur, const PrepRows<T, BT, D, DV>& rows,
+                                                int tid) {
+  using P = PrepIn<T, BT, D, DV>;
+  constexpr int NB = BT / 16, VN = 16 / sizeof(T), LDF = D + 4, MKR = D / VN, LDK = D + VN;
+  const bool isM = tid >= 256;
+  const int i = (tid >> 4) & 15, j = tid & 15;
+  const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
+  // rolled loops: this step runs only for steep blocks and must not grow the kernel's code
+#pragma unroll 1
+  for (int b = 0; b < NB; ++b) {
+    if (!stf[b]) continue;
+#pragma unroll
+    for (int x = 0; x < P::NK; ++x) {
+      const int p = tid + CNT * x;
+      const int r = p / P::NPR - 16 * b, c0 = (p % P::NPR) * VN;
+      if (p < P::NPK && r >= 0 && r < 16) {
+        const bool ok = rows.rk[x] >= 0;
+        stq(Sk + r * LDK + c0, ok ? cur.k[x] : z4);
+        stq(Sq + r * LDK + c0, ok ? cur.q[x] : z4);
+      }
+    }
+    __syncthreads();
+    if (tid < 512) {
+      float acc = 0.f;
+      if (isM ? i >= j : i > j) {
+        const T* xp = (isM ? Sq : Sk) + i * LDK;
+        const T* kp = Sk + j * LDK;
+        const float* Li = Gf + (16 * b + i) * LDF;
+        const float* Lj = Gf + (16 * b + j) * LDF;
+        const uint8_t* mrow = smask + (16 * b + i) * MKR;
+#pragma unroll 1
+        for (int g = 0; g < MKR; ++g) {
+          const int bits = mrow[g];
+          if (!bits) continue;
+#pragma unroll
+          for (int t = 0; t < VN; ++t)
+            if ((bits >> t) & 1)
+              acc += to_f(xp[VN * g + t]) * to_f(kp[VN * g + t]) * __expf(Li[VN * g + t] - Lj[VN * g + t]);
+        }
+      }
+      (isM ? DM : DA)[b * 256 + i * 16 + j] = acc;
+    }
+    __syncthreads();
+  }
+}
+
 // ------------------------------------------------------------------------------------------
 // Per-chunk preparation.  Persistent: one workgroup of CNT threads per CU walks the
 // (chunk, head) items of the round; the next item's rows and inputs are fetched into
@@ -166,6 +259,10 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   float* EH = vec + Ly::EH;
   float* Sx = vec + Ly::SXV;
   float* bet = vec + Ly::BET;
+  float* DA = vec + Ly::DAV;
+  float* DM = vec + Ly::DMV;
+  int* stf = reinterpret_cast<int*>(vec + Ly::STF);
+  uint8_t* smask = reinterpret_cast<uint8_t*>(vec + Ly::SMK);
 
   const int tid0 = threadIdx.x;
   const int nitems = a.nchunk * H;
@@ -218,6 +315,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
+    if (tid <= NB) stf[tid] = 0;
     __syncthreads();
     // the item after the next one: its rows are fetched a whole item ahead of their use
     const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
@@ -254,18 +352,16 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
 #pragma unroll
       for (int b = 0; b < NB; ++b) EH[b * D + c] = __expf(f - fv[b + 1]);
-      // block totals become e^{T_b}: e^{T_b - L} = e^{T_b} e^{-L} below
-#pragma unroll
-      for (int b = 0; b < NB; ++b) Tv[b * D + c] = __expf(tb[b]);
 #pragma unroll
       for (int bi = 2; bi < NB; ++bi)
 #pragma unroll
         for (int bj = 0; bj + 2 <= bi; ++bj) Sx[pair_index(bi, bj) * D + c] = __expf(fv[bi] - fv[bj + 1]);
     }
     __syncthreads();
-    // 4. operand arrays: Kr = k e^L, Qr = q e^L, Kc0 = k e^{T_b - L}, Kcd = k e^{-L}, Kcx = Kc0 * pair scale.
-    //    L stays in registers for step 6.
-    float Er[NK][VN], En[NK][VN];  // e^{L}, e^{-L} of this thread's elements
+    // 4. operand arrays: Kr = k e^L, Qr = q e^L, Kc0 = k e^{T_b - L}, Kcd = k e^{-L} (0 on steep
+    //    elements, L < -kSteepGate, which are marked in the mask), Kcx = Kc0 * pair scale.
+    //    e^L and e^{T_b - L} stay in registers for step 6.
+    float Er[NK][VN], En[NK][VN];  // e^{L}, e^{T_b - L} of this thread's elements
     const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int x = 0; x < NK; ++x) {
@@ -275,17 +371,22 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         float kk[VN], qq[VN], kr[VN], qr[VN], kc[VN], kd[VN];
         unpack16<T>(rows.rk[x] >= 0 ? cur.k[x] : z4, kk);
         unpack16<T>(rows.rk[x] >= 0 ? cur.q[x] : z4, qq);
+        int bits = 0;
 #pragma unroll
         for (int t = 0; t < VN; ++t) {
-          const float Lv = Gf[i * LDF + c0 + t];
-          const float er = __expf(Lv), en = __expf(-Lv);
+          const float Lv = Gf[i * LDF + c0 + t], Tb = Gf[(16 * b + 15) * LDF + c0 + t];
+          const bool st = Lv < -kSteepGate;
+          const float er = __expf(Lv), ec = __expf(Tb - Lv), en = __expf(st ? 0.f : -Lv);
           Er[x][t] = er;
-          En[x][t] = en;
+          En[x][t] = ec;
           kr[t] = kk[t] * er;
           qr[t] = qq[t] * er;
-          kc[t] = kk[t] * (Tv[b * D + c0 + t] * en);
-          kd[t] = kk[t] * en;
+          kc[t] = kk[t] * ec;
+          kd[t] = st ? 0.f : kk[t] * en;
+          bits |= int(st) << t;
         }
+        smask[i * Ly::MKR + c0 / VN] = uint8_t(bits);
+        if (bits) stf[b] = stf[NB] = 1;
         stq(Kr + i * LDK + c0, pack16<T>(kr));
         stq(Qr + i * LDK + c0, pack16<T>(qr));
         stq(Kc0 + i * LDK + c0, pack16<T>(kc));
@@ -304,6 +405,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     }
     __syncthreads();
     prep_load<T, BT, D, DV, 2>(nxt, rows_x, a, hn, H, tid);
+    // 4b. steep channels of a diagonal block: A_ij and M_ij terms sum_c x_ic k_jc e^{L_ic - L_jc}
+    //     formed pairwise (x = k for A, q for M) from the raw inputs, one entry per thread
+    if (stf[NB])
+      steep_diag_sums<T, BT, D, DV>(DA, DM, reinterpret_cast<T*>(smem + Ly::O_STG),
+                                    reinterpret_cast<T*>(smem + Ly::O_STG) + 16 * LDK, Gf, smask, stf, cur, rows, tid);
     // 5. A (strict lower, fp32) into Af; M (lower incl.) to the workspace (and Ml), one 16x16 tile each
     T* Mg = static_cast<T*>(a.ws.Mm) + wsi * BT * BT;
     {
@@ -316,9 +422,20 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           const T* col = bi == bj ? Kcd + 16 * bj * LDK
                          : (bi - bj == 1 ? Kc0 + 16 * bj * LDK : Kcx + pair_index(bi, bj) * 16 * LDK);
           f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          if (bi == bj && stf[bi]) {
+            // steep elements of the rows masked out, their terms summed pairwise (DA)
+            const uint8_t* mrow = smask + (16 * bi + (lane & 15)) * Ly::MKR;
 #pragma unroll
-          for (int k0 = 0; k0 < D; k0 += MM::KS)
-            acc = MM::mma(MM::kc(Kr + 16 * bi * LDK, LDK, 0, k0, lane), MM::kc(col, LDK, 0, k0, lane), acc);
+            for (int k0 = 0; k0 < D; k0 += MM::KS)
+              acc = MM::mma(steep_masked<T>(MM::kc(Kr + 16 * bi * LDK, LDK, 0, k0, lane), mrow, k0, lane),
+                            MM::kc(col, LDK, 0, k0, lane), acc);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] += DA[bi * 256 + crow(lane, r) * 16 + ccol(lane)];
+          } else {
+#pragma unroll
+            for (int k0 = 0; k0 < D; k0 += MM::KS)
+              acc = MM::mma(MM::kc(Kr + 16 * bi * LDK, LDK, 0, k0, lane), MM::kc(col, LDK, 0, k0, lane), acc);
+          }
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int i = 16 * bi + crow(lane, r), j = 16 * bj + ccol(lane);
@@ -332,9 +449,19 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             const T* col = bi == bj ? Kcd + 16 * bj * LDK
                            : (bi - bj == 1 ? Kc0 + 16 * bj * LDK : Kcx + pair_index(bi, bj) * 16 * LDK);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if (bi == bj && stf[bi]) {
+              const uint8_t* mrow = smask + (16 * bi + (lane & 15)) * Ly::MKR;
 #pragma unroll
-            for (int k0 = 0; k0 < D; k0 += MM::KS)
-              acc = MM::mma(MM::kc(col, LDK, 0, k0, lane), MM::kc(Qr + 16 * bi * LDK, LDK, 0, k0, lane), acc);
+              for (int k0 = 0; k0 < D; k0 += MM::KS)
+                acc = MM::mma(MM::kc(col, LDK, 0, k0, lane),
+                              steep_masked<T>(MM::kc(Qr + 16 * bi * LDK, LDK, 0, k0, lane), mrow, k0, lane), acc);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[r] += DM[bi * 256 + ccol(lane) * 16 + crow(lane, r)];
+            } else {
+#pragma unroll
+              for (int k0 = 0; k0 < D; k0 += MM::KS)
+                acc = MM::mma(MM::kc(col, LDK, 0, k0, lane), MM::kc(Qr + 16 * bi * LDK, LDK, 0, k0, lane), acc);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
@@ -391,7 +518,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           const float er = Er[x][t], ef = EF[b * D + c0 + t];
           kt[t] = kk[t] * er * ef;
           qt[t] = qq[t] * er * ef;
-          kh[t] = kk[t] * (Tv[b * D + c0 + t] * En[x][t]) * EH[b * D + c0 + t];
+          kh[t] = kk[t] * En[x][t] * EH[b * D + c0 + t];
         }
         stq(Kt + i * LDK + c0, pack16<T>(kt));
         if constexpr (BWD && !PF) fm_store<T>(static_cast<T*>(a.ws.Kh) + wsi * BT * D, D, i, c0, kh, VN);
