@@ -18,7 +18,8 @@ Contents, each written from the pages (HARTS, arXiv 2608.28158):
   hand-derived reverse pass (C, OpenMP; ``recurrent.c``).
 * ``oracle.chunkwise`` -- float64 chunkwise form of the same rule, and a tree
   execution with bounded replay built on it (used only for self-checks).
-* ``oracle.logprob``   -- float64 log-softmax gather from its definition, its
+* ``oracle.logprob``   -- float64 log-softmax gather from its definition (per position,
+  or with each row's log-sum-exp taken once by a library routine), its
   gradient (per-position terms summed into their compact row), occurrence
   counts.
 * ``oracle.conv``      -- float64 depthwise causal convolution over each

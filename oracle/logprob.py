@@ -37,6 +37,19 @@ def logprob(rows_fp64: np.ndarray, row_index: np.ndarray, labels: np.ndarray) ->
     return out
 
 
+def logprob_rowwise(rows_fp64, row_index: np.ndarray, labels: np.ndarray) -> np.ndarray:
+    """The same log p_s, with each row's log-sum-exp taken once by a library routine
+    (``torch.logsumexp`` over a float64 CPU tensor) and read by every position of that row; for
+    full-size rows, where forming it again for each of the S positions would cost S * V
+    exponentials.  ``rows_fp64``: float64 logits [R, V] (numpy or CPU torch)."""
+    import torch
+    x = torch.as_tensor(rows_fp64, dtype=torch.float64)
+    lse = torch.logsumexp(x, dim=1)
+    ri = torch.as_tensor(np.asarray(row_index, dtype=np.int64))
+    lab = torch.as_tensor(np.asarray(labels, dtype=np.int64))
+    return (x[ri, lab] - lse[ri]).numpy()
+
+
 def counts(m: np.ndarray, C: int) -> np.ndarray:
     """q_c = #{s : m(s) = c}."""
     q = np.zeros(C, dtype=np.int64)

@@ -27,6 +27,22 @@ def test_matches_library_log_softmax():
     np.testing.assert_allclose(logprob.logprob(x, m, y), want, rtol=0, atol=1e-12)
 
 
+def test_rowwise_form_matches_the_per_position_definition_and_library():
+    rng = np.random.default_rng(3)
+    C, V = 23, 777
+    x = rng.standard_normal((C, V)) * 3.0
+    x[5] = 1.25  # a constant row: exactly -ln V
+    m = rng.integers(0, C, size=200)
+    m[:4] = 5
+    y = rng.integers(0, V, size=200)
+    got = logprob.logprob_rowwise(x, m, y)
+    np.testing.assert_allclose(got, logprob.logprob(x, m, y), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got, scipy.special.log_softmax(x, axis=1)[m, y], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(got[:4], -np.log(V), rtol=0, atol=1e-12)
+    big = np.array([[1000.0, 0.0, -1000.0]])
+    np.testing.assert_allclose(logprob.logprob_rowwise(big, [0, 0], [0, 2]), [0.0, -2000.0], atol=1e-12)
+
+
 def test_large_logits_are_stable():
     x = np.array([[1000.0, 0.0, -1000.0]])
     lp = logprob.logprob(x, np.array([0, 0]), np.array([0, 1]))
