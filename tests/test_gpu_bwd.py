@@ -27,8 +27,8 @@ def run_tree_bwd(t, feats, B, H, D, dt, keep=False):
     x = device_inputs(feats, nodes)
     dp = harts.DevicePlan(hp, H, D, D, harts_dtype(dt))
     ns = max(1, hp.info.n_slots)
-    o = torch.zeros((C, H, D), dtype=torch_dtype(dt), device="cuda")
-    slots = torch.zeros((ns, H, D, D), dtype=torch.float32, device="cuda")
+    o = torch.full((C, H, D), float("nan"), dtype=torch_dtype(dt), device="cuda")
+    slots = torch.full((ns, H, D, D), float("nan"), dtype=torch.float32, device="cuda")
     ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True), dp.workspace_size(2)),
                      dtype=torch.uint8, device="cuda")
     harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=keep)
@@ -165,46 +165,6 @@ def test_backward_repeat_runs_are_identical():
     b = run_tree_bwd(t, feats, 64, 2, 128, "bf16")[2]
     for k in a:
         assert np.array_equal(a[k], b[k]), k
-
-
-def test_rollout_tree_backward_sampled():
-    """Full 64-leaf tree, H=16, d=128, in the benchmark's configuration (the forward keeps
-    the backward's operands): every compact row's gradient checked on the leaf-only rows
-    (multiplicity 1) of the two trajectories with the most of them, whose gradients depend
-    only on their own trajectory; the recomputing backward must agree bit for bit."""
-    H, D, B = 16, 128, 64
-    t = trees.random_rollout_tree(seed=0)
-    feats = tensors.draw_features(t.n_nodes, H, D, D, seed=1, dtype="bf16")
-    hp, nodes_h, got, q = run_tree_bwd(t, feats, B, H, D, "bf16", keep=True)
-    rec = run_tree_bwd(t, feats, B, H, D, "bf16")[2]
-    for k in got:
-        assert np.array_equal(got[k], rec[k], equal_nan=True), k
-    del rec
-    for n in ("dq", "dk", "dv", "dg", "dbeta"):
-        assert not np.isnan(got[n]).any(), n
-    m, _, _ = hp.maps()
-    leaf_rows = np.array([(q[m[t.offsets[x]:t.offsets[x + 1]]] == 1).sum() for x in range(t.n_traj)])
-    which = [int(i) for i in np.argsort(-leaf_rows)[:2]]
-    F = oracle_feats(feats)
-    rows = [t.node_of_pos[t.offsets[x]:t.offsets[x + 1]] for x in which]
-    tr = Trajectories(rows, F["q"], F["k"], F["v"], F["g"], F["beta"])
-    dO = np.concatenate([F["do"][r] for r in rows])
-    ref = tr.backward(dO)
-    sel_pos, sel_rows = [], []
-    base = 0
-    for x in which:
-        mm = m[t.offsets[x]:t.offsets[x + 1]]
-        own = np.nonzero(q[mm] == 1)[0]
-        sel_pos.append(base + own)
-        sel_rows.append(mm[own])
-        base += len(mm)
-    sel_pos = np.concatenate(sel_pos)
-    sel_rows = np.concatenate(sel_rows)
-    assert len(sel_rows) > 1000
-    for n in ("dq", "dk", "dv", "dg", "dbeta"):
-        e = rel_err(got[n][sel_rows], ref[n][sel_pos])
-        print(n, "rows", len(sel_rows), "rel err", e)
-        assert e <= TOL["bf16"], (n, e)
 
 
 def test_graph_replay_equals_eager():

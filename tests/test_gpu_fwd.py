@@ -167,10 +167,10 @@ def _varlen_case(lens, H, D, B, dt, seed, emit=True):
     dp = harts.DevicePlan(vp, H, D, D, harts_dtype(dt))
     x = device_inputs(feats, np.arange(cu[-1]))
     N = int(cu[-1])
-    o = torch.zeros((N, H, D), dtype=torch_dtype(dt), device="cuda")
+    o = torch.full((N, H, D), float("nan"), dtype=torch_dtype(dt), device="cuda")
     nb = vp.info.n_boundaries
-    bst = torch.zeros((max(nb, 1), H, D, D), dtype=torch.float32, device="cuda")
-    fin = torch.zeros((n, H, D, D), dtype=torch.float32, device="cuda")
+    bst = torch.full((max(nb, 1), H, D, D), float("nan"), dtype=torch.float32, device="cuda")
+    fin = torch.full((n, H, D, D), float("nan"), dtype=torch.float32, device="cuda")
     init_t = torch.from_numpy(init).cuda()
     ws = torch.empty(dp.workspace_size(False), dtype=torch.uint8, device="cuda")
     harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=bst if emit else None,
