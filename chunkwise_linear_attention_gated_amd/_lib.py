@@ -89,6 +89,7 @@ _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
 _lpb = _sig("harts_logprob_backward", I32, P, I64, I64, I32, P, P, P, P, P, I64, P, P)
 _lp_rows = _sig("harts_logprob_rows", I32, P, I64, I64, P, P)
+_lp_check = _sig("harts_logprob_check_map", I32, P, P, I64, I64, I64)
 _conv_tables = _sig("harts_conv_tables", I32, P, P, I64, I64, I32, P, P, P)
 _conv_ws = _sig("harts_conv_workspace_size", ctypes.c_size_t, I64, I32, I32)
 _conv_fwd = _sig("harts_conv_fwd", I32, P, P, P, I64, I32, I32, I32, P, P)
@@ -301,6 +302,14 @@ def logprob_backward(logits, lse, row_off, row_pos, labels, dlogp, dlogits, stre
     dtype = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_FP32
     _check(_lpb(_ptr(logits), C, V, dtype, _ptr(lse), _ptr(row_off), _ptr(row_pos), _ptr(labels), _ptr(dlogp),
                 labels.numel(), _ptr(dlogits), _stream(stream)))
+
+
+def logprob_check_map(m, labels, C: int, V: int):
+    """harts_logprob_check_map (host): raises HartsError (HARTS_ERANGE) naming the first semantic
+    position whose row is outside [0, C) or whose label is outside [0, V)."""
+    m = np.ascontiguousarray(m, dtype=np.int64)
+    lab = None if labels is None else np.ascontiguousarray(labels, dtype=np.int32)
+    _check(_lp_check(m.ctypes.data, None if lab is None else lab.ctypes.data, m.shape[0], C, V))
 
 
 def logprob_rows(m, C: int):

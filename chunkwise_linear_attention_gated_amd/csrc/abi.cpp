@@ -48,6 +48,10 @@ struct harts_dev_plan {
          off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_dslot = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
   size_t off_ctr = 0;
+  // the workspace whose kept operands and chunk-start states the last forward left (keep = 1);
+  // a forward without keep on that workspace clears it (harts_kda_bwd with keep = 1 checks it)
+  mutable std::mutex kept_mu;
+  mutable const void* kept_ws = nullptr;
 };
 
 namespace {
@@ -398,6 +402,7 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
     *out = nullptr;
     if (H < 1) throw Error(HARTS_EINVAL, "H must be >= 1");
     if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+    harts::validate_plan(plan->p);  // every index the kernels use, before anything reaches the device
     harts::KdaDims dims{H, dk, dv, plan->p.B, dtype};
     if (!harts::kda_supported(dims))
       throw Error(HARTS_EINVAL, "unsupported (dtype, chunk_B, dk, dv) = (" + std::to_string(dtype) + ", " +
@@ -527,6 +532,11 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     // keep: the preparation also writes the backward's per-chunk operands and the serial pass
     // every chunk-start state, so that the backward neither prepares nor recomputes
     const bool keep = io->keep && slab;
+    {
+      std::lock_guard<std::mutex> lk(d->kept_mu);
+      if (keep) d->kept_ws = io->workspace;
+      else if (d->kept_ws == io->workspace) d->kept_ws = nullptr;
+    }
     int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
     hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(d->p.n_rounds), s0), "counter reset");
     fork(s0, s1, ev);
@@ -572,6 +582,11 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     char* ws = static_cast<char*>(io->workspace);
     const bool slab = harts::kda_slab_supported(d->dims);
     const bool keep = io->keep && slab;  // operands and chunk-start states are in the workspace
+    if (keep) {
+      std::lock_guard<std::mutex> lk(d->kept_mu);
+      if (d->kept_ws != io->workspace)
+        throw Error(HARTS_EINVAL, "keep = 1 needs this workspace as left by a forward with keep = 1 on this device plan");
+    }
     const int R = d->p.n_rounds;
     // Three streams, rounds in reverse:
     //   s1: preparation and state recompute of every round (they need no gradient);
@@ -717,6 +732,18 @@ int harts_logprob_backward(const void* logits, int64_t C, int64_t V, int32_t dty
     hip_check(harts::launch_logprob_bwd(logits, C, V, dtype, lse, row_off, row_pos, labels, dlogp, dlogits_out,
                                         static_cast<hipStream_t>(stream)),
               "log-prob backward kernel launch");
+  });
+}
+
+int harts_logprob_check_map(const int64_t* m, const int32_t* labels, int64_t S, int64_t C, int64_t V) {
+  return guarded([&] {
+    if (S < 0 || C < 0 || V < 1) throw Error(HARTS_EINVAL, "need S >= 0, C >= 0, V >= 1");
+    if (S > 0 && !m) throw Error(HARTS_EINVAL, "m is NULL");
+    for (int64_t s = 0; s < S; ++s) {
+      if (m[s] < 0 || m[s] >= C) throw Error(HARTS_ERANGE, "m[" + std::to_string(s) + "] is outside [0, C)");
+      if (labels && (labels[s] < 0 || labels[s] >= V))
+        throw Error(HARTS_ERANGE, "labels[" + std::to_string(s) + "] is outside [0, V)");
+    }
   });
 }
 

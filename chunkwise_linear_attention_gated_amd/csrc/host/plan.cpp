@@ -327,6 +327,73 @@ PlanHost make_plan(const TreeHost& t, int32_t B) {
   return P;
 }
 
+// ---------------------------------------------------------------------------------------------
+void validate_plan(const PlanHost& P) {
+  auto bad = [](int code, const std::string& what) { throw Error(code, "plan descriptor check: " + what); };
+  const int64_t nv = int64_t(P.vrows.size()), ns = int64_t(P.seq_desc.size()), nc = int64_t(P.chunk_desc.size());
+  const int32_t B = P.B;
+  if (B != 16 && B != 32 && B != 64) bad(HARTS_EINVAL, "chunk_B " + std::to_string(B));
+  if (ns != int64_t(P.seqs.size())) bad(HARTS_EINVAL, "sequence tables disagree");
+  for (int64_t i = 0; i < nv; ++i)
+    if (P.vrows[i] < 0 || P.vrows[i] >= P.C) bad(HARTS_ERANGE, "virtual row " + std::to_string(i) + " outside [0, C)");
+  // state indices: tree plans read and write the slot pool; varlen plans read init_states and
+  // write final_states per sequence and boundary states in [0, n_boundaries)
+  const int64_t n_init = P.varlen ? ns : P.n_slots, n_emit = P.varlen ? P.n_boundaries : P.n_slots;
+  std::vector<int32_t> produced_in(size_t(std::max<int64_t>(n_emit, 0)), -1);
+  if (int64_t(P.rounds.size()) != P.n_rounds) bad(HARTS_EINVAL, "round count");
+  int32_t seq_expect = 0, chunk_expect = 0;
+  for (int32_t r = 0; r < P.n_rounds; ++r) {
+    const RoundRange& rr = P.rounds[size_t(r)];
+    if (rr.seq0 != seq_expect || rr.seq1 < rr.seq0 || rr.seq1 > ns || rr.chunk0 != chunk_expect || rr.chunk1 < rr.chunk0 ||
+        rr.chunk1 > nc || rr.vrow0 < 0 || rr.vrow1 < rr.vrow0 || rr.vrow1 > nv)
+      bad(HARTS_ERANGE, "round " + std::to_string(r + 1) + " ranges");
+    seq_expect = rr.seq1;
+    chunk_expect = rr.chunk1;
+    for (int32_t q = rr.seq0; q < rr.seq1; ++q) {
+      const SeqDesc& d = P.seq_desc[size_t(q)];
+      const std::string who = "sequence " + std::to_string(q);
+      if (d.vbase < rr.vrow0 || d.vlen < 1 || int64_t(d.vbase) + d.vlen > rr.vrow1) bad(HARTS_ERANGE, who + " rows");
+      if (d.n_replay < 0 || d.n_replay >= B || d.n_replay > d.vlen) bad(HARTS_ERANGE, who + " replay length");
+      if (d.n_chunks != (d.vlen + B - 1) / B || d.chunk_base < 0 || rr.chunk0 + d.chunk_base + d.n_chunks > rr.chunk1)
+        bad(HARTS_ERANGE, who + " chunks");
+      if (d.init < -1 || d.init >= n_init) bad(HARTS_ERANGE, who + " initial state index");
+      if (d.final_idx < -1 || d.final_idx >= (P.varlen ? ns : 0)) bad(HARTS_ERANGE, who + " final state index");
+      if (!P.varlen && d.init >= 0 && (produced_in[size_t(d.init)] < 0 || produced_in[size_t(d.init)] >= r))
+        bad(HARTS_EINVAL, who + " consumes slot " + std::to_string(d.init) + " before a round produced it");
+      for (int32_t c = 0; c < d.n_chunks; ++c) {
+        const ChunkDesc& ch = P.chunk_desc[size_t(rr.chunk0 + d.chunk_base + c)];
+        const std::string cw = who + " chunk " + std::to_string(c);
+        if (ch.seq != q || ch.cidx != c || ch.local != d.chunk_base + c || ch.vbase != d.vbase + c * B ||
+            ch.len != std::min(B, d.vlen - c * B) || ch.own_from < 0 || ch.own_from > ch.len)
+          bad(HARTS_ERANGE, cw + " layout");
+        if (ch.emit < -1 || ch.emit >= n_emit) bad(HARTS_ERANGE, cw + " emitted state index");
+        if (ch.emit >= 0) {
+          if (produced_in[size_t(ch.emit)] >= 0) bad(HARTS_EINVAL, cw + " writes state " + std::to_string(ch.emit) + " twice");
+          produced_in[size_t(ch.emit)] = r;
+        }
+        if (ch.own_from > 0 && (ch.replay_base < 0 || ch.replay_base + ch.own_from > P.replay_total))
+          bad(HARTS_ERANGE, cw + " replay index");
+      }
+    }
+  }
+  if (seq_expect != ns || chunk_expect != nc) bad(HARTS_ERANGE, "rounds do not cover every sequence and chunk");
+  if (!P.varlen) {
+    if (int64_t(P.slot_cons_off.size()) != int64_t(P.n_slots) + 1) bad(HARTS_EINVAL, "slot consumer offsets");
+    for (size_t i = 0; i < P.slot_cons.size(); ++i)
+      if (P.slot_cons[i] < 0 || P.slot_cons[i] >= ns) bad(HARTS_ERANGE, "slot consumer index");
+    for (int32_t sl = 0; sl < P.n_slots; ++sl)
+      if (P.slot_cons_off[size_t(sl) + 1] < P.slot_cons_off[size_t(sl)] ||
+          P.slot_cons_off[size_t(sl) + 1] > int64_t(P.slot_cons.size()))
+        bad(HARTS_ERANGE, "slot consumer offsets");
+  }
+  if (P.fix_off.size() != P.fix_rows.size() + 1 || P.fix_off.back() != int32_t(P.fix_idx.size()))
+    bad(HARTS_EINVAL, "replay fixup offsets");
+  for (int32_t row : P.fix_rows)
+    if (row < 0 || row >= P.C) bad(HARTS_ERANGE, "replay fixup row outside [0, C)");
+  for (int32_t ix : P.fix_idx)
+    if (ix < 0 || ix >= P.replay_total) bad(HARTS_ERANGE, "replay fixup index");
+}
+
 PlanHost make_varlen_plan(const int64_t* cu, int64_t n, int32_t B, const uint8_t* has_init, bool emit_boundaries) {
   if (B != 16 && B != 32 && B != 64) throw Error(HARTS_EINVAL, "chunk_B must be 16, 32 or 64");
   if (n < 1 || !cu) throw Error(HARTS_EINVAL, "need at least one sequence");

@@ -92,6 +92,12 @@ struct PlanHost {
 };
 
 PlanHost make_plan(const TreeHost& tree, int32_t B);
+// Checks every device descriptor of a plan against the bounds the kernels index with (virtual
+// rows inside [0, C); sequence and chunk ranges inside the virtual-row table; replay shorter
+// than B; state indices inside the slot pool or the caller's state arrays; every handed-off
+// state produced in an earlier round than each of its consumers; fixup and consumer lists in
+// range).  Throws Error(HARTS_ERANGE or HARTS_EINVAL) naming the first violation.
+void validate_plan(const PlanHost& p);
 PlanHost make_varlen_plan(const int64_t* cu_seqlens, int64_t n_seq, int32_t B, const uint8_t* has_init,
                           bool emit_boundaries);
 

@@ -117,14 +117,21 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// A position whose row is outside [0, C) or whose label is outside [0, V) reads nothing, gets
+// NaN and is not counted.
 template <typename T>
-__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, int64_t V, const int64_t* __restrict__ m,
-                                                     const int32_t* __restrict__ labels, int64_t S,
-                                                     const float* __restrict__ lse, float* __restrict__ logp,
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, int64_t C, int64_t V,
+                                                     const int64_t* __restrict__ m, const int32_t* __restrict__ labels,
+                                                     int64_t S, const float* __restrict__ lse, float* __restrict__ logp,
                                                      int32_t* __restrict__ q) {
   for (int64_t s = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; s < S; s += int64_t(gridDim.x) * blockDim.x) {
     const int64_t c = m[s];
-    logp[s] = to_f(x[c * V + labels[s]]) - lse[c];
+    const int32_t y = labels[s];
+    if (c < 0 || c >= C || y < 0 || y >= V) {
+      logp[s] = __builtin_nanf("");
+      continue;
+    }
+    logp[s] = to_f(x[c * V + y]) - lse[c];
     if (q) atomicAdd(q + c, 1);
   }
 }
@@ -200,6 +207,7 @@ __global__ __launch_bounds__(256) void logprob_bwd_kernel(const T* __restrict__ 
   // weights of all its positions with that label, in increasing s
   for (int64_t k = threadIdx.x; k < n; k += 256) {
     const int32_t y = lab_of(k);
+    if (y < 0 || y >= V) continue;  // a label outside the vocabulary writes nothing
     bool first = true;
     for (int64_t j = 0; j < k && first; ++j) first = lab_of(j) != y;
     if (!first) continue;
@@ -245,10 +253,10 @@ hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, c
   if (S > 0) {
     const unsigned nb = unsigned((S + 255) / 256 < 8192 ? (S + 255) / 256 : 8192);
     if (dtype == 0)
-      hipLaunchKernelGGL(gather_kernel<bf16>, dim3(nb), dim3(256), 0, s, static_cast<const bf16*>(logits), V, m, labels,
-                         S, lse, logp, q);
+      hipLaunchKernelGGL(gather_kernel<bf16>, dim3(nb), dim3(256), 0, s, static_cast<const bf16*>(logits), C, V, m,
+                         labels, S, lse, logp, q);
     else
-      hipLaunchKernelGGL(gather_kernel<float>, dim3(nb), dim3(256), 0, s, static_cast<const float*>(logits), V, m,
+      hipLaunchKernelGGL(gather_kernel<float>, dim3(nb), dim3(256), 0, s, static_cast<const float*>(logits), C, V, m,
                          labels, S, lse, logp, q);
   }
   return hipGetLastError();

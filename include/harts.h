@@ -180,7 +180,11 @@ void harts_dev_plan_free(harts_dev_plan *dplan);
  *   following harts_kda_bwd with keep = 1 on the same inputs, states and
  *   workspace (untouched in between) skips the per-round preparation and state
  *   recompute.  Results are the same either way.  Honoured for the bf16
- *   configurations; elsewhere both calls recompute as with keep = 0.
+ *   configurations; elsewhere both calls recompute as with keep = 0.  The
+ *   device plan records the workspace of its last forward with keep = 1 (a
+ *   forward without keep on that workspace clears the record); harts_kda_bwd
+ *   with keep = 1 on any other workspace returns HARTS_EINVAL.  That the inputs
+ *   are the same is the caller's contract.
  */
 typedef struct {
   const void *q, *k, *v, *g, *beta;
@@ -232,7 +236,9 @@ int harts_kda_bwd(const harts_dev_plan *dplan, const harts_kda_io *io, const har
  * logp_out: device float32 [S]; q_out: device int32 [C] (may be NULL);
  * lse_out: device float32 [C] (may be NULL).
  * workspace: device, >= harts_logprob_workspace_size(C) bytes.
- * Out-of-range m or labels are not checked on the device (caller contract).
+ * A position whose m is outside [0, C) or whose label is outside [0, V) reads
+ * no logit, gets NaN and is not counted in q (harts_logprob_check_map checks
+ * host copies of m and labels beforehand).
  */
 size_t harts_logprob_workspace_size(int64_t C);
 int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype, const int64_t *m,
@@ -257,11 +263,17 @@ int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype
  * labels: device int32 [S] in [0, V); dlogp: device float32 [S].
  * dlogits_out: device [C, V], the logits' dtype, every element written; must
  *   not overlap logits.
- * Offsets, positions and labels are not checked on the device (caller contract).
+ * Offsets and positions are not checked on the device (caller contract); a
+ * label outside [0, V) adds nothing to its row.
  */
 int harts_logprob_backward(const void *logits, int64_t C, int64_t V, int32_t dtype, const float *lse,
                            const int64_t *row_off, const int64_t *row_pos, const int32_t *labels,
                            const float *dlogp, int64_t S, void *dlogits_out, void *stream);
+
+/* Host: checks host copies of m (int64 [S]) and labels (int32 [S], may be NULL)
+ * against C rows and V labels.  HARTS_OK, or HARTS_ERANGE naming the first
+ * position out of range. */
+int harts_logprob_check_map(const int64_t *m, const int32_t *labels, int64_t S, int64_t C, int64_t V);
 
 /* Host: the inverse of the semantic map m (host int64 [S], values in [0, C)) as
  * CSR arrays: row_off (host int64 [C + 1]) and row_pos (host int64 [S]), each

@@ -67,6 +67,22 @@ def test_logprob_rows_is_the_stable_inverse_of_m():
     assert e.value.code == -1 and "outside" in str(e.value)
 
 
+def test_logprob_map_check_names_the_first_position_out_of_range():
+    m = np.array([0, 2, 1, 2], np.int64)
+    lab = np.array([5, 0, 9, 3], np.int32)
+    harts.logprob_check_map(m, lab, 3, 10)
+    harts.logprob_check_map(m, None, 3, 1)
+    with pytest.raises(harts.HartsError) as e:
+        harts.logprob_check_map(np.array([0, 3, -1], np.int64), None, 3, 10)
+    assert e.value.code == -2 and "m[1]" in str(e.value)
+    with pytest.raises(harts.HartsError) as e:
+        harts.logprob_check_map(m, np.array([5, 0, 10, -1], np.int32), 3, 10)
+    assert e.value.code == -2 and "labels[2]" in str(e.value)
+    with pytest.raises(harts.HartsError) as e:
+        harts.logprob_check_map(m, np.array([5, -1, 0, 0], np.int32), 3, 10)
+    assert "labels[1]" in str(e.value)
+
+
 def test_logprob_backward_rejects_bad_arguments_before_any_device_work():
     f = _lib._lpb
     assert f(None, 4, 0, 0, None, None, None, None, None, 0, None, None) == -1  # V < 1

@@ -152,6 +152,39 @@ def test_kept_operands_equal_recompute_bitwise():
             assert np.array_equal(a[k], b[k], equal_nan=True), k
 
 
+def test_kept_backward_needs_the_kept_workspace():
+    """A backward that reads kept operands refuses a workspace no forward with keep filled, and
+    one whose record a later forward without keep cleared."""
+    t = trees.figure2_tree()
+    feats = tensors.draw_features(t.n_nodes, 2, 128, 128, seed=1, dtype="bf16")
+    hp = harts.TreePlan(t.tokens, t.offsets, 64)
+    m, _, _ = hp.maps()
+    C = hp.info.C
+    x = device_inputs(feats, node_of_row(m, t.node_of_pos, C))
+    dp = harts.DevicePlan(hp, 2, 128, 128, harts.DTYPE_BF16)
+    o = torch.zeros((C, 2, 128), dtype=torch.bfloat16, device="cuda")
+    slots = torch.zeros((max(1, hp.info.n_slots), 2, 128, 128), device="cuda")
+    ws = torch.empty(dp.workspace_size(2), dtype=torch.uint8, device="cuda")
+    ws2 = torch.empty_like(ws)
+    gr = {n: torch.zeros_like(x[n]) for n in NAMES}
+    dsl = torch.zeros_like(slots)
+
+    def bwd(w):
+        harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"], gr["g"],
+                      gr["beta"], states=slots, dstates=dsl, workspace=w, keep=True)
+
+    with pytest.raises(harts.HartsError):
+        bwd(ws)
+    harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws, keep=True)
+    with pytest.raises(harts.HartsError):
+        bwd(ws2)
+    bwd(ws)
+    harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws)
+    with pytest.raises(harts.HartsError):
+        bwd(ws)
+    torch.cuda.synchronize()
+
+
 def test_kept_operands_fp32_fall_back_to_recompute():
     t = trees.random_small_tree(np.random.default_rng(78), max_segments=6, max_len=90)
     errs = compare_tree_bwd(t, 32, 2, 32, "fp32", seed=3, keep=True)

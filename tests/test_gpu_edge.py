@@ -172,3 +172,41 @@ def test_beta0_decays_initial_states(dt, B, D):
     for nm in ("q", "k", "v", "g", "beta"):
         _check(gr[nm].float().cpu().numpy(), ref["d" + nm], dt, "d" + nm)
     _check(dinit.cpu().numpy(), ref["dS0"], dt, "dS0")
+
+
+def test_nan_in_one_sequence_stays_in_that_sequence():
+    """Inputs are not checked for NaN: a NaN value in one sequence of a packed call reaches that
+    sequence's outputs and final state, and every other sequence (forward and backward) is bit for
+    bit what it is without it."""
+    B, D, H, dt = 64, 128, 2, "bf16"
+    lens = np.array([150, 200, 90])
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    g = trees.forest_of_sequences(lens, seed=5)
+    feats = tensors.draw_features(g.n_nodes, H, D, D, seed=5, dtype=dt)
+    vp = harts.VarlenPlan(cu, B)
+    dp = harts.DevicePlan(vp, H, D, D, harts_dtype(dt))
+    ws = torch.empty(max(dp.workspace_size(False), dp.workspace_size(True)), dtype=torch.uint8, device="cuda")
+
+    def run(poison):
+        x = device_inputs(feats, np.arange(cu[-1]))
+        if poison:
+            x["v"][cu[1] + 70, 1, 5] = float("nan")
+        N = int(cu[-1])
+        o = torch.full((N, H, D), 7.0, dtype=torch_dtype(dt), device="cuda")
+        fin = torch.zeros((len(lens), H, D, D), device="cuda")
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, final_states=fin, workspace=ws)
+        gr = {n: torch.zeros_like(x[n]) for n in ("q", "k", "v", "g", "beta")}
+        harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"], gr["g"],
+                      gr["beta"], workspace=ws)
+        torch.cuda.synchronize()
+        out = {"o": o.float().cpu().numpy(), "fin": fin.cpu().numpy()}
+        out.update({n: t.float().cpu().numpy() for n, t in gr.items()})
+        return out
+
+    clean, bad = run(False), run(True)
+    other = np.r_[cu[0]:cu[1], cu[2]:cu[3]]
+    for n in ("o", "q", "k", "v", "g", "beta"):
+        assert np.array_equal(clean[n][other], bad[n][other]), n
+    assert np.array_equal(clean["fin"][[0, 2]], bad["fin"][[0, 2]])
+    assert np.isnan(bad["o"][cu[1] + 70:cu[2]]).any() and np.isnan(bad["fin"][1]).any()
+    assert np.isfinite(clean["o"]).all() and np.isfinite(clean["fin"]).all()

@@ -126,3 +126,22 @@ def test_logprob_backward_no_positions_and_repeat_runs_identical():
     a = _bwd(x, w.m, w.labels, g, C)
     b = _bwd(x, w.m, w.labels, g, C)
     assert np.array_equal(a, b)
+
+
+def test_gather_positions_out_of_range_get_nan_and_are_not_counted():
+    C, V = 9, 300
+    x = torch.randn((C, V), device="cuda").to(torch.bfloat16)
+    m = np.array([0, 3, 9, -1, 8, 3, 2], np.int64)
+    lab = np.array([1, 299, 4, 4, 300, -5, 7], np.int32)
+    logp = torch.zeros(len(m), device="cuda")
+    q = torch.full((C,), -7, dtype=torch.int32, device="cuda")
+    harts.logprob_gather(x, torch.from_numpy(m).cuda(), torch.from_numpy(lab).cuda(), logp, q=q,
+                         workspace=torch.empty(harts.logprob_workspace_size(C), dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    got = logp.cpu().numpy()
+    ok = (m >= 0) & (m < C) & (lab >= 0) & (lab < V)
+    assert np.isnan(got[~ok]).all() and np.isfinite(got[ok]).all()
+    xr = x.double().cpu().numpy()
+    ref = olp.logprob(xr, m[ok], lab[ok])
+    assert np.abs(got[ok] - ref).max() <= 1e-3
+    assert np.array_equal(q.cpu().numpy(), np.bincount(m[ok], minlength=C).astype(np.int32))
