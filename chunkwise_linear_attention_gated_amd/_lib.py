@@ -87,6 +87,7 @@ _kda_fwd = _sig("harts_kda_fwd", I32, P, ctypes.POINTER(KdaIO), P)
 _kda_bwd = _sig("harts_kda_bwd", I32, P, ctypes.POINTER(KdaIO), ctypes.POINTER(KdaGrad), P)
 _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
+_lp_na = _sig("harts_logprob_gather_noalloc", I32, P, I64, I64, I32, P, P, I64, P, P, P)
 _lpb = _sig("harts_logprob_backward", I32, P, I64, I64, I32, P, P, P, P, P, I64, P, P)
 _lp_rows = _sig("harts_logprob_rows", I32, P, I64, I64, P, P)
 _lp_check = _sig("harts_logprob_check_map", I32, P, P, I64, I64, I64)
@@ -290,6 +291,17 @@ def logprob_gather(logits, m, labels, logp, q=None, lse=None, workspace=None, st
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lp(_ptr(logits), C, V, dtype, _ptr(m), _ptr(labels), S, _ptr(logp), _ptr(q), _ptr(lse),
                _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def logprob_gather_noalloc(logits, m, labels, logp, q=None, stream=None):
+    """harts_logprob_gather_noalloc: harts_logprob_gather with the library's own per-device scratch
+    (no workspace, no allocation; at most HARTS_LOGPROB_NOALLOC_MAX_ROWS rows)."""
+    import torch
+    C, V = logits.shape
+    if logits.dtype not in (torch.bfloat16, torch.float32):
+        raise HartsError(-1, "logits must be bf16 or fp32")
+    dtype = DTYPE_BF16 if logits.dtype == torch.bfloat16 else DTYPE_FP32
+    _check(_lp_na(_ptr(logits), C, V, dtype, _ptr(m), _ptr(labels), m.numel(), _ptr(logp), _ptr(q), _stream(stream)))
 
 
 def logprob_backward(logits, lse, row_off, row_pos, labels, dlogp, dlogits, stream=None):

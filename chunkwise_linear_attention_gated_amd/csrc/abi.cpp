@@ -713,6 +713,24 @@ int harts_logprob_gather(const void* logits, int64_t C, int64_t V, int32_t dtype
   });
 }
 
+int harts_logprob_gather_noalloc(const void* logits, int64_t C, int64_t V, int32_t dtype, const int64_t* m,
+                                 const int32_t* labels, int64_t S, float* logp_out, int32_t* q_out, void* stream) {
+  return guarded([&] {
+    if (C > HARTS_LOGPROB_NOALLOC_MAX_ROWS)
+      throw Error(HARTS_EINVAL, "C = " + std::to_string(C) + " exceeds the no-allocation maximum of " +
+                                    std::to_string(HARTS_LOGPROB_NOALLOC_MAX_ROWS) + " rows");
+    if (C < 0 || V < 1 || S < 0) throw Error(HARTS_EINVAL, "need C >= 0, V >= 1, S >= 0");
+    if (dtype != HARTS_DTYPE_BF16 && dtype != HARTS_DTYPE_FP32) throw Error(HARTS_EINVAL, "unknown dtype");
+    if (C > 0 && !logits) throw Error(HARTS_EINVAL, "logits is NULL");
+    if (S > 0 && (!m || !labels || !logp_out)) throw Error(HARTS_EINVAL, "m, labels and logp_out are required");
+    static_assert(HARTS_LOGPROB_NOALLOC_MAX_ROWS == harts::kLogprobStaticRows, "one maximum");
+    // no timing scope here: it would create events
+    hip_check(harts::launch_logprob_static(logits, C, V, dtype, m, labels, S, logp_out, q_out,
+                                           static_cast<hipStream_t>(stream)),
+              "log-prob kernel launch");
+  });
+}
+
 int harts_logprob_backward(const void* logits, int64_t C, int64_t V, int32_t dtype, const float* lse,
                            const int64_t* row_off, const int64_t* row_pos, const int32_t* labels, const float* dlogp,
                            int64_t S, void* dlogits_out, void* stream) {

@@ -104,6 +104,11 @@ bool kda_supported(const KdaDims& d);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m, const int32_t* labels,
                           int64_t S, float* logp, int32_t* q, float* lse, hipStream_t s);
+// The same gather with lse in the library's own per-device array of kLogprobStaticRows floats
+// (hipErrorInvalidValue when C exceeds it); allocates nothing.
+constexpr int64_t kLogprobStaticRows = int64_t(1) << 20;
+hipError_t launch_logprob_static(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m,
+                                 const int32_t* labels, int64_t S, float* logp, int32_t* q, hipStream_t s);
 // Tree softmax attention (attn.hip).  which: 0 forward, 1 delta = <dout, o>, 2 dq, 3 dk and dv.
 struct AttnArgs {
   const __bf16 *q, *k, *v, *o, *dout;

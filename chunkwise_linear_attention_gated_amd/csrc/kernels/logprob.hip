@@ -15,6 +15,8 @@
 //
 // The row pass is a pure HBM stream: 16-byte loads, four in flight per
 // thread, online max / sum-exp in base 2 (one exp2 per element).
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -260,6 +262,43 @@ hipError_t launch_logprob(const void* logits, int64_t C, int64_t V, int dtype, c
                          labels, S, lse, logp, q);
   }
   return hipGetLastError();
+}
+
+
+// ---- the gather without allocation: the per-row log-sum-exp in a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in); it resolves each device's address once, with that
+// device current, and passes that.
+static __device__ __align__(256) float scratch[kLogprobStaticRows];
+
+namespace {
+std::mutex g_scratch_mu;
+float* g_scratch_dev[64] = {};
+}  // namespace
+
+static hipError_t scratch_for_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_logprob_static(const void* logits, int64_t C, int64_t V, int dtype, const int64_t* m,
+                                 const int32_t* labels, int64_t S, float* logp, int32_t* q, hipStream_t s) {
+  if (C > kLogprobStaticRows) return hipErrorInvalidValue;
+  float* lse = nullptr;
+  const hipError_t e = scratch_for_current_device(&lse);
+  if (e != hipSuccess) return e;
+  return launch_logprob(logits, C, V, dtype, m, labels, S, logp, q, lse, s);
 }
 
 }  // namespace harts

@@ -245,6 +245,21 @@ int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype
                          const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, float *lse_out,
                          void *workspace, size_t workspace_bytes, void *stream);
 
+/* No-allocation variant of harts_logprob_gather, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same logp_out and q_out as
+ * harts_logprob_gather (lse is not returned); the per-row log-sum-exp lives in
+ * a device array of HARTS_LOGPROB_NOALLOC_MAX_ROWS floats (4 MiB) that the
+ * library's code object holds on each GPU it runs on until the process ends.
+ * No hipMalloc, hipFree or allocating routine is called.  C above the maximum:
+ * HARTS_EINVAL, before any device work.  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (two streams, two threads) race
+ * and must be serialised by the caller; the array needs no clearing (every
+ * call writes the rows it reads). */
+#define HARTS_LOGPROB_NOALLOC_MAX_ROWS (1 << 20)
+int harts_logprob_gather_noalloc(const void *logits, int64_t C, int64_t V, int32_t dtype, const int64_t *m,
+                                 const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, void *stream);
+
 /* ---------------------------------------------------------------- log-prob gradient
  * [blog 4.4, equation 19] For L = sum_s dlogp[s] * logp[s], every semantic
  * position forms its own gradient and the positions that read one compact row
