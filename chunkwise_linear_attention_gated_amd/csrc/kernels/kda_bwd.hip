@@ -320,7 +320,7 @@ template <typename T> __device__ __forceinline__ f32x4 mma_k16r(k16_t<T> a, k16_
 
 // c + a b with a right operand b given in fp32: for bf16 operands b is split into a bf16 head
 // and the bf16 rounding of its remainder, two products, so b carries about 16 significant bits.
-// The gated 16-token block products need them: with steep gates dg is a small difference of
+// The gated diagonal-block products need them: with steep gates dg is a small difference of
 // large terms that the row side and the column side compute from differently scaled operands,
 // and one bf16 rounding of each would not cancel.
 template <typename T> __device__ __forceinline__ f32x4 mma_k16r_split(k16_t<T> a, const float (&b)[4], f32x4 c) {
@@ -1054,9 +1054,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       F[bb + 1] = F[bb] + Tb[bb];
     }
     // gated state products; csum = sum over this lane's rows of k e^{G_last - G} (U dS^T), the
-    // K^ part of dG_last
+    // K^ part of dG_last.  e^{L} and e^{T_b - L} (exponents <= 0) of this lane's rows.
     rs *= __expf(F[NB]);
-    float csum = 0.f;
+    float csum = 0.f, eL[NB][4], ecL[NB][4];
 #pragma unroll
     for (int bb = 0; bb < NB; ++bb) {
       const float ef = __expf(F[bb]), eh = __expf(F[NB] - F[bb + 1]);
@@ -1064,39 +1064,39 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       col4_load<T>(Kb, LDK, 16 * bb, 16 * wave, lane, kvv);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        eL[bb][r] = __expf(L[bb][r]);
+        ecL[bb][r] = __expf(Tb[bb] - L[bb][r]);
         dqa[bb][r] *= ef;
         X1[bb][r] *= -ef;
         X23[bb][r] *= eh;
-        csum += kvv[r] * __expf(Tb[bb] - L[bb][r]) * X23[bb][r];
+        csum += kvv[r] * ecL[bb][r] * X23[bb][r];
       }
     }
     ga_load<T, BT, D, DV, 2>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
-    float eL[NB][4];
-#pragma unroll
-    for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) eL[bb][r] = __expf(L[bb][r]);
     // B4. 16-token block products with the gated masks factored per block pair, every
     //     exponent <= 0 off the diagonal blocks (P = dM with x = q, P = dA with x = k):
-    //     row side  sum_j P_ij k_j e^{F_bi - G_j}      (F_bi - G_j = F_bi - F_bj - L_j <= T_bj - L_j <= 0)
+    //     row side  sum_j P_ij k_j e^{F_bi - G_j},  e^{F_bi - G_j} = e^{F_bi - F_{bj+1}} e^{T_bj - L_j}
     //     col side  sum_i P_ij x_i e^{G_i - F_{bj+1}},  e^{G_i - F_{bj+1}} = e^{L_i} e^{F_bi - F_{bj+1}}
-    //     and on a diagonal block e^{-L_j} and e^{L_i - T_b} = e^{L_i} e^{-T_b}, both at most
-    //     e^{kSteepGate}; a steep block (gate sum below -kSteepGate) takes 0 here and its
-    //     diagonal terms pairwise in B5
+    //     and on a diagonal block e^{-L_j} = e^{T_b - L_j} e^{-T_b} and e^{L_i - T_b} = e^{L_i} e^{-T_b},
+    //     both at most e^{kSteepGate}; a steep block (gate sum below -kSteepGate) takes 0 here and
+    //     its diagonal terms pairwise in B5
 #pragma unroll
     for (int bi = 0; bi < NB; ++bi)
 #pragma unroll
       for (int bj = 0; bj <= bi; ++bj) {
-        const bool dg = bi == bj, stp = Tb[bi] < -kSteepGate;
-        const float ep = dg ? (stp ? 0.f : __expf(-Tb[bi])) : __expf(F[bi] - F[bj + 1]);
+        const float ep = bi == bj ? (Tb[bi] < -kSteepGate ? 0.f : __expf(-Tb[bi])) : __expf(F[bi] - F[bj + 1]);
         float bk[4];
         col4_load<T>(Kb, LDK, 16 * bj, 16 * wave, lane, bk);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) bk[t] *= (dg && stp) ? 0.f : __expf(F[bi] - F[bj] - L[bj][t]);
+        for (int t = 0; t < 4; ++t) bk[t] *= ep * ecL[bj][t];
         const k16_t<T> dMr = k16_row<T>(dMl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);
         const k16_t<T> dAr = k16_row<T>(dAl + (16 * bi + cc) * LDJ + 16 * bj + 4 * g4);
-        dqa[bi] = mma_k16r_split<T>(dMr, bk, dqa[bi]);
-        X1[bi] = mma_k16r_split<T>(dAr, bk, X1[bi]);
+        // the diagonal block's terms (decay near 1) are the ones that cancel in dg under steep
+        // gates: their right operands carry a bf16 remainder; off the diagonal the decay factor
+        // is at most e^{T_b} and one bf16 rounding is enough
+        const bool dgb = bi == bj;
+        dqa[bi] = dgb ? mma_k16r_split<T>(dMr, bk, dqa[bi]) : mma_k16r<T>(dMr, k16_pack<T>(bk), dqa[bi]);
+        X1[bi] = dgb ? mma_k16r_split<T>(dAr, bk, X1[bi]) : mma_k16r<T>(dAr, k16_pack<T>(bk), X1[bi]);
         float bq[4], bk2[4];
         col4_load<T>(Qb, LDK, 16 * bi, 16 * wave, lane, bq);
         col4_load<T>(Kb, LDK, 16 * bi, 16 * wave, lane, bk2);
@@ -1106,8 +1106,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
           bq[t] *= e;
           bk2[t] *= e;
         }
-        X23[bj] = mma_k16r_split<T>(k16_col<T>(dMl, LDJ, 16 * bi, 16 * bj, lane), bq, X23[bj]);
-        X23[bj] = mma_k16r_split<T>(k16_col<T>(dAl, LDJ, 16 * bi, 16 * bj, lane), bk2, X23[bj]);
+        const k16_t<T> dMc = k16_col<T>(dMl, LDJ, 16 * bi, 16 * bj, lane), dAc = k16_col<T>(dAl, LDJ, 16 * bi, 16 * bj, lane);
+        X23[bj] = dgb ? mma_k16r_split<T>(dMc, bq, X23[bj]) : mma_k16r<T>(dMc, k16_pack<T>(bq), X23[bj]);
+        X23[bj] = dgb ? mma_k16r_split<T>(dAc, bk2, X23[bj]) : mma_k16r<T>(dAc, k16_pack<T>(bk2), X23[bj]);
       }
     ga_load<T, BT, D, DV, 3>(nxt, rows_x, b, size_t(itn), itn % H, H, tid, wave, lane);
     // B5. assemble dq, dk, dG with exact q, k and fp32 factors: dq into dqa, the row and column
@@ -1119,7 +1120,7 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
         const float er = eL[bb][r];
         dqa[bb][r] *= er;
         X1[bb][r] *= er;
-        X23[bb][r] *= __expf(Tb[bb] - L[bb][r]);
+        X23[bb][r] *= ecL[bb][r];
       }
     }
 #pragma unroll

@@ -76,6 +76,7 @@ def _tree(dt, B, seed):
 def _check(got, ref, dt, name):
     assert np.isfinite(got).all(), name + ": non-finite values"
     e = rel_err(got, ref)
+    print("  %-26s %.3e" % (name, e))
     assert e <= TOL[dt], (name, e)
     return e
 
