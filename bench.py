@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--no-flat", action="store_true", help="skip the flat packed call (32 sequences, all states)")
+    ap.add_argument("--only-kda", action="store_true",
+                    help="only the headline step (recompute mode) and its per-kernel table (for profiling it alone)")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--only-conv", action="store_true",
                     help="only the tree causal convolution (for profiling it alone)")
@@ -568,6 +570,9 @@ def main():
     roof["alg_bytes_per_launch"] = dk["alg_bytes_per_launch"]
     roof["bytes_per_token_head"] = ALG_BYTES_PER_TOKEN_HEAD[dom]
 
+    if args.only_kda:
+        print(json.dumps({"ms_per_step": ms_step, "value": value, "roofline": roof, "kernels": kernels}))
+        return
     # ---------------------------------------------------------------- the keep variant (same step, more memory)
     for _ in range(2):
         step(True)
