@@ -165,13 +165,13 @@ __device__ __forceinline__ f32x4 mma16_f32(f32x4 a, f32x4 b, f32x4 c) {
 
 // Item order of a persistent per-chunk kernel.  Workgroup b takes items b and b + G (G = grid
 // size) statically, then items 2G + t for tickets t drawn from a per-launch counter that starts
-// at zero.  Thread 0 draws a ticket at the top of each item and publishes it through one LDS
-// word at the top of the next item; the workgroup reads it after that item's first barrier, so a
-// ticket is drawn two items before it is processed.  A workgroup that starts late (its compute
-// unit was busy with another kernel) simply draws fewer tickets.  Each workgroup's draws
-// increase, so once its item is past the end so are all its later draws, and every ticket below
-// the end is processed by the workgroup that drew it.
-__device__ __forceinline__ int draw_ticket(int* ctr) { return atomicAdd(ctr, 1); }
+// at zero.  Thread 0 draws a ticket at the top of each item, before that item's fetches, and
+// publishes it through one LDS word just before one of the item's early barriers; the workgroup
+// reads it after that barrier and fetches the rows of the ticket's item, which it processes two
+// items later.  A workgroup that starts late (its compute unit was busy with another kernel)
+// simply draws fewer tickets.  Each workgroup's draws increase, so once its item is past the
+// end so are all its later draws, and every ticket below the end is processed by the workgroup
+// that drew it.
 
 // A zero the compiler cannot see through.  Loads of per-chunk descriptor fields are
 // indexed with it so their values stay per-lane: a value the compiler knows to be
@@ -182,6 +182,12 @@ __device__ __forceinline__ int lane_zero() {
   asm volatile("v_mov_b32 %0, 0" : "=v"(z));
   return z;
 }
+
+// One lane draws.  The counter's address goes through lane_zero(): for an address it knows to
+// be uniform the compiler rewrites the atomic for the whole wave and reads the returned value
+// at once, which waits for every fetch issued before it; here the ticket is read only where it
+// is consumed, a phase or two later.
+__device__ __forceinline__ int draw_ticket(int* ctr) { return atomicAdd(ctr + lane_zero(), 1); }
 
 // ---- workspace layouts read by the matrix cores -------------------------------------------
 // Fragment-major ("FM") layout of an [R][K] matrix used as a matrix-core operand with rows R

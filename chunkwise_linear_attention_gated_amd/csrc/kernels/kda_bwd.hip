@@ -502,7 +502,7 @@ template <typename T, int BT, int D, int DV>
 struct GBIn {
   using C = GBCfg<T, BT, D, DV>;
   using F = typename C::MM::Frag;
-  f32x4 q[C::NK], k[C::NK], g[C::NK];
+  f32x4 q[C::NK];  // k and g are the token side's own pieces (same threads, same layout)
   // bf16: this wave's channels of S_n and dS_n, read from their S_n^T fragment-major copies
   // (16-byte pieces, staged in LDS and read back as matrix-core B operands); fp32: the B
   // operands from the channel-major copies
@@ -512,7 +512,7 @@ struct GBIn {
 };
 
 // Unconditional loads from clamped addresses: padding is masked where the values are used.
-// P selects a part of the fetch: 0 q, k, g; 1 the state slices.
+// P selects a part of the fetch: 0 q; 1 the state slices.
 template <typename T, int BT, int D, int DV, int P>
 __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GARows<T, BT, D, DV>& r, const BwdRoundArgs& b,
                                         size_t wsi, int h, int H, int tid, int wave, int lane) {
@@ -525,8 +525,6 @@ __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GARows<T, B
       const int c0 = ((tid + C::NT * x) % C::NPR) * C::VN;
       const size_t off = (size_t(r.rk[x] >= 0 ? r.rk[x] : 0) * H + h) * D + c0;
       o.q[x] = ldq(static_cast<const T*>(a.q) + off);
-      o.k[x] = ldq(static_cast<const T*>(a.k) + off);
-      o.g[x] = ldq(static_cast<const T*>(a.g) + off);
     }
   }
   if constexpr (P == 1) {
@@ -557,9 +555,10 @@ __device__ __forceinline__ void gb_load(GBIn<T, BT, D, DV>& o, const GARows<T, B
 // ------------------------------------------------------------------------------------------
 // The gradient kernel: a workgroup takes each (chunk, head) item through the token side and
 // then the channel side.  U, dR, dM and dA stay in LDS between the halves and dO is staged
-// once for both, so the intermediates never reach HBM and the shared inputs are read once.  The channel side's own
-// inputs (q, k, g and its state slices) are fetched while the token side computes, the next
-// item's token-side inputs while the channel side computes.
+// once for both, so the intermediates never reach HBM and the shared inputs are read once: the
+// channel side stages k and g from the token side's registers (both sides give a thread the same
+// pieces).  The channel side's own inputs (q and its state slices) are fetched while the token
+// side computes, the next item's token-side inputs while the channel side computes.
 template <typename T, int BT, int D, int DV>
 struct GFCfg {
   using A = GACfg<T, BT, D, DV>;
@@ -677,8 +676,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
   int item_n = item + gridDim.x;
   ga_rows<T, BT, D, DV>(rows_n, a, (item_n < nitems ? item_n : item) / H, tid0);
   __shared__ int tk_slot;
-  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
-  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
+  // Nothing fetched before the loop stays outstanding into it.  The compiler's wait counts at the
+  // loop head take the more cautious of its two entries; the prologue issues only a few memory
+  // operations after its fetches, the loop body many (the item's stores), so without this wait
+  // every item would wait at its top for nearly all of the previous item's stores to complete.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   while (item < nitems) {
     int tid = threadIdx.x;
@@ -691,11 +693,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
     rows = rows_x;
     const int itn = item_n < nitems ? item_n : item;
     rows_x = rows_n;
-    gb_load<T, BT, D, DV, 0>(cb, rows, b, wsi, h, H, tid, wave, lane);  // q, k, g of this item
-    if (a.ctr && tid == 0) {
-      tk_slot = tk;
-      tk = draw_ticket(a.ctr);
-    }
+    int tk = 0;  // thread 0: the ticket for the item after the next one
+    if (a.ctr && tid == 0) tk = draw_ticket(a.ctr);
+    gb_load<T, BT, D, DV, 0>(cb, rows, b, wsi, h, H, tid, wave, lane);  // q of this item
 
     // ---------------- token side ----------------
     // A1. stage the inputs (padding rows zero; dO zero on replayed rows)
@@ -746,9 +746,6 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
     }
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
     __syncthreads();
-    // the item after the next one: its rows are fetched a whole item ahead of their use
-    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
-    ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
     // A2. decay per (16-row block, channel): block totals
     HARTS_STRIDED(idx, tid, NB * D, NT) {
       const int bb = idx / D, c = idx % D;
@@ -779,7 +776,11 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
         Kh[i * LDK + c] = from_f<T>(kv * __expf(fe - fb - Lr));
       }
     }
+    if (a.ctr && tid == 0) tk_slot = tk;
     __syncthreads();
+    // the item after the next one: its rows are fetched a whole item ahead of their use
+    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
+    ga_rows<T, BT, D, DV>(rows_n, a, (item_nn < nitems ? item_nn : item) / H, tid);
     // A4. R = V - K~ S0 and dU = K^ dS + M^T dO for this wave's value columns
     const int jv = 16 * wave + cc;
     f32x4 R[NB], dU[NB];
@@ -1023,8 +1024,8 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
         const int i = p / NPR, c0 = (p % NPR) * VN;
         const bool ok = rows.rk[x] >= 0;
         stq(Qb + i * LDK + c0, ok ? cb.q[x] : z4);
-        stq(Kb + i * LDK + c0, ok ? cb.k[x] : z4);
-        stq(Gb + i * LDK + c0, ok ? cb.g[x] : z4);
+        stq(Kb + i * LDK + c0, ok ? cur.k[x] : z4);
+        stq(Gb + i * LDK + c0, ok ? cur.g[x] : z4);
       }
     }
     __syncthreads();
@@ -1204,8 +1205,9 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       }
     }
     __syncthreads();  // the next item restages every region
+    // the ticket word is read again rather than the item held across the item's phases
     item = item_n;
-    item_n = item_nn;
+    item_n = a.ctr ? 2 * int(gridDim.x) + tk_slot : item + int(gridDim.x);
   }
 }
 

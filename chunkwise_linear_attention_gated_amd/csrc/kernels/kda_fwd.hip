@@ -277,8 +277,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   int item_n = item + gridDim.x;
   prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_n < nitems ? item_n : item) / H, tid0);
   __shared__ int tk_slot;
-  int tk = 0;  // thread 0: the ticket drawn at the top of the previous item
-  if (a.ctr && tid0 == 0) tk = draw_ticket(a.ctr);
+  // Nothing fetched before the loop stays outstanding into it.  The compiler's wait counts at the
+  // loop head take the more cautious of its two entries; the prologue issues only a few memory
+  // operations after its fetches, the loop body many (the item's stores), so without this wait
+  // every item would wait at its top for nearly all of the previous item's stores to complete.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
   while (item < nitems) {
     // thread-derived addresses are recomputed per item instead of being held across the loop
@@ -290,16 +293,14 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     const size_t wsi = size_t(item);  // (round-local chunk) * H + head
     cur = nxt;
     rows = rows_x;
+    int tk = 0;  // thread 0: the ticket for the item after the next one
+    if (a.ctr && tid == 0) tk = draw_ticket(a.ctr);
     // this item's values; fetch ahead: inputs of the next item, rows of the one after
     f32x4 vv[NV];
     prep_load_v<T, BT, D, DV>(vv, rows, a, h, H, tid);
     const int hn = (item_n < nitems ? item_n : item) % H;
     prep_load<T, BT, D, DV, 0>(nxt, rows_n, a, hn, H, tid);
     rows_x = rows_n;
-    if (a.ctr && tid == 0) {
-      tk_slot = tk;
-      tk = draw_ticket(a.ctr);
-    }
 
     // 1. g -> Gf (fp32), beta
 #pragma unroll
@@ -317,9 +318,6 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     if (tid < BT) bet[tid] = rows.rb >= 0 ? to_f(cur.beta) : 0.f;
     if (tid <= NB) stf[tid] = 0;
     __syncthreads();
-    // the item after the next one: its rows are fetched a whole item ahead of their use
-    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
-    prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
     // 2. block-local cumulative sums L and block totals
     HARTS_STRIDED(idx, tid, NB * D, CNT) {
       const int b = idx / D, c = idx % D;
@@ -334,7 +332,11 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
       Tv[b * D + c] = acc;
     }
+    if (a.ctr && tid == 0) tk_slot = tk;
     __syncthreads();
+    // the item after the next one: its rows are fetched a whole item ahead of their use
+    const int item_nn = a.ctr ? 2 * int(gridDim.x) + tk_slot : item_n + int(gridDim.x);
+    prep_rows<T, BT, D, DV>(rows_n, a.crows, (item_nn < nitems ? item_nn : item) / H, tid);
     prep_load<T, BT, D, DV, 1>(nxt, rows_x, a, hn, H, tid);
     // 3. per channel: block entry log-decays F_b, e^{F_b}, e^{F_end - F_{b+1}}, pair scales
     HARTS_STRIDED(c, tid, D, CNT) {
@@ -768,8 +770,9 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
       }
     }
     __syncthreads();  // the next item overwrites every region
+    // the ticket word is read again rather than the item held across the item's phases
     item = item_n;
-    item_n = item_nn;
+    item_n = a.ctr ? 2 * int(gridDim.x) + tk_slot : item + int(gridDim.x);
   }
 }
 
