@@ -97,8 +97,9 @@ def test_attn_small_trees(dims):
 
 
 def test_attn_chains_and_ragged_tiles():
-    # one chain spanning several key tiles, and a forest of sequences of 1, 63, 64, 65, 130 rows
-    for i, lens in enumerate([[200], [1, 63, 64, 65, 130]]):
+    # one chain spanning several tiles, and forests of sequences around the 64-row operand tiles
+    # and the 128-row query and key tiles
+    for i, lens in enumerate([[300], [1, 63, 64, 65, 130], [127, 128, 129, 260]]):
         t = trees.forest_of_sequences(lens, seed=i)
         m, off, C = _maps(t)
         print(f"attn chains {lens}: C={C}", flush=True)
