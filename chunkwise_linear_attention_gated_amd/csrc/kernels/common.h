@@ -294,8 +294,10 @@ constexpr float kSteepGate = 60.f;
 // Waves of a serial state-pass workgroup: one per 16 state rows, at most 8.
 template <int D> constexpr int state_waves() { return D / 16 < 8 ? D / 16 : 8; }
 
-// Workgroup size of the persistent per-chunk kernels: 8 waves, two per SIMD.
-constexpr int CNT = 512;
+// Workgroup size of the persistent preparation kernel: 16 waves, four per SIMD (at most 128
+// registers each).  One workgroup fills a compute unit (its LDS), so the waves of one item are
+// all the latency hiding there is: at 8 waves the kernel took 8-17 % longer.
+constexpr int CNT = 1024;
 constexpr int CNW = CNT / 64;
 
 // Blocks of a grid are dealt round-robin to the 8 XCDs; remap so that runs of

@@ -177,6 +177,7 @@ __device__ __forceinline__ void steep_diag_sums(float* DA, float* DM, T* Sk, T* 
                                                 int tid) {
   using P = PrepIn<T, BT, D, DV>;
   constexpr int NB = BT / 16, VN = 16 / sizeof(T), LDF = D + 4, MKR = D / VN, LDK = D + VN;
+  static_assert(CNT >= 512, "one thread per entry of A and of M");
   const bool isM = tid >= 256;
   const int i = (tid >> 4) & 15, j = tid & 15;
   const f32x4 z4 = {0.f, 0.f, 0.f, 0.f};
