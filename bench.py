@@ -59,6 +59,9 @@ def parse():
                     help="only the router statistics (for profiling them alone)")
     ap.add_argument("--only-logprob", action="store_true",
                     help="only the log-prob gather and its backward (for profiling them alone)")
+    ap.add_argument("--save-plan", default=None,
+                    help="write the workload's trajectories and its plan (maps, sequences, replay rows, "
+                         "emits) to this .npz file")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
     return ap.parse_args()
@@ -282,6 +285,25 @@ def conv_bench(args, out, t, plan, C):
     del x, dout, y, dx
 
 
+def plan_record(t, plan):
+    """The workload's trajectories and the plan built from them as plain arrays, and a SHA-256 over
+    all of them: the bench line names the exact rounds it timed, and --save-plan keeps them."""
+    m, q, n2r = plan.maps()
+    seqs = plan.sequences()
+    fields = sorted(seqs[0]) if seqs else []
+    sq = np.array([[s[f] for f in fields] for s in seqs], np.int64).reshape(len(seqs), len(fields))
+    eb, et = plan.emits()
+    arrays = {"tokens": np.asarray(t.tokens, np.int32), "offsets": np.asarray(t.offsets, np.int64),
+              "m": m, "q": q, "node_to_row": n2r, "sequences": sq,
+              "sequence_fields": np.array(fields), "replay_rows": plan.replay_rows(),
+              "emit_chunk": eb, "emit_slot": et}
+    h = hashlib.sha256()
+    for k in sorted(arrays):
+        h.update(k.encode())
+        h.update(np.ascontiguousarray(arrays[k]).tobytes())
+    return h.hexdigest(), arrays
+
+
 def attn_bench(args, out, t, plan, C):
     """Tree softmax attention of the full-attention (MLA) layer over the benchmark tree's compact
     rows: 16 heads, q/k head dim 192 (128 + 64 rotary), v head dim 128, bf16.  Forward and
@@ -479,6 +501,9 @@ def main():
     info = plan.info
     C, S = info.C, info.S
     m, q_counts, _ = plan.maps()
+    plan_digest, plan_arrays = plan_record(t, plan)
+    if args.save_plan:
+        np.savez_compressed(args.save_plan, **plan_arrays)
     nodes = np.empty(C, np.int64)
     nodes[m] = t.node_of_pos
     x = {n: tensors.to_torch(getattr(feats, n)[nodes], "bf16", dev) for n in ("q", "k", "v", "g", "beta", "do")}
@@ -607,7 +632,8 @@ def main():
                                "backward (no operands kept between the two)" % args.seed,
                    "mode": "recompute",
                    "C": C, "S": S, "expansion": S / C, "n_rounds": info.n_rounds, "n_sequences": info.n_sequences,
-                   "n_slots": info.n_slots, "replay_tokens": info.replay_total, "n_chunks": info.n_chunks},
+                   "n_slots": info.n_slots, "replay_tokens": info.replay_total, "n_chunks": info.n_chunks,
+                   "plan_sha256": plan_digest},
         "mfma_pct": 100 * flops_step / (ms_step / 1e3) / PEAK_BF16,
         "hbm_pct_alg_bytes": 100 * bytes_step / (ms_step / 1e3) / PEAK_HBM,
         "path_flops_per_step": flops_step,
