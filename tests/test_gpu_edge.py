@@ -211,3 +211,19 @@ def test_nan_in_one_sequence_stays_in_that_sequence():
     assert np.array_equal(clean["fin"][[0, 2]], bad["fin"][[0, 2]])
     assert np.isnan(bad["o"][cu[1] + 70:cu[2]]).any() and np.isnan(bad["fin"][1]).any()
     assert np.isfinite(clean["o"]).all() and np.isfinite(clean["fin"]).all()
+
+
+@pytest.mark.parametrize("kind", ["steep5", "mixed", "gneg", "beta0"])
+def test_kept_operands_equal_recompute_under_special_gates(kind):
+    """The forward that keeps its operands for the backward (preparation in both modes at once)
+    and the backward that recomputes them take the same steep-row and diagonal-block decisions:
+    every output and gradient agrees bit for bit."""
+    B, D, H, dt = 64, 128, 2, "bf16"
+    rng = np.random.default_rng(83)
+    t = trees.random_small_tree(rng, max_segments=7, max_len=3 * B)
+    feats = edge_features(t.n_nodes, H, D, dt, int(rng.integers(1000)), kind)
+    a = run_tree_bwd(t, feats, B, H, D, dt)[2]
+    b = run_tree_bwd(t, feats, B, H, D, dt, keep=True)[2]
+    for n in a:
+        assert np.isfinite(a[n]).all(), n
+        assert np.array_equal(a[n], b[n]), n
