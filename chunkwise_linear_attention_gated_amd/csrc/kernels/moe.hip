@@ -5,13 +5,16 @@
 // assignment counts, so the statistics equal those of the expanded positions
 // while routing decisions stay those of the row.
 //
-//   route:  one wave per row (E / 64 logits per lane): softmax, lse, top-k of
-//           p + bias by k wave-wide arg-max rounds (ties: lower expert); per
-//           workgroup: q-weighted counts by LDS integer adds (exact), mass and
-//           z-loss in a fixed order, written as one partial row
-//   reduce: one workgroup per column of the partials, fixed-order sum
+//   route:  one 16-lane group per row (E / 16 logits per lane, four rows per
+//           wave at once): softmax, lse, top-k of p + bias by k arg-max rounds
+//           over the group (ties: lower expert); per workgroup: q-weighted
+//           counts by LDS integer adds (exact), mass and z-loss summed over its
+//           rows in row order, written as one partial row
+//   reduce: two fixed-order levels: whole rows of the partials in 64 row chunks,
+//           then one workgroup per column of the chunk sums
 //   aux:    E / (k S^2) sum_e n_e P_e
-//   grad:   dz = z_coef 2 q lse p / S + aux_coef E / (k S^2) q p (n - <n, p>)
+//   grad:   dz = z_coef 2 q lse p / S + aux_coef E / (k S^2) q p (n - <n, p>),
+//           a row per 16-lane group
 //   bias:   b_e += gamma sign(mean n - n_e)
 #include <cmath>
 
@@ -21,123 +24,184 @@
 namespace harts {
 namespace {
 
-constexpr int MR = 16;   // rows per workgroup (4 per wave: latency-bound shuffle chains want many waves)
-constexpr int MT = 256;  // 4 waves, one row at a time each
+constexpr int MR = 16;   // rows per workgroup: a row per 16-lane group
+constexpr int MT = 256;  // 4 waves
 
-// partial rows: [nblk][E + 1] float (mass, z-loss sum), then [nblk][E] int32 (counts)
-__host__ __device__ inline int64_t moe_partial_rows_dev(int64_t C) { return (C + MR - 1) / MR; }
+constexpr int MR1 = 64;  // row chunks of the first reduction level
+// partial rows: [rows][E + 1] float (mass, z-loss sum), then [rows][E] int32 (counts); rows = one
+// per route workgroup, then MR1 rows of first-level sums
+__host__ __device__ inline int64_t moe_blocks(int64_t C) { return (C + MR - 1) / MR; }
+__host__ __device__ inline int64_t moe_partial_rows_dev(int64_t C) { return moe_blocks(C) + MR1; }
 
-__device__ __forceinline__ float wsum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
+// Exchanges within a row group of 16 lanes by data-parallel-primitive moves (vector ALU, no LDS
+// round trip): swap adjacent lanes, swap lane pairs, mirror each half row, mirror the row.  After
+// the four steps of a reduction every lane of the group holds the group's result.
+constexpr int kDppSwap1 = 0xB1;       // quad_perm [1, 0, 3, 2]
+constexpr int kDppSwap2 = 0x4E;       // quad_perm [2, 3, 0, 1]
+constexpr int kDppHalfMirror = 0x141; // row_half_mirror
+constexpr int kDppMirror = 0x140;     // row_mirror
+template <int CTRL> __device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_mov_dpp(x, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ float wmax(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, dpp_i<CTRL>(__builtin_bit_cast(int, x)));
 }
-
-// softmax of one row held as NE values per lane (expert lane + 64 j)
-template <int NE>
-__device__ __forceinline__ float row_softmax(float (&x)[NE]) {
-  float m = x[0];
-#pragma unroll
-  for (int j = 1; j < NE; ++j) m = fmaxf(m, x[j]);
-  m = wmax(m);
-  float s = 0.f;
-#pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    x[j] = expf(x[j] - m);
-    s += x[j];
+__device__ __forceinline__ float gsum(float x) {
+  x += dpp_f<kDppSwap1>(x);
+  x += dpp_f<kDppSwap2>(x);
+  x += dpp_f<kDppHalfMirror>(x);
+  return x + dpp_f<kDppMirror>(x);
+}
+__device__ __forceinline__ float gmax(float x) {
+  x = fmaxf(x, dpp_f<kDppSwap1>(x));
+  x = fmaxf(x, dpp_f<kDppSwap2>(x));
+  x = fmaxf(x, dpp_f<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_f<kDppMirror>(x));
+}
+// (value, expert) of the larger score, the lower expert on a tie
+template <int CTRL> __device__ __forceinline__ void gargmax_step(float& bv, int& bi) {
+  const float ov = dpp_f<CTRL>(bv);
+  const int oi = dpp_i<CTRL>(bi);
+  if (ov > bv || (ov == bv && oi < bi)) {
+    bv = ov;
+    bi = oi;
   }
-  s = wsum(s);
-  const float inv = 1.f / s;
-#pragma unroll
-  for (int j = 0; j < NE; ++j) x[j] *= inv;
-  return m + logf(s);
 }
 
+// Route: a row per 16-lane group (4 rows per wave at once), lane i of the group holding experts
+// NL i .. NL i + NL - 1 (NL = E / 16, contiguous: two or more 16-byte loads).  The top-k rounds
+// are butterflies over the group's 16 lanes, four rows' chains interleaved in each wave.
 template <int NE>
 __global__ __launch_bounds__(MT) void moe_route_kernel(MoeArgs a) {
-  constexpr int E = NE * 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float b[NE], mass[NE];
+  constexpr int E = NE * 64, NL = E / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, gl = lane & 15, grp = lane >> 4;
+  const int e0 = NL * gl;
+  float b[NL], mass[NL];
 #pragma unroll
-  for (int j = 0; j < NE; ++j) {
-    b[j] = a.bias ? a.bias[lane + 64 * j] : 0.f;
+  for (int j = 0; j < NL; ++j) {
+    b[j] = a.bias ? a.bias[e0 + j] : 0.f;
     mass[j] = 0.f;
   }
   float zs = 0.f;
   __shared__ int32_t cnt[E];
   for (int e = threadIdx.x; e < E; e += MT) cnt[e] = 0;
   __syncthreads();
-  for (int r = wave; r < MR; r += MT / 64) {
-    const int64_t c = int64_t(blockIdx.x) * MR + r;
-    if (c >= a.C) break;
-    float p[NE];
+  const int64_t c = int64_t(blockIdx.x) * MR + 4 * wave + grp;  // MR == 4 rows x 4 waves
+  if (c < a.C) {
+    float p[NL];
+    const float* zr = a.z + c * E + e0;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) p[j] = a.z[c * E + lane + 64 * j];
-    const float lse = row_softmax<NE>(p);
+    for (int j = 0; j < NL; j += 4) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(zr + j);
+      p[j] = v[0];
+      p[j + 1] = v[1];
+      p[j + 2] = v[2];
+      p[j + 3] = v[3];
+    }
+    float m = p[0];
+#pragma unroll
+    for (int j = 1; j < NL; ++j) m = fmaxf(m, p[j]);
+    m = gmax(m);
+    float sum = 0.f;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+      p[j] = expf(p[j] - m);
+      sum += p[j];
+    }
+    sum = gsum(sum);
+    const float inv = 1.f / sum, lse = m + logf(sum);
     const int qc = a.q[c];
     const float qf = float(qc);
-    float sc[NE];
+    float sc[NL];
 #pragma unroll
-    for (int j = 0; j < NE; ++j) {
-      mass[j] += qf * p[j];
+    for (int j = 0; j < NL; ++j) {
+      p[j] *= inv;
+      mass[j] = qf * p[j];
       sc[j] = p[j] + b[j];
     }
-    zs += qf * lse * lse;
+    zs = qf * lse * lse;
     for (int t = 0; t < a.k; ++t) {
       float bv = sc[0];
-      int bi = lane;
+      int bi = e0;
 #pragma unroll
-      for (int j = 1; j < NE; ++j)
+      for (int j = 1; j < NL; ++j)
         if (sc[j] > bv) {  // strict: the lower expert of a tie stays
           bv = sc[j];
-          bi = lane + 64 * j;
+          bi = e0 + j;
         }
+      gargmax_step<kDppSwap1>(bv, bi);
+      gargmax_step<kDppSwap2>(bv, bi);
+      gargmax_step<kDppHalfMirror>(bv, bi);
+      gargmax_step<kDppMirror>(bv, bi);
 #pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (ov > bv || (ov == bv && oi < bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NE; ++j)
-        if (bi == lane + 64 * j) sc[j] = -INFINITY;
-      if (lane == 0) {
+      for (int j = 0; j < NL; ++j)
+        if (bi == e0 + j) sc[j] = -INFINITY;
+      if (gl == 0) {
         a.top[c * a.k + t] = bi;
         atomicAdd(cnt + bi, qc);  // LDS
       }
     }
-    if (lane == 0) a.lse[c] = lse;
+    if (gl == 0) a.lse[c] = lse;
   }
-  __shared__ float sm[MT / 64][E];
-  __shared__ float sz[MT / 64];
+  // this workgroup's mass and z-loss sums over its 16 rows, in row order
+  __shared__ float sm[MR][E];
+  __shared__ float sz[MR];
 #pragma unroll
-  for (int j = 0; j < NE; ++j) sm[wave][lane + 64 * j] = mass[j];
-  if (lane == 0) sz[wave] = zs;
+  for (int j = 0; j < NL; ++j) sm[4 * wave + grp][e0 + j] = mass[j];
+  if (gl == 0) sz[4 * wave + grp] = zs;
   __syncthreads();
   float* part = a.part + int64_t(blockIdx.x) * (E + 1);
   int32_t* ipart = reinterpret_cast<int32_t*>(a.part + moe_partial_rows_dev(a.C) * (E + 1)) + int64_t(blockIdx.x) * E;
   for (int e = threadIdx.x; e < E; e += MT) {
-    part[e] = ((sm[0][e] + sm[1][e]) + sm[2][e]) + sm[3][e];
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc += sm[r][e];
+    part[e] = acc;
     ipart[e] = cnt[e];
   }
-  if (threadIdx.x == 0) part[E] = ((sz[0] + sz[1]) + sz[2]) + sz[3];
+  if (threadIdx.x == 0) {
+    float acc = 0.f;
+#pragma unroll
+    for (int r = 0; r < MR; ++r) acc += sz[r];
+    part[E] = acc;
+  }
 }
 
-// column e of the partials (e == E: the z-loss sums), fixed order: strided per thread, then a tree
-__global__ __launch_bounds__(256) void moe_reduce_kernel(MoeArgs a, int64_t nblk) {
+// First level: chunk rc of the route partials' rows, 64 columns per workgroup (e == E: the
+// z-loss sums), four row phases summed in row order each, then in phase order; reads whole rows
+__global__ __launch_bounds__(256) void moe_reduce1_kernel(MoeArgs a) {
+  const int E = a.E;
+  const int64_t nblk = moe_blocks(a.C), rows = moe_partial_rows_dev(a.C), per = (nblk + MR1 - 1) / MR1;
+  const int l = threadIdx.x & 63, ph = threadIdx.x >> 6, col = 64 * blockIdx.x + l;
+  const int64_t rc = blockIdx.y, r0 = rc * per, r1 = r0 + per < nblk ? r0 + per : nblk;
+  int32_t* ipart = reinterpret_cast<int32_t*>(a.part + rows * (E + 1));
+  float acc = 0.f;
+  int32_t iacc = 0;
+  if (col <= E)
+    for (int64_t i = r0 + ph; i < r1; i += 4) {
+      acc += a.part[i * (E + 1) + col];
+      if (col < E) iacc += ipart[i * E + col];
+    }
+  __shared__ float red[4][64];
+  __shared__ int32_t ired[4][64];
+  red[ph][l] = acc;
+  ired[ph][l] = iacc;
+  __syncthreads();
+  if (ph == 0 && col <= E) {
+    a.part[(nblk + rc) * (E + 1) + col] = ((red[0][l] + red[1][l]) + red[2][l]) + red[3][l];
+    if (col < E) ipart[(nblk + rc) * E + col] = ((ired[0][l] + ired[1][l]) + ired[2][l]) + ired[3][l];
+  }
+}
+
+// column e of the first-level sums (e == E: the z-loss sums), fixed order: strided per thread,
+// then a tree
+__global__ __launch_bounds__(256) void moe_reduce_kernel(MoeArgs a) {
   const int E = a.E, e = blockIdx.x;
-  const int32_t* ipart = reinterpret_cast<const int32_t*>(a.part + nblk * (E + 1));
+  const int64_t nblk = moe_blocks(a.C), rows = moe_partial_rows_dev(a.C);
+  const int32_t* ipart = reinterpret_cast<const int32_t*>(a.part + rows * (E + 1));
   float acc = 0.f;
   int64_t iacc = 0;
-  for (int64_t i = threadIdx.x; i < nblk; i += 256) {
+  for (int64_t i = nblk + threadIdx.x; i < rows; i += 256) {
     acc += a.part[i * (E + 1) + e];
     if (e < E) iacc += ipart[i * E + e];
   }
@@ -180,30 +244,57 @@ __global__ __launch_bounds__(256) void moe_aux_kernel(MoeArgs a) {
   }
 }
 
+// Gradient: a row per 16-lane group as in the route, NL contiguous experts per lane.
 template <int NE>
 __global__ __launch_bounds__(MT) void moe_grad_kernel(MoeArgs a) {
-  constexpr int E = NE * 64;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float n[NE];
+  constexpr int E = NE * 64, NL = E / 16;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, gl = lane & 15, grp = lane >> 4;
+  const int e0 = NL * gl;
+  const int64_t c = int64_t(blockIdx.x) * MR + 4 * wave + grp;
+  if (c >= a.C) return;
+  float n[NL];
 #pragma unroll
-  for (int j = 0; j < NE; ++j) n[j] = float(a.counts[lane + 64 * j]);
+  for (int j = 0; j < NL; ++j) n[j] = float(a.counts[e0 + j]);
   const double S = double(a.S);
   const float cz = float(2.0 * double(a.z_coef) / S);
   const float ca = float(double(a.aux_coef) * double(E) / (double(a.k) * S * S));
-  for (int r = wave; r < MR; r += MT / 64) {
-    const int64_t c = int64_t(blockIdx.x) * MR + r;
-    if (c >= a.C) break;
-    float p[NE];
+  float p[NL];
+  const float* zr = a.z + c * E + e0;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) p[j] = a.z[c * E + lane + 64 * j];
-    const float lse = row_softmax<NE>(p);
-    float nb = 0.f;
+  for (int j = 0; j < NL; j += 4) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(zr + j);
+    p[j] = v[0];
+    p[j + 1] = v[1];
+    p[j + 2] = v[2];
+    p[j + 3] = v[3];
+  }
+  float m = p[0];
 #pragma unroll
-    for (int j = 0; j < NE; ++j) nb += p[j] * n[j];
-    nb = wsum(nb);
-    const float qf = float(a.q[c]);
+  for (int j = 1; j < NL; ++j) m = fmaxf(m, p[j]);
+  m = gmax(m);
+  float sum = 0.f;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) a.dz[c * E + lane + 64 * j] = qf * p[j] * (cz * lse + ca * (n[j] - nb));
+  for (int j = 0; j < NL; ++j) {
+    p[j] = expf(p[j] - m);
+    sum += p[j];
+  }
+  sum = gsum(sum);
+  const float inv = 1.f / sum, lse = m + logf(sum);
+  float nb = 0.f;
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    p[j] *= inv;
+    nb += p[j] * n[j];
+  }
+  nb = gsum(nb);
+  const float qf = float(a.q[c]);
+  float* dr = a.dz + c * E + e0;
+#pragma unroll
+  for (int j = 0; j < NL; j += 4) {
+    f32x4 v;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = qf * p[j + t] * (cz * lse + ca * (n[j + t] - nb));
+    *reinterpret_cast<f32x4*>(dr + j) = v;
   }
 }
 
@@ -227,10 +318,11 @@ __global__ __launch_bounds__(256) void moe_bias_kernel(const int32_t* counts, in
 
 template <int NE>
 hipError_t moe_run(int which, const MoeArgs& a, hipStream_t s) {
-  const int64_t nblk = (a.C + MR - 1) / MR;
+  const int64_t nblk = moe_blocks(a.C);
   if (which == 0) {
     if (a.C > 0) hipLaunchKernelGGL(moe_route_kernel<NE>, dim3(unsigned(nblk)), dim3(MT), 0, s, a);
-    hipLaunchKernelGGL(moe_reduce_kernel, dim3(unsigned(a.E + 1)), dim3(256), 0, s, a, nblk);
+    hipLaunchKernelGGL(moe_reduce1_kernel, dim3(unsigned((a.E + 1 + 63) / 64), unsigned(MR1)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(moe_reduce_kernel, dim3(unsigned(a.E + 1)), dim3(256), 0, s, a);
     hipLaunchKernelGGL(moe_aux_kernel, dim3(1), dim3(256), 0, s, a);
   } else if (a.C > 0) {
     hipLaunchKernelGGL(moe_grad_kernel<NE>, dim3(unsigned(nblk)), dim3(MT), 0, s, a);
