@@ -268,9 +268,11 @@ def conv_bench(args, out, t, plan, C):
     reps = max(3, min(args.steps, 10))
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     res = {"C": C, "channels": ch, "w": w}
+    # algorithmic bytes: forward reads x and writes out; both gradients read dout and x once and
+    # write dx (the weights and their gradient are ch * w floats)
     for name, fn, by in (("fwd", lambda: harts.conv_fwd(x, wt, ancd, y), 2 * C * ch * 2),
                          ("bwd", lambda: harts.conv_bwd(x, wt, ancd, goffd, gld, dout, dx=dx, dweight=dw, workspace=ws),
-                          4 * C * ch * 2)):
+                          3 * C * ch * 2)):
         for _ in range(2):
             fn()
         torch.cuda.synchronize()
