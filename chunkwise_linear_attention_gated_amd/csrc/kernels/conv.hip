@@ -208,13 +208,24 @@ __global__ __launch_bounds__(256) void conv_dw_partial_kernel(const T* __restric
     for (int j = 0; j < W; ++j) pb[e * W + j] = acc[j][e];
 }
 
+// dweight[i] = sum over the row blocks b of part[b][i]: 32 outputs per workgroup, eight phases
+// of blocks (b = ph, ph + 8, ..) summed in order each, then the phases in order
 __global__ __launch_bounds__(256) void conv_dw_sum_kernel(const float* __restrict__ part, int64_t nblk, int64_t n,
                                                           float* __restrict__ dw) {
-  const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-  if (i >= n) return;
+  const int l = threadIdx.x & 31, ph = threadIdx.x >> 5;
+  const int64_t i = blockIdx.x * int64_t(32) + l;
   float s = 0.f;
-  for (int64_t b = 0; b < nblk; ++b) s += part[b * n + i];
-  dw[i] = s;
+  if (i < n)
+    for (int64_t b = ph; b < nblk; b += 8) s += part[b * n + i];
+  __shared__ float red[8][32];
+  red[ph][l] = s;
+  __syncthreads();
+  if (ph == 0 && i < n) {
+    float t = red[0][l];
+#pragma unroll
+    for (int q = 1; q < 8; ++q) t += red[q][l];
+    dw[i] = t;
+  }
 }
 
 size_t conv_workspace_bytes(int64_t C, int32_t ch, int32_t w) {
@@ -245,7 +256,7 @@ static hipError_t conv_bwd_t(const void* x, const float* wt, const int32_t* anc,
     hipLaunchKernelGGL((conv_dw_partial_kernel<T, W>), dim3(unsigned((ch / 8 + 255) / 256), unsigned(nblk)), dim3(256), 0,
                        s, static_cast<const T*>(x), static_cast<const T*>(dout), anc, C, ch, part);
     const int64_t n = int64_t(ch) * W;
-    hipLaunchKernelGGL(conv_dw_sum_kernel, dim3(unsigned((n + 255) / 256)), dim3(256), 0, s, part, nblk, n, dw);
+    hipLaunchKernelGGL(conv_dw_sum_kernel, dim3(unsigned((n + 31) / 32)), dim3(256), 0, s, part, nblk, n, dw);
   }
   return hipGetLastError();
 }
