@@ -13,7 +13,7 @@
 // in one streaming read and write of the row; the positions of a row come from the CSR inverse
 // of m and are summed in increasing s, so the result does not depend on scheduling.
 //
-// The row pass is a pure HBM stream: 16-byte loads, four in flight per
+// The row pass is a pure HBM stream: 16-byte loads, eight in flight per
 // thread, online max / sum-exp in base 2 (one exp2 per element).
 #include <mutex>
 
@@ -54,31 +54,33 @@ __global__ __launch_bounds__(256) void row_lse_kernel(const T* __restrict__ x, i
   const int64_t nvec = vec_ok ? V / VN : 0;
   const f32x4* rv = reinterpret_cast<const f32x4*>(row);
   int64_t i = threadIdx.x;
-  // four 16-byte loads in flight per thread
-  for (; i + 3 * 256 < nvec; i += 4 * 256) {
-    f32x4 raw[4];
+  // eight 16-byte loads in flight per thread; the maximum is taken on the raw values, so each
+  // element costs one fused multiply-add into base 2 and one exp2
+  for (; i + 7 * 256 < nvec; i += 8 * 256) {
+    f32x4 raw[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
+    for (int u = 0; u < 8; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       float v[VN];
       if constexpr (sizeof(T) == 2) {
         const bf16x8 b = __builtin_bit_cast(bf16x8, raw[u]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = (float)b[t] * kLog2e;
+        for (int t = 0; t < 8; ++t) v[t] = (float)b[t];
       } else {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = raw[u][t] * kLog2e;
+        for (int t = 0; t < 4; ++t) v[t] = raw[u][t];
       }
       float vm = v[0];
 #pragma unroll
       for (int t = 1; t < VN; ++t) vm = fmaxf(vm, v[t]);
+      vm *= kLog2e;
       if (vm > m) {
         s *= exp2f(m - vm);
         m = vm;
       }
 #pragma unroll
-      for (int t = 0; t < VN; ++t) s += exp2f(v[t] - m);
+      for (int t = 0; t < VN; ++t) s += exp2f(fmaf(v[t], kLog2e, -m));
     }
   }
   for (; i < nvec; i += 256) {
