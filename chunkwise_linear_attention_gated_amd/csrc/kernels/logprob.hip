@@ -182,16 +182,16 @@ __global__ __launch_bounds__(256) void logprob_bwd_kernel(const T* __restrict__ 
   const int64_t nvec = vec_ok ? V / VN : 0;
   const f32x4* rv = reinterpret_cast<const f32x4*>(row);
   int64_t i = threadIdx.x;
-  for (; i + 3 * 256 < nvec; i += 4 * 256) {
-    f32x4 raw[4];
+  for (; i + 7 * 256 < nvec; i += 8 * 256) {
+    f32x4 raw[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
+    for (int u = 0; u < 8; ++u) raw[u] = __builtin_nontemporal_load(rv + i + u * 256);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 8; ++u) {
       float v[VN];
       unpack16<T>(raw[u], v);
 #pragma unroll
-      for (int t = 0; t < VN; ++t) v[t] = ng * exp2f(v[t] * kLog2e - l2);
+      for (int t = 0; t < VN; ++t) v[t] = ng * exp2f(fmaf(v[t], kLog2e, -l2));
       __builtin_nontemporal_store(pack16<T>(v), reinterpret_cast<f32x4*>(out) + i + u * 256);
     }
   }
