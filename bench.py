@@ -130,8 +130,13 @@ def path_flops(chunk_lens):
 
 
 def kernel_src_hash():
+    """SHA-256 (16 hex digits) over the sources of the KDA kernels and the headers they include:
+    counters recorded in profiles/traffic.json stay valid while these bytes are unchanged."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "chunkwise_linear_attention_gated_amd", "csrc", "kernels", "*"))):
+    kdir = os.path.join(ROOT, "chunkwise_linear_attention_gated_amd", "csrc", "kernels")
+    files = sorted(glob.glob(os.path.join(kdir, "kda_*.hip"))) + [
+        os.path.join(kdir, n) for n in ("common.h", "launch.h", "state_common.h")]
+    for f in files:
         h.update(open(f, "rb").read())
     return h.hexdigest()[:16]
 
