@@ -44,7 +44,7 @@ struct harts_dev_plan {
   int32_t* units = nullptr;            // per round, (sequence, head) launch order of the serial passes
   std::vector<int32_t> rslot_off;      // [n_rounds + 1] offsets into rslots
   // workspace layout (byte offsets)
-  size_t off_W = 0, off_Op = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
+  size_t off_W = 0, off_Mf = 0, off_UpT = 0, off_KhT = 0, off_Qt = 0, off_Mm = 0, off_El = 0, off_Qe = 0, off_h = 0, off_dh = 0, off_hc = 0, off_dhc = 0, off_WT = 0, off_Kh = 0, off_sink = 0,
          off_dinit = 0, off_rg = 0, off_Tm = 0, off_Xm = 0, off_Am = 0, off_dslot = 0;
   size_t ws_fwd = 0, ws_bwd = 0;
   size_t off_ctr = 0;
@@ -248,16 +248,18 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.El = reinterpret_cast<float*>(at(d->off_El, dk, 4));
   a.sink = ws + d->off_sink;
   const bool f32 = d->dims.dtype == HARTS_DTYPE_FP32;
-  a.ws.QeffT = f32 ? at(d->off_Qe, dk * BT, es) : nullptr;
+  a.ws.QeffT = at(d->off_Qe, dk * BT, es);
   a.ws.WT = f32 ? at(d->off_WT, dk * BT, es) : nullptr;
   a.ws.Kh = f32 ? at(d->off_Kh, BT * dk, es) : nullptr;
   a.ws.Tm = at(d->off_Tm, BT * BT, es);
   a.ws.Xm = at(d->off_Xm, BT * BT, es);
   a.ws.Am = at(d->off_Am, BT * BT, es);
-  a.ws.Op = at(d->off_Op, BT * dv, es);
+  a.ws.Mf = at(d->off_Mf, BT * BT, es);
   a.h = at(d->off_h, dv * dk, es);
   a.hc = d->dims.dtype == HARTS_DTYPE_FP32 ? at(d->off_hc, dv * dk, es) : nullptr;
   a.ctr = nullptr;
+  a.zero = nullptr;
+  a.nzero = 0;
   return a;
 }
 
@@ -471,19 +473,21 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       // backward preparation and the gradient kernel; zeroed at the start of every call
       d->off_ctr = take(size_t(3) * d->p.rounds.size() * sizeof(int32_t));
       d->off_Qt = take(MC * BT * dk * es);
-      d->off_Op = take(MC * BT * dv * es);
+      d->off_Mf = take(MC * BT * BT * es);
       d->ws_fwd = off;
       // the backward arrays follow the forward's, so that a forward that keeps them for the
       // backward (harts_kda_io::keep) leaves its own outputs intact
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
-      // fp32 path only: channel-major copies of the chunk-start states and their gradients, and
-      // the state-gradient operands Qeff^T, W^T, K^ (the bf16 gradient kernel transposes its state
-      // slices in LDS, and the bf16 state-gradient pass reads the forward's operands transposed)
+      // the state-gradient pass's Qeff (bf16: [BT][D] fragment-major, read back transposed;
+      // fp32: Qeff^T); fp32 path only: channel-major copies of the chunk-start states and their
+      // gradients, and the state-gradient operands W^T, K^ (the bf16 gradient kernel transposes
+      // its state slices in LDS, and the bf16 state-gradient pass reads the forward's operands
+      // transposed)
+      d->off_Qe = take(MC * dk * BT * es);
       if (dtype == HARTS_DTYPE_FP32) {
         d->off_hc = take(MC * dv * dk * es);
         d->off_dhc = take(MC * dv * dk * es);
-        d->off_Qe = take(MC * dk * BT * es);
         d->off_WT = take(MC * dk * BT * es);
         d->off_Kh = take(MC * BT * dk * es);
       }
@@ -524,8 +528,8 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
     check_io(d, io, false);
     hipStream_t s0 = static_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(io->workspace);
-    // Preparation runs on an auxiliary stream (it depends on the inputs only); the serial
-    // passes follow in round order on the caller's stream.
+    // Preparation of every round after the first runs on an auxiliary stream (it depends on the
+    // inputs only); the serial passes follow in round order on the caller's stream.
     Events ev;
     hipStream_t s1 = aux_stream(0);
     const bool slab = harts::kda_slab_supported(d->dims);
@@ -538,22 +542,28 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
       else if (d->kept_ws == io->workspace) d->kept_ws = nullptr;
     }
     int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
-    hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(d->p.n_rounds), s0), "counter reset");
-    fork(s0, s1, ev);
-    // Round r + 1's preparation is enqueued behind the start of round r's serial pass, so that
-    // the serial pass takes its compute units first; the preparation's workgroups draw items
-    // from a counter and fill the rest of the chip as it frees up.
+    // The first round's preparation runs on the caller's stream in static item order and clears
+    // the item counters of every later launch (no separate reset launch); round r + 1's
+    // preparation is enqueued behind the start of round r's serial pass, so that the serial pass
+    // takes its compute units first, and its workgroups draw items from a counter and fill the
+    // rest of the chip as it frees up.
     hipEvent_t started = nullptr;
     for (int r = 0; r < d->p.n_rounds; ++r) {
       const int64_t units = int64_t(d->p.rounds[r].vrow1 - d->p.rounds[r].vrow0) * d->dims.H;
+      hipStream_t sp = r == 0 ? s0 : s1;
       if (started) hip_check(hipStreamWaitEvent(s1, started, 0), "hipStreamWaitEvent");
       {
         harts::RoundArgs a = round_args(d, io, r, ws);
-        a.ctr = ctr + 3 * r;
-        ProfScope ps("kda_prep_fwd", s1, units);
-        hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, s1), "prep kernel launch");
+        if (r == 0) {
+          a.zero = ctr;
+          a.nzero = 3 * d->p.n_rounds;
+        } else {
+          a.ctr = ctr + 3 * r;
+        }
+        ProfScope ps("kda_prep_fwd", sp, units);
+        hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, sp), "prep kernel launch");
       }
-      hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
+      if (r > 0) hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
       started = ev.record(s0);
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
@@ -597,9 +607,9 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     Events ev;
     hipStream_t s1 = aux_stream(0), s2 = aux_stream(1);
     int32_t* ctr = reinterpret_cast<int32_t*>(ws + d->off_ctr);
-    hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(R), s0), "counter reset");
-    fork(s0, s1, ev);
-    fork(s0, s2, ev);
+    // Recompute: the last round's preparation runs first, on the caller's stream, in static item
+    // order, and clears the item counters of every later launch.  Keep: a reset launch does.
+    if (keep) hip_check(harts::launch_zero_i32(ctr, 3 * int64_t(R), s0), "counter reset");
     auto round = [&](int r) {
       harts::BwdRoundArgs b{};
       b.r = round_args(d, io, r, ws);
@@ -626,13 +636,25 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     std::vector<hipEvent_t> prepped(R, nullptr), recomputed(R, nullptr);
     for (int r = R - 1; r >= 0 && !keep; --r) {
       harts::BwdRoundArgs b = round(r);
+      const bool first = r == R - 1;
       {
-        ProfScope ps("kda_prep_bwd", s1, units(r));
+        hipStream_t sp = first ? s0 : s1;
+        ProfScope ps("kda_prep_bwd", sp, units(r));
         harts::RoundArgs a = b.r;
-        a.ctr = ctr + 3 * r + 1;
-        hip_check(harts::launch_kda_prep(d->dims, a, 1, s1), "prep kernel launch");
+        if (first) {
+          a.zero = ctr;
+          a.nzero = 3 * R;
+        } else {
+          a.ctr = ctr + 3 * r + 1;
+        }
+        hip_check(harts::launch_kda_prep(d->dims, a, 1, sp), "prep kernel launch");
       }
-      prepped[size_t(r)] = ev.record(s1);
+      if (first) {
+        fork(s0, s1, ev);
+        prepped[size_t(r)] = nullptr;  // on the caller's stream already
+      } else {
+        prepped[size_t(r)] = ev.record(s1);
+      }
       {
         ProfScope ps("kda_state_bwd", s1, units(r));
         if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 1, d->p.rounds[r].max_chunks, s1), "state kernel launch");
@@ -652,9 +674,10 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
         hip_check(harts::launch_kda_grad(d->dims, b, s2), "gradient kernel launch");
       }
     };
+    if (keep) fork(s0, s1, ev);
+    fork(s0, s2, ev);
     for (int r = R - 1; r >= 0; --r) {
       harts::BwdRoundArgs b = round(r);
-      if (!keep) hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       if (b.dslot) {
         // gradients of the states this round hands off: complete, since every consumer runs later
         const int32_t n0 = d->rslot_off[size_t(r)], n1 = d->rslot_off[size_t(r) + 1];
@@ -663,6 +686,9 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
                                           const_cast<float*>(b.dslot), s0),
                   "slot gradient launch");
       }
+      // the slot gradients above need only the later rounds; this round's preparation is awaited
+      // after them
+      if (prepped[size_t(r)]) hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       // round r + 1's state gradient (and everything before it on s0) is complete here
       hipEvent_t ready = ev.record(s0);
       {

@@ -8,6 +8,8 @@
 //   T = (I + diag(beta) A)^{-1} diag(beta),
 //   W = T (K e^G), U' = T V,
 //   U = U' - W S0,  O = (Q e^G) S0 + M U,  S = diag(e^{G_last}) S0 + (K e^{G_last - G})^T U.
+// The serial pass forms O from Q e^G and M itself (both are written here); the backward's
+// state-gradient pass takes Qeff = Q e^G - M W, which the backward preparation writes.
 // "gated" products use e^{G_i - G_j} factored through 16-row sub-block
 // reference points: for rows i in block bi and j in block bj < bi,
 // e^{G_i - G_j} = e^{G_i - F_bi} * e^{F_bi - F_{bj+1}} * e^{F_{bj+1} - G_j}, F_b the
@@ -266,6 +268,8 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
   uint8_t* smask = reinterpret_cast<uint8_t*>(vec + Ly::SMK);
 
   const int tid0 = threadIdx.x;
+  if (a.zero && blockIdx.x == 0)
+    for (int i = tid0; i < a.nzero; i += CNT) a.zero[i] = 0;
   const int nitems = a.nchunk * H;
   int item = blockIdx.x;
   if (item >= nitems) return;
@@ -468,14 +472,16 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
-          // M to the workspace: row-major for the bf16 gradient kernel, fragment-major for the
+          // M to the workspace: row-major for the bf16 gradient kernel, permuted fragment-major
+          // (rows i, contraction j) for the bf16 forward serial pass, fragment-major for the
           // fp32 serial pass
           if constexpr (PF) {
             if constexpr (BWD) store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
+            if constexpr (FO) store4(static_cast<T*>(a.ws.Mf) + wsi * BT * BT + pf_off(i, j0, BT), v[0], v[1], v[2], v[3]);
           } else {
             fm_store<T>(Mg, BT, i, j0, v, 4);
           }
-          if (BWD || PF) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
+          if constexpr (BWD) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -596,6 +602,16 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
+      if constexpr (PF && FO) {
+        // Q~ [BT][D] permuted fragment-major (rows: tokens, contraction: channels) from the
+        // token-major Q~, one 16-byte operand register per piece
+        T* qg = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
+        HARTS_STRIDED(pc, ht, BT * D / 8, HN) {
+          const int blk = pc / 64, l = pc % 64;
+          const int rt = blk / (D / 32), kb = blk % (D / 32);
+          *reinterpret_cast<bf16x8*>(qg + size_t(pc) * 8) = pf_kc(Qr, LDK, 16 * rt, 32 * kb, l);
+        }
+      }
       if constexpr (BWD) {
         T* ag = static_cast<T*>(a.ws.Am) + wsi * size_t(BT) * BT;
         HARTS_STRIDED(idx, ht, BT * (BT / VN), HN) {
@@ -609,16 +625,14 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     }
     __syncthreads();
     // 8. U' = T V (accumulator tiles), W = T K~; backward: T, X out.
-    //    PF: W (and W^T) are stored negated; W stays in registers for Qeff = Q~ - M W.
+    //    PF: W is stored negated.  Backward: W stays in registers for Qeff = Q~ - M W.
     {
       T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
       T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
-      // PF forward outputs: U' kept in registers, staged over V once every wave has read V
-      T* Ul = Vl;
       constexpr int NU = (BT / 16) * (DV / 16), NW = (D / 16) * (BT / 16);
-      constexpr bool KEEPW = BWD || PF, KEEPU = PF && FO;
+      constexpr bool KEEPW = BWD;
       constexpr int NWW = KEEPW ? (NW + CNW - 1) / CNW : 1, NUW = (NU + CNW - 1) / CNW;
-      f32x4 wacc[NWW], uacc[KEEPU ? NUW : 1];
+      f32x4 wacc[NWW];
 #pragma unroll
       for (int u = 0; u < NUW; ++u) {
         const int jb = wave + CNW * u;
@@ -630,7 +644,6 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           for (int k0 = 0; k0 < BT; k0 += MM::KS)
             acc = MM::mma(MM::kc(Tm, LDJ, 16 * mt, k0, lane), MM::rc(Vl, LDV, 16 * nt, k0, lane), acc);
           store4(upg + cm_off(16 * mt + crow(lane, 0), 16 * nt + ccol(lane), DV), acc[0], acc[1], acc[2], acc[3]);
-          if constexpr (KEEPU) uacc[u] = acc;
         }
       }
       if constexpr (KEEPW) {
@@ -667,8 +680,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           for (int k0 = 0; k0 < BT; k0 += MM::KS)
             acc = MM::mma(MM::rc(Kt, LDK, 16 * mt, k0, lane), MM::kc(Tm, LDJ, 16 * nt, k0, lane), acc);
           const int i = 16 * nt + ccol(lane), c0 = 16 * mt + crow(lane, 0);
-          const float wv[4] = {acc[0], acc[1], acc[2], acc[3]};
-          fm_store<T>(wg, D, i, c0, wv, 4);
+          if constexpr (PF) {
+            store4(wg + pf_off(i, c0, D), -acc[0], -acc[1], -acc[2], -acc[3]);
+          } else {
+            const float wv[4] = {acc[0], acc[1], acc[2], acc[3]};
+            fm_store<T>(wg, D, i, c0, wv, 4);
+          }
         }
       }
       if constexpr (!PF) {  // (bf16: exported during step 7)
@@ -694,7 +711,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
         }
       }
       if constexpr (KEEPW) {
-        __syncthreads();  // every wave is done reading K~ and V: W and U' take their places
+        __syncthreads();  // every wave is done reading K~: W takes its place
 #pragma unroll
         for (int u = 0; u < NWW; ++u) {
           const int jb = wave + CNW * u;
@@ -705,25 +722,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             store4(Kt + i * LDK + c0, wacc[u][0], wacc[u][1], wacc[u][2], wacc[u][3]);
           }
         }
-        if constexpr (KEEPU) {
-#pragma unroll
-          for (int u = 0; u < NUW; ++u) {
-            const int jb = wave + CNW * u;
-            if (jb < NU) {
-              constexpr int NT = DV / 16;
-              const int mt = jb / NT, nt = jb % NT;
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                Ul[(16 * mt + crow(lane, r)) * LDV + 16 * nt + ccol(lane)] = from_f<T>(uacc[u][r]);
-            }
-          }
-        }
         __syncthreads();
         if constexpr (PF) {
           // 9. Qeff = Q~ - M W, in tiles of token rows and channel columns, stored as Qeff [BT][D]
           //    after a 4 x 4 lane transpose (the state-gradient pass reads it back transposed);
           //    Q~ of the tile by one transposing read
-          T* qe = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
+          T* qe = static_cast<T*>(a.ws.QeffT) + wsi * BT * D;
           constexpr int MT = BT / 16, NT = D / 16;
           HARTS_STRIDED(jb, wave, MT * NT, CNW) {
             const int mt = jb / NT, nt = jb % NT;
@@ -754,18 +758,6 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = to_f(Qr[(i0 + r) * LDK + c]) - acc[r];
             fm_store<T>(qe, BT, c, i0, v, 4);
-          }
-        }
-        if constexpr (PF && FO) {
-          // O' = M U' as accumulator tiles of O'^T (value rows, token columns)
-          T* opg = static_cast<T*>(a.ws.Op) + wsi * BT * DV;
-          HARTS_STRIDED(jb, wave, (DV / 16) * (BT / 16), CNW) {
-            const int jt = jb / (BT / 16), it = jb % (BT / 16);
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BT; k0 += MM::KS)
-              acc = MM::mma(MM::rc(Ul, LDV, 16 * jt, k0, lane), MM::kc(Ml, LDJ, 16 * it, k0, lane), acc);
-            store4(opg + ((size_t(jt) * (BT / 16) + it) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
           }
         }
       }
@@ -988,8 +980,8 @@ __global__ __launch_bounds__(64 * state_waves<D>()) void kda_state_kernel(RoundA
 // ------------------------------------------------------------------------------------------
 template <typename T, int BT, int D, int DV>
 static hipError_t prep_launch(const KdaDims& d, const RoundArgs& a, int mode, hipStream_t s) {
-  if (a.nchunk <= 0) return hipSuccess;
-  dim3 grid(persistent_grid(unsigned(a.nchunk) * d.H)), block(CNT);
+  if (a.nchunk <= 0 && !a.zero) return hipSuccess;
+  dim3 grid(a.nchunk > 0 ? persistent_grid(unsigned(a.nchunk) * d.H) : 1u), block(CNT);
   if (mode == 1) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 1>), grid, block, 0, s, a, d.H);
   else if (mode == 0) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 0>), grid, block, 0, s, a, d.H);
   else if constexpr (sizeof(T) == 2) hipLaunchKernelGGL((kda_prep_kernel<T, BT, D, DV, 2>), grid, block, 0, s, a, d.H);

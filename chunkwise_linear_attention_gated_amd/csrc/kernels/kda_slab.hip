@@ -5,8 +5,8 @@
 // blog, sections 1.2 and 4.2); boundary states are handed between packed calls and their
 // gradients flow back through the handoff (blog, section 4.3).  Per chunk, with the chunk
 // quantities of the preparation kernel (W = T (K e^G), U' = T V, K^ = K e^{G_last - G},
-// Qeff = Q e^G - M W, O' = M U', E = e^{G_last}):
-//   forward:    U = U' - W S,   O = Qeff S + O',   S <- diag(E) S + K^^T U
+// Q~ = Q e^G, M = lower(gated Q K^T), Qeff = Q~ - M W, E = e^{G_last}):
+//   forward:    U = U' - W S,   O = Q~ S + M U,    S <- diag(E) S + K^^T U
 //   recompute:  the forward's state chain only, writing every chunk-start state
 //   gradient:   Y = K^ dS,      dS <- diag(E) dS + Qeff^T dO - W^T Y   (reverse over chunks)
 //
@@ -17,8 +17,8 @@
 // state nor U nor Y ever leaves the wave.
 //
 // Each workgroup has one producer wave besides its NC compute waves.  The producer issues
-// every load of a chunk -- the operands shared by all slabs (W, Qeff, K^^T; K^, Qeff^T, W^T;
-// E), the per-slab inputs (U', O'; dO) and the chunk descriptor -- as direct-to-LDS buffer
+// every load of a chunk -- the operands shared by all slabs (W, Q~, K^^T, M; K^, Qeff^T, W^T;
+// E), the per-slab inputs (U'; dO) and the chunk descriptor -- as direct-to-LDS buffer
 // loads into a ring of RD buffers, RD-1 chunks ahead; one workgroup barrier per chunk hands
 // a buffer over.  The compute waves never wait on memory: they read LDS, run the matrix
 // cores and store their outputs.
@@ -40,15 +40,17 @@ struct SlabCfg {
   static constexpr int KBD = D / 32, KBT = BT / 32, NTT = BT / 16, NTS = D / 16;
   static constexpr int BD = BT * D / 512;                // 1 KiB operand blocks per shared array
   static constexpr bool FO = MODE == SLAB_FWD || MODE == SLAB_FWDS;  // forward outputs
-  static constexpr int NARR = MODE == SLAB_REC ? 2 : 3;  // shared arrays
-  static constexpr int EOFF = NARR * BD * 1024;          // E (fp32 [D]), then the chunk descriptor
+  static constexpr int NARR = MODE == SLAB_REC ? 2 : 3;  // shared [BT][D] arrays
+  static constexpr int MB = FO ? BT * BT / 512 : 0;      // forward: M ([BT][BT]) blocks after them
+  static constexpr int MOFF = NARR * BD * 1024;
+  static constexpr int EOFF = MOFF + MB * 1024;          // E (fp32 [D]), then the chunk descriptor
   static constexpr int SOFF = EOFF + 1024;               // per-slab inputs
   static constexpr int PA = BT * 32;                     // bytes of one per-slab array (BT x 16 x 2 B)
-  static constexpr int NPA = FO ? 2 : 1;             // per-slab arrays: U', O' | U' | dO
+  static constexpr int NPA = 1;                          // per-slab arrays: U' | dO
   static constexpr int SLABS = NC * NS, NGRP = DV / (16 * SLABS);
   static constexpr int BUF = SOFF + SLABS * NPA * PA;    // bytes per ring buffer
   // producer loads per chunk: shared blocks, E, descriptor, per-slab blocks
-  static constexpr int NDMA = NARR * BD + 2 + SLABS * NPA * (PA / 1024);
+  static constexpr int NDMA = NARR * BD + MB + 2 + SLABS * NPA * (PA / 1024);
   static constexpr int NW = NC + 1;                      // waves per workgroup
   static_assert(BT % 32 == 0 && D % 32 == 0 && D * 4 + 32 <= 1024, "slab tiling");
   static_assert(DV % (16 * SLABS) == 0 && PA % 1024 == 0, "slab split");
@@ -107,7 +109,7 @@ struct SlabPass {
 
   // ---- producer ---------------------------------------------------------------------------
   struct Src {
-    __amdgpu_buffer_rsrc_t arr[3], el, up, op, dO, desc;
+    __amdgpu_buffer_rsrc_t arr[3], el, up, m, dO, desc;
   };
   __device__ __forceinline__ void make_src(Src& r) const {
     const RoundArgs& a = b.r;
@@ -116,7 +118,7 @@ struct SlabPass {
     if constexpr (MODE == SLAB_DST) {
       // the forward's operand layouts, read back transposed (see read_phase)
       r.arr[0] = buf_rsrc(a.ws.KhT, opb);
-      r.arr[1] = buf_rsrc(a.ws.Qt, opb);
+      r.arr[1] = buf_rsrc(a.ws.QeffT, opb);
       r.arr[2] = buf_rsrc(a.ws.W, opb);
       r.dO = buf_rsrc(b.dO, size_t(0x7fffffff));
     } else {
@@ -124,7 +126,7 @@ struct SlabPass {
       r.arr[1] = buf_rsrc(FO ? a.ws.Qt : a.ws.KhT, opb);
       r.arr[2] = buf_rsrc(a.ws.KhT, opb);
       r.up = buf_rsrc(a.ws.UpT, items * BT * DV * 2);
-      r.op = buf_rsrc(FO ? a.ws.Op : a.ws.UpT, items * BT * DV * 2);
+      r.m = buf_rsrc(FO ? a.ws.Mf : a.ws.UpT, items * BT * BT * 2);
     }
     r.el = buf_rsrc(a.ws.El, items * D * 4);
     r.desc = buf_rsrc(a.chunks, size_t(a.nchunk) * sizeof(ChunkDesc));
@@ -141,6 +143,8 @@ struct SlabPass {
     for (int ar = 0; ar < C::NARR; ++ar)
 #pragma unroll
       for (int q = 0; q < BD; ++q) lds_load16(r.arr[ar], dst + (ar * BD + q) * 1024, vs, int(w * BT * D * 2) + q * 1024);
+#pragma unroll
+    for (int q = 0; q < C::MB; ++q) lds_load16(r.m, dst + C::MOFF + q * 1024, vo, int(w * BT * BT * 2) + q * 1024);
     // E in lanes [0, D/4), the chunk descriptor (32 bytes) in the next two lanes
     constexpr int NE = D / 4;
     if (lane < NE) lds_load16(r.el, dst + C::EOFF, vo, int(w * D * 4));
@@ -167,32 +171,32 @@ struct SlabPass {
           const int i = 2 * x + (lane >> 5);
           lds_load16(r.up, sdst + x * 1024, (i * (DV / 16) + j) * 512 + (lane & 31) * 16, int(w * BT * DV * 2));
         }
-        if constexpr (FO) {
-          // O'^T accumulator tiles (slab j, token block i): contiguous per slab
-#pragma unroll
-          for (int x = 0; x < C::PA / 1024; ++x)
-            lds_load16(r.op, sdst + C::PA + x * 1024, j * NTT * 512 + x * 1024 + vo, int(w * BT * DV * 2));
-        }
       }
     }
   }
 
   // ---- compute: LDS operand phases ------------------------------------------------------
-  // A chunk's products form 2-3 phases of up to 16 operand fragments each (one product:
-  // U, O, S forward; Qeff^T dO, Y, W^T Y gradient).  Fragments are ordered contraction slice
-  // outer, tile inner, so consecutive matrix-core operations feed independent accumulators;
-  // phase p+1 is read from LDS while the matrix cores work through phase p.
+  // A chunk's products form 2-4 phases of up to 16 operand fragments each (one product:
+  // U, Q~ S, S, M U forward; Qeff^T dO, Y, W^T Y gradient).  Fragments are ordered contraction
+  // slice outer, tile inner, so consecutive matrix-core operations feed independent
+  // accumulators; phase p+1 is read from LDS while the matrix cores work through phase p.
   static constexpr int NFT = KBD * NTT;  // token-block products (U, O, Y)
   static constexpr int NFS = KBT * NTS;  // state-tile products (S, Qeff^T dO, W^T Y)
+  static constexpr int NFQ = KBT * NTT;  // in-chunk product (M U)
   static constexpr int NFM = NFT > NFS ? NFT : NFS;
-  static constexpr int NP = MODE == SLAB_REC ? 2 : 3;
+  static constexpr int NP = MODE == SLAB_REC ? 2 : (FO ? 4 : 3);
   struct Phase {
     bf16x8 f[NFM];
     f32x4 e[NTS];
   };
-  // kind of phase p: 0 token-block product, 1 state-tile product
+  // kind of phase p: 0 token-block product, 1 state-tile product, 2 in-chunk product
   __device__ __forceinline__ static constexpr int phase_kind(int ph) {
-    return MODE == SLAB_DST ? (ph == 1 ? 0 : 1) : (ph == NP - 1 ? 1 : 0);
+    if (MODE == SLAB_DST) return ph == 1 ? 0 : 1;
+    if (MODE == SLAB_REC) return ph;
+    return ph < 2 ? 0 : ph - 1;
+  }
+  __device__ __forceinline__ static constexpr int phase_mfma(int ph) {
+    return (phase_kind(ph) == 2 ? NFQ : NFM) * NS;
   }
   __device__ __forceinline__ bf16x8 frag(const char* arr, int blk) const {
     return *reinterpret_cast<const bf16x8*>(arr + (size_t(blk) * 64 + lane) * 16);
@@ -205,8 +209,8 @@ struct SlabPass {
       arr = p + (ph == 0 ? 1 : (ph == 1 ? 0 : 2)) * BD * 1024;  // Qeff^T, K^, W^T
       with_e = ph == 0;
     } else {
-      arr = p + (ph == NP - 1 ? NP - 1 : ph) * BD * 1024;  // W, [Qeff], K^^T
-      with_e = ph == NP - 1;
+      arr = p + (phase_kind(ph) == 2 ? C::MOFF : ph * BD * 1024);  // W, [Q~], K^^T, [M]
+      with_e = phase_kind(ph) == 1;
     }
     if constexpr (MODE == SLAB_DST) {
       // The gradient's operands are the transposes of the forward's: K^ from K^^T [D][BT], Qeff^T
@@ -240,6 +244,11 @@ struct SlabPass {
       for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
         for (int i = 0; i < NTT; ++i) g.f[kb * NTT + i] = frag(arr, i * KBD + kb);
+    } else if (phase_kind(ph) == 2) {
+#pragma unroll
+      for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+        for (int i = 0; i < NTT; ++i) g.f[kb * NTT + i] = frag(arr, i * KBT + kb);
     } else {
 #pragma unroll
       for (int kb = 0; kb < KBT; ++kb)
@@ -263,7 +272,7 @@ struct SlabPass {
       prep(ph, g[ph & 1]);
       mma(ph, g[ph & 1]);
 #pragma unroll
-      for (int x = 0; x < NFM * NS; ++x) {
+      for (int x = 0; x < phase_mfma(ph); ++x) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                        // one matrix-core op
         __builtin_amdgcn_sched_group_barrier(0x100, MODE == SLAB_DST ? 2 : 1, 0);  // its share of LDS reads
       }
@@ -320,7 +329,7 @@ struct SlabPass {
 #pragma unroll
       for (int i = 0; i < NTT; ++i) {
         U[s][i] = f4_of(*reinterpret_cast<const bf16x4*>(in + i * 512 + lane * 8));
-        if constexpr (FO) O[s][i] = f4_of(*reinterpret_cast<const bf16x4*>(in + C::PA + i * 512 + lane * 8));
+        if constexpr (FO) O[s][i] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
     walk(
@@ -350,13 +359,22 @@ struct SlabPass {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) U[s][i] = mfma_bf16(g.f[kb * NTT + i], Sf[s][kb], U[s][i]);
           } else if (phase_kind(ph) == 0) {
-            // O^T = S^T Qeff^T + O'^T
+            // O^T = S^T Q~^T
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
               for (int i = 0; i < NTT; ++i)
 #pragma unroll
                 for (int s = 0; s < NS; ++s) O[s][i] = mfma_bf16(Sf[s][kb], g.f[kb * NTT + i], O[s][i]);
+          } else if (phase_kind(ph) == 2) {
+            // O^T += U^T M^T: the bf16 U fragments of the state update are U^T's operand
+            // registers in the same contraction order as M's fragments
+#pragma unroll
+            for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+              for (int i = 0; i < NTT; ++i)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) O[s][i] = mfma_bf16(Uf[s][kb], g.f[kb * NTT + i], O[s][i]);
           } else {
 #pragma unroll
             for (int kb = 0; kb < KBT; ++kb)
@@ -609,10 +627,18 @@ static hipError_t slab_go(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s
 // of the chip (at most a quarter of the compute units' worth of slabs) runs one slab per
 // workgroup, for the shortest chain latency; a larger round shares the chip with the per-chunk
 // kernels of other rounds, and packing its chains onto fewer compute units leaves them more.
+// A forward round of at most half the compute units' worth of slabs (a long root sequence)
+// runs one compute wave of two slabs per workgroup: the same chain per wave on twice the
+// compute units, each wave with its ring and LDS to itself.
 template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
-  if (4 * slabs <= persistent_grid(1u << 30)) return slab_go<MODE, BT, D, DV, 1, 1, 3>(d, b, s);
+  constexpr bool FWD = MODE == SLAB_FWD || MODE == SLAB_FWDS;
+  // (the forward's ring buffers also hold M: two of them fit)
+  constexpr int RD1 = FWD ? 2 : 3;
+  const unsigned cus = persistent_grid(1u << 30);
+  if (4 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 1, RD1>(d, b, s);
+  if (FWD && 2 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);
   return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
 }
 

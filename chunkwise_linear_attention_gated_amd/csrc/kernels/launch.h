@@ -15,16 +15,16 @@ struct ChunkWs {
   void* W;      // [BT][D]   W = T (K * e^G)                      (token-major)
   void* UpT;    // [DV][BT]  (T V)^T
   void* KhT;    // [D][BT]   (K * e^{G_last - G})^T
-  void* Qt;     // [BT][D]   Q * e^G                               (forward)
+  void* Qt;     // [BT][D]   Q~ = Q * e^G                          (forward)
   void* Mm;     // [BT][BT]  M = lower(gated Q K^T)
   float* El;    // [D]       e^{G_last}
-  void* QeffT;  // [D][BT]   (Q~ - M W)^T                          (backward, fp32 path)
+  void* QeffT;  // [D][BT]   (Q~ - M W)^T; bf16: Qeff [BT][D]      (backward)
   void* WT;     // [D][BT]   W^T                                   (backward, fp32 path)
   void* Kh;     // [BT][D]   K * e^{G_last - G}                    (backward, fp32 path)
   void* Tm;     // [BT][BT]  T = X diag(beta)                      (backward)
   void* Xm;     // [BT][BT]  X = (I + diag(beta) A)^{-1}           (backward)
   void* Am;     // [BT][BT]  A (strictly lower)                    (backward)
-  void* Op;     // O'^T = (M U')^T as accumulator tiles             (forward, slab passes)
+  void* Mf;     // [BT][BT]  M, permuted fragment-major             (forward, bf16 slab passes)
 };
 
 struct KdaDims {
@@ -50,6 +50,8 @@ struct RoundArgs {
   void* hc;                   // backward: S_n per chunk, channel-major [chunk][H][D][DV] (nullable)
   int* ctr;                   // zeroed item counter of this launch of a persistent per-chunk kernel
                               // (nullable: static item order)
+  int* zero;                  // preparation kernel: item counters that its block 0 clears for the
+  int32_t nzero;              // launches ordered after it (nullable)
   const int32_t* units;       // serial passes: this round's (sequence, head) pairs s * H + h in
                               // launch order (nullable: natural order)
 };
