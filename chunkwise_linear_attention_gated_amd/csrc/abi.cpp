@@ -248,7 +248,7 @@ harts::RoundArgs round_args(const harts_dev_plan* d, const harts_kda_io* io, int
   a.ws.El = reinterpret_cast<float*>(at(d->off_El, dk, 4));
   a.sink = ws + d->off_sink;
   const bool f32 = d->dims.dtype == HARTS_DTYPE_FP32;
-  a.ws.QeffT = at(d->off_Qe, dk * BT, es);
+  a.ws.QeffT = f32 ? at(d->off_Qe, dk * BT, es) : nullptr;
   a.ws.WT = f32 ? at(d->off_WT, dk * BT, es) : nullptr;
   a.ws.Kh = f32 ? at(d->off_Kh, BT * dk, es) : nullptr;
   a.ws.Tm = at(d->off_Tm, BT * BT, es);
@@ -479,15 +479,13 @@ int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv,
       // backward (harts_kda_io::keep) leaves its own outputs intact
       d->off_h = take(MC * dv * dk * es);
       d->off_dh = take(MC * dv * dk * es);
-      // the state-gradient pass's Qeff (bf16: [BT][D] fragment-major, read back transposed;
-      // fp32: Qeff^T); fp32 path only: channel-major copies of the chunk-start states and their
-      // gradients, and the state-gradient operands W^T, K^ (the bf16 gradient kernel transposes
-      // its state slices in LDS, and the bf16 state-gradient pass reads the forward's operands
-      // transposed)
-      d->off_Qe = take(MC * dk * BT * es);
+      // fp32 path only: channel-major copies of the chunk-start states and their gradients, and
+      // the state-gradient operands Qeff^T, W^T, K^ (the bf16 gradient kernel transposes its state
+      // slices in LDS, and the bf16 state-gradient pass reads the forward's operands transposed)
       if (dtype == HARTS_DTYPE_FP32) {
         d->off_hc = take(MC * dv * dk * es);
         d->off_dhc = take(MC * dv * dk * es);
+        d->off_Qe = take(MC * dk * BT * es);
         d->off_WT = take(MC * dk * BT * es);
         d->off_Kh = take(MC * BT * dk * es);
       }

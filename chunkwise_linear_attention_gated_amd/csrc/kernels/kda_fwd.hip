@@ -8,8 +8,8 @@
 //   T = (I + diag(beta) A)^{-1} diag(beta),
 //   W = T (K e^G), U' = T V,
 //   U = U' - W S0,  O = (Q e^G) S0 + M U,  S = diag(e^{G_last}) S0 + (K e^{G_last - G})^T U.
-// The serial pass forms O from Q e^G and M itself (both are written here); the backward's
-// state-gradient pass takes Qeff = Q e^G - M W, which the backward preparation writes.
+// The bf16 serial passes take Q e^G and M (both written here) and form their products with
+// Qeff = Q e^G - M W through them; the fp32 state-gradient kernel reads Qeff^T.
 // "gated" products use e^{G_i - G_j} factored through 16-row sub-block
 // reference points: for rows i in block bi and j in block bj < bi,
 // e^{G_i - G_j} = e^{G_i - F_bi} * e^{F_bi - F_{bj+1}} * e^{F_{bj+1} - G_j}, F_b the
@@ -473,15 +473,15 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
             for (int r = 0; r < 4; ++r) v[r] = (bi == bj && j0 + r > i) ? 0.f : acc[r];
           }
           // M to the workspace: row-major for the bf16 gradient kernel, permuted fragment-major
-          // (rows i, contraction j) for the bf16 forward serial pass, fragment-major for the
-          // fp32 serial pass
+          // (rows i, contraction j) for the bf16 serial passes, fragment-major for the fp32
+          // serial pass
           if constexpr (PF) {
             if constexpr (BWD) store4(Mg + i * BT + j0, v[0], v[1], v[2], v[3]);
-            if constexpr (FO) store4(static_cast<T*>(a.ws.Mf) + wsi * BT * BT + pf_off(i, j0, BT), v[0], v[1], v[2], v[3]);
+            store4(static_cast<T*>(a.ws.Mf) + wsi * BT * BT + pf_off(i, j0, BT), v[0], v[1], v[2], v[3]);
           } else {
             fm_store<T>(Mg, BT, i, j0, v, 4);
           }
-          if constexpr (BWD) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
+          if constexpr (BWD && !PF) store4(Ml + i * LDJ + j0, v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           *reinterpret_cast<bf16x8*>(khg + size_t(pc) * 8) = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         }
       }
-      if constexpr (PF && FO) {
+      if constexpr (PF) {
         // Q~ [BT][D] permuted fragment-major (rows: tokens, contraction: channels) from the
         // token-major Q~, one 16-byte operand register per piece
         T* qg = static_cast<T*>(a.ws.Qt) + wsi * BT * D;
@@ -625,12 +625,12 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
     }
     __syncthreads();
     // 8. U' = T V (accumulator tiles), W = T K~; backward: T, X out.
-    //    PF: W is stored negated.  Backward: W stays in registers for Qeff = Q~ - M W.
+    //    PF: W is stored negated.  fp32 backward: W stays in registers for Qeff = Q~ - M W.
     {
       T* upg = static_cast<T*>(a.ws.UpT) + wsi * DV * BT;
       T* wg = static_cast<T*>(a.ws.W) + wsi * BT * D;
       constexpr int NU = (BT / 16) * (DV / 16), NW = (D / 16) * (BT / 16);
-      constexpr bool KEEPW = BWD;
+      constexpr bool KEEPW = BWD && !PF;
       constexpr int NWW = KEEPW ? (NW + CNW - 1) / CNW : 1, NUW = (NU + CNW - 1) / CNW;
       f32x4 wacc[NWW];
 #pragma unroll
@@ -723,27 +723,7 @@ __global__ __launch_bounds__(CNT) void kda_prep_kernel(RoundArgs a, int H) {
           }
         }
         __syncthreads();
-        if constexpr (PF) {
-          // 9. Qeff = Q~ - M W, in tiles of token rows and channel columns, stored as Qeff [BT][D]
-          //    after a 4 x 4 lane transpose (the state-gradient pass reads it back transposed);
-          //    Q~ of the tile by one transposing read
-          T* qe = static_cast<T*>(a.ws.QeffT) + wsi * BT * D;
-          constexpr int MT = BT / 16, NT = D / 16;
-          HARTS_STRIDED(jb, wave, MT * NT, CNW) {
-            const int mt = jb / NT, nt = jb % NT;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k0 = 0; k0 < BT; k0 += MM::KS)
-              acc = MM::mma(MM::kc(Ml, LDJ, 16 * mt, k0, lane), MM::rc(Kt, LDK, 16 * nt, k0, lane), acc);
-            const int i0 = 16 * mt + crow(lane, 0), q = lane & 15;
-            const bf16x4 qv = ds_tr16(Qr + (16 * mt + 4 * (lane >> 4) + (q >> 2)) * LDK + 16 * nt + 4 * (q & 3));
-            f32x4 v;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) v[r] = (float)qv[r] - acc[r];
-            const f32x4 y = quad_transpose(v, lane);
-            store4(qe + pf_off(i0 + (lane & 3), 16 * nt + 4 * (q >> 2), D), y[0], y[1], y[2], y[3]);
-          }
-        } else if constexpr (BWD) {
+        {
           // 9. Qeff = Q~ - M W, stored as Qeff^T [D][BT]
           T* qe = static_cast<T*>(a.ws.QeffT) + wsi * D * BT;
           constexpr int MT = BT / 16, NT = D / 16;

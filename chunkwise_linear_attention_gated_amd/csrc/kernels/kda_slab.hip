@@ -8,7 +8,8 @@
 // Q~ = Q e^G, M = lower(gated Q K^T), Qeff = Q~ - M W, E = e^{G_last}):
 //   forward:    U = U' - W S,   O = Q~ S + M U,    S <- diag(E) S + K^^T U
 //   recompute:  the forward's state chain only, writing every chunk-start state
-//   gradient:   Y = K^ dS,      dS <- diag(E) dS + Qeff^T dO - W^T Y   (reverse over chunks)
+//   gradient:   Y = K^ dS + M^T dO,  dS <- diag(E) dS + Q~^T dO - W^T Y   (reverse over chunks;
+//               Qeff^T dO - W^T K^ dS regrouped, Qeff = Q~ - M W)
 //
 // The value columns of S (and dS) evolve independently.  Each compute wave owns NS slabs of
 // 16 value columns of one (sequence, head) and keeps them in accumulator registers for the
@@ -17,7 +18,7 @@
 // state nor U nor Y ever leaves the wave.
 //
 // Each workgroup has one producer wave besides its NC compute waves.  The producer issues
-// every load of a chunk -- the operands shared by all slabs (W, Q~, K^^T, M; K^, Qeff^T, W^T;
+// every load of a chunk -- the operands shared by all slabs (W, Q~, K^^T, M; K^, Q~^T, W^T, M^T;
 // E), the per-slab inputs (U'; dO) and the chunk descriptor -- as direct-to-LDS buffer
 // loads into a ring of RD buffers, RD-1 chunks ahead; one workgroup barrier per chunk hands
 // a buffer over.  The compute waves never wait on memory: they read LDS, run the matrix
@@ -41,7 +42,7 @@ struct SlabCfg {
   static constexpr int BD = BT * D / 512;                // 1 KiB operand blocks per shared array
   static constexpr bool FO = MODE == SLAB_FWD || MODE == SLAB_FWDS;  // forward outputs
   static constexpr int NARR = MODE == SLAB_REC ? 2 : 3;  // shared [BT][D] arrays
-  static constexpr int MB = FO ? BT * BT / 512 : 0;      // forward: M ([BT][BT]) blocks after them
+  static constexpr int MB = MODE == SLAB_REC ? 0 : BT * BT / 512;  // M ([BT][BT]) blocks after them
   static constexpr int MOFF = NARR * BD * 1024;
   static constexpr int EOFF = MOFF + MB * 1024;          // E (fp32 [D]), then the chunk descriptor
   static constexpr int SOFF = EOFF + 1024;               // per-slab inputs
@@ -118,8 +119,9 @@ struct SlabPass {
     if constexpr (MODE == SLAB_DST) {
       // the forward's operand layouts, read back transposed (see read_phase)
       r.arr[0] = buf_rsrc(a.ws.KhT, opb);
-      r.arr[1] = buf_rsrc(a.ws.QeffT, opb);
+      r.arr[1] = buf_rsrc(a.ws.Qt, opb);
       r.arr[2] = buf_rsrc(a.ws.W, opb);
+      r.m = buf_rsrc(a.ws.Mf, items * BT * BT * 2);
       r.dO = buf_rsrc(b.dO, size_t(0x7fffffff));
     } else {
       r.arr[0] = buf_rsrc(a.ws.W, opb);
@@ -144,7 +146,7 @@ struct SlabPass {
 #pragma unroll
       for (int q = 0; q < BD; ++q) lds_load16(r.arr[ar], dst + (ar * BD + q) * 1024, vs, int(w * BT * D * 2) + q * 1024);
 #pragma unroll
-    for (int q = 0; q < C::MB; ++q) lds_load16(r.m, dst + C::MOFF + q * 1024, vo, int(w * BT * BT * 2) + q * 1024);
+    for (int q = 0; q < C::MB; ++q) lds_load16(r.m, dst + C::MOFF + q * 1024, vs, int(w * BT * BT * 2) + q * 1024);
     // E in lanes [0, D/4), the chunk descriptor (32 bytes) in the next two lanes
     constexpr int NE = D / 4;
     if (lane < NE) lds_load16(r.el, dst + C::EOFF, vo, int(w * D * 4));
@@ -177,21 +179,21 @@ struct SlabPass {
 
   // ---- compute: LDS operand phases ------------------------------------------------------
   // A chunk's products form 2-4 phases of up to 16 operand fragments each (one product:
-  // U, Q~ S, S, M U forward; Qeff^T dO, Y, W^T Y gradient).  Fragments are ordered contraction
-  // slice outer, tile inner, so consecutive matrix-core operations feed independent
+  // U, Q~ S, S, M U forward; Q~^T dO, M^T dO, K^ dS, W^T Y gradient).  Fragments are ordered
+  // contraction slice outer, tile inner, so consecutive matrix-core operations feed independent
   // accumulators; phase p+1 is read from LDS while the matrix cores work through phase p.
   static constexpr int NFT = KBD * NTT;  // token-block products (U, O, Y)
   static constexpr int NFS = KBT * NTS;  // state-tile products (S, Qeff^T dO, W^T Y)
-  static constexpr int NFQ = KBT * NTT;  // in-chunk product (M U)
+  static constexpr int NFQ = KBT * NTT;  // in-chunk products (M U, M^T dO)
   static constexpr int NFM = NFT > NFS ? NFT : NFS;
-  static constexpr int NP = MODE == SLAB_REC ? 2 : (FO ? 4 : 3);
+  static constexpr int NP = MODE == SLAB_REC ? 2 : 4;
   struct Phase {
     bf16x8 f[NFM];
     f32x4 e[NTS];
   };
   // kind of phase p: 0 token-block product, 1 state-tile product, 2 in-chunk product
   __device__ __forceinline__ static constexpr int phase_kind(int ph) {
-    if (MODE == SLAB_DST) return ph == 1 ? 0 : 1;
+    if (MODE == SLAB_DST) return ph == 1 ? 2 : (ph == 2 ? 0 : 1);
     if (MODE == SLAB_REC) return ph;
     return ph < 2 ? 0 : ph - 1;
   }
@@ -206,15 +208,16 @@ struct SlabPass {
     const char* arr;
     bool with_e;
     if constexpr (MODE == SLAB_DST) {
-      arr = p + (ph == 0 ? 1 : (ph == 1 ? 0 : 2)) * BD * 1024;  // Qeff^T, K^, W^T
+      arr = ph == 1 ? p + C::MOFF : p + (ph == 0 ? 1 : (ph == 2 ? 0 : 2)) * BD * 1024;  // Q~^T, M^T, K^, W^T
       with_e = ph == 0;
     } else {
       arr = p + (phase_kind(ph) == 2 ? C::MOFF : ph * BD * 1024);  // W, [Q~], K^^T, [M]
       with_e = phase_kind(ph) == 1;
     }
     if constexpr (MODE == SLAB_DST) {
-      // The gradient's operands are the transposes of the forward's: K^ from K^^T [D][BT], Qeff^T
-      // and -W^T from Qeff and -W [BT][D], all in the permuted fragment-major layout.  A
+      // The gradient's operands are the transposes of the forward's: K^ from K^^T [D][BT], Q~^T
+      // and -W^T from Q~ and -W [BT][D], M^T from M [BT][BT], all in the permuted fragment-major
+      // layout.  A
       // transposed fragment (rows r0 + lane % 16, contraction k0 + pf_k(lane / 16, 0..7)) is two
       // transposing reads: lane q of a 16-lane group points at 4 consecutive columns r0 + 4 (q % 4)
       // of source row k0 + 4 (lane / 16) + q / 4 (then + 16), and receives column r0 + q of the
@@ -231,6 +234,11 @@ struct SlabPass {
       if (phase_kind(ph) == 0) {
 #pragma unroll
         for (int kb = 0; kb < KBD; ++kb)
+#pragma unroll
+          for (int i = 0; i < NTT; ++i) g.f[kb * NTT + i] = tr(32 * kb + k4, 16 * i + r4, BT);
+      } else if (phase_kind(ph) == 2) {
+#pragma unroll
+        for (int kb = 0; kb < KBT; ++kb)
 #pragma unroll
           for (int i = 0; i < NTT; ++i) g.f[kb * NTT + i] = tr(32 * kb + k4, 16 * i + r4, BT);
       } else {
@@ -464,14 +472,14 @@ struct SlabPass {
         p,
         [&](int ph, const Phase& g) {
           if (ph == 0) {
-            // dS <- diag(E) dS (+ Qeff^T dO below)
+            // dS <- diag(E) dS (+ Q~^T dO below)
 #pragma unroll
             for (int t = 0; t < NTS; ++t)
 #pragma unroll
               for (int s = 0; s < NS; ++s)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) S[s][t][r] *= g.e[t][r];
-          } else if (ph == 2) {
+          } else if (ph == 3) {
 #pragma unroll
             for (int s = 0; s < NS; ++s)
 #pragma unroll
@@ -487,7 +495,15 @@ struct SlabPass {
 #pragma unroll
                 for (int s = 0; s < NS; ++s) S[s][t] = mfma_bf16(g.f[kb * NTS + t], dof[s][kb], S[s][t]);
           } else if (ph == 1) {
-            // Y = K^ dS(chunk end)
+            // Y = M^T dO
+#pragma unroll
+            for (int kb = 0; kb < KBT; ++kb)
+#pragma unroll
+              for (int i = 0; i < NTT; ++i)
+#pragma unroll
+                for (int s = 0; s < NS; ++s) Y[s][i] = mfma_bf16(g.f[kb * NTT + i], dof[s][kb], Y[s][i]);
+          } else if (ph == 2) {
+            // Y += K^ dS(chunk end)
 #pragma unroll
             for (int kb = 0; kb < KBD; ++kb)
 #pragma unroll
@@ -634,8 +650,8 @@ template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
   constexpr bool FWD = MODE == SLAB_FWD || MODE == SLAB_FWDS;
-  // (the forward's ring buffers also hold M: two of them fit)
-  constexpr int RD1 = FWD ? 2 : 3;
+  // (the forward's and the gradient's ring buffers also hold M: two of them fit)
+  constexpr int RD1 = MODE == SLAB_REC ? 3 : 2;
   const unsigned cus = persistent_grid(1u << 30);
   if (4 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 1, RD1>(d, b, s);
   if (FWD && 2 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);

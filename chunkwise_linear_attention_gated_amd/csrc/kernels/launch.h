@@ -18,13 +18,13 @@ struct ChunkWs {
   void* Qt;     // [BT][D]   Q~ = Q * e^G                          (forward)
   void* Mm;     // [BT][BT]  M = lower(gated Q K^T)
   float* El;    // [D]       e^{G_last}
-  void* QeffT;  // [D][BT]   (Q~ - M W)^T; bf16: Qeff [BT][D]      (backward)
+  void* QeffT;  // [D][BT]   (Q~ - M W)^T                          (backward, fp32 path)
   void* WT;     // [D][BT]   W^T                                   (backward, fp32 path)
   void* Kh;     // [BT][D]   K * e^{G_last - G}                    (backward, fp32 path)
   void* Tm;     // [BT][BT]  T = X diag(beta)                      (backward)
   void* Xm;     // [BT][BT]  X = (I + diag(beta) A)^{-1}           (backward)
   void* Am;     // [BT][BT]  A (strictly lower)                    (backward)
-  void* Mf;     // [BT][BT]  M, permuted fragment-major             (forward, bf16 slab passes)
+  void* Mf;     // [BT][BT]  M, permuted fragment-major             (bf16 slab passes)
 };
 
 struct KdaDims {
