@@ -562,7 +562,7 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
         hip_check(harts::launch_kda_prep(d->dims, a, keep ? 2 : 0, sp), "prep kernel launch");
       }
       if (r > 0) hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
-      started = ev.record(s0);
+      if (r + 1 < d->p.n_rounds) started = ev.record(s0);
       harts::RoundArgs a = round_args(d, io, r, ws);
       a.o = io->o;
       if (!keep) a.h = a.hc = nullptr;
@@ -672,8 +672,8 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
         hip_check(harts::launch_kda_grad(d->dims, b, s2), "gradient kernel launch");
       }
     };
-    if (keep) fork(s0, s1, ev);
-    fork(s0, s2, ev);
+    // s2 needs no fork of its own: each gradient launch waits for an event recorded on s0 after
+    // this call's first launch.  (keep: s1 runs nothing.)
     for (int r = R - 1; r >= 0; --r) {
       harts::BwdRoundArgs b = round(r);
       if (b.dslot) {
@@ -688,7 +688,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
       // after them
       if (prepped[size_t(r)]) hip_check(hipStreamWaitEvent(s0, prepped[size_t(r)], 0), "hipStreamWaitEvent");
       // round r + 1's state gradient (and everything before it on s0) is complete here
-      hipEvent_t ready = ev.record(s0);
+      hipEvent_t ready = r + 1 < R ? ev.record(s0) : nullptr;
       {
         ProfScope ps("kda_dstate", s0, units(r));
         if (slab) hip_check(harts::launch_kda_slab(d->dims, b, 2, d->p.rounds[r].max_chunks, s0), "state-gradient kernel launch");
@@ -701,16 +701,17 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
     }
     hip_check(hipStreamWaitEvent(s2, ev.record(s0), 0), "hipStreamWaitEvent");
     grads(0);
-    // join: the caller's stream continues after every round's gradients
-    hip_check(hipStreamWaitEvent(s0, ev.record(s2), 0), "hipStreamWaitEvent");
-    hip_check(hipStreamWaitEvent(s0, ev.record(s1), 0), "hipStreamWaitEvent");
+    // replayed rows' gradients into their own rows: every gradient launch is behind it on s2
     if (!d->p.fix_rows.empty()) {
-      ProfScope ps("kda_replay_fixup", s0, int64_t(d->p.replay_total) * d->dims.H);
+      ProfScope ps("kda_replay_fixup", s2, int64_t(d->p.replay_total) * d->dims.H);
       hip_check(harts::launch_replay_fixup(d->dims, d->fix_rows, d->fix_off, d->fix_idx,
                                            int32_t(d->p.fix_rows.size()), reinterpret_cast<float*>(ws + d->off_rg),
-                                           g->dk, g->dv, g->dg, g->dbeta, s0),
+                                           g->dk, g->dv, g->dg, g->dbeta, s2),
                 "replay fixup launch");
     }
+    // join: the caller's stream continues after every round's gradients (s1's last launch, the
+    // first round's recompute, precedes the first round's gradients)
+    hip_check(hipStreamWaitEvent(s0, ev.record(s2), 0), "hipStreamWaitEvent");
   });
 }
 
