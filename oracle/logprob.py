@@ -15,6 +15,9 @@ semantic position forms its own gradient g_s (onehot(y_s) - softmax(x[m(s)]))
 and the gradients of all positions that read one compact row are summed into
 that row -- a sum of independently formed terms, not a reuse count times one
 term, so positions with different labels or weights keep their own parts.
+For full-size rows both directions also come in a row-wise form that takes each
+row's log-sum-exp (softmax) once with a library routine; those forms are pinned
+to the per-position definitions.
 """
 from __future__ import annotations
 
@@ -73,6 +76,26 @@ def logprob_backward(rows_fp64: np.ndarray, row_index: np.ndarray, labels: np.nd
         g = -dlogp[s] * (e / e.sum())
         g[labels[s]] += dlogp[s]
         out[row_index[s]] += g
+    return out
+
+
+def logprob_backward_rowwise(rows_fp64, row_index: np.ndarray, labels: np.ndarray,
+                             dlogp: np.ndarray) -> np.ndarray:
+    """The same dL/dx [R, V], each row's softmax taken once by a library routine
+    (``torch.softmax`` over a float64 CPU tensor): a row's gradient is the sum over its
+    positions of g_s onehot(y_s) - g_s softmax(row), and the softmax depends on the row alone,
+    so the positions' terms sum to  (sum_s g_s) (-softmax(row))  plus each g_s at its label --
+    the per-position sum regrouped, for full-size rows where forming the softmax again for each
+    of the S positions would cost S * V exponentials.  ``rows_fp64``: float64 logits [R, V]
+    (numpy or CPU torch)."""
+    import torch
+    x = torch.as_tensor(rows_fp64, dtype=torch.float64)
+    ri = np.asarray(row_index, dtype=np.int64)
+    g = np.asarray(dlogp, dtype=np.float64)
+    weight = np.zeros(x.shape[0], dtype=np.float64)
+    np.add.at(weight, ri, g)
+    out = torch.softmax(x, dim=1).mul_(-torch.as_tensor(weight)[:, None]).numpy()
+    np.add.at(out, (ri, np.asarray(labels, dtype=np.int64)), g)
     return out
 
 

@@ -117,6 +117,26 @@ def test_backward_repeated_positions_add():
                                rtol=0, atol=1e-14)
 
 
+def test_rowwise_backward_matches_the_per_position_definition_and_autograd():
+    torch = __import__("pytest").importorskip("torch")
+    rng = np.random.default_rng(10)
+    C, V, S = 9, 53, 40
+    x = rng.standard_normal((C, V)) * 2.0
+    m = rng.integers(0, C - 2, size=S)  # the last two rows are read by no position
+    y = rng.integers(0, V, size=S)
+    y[5], m[5] = y[4], m[4]  # a repeated (row, label) pair
+    w = rng.standard_normal(S)
+    g = logprob.logprob_backward_rowwise(x, m, y, w)
+    np.testing.assert_allclose(g, logprob.logprob_backward(x, m, y, w), rtol=0, atol=1e-13)
+    assert not g[C - 2:].any()
+    xt = torch.tensor(x, requires_grad=True)
+    lp = torch.log_softmax(xt, dim=1)[torch.tensor(m), torch.tensor(y)]
+    (lp * torch.tensor(w)).sum().backward()
+    np.testing.assert_allclose(g, xt.grad.numpy(), rtol=0, atol=1e-13)
+    for c, v in [(int(m[0]), int(y[0])), (int(m[7]), 3), (0, 11)]:
+        assert abs(g[c, v] - _fd_grad(x, m, y, w, c, v)) < 1e-7
+
+
 def test_rows_of_map_is_the_stable_inverse():
     rng = np.random.default_rng(9)
     m = rng.integers(0, 7, size=40)
