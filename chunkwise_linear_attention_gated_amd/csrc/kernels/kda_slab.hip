@@ -645,7 +645,12 @@ static hipError_t slab_go(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s
 // kernels of other rounds, and packing its chains onto fewer compute units leaves them more.
 // A forward round of at most half the compute units' worth of slabs (a long root sequence)
 // runs one compute wave of two slabs per workgroup: the same chain per wave on twice the
-// compute units, each wave with its ring and LDS to itself.
+// compute units, each wave with its ring and LDS to itself.  The recompute pass of a round of
+// many sequences (more than twice the compute units' worth of slabs) runs a whole head per
+// workgroup, four compute waves of two slabs: its two shared arrays are loaded once per head
+// instead of twice, and half as many workgroups take compute units from the concurrent passes
+// (the forward and gradient modes, with four more operand arrays per chunk, lose more to LDS
+// traffic and register spills at that size than they save).
 template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
@@ -655,6 +660,9 @@ static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t
   const unsigned cus = persistent_grid(1u << 30);
   if (4 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 1, RD1>(d, b, s);
   if (FWD && 2 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);
+  if constexpr (DV == 128 && MODE == SLAB_REC) {
+    if (slabs > 2 * cus) return slab_go<MODE, BT, D, DV, 4, 2, 2>(d, b, s);
+  }
   return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
 }
 
