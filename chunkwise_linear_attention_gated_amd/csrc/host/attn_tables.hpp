@@ -21,7 +21,7 @@
 namespace harts {
 
 constexpr int kAttnQTile = 128;
-constexpr int kAttnKTile = 64;
+constexpr int kAttnKTile = 128;
 
 struct AttnTables {
   int64_t C = 0;

@@ -7,7 +7,7 @@
 //
 // A workgroup owns one tile of one head: a 128-row query tile (forward: 4 waves of
 // 32 queries, so every key/value fragment read from LDS feeds two products; dq: 8
-// waves of 16) or a 64-row key tile (dk/dv: 4 waves of 16 keys).  The gathered
+// waves of 16) or a 128-row key tile (dk/dv: 8 waves of 16 keys).  The gathered
 // operand tile (64 rows) goes through LDS with a register prefetch of the next
 // tile; products run on v_mfma_f32_16x16x32_bf16.
 //
@@ -319,8 +319,11 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dq_kernel(AttnArgs g) {
   }
 }
 
+// dk / dv over a 128-row key tile: 8 waves of 16 keys, so that each gathered query tile serves
+// 128 keys and two waves share a SIMD (the accumulators and the operands of 16 keys, and half of
+// the register prefetch of a 64-row tile, fit in 256 registers)
 template <int DQ, int DV>
-__global__ __launch_bounds__(ATHR) void attn_dkv_kernel(AttnArgs g) {
+__global__ __launch_bounds__(2 * ATHR) void attn_dkv_kernel(AttnArgs g) {
   using Cf = AttnCfg<DQ, DV>;
   __shared__ __align__(16) bf16 sQ[AT * Cf::LA];
   __shared__ __align__(16) bf16 sO[AT * Cf::LB];  // dout rows
@@ -343,8 +346,8 @@ __global__ __launch_bounds__(ATHR) void attn_dkv_kernel(AttnArgs g) {
 #pragma unroll
     for (int s = 0; s < DV / 32; ++s) vf[s] = *reinterpret_cast<const bf16x8*>(vp + 32 * s);
   }
-  const int lr = tid >> 2, lp = tid & 3;
-  RowLoad<DQ, DV, 4> ld;
+  const int lr = tid >> 3, lp = tid & 7;
+  RowLoad<DQ, DV, 8> ld;
   float xl = 0.f, xd = 0.f;
   auto issue = [&](int row) {
     ld.issue(qh, oh, ldq, ldv, row, lp);
@@ -437,7 +440,7 @@ hipError_t attn_dispatch(int which, const AttnArgs& a, int64_t n_tiles, hipStrea
   const dim3 grid(unsigned(n_tiles * a.H)), block(ATHR);
   if (which == 0) hipLaunchKernelGGL((attn_fwd_kernel<DQ, DV>), grid, block, 0, s, a);
   else if (which == 2) hipLaunchKernelGGL((attn_dq_kernel<DQ, DV>), grid, dim3(2 * ATHR), 0, s, a);
-  else hipLaunchKernelGGL((attn_dkv_kernel<DQ, DV>), grid, block, 0, s, a);
+  else hipLaunchKernelGGL((attn_dkv_kernel<DQ, DV>), grid, dim3(2 * ATHR), 0, s, a);
   return hipGetLastError();
 }
 

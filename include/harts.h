@@ -347,7 +347,7 @@ int harts_conv_bwd(const void *x, const float *weight, const int32_t *anc, const
  * Host: harts_attn_tables_build derives the paths from m (host int64 [S],
  * semantic -> compact) and the trajectory offsets (host int64 [n_traj + 1]),
  * cuts the rows into fork-free segments and those into query tiles of up to 128
- * rows and key tiles of up to 64 rows.
+ * rows and key tiles of up to 128 rows.
  * harts_attn_tables_copy fills caller arrays (sizes from harts_attn_info):
  *   qtiles  int32 [n_qtiles][4]   {row0, n, off, base}: query rows row0..row0+n-1,
  *           keys kv_list[off + v] for v < base + n; query row0 + i sees v iff v <= base + i

@@ -133,7 +133,7 @@ def _attn_check_tables(m, off, C):
             readers[int(a)].add(t)
     seen_k = np.zeros(C, np.int64)
     for row0, n, o, nq in kt:
-        assert 1 <= n <= 64
+        assert 1 <= n <= 128
         for j in range(n):
             seen_k[row0 + j] += 1
             got = list(ql[o + j:o + nq])
