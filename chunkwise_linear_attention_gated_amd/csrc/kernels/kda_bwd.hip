@@ -1271,6 +1271,7 @@ static hipError_t fixup_launch(const KdaDims& d, const int32_t* rows, const int3
   X(bf16, 64, 128, 128)          \
   X(bf16, 64, 64, 64)            \
   X(bf16, 32, 64, 64)            \
+  X(bf16, 32, 32, 32)            \
   X(float, 16, 16, 16)           \
   X(float, 32, 32, 32)
 

@@ -987,6 +987,7 @@ static hipError_t state_launch(const KdaDims& d, const RoundArgs& a, bool bwd, h
   X(bf16, 64, 128, 128)      \
   X(bf16, 64, 64, 64)        \
   X(bf16, 32, 64, 64)        \
+  X(bf16, 32, 32, 32)        \
   X(float, 16, 16, 16)       \
   X(float, 32, 32, 32)
 

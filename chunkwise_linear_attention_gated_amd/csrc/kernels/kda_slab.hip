@@ -650,7 +650,8 @@ static hipError_t slab_go(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s
 // workgroup, four compute waves of two slabs: its two shared arrays are loaded once per head
 // instead of twice, and half as many workgroups take compute units from the concurrent passes
 // (the forward and gradient modes, with four more operand arrays per chunk, lose more to LDS
-// traffic and register spills at that size than they save).
+// traffic and register spills at that size than they save).  A head of 32 value columns runs its
+// two slabs on one compute wave.
 template <int MODE, int BT, int D, int DV>
 static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t s) {
   const unsigned slabs = unsigned(b.r.nseq) * d.H * (DV / 16);
@@ -659,11 +660,15 @@ static hipError_t slab_pick(const KdaDims& d, const BwdRoundArgs& b, hipStream_t
   constexpr int RD1 = MODE == SLAB_REC ? 3 : 2;
   const unsigned cus = persistent_grid(1u << 30);
   if (4 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 1, RD1>(d, b, s);
-  if (FWD && 2 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);
-  if constexpr (DV == 128 && MODE == SLAB_REC) {
-    if (slabs > 2 * cus) return slab_go<MODE, BT, D, DV, 4, 2, 2>(d, b, s);
+  if constexpr (DV < 64) {
+    return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);  // two slabs: the whole head
+  } else {
+    if (FWD && 2 * slabs <= cus) return slab_go<MODE, BT, D, DV, 1, 2, 2>(d, b, s);
+    if constexpr (DV == 128 && MODE == SLAB_REC) {
+      if (slabs > 2 * cus) return slab_go<MODE, BT, D, DV, 4, 2, 2>(d, b, s);
+    }
+    return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
   }
-  return slab_go<MODE, BT, D, DV, 2, 2, 2>(d, b, s);
 }
 
 template <int BT, int D, int DV>
@@ -678,7 +683,8 @@ static hipError_t slab_mode(const KdaDims& d, const BwdRoundArgs& b, int mode, h
 #define HARTS_SLAB_CONFIGS(X) \
   X(64, 128, 128)             \
   X(64, 64, 64)               \
-  X(32, 64, 64)
+  X(32, 64, 64)               \
+  X(32, 32, 32)
 
 bool kda_slab_supported(const KdaDims& d) {
 #define X(B_, D_, V_) \

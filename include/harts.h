@@ -144,8 +144,9 @@ void harts_plan_free(harts_plan *plan);
  * Uploads the per-round descriptors (virtual-row gather lists, chunk and
  * sequence tables, emit targets) for heads H and key / value width dk, dv on
  * the given stream, and records the workspace size the device calls need.
- * dk, dv in {16, 32, 64, 128}; dtype HARTS_DTYPE_BF16 (dk = dv = 128 or 64) or
- * HARTS_DTYPE_FP32 (dk = dv <= 64).  The descriptor memory belongs to the
+ * dk, dv in {16, 32, 64, 128}; dtype HARTS_DTYPE_BF16 (dk = dv = 128 or 64 with
+ * chunk_B = 64; dk = dv = 64 or 32 with chunk_B = 32) or HARTS_DTYPE_FP32
+ * (dk = dv = 16 with chunk_B = 16, dk = dv = 32 with chunk_B = 32).  The descriptor memory belongs to the
  * handle (hipMalloc here, hipFree in harts_dev_plan_free).
  */
 int harts_plan_upload(const harts_plan *plan, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void *stream,

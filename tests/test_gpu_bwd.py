@@ -78,12 +78,19 @@ def test_figure_trees_backward_bf16():
         compare_tree_bwd(t, 64, 2, 128, "bf16", seed=5)
 
 
-@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64)])
+@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64), (32, 32)])
 def test_random_trees_backward_bf16(B, D):
     rng = np.random.default_rng(31 + B + D)
     for _ in range(3):
         t = trees.random_small_tree(rng, max_segments=7, max_len=3 * B, forest=True)
         compare_tree_bwd(t, B, 3, D, "bf16", seed=int(rng.integers(1000)))
+
+
+def test_narrow_heads_many_sequences_backward_bf16():
+    # d = 32 with 16 heads over a forest and a tree: two slabs of a head per wave in the serial passes
+    compare_tree_bwd(trees.forest_of_sequences([70, 33, 95, 64, 129], seed=4), 32, 16, 32, "bf16", seed=13)
+    rng = np.random.default_rng(90)
+    compare_tree_bwd(trees.random_small_tree(rng, max_segments=7, max_len=96, forest=True), 32, 16, 32, "bf16", seed=14)
 
 
 def test_random_trees_backward_fp32_b32():
@@ -131,7 +138,7 @@ def test_varlen_backward_initial_state_gradient():
     assert rel_err(dinit.cpu().numpy(), ref["dS0"]) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64)])
+@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64), (32, 32)])
 def test_kept_forward_operands_backward_bf16(B, D):
     # the forward keeps the backward's per-chunk operands and chunk-start states
     rng = np.random.default_rng(57 + B + D)

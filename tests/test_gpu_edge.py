@@ -27,7 +27,7 @@ from test_gpu_bwd import run_tree_bwd  # noqa: E402
 from test_gpu_fwd import _expanded_fwd, run_tree_fwd  # noqa: E402
 
 KINDS = ["beta0", "gneg", "overwrite", "steep3", "steep5", "mixed"]
-CONFIGS = [("fp32", 16, 16), ("fp32", 32, 32), ("bf16", 64, 128), ("bf16", 64, 64), ("bf16", 32, 64)]
+CONFIGS = [("fp32", 16, 16), ("fp32", 32, 32), ("bf16", 64, 128), ("bf16", 64, 64), ("bf16", 32, 64), ("bf16", 32, 32)]
 
 
 def _rnd(x, dt):

@@ -72,12 +72,19 @@ def test_figure_trees_bf16():
         compare_tree_fwd(t, 64, 2, 128, "bf16", seed=3)
 
 
-@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64)])
+@pytest.mark.parametrize("B,D", [(64, 128), (64, 64), (32, 64), (32, 32)])
 def test_random_trees_bf16(B, D):
     rng = np.random.default_rng(11 + B + D)
     for _ in range(3):
         t = trees.random_small_tree(rng, max_segments=7, max_len=3 * B, forest=True)
         compare_tree_fwd(t, B, 3, D, "bf16", seed=int(rng.integers(1000)))
+
+
+def test_narrow_heads_many_sequences_bf16():
+    # d = 32 with 16 heads over a forest: enough (sequence, head) pairs per round that each
+    # workgroup of the serial pass runs both 16-column slabs of a head on one wave
+    t = trees.forest_of_sequences([70, 33, 95, 64, 129], seed=4)
+    compare_tree_fwd(t, 32, 16, 32, "bf16", seed=12)
 
 
 def test_fp32_b32():
