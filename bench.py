@@ -69,7 +69,7 @@ def parse():
 
 # ------------------------------------------------------------------ algorithmic work per kernel
 # Multiply-accumulates per chunk of l tokens (replay included) and head, d = d_k = d_v, for the
-# products each kernel performs ("Kernels, data layout, rooflines").  In the
+# products each kernel performs (the WY chunk algebra the kernels' source comments state).  In the
 # recompute mode (the headline) the forward runs kda_prep_fwd + kda_state_fwd per round and the
 # backward kda_prep_bwd + kda_state_bwd (recompute) + kda_dstate + kda_grad per round.  With keep
 # the forward's preparation also produces the backward's operands (kda_prep_fwd counts both) and
