@@ -64,6 +64,10 @@ def parse():
                          "emits) to this .npz file")
     ap.add_argument("--copy-calib", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter calibration)")
+    ap.add_argument("--config", type=int, choices=range(5), default=None,
+                    help="only one workload: 0 the tiny tree (H=2, d=16, B=16, fp32, forward + backward), "
+                         "1 the flat packed call, 2 the rollout tree forward, 3 the headline step "
+                         "(as --only-kda), 4 the log-prob gather and its backward (as --only-logprob)")
     return ap.parse_args()
 
 
@@ -199,6 +203,65 @@ def device_features(N, seed, dev):
     g = (-torch.nn.functional.softplus(r(N, H, D))).to(torch.bfloat16)
     beta = torch.sigmoid(r(N, H)).to(torch.bfloat16)
     return q, k, v, g, beta
+
+
+def tree_forward_bench(args, fwd, timed, plan, C):
+    """The rollout tree's packed forward alone (C / t_fwd): every round, o and the handed-off
+    states, no backward."""
+    for _ in range(2):
+        fwd(False)
+    ms_f, _ = timed(lambda: fwd(False), args.steps)
+    ms_f /= args.steps
+    rch = round_chunks(plan)
+    fwd_flops = 0.0
+    for r in rch:
+        for l in rch[r]:
+            fwd_flops += 2 * (4 * l * l * D + 3 * l * D * D + l ** 3 / 6) * H
+    fwd_bytes = C * H * 1282 + plan.info.n_slots * H * D * D * 4
+    return {"ms": ms_f, "value": C / (ms_f / 1e3), "unit": "compact tokens/s",
+            "mfma_pct": 100 * fwd_flops / (ms_f / 1e3) / PEAK_BF16,
+            "hbm_pct_alg_bytes": 100 * fwd_bytes / (ms_f / 1e3) / PEAK_HBM}
+
+
+def tiny_bench(args):
+    """The tiny CPU-checkable tree (reading G: 4 leaves, C = 124), H=2, d=16, B=16, fp32: one
+    packed forward + backward per step.  Launch-bound at this size; reported for completeness."""
+    import torch
+    import chunkwise_linear_attention_gated_amd as harts
+    from synthetic import tensors, trees
+    t = trees.tiny_tree("G")
+    Ht, Dt, Bt = 2, 16, 16
+    feats = tensors.draw_features(t.n_nodes, Ht, Dt, Dt, seed=args.seed, dtype="fp32")
+    hp = harts.TreePlan(t.tokens, t.offsets, Bt)
+    m, _, _ = hp.maps()
+    C = hp.info.C
+    nodes = np.empty(C, np.int64)
+    nodes[m] = t.node_of_pos
+    x = {n: torch.from_numpy(np.ascontiguousarray(getattr(feats, n)[nodes])).cuda() for n in ("q", "k", "v", "g", "beta", "do")}
+    dp = harts.DevicePlan(hp, Ht, Dt, Dt, harts.DTYPE_FP32)
+    o = torch.empty((C, Ht, Dt), device="cuda")
+    slots = torch.zeros((max(1, hp.info.n_slots), Ht, Dt, Dt), device="cuda")
+    dslots = torch.zeros_like(slots)
+    gr = {n: torch.empty_like(x[n]) for n in ("q", "k", "v", "g", "beta")}
+    ws = torch.empty(dp.workspace_size(True), dtype=torch.uint8, device="cuda")
+
+    def step():
+        harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o, states=slots, workspace=ws)
+        harts.kda_bwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], x["do"], gr["q"], gr["k"], gr["v"], gr["g"],
+                      gr["beta"], states=slots, dstates=dslots, workspace=ws)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    return {"ms_per_step": ms, "value": C / (ms / 1e3), "unit": "compact tokens/s", "C": C, "S": hp.info.S,
+            "n_rounds": hp.info.n_rounds, "H": Ht, "d": Dt, "B": Bt, "dtype": "fp32"}
 
 
 def flat_bench(args, out):
@@ -472,6 +535,18 @@ def main():
         print(json.dumps({"copy_calib_bytes": n}))
         return
 
+    if args.config == 3:
+        args.only_kda = True
+    if args.config == 4:
+        args.only_logprob = True
+    if args.config == 0:
+        print(json.dumps({"tiny_tree": tiny_bench(args)}))
+        return
+    if args.config == 1:
+        out = {}
+        flat_bench(args, out)
+        print(json.dumps(out))
+        return
     if args.only_logprob:
         out = {}
         logprob_bench(args, out)
@@ -544,6 +619,9 @@ def main():
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1), time.perf_counter() - w0
 
+    if args.config == 2:
+        print(json.dumps({"tree_forward": tree_forward_bench(args, fwd, timed, plan, C)}))
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -616,17 +694,7 @@ def main():
                     "kernels": keep_kernels}
 
     # ---------------------------------------------------------------- tree forward alone (C / t_fwd)
-    for _ in range(2):
-        fwd(False)
-    ms_f, _ = timed(lambda: fwd(False), args.steps)
-    ms_f /= args.steps
-    fwd_flops = 0.0
-    for l in all_chunks:
-        fwd_flops += 2 * (4 * l * l * D + 3 * l * D * D + l ** 3 / 6) * H
-    fwd_bytes = C * H * 1282 + slot_bytes
-    tree_forward = {"ms": ms_f, "value": C / (ms_f / 1e3), "unit": "compact tokens/s",
-                    "mfma_pct": 100 * fwd_flops / (ms_f / 1e3) / PEAK_BF16,
-                    "hbm_pct_alg_bytes": 100 * fwd_bytes / (ms_f / 1e3) / PEAK_HBM}
+    tree_forward = tree_forward_bench(args, fwd, timed, plan, C)
 
     out = {
         "metric": "compact tokens/s, tree-packed chunkwise gated-delta fwd+bwd; MFMA % of peak",
