@@ -57,6 +57,17 @@ class KdaGrad(ctypes.Structure):
     _fields_ = [("dO", P), ("dq", P), ("dk", P), ("dv", P), ("dg", P), ("dbeta", P), ("dstates", P), ("dinit", P)]
 
 
+class RoundView(ctypes.Structure):
+    _fields_ = [("n_seq", I32), ("row_start", P), ("row_end", P), ("abs_start", P), ("replay_off", P),
+                ("replay_rows", P), ("init_slot", P), ("emit_off", P), ("emit_chunk", P), ("emit_slot", P)]
+
+
+class VarlenArgs(ctypes.Structure):
+    _fields_ = [("q", P), ("k", P), ("v", P), ("g", P), ("beta", P), ("cu_seqlens", P), ("n_seq", I64),
+                ("init_states", P), ("init_mask", P), ("o", P), ("boundary_states", P), ("boundary_offsets", P),
+                ("final_states", P), ("H", I32), ("dk", I32), ("dv", I32), ("chunk_B", I32), ("dtype", I32)]
+
+
 class ProfileEntry(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 40), ("launches", I64), ("total_ms", ctypes.c_double), ("units", I64)]
 
@@ -79,13 +90,16 @@ _plan_sequences = _sig("harts_plan_sequences", I32, P, P)
 _plan_replay_rows = _sig("harts_plan_replay_rows", I32, P, P)
 _plan_emits = _sig("harts_plan_emits", I32, P, P, P)
 _plan_boundary_offsets = _sig("harts_plan_boundary_offsets", I32, P, P)
+_plan_round = _sig("harts_plan_round", I32, P, I32, ctypes.POINTER(RoundView))
 _plan_free = _sig("harts_plan_free", None, P)
 _plan_upload = _sig("harts_plan_upload", I32, P, I32, I32, I32, I32, P, ctypes.POINTER(P))
 _ws_size = _sig("harts_kda_workspace_size", I32, P, I32, ctypes.POINTER(ctypes.c_size_t))
 _dev_free = _sig("harts_dev_plan_free", None, P)
 _kda_fwd = _sig("harts_kda_fwd", I32, P, ctypes.POINTER(KdaIO), P)
 _kda_bwd = _sig("harts_kda_bwd", I32, P, ctypes.POINTER(KdaIO), ctypes.POINTER(KdaGrad), P)
+_kda_fwd_varlen = _sig("harts_kda_fwd_varlen", I32, ctypes.POINTER(VarlenArgs), P)
 _lp_ws = _sig("harts_logprob_workspace_size", ctypes.c_size_t, I64)
+_lp_ws2 = _sig("harts_logprob_workspace", ctypes.c_size_t, I64, I64)
 _lp = _sig("harts_logprob_gather", I32, P, I64, I64, I32, P, P, I64, P, P, P, P, ctypes.c_size_t, P)
 _lp_na = _sig("harts_logprob_gather_noalloc", I32, P, I64, I64, I32, P, P, I64, P, P, P)
 _lpb = _sig("harts_logprob_backward", I32, P, I64, I64, I32, P, P, P, P, P, I64, P, P)
@@ -182,6 +196,29 @@ class _PlanBase:
         _check(_plan_emits(self._h, b.ctypes.data, t.ctypes.data))
         return b, t
 
+    def round(self, r: int) -> dict:
+        """harts_plan_round: the sequences of round r (0-based) as numpy copies of the
+        plan-owned arrays."""
+        rv = RoundView()
+        _check(_plan_round(self._h, r, ctypes.byref(rv)))
+        n = rv.n_seq
+
+        def arr(ptr, count, ctype, dtype):
+            if count == 0:
+                return np.empty(0, dtype)
+            return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ctype)), (count,)).astype(dtype)
+
+        out = {"n_seq": n}
+        for f in ("row_start", "row_end", "abs_start"):
+            out[f] = arr(getattr(rv, f), n, I64, np.int64)
+        out["init_slot"] = arr(rv.init_slot, n, I32, np.int32)
+        out["replay_off"] = arr(rv.replay_off, n + 1, I64, np.int64)
+        out["emit_off"] = arr(rv.emit_off, n + 1, I64, np.int64)
+        out["replay_rows"] = arr(rv.replay_rows, int(out["replay_off"][-1]), I64, np.int64)
+        out["emit_chunk"] = arr(rv.emit_chunk, int(out["emit_off"][-1]), I32, np.int32)
+        out["emit_slot"] = arr(rv.emit_slot, int(out["emit_off"][-1]), I32, np.int32)
+        return out
+
     def __del__(self):
         if self._h:
             _plan_free(self._h)
@@ -267,6 +304,30 @@ def kda_fwd(dplan: DevicePlan, q, k, v, g, beta, o, states=None, init_states=Non
     _check(_kda_fwd(dplan._h, ctypes.byref(io), _stream(stream)))
 
 
+def kda_fwd_varlen(q, k, v, g, beta, cu_seqlens, o, chunk_B: int, init_states=None, init_mask=None,
+                   boundary_states=None, final_states=None, stream=None):
+    """harts_kda_fwd_varlen: the flat packed call in one function (plans, uploads, allocates its
+    workspace, runs and waits).  q, k, g, o [N, H, dk or dv]; beta [N, H]; cu_seqlens host [n_seq + 1].
+    Returns the boundary offsets [n_seq + 1] when boundary_states is given, else None."""
+    import torch
+    cu = _np(cu_seqlens, np.int64)
+    n = len(cu) - 1
+    if q.dim() != 3 or v.dim() != 3:
+        raise HartsError(-1, "q and v must be [N, H, d]")
+    N, H, dk = q.shape
+    dv = v.shape[2]
+    dtype = DTYPE_BF16 if q.dtype == torch.bfloat16 else DTYPE_FP32
+    mask = None if init_mask is None else _np(init_mask, np.uint8)
+    if mask is not None and len(mask) != n:
+        raise HartsError(-1, "init_mask must have n_seq entries")
+    offs = np.empty(n + 1, np.int64) if boundary_states is not None else None
+    a = VarlenArgs(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), cu.ctypes.data, n, _ptr(init_states),
+                   None if mask is None else mask.ctypes.data, _ptr(o), _ptr(boundary_states),
+                   None if offs is None else offs.ctypes.data, _ptr(final_states), H, dk, dv, chunk_B, dtype)
+    _check(_kda_fwd_varlen(ctypes.byref(a), _stream(stream)))
+    return offs
+
+
 def kda_bwd(dplan: DevicePlan, q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta, states=None, init_states=None,
             dstates=None, dinit=None, workspace=None, stream=None, keep=False):
     """harts_kda_bwd over every round of the plan, in reverse (keep: read what
@@ -278,6 +339,11 @@ def kda_bwd(dplan: DevicePlan, q, k, v, g, beta, dO, dq, dk, dv, dg, dbeta, stat
 
 def logprob_workspace_size(C: int) -> int:
     return int(_lp_ws(C))
+
+
+def logprob_workspace(C: int, S: int) -> int:
+    """harts_logprob_workspace: workspace bytes for C compact rows and S semantic positions."""
+    return int(_lp_ws2(C, S))
 
 
 def logprob_gather(logits, m, labels, logp, q=None, lse=None, workspace=None, stream=None):

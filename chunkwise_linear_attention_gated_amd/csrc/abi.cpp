@@ -27,6 +27,13 @@ struct harts_tree {
 };
 struct harts_plan {
   harts::PlanHost p;
+  // per-round host views (harts_plan_round), built on first use
+  struct RoundStore {
+    std::vector<int64_t> row_start, row_end, abs_start, replay_off, replay_rows, emit_off;
+    std::vector<int32_t> init_slot, emit_chunk, emit_slot;
+  };
+  mutable std::mutex views_mu;
+  mutable std::vector<RoundStore> views;
 };
 struct harts_dev_plan {
   harts::PlanHost p;
@@ -395,6 +402,48 @@ int harts_plan_boundary_offsets(const harts_plan* plan, int64_t* offsets) {
   });
 }
 
+int harts_plan_round(const harts_plan* plan, int32_t r, harts_round_view* out) {
+  return guarded([&] {
+    if (!plan || !out) throw Error(HARTS_EINVAL, "plan and out must be non-NULL");
+    if (r < 0 || r >= plan->p.n_rounds)
+      throw Error(HARTS_EINVAL, "round " + std::to_string(r) + " outside [0, " + std::to_string(plan->p.n_rounds) + ")");
+    std::lock_guard<std::mutex> lk(plan->views_mu);
+    if (plan->views.empty()) {
+      std::vector<harts_plan::RoundStore> v(size_t(plan->p.n_rounds));
+      for (auto& st : v) {
+        st.replay_off.push_back(0);
+        st.emit_off.push_back(0);
+      }
+      for (const harts::SeqHost& q : plan->p.seqs) {
+        harts_plan::RoundStore& st = v[size_t(q.round - 1)];
+        st.row_start.push_back(q.row_begin);
+        st.row_end.push_back(q.row_end);
+        st.abs_start.push_back(q.start);
+        st.init_slot.push_back(q.init);
+        for (int32_t i = 0; i < q.n_replay; ++i) st.replay_rows.push_back(plan->p.replay_rows[size_t(q.replay_off + i)]);
+        st.replay_off.push_back(int64_t(st.replay_rows.size()));
+        for (int32_t i = 0; i < q.n_emits; ++i) {
+          st.emit_chunk.push_back(plan->p.emit_boundary[size_t(q.emit_off + i)]);
+          st.emit_slot.push_back(plan->p.emit_target[size_t(q.emit_off + i)]);
+        }
+        st.emit_off.push_back(int64_t(st.emit_chunk.size()));
+      }
+      plan->views = std::move(v);
+    }
+    const harts_plan::RoundStore& st = plan->views[size_t(r)];
+    out->n_seq = int32_t(st.row_start.size());
+    out->row_start = st.row_start.data();
+    out->row_end = st.row_end.data();
+    out->abs_start = st.abs_start.data();
+    out->replay_off = st.replay_off.data();
+    out->replay_rows = st.replay_rows.data();
+    out->init_slot = st.init_slot.data();
+    out->emit_off = st.emit_off.data();
+    out->emit_chunk = st.emit_chunk.data();
+    out->emit_slot = st.emit_slot.data();
+  });
+}
+
 void harts_plan_free(harts_plan* plan) { delete plan; }
 
 int harts_plan_upload(const harts_plan* plan, int32_t H, int32_t dk, int32_t dv, int32_t dtype, void* stream,
@@ -580,6 +629,56 @@ int harts_kda_fwd(const harts_dev_plan* d, const harts_kda_io* io, void* stream)
   });
 }
 
+int harts_kda_fwd_varlen(const harts_varlen_args* a, void* stream) {
+  harts_plan* plan = nullptr;
+  harts_dev_plan* dp = nullptr;
+  void* ws = nullptr;
+  const int rc = guarded([&] {
+    if (!a) throw Error(HARTS_EINVAL, "args is NULL");
+    if (!a->cu_seqlens || a->n_seq < 1) throw Error(HARTS_EINVAL, "cu_seqlens and n_seq >= 1 are required");
+    std::vector<uint8_t> mask;
+    const uint8_t* has_init = nullptr;
+    if (a->init_states) {
+      mask.assign(size_t(a->n_seq), 1);
+      if (a->init_mask) std::copy(a->init_mask, a->init_mask + a->n_seq, mask.begin());
+      has_init = mask.data();
+    }
+    int e = harts_plan_create_varlen(a->cu_seqlens, a->n_seq, a->chunk_B, has_init, a->boundary_states ? 1 : 0, &plan);
+    if (e != HARTS_OK) throw Error(e, g_err);
+    e = harts_plan_upload(plan, a->H, a->dk, a->dv, a->dtype, stream, &dp);
+    if (e != HARTS_OK) throw Error(e, g_err);
+    if (a->boundary_states && a->boundary_offsets) {
+      e = harts_plan_boundary_offsets(plan, a->boundary_offsets);
+      if (e != HARTS_OK) throw Error(e, g_err);
+    }
+    size_t bytes = 0;
+    e = harts_kda_workspace_size(dp, 0, &bytes);
+    if (e != HARTS_OK) throw Error(e, g_err);
+    hip_check(hipMalloc(&ws, bytes), "hipMalloc (workspace)");
+    harts_kda_io io{};
+    io.q = a->q;
+    io.k = a->k;
+    io.v = a->v;
+    io.g = a->g;
+    io.beta = a->beta;
+    io.o = a->o;
+    io.states = a->boundary_states;
+    io.init_states = a->init_states;
+    io.final_states = a->final_states;
+    io.workspace = ws;
+    io.workspace_bytes = bytes;
+    e = harts_kda_fwd(dp, &io, stream);
+    if (e != HARTS_OK) throw Error(e, g_err);
+    hip_check(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+  });
+  // every path waits for the stream before the plan's descriptors and the workspace are freed
+  if (rc != HARTS_OK && (dp || ws)) (void)hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (ws) (void)hipFree(ws);
+  harts_dev_plan_free(dp);
+  harts_plan_free(plan);
+  return rc;
+}
+
 int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_kda_grad* g, void* stream) {
   return guarded([&] {
     if (!d) throw Error(HARTS_EINVAL, "dplan is NULL");
@@ -716,6 +815,7 @@ int harts_kda_bwd(const harts_dev_plan* d, const harts_kda_io* io, const harts_k
 }
 
 size_t harts_logprob_workspace_size(int64_t C) { return C > 0 ? align256(size_t(C) * 4) : 256; }
+size_t harts_logprob_workspace(int64_t C, int64_t) { return harts_logprob_workspace_size(C); }
 
 int harts_logprob_gather(const void* logits, int64_t C, int64_t V, int32_t dtype, const int64_t* m,
                          const int32_t* labels, int64_t S, float* logp_out, int32_t* q_out, float* lse_out,

@@ -138,6 +138,27 @@ int harts_plan_emits(const harts_plan *plan, int32_t *boundary, int32_t *target)
 /* Varlen plans with emit_boundaries: host int64 [n_seq + 1]. */
 int harts_plan_boundary_offsets(const harts_plan *plan, int64_t *offsets);
 
+/*
+ * Host view of one round (one packed call) [blog 4.2, 4.3]: its sequences in launch order, with
+ * their own compact rows, the absolute position their virtual stream starts at, the rows they
+ * replay, their initial state and the states they emit.  r is 0-based (< n_rounds, else
+ * HARTS_EINVAL).  The arrays belong to the plan and stay valid until harts_plan_free; the call
+ * is thread-safe.
+ */
+typedef struct {
+  int32_t n_seq;
+  const int64_t *row_start, *row_end; /* own compact rows [row_start[i], row_end[i]) */
+  const int64_t *abs_start;           /* absolute position of the first (replayed or own) token */
+  const int64_t *replay_off;          /* [n_seq + 1]: sequence i replays replay_rows[replay_off[i] ..) */
+  const int64_t *replay_rows;         /* compact rows replayed, per sequence in path order */
+  const int32_t *init_slot;           /* slot (trees) or init-state index (varlen) of the initial state, -1 = zero */
+  const int64_t *emit_off;            /* [n_seq + 1] into emit_chunk and emit_slot */
+  const int32_t *emit_chunk;          /* local chunk boundary (>= 1) after which a state is emitted */
+  const int32_t *emit_slot;           /* its target: slot id (trees) or boundary-state index (varlen) */
+} harts_round_view;
+
+int harts_plan_round(const harts_plan *plan, int32_t r, harts_round_view *out);
+
 void harts_plan_free(harts_plan *plan);
 
 /* ---------------------------------------------------------------- device plan
@@ -200,6 +221,34 @@ typedef struct {
 
 int harts_kda_fwd(const harts_dev_plan *dplan, const harts_kda_io *io, void *stream);
 
+/*
+ * The flat packed call in one function [blog 1.2, 4.3]: independent sequences (no tree, no
+ * replay) given by host cu_seqlens [n_seq + 1], one round, from the zero state or from
+ * init_states[i] where init_mask[i] != 0 (init_mask host uint8 [n_seq], or NULL: every sequence
+ * with init_states != NULL starts from it), writing o and, when boundary_states != NULL, the state
+ * after every multiple of chunk_B inside each sequence (sum_i floor(L_i / chunk_B) states,
+ * sequence-major, chunk order; boundary_offsets, host int64 [n_seq + 1] or NULL, receives where
+ * each sequence's states start) and, when final_states != NULL, every final state.  Device
+ * tensors as for harts_kda_fwd (N = cu_seqlens[n_seq]).  For one-off calls: it builds and uploads
+ * its plan, allocates its workspace with hipMalloc, enqueues the forward on stream, waits for the
+ * stream and frees both; repeated calls on the same lengths should create the plan once
+ * (harts_plan_create_varlen, harts_plan_upload) and call harts_kda_fwd.
+ */
+typedef struct {
+  const void *q, *k, *v, *g, *beta;
+  const int64_t *cu_seqlens;
+  int64_t n_seq;
+  const float *init_states;
+  const uint8_t *init_mask;
+  void *o;
+  float *boundary_states;
+  int64_t *boundary_offsets;
+  float *final_states;
+  int32_t H, dk, dv, chunk_B, dtype;
+} harts_varlen_args;
+
+int harts_kda_fwd_varlen(const harts_varlen_args *args, void *stream);
+
 /* ---------------------------------------------------------------- gated-delta backward
  * [blog 4.3] differentiable handoff: initial-state gradients accumulate back
  * into the call that produced the boundary; [plsum 4] recomputation under the
@@ -242,6 +291,9 @@ int harts_kda_bwd(const harts_dev_plan *dplan, const harts_kda_io *io, const har
  * host copies of m and labels beforehand).
  */
 size_t harts_logprob_workspace_size(int64_t C);
+/* The same size for C compact rows and S semantic positions (the gather's workspace depends on C
+ * alone). */
+size_t harts_logprob_workspace(int64_t C, int64_t S);
 int harts_logprob_gather(const void *logits, int64_t C, int64_t V, int32_t dtype, const int64_t *m,
                          const int32_t *labels, int64_t S, float *logp_out, int32_t *q_out, float *lse_out,
                          void *workspace, size_t workspace_bytes, void *stream);

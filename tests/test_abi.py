@@ -67,6 +67,25 @@ def test_logprob_rows_is_the_stable_inverse_of_m():
     assert e.value.code == -1 and "outside" in str(e.value)
 
 
+def test_logprob_workspace_takes_compact_and_semantic_sizes():
+    for C, S in [(0, 0), (1, 5), (4097, 100000)]:
+        assert harts.logprob_workspace(C, S) == harts.logprob_workspace_size(C)
+    assert harts.logprob_workspace(4097, 1) % 256 == 0 and harts.logprob_workspace(4097, 1) >= 4097 * 4
+
+
+def test_kda_fwd_varlen_rejects_bad_arguments_before_any_device_work():
+    f = _lib._kda_fwd_varlen
+    assert f(None, None) == -1
+    a = _lib.VarlenArgs()
+    assert f(ctypes.byref(a), None) == -1 and b"cu_seqlens" in _lib._last_error()
+    cu = np.array([0, 5, 3], np.int64)
+    a.cu_seqlens, a.n_seq, a.H, a.dk, a.dv, a.chunk_B = cu.ctypes.data, 2, 2, 128, 128, 64
+    assert f(ctypes.byref(a), None) == -1  # decreasing cu_seqlens: the plan is refused
+    cu2 = np.array([0, 5, 9], np.int64)
+    a.cu_seqlens, a.dk, a.dv = cu2.ctypes.data, 48, 48
+    assert f(ctypes.byref(a), None) == -1 and b"unsupported" in _lib._last_error()
+
+
 def test_logprob_map_check_names_the_first_position_out_of_range():
     m = np.array([0, 2, 1, 2], np.int64)
     lab = np.array([5, 0, 9, 3], np.int32)

@@ -219,3 +219,56 @@ def test_varlen_small_bf16():
             assert rel_err(got, ref) <= TOL["bf16"]
         assert rel_err(r["fin"][i], st[k + nb]) <= TOL["bf16"]
         k += nb + 1
+
+
+@pytest.mark.parametrize("dt,B,D,mask", [("bf16", 64, 128, "alternate"), ("bf16", 32, 64, "all"),
+                                         ("fp32", 16, 16, "none")])
+def test_kda_fwd_varlen_one_call_equals_the_planned_call(dt, B, D, mask):
+    """harts_kda_fwd_varlen (plan, upload, workspace and forward in one call) writes the same
+    bytes as harts_plan_create_varlen + harts_plan_upload + harts_kda_fwd, and both match the
+    oracle."""
+    lens = np.array([3 * B + 5, B, 1, 2 * B, 7])
+    H, n = 2, len(lens)
+    r = _varlen_case(lens, H, D, B, dt, seed=5)
+    cu, init = r["cu"], r["init"]
+    feats = r["feats"]
+    x = device_inputs(feats, np.arange(cu[-1]))
+    init_t = torch.from_numpy(init).cuda()
+    if mask == "alternate":
+        init_mask, has = r["has"], r["has"]
+    elif mask == "all":
+        init_mask, has = None, np.ones(n, np.uint8)
+    else:
+        init_mask, has, init_t = None, np.zeros(n, np.uint8), None
+    vp = harts.VarlenPlan(cu, B, has_init=has if init_t is not None else None, emit_boundaries=True)
+    dp = harts.DevicePlan(vp, H, D, D, harts_dtype(dt))
+    N, nb = int(cu[-1]), vp.info.n_boundaries
+
+    def bufs():
+        return (torch.full((N, H, D), float("nan"), dtype=torch_dtype(dt), device="cuda"),
+                torch.full((nb, H, D, D), float("nan"), dtype=torch.float32, device="cuda"),
+                torch.full((n, H, D, D), float("nan"), dtype=torch.float32, device="cuda"))
+
+    o1, b1, f1 = bufs()
+    ws = torch.empty(dp.workspace_size(False), dtype=torch.uint8, device="cuda")
+    harts.kda_fwd(dp, x["q"], x["k"], x["v"], x["g"], x["beta"], o1, states=b1, init_states=init_t,
+                  final_states=f1, workspace=ws)
+    o2, b2, f2 = bufs()
+    offs = harts.kda_fwd_varlen(x["q"], x["k"], x["v"], x["g"], x["beta"], cu, o2, B, init_states=init_t,
+                                init_mask=init_mask, boundary_states=b2, final_states=f2)
+    torch.cuda.synchronize()
+    assert np.array_equal(offs, vp.boundary_offsets())
+    for a, b in ((o1, o2), (b1, b2), (f1, f2)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    # the one-call result against the oracle
+    which = list(range(n))
+    r2 = dict(r, has=has)
+    o_ref, st = _varlen_oracle(r2, which, B)
+    assert rel_err(o2.float().cpu().numpy(), o_ref) <= TOL[dt]
+    k = 0
+    for i in which:
+        m = int(lens[i]) // B
+        if m:
+            assert rel_err(b2[offs[i]:offs[i] + m].cpu().numpy(), st[k:k + m]) <= TOL[dt]
+        assert rel_err(f2[i].cpu().numpy(), st[k + m]) <= TOL[dt]
+        k += m + 1

@@ -30,9 +30,29 @@ def _compare(t, B):
         em = list(zip(eb[s["emit_off"]:s["emit_off"] + s["n_emits"]].tolist(),
                       et[s["emit_off"]:s["emit_off"] + s["n_emits"]].tolist()))
         assert em == o.emits
+    _compare_rounds(hp, op)
     st = hp.tree_stats()
     assert st["n_segments"] == len(op.segments.nodes)
     return op
+
+
+def _compare_rounds(hp, op):
+    """harts_plan_round: round r's sequences, in plan order, with their replay rows and emits."""
+    for r in range(op.n_rounds):
+        rv = hp.round(r)
+        mine = [o for o in op.seqs if o.round == r + 1]
+        assert rv["n_seq"] == len(mine)
+        for i, o in enumerate(mine):
+            assert (rv["row_start"][i], rv["row_end"][i]) == (o.own_rows[0], o.own_rows[-1] + 1)
+            assert rv["abs_start"][i] == o.start and rv["init_slot"][i] == o.init_slot
+            a, b = rv["replay_off"][i:i + 2]
+            assert list(rv["replay_rows"][a:b]) == o.replay_rows
+            a, b = rv["emit_off"][i:i + 2]
+            assert list(zip(rv["emit_chunk"][a:b].tolist(), rv["emit_slot"][a:b].tolist())) == o.emits
+    for bad in (-1, op.n_rounds):
+        with pytest.raises(harts.HartsError) as e:
+            hp.round(bad)
+        assert e.value.code == -1 and "outside" in str(e.value)
 
 
 @pytest.mark.parametrize("B", [16, 32, 64])
@@ -89,3 +109,7 @@ def test_varlen_plan():
     assert [s["init_slot"] for s in seqs] == [i if has[i] else -1 for i in range(32)]
     m, q, n2r = vp.maps()
     assert np.array_equal(m, np.arange(cu[-1])) and (q == 1).all()
+    rv = vp.round(0)
+    assert rv["n_seq"] == 32 and np.array_equal(rv["row_start"], cu[:-1]) and np.array_equal(rv["row_end"], cu[1:])
+    assert np.array_equal(rv["abs_start"], np.zeros(32)) and len(rv["replay_rows"]) == 0
+    assert np.array_equal(np.diff(rv["emit_off"]), lens // 64)
