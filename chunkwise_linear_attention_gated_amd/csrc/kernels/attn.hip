@@ -133,11 +133,15 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
     for (int s = 0; s < DQ / 32; ++s) qf[n][s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
   }
-  const int lr = tid >> 2, lp = tid & 3;
-  RowLoad<DQ, DV, 4> ld;
-  ld.issue(kh, vh, ldq, ldv, lr < nkv ? lst[lr] : -1, lp);
-  int nxt = AT + lr < nkv ? lst[AT + lr] : -1;
-  ld.put(sK, sV, lr, lp);
+  // rows lr and lr + 32 of each gathered tile, 8 threads per row: every 8-lane group of a tile
+  // store writes 128 contiguous bytes of one row (4 threads per row measured LDS bank conflicts)
+  const int lr = tid >> 3, lp = tid & 7;
+  RowLoad<DQ, DV, 8> ld0, ld1;
+  ld0.issue(kh, vh, ldq, ldv, lr < nkv ? lst[lr] : -1, lp);
+  ld1.issue(kh, vh, ldq, ldv, lr + 32 < nkv ? lst[lr + 32] : -1, lp);
+  int nxt0 = AT + lr < nkv ? lst[AT + lr] : -1, nxt1 = AT + 32 + lr < nkv ? lst[AT + 32 + lr] : -1;
+  ld0.put(sK, sV, lr, lp);
+  ld1.put(sK, sV, lr + 32, lp);
   __syncthreads();
 
   const float c = g.scale * kLog2e;
@@ -149,9 +153,11 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     for (int d = 0; d < DV / 16; ++d) acc[n][d] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < nt; ++j) {
     if (j + 1 < nt) {
-      ld.issue(kh, vh, ldq, ldv, nxt, lp);
+      ld0.issue(kh, vh, ldq, ldv, nxt0, lp);
+      ld1.issue(kh, vh, ldq, ldv, nxt1, lp);
       const int u = (j + 2) * AT + lr;
-      nxt = u < nkv ? lst[u] : -1;
+      nxt0 = u < nkv ? lst[u] : -1;
+      nxt1 = u + 32 < nkv ? lst[u + 32] : -1;
     }
     f32x4 sc[2][4];
 #pragma unroll
@@ -208,7 +214,8 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     }
     if (j + 1 < nt) {
       __syncthreads();
-      ld.put(sK, sV, lr, lp);
+      ld0.put(sK, sV, lr, lp);
+      ld1.put(sK, sV, lr + 32, lp);
       __syncthreads();
     }
   }
