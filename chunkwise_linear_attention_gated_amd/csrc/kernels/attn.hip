@@ -115,7 +115,7 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
   const int4 T = reinterpret_cast<const int4*>(g.tiles)[tile];
   const int row0 = T.x, nr = T.y, base = T.w, nkv = base + nr, nt = (nkv + AT - 1) / AT;
   const int32_t* lst = g.list + T.z;
-  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // the wave's two query halves: qi[n] = 32 w + 16 n + l % 16
   int qi[2], qrow[2];
 #pragma unroll
@@ -177,11 +177,19 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
     for (int n = 0; n < 2; ++n) {
       const int lim = base + qi[n] - j * AT;  // keys of this tile with index <= lim are visible
       float mx = -INFINITY;
+      // hidden keys to -inf, only where the tile is not wholly visible to the half's first query
+      // (so to all of its queries)
+      if (base + 32 * wv + 16 * n - j * AT < AT - 1) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[n][kb][i] = 16 * kb + 4 * gq + i <= lim ? sc[n][kb][i] : -INFINITY;
+      }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x = 16 * kb + 4 * gq + i <= lim ? sc[n][kb][i] * c : -INFINITY;
+          const float x = sc[n][kb][i] * c;
           sc[n][kb][i] = x;
           mx = fmaxf(mx, x);
         }
@@ -262,6 +270,7 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dq_kernel(AttnArgs g) {
   const int row0 = T.x, nr = T.y, base = T.w, nkv = base + nr, nt = (nkv + AT - 1) / AT;
   const int32_t* lst = g.list + T.z;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, qi = 16 * (tid >> 6) + (lane & 15);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qrow = row0 + min(qi, nr - 1);
   const int64_t ldq = int64_t(H) * DQ, ldv = int64_t(H) * DV;
   const bf16* kh = g.k + h * DQ;
@@ -303,13 +312,18 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dq_kernel(AttnArgs g) {
       dp[kb] = a;
     }
     const int lim = base + qi - j * AT;
+    // hidden keys to -inf (probability 0), only where the tile is not wholly visible to the
+    // wave's first query
+    if (base + 16 * wv - j * AT < AT - 1) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[kb][i] = 16 * kb + 4 * gq + i <= lim ? sc[kb][i] : -INFINITY;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = 16 * kb + 4 * gq + i <= lim ? exp2_hw(sc[kb][i] * c - lse2) : 0.f;
-        sc[kb][i] = p * (dp[kb][i] - dlt);
-      }
+      for (int i = 0; i < 4; ++i) sc[kb][i] = exp2_hw(sc[kb][i] * c - lse2) * (dp[kb][i] - dlt);
     const bf16x8 s0 = pf_pair(sc[0], sc[1]), s1 = pf_pair(sc[2], sc[3]);
 #pragma unroll
     for (int d = 0; d < DQ / 16; ++d) {
@@ -345,6 +359,7 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dkv_kernel(AttnArgs g) {
   const int row0 = T.x, nk = T.y, nq = T.w, nt = (nq + AT - 1) / AT;
   const int32_t* lst = g.list + T.z;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, kk = 16 * (tid >> 6) + (lane & 15);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int krow = row0 + min(kk, nk - 1);
   const int64_t ldq = int64_t(H) * DQ, ldv = int64_t(H) * DV;
   const bf16* qh = g.q + h * DQ;
@@ -393,6 +408,8 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dkv_kernel(AttnArgs g) {
       nxt = u < nq ? lst[u] : -1;
     }
     f32x4 sp[4], sd[4];
+    // every query of the tile sees every key of the wave: below the wave's last key, inside nq
+    const bool open = j * AT >= 16 * wv + 15 && (j + 1) * AT <= nq;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
@@ -402,10 +419,16 @@ __global__ __launch_bounds__(2 * ATHR) void attn_dkv_kernel(AttnArgs g) {
       for (int s = 0; s < DV / 32; ++s) b = Mma<bf16>::mma(Mma<bf16>::kc(sO, Cf::LB, 16 * qb, 32 * s, lane), vf[s], b);
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(sL + 16 * qb + 4 * gq);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(sD + 16 * qb + 4 * gq);
+      if (!open) {  // hidden pairs to -inf (probability 0)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int u = j * AT + 16 * qb + 4 * gq + i;
+          a[i] = (u >= kk && u < nq) ? a[i] : -INFINITY;
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int u = j * AT + 16 * qb + 4 * gq + i;
-        const float p = (u >= kk && u < nq) ? exp2_hw(a[i] * c - l4[i]) : 0.f;
+        const float p = exp2_hw(a[i] * c - l4[i]);
         sp[qb][i] = p;
         sd[qb][i] = p * (b[i] - d4[i]);
       }
