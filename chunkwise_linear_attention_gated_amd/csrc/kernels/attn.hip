@@ -188,26 +188,31 @@ __global__ __launch_bounds__(ATHR) __attribute__((amdgpu_waves_per_eu(2))) void 
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = sc[n][kb][i] * c;
-          sc[n][kb][i] = x;
-          mx = fmaxf(mx, x);
-        }
-      const float mnew = fmaxf(mrun[n], wave_quad_max(mx));
-      const float alpha = exp2_hw(mrun[n] - mnew);
-      mrun[n] = mnew;
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[n][kb][i]);
+      mx = wave_quad_max(mx) * c;  // the scale is positive: the maximum of the scaled scores
+      // The reference m of the exponentials moves only when some query's maximum passes it by
+      // more than 8 (base 2): otherwise the probabilities stay below 2^8 and neither the
+      // accumulators nor l need rescaling.  o = acc / l and lse = m + log2 l hold for any m
+      // the whole sum shares.  The first tile always moves it (m starts at -inf, and key 0 of
+      // the first tile is visible to every query).
+      if (__any(mx > mrun[n] + 8.f)) {
+        const float mnew = fmaxf(mrun[n], mx);
+        const float alpha = exp2_hw(mrun[n] - mnew);
+        mrun[n] = mnew;
+        lsum[n] *= alpha;
+#pragma unroll
+        for (int d = 0; d < DV / 16; ++d) acc[n][d] *= alpha;
+      }
       float ps = 0.f;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = exp2_hw(sc[n][kb][i] - mnew);
+          const float p = exp2_hw(fmaf(sc[n][kb][i], c, -mrun[n]));
           sc[n][kb][i] = p;
           ps += p;
         }
-      lsum[n] = lsum[n] * alpha + ps;
-#pragma unroll
-      for (int d = 0; d < DV / 16; ++d) acc[n][d] *= alpha;
+      lsum[n] += ps;
       pb[n][0] = pf_pair(sc[n][0], sc[n][1]);
       pb[n][1] = pf_pair(sc[n][2], sc[n][3]);
     }

@@ -29,12 +29,15 @@ def _maps(t):
 class _Run:
     """Device tables + one forward and backward of the library on seeded bf16 inputs."""
 
-    def __init__(self, m, off, C, H, dqk, dv, seed, gen_on_gpu=False):
+    def __init__(self, m, off, C, H, dqk, dv, seed, gen_on_gpu=False, inputs=None):
         tb = harts.attn_tables(m, off, C)
         self.tb = tb
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.qt, self.kv, self.kt, self.ql = dev(tb["qtiles"]), dev(tb["kv_list"]), dev(tb["ktiles"]), dev(tb["q_list"])
-        if gen_on_gpu:
+        if inputs is not None:  # float arrays [C, H, d]: q, k, v, dout
+            self.q, self.k, self.v, self.do = (torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).cuda()
+                                               for a in inputs)
+        elif gen_on_gpu:
             g = torch.Generator(device="cuda").manual_seed(seed)
             mk = lambda d: torch.randn((C, H, d), generator=g, device="cuda").to(torch.bfloat16)
             self.q, self.k, self.v, self.do = mk(dqk), mk(dqk), mk(dv), mk(dv)
@@ -104,6 +107,53 @@ def test_attn_chains_and_ragged_tiles():
         m, off, C = _maps(t)
         print(f"attn chains {lens}: C={C}", flush=True)
         _check_full(_Run(m, off, C, 3, 192, 128, seed=20 + i), m, off)
+
+
+@pytest.mark.parametrize("trend", [1.0, -1.0])
+def test_attn_scores_rising_or_falling_along_the_path(trend):
+    """Scores whose maximum rises by about 10 (base 2) from one 64-key tile to the next move the
+    forward's softmax reference on every tile; falling scores leave it at the first tile and add
+    probabilities far below 1 from the later ones.  One chain of 520 rows (nine 64-key tiles)."""
+    dqk, dv, H = 192, 128, 2
+    t = trees.forest_of_sequences([520], seed=0)
+    m, off, C = _maps(t)
+    rng = np.random.default_rng(17)
+    u = rng.standard_normal(dqk)
+    u *= np.sqrt(dqk) / np.linalg.norm(u)
+    pos = np.empty(C)
+    pos[m] = np.arange(len(m))  # the position of each compact row on the chain
+    b = (pos / 64.0) if trend > 0 else (pos.max() - pos) / 64.0
+    q = 0.5 * u[None, None, :] + 0.3 * rng.standard_normal((C, H, dqk))
+    k = b[:, None, None] * u[None, None, :] + 0.3 * rng.standard_normal((C, H, dqk))
+    v = rng.standard_normal((C, H, dv))
+    do = rng.standard_normal((C, H, dv))
+    r = _Run(m, off, C, H, dqk, dv, seed=0, inputs=(q, k, v, do))
+    qq, kk, vv, dd = (_np(x) for x in (r.q, r.k, r.v, r.do))
+    o, lse = oatt.attention_forward(qq, kk, vv, m, off, r.scale)
+    dq, dk, dvv = oatt.attention_backward(qq, kk, vv, dd, m, off, r.scale)
+    got_o = _np(r.o)
+    assert np.isfinite(got_o).all()
+    assert np.abs(got_o - o).max() <= 2.0 ** -7 * np.abs(vv).max()
+    assert np.abs(_np(r.lse) - lse).max() <= 1e-3
+    for got, ref, name in ((r.dk, dk, "dk"), (r.dv, dvv, "dv")):
+        g = _np(got)
+        _close(g, ref, 2.0 ** -6, name)
+        assert np.linalg.norm(g - ref) <= 2.0 ** -7 * np.linalg.norm(ref), name
+    # dq = scale sum_j ds_j k_j with sum_j ds_j = 0: the keys' large common part (b_j u) cancels
+    # in exact arithmetic, but not once ds_j = p_j (dp_j - delta) is rounded to bf16 for the matrix
+    # cores (relative 2^-9) with delta taken from the bf16 output.  Per row and head the error is
+    # held to 2^-7 scale sum_j (|ds_j| + p_j sum_e |dout_e o_e|) max|k_j|, four times those roundings.
+    g = _np(r.dq)
+    assert np.isfinite(g).all()
+    P = oatt.paths(m, off, C)
+    kmax = np.abs(kk).max(axis=2)  # [C, H]
+    for t_ in range(C):
+        for h in range(H):
+            _, _, p_, ds = oatt.row_terms(qq, kk, vv, dd, P[t_], t_, h, r.scale)
+            dabs = np.abs(dd[t_, h] * o[t_, h]).sum()
+            bound = 2.0 ** -7 * r.scale * ((np.abs(ds) + p_ * dabs) @ kmax[P[t_], h]) + 1e-4
+            err = np.abs(g[t_, h] - dq[t_, h]).max()
+            assert err <= bound, ("dq", t_, h, err, bound)
 
 
 def test_attn_single_row():
