@@ -223,7 +223,8 @@ int harts_kda_fwd(const harts_dev_plan *dplan, const harts_kda_io *io, void *str
 
 /*
  * The flat packed call in one function [blog 1.2, 4.3]: independent sequences (no tree, no
- * replay) given by host cu_seqlens [n_seq + 1], one round, from the zero state or from
+ * replay) given by host cu_seqlens [n_seq + 1] (lengths >= 1, else HARTS_EINVAL before any device
+ * work, as for harts_plan_create_varlen), one round, from the zero state or from
  * init_states[i] where init_mask[i] != 0 (init_mask host uint8 [n_seq], or NULL: every sequence
  * with init_states != NULL starts from it), writing o and, when boundary_states != NULL, the state
  * after every multiple of chunk_B inside each sequence (sum_i floor(L_i / chunk_B) states,
