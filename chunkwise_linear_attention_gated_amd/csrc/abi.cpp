@@ -636,6 +636,8 @@ int harts_kda_fwd_varlen(const harts_varlen_args* a, void* stream) {
   const int rc = guarded([&] {
     if (!a) throw Error(HARTS_EINVAL, "args is NULL");
     if (!a->cu_seqlens || a->n_seq < 1) throw Error(HARTS_EINVAL, "cu_seqlens and n_seq >= 1 are required");
+    if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)
+      throw Error(HARTS_EINVAL, "q, k, v, g, beta and o are required");
     std::vector<uint8_t> mask;
     const uint8_t* has_init = nullptr;
     if (a->init_states) {

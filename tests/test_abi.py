@@ -80,7 +80,10 @@ def test_kda_fwd_varlen_rejects_bad_arguments_before_any_device_work():
     assert f(ctypes.byref(a), None) == -1 and b"cu_seqlens" in _lib._last_error()
     cu = np.array([0, 5, 3], np.int64)
     a.cu_seqlens, a.n_seq, a.H, a.dk, a.dv, a.chunk_B = cu.ctypes.data, 2, 2, 128, 128, 64
-    assert f(ctypes.byref(a), None) == -1  # decreasing cu_seqlens: the plan is refused
+    assert f(ctypes.byref(a), None) == -1 and b"required" in _lib._last_error()  # no tensors
+    # stand-in addresses: every case below is refused on the host, before any of them is used
+    a.q = a.k = a.v = a.g = a.beta = a.o = 256
+    assert f(ctypes.byref(a), None) == -1 and b"decreasing" in _lib._last_error()  # the plan is refused
     cu2 = np.array([0, 5, 9], np.int64)
     a.cu_seqlens, a.dk, a.dv = cu2.ctypes.data, 48, 48
     assert f(ctypes.byref(a), None) == -1 and b"unsupported" in _lib._last_error()
