@@ -122,7 +122,23 @@ __global__ __launch_bounds__(256) void conv_dx_kernel(const T* __restrict__ dout
     ld8<T>(dout + s * ch + c0, cur);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = wv[0][e] * cur[e];
-    for (int64_t i = so[s - s0]; i < so[s - s0 + 1]; ++i) {
+    // Inside a branch the list is exactly (s + 1, 1) .. (s + W - 1, W - 1), rows this thread
+    // already holds: the window's weights then apply at fixed places.  Rows near a fork, a leaf
+    // end or the block's end take the general walk.  The test is the same for the block's threads.
+    const int64_t ia = so[s - s0], ib = so[s - s0 + 1];
+    bool inner = ib - ia == W - 1 && s + W - 1 < s1;
+#pragma unroll
+    for (int q = 1; q < W; ++q) {
+      const int64_t i = ia + q - 1;
+      const int64_t ge = !inner ? -1 : i - g0 < KG ? sg[i - g0] : gl[i];
+      inner = inner && ge == (((s + q) << 3) | q);
+    }
+    if (inner) {
+#pragma unroll
+      for (int q = 1; q < W; ++q)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += wv[q][e] * next[q - 1][e];
+    } else for (int64_t i = ia; i < ib; ++i) {
       const int64_t ge = i - g0 < KG ? sg[i - g0] : gl[i];
       const int64_t t = ge >> 3;
       const int j = int(ge & 7);
