@@ -995,7 +995,10 @@ __global__ __launch_bounds__(64 * (DV / 16)) void kda_grad_kernel(BwdRoundArgs b
       for (int ks = 0; ks < CB::NKS; ++ks) {
         const bf16x8 df = frag(ks);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) rs += (float)hf[ks][t] * (float)df[t];
+        for (int t = 0; t < 8; t += 2) {  // two bf16 products per instruction, summed in fp32
+          typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+          rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{hf[ks][t], hf[ks][t + 1]}, bf16x2{df[t], df[t + 1]}, rs, false);
+        }
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb) X23[bb] = MM::mma(MM::kc(Us, LDV, 16 * bb, ks * MM::KS, lane), df, X23[bb]);
       }
