@@ -105,7 +105,7 @@ __global__ __launch_bounds__(MT) void moe_route_kernel(MoeArgs a) {
     float sum = 0.f;
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      p[j] = expf(p[j] - m);
+      p[j] = __expf(p[j] - m);  // exponent <= 0: the hardware 2^x after one multiply
       sum += p[j];
     }
     sum = gsum(sum);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(MT) void moe_grad_kernel(MoeArgs a) {
   float sum = 0.f;
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
-    p[j] = expf(p[j] - m);
+    p[j] = __expf(p[j] - m);  // as in the route kernel
     sum += p[j];
   }
   sum = gsum(sum);
